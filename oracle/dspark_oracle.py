@@ -1,0 +1,373 @@
+"""fp64 oracle: the DSpark draft-attention forward as the design page defines it.
+
+TEST INFRASTRUCTURE -- see the package docstring for who may import this.
+
+Source: the GLM 5.2 DSpark training-design page ("GLM 5.2 DSpark 投机训练设计").
+Sections cited below:
+  * parameter summary (参数摘要): dims, SWA window W, block length 5;
+  * §2 model inputs (模型输入): "Anchor sampling", "QKV construction";
+  * §3 attention mask (注意力掩码): causal window, bidirectional block,
+    padding block;
+  * §4 MLA: "MLA Projection" (q^C/q^R, c^KV -> k^C, v; k^R), scale, "RoPE";
+  * §6 training objective, "eval_mask" paragraph (loss_mask[S-1] := 0);
+  * appendix A, option 2 (loss_mask[S-1] := 0 on read);
+  * appendix "Attention implementation": the mask shape, the attention
+    equation softmax(QK^T/sqrt(d) + Lambda(M)) V, and the dense eager/sdpa
+    materialisation.
+
+Readings where the page is silent or ambiguous (each also listed in the design
+notes of the repository):
+  * scale: the §4 value (d_c + d_r)^(-1/2), not the generic sqrt(d) of the
+    appendix equation;
+  * RoPE: base 10000, pair i = (2i, 2i+1) rotated counter-clockwise by
+    p * base^(-2i/d_r) (interleaved adjacent pairs, §4 "RoPE");
+  * weights: W_UK [H, d_c, D] and W_UV [H, d_v, D] (out x in), so that
+    k^C_h = W_UK[h] c and v_h = W_UV[h] c;
+  * padding rows have no defined output; this oracle returns NaN for them;
+  * "pick N at random": the integer-only SplitMix64 partial Fisher-Yates
+    spec in ``select_anchors``.
+
+Everything is fp64.  bf16 inputs arrive as raw uint16 bit patterns and are
+decoded exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 5
+MASK64 = (1 << 64) - 1
+
+
+# ---------------------------------------------------------------------------
+# input decoding
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact bf16 -> fp64: a bf16 value is the top 16 bits of an fp32."""
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def _f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_to_f64(x)
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# anchors  (§2 "Anchor sampling"; §6 "eval_mask"; appendix A option 2)
+# ---------------------------------------------------------------------------
+
+def candidates(loss_mask_row: np.ndarray) -> np.ndarray:
+    """Valid anchor positions, ascending.
+
+    §2: A is a candidate iff A in [0, S-2], loss_mask[A] = 1 and
+    loss_mask[A+1] = 1.  §6 / appendix A: on read, loss_mask[S-1] is set to 0
+    (so x_{S-1} is neither an anchor nor a label).
+    """
+    lm = np.array(loss_mask_row, dtype=np.int64, copy=True)
+    S = lm.shape[0]
+    lm[S - 1] = 0
+    out = []
+    for a in range(0, S - 1):           # A in [0, S-2]
+        if lm[a] == 1 and lm[a + 1] == 1:
+            out.append(a)
+    return np.array(out, dtype=np.int64)
+
+
+class SplitMix64:
+    """SplitMix64 (Steele, Lea & Flood, OOPSLA 2014; Vigna's splitmix64.c):
+    the state advances by the golden-ratio increment 0x9E3779B97F4A7C15 and
+    each output is the state passed through the variant-13 xor-shift-multiply
+    finaliser (shifts 30, 27, 31; multipliers 0xBF58476D1CE4E5B9,
+    0x94D049BB133111EB)."""
+
+    def __init__(self, seed: int):
+        self.state = seed & MASK64
+
+    def next(self) -> int:
+        self.state = (self.state + 0x9E3779B97F4A7C15) & MASK64
+        z = self.state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK64
+        return z ^ (z >> 31)
+
+
+def select_anchors(loss_mask_row: np.ndarray, num_anchors: int, seed: int):
+    """§2 "Anchor sampling": draw N of the valid positions at random, N <=
+    num_anchors; padding blocks fill the batch when fewer are valid (§3
+    "Padding block").
+
+    The page fixes neither the generator nor the draw, so this is the spec:
+      C = candidates(loss_mask)
+      |C| <= N : anchors = C then (N-|C|) padding slots (A = 0, keep = 0)
+      |C| >  N : partial Fisher-Yates over C with SplitMix64(seed):
+                 for i in 0..N-1: j = i + next() mod (|C| - i); swap C[i], C[j]
+                 anchors = sorted(C[0:N]); keep = 1
+    Returns (anchors int32 [N], keep uint8 [N]).
+    """
+    C = [int(c) for c in candidates(loss_mask_row)]
+    N = int(num_anchors)
+    anchors = np.zeros(N, dtype=np.int32)
+    keep = np.zeros(N, dtype=np.uint8)
+    if len(C) <= N:
+        anchors[: len(C)] = C
+        keep[: len(C)] = 1
+        return anchors, keep
+    rng = SplitMix64(seed)
+    for i in range(N):
+        j = i + rng.next() % (len(C) - i)
+        C[i], C[j] = C[j], C[i]
+    anchors[:] = sorted(C[:N])
+    keep[:] = 1
+    return anchors, keep
+
+
+# ---------------------------------------------------------------------------
+# KV axis, positions and mask  (§2 "QKV construction"; §3; appendix)
+# ---------------------------------------------------------------------------
+
+def positions(S: int, anchors_row: np.ndarray, block: int = BLOCK):
+    """§2 "QKV construction" and §4 "RoPE": the KV axis is [S context ; N
+    blocks of 5]; context positions are 0..S-1, block n has A_n..A_n+4; the
+    queries use the second part of the axis."""
+    pos_kv = list(range(S))
+    for a in np.asarray(anchors_row).tolist():
+        pos_kv.extend(int(a) + j for j in range(block))
+    pos_kv = np.array(pos_kv, dtype=np.int64)
+    return pos_kv, pos_kv[S:]
+
+
+def mask_rows(S: int, N: int, W: int, anchors_row, keep_row, n: int, block: int = BLOCK):
+    """The `block` rows of M belonging to block n, whole rows of length S+5N.
+
+    §3: for kv < S, row q of a kept block sees A-W+1 <= kv < A (the same
+    window for all 5 queries, not shifted with the offset; A itself excluded);
+    for kv >= S it sees only its own block's 5 positions (bidirectional).
+    A padding block (keep = 0) sees nothing.  The anchor of a padding block
+    is never read.
+    """
+    L = S + block * N
+    rows = np.zeros((block, L), dtype=bool)
+    if not keep_row[n]:
+        return rows
+    A = int(anchors_row[n])
+    kv = np.arange(L, dtype=np.int64)
+    for j in range(block):          # every query of the block, evaluated on its own
+        ctx_part = (kv < S) & (A - W + 1 <= kv) & (kv < A)
+        draft_part = (kv >= S) & ((kv - S) // block == n)
+        rows[j] = ctx_part | draft_part
+    return rows
+
+
+def build_mask(S: int, N: int, W: int, anchors_row, keep_row, block: int = BLOCK) -> np.ndarray:
+    """Dense boolean M in {0,1}^{5N x (S+5N)} for one sample (appendix
+    "Attention implementation": the eager/sdpa backend materialises exactly
+    this tensor, broadcast over heads)."""
+    return np.concatenate([mask_rows(S, N, W, anchors_row, keep_row, n, block)
+                           for n in range(N)], axis=0)
+
+
+def row_index_sets(M: np.ndarray, S: int):
+    """Per row: (visible context columns, visible draft columns) as sorted
+    int arrays, read off the materialised mask."""
+    out = []
+    for r in range(M.shape[0]):
+        nz = np.nonzero(M[r])[0]
+        out.append((nz[nz < S], nz[nz >= S]))
+    return out
+
+
+def block_index_records(S: int, N: int, W: int, anchors_row, keep_row, block: int = BLOCK):
+    """Per block: (ctx_lo, ctx_len, pos0, keep) read off the block's mask rows:
+    ctx_lo/ctx_len describe the visible context columns (which §3 makes a
+    contiguous run), pos0 is the RoPE position of the block's first query.
+    A padding block reports (0, 0, 0, 0)."""
+    recs = np.zeros((N, 4), dtype=np.int64)
+    for n in range(N):
+        if not keep_row[n]:
+            continue
+        rows = mask_rows(S, N, W, anchors_row, keep_row, n, block)
+        ctx = np.nonzero(rows[0, :S])[0]
+        lo = int(ctx[0]) if len(ctx) else int(anchors_row[n])
+        recs[n] = (lo, len(ctx), int(anchors_row[n]), 1)
+    return recs
+
+
+# ---------------------------------------------------------------------------
+# RoPE  (§4 "RoPE")
+# ---------------------------------------------------------------------------
+
+def rope_theta(d_r: int, base: float) -> np.ndarray:
+    """theta_i = base^(-2i/d_r) for pair i = 0 .. d_r/2-1."""
+    i = np.arange(d_r // 2, dtype=np.float64)
+    return np.power(float(base), -2.0 * i / d_r)
+
+
+def rope_interleaved(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """Rotate the d_r-wide rope slice by position, interleaved adjacent pairs
+    (GLM rope_interleave = true): (x_{2i}, x_{2i+1}) ->
+    (x_{2i} cos phi - x_{2i+1} sin phi, x_{2i} sin phi + x_{2i+1} cos phi),
+    phi = pos * theta_i.  x has shape [..., T, d_r] (any leading dims are
+    broadcast), pos has shape [T]."""
+    x = np.asarray(x, dtype=np.float64)
+    d_r = x.shape[-1]
+    phi = np.asarray(pos, dtype=np.float64)[:, None] * rope_theta(d_r, base)[None, :]
+    c, s = np.cos(phi), np.sin(phi)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = x0 * c - x1 * s
+    y[..., 1::2] = x0 * s + x1 * c
+    return y
+
+
+# ---------------------------------------------------------------------------
+# expanded MLA per head  (§4 "MLA Projection")
+# ---------------------------------------------------------------------------
+
+def expand_head(ckv_all: np.ndarray, kr_rot_all: np.ndarray, w_uk: np.ndarray,
+                w_uv: np.ndarray, h: int):
+    """§4: c^KV expands through kv_b_proj into per-head k^C (d_c) and v (d_v);
+    k^R is not expanded, it is rotated and copied to every head and
+    concatenated: K_h = [k^C_h ; k^R] (d_c + d_r), V_h = v_h (d_v).
+    Each key is a function of exactly its 576 = 512 + 64 cached numbers
+    (parameter summary, "KV cache")."""
+    Kc = ckv_all @ w_uk[h].T            # [L, d_c]
+    K = np.concatenate([Kc, kr_rot_all], axis=1)
+    V = ckv_all @ w_uv[h].T             # [L, d_v]
+    return K, V
+
+
+# ---------------------------------------------------------------------------
+# attention  (appendix "Attention implementation"; §4 scale)
+# ---------------------------------------------------------------------------
+
+def softmax_scale(d_c: int, d_r: int) -> float:
+    """§4: the attention scale is (d_c + d_r)^(-1/2) (1/16 for the GLM dims)."""
+    return float(d_c + d_r) ** -0.5
+
+
+def _softmax_rows(logits: np.ndarray) -> np.ndarray:
+    m = np.max(logits, axis=-1, keepdims=True)
+    e = np.exp(logits - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attend_dense(Q: np.ndarray, K: np.ndarray, V: np.ndarray, M: np.ndarray,
+                 scale: float) -> np.ndarray:
+    """Literal form: softmax(scale * Q K^T + Lambda(M)) V with Lambda = 0
+    where M = 1 and -inf where M = 0.  Rows with no visible key (padding
+    rows) have no defined value and come back as NaN."""
+    logits = scale * (Q @ K.T)
+    logits = np.where(M, logits, -np.inf)
+    out = np.full((Q.shape[0], V.shape[1]), np.nan)
+    live = M.any(axis=1)
+    if live.any():
+        out[live] = _softmax_rows(logits[live]) @ V
+    return out
+
+
+def attend_gathered(Q: np.ndarray, K: np.ndarray, V: np.ndarray, M: np.ndarray,
+                    scale: float) -> np.ndarray:
+    """Each row restricted to its visible columns {kv : M = 1}; identical to
+    the literal form because exp(-inf) = 0."""
+    out = np.full((Q.shape[0], V.shape[1]), np.nan)
+    for r in range(Q.shape[0]):
+        cols = np.nonzero(M[r])[0]
+        if len(cols) == 0:
+            continue
+        w = _softmax_rows((scale * (K[cols] @ Q[r]))[None, :])[0]
+        out[r] = w @ V[cols]
+    return out
+
+
+def _layer_f64(wl, layer):
+    dt = wl.dtype
+    return {name: _f64(getattr(layer, name), dt) for name in
+            ("q_nope", "q_rope", "ckv_ctx", "kr_ctx", "ckv_blk", "kr_blk", "w_uk", "w_uv")}
+
+
+def forward(wl, layer_idx: int = 0, anchors=None, keep=None, form: str = "dense",
+            blocks=None, scale=None):
+    """Reference output [B, 5N, H, d_v] (fp64; padding rows are NaN).
+
+    wl: a ``workloads.Workload``.  anchors/keep default to the workload's.
+    form: "dense" (literal masked softmax over the whole KV axis) or
+    "gathered" (visible columns only).
+    blocks: None for every block; otherwise a list of (b, n) pairs -- then
+    only those blocks' rows are computed (their mask rows are still whole
+    rows of length S+5N) and the keys are expanded only at the columns those
+    rows see; every other row is NaN.
+    scale: None for the §4 value; a float overrides it.
+    """
+    scale = softmax_scale(wl.d_c, wl.d_r) if scale is None else float(scale)
+    anchors = wl.anchors if anchors is None else anchors
+    keep = wl.keep if keep is None else keep
+    B, S, N, W, H, bl = wl.B, wl.S, wl.N, wl.W, wl.H, wl.block
+    x = _layer_f64(wl, wl.layers[layer_idx])
+    out = np.full((B, bl * N, H, wl.d_v), np.nan)
+    by_sample = {}
+    if blocks is not None:
+        for (b, n) in blocks:
+            by_sample.setdefault(int(b), []).append(int(n))
+    for b in range(B):
+        if blocks is not None and b not in by_sample:
+            continue
+        pos_kv, pos_q = positions(S, anchors[b], bl)
+        ckv_all = np.concatenate([x["ckv_ctx"][b], x["ckv_blk"][b]], axis=0)
+        kr_rot = rope_interleaved(np.concatenate([x["kr_ctx"][b], x["kr_blk"][b]], axis=0),
+                                  pos_kv, wl.rope_base)
+        qr_rot = rope_interleaved(x["q_rope"][b].transpose(1, 0, 2), pos_q, wl.rope_base)
+        if blocks is None:
+            M = build_mask(S, N, W, anchors[b], keep[b], bl)
+            rows = np.arange(bl * N)
+        else:
+            ns = sorted(set(by_sample[b]))
+            M = np.concatenate([mask_rows(S, N, W, anchors[b], keep[b], n, bl) for n in ns], 0)
+            rows = np.array([bl * n + j for n in ns for j in range(bl)])
+            cols = np.nonzero(M.any(axis=0))[0]
+            # only the visible columns are ever weighted; restrict the axis
+            ckv_all, kr_rot, M = ckv_all[cols], kr_rot[cols], M[:, cols]
+        for h in range(H):
+            K, V = expand_head(ckv_all, kr_rot, x["w_uk"], x["w_uv"], h)
+            Q = np.concatenate([x["q_nope"][b][rows, h, :], qr_rot[h][rows]], axis=1)
+            if form == "dense":
+                o = attend_dense(Q, K, V, M, scale)
+            elif form == "gathered":
+                o = attend_gathered(Q, K, V, M, scale)
+            else:
+                raise ValueError(form)
+            out[b, rows, h, :] = o
+    return out
+
+
+def forward_absorbed(wl, layer_idx: int = 0, anchors=None, keep=None, scale=None):
+    """The same forward computed in the absorbed latent form (used only to
+    pin the identity the GPU path relies on):
+      q_abs = W_UK[h]^T q^C,  score = scale * (q_abs . c^KV + q^R . k^R),
+      o_lat = sum_k p_k c^KV_k,  out = W_UV[h] o_lat.
+    Per-row loop over blocks, plain numpy."""
+    scale = softmax_scale(wl.d_c, wl.d_r) if scale is None else float(scale)
+    anchors = wl.anchors if anchors is None else anchors
+    keep = wl.keep if keep is None else keep
+    B, S, N, W, H, bl = wl.B, wl.S, wl.N, wl.W, wl.H, wl.block
+    x = _layer_f64(wl, wl.layers[layer_idx])
+    out = np.full((B, bl * N, H, wl.d_v), np.nan)
+    for b in range(B):
+        pos_kv, pos_q = positions(S, anchors[b], bl)
+        ckv_all = np.concatenate([x["ckv_ctx"][b], x["ckv_blk"][b]], axis=0)
+        kr_rot = rope_interleaved(np.concatenate([x["kr_ctx"][b], x["kr_blk"][b]], axis=0),
+                                  pos_kv, wl.rope_base)
+        qr_rot = rope_interleaved(x["q_rope"][b].transpose(1, 0, 2), pos_q, wl.rope_base)
+        M = build_mask(S, N, W, anchors[b], keep[b], bl)
+        for r in range(bl * N):
+            cols = np.nonzero(M[r])[0]
+            if len(cols) == 0:
+                continue
+            for h in range(H):
+                q_abs = x["w_uk"][h].T @ x["q_nope"][b][r, h]
+                s = scale * (ckv_all[cols] @ q_abs + kr_rot[cols] @ qr_rot[h][r])
+                p = _softmax_rows(s[None, :])[0]
+                o_lat = p @ ckv_all[cols]
+                out[b, r, h] = x["w_uv"][h] @ o_lat
+    return out

@@ -1,0 +1,267 @@
+"""Seeded synthetic inputs for the DSpark draft-attention forward.
+
+This module is the only code shared by the fp64 oracle and the HIP path.  It
+draws random numbers and lays them out; it contains none of the method's
+arithmetic (no mask, no RoPE, no attention, no candidate-anchor rule).
+
+Shapes follow the GLM-5.2 DSpark design page (parameter summary and the
+"QKV construction" section): per draft layer the attention consumes
+
+    q_nope  [B, 5N, H, d_c]   q_rope [B, 5N, H, d_r]   (unrotated)
+    ckv_ctx [B, S, D]         kr_ctx [B, S, d_r]       (context latents)
+    ckv_blk [B, 5N, D]        kr_blk [B, 5N, d_r]      (draft-block latents)
+    w_uk    [H, d_c, D]       w_uv   [H, d_v, D]       (kv_b_proj split, out x in)
+    anchors [B, N] int32      keep   [B, N] uint8
+
+bf16 tensors are produced in fp32 and rounded to bf16 with round-to-nearest-
+even here, and stored as raw uint16 bit patterns; both sides consume exactly
+those values.  Activations are N(0, 1); weights are N(0, 1/D) (variance 1/D).
+
+Anchors are never derived from the loss mask here.  A recipe either places
+anchors itself and then forces loss_mask[A] = loss_mask[A+1] = 1 so that they
+are valid by construction (positions are drawn from [0, S-3], because the
+page resets loss_mask[S-1] to 0 on read), or it hands the loss mask and a
+sampler seed to each side, which runs its own anchor sampler.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+
+BLOCK = 5
+
+# GLM-5.2 DSpark draft attention dims (design page, parameter summary).
+GLM_DIMS = dict(H=64, D=512, d_c=192, d_r=64, d_v=256, W=128)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (round to nearest, ties to even); raw bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class Layer:
+    q_nope: np.ndarray
+    q_rope: np.ndarray
+    ckv_ctx: np.ndarray
+    kr_ctx: np.ndarray
+    ckv_blk: np.ndarray
+    kr_blk: np.ndarray
+    w_uk: np.ndarray
+    w_uv: np.ndarray
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    B: int
+    S: int
+    N: int
+    W: int
+    H: int
+    D: int
+    d_c: int
+    d_r: int
+    d_v: int
+    dtype: str                      # "bf16" (uint16 bit arrays) or "f32"
+    rope_base: float
+    loss_mask: np.ndarray           # [B, S] uint8
+    anchors: Optional[np.ndarray]   # [B, N] int32, None when anchor_source == "sampler"
+    keep: Optional[np.ndarray]      # [B, N] uint8
+    anchor_source: str              # "given" or "sampler"
+    sampler_seed: int
+    layers: List[Layer]
+    block: int = BLOCK
+
+    @property
+    def q_len(self) -> int:
+        return self.block * self.N
+
+    def desc(self) -> dict:
+        return dict(B=self.B, S=self.S, N=self.N, block=self.block, window=self.W,
+                    n_heads=self.H, d_latent=self.D, d_nope=self.d_c, d_rope=self.d_r,
+                    d_v=self.d_v, rope_base=self.rope_base, dtype=self.dtype)
+
+
+# --------------------------------------------------------------------------
+# random tensors
+# --------------------------------------------------------------------------
+
+def _normal(rng: np.random.Generator, shape, std: float, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    return x
+
+
+def _make_layer(rng, B, S, N, H, D, d_c, d_r, d_v, dtype) -> Layer:
+    L5 = BLOCK * N
+    wstd = float(1.0 / np.sqrt(D))
+    # fixed draw order: q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv
+    return Layer(
+        q_nope=_normal(rng, (B, L5, H, d_c), 1.0, dtype),
+        q_rope=_normal(rng, (B, L5, H, d_r), 1.0, dtype),
+        ckv_ctx=_normal(rng, (B, S, D), 1.0, dtype),
+        kr_ctx=_normal(rng, (B, S, d_r), 1.0, dtype),
+        ckv_blk=_normal(rng, (B, L5, D), 1.0, dtype),
+        kr_blk=_normal(rng, (B, L5, d_r), 1.0, dtype),
+        w_uk=_normal(rng, (H, d_c, D), wstd, dtype),
+        w_uv=_normal(rng, (H, d_v, D), wstd, dtype),
+    )
+
+
+def _force_valid(lm_row: np.ndarray, anchors_row: np.ndarray, keep_row: np.ndarray) -> None:
+    for a, k in zip(anchors_row, keep_row):
+        if k:
+            lm_row[a] = 1
+            lm_row[a + 1] = 1
+
+
+# --------------------------------------------------------------------------
+# anchor recipes (placement only; validity is forced, never tested here)
+# --------------------------------------------------------------------------
+
+def _recipe_uniform(rng, S, N, W, n_forced_low=0):
+    """N distinct anchors uniform over [0, S-3]; the first n_forced_low of them
+    are drawn from [0, W-2] (clamped windows)."""
+    chosen = set()
+    low = []
+    while len(low) < n_forced_low:
+        a = int(rng.integers(0, max(1, min(W - 1, S - 2))))
+        if a not in chosen:
+            chosen.add(a)
+            low.append(a)
+    while len(chosen) < N:
+        chosen.add(int(rng.integers(0, S - 2)))
+    anchors = np.array(sorted(chosen), dtype=np.int32)
+    return anchors, np.ones(N, dtype=np.uint8)
+
+
+def _recipe_clustered(rng, S, N, frac=0.30, cluster=8, span=64):
+    """~frac of the anchors in clusters of `cluster` drawn without replacement
+    from [c, c+span-1]; the rest uniform over the remaining positions."""
+    n_cl = int(round(frac * N))
+    chosen = set()
+    while len(chosen) < n_cl:
+        c = int(rng.integers(0, S - span - 1))
+        take = min(cluster, n_cl - len(chosen))
+        pool = [p for p in range(c, c + span) if p <= S - 3 and p not in chosen]
+        if len(pool) < take:
+            continue
+        for p in rng.choice(np.array(pool), size=take, replace=False):
+            chosen.add(int(p))
+    while len(chosen) < N:
+        chosen.add(int(rng.integers(0, S - 2)))
+    anchors = np.array(sorted(chosen), dtype=np.int32)
+    return anchors, np.ones(N, dtype=np.uint8)
+
+
+def _recipe_headline(rng, S, N, W, pad_frac=0.25, low_frac=0.05):
+    """pad_frac of the slots are padding (keep=0, garbage anchor values);
+    low_frac of the slots hold clamped-window anchors in [0, W-2] that include
+    0, 1 and W-2; the rest are uniform over [W-1, S-3].  Kept anchors ascend
+    across slots."""
+    n_pad = int(round(pad_frac * N))
+    n_low = int(round(low_frac * N))
+    n_hi = N - n_pad - n_low
+    low = {0, 1, W - 2} if n_low >= 3 else set()
+    while len(low) < n_low:
+        low.add(int(rng.integers(0, W - 1)))
+    hi = set()
+    while len(hi) < n_hi:
+        hi.add(int(rng.integers(W - 1, S - 2)))
+    kept = np.array(sorted(low) + sorted(hi), dtype=np.int32)
+    pad_slots = np.sort(rng.choice(N, size=n_pad, replace=False))
+    keep = np.ones(N, dtype=np.uint8)
+    keep[pad_slots] = 0
+    anchors = np.empty(N, dtype=np.int32)
+    anchors[keep == 1] = kept
+    garbage = np.array([-1, S + 7, -(2 ** 31), 2 ** 31 - 1, S - 1, S], dtype=np.int64)
+    anchors[keep == 0] = garbage[np.arange(n_pad) % len(garbage)].astype(np.int32)
+    return anchors, keep
+
+
+def make_workload(name: str, *, B: int, S: int, N: int, dims: dict, dtype: str,
+                  recipe: str, seed: int, layers: int = 1, rope_base: float = 10000.0,
+                  recipe_args: Optional[dict] = None) -> Workload:
+    recipe_args = recipe_args or {}
+    H, D, d_c, d_r, d_v, W = (dims[k] for k in ("H", "D", "d_c", "d_r", "d_v", "W"))
+    ss = np.random.SeedSequence(seed)
+    s_lm, s_anchor, s_tensor = ss.spawn(3)
+    rng_lm = np.random.Generator(np.random.PCG64(s_lm))
+    rng_a = np.random.Generator(np.random.PCG64(s_anchor))
+    rng_t = np.random.Generator(np.random.PCG64(s_tensor))
+
+    lm = (rng_lm.random((B, S)) < 0.9).astype(np.uint8)
+    anchors = keep = None
+    source = "given"
+    if recipe == "sampler":
+        source = "sampler"
+    else:
+        anchors = np.empty((B, N), dtype=np.int32)
+        keep = np.empty((B, N), dtype=np.uint8)
+        for b in range(B):
+            if recipe == "uniform":
+                a, k = _recipe_uniform(rng_a, S, N, W, **recipe_args)
+            elif recipe == "clustered":
+                a, k = _recipe_clustered(rng_a, S, N, **recipe_args)
+            elif recipe == "headline":
+                a, k = _recipe_headline(rng_a, S, N, W, **recipe_args)
+            else:
+                raise ValueError(f"unknown anchor recipe {recipe!r}")
+            anchors[b], keep[b] = a, k
+            _force_valid(lm[b], a, k)
+    lays = [_make_layer(rng_t, B, S, N, H, D, d_c, d_r, d_v, dtype) for _ in range(layers)]
+    return Workload(name=name, B=B, S=S, N=N, W=W, H=H, D=D, d_c=d_c, d_r=d_r, d_v=d_v,
+                    dtype=dtype, rope_base=rope_base,
+                    loss_mask=lm, anchors=anchors, keep=keep, anchor_source=source,
+                    sampler_seed=0x5EED0000 + (seed & 0xFFFF), layers=lays)
+
+
+TINY_DIMS = dict(H=2, D=32, d_c=16, d_r=8, d_v=16, W=16)
+
+
+def config(k: int, *, seed: Optional[int] = None) -> Workload:
+    """The five benchmark configurations at full size (1-based index)."""
+    seed = 1000 + k if seed is None else seed
+    if k == 1:
+        return make_workload("tiny-fp32 B1 S48 N4 W16 H2", B=1, S=48, N=4, dims=TINY_DIMS,
+                             dtype="f32", recipe="uniform", seed=seed,
+                             recipe_args=dict(n_forced_low=1))
+    if k == 2:
+        return make_workload("glm-layer B1 S2048 N64", B=1, S=2048, N=64, dims=GLM_DIMS,
+                             dtype="bf16", recipe="sampler", seed=seed)
+    if k == 3:
+        return make_workload("overlap B2 S8192 N512", B=2, S=8192, N=512, dims=GLM_DIMS,
+                             dtype="bf16", recipe="clustered", seed=seed)
+    if k == 4:
+        return make_workload("headline B1 S32768 N1024", B=1, S=32768, N=1024, dims=GLM_DIMS,
+                             dtype="bf16", recipe="headline", seed=seed)
+    if k == 5:
+        return make_workload("three-layer B1 S131072 N4096 L3", B=1, S=131072, N=4096,
+                             dims=GLM_DIMS, dtype="bf16", recipe="sampler", seed=seed, layers=3)
+    raise ValueError(k)
+
+
+def scaled(k: int, *, S: int, N: int, B: Optional[int] = None, seed: Optional[int] = None,
+           dims: Optional[dict] = None, dtype: Optional[str] = None) -> Workload:
+    """A configuration's recipe at a smaller size (oracle-friendly parity cases)."""
+    seed = 2000 + k if seed is None else seed
+    dims = dims or (TINY_DIMS if k == 1 else GLM_DIMS)
+    dtype = dtype or ("f32" if k == 1 else "bf16")
+    recipe, args, Bd = {1: ("uniform", dict(n_forced_low=1), 1), 2: ("sampler", {}, 1),
+                        3: ("clustered", {}, 2), 4: ("headline", {}, 1),
+                        5: ("sampler", {}, 1)}[k]
+    return make_workload(f"cfg{k}-scaled B{B or Bd} S{S} N{N}", B=B or Bd, S=S, N=N, dims=dims,
+                         dtype=dtype, recipe=recipe, seed=seed, recipe_args=args,
+                         layers=3 if k == 5 else 1)
