@@ -1,0 +1,184 @@
+/*
+ * dspark_attn.h -- C ABI of libdspark_attn.so, the MI355X (gfx950) DSpark
+ * draft-attention forward.
+ *
+ * What is computed (GLM 5.2 DSpark training-design page, "GLM 5.2 DSpark
+ * 投机训练设计"): for every draft block n of every sample b, anchored at
+ * context position A_n, the 5 queries [x_A, MASK x4] attend over
+ *   - the context window [A_n - W + 1, A_n) of the projected context
+ *     (§3 "Causal attention"; the same window for all 5 queries, A_n itself
+ *     excluded, clamped at 0), and
+ *   - the 5 positions of their own block, bidirectionally (§3
+ *     "Bidirectional attention");
+ * a padding block (keep = 0) attends to nothing (§3 "Padding block").
+ * Keys and values are the MLA ones of §4 "MLA Projection": per head
+ * K_h = [W_UK[h] c^KV ; RoPE(k^R)], V_h = W_UV[h] c^KV; queries are
+ * [q^C ; RoPE(q^R)]; the scale is (d_c + d_r)^(-1/2) (§4); RoPE rotates
+ * interleaved adjacent pairs at the positions of §2 "QKV construction"
+ * (context 0..S-1, block n: A_n .. A_n+4).  The attention itself is the
+ * equation of the appendix "Attention implementation":
+ * softmax(scale * Q K^T + Lambda(M)) V.
+ *
+ * The library computes the same values in the absorbed latent form
+ * (q_abs = W_UK[h]^T q^C, scores over the 576 cached numbers per key,
+ * P . c^KV over 512, then W_UV[h]), which is an algebraic identity.
+ *
+ * Conventions for every entry point:
+ *   - all tensor pointers are DEVICE pointers to contiguous row-major data,
+ *     16-byte aligned, unless the comment says "host";
+ *   - the caller owns every buffer, including the workspace; the library
+ *     allocates and frees nothing and keeps no mutable global state, so calls
+ *     on different streams with different workspaces are independent;
+ *   - `stream` is a hipStream_t (NULL = the default stream); device work is
+ *     enqueued asynchronously and DSPARK_OK means "enqueued";
+ *   - no C++ exception crosses the ABI; on error the function returns a
+ *     negative dspark_status, enqueues nothing, and dspark_last_error()
+ *     returns a thread-local message.
+ */
+#ifndef DSPARK_ATTN_H
+#define DSPARK_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSPARK_ABI_VERSION 1
+
+typedef enum dspark_status {
+    DSPARK_OK = 0,
+    DSPARK_EINVAL = -1,       /* bad argument: null/misaligned pointer, bad size */
+    DSPARK_EUNSUPPORTED = -2, /* valid but unsupported shape or dtype */
+    DSPARK_EWORKSPACE = -3,   /* workspace missing, misaligned or too small */
+    DSPARK_EHIP = -4,         /* a HIP runtime call failed (message has the HIP error) */
+    DSPARK_EANCHOR = -5       /* a kept block had an anchor outside [0, S-2] */
+} dspark_status;
+
+typedef enum dspark_dtype {
+    DSPARK_F32 = 0,  /* fp32 inputs, weights and output */
+    DSPARK_BF16 = 1  /* bf16 inputs, weights and output */
+} dspark_dtype;
+
+/* Problem description.
+ *   B         samples; S context length; N anchor blocks per sample
+ *   block     draft block length; must be 5 (design page, §2 "Draft inputs")
+ *   window    W of the sliding window: W-1 context positions visible (§3)
+ *   n_heads   H;  d_latent D (kv rank, 512 for GLM);  d_nope d_c (192);
+ *   d_rope    d_r (64, even);  d_v (256)
+ *   rope_base RoPE base (> 0); theta_i = rope_base^(-2i/d_r)
+ *   softmax_scale  > 0 overrides the scale; <= 0 selects (d_nope+d_rope)^-1/2
+ *   dtype     a dspark_dtype
+ * Supported: any positive dims with d_rope even (generic kernels, fp32
+ * arithmetic); the MFMA fast path is taken for dtype BF16 with H = 64,
+ * D = 512, d_c = 192, d_r = 64, d_v = 256. */
+typedef struct dspark_attn_desc {
+    int32_t B, S, N, block, window;
+    int32_t n_heads, d_latent, d_nope, d_rope, d_v;
+    double rope_base;
+    double softmax_scale;
+    int32_t dtype;
+} dspark_attn_desc;
+
+/* Bytes of workspace dspark_attn_fwd needs for `desc` (0 on an invalid
+ * descriptor; see dspark_last_error).  The workspace holds the per-block
+ * index records, the compacted list of kept blocks, a small status area, the
+ * RoPE cos/sin table and, on the MFMA path, the bf16 latent intermediates
+ * q_abs and o_lat ([H, 5*B*N, D] each).  It must be 256-byte aligned. */
+size_t dspark_attn_workspace_size(const dspark_attn_desc* desc);
+
+/* The masked MLA attention forward of one draft layer.
+ *   q_nope  [B, 5N, H, d_c]   q^C of the draft queries (§4 "MLA Projection")
+ *   q_rope  [B, 5N, H, d_r]   q^R, NOT yet rotated
+ *   ckv_ctx [B, S, D]         c^KV of the context (after kv_a_layernorm)
+ *   kr_ctx  [B, S, d_r]       k^R of the context, not rotated
+ *   ckv_blk [B, 5N, D]        c^KV of the draft-block positions
+ *   kr_blk  [B, 5N, d_r]      k^R of the draft-block positions, not rotated
+ *   w_uk    [H, d_c, D]       k^C_h = w_uk[h] @ c^KV   (kv_b_proj, key part)
+ *   w_uv    [H, d_v, D]       v_h   = w_uv[h] @ c^KV   (kv_b_proj, value part)
+ *   anchors [B, N] int32      A_n; read only where keep = 1
+ *   keep    [B, N] uint8      block_keep_mask (0 = padding block)
+ *   out     [B, 5N, H, d_v]   attention output per head (before o_proj)
+ * Rows of padding blocks are written as 0.  A kept block whose anchor lies
+ * outside [0, S-2] is an error detected on the device: its rows are written
+ * as NaN and dspark_read_device_status reports DSPARK_EANCHOR.
+ * Inputs and output share desc->dtype.  Tensors must not alias `out` or the
+ * workspace. */
+dspark_status dspark_attn_fwd(const dspark_attn_desc* desc,
+                              const void* q_nope, const void* q_rope,
+                              const void* ckv_ctx, const void* kr_ctx,
+                              const void* ckv_blk, const void* kr_blk,
+                              const void* w_uk, const void* w_uv,
+                              const int32_t* anchors, const uint8_t* keep,
+                              void* out, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/* Extra controls for dspark_attn_fwd_ex (zero-initialise, then set fields). */
+typedef struct dspark_attn_opts {
+    /* NULL, or n_stage_events hipEvent_t handles recorded on `stream` at the
+     * stage boundaries: [0] before the index build, [1] after it, [2] after
+     * the q_abs absorb, [3] after the attention kernel, [4] after the W_UV
+     * projection (generic path: [2] and [3] coincide with [1]). */
+    void* const* stage_events;
+    int32_t n_stage_events;   /* 0 or 5 */
+    int32_t force_generic;    /* nonzero: use the generic fp32 kernels even
+                                 where the MFMA path applies */
+} dspark_attn_opts;
+
+/* dspark_attn_fwd with options; opts may be NULL. */
+dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc,
+                                 const void* q_nope, const void* q_rope,
+                                 const void* ckv_ctx, const void* kr_ctx,
+                                 const void* ckv_blk, const void* kr_blk,
+                                 const void* w_uk, const void* w_uv,
+                                 const int32_t* anchors, const uint8_t* keep,
+                                 void* out, void* workspace, size_t ws_bytes,
+                                 void* stream, const dspark_attn_opts* opts);
+
+/* The anchor/window index builder alone (the first stage of the forward).
+ * index_out [B, N, 4] int32 per block: {ctx_lo, ctx_len, pos0, slot}
+ *   kept block with 0 <= A <= S-2: ctx_lo = max(0, A-W+1), ctx_len = A-ctx_lo
+ *     (the visible context columns [ctx_lo, A), §3), pos0 = A (RoPE position
+ *     of the block's first query, §2), slot = rank among kept blocks in
+ *     (b, n) order;
+ *   padding block: {0, 0, 0, -1};  kept block with a bad anchor: {0, 0, 0, -2}.
+ * The block's draft columns are S + 5n .. S + 5n + 4 (§3).  The workspace
+ * must be sized by dspark_attn_workspace_size(desc). */
+dspark_status dspark_build_index(const dspark_attn_desc* desc,
+                                 const int32_t* anchors, const uint8_t* keep,
+                                 int32_t* index_out, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
+/* Host-side anchor sampler (§2 "Anchor sampling"; loss_mask[S-1] is taken as 0,
+ * §6 "eval_mask" / appendix A option 2).  All pointers are HOST pointers.
+ *   loss_mask [S] uint8 (nonzero = 1), anchors [num_anchors] int32 out,
+ *   keep [num_anchors] uint8 out.
+ * Candidates C = {A in [0, S-2] : lm[A] = lm[A+1] = 1}, ascending.  If
+ * |C| <= num_anchors: C then padding slots (A = 0, keep = 0).  Otherwise a
+ * partial Fisher-Yates over C driven by SplitMix64(seed):
+ * for i < N: j = i + next() mod (|C| - i), swap C[i], C[j]; then the first N
+ * sorted ascending, keep = 1.  Integer-only, hence reproducible exactly. */
+dspark_status dspark_select_anchors_host(const uint8_t* loss_mask, int32_t S,
+                                         int32_t num_anchors, uint64_t seed,
+                                         int32_t* anchors, uint8_t* keep);
+
+/* Synchronises `stream`, then reads the status area of a workspace used by
+ * the last dspark_attn_fwd / dspark_build_index on it.  Returns DSPARK_OK, or
+ * DSPARK_EANCHOR with *first_bad_block = b*N + n of the first kept block
+ * whose anchor was outside [0, S-2] (-1 when none).  first_bad_block may be
+ * NULL. */
+dspark_status dspark_read_device_status(const void* workspace, void* stream,
+                                        int32_t* first_bad_block);
+
+/* Thread-local text of the last error on the calling thread ("" if none). */
+const char* dspark_last_error(void);
+
+/* DSPARK_ABI_VERSION of the loaded library. */
+int32_t dspark_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_ATTN_H */

@@ -178,13 +178,15 @@ def row_index_sets(M: np.ndarray, S: int):
     return out
 
 
-def block_index_records(S: int, N: int, W: int, anchors_row, keep_row, block: int = BLOCK):
+def block_index_records(S: int, N: int, W: int, anchors_row, keep_row, block: int = BLOCK,
+                        ns=None):
     """Per block: (ctx_lo, ctx_len, pos0, keep) read off the block's mask rows:
     ctx_lo/ctx_len describe the visible context columns (which §3 makes a
     contiguous run), pos0 is the RoPE position of the block's first query.
-    A padding block reports (0, 0, 0, 0)."""
+    A padding block reports (0, 0, 0, 0).  ns: the blocks to fill (default
+    all); the other rows stay 0."""
     recs = np.zeros((N, 4), dtype=np.int64)
-    for n in range(N):
+    for n in (range(N) if ns is None else ns):
         if not keep_row[n]:
             continue
         rows = mask_rows(S, N, W, anchors_row, keep_row, n, block)

@@ -1,0 +1,28 @@
+"""MI355X (gfx950) DSpark draft-attention forward.
+
+The compute lives in libdspark_attn.so (hand-written HIP kernels behind the C
+ABI of include/dspark_attn.h); this package is its Python binding.  Build the
+library with ``python -m speculative_decoding_draft_amd.build``.
+"""
+from ._lib import (  # noqa: F401
+    DSPARK_BF16,
+    DSPARK_EANCHOR,
+    DSPARK_EHIP,
+    DSPARK_EINVAL,
+    DSPARK_EUNSUPPORTED,
+    DSPARK_EWORKSPACE,
+    DSPARK_F32,
+    DSPARK_OK,
+    EXPORTS,
+    LIB_PATH,
+    Desc,
+    DSparkError,
+    abi_version,
+    attn_fwd,
+    build_index,
+    last_error,
+    make_desc,
+    read_device_status,
+    select_anchors_host,
+    workspace_size,
+)

@@ -1,0 +1,174 @@
+"""ctypes binding of libdspark_attn.so (argument marshalling only).
+
+Every function mirrors an ``extern "C"`` entry point of
+``include/dspark_attn.h``; tensors are torch tensors that live on the GPU
+(torch supplies device memory and the current HIP stream), except where the
+header says "host".  Nothing here computes any part of the forward; if the
+library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdspark_attn.so")
+
+DSPARK_OK = 0
+DSPARK_EINVAL = -1
+DSPARK_EUNSUPPORTED = -2
+DSPARK_EWORKSPACE = -3
+DSPARK_EHIP = -4
+DSPARK_EANCHOR = -5
+STATUS_NAMES = {0: "DSPARK_OK", -1: "DSPARK_EINVAL", -2: "DSPARK_EUNSUPPORTED",
+                -3: "DSPARK_EWORKSPACE", -4: "DSPARK_EHIP", -5: "DSPARK_EANCHOR"}
+DSPARK_F32 = 0
+DSPARK_BF16 = 1
+
+EXPORTS = ("dspark_attn_workspace_size", "dspark_attn_fwd", "dspark_attn_fwd_ex",
+           "dspark_build_index", "dspark_select_anchors_host", "dspark_read_device_status",
+           "dspark_last_error", "dspark_abi_version")
+
+
+class DSparkError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("d_latent", ctypes.c_int32),
+                ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_double),
+                ("dtype", ctypes.c_int32)]
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+                ("n_stage_events", ctypes.c_int32), ("force_generic", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m speculative_decoding_draft_amd.build`")
+    # torch must bring in its HIP runtime (soname libamdhip64.so.7) first, so
+    # that the library binds to that one instance: torch owns the device
+    # memory and streams passed in, and a second runtime in the process would
+    # not see the device.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+    pd = ctypes.POINTER(Desc)
+    lib.dspark_attn_workspace_size.argtypes = [pd]
+    lib.dspark_attn_workspace_size.restype = sz
+    fwd_args = [pd] + [vp] * 8 + [vp, vp, vp, vp, sz, vp]
+    lib.dspark_attn_fwd.argtypes = fwd_args
+    lib.dspark_attn_fwd.restype = i32
+    lib.dspark_attn_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(Opts)]
+    lib.dspark_attn_fwd_ex.restype = i32
+    lib.dspark_build_index.argtypes = [pd, vp, vp, vp, vp, sz, vp]
+    lib.dspark_build_index.restype = i32
+    lib.dspark_select_anchors_host.argtypes = [vp, i32, i32, u64, vp, vp]
+    lib.dspark_select_anchors_host.restype = i32
+    lib.dspark_read_device_status.argtypes = [vp, vp, ctypes.POINTER(i32)]
+    lib.dspark_read_device_status.restype = i32
+    lib.dspark_last_error.argtypes = []
+    lib.dspark_last_error.restype = ctypes.c_char_p
+    lib.dspark_abi_version.argtypes = []
+    lib.dspark_abi_version.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.dspark_last_error().decode()
+
+
+def abi_version() -> int:
+    return int(lib.dspark_abi_version())
+
+
+def _check(status: int) -> None:
+    if status != DSPARK_OK:
+        raise DSparkError(status, last_error())
+
+
+def make_desc(*, B, S, N, window, n_heads, d_latent, d_nope, d_rope, d_v, rope_base=10000.0,
+              softmax_scale=0.0, dtype="bf16", block=5) -> Desc:
+    dt = {"bf16": DSPARK_BF16, "f32": DSPARK_F32}.get(dtype, dtype)
+    return Desc(B, S, N, block, window, n_heads, d_latent, d_nope, d_rope, d_v,
+                float(rope_base), float(softmax_scale), int(dt))
+
+
+def workspace_size(desc: Desc) -> int:
+    n = int(lib.dspark_attn_workspace_size(ctypes.byref(desc)))
+    if n == 0:
+        raise DSparkError(DSPARK_EINVAL, last_error())
+    return n
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def attn_fwd(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
+             anchors, keep, out, workspace, stream=None,
+             stage_events: Optional[Sequence[int]] = None, force_generic: bool = False) -> None:
+    """dspark_attn_fwd / dspark_attn_fwd_ex; raises DSparkError on a non-OK status."""
+    args = [ctypes.byref(desc)] + [_ptr(t) for t in (q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk,
+                                                     kr_blk, w_uk, w_uv, anchors, keep, out,
+                                                     workspace)]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args += [ws_bytes, _stream(stream)]
+    if stage_events is None and not force_generic:
+        _check(lib.dspark_attn_fwd(*args))
+        return
+    opts = Opts()
+    if stage_events is not None:
+        arr = (ctypes.c_void_p * len(stage_events))(*stage_events)
+        opts.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        opts.n_stage_events = len(stage_events)
+    opts.force_generic = 1 if force_generic else 0
+    _check(lib.dspark_attn_fwd_ex(*args, ctypes.byref(opts)))
+
+
+def build_index(desc: Desc, anchors, keep, index_out, workspace, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.dspark_build_index(ctypes.byref(desc), _ptr(anchors), _ptr(keep), _ptr(index_out),
+                                  _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def select_anchors_host(loss_mask: np.ndarray, num_anchors: int, seed: int):
+    """Host sampler; returns (anchors int32 [num_anchors], keep uint8 [num_anchors])."""
+    lm = np.ascontiguousarray(loss_mask, dtype=np.uint8)
+    anchors = np.zeros(num_anchors, dtype=np.int32)
+    keep = np.zeros(num_anchors, dtype=np.uint8)
+    _check(lib.dspark_select_anchors_host(lm.ctypes.data, lm.shape[0], num_anchors,
+                                          ctypes.c_uint64(seed & (2 ** 64 - 1)),
+                                          anchors.ctypes.data, keep.ctypes.data))
+    return anchors, keep
+
+
+def read_device_status(workspace, stream=None):
+    """Synchronises the stream; returns (status, first_bad_block)."""
+    fb = ctypes.c_int32(-1)
+    st = lib.dspark_read_device_status(_ptr(workspace), _stream(stream), ctypes.byref(fb))
+    return int(st), int(fb.value)

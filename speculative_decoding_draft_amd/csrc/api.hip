@@ -1,0 +1,243 @@
+// extern "C" entry points of libdspark_attn.so: argument validation,
+// workspace layout, kernel launches.  See include/dspark_attn.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace dspark {
+namespace {
+
+thread_local std::string g_last_error;
+
+dspark_status fail(dspark_status code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+dspark_status ok() {
+    g_last_error.clear();
+    return DSPARK_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_fast_path(const dspark_attn_desc& d) {
+    return d.dtype == DSPARK_BF16 && d.n_heads == kH && d.d_latent == kD && d.d_nope == kDc &&
+           d.d_rope == kDr && d.d_v == kDv && d.window <= kMaxWindow;
+}
+
+// Validates the descriptor; `empty` is set when there is nothing to compute.
+dspark_status check_desc(const dspark_attn_desc* d, bool* empty) {
+    if (!d) return fail(DSPARK_EINVAL, "desc is NULL");
+    if (d->block != kBlock)
+        return fail(DSPARK_EUNSUPPORTED, "block must be 5 (got %d)", d->block);
+    if (d->B < 0 || d->N < 0) return fail(DSPARK_EINVAL, "B and N must be >= 0");
+    if (d->S < 1) return fail(DSPARK_EINVAL, "S must be >= 1 (got %d)", d->S);
+    if (d->window < 1) return fail(DSPARK_EINVAL, "window must be >= 1 (got %d)", d->window);
+    if (d->n_heads < 1 || d->d_latent < 1 || d->d_nope < 1 || d->d_v < 1 || d->d_rope < 0)
+        return fail(DSPARK_EINVAL, "n_heads, d_latent, d_nope, d_v must be >= 1, d_rope >= 0");
+    if (d->d_rope % 2 != 0) return fail(DSPARK_EINVAL, "d_rope must be even (got %d)", d->d_rope);
+    if (d->d_rope / 2 > kMaxRopePairs)
+        return fail(DSPARK_EUNSUPPORTED, "d_rope must be <= %d", 2 * kMaxRopePairs);
+    if (d->dtype != DSPARK_F32 && d->dtype != DSPARK_BF16)
+        return fail(DSPARK_EINVAL, "dtype must be DSPARK_F32 or DSPARK_BF16 (got %d)", d->dtype);
+    if (!(d->rope_base > 0.0) || !std::isfinite(d->rope_base))
+        return fail(DSPARK_EINVAL, "rope_base must be a finite positive number");
+    if (!std::isfinite(d->softmax_scale))
+        return fail(DSPARK_EINVAL, "softmax_scale must be finite");
+    const long long blocks = (long long)d->B * d->N;
+    if (blocks > (1LL << 26))
+        return fail(DSPARK_EUNSUPPORTED, "B*N = %lld exceeds 2^26 blocks", blocks);
+    if ((long long)d->S + 8 > (1LL << 30)) return fail(DSPARK_EUNSUPPORTED, "S too large");
+    if (d->n_heads > 65535) return fail(DSPARK_EUNSUPPORTED, "n_heads must be <= 65535");
+    *empty = blocks == 0;
+    return DSPARK_OK;
+}
+
+Problem make_problem(const dspark_attn_desc& d) {
+    Problem p;
+    p.B = d.B; p.S = d.S; p.N = d.N; p.W = d.window; p.H = d.n_heads;
+    p.D = d.d_latent; p.dc = d.d_nope; p.dr = d.d_rope; p.dv = d.d_v;
+    p.L5 = kBlock * d.N;
+    p.rows_max = kBlock * d.B * d.N;
+    p.scale = (float)(d.softmax_scale > 0.0 ? d.softmax_scale
+                                            : 1.0 / std::sqrt((double)(d.d_nope + d.d_rope)));
+    return p;
+}
+
+Workspace carve(void* base, const WsLayout& L) {
+    char* c = static_cast<char*>(base);
+    Workspace w;
+    w.idx = reinterpret_cast<int4*>(c + L.idx);
+    w.kept = reinterpret_cast<int32_t*>(c + L.kept);
+    w.status = reinterpret_cast<int32_t*>(c + L.status);
+    w.rope = reinterpret_cast<float2*>(c + L.rope);
+    w.qabs = L.qabs ? reinterpret_cast<bf16*>(c + L.qabs) : nullptr;
+    w.olat = L.olat ? reinterpret_cast<bf16*>(c + L.olat) : nullptr;
+    return w;
+}
+
+dspark_status check_workspace(const void* ws, size_t ws_bytes, size_t need) {
+    if (!ws) return fail(DSPARK_EWORKSPACE, "workspace is NULL");
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return fail(DSPARK_EWORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(DSPARK_EWORKSPACE, "workspace too small: %zu bytes given, %zu needed",
+                    ws_bytes, need);
+    return DSPARK_OK;
+}
+
+dspark_status hip_fail(hipError_t e, const char* what) {
+    return fail(DSPARK_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+RopeTheta make_theta(const dspark_attn_desc& d) {
+    RopeTheta th;
+    std::memset(&th, 0, sizeof(th));
+    for (int i = 0; i < d.d_rope / 2; ++i)
+        th.t[i] = std::pow(d.rope_base, -2.0 * i / (double)d.d_rope);
+    return th;
+}
+
+}  // namespace
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" {
+
+int32_t dspark_abi_version(void) { return DSPARK_ABI_VERSION; }
+
+const char* dspark_last_error(void) { return g_last_error.c_str(); }
+
+size_t dspark_attn_workspace_size(const dspark_attn_desc* desc) {
+    bool empty = false;
+    if (check_desc(desc, &empty) != DSPARK_OK) return 0;
+    g_last_error.clear();
+    return ws_layout(*desc, is_fast_path(*desc)).total;
+}
+
+dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nope,
+                                 const void* q_rope, const void* ckv_ctx, const void* kr_ctx,
+                                 const void* ckv_blk, const void* kr_blk, const void* w_uk,
+                                 const void* w_uv, const int32_t* anchors, const uint8_t* keep,
+                                 void* out, void* workspace, size_t ws_bytes, void* stream,
+                                 const dspark_attn_opts* opts) {
+    bool empty = false;
+    dspark_status st = check_desc(desc, &empty);
+    if (st != DSPARK_OK) return st;
+    if (empty) return ok();
+    const dspark_attn_desc& d = *desc;
+    const void* ptrs[] = {q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
+                          anchors, keep, out};
+    const char* names[] = {"q_nope", "q_rope", "ckv_ctx", "kr_ctx", "ckv_blk", "kr_blk",
+                           "w_uk", "w_uv", "anchors", "keep", "out"};
+    for (int i = 0; i < 11; ++i) {
+        const bool may_be_null = (i == 1 || i == 3 || i == 5) && d.d_rope == 0;
+        if (!ptrs[i] && !may_be_null) return fail(DSPARK_EINVAL, "%s is NULL", names[i]);
+        if (ptrs[i] && i != 9 && !aligned16(ptrs[i]))
+            return fail(DSPARK_EINVAL, "%s must be 16-byte aligned", names[i]);
+    }
+    if (opts && opts->stage_events && opts->n_stage_events != 5)
+        return fail(DSPARK_EINVAL, "n_stage_events must be 5 when stage_events is given");
+    const bool fast = is_fast_path(d) && !(opts && opts->force_generic);
+    const WsLayout L = ws_layout(d, fast);
+    st = check_workspace(workspace, ws_bytes, L.total);
+    if (st != DSPARK_OK) return st;
+
+    const Problem p = make_problem(d);
+    if (!fast) {
+        if (generic_lds_bytes(p) > 64 * 1024)
+            return fail(DSPARK_EUNSUPPORTED,
+                        "shape needs %zu bytes of LDS in the generic kernel (max 65536)",
+                        generic_lds_bytes(p));
+    }
+    const Workspace ws = carve(workspace, L);
+    const Inputs in{q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv, out};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* const* ev = (opts && opts->stage_events) ? opts->stage_events : nullptr;
+    auto mark = [&](int k) -> hipError_t {
+        return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[k]), s) : hipSuccess;
+    };
+
+    hipError_t e;
+    if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = launch_index(p, anchors, keep, ws, nullptr, s)) != hipSuccess)
+        return hip_fail(e, "index kernel launch");
+    if ((e = launch_rope_table(p, L.rope_rows, make_theta(d), ws, s)) != hipSuccess)
+        return hip_fail(e, "rope table launch");
+    if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if (fast) {
+        if ((e = launch_absorb(p, in, ws, s)) != hipSuccess) return hip_fail(e, "absorb launch");
+        if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if ((e = launch_attn(p, in, ws, s)) != hipSuccess) return hip_fail(e, "attention launch");
+        if ((e = mark(3)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if ((e = launch_uv(p, in, ws, s)) != hipSuccess) return hip_fail(e, "W_UV launch");
+    } else {
+        if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if ((e = mark(3)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if ((e = launch_generic(p, d.dtype == DSPARK_BF16, in, ws, s)) != hipSuccess)
+            return hip_fail(e, "generic kernel launch");
+    }
+    if ((e = mark(4)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    return ok();
+}
+
+dspark_status dspark_attn_fwd(const dspark_attn_desc* desc, const void* q_nope,
+                              const void* q_rope, const void* ckv_ctx, const void* kr_ctx,
+                              const void* ckv_blk, const void* kr_blk, const void* w_uk,
+                              const void* w_uv, const int32_t* anchors, const uint8_t* keep,
+                              void* out, void* workspace, size_t ws_bytes, void* stream) {
+    return dspark_attn_fwd_ex(desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
+                              anchors, keep, out, workspace, ws_bytes, stream, nullptr);
+}
+
+dspark_status dspark_build_index(const dspark_attn_desc* desc, const int32_t* anchors,
+                                 const uint8_t* keep, int32_t* index_out, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+    bool empty = false;
+    dspark_status st = check_desc(desc, &empty);
+    if (st != DSPARK_OK) return st;
+    if (empty) return ok();
+    if (!anchors || !keep || !index_out)
+        return fail(DSPARK_EINVAL, "anchors, keep and index_out must be non-NULL");
+    if (!aligned16(anchors) || !aligned16(index_out))
+        return fail(DSPARK_EINVAL, "anchors and index_out must be 16-byte aligned");
+    const WsLayout L = ws_layout(*desc, is_fast_path(*desc));
+    // the index build touches only the status, index and kept-list areas
+    st = check_workspace(workspace, ws_bytes, L.rope);
+    if (st != DSPARK_OK) return st;
+    const Problem p = make_problem(*desc);
+    const Workspace ws = carve(workspace, L);
+    hipError_t e = launch_index(p, anchors, keep, ws, index_out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "index kernel launch");
+    return ok();
+}
+
+dspark_status dspark_read_device_status(const void* workspace, void* stream,
+                                        int32_t* first_bad_block) {
+    if (first_bad_block) *first_bad_block = -1;
+    if (!workspace) return fail(DSPARK_EWORKSPACE, "workspace is NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    int32_t words[kStWords];
+    e = hipMemcpy(words, workspace, sizeof(words), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy of the status area");
+    if (first_bad_block) *first_bad_block = words[kStFirstBad];
+    if (words[kStFirstBad] >= 0)
+        return fail(DSPARK_EANCHOR, "kept block %d has an anchor outside [0, S-2]",
+                    words[kStFirstBad]);
+    return ok();
+}
+
+}  // extern "C"

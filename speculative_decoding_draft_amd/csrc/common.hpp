@@ -1,0 +1,111 @@
+// Internal definitions shared by the host API and the gfx950 kernels of
+// libdspark_attn.so.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dspark_attn.h"
+
+namespace dspark {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 5;          // draft block length (design page, §2)
+constexpr int kMaxRopePairs = 128; // d_rope <= 256
+
+// GLM-5.2 DSpark draft attention dims served by the MFMA kernels.
+constexpr int kH = 64, kD = 512, kDc = 192, kDr = 64, kDv = 256;
+constexpr int kMaxWindow = 128;    // W <= 128: at most 127 context + 5 block keys
+constexpr int kMaxKeys = kMaxWindow - 1 + kBlock;   // 132
+
+// Status area of the workspace (int32 words).
+enum StatusWord { kStKeptCount = 0, kStFirstBad = 1, kStWords = 16 };
+
+// RoPE angles theta_i = base^(-2i/d_r), computed on the host in fp64.
+struct RopeTheta {
+    double t[kMaxRopePairs];
+};
+
+// The status area is always at offset 0 so that it can be found from the
+// workspace pointer alone.
+struct WsLayout {
+    size_t status = 0;   // int32 [kStWords]
+    size_t idx = 0;      // int4 [B*N]       {ctx_lo, ctx_len, pos0, slot}
+    size_t kept = 0;     // int32 [B*N]      slot -> b*N + n
+    size_t rope = 0;     // float2 [S + 8][d_r/2]  (cos, sin)
+    size_t qabs = 0;     // bf16 [H][5*B*N][D]  (MFMA path)
+    size_t olat = 0;     // bf16 [H][5*B*N][D]  (MFMA path)
+    size_t total = 0;
+    int rope_rows = 0;   // S + 8
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline WsLayout ws_layout(const dspark_attn_desc& d, bool mfma) {
+    WsLayout w;
+    const size_t blocks = size_t(d.B) * size_t(d.N);
+    size_t off = 0;
+    w.status = off; off = align256(off + kStWords * 4);
+    w.idx = off;    off = align256(off + blocks * 16);
+    w.kept = off;   off = align256(off + blocks * 4);
+    w.rope_rows = d.S + 8;
+    w.rope = off;   off = align256(off + size_t(w.rope_rows) * size_t(d.d_rope / 2) * 8);
+    if (mfma) {
+        const size_t lat = size_t(d.n_heads) * kBlock * blocks * size_t(d.d_latent) * 2;
+        w.qabs = off; off = align256(off + lat);
+        w.olat = off; off = align256(off + lat);
+    }
+    w.total = off;
+    return w;
+}
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Give each
+// XCD a contiguous range of logical ids so that neighbouring work items (for
+// example blocks with overlapping windows) share that XCD's L2.
+__device__ inline int xcd_remap(int id, int grid) {
+    if (grid % 8 != 0) return id;
+    return (id % 8) * (grid / 8) + id / 8;
+}
+
+__device__ inline bf16x8 ld16(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ inline void st16(bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
+__device__ inline bf16x4 ld8(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+__device__ inline void st8(bf16* p, bf16x4 v) { *reinterpret_cast<bf16x4*>(p) = v; }
+
+__device__ inline bf16x8 cat(bf16x4 lo, bf16x4 hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// D(16x16, f32) += A(16x32) * B(32x16), bf16 operands.  Lane l supplies row
+// l%16 of A and column l%16 of B, each with 8 k-values (k-group l/16); lane l
+// receives D[4*(l/16) + i][l%16], i = 0..3.
+__device__ inline f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Same with K = 16: 4 k-values per lane (k-group l/16).
+__device__ inline f32x4 mfma_16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a),
+                                                     __builtin_bit_cast(short4v, b), c, 0, 0, 0);
+}
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane r*4 + c points at 4 consecutive 16-bit elements of "row" r
+// (r = 0..3); lane j of the group receives element j%4 of the chunk held by
+// lane (row e)*4 + j/4, for e = 0..3, i.e. column j of the 4 x 16 tile.
+__device__ inline bf16x4 lds_read_tr(const bf16* p) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+}  // namespace dspark

@@ -1,0 +1,48 @@
+// Launch wrappers of the gfx950 kernels (internal to libdspark_attn.so).
+#pragma once
+
+#include "common.hpp"
+
+namespace dspark {
+
+// Per-call problem constants handed to every kernel.
+struct Problem {
+    int B, S, N, W, H, D, dc, dr, dv;
+    int L5;          // 5 * N queries per sample
+    int rows_max;    // 5 * B * N kept-row capacity of the latent buffers
+    float scale;     // softmax scale
+};
+
+struct Inputs {
+    const void* q_nope;
+    const void* q_rope;
+    const void* ckv_ctx;
+    const void* kr_ctx;
+    const void* ckv_blk;
+    const void* kr_blk;
+    const void* w_uk;
+    const void* w_uv;
+    void* out;
+};
+
+struct Workspace {
+    int4* idx;
+    int32_t* kept;
+    int32_t* status;
+    float2* rope;
+    bf16* qabs;
+    bf16* olat;
+};
+
+hipError_t launch_index(const Problem& p, const int32_t* anchors, const uint8_t* keep,
+                        const Workspace& ws, int32_t* index_copy, hipStream_t s);
+hipError_t launch_rope_table(const Problem& p, int rope_rows, const RopeTheta& th,
+                             const Workspace& ws, hipStream_t s);
+hipError_t launch_generic(const Problem& p, bool bf16_io, const Inputs& in,
+                          const Workspace& ws, hipStream_t s);
+size_t generic_lds_bytes(const Problem& p);
+hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws, hipStream_t s);
+hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, hipStream_t s);
+hipError_t launch_uv(const Problem& p, const Inputs& in, const Workspace& ws, hipStream_t s);
+
+}  // namespace dspark

@@ -1,0 +1,122 @@
+"""Helpers for the GPU tests: run the HIP path through the C ABI and compare
+with the oracle.  The oracle values are computed here on the host from the
+same seeded inputs; nothing flows from the GPU into the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle as O
+import workloads as wk
+from workloads.device import upload_anchors, upload_layer
+
+BF16_MAX_ABS = 2e-2     # tolerance fixed for bf16 inputs with fp32 accumulation
+BF16_REL_L2 = 5e-3
+# fp32 path: each output is a chain of fp32 dot products over <= 512 terms,
+# a softmax and fp32 RoPE from an fp64-reduced angle; errors stay ~1e-6
+# relative, so 1e-4 absolute / 2e-5 relative leave a wide margin.
+F32_MAX_ABS = 1e-4
+F32_REL_L2 = 2e-5
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def anchors_for(wl):
+    """(GPU anchors, GPU keep, oracle anchors, oracle keep).  For sampler
+    workloads each side runs its own sampler on the same mask and seed."""
+    import speculative_decoding_draft_amd as sd
+    if wl.anchor_source == "given":
+        return wl.anchors, wl.keep, wl.anchors, wl.keep
+    ga = np.zeros((wl.B, wl.N), np.int32)
+    gk = np.zeros((wl.B, wl.N), np.uint8)
+    oa = np.zeros((wl.B, wl.N), np.int32)
+    ok = np.zeros((wl.B, wl.N), np.uint8)
+    for b in range(wl.B):
+        ga[b], gk[b] = sd.select_anchors_host(wl.loss_mask[b], wl.N, wl.sampler_seed + b)
+        oa[b], ok[b] = O.select_anchors(wl.loss_mask[b], wl.N, wl.sampler_seed + b)
+    return ga, gk, oa, ok
+
+
+def desc_for(wl, softmax_scale=0.0):
+    import speculative_decoding_draft_amd as sd
+    return sd.make_desc(B=wl.B, S=wl.S, N=wl.N, window=wl.W, n_heads=wl.H, d_latent=wl.D,
+                        d_nope=wl.d_c, d_rope=wl.d_r, d_v=wl.d_v, rope_base=wl.rope_base,
+                        softmax_scale=softmax_scale, dtype=wl.dtype)
+
+
+class GpuRun:
+    """Uploads one layer, owns out + workspace, runs the forward."""
+
+    def __init__(self, wl, layer_idx=0, anchors=None, keep=None, guard=0, softmax_scale=0.0,
+                 force_generic=False):
+        import torch
+        import speculative_decoding_draft_amd as sd
+        self.wl, self.sd, self.torch = wl, sd, torch
+        self.desc = desc_for(wl, softmax_scale)
+        self.t = upload_layer(wl, layer_idx)
+        self.anchors, self.keep = upload_anchors(anchors, keep)
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        n_out = wl.B * wl.q_len * wl.H * wl.d_v
+        self.guard = guard
+        # guard regions around `out` hold NaN canaries
+        self.out_full = torch.full((n_out + 2 * guard,), float("nan"), dtype=tdt, device="cuda")
+        self.out = self.out_full[guard:guard + n_out].view(wl.B, wl.q_len, wl.H, wl.d_v)
+        ws = sd.workspace_size(self.desc)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
+        self.force_generic = force_generic
+
+    def run(self, stream=None):
+        t = self.t
+        self.sd.attn_fwd(self.desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"],
+                         t["ckv_blk"], t["kr_blk"], t["w_uk"], t["w_uv"], self.anchors, self.keep,
+                         self.out, self.ws, stream=stream, force_generic=self.force_generic)
+        return self
+
+    def result(self) -> np.ndarray:
+        self.torch.cuda.synchronize()
+        return self.out.float().cpu().numpy().astype(np.float64)
+
+    def guards_intact(self) -> bool:
+        if self.guard == 0:
+            return True
+        g = self.guard
+        head = self.out_full[:g].float().cpu().numpy()
+        tail = self.out_full[-g:].float().cpu().numpy()
+        return bool(np.all(np.isnan(head)) and np.all(np.isnan(tail)))
+
+
+def compare(gpu: np.ndarray, ref: np.ndarray, keep: np.ndarray, max_abs: float, rel_l2: float,
+            what: str = "") -> dict:
+    """Rows of padding blocks must be exactly 0 on the GPU and are excluded;
+    rows the reference did not compute (NaN) are skipped; the rest must match
+    within max_abs and rel-L2."""
+    B, L5 = gpu.shape[:2]
+    kept_rows = np.repeat(keep.astype(bool), 5, axis=1)           # [B, 5N]
+    pad = gpu[~kept_rows]
+    assert np.all(pad == 0), f"{what}: padding rows are not zero"
+    checked = kept_rows[:, :, None, None] & np.isfinite(ref)
+    assert checked.any(), f"{what}: nothing compared"
+    g, r = gpu[checked], ref[checked]
+    assert np.all(np.isfinite(g)), f"{what}: non-finite GPU output in kept rows"
+    err = np.abs(g - r)
+    stats = dict(max_abs=float(err.max()), rel_l2=float(np.linalg.norm(g - r) / np.linalg.norm(r)),
+                 n=int(g.size))
+    log(f"  {what}: max_abs={stats['max_abs']:.3e} rel_l2={stats['rel_l2']:.3e} n={stats['n']}")
+    assert stats["max_abs"] <= max_abs, f"{what}: max_abs {stats['max_abs']} > {max_abs}"
+    assert stats["rel_l2"] <= rel_l2, f"{what}: rel_l2 {stats['rel_l2']} > {rel_l2}"
+    return stats
+
+
+def sample_blocks(keep_row: np.ndarray, anchors_row: np.ndarray, W: int, n_random: int, seed: int):
+    """Kept blocks to check at full size: every clamped-window block
+    (A < W-1) plus n_random others."""
+    kept = np.nonzero(keep_row)[0]
+    clamped = [int(n) for n in kept if anchors_row[n] < W - 1]
+    rest = [int(n) for n in kept if anchors_row[n] >= W - 1]
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(rest, size=min(n_random, len(rest)), replace=False).tolist() if rest else []
+    return sorted(set(clamped + pick + ([rest[0], rest[-1]] if rest else [])))

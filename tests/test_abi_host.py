@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point the header declares, validates its arguments before any
+device work, and its host anchor sampler matches the oracle bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as wk
+from conftest import ROOT
+
+sd = pytest.importorskip("speculative_decoding_draft_amd")
+
+
+def header_functions():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(dspark_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    declared = header_functions()
+    assert {"dspark_attn_fwd", "dspark_attn_workspace_size", "dspark_build_index",
+            "dspark_select_anchors_host", "dspark_read_device_status", "dspark_last_error",
+            "dspark_abi_version", "dspark_attn_fwd_ex"} <= declared
+    lib = ctypes.CDLL(sd.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+    assert set(sd.EXPORTS) == declared
+    assert sd.abi_version() == 1
+
+
+def glm_desc(**kw):
+    d = dict(B=1, S=2048, N=64, window=128, n_heads=64, d_latent=512, d_nope=192, d_rope=64,
+             d_v=256, dtype="bf16")
+    d.update(kw)
+    return sd.make_desc(**d)
+
+
+def test_workspace_size_accounts_for_latent_buffers():
+    d = glm_desc()
+    n = sd.workspace_size(d)
+    lat = 64 * 5 * 64 * 512 * 2
+    assert n >= 2 * lat and n < 2 * lat + 4 * 2**20
+    # a non-GLM shape takes the generic kernels: no latent buffers
+    small = sd.workspace_size(glm_desc(n_heads=2, d_latent=32, d_nope=16, d_rope=8, d_v=16))
+    assert small < 2**20
+    # W > 128 also leaves the MFMA path
+    assert sd.workspace_size(glm_desc(window=256)) < n
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("block", 4, sd.DSPARK_EUNSUPPORTED), ("window", 0, sd.DSPARK_EINVAL),
+    ("S", 0, sd.DSPARK_EINVAL), ("d_rope", 7, sd.DSPARK_EINVAL),
+    ("dtype", 9, sd.DSPARK_EINVAL), ("rope_base", -1.0, sd.DSPARK_EINVAL),
+    ("n_heads", 0, sd.DSPARK_EINVAL), ("B", -1, sd.DSPARK_EINVAL)])
+def test_bad_descriptor_is_rejected(field, value, status):
+    d = glm_desc()
+    setattr(d, field, value)
+    assert sd._lib.lib.dspark_attn_workspace_size(ctypes.byref(d)) == 0
+    st = sd._lib.lib.dspark_attn_fwd(ctypes.byref(d), *([None] * 12), 0, None)
+    assert st == status
+    assert sd.last_error() != ""
+
+
+class FakePtr:
+    """Stands in for a device tensor when only host-side validation runs."""
+
+    def __init__(self, addr, nbytes=0):
+        self.addr, self.nbytes = addr, nbytes
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
+
+
+def _call(d, ptrs, ws, ws_bytes):
+    lib = sd._lib.lib
+    return lib.dspark_attn_fwd(ctypes.byref(d), *ptrs, ws, ws_bytes, None)
+
+
+def test_null_misaligned_and_workspace_errors_before_any_launch():
+    d = glm_desc()
+    good = [0x10000 * (i + 1) for i in range(11)]
+    need = sd.workspace_size(d)
+    ws = 0x7000000
+    for i in range(11):
+        p = list(good)
+        p[i] = None
+        assert _call(d, p, ws, need) == sd.DSPARK_EINVAL
+        assert "NULL" in sd.last_error()
+    p = list(good)
+    p[0] += 4
+    assert _call(d, p, ws, need) == sd.DSPARK_EINVAL
+    assert "aligned" in sd.last_error()
+    assert _call(d, good, ws, need - 1) == sd.DSPARK_EWORKSPACE
+    assert "too small" in sd.last_error()
+    assert _call(d, good, ws + 64, need) == sd.DSPARK_EWORKSPACE
+    assert _call(d, good, None, need) == sd.DSPARK_EWORKSPACE
+
+
+def test_empty_problem_is_a_no_op():
+    d = glm_desc(N=0)
+    assert sd._lib.lib.dspark_attn_fwd(ctypes.byref(d), *([None] * 12), 0, None) == sd.DSPARK_OK
+
+
+def test_generic_lds_limit_is_reported():
+    d = glm_desc(dtype="f32", window=4000, d_latent=2048)
+    need = sd.workspace_size(d)
+    p = [0x10000 * (i + 1) for i in range(11)]
+    assert _call(d, p, 0x7000000, need) == sd.DSPARK_EUNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# host sampler vs the oracle sampler (bit-exact)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S,N,p", [(48, 4, 0.9), (200, 10, 0.9), (64, 40, 0.5), (30, 30, 0.3),
+                                   (2, 1, 1.0), (1, 3, 1.0), (5000, 512, 0.9)])
+def test_sampler_matches_oracle(S, N, p):
+    rng = np.random.default_rng(S * 31 + N)
+    for trial in range(20):
+        lm = (rng.random(S) < p).astype(np.uint8)
+        seed = int(rng.integers(0, 2**63))
+        a_c, k_c = sd.select_anchors_host(lm, N, seed)
+        a_o, k_o = O.select_anchors(lm, N, seed)
+        assert np.array_equal(a_c, a_o) and np.array_equal(k_c, k_o), (S, N, trial)
+
+
+@pytest.mark.parametrize("k", [2, 5])
+def test_sampler_matches_oracle_on_benchmark_masks(k):
+    wl = wk.config(k, tensors=False)
+    for b in range(wl.B):
+        a_c, k_c = sd.select_anchors_host(wl.loss_mask[b], wl.N, wl.sampler_seed + b)
+        a_o, k_o = O.select_anchors(wl.loss_mask[b], wl.N, wl.sampler_seed + b)
+        assert np.array_equal(a_c, a_o) and np.array_equal(k_c, k_o)
+        assert k_c.all()

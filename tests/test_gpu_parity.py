@@ -1,0 +1,234 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Index records must match bit for bit; outputs within the
+stated tolerances; padding rows must be exactly zero."""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as wk
+from gpu_util import (BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS, F32_REL_L2, GpuRun, anchors_for,
+                      compare, desc_for, log, sample_blocks)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sd():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import speculative_decoding_draft_amd as sd
+    return sd
+
+
+def check_full(wl, form="dense", layer=0, force_generic=False, tol=None, guard=0):
+    ga, gk, oa, ok = anchors_for(wl)
+    assert np.array_equal(ga, oa) and np.array_equal(gk, ok), "anchor selection differs"
+    run = GpuRun(wl, layer, ga, gk, guard=guard, force_generic=force_generic).run()
+    gpu = run.result()
+    ref = O.forward(wl, layer, oa, ok, form=form)
+    if tol is None:
+        tol = (F32_MAX_ABS, F32_REL_L2) if wl.dtype == "f32" else (BF16_MAX_ABS, BF16_REL_L2)
+    stats = compare(gpu, ref, ok, *tol, what=wl.name)
+    assert run.guards_intact(), "write outside `out`"
+    return run, gpu, stats
+
+
+# ---------------------------------------------------------------------------
+# index builder: bit-exact against the oracle's mask
+# ---------------------------------------------------------------------------
+
+def gpu_index(sd, wl, anchors, keep):
+    import torch
+    desc = desc_for(wl)
+    ws = torch.empty(sd.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    a = torch.from_numpy(np.ascontiguousarray(anchors, np.int32)).cuda()
+    k = torch.from_numpy(np.ascontiguousarray(keep, np.uint8)).cuda()
+    out = torch.full((wl.B, wl.N, 4), -7, dtype=torch.int32, device="cuda")
+    sd.build_index(desc, a, k, out, ws)
+    st, first_bad = sd.read_device_status(ws)
+    return out.cpu().numpy(), st, first_bad
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_index_records_bit_exact(sd, k):
+    wl = wk.config(k, tensors=False)
+    ga, gk, oa, ok = anchors_for(wl)
+    assert np.array_equal(ga, oa) and np.array_equal(gk, ok)
+    rec, st, first_bad = gpu_index(sd, wl, ga, gk)
+    assert st == sd.DSPARK_OK and first_bad == -1
+    # slots are the ranks of the kept blocks in (b, n) order
+    rank = np.cumsum(ok.ravel().astype(np.int64)) - 1
+    assert np.array_equal(rec[..., 3].ravel(), np.where(ok.ravel() == 1, rank, -1))
+    rng = np.random.default_rng(k)
+    for b in range(wl.B):
+        # every block for the smaller configs, 600 of the 4096 for the largest
+        ns = range(wl.N) if wl.N <= 1024 else sorted(
+            set(rng.choice(wl.N, 600, replace=False).tolist()) | {0, wl.N - 1})
+        want = O.block_index_records(wl.S, wl.N, wl.W, oa[b], ok[b], ns=ns)
+        for n in ns:
+            if ok[b, n]:
+                assert rec[b, n, :3].tolist() == want[n, :3].tolist(), (b, n)
+            else:
+                assert rec[b, n].tolist() == [0, 0, 0, -1], (b, n)
+    log(f"  cfg{k}: {int(ok.sum())} kept blocks, records identical")
+
+
+def test_index_sets_equal_mask_rows(sd):
+    """Column sets implied by the GPU records equal the nonzeros of the
+    oracle's materialised mask, row by row (headline recipe, small S)."""
+    wl = wk.make_workload("idx", B=2, S=700, N=64, dims=wk.GLM_DIMS, dtype="bf16",
+                          recipe="headline", seed=5, tensors=False)
+    rec, st, _ = gpu_index(sd, wl, wl.anchors, wl.keep)
+    assert st == sd.DSPARK_OK
+    for b in range(wl.B):
+        M = O.build_mask(wl.S, wl.N, wl.W, wl.anchors[b], wl.keep[b])
+        sets = O.row_index_sets(M, wl.S)
+        for n in range(wl.N):
+            lo, ln, pos0, slot = rec[b, n]
+            for j in range(5):
+                ctx, drf = sets[5 * n + j]
+                if slot < 0:
+                    assert len(ctx) == 0 and len(drf) == 0
+                    continue
+                assert ctx.tolist() == list(range(lo, lo + ln))
+                assert drf.tolist() == [wl.S + 5 * n + i for i in range(5)]
+                assert pos0 == wl.anchors[b, n]
+
+
+def test_bad_kept_anchor_is_reported(sd):
+    wl = wk.make_workload("bad", B=1, S=300, N=8, dims=wk.GLM_DIMS, dtype="bf16",
+                          recipe="uniform", seed=3, tensors=False)
+    a, k = wl.anchors.copy(), wl.keep.copy()
+    a[0, 5] = wl.S - 1          # one past the last valid anchor
+    a[0, 6] = -3
+    rec, st, first_bad = gpu_index(sd, wl, a, k)
+    assert st == sd.DSPARK_EANCHOR and first_bad == 5
+    assert rec[0, 5].tolist() == [0, 0, 0, -2] and rec[0, 6].tolist() == [0, 0, 0, -2]
+    assert rec[0, 7, 3] == 5    # later kept blocks keep consecutive slots
+
+
+# ---------------------------------------------------------------------------
+# forward parity
+# ---------------------------------------------------------------------------
+
+def test_cfg1_tiny_fp32(sd):
+    log("cfg1 tiny fp32 (generic kernel)")
+    check_full(wk.config(1), guard=64)
+
+
+def test_cfg2_glm_layer(sd):
+    log("cfg2 GLM layer B1 S2048 N64 (MFMA, head-split launch)")
+    check_full(wk.config(2), guard=4096)
+
+
+def test_cfg2_generic_kernel_bf16(sd):
+    log("cfg2 through the generic kernel")
+    check_full(wk.config(2), force_generic=True)
+
+
+def test_cfg3_recipe_small(sd):
+    log("cfg3 recipe B2 S1024 N64")
+    check_full(wk.scaled(3, S=1024, N=64), form="gathered")
+
+
+def test_cfg4_recipe_small(sd):
+    log("cfg4 recipe B1 S4096 N128 (padding + clamped windows)")
+    check_full(wk.scaled(4, S=4096, N=128), form="gathered", guard=4096)
+
+
+def test_cfg4_recipe_four_wave_launch(sd):
+    log("cfg4 recipe B1 S4096 N600 (one workgroup per block)")
+    check_full(wk.scaled(4, S=4096, N=600), form="gathered")
+
+
+@pytest.mark.parametrize("W", [1, 2, 16, 127, 128])
+def test_window_sizes_on_mfma_path(sd, W):
+    dims = dict(wk.GLM_DIMS, W=W)
+    wl = wk.make_workload(f"W{W}", B=1, S=400, N=40, dims=dims, dtype="bf16", recipe="headline",
+                          seed=40 + W, recipe_args=dict(low_frac=0.1) if W > 3 else
+                          dict(low_frac=0.0))
+    log(f"window {W}")
+    check_full(wl, form="gathered")
+
+
+def test_all_padding_and_anchor_zero(sd):
+    wl = wk.make_workload("edge", B=2, S=256, N=6, dims=wk.GLM_DIMS, dtype="bf16",
+                          recipe="uniform", seed=77)
+    wl.keep[0, :] = 0                      # sample 0: all padding, garbage anchors
+    wl.anchors[0, :] = np.array([-5, 10**6, 0, 255, -1, 3])
+    wl.anchors[1, :] = np.array([0, 1, 2, 3, 100, 200])   # A = 0: block keys only
+    for a in wl.anchors[1]:
+        wl.loss_mask[1, a] = wl.loss_mask[1, a + 1] = 1
+    check_full(wl, form="gathered")
+
+
+def test_bad_anchor_rows_are_nan_and_reported(sd):
+    wl = wk.make_workload("badfwd", B=1, S=512, N=20, dims=wk.GLM_DIMS, dtype="bf16",
+                          recipe="uniform", seed=9)
+    a, k = wl.anchors.copy(), wl.keep.copy()
+    a[0, 7] = 511            # S - 1: invalid
+    run = GpuRun(wl, 0, a, k).run()
+    st, fb = sd.read_device_status(run.ws)
+    assert st == sd.DSPARK_EANCHOR and fb == 7
+    gpu = run.result()
+    assert np.all(np.isnan(gpu[0, 35:40]))
+    ok = k.copy()
+    ok[0, 7] = 0
+    ref = O.forward(wl, 0, a, ok, form="gathered")
+    gpu[0, 35:40] = 0.0      # excluded from the comparison as a non-kept block
+    compare(gpu, ref, ok, BF16_MAX_ABS, BF16_REL_L2, what="other blocks")
+
+
+def test_explicit_softmax_scale(sd):
+    wl = wk.scaled(4, S=1024, N=32)
+    run = GpuRun(wl, 0, wl.anchors, wl.keep, softmax_scale=0.03).run()
+    ref = O.forward(wl, 0, form="gathered", scale=0.03)
+    compare(run.result(), ref, wl.keep, BF16_MAX_ABS, BF16_REL_L2, what="scale 0.03")
+
+
+def test_deterministic(sd):
+    wl = wk.scaled(4, S=2048, N=96)
+    r = GpuRun(wl, 0, wl.anchors, wl.keep)
+    a = r.run().result()
+    b = r.run().result()
+    assert np.array_equal(np.nan_to_num(a, nan=7.0), np.nan_to_num(b, nan=7.0))
+
+
+# ---------------------------------------------------------------------------
+# full benchmark sizes: sampled blocks
+# ---------------------------------------------------------------------------
+
+def check_sampled(wl, layer, ga, gk, oa, ok, n_random, seed):
+    run = GpuRun(wl, layer, ga, gk).run()
+    gpu = run.result()
+    st, fb = run.sd.read_device_status(run.ws)
+    assert st == 0 and fb == -1
+    pick = []
+    for b in range(wl.B):
+        pick += [(b, n) for n in sample_blocks(ok[b], oa[b], wl.W, n_random, seed + b)]
+    ref = O.forward(wl, layer, oa, ok, form="gathered", blocks=pick)
+    compare(gpu, ref, ok, BF16_MAX_ABS, BF16_REL_L2, what=f"{wl.name} layer {layer} "
+            f"({len(pick)} sampled blocks)")
+
+
+def test_cfg3_full_size_sampled(sd):
+    wl = wk.config(3)
+    log("cfg3 full size")
+    ga, gk, oa, ok = anchors_for(wl)
+    check_sampled(wl, 0, ga, gk, oa, ok, n_random=24, seed=3)
+
+
+def test_cfg4_full_size_sampled(sd):
+    wl = wk.config(4)
+    log("cfg4 full size")
+    ga, gk, oa, ok = anchors_for(wl)
+    check_sampled(wl, 0, ga, gk, oa, ok, n_random=40, seed=4)
+
+
+def test_cfg5_full_size_sampled(sd):
+    wl = wk.config(5)
+    log("cfg5 full size, 3 layers with shared anchors")
+    ga, gk, oa, ok = anchors_for(wl)
+    assert np.array_equal(ga, oa) and np.array_equal(gk, ok)
+    for layer in range(3):
+        check_sampled(wl, layer, ga, gk, oa, ok, n_random=12, seed=50 + layer)

@@ -193,7 +193,7 @@ def _recipe_headline(rng, S, N, W, pad_frac=0.25, low_frac=0.05):
 
 def make_workload(name: str, *, B: int, S: int, N: int, dims: dict, dtype: str,
                   recipe: str, seed: int, layers: int = 1, rope_base: float = 10000.0,
-                  recipe_args: Optional[dict] = None) -> Workload:
+                  recipe_args: Optional[dict] = None, tensors: bool = True) -> Workload:
     recipe_args = recipe_args or {}
     H, D, d_c, d_r, d_v, W = (dims[k] for k in ("H", "D", "d_c", "d_r", "d_v", "W"))
     ss = np.random.SeedSequence(seed)
@@ -221,7 +221,8 @@ def make_workload(name: str, *, B: int, S: int, N: int, dims: dict, dtype: str,
                 raise ValueError(f"unknown anchor recipe {recipe!r}")
             anchors[b], keep[b] = a, k
             _force_valid(lm[b], a, k)
-    lays = [_make_layer(rng_t, B, S, N, H, D, d_c, d_r, d_v, dtype) for _ in range(layers)]
+    lays = ([_make_layer(rng_t, B, S, N, H, D, d_c, d_r, d_v, dtype) for _ in range(layers)]
+            if tensors else [])
     return Workload(name=name, B=B, S=S, N=N, W=W, H=H, D=D, d_c=d_c, d_r=d_r, d_v=d_v,
                     dtype=dtype, rope_base=rope_base,
                     loss_mask=lm, anchors=anchors, keep=keep, anchor_source=source,
@@ -231,25 +232,26 @@ def make_workload(name: str, *, B: int, S: int, N: int, dims: dict, dtype: str,
 TINY_DIMS = dict(H=2, D=32, d_c=16, d_r=8, d_v=16, W=16)
 
 
-def config(k: int, *, seed: Optional[int] = None) -> Workload:
-    """The five benchmark configurations at full size (1-based index)."""
+def config(k: int, *, seed: Optional[int] = None, tensors: bool = True) -> Workload:
+    """The five benchmark configurations at full size (1-based index).
+    tensors=False skips the activations and weights (mask and anchors only)."""
     seed = 1000 + k if seed is None else seed
     if k == 1:
         return make_workload("tiny-fp32 B1 S48 N4 W16 H2", B=1, S=48, N=4, dims=TINY_DIMS,
-                             dtype="f32", recipe="uniform", seed=seed,
+                             dtype="f32", recipe="uniform", seed=seed, tensors=tensors,
                              recipe_args=dict(n_forced_low=1))
     if k == 2:
         return make_workload("glm-layer B1 S2048 N64", B=1, S=2048, N=64, dims=GLM_DIMS,
-                             dtype="bf16", recipe="sampler", seed=seed)
+                             dtype="bf16", recipe="sampler", seed=seed, tensors=tensors)
     if k == 3:
         return make_workload("overlap B2 S8192 N512", B=2, S=8192, N=512, dims=GLM_DIMS,
-                             dtype="bf16", recipe="clustered", seed=seed)
+                             dtype="bf16", recipe="clustered", seed=seed, tensors=tensors)
     if k == 4:
         return make_workload("headline B1 S32768 N1024", B=1, S=32768, N=1024, dims=GLM_DIMS,
-                             dtype="bf16", recipe="headline", seed=seed)
+                             dtype="bf16", recipe="headline", seed=seed, tensors=tensors)
     if k == 5:
         return make_workload("three-layer B1 S131072 N4096 L3", B=1, S=131072, N=4096,
-                             dims=GLM_DIMS, dtype="bf16", recipe="sampler", seed=seed, layers=3)
+                             dims=GLM_DIMS, dtype="bf16", recipe="sampler", seed=seed, tensors=tensors, layers=3)
     raise ValueError(k)
 
 
