@@ -1,0 +1,240 @@
+"""Benchmark of the DSpark draft-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
+
+A step is one dspark_attn_fwd call (index build, RoPE table, absorb,
+attention, W_UV) over the whole workload, with inputs resident in HBM.  The
+default workload is the S=32768, N=1024 headline configuration (25% padding
+blocks, 5% clamped windows, synthetic N(0,1) activations and N(0,1/512)
+weights).  Prints one JSON line.
+
+Useful FLOP count only what the absorbed method must compute for kept blocks
+and visible keys: per kept block 5*H*(2*d_c*D + 2*(D+d_r)*v + 2*D*v + 2*D*d_v)
+with v = min(A, W-1) + 5.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MI355X_BF16_PEAK_TFLOPS = 2516.6     # 256 CU * 2.4 GHz * 4096 FLOP/CU/clk, dense
+MI355X_HBM_PEAK_GBS = 8000.0
+STAGES = ("index+rope", "absorb", "attention", "w_uv")
+
+
+def useful_flop(anchors, keep, W, H, D, d_c, d_r, d_v, block=5) -> int:
+    total = 0
+    for a, k in zip(np.asarray(anchors).ravel(), np.asarray(keep).ravel()):
+        if k:
+            v = min(int(a), W - 1) + block
+            total += block * H * (2 * d_c * D + 2 * (D + d_r) * v + 2 * D * v + 2 * D * d_v)
+    return total
+
+
+def stage_bytes(wl, anchors, keep):
+    """Algorithmic HBM bytes per launch of each stage (bf16 = 2 B):
+    every input read once, the context read as the union of the kept
+    windows, each output written once."""
+    kept = int(np.asarray(keep).sum())
+    rows = 5 * kept
+    H, D, dc, dr, dv = wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v
+    union = 0
+    for b in range(wl.B):
+        cover = np.zeros(wl.S, dtype=bool)
+        for a, k in zip(anchors[b], keep[b]):
+            if k:
+                cover[max(0, a - wl.W + 1):a] = True
+        union += int(cover.sum())
+    pad_rows = 5 * (wl.B * wl.N - kept)
+    return {
+        "absorb": rows * H * (dc + D) * 2 + H * dc * D * 2,
+        "attention": rows * H * (D + dr + D) * 2 + (union + rows) * (D + dr) * 2
+                     + pad_rows * H * dv * 2,
+        "w_uv": rows * H * (D + dv) * 2 + H * dv * D * 2,
+    }
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch loaded (one runtime per
+    process), so that they can be recorded by the library on torch's stream."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (brings in the runtime)
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def record(self, ev, stream):
+        assert self.hip.hipEventRecord(ev, stream) == 0
+
+    def elapsed_ms(self, a, b) -> float:
+        assert self.hip.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def cpu_baseline(wl, anchors, keep, budget_s: float = 15.0):
+    """The fp64 oracle as it stands, on a bounded sample of the same
+    workload's kept blocks (timed on the host, single process)."""
+    import oracle as O
+    kept = [(b, n) for b in range(wl.B) for n in range(wl.N) if keep[b, n]]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(kept))
+    n_blocks, spent, done = 4, 0.0, []
+    while spent < budget_s and len(done) < len(kept):
+        pick = [kept[i] for i in order[len(done):len(done) + n_blocks]]
+        t0 = time.perf_counter()
+        O.forward(wl, 0, anchors, keep, form="gathered", blocks=pick)
+        spent += time.perf_counter() - t0
+        done += pick
+        n_blocks *= 2
+    flop = sum(useful_flop([anchors[b, n]], [1], wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v)
+               for b, n in done)
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info())
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return {"value": flop / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "blocks_per_s": len(done) / spent,
+            "sample": f"{len(done)} random kept blocks of the same workload "
+                      f"(fp64 numpy, gathered form, {spent:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import workloads as wk
+    import speculative_decoding_draft_amd as sd
+    from workloads.device import upload_anchors, upload_layer
+
+    wl = wk.config(args.config)
+    if wl.anchor_source == "sampler":
+        anchors = np.zeros((wl.B, wl.N), np.int32)
+        keep = np.zeros((wl.B, wl.N), np.uint8)
+        for b in range(wl.B):
+            anchors[b], keep[b] = sd.select_anchors_host(wl.loss_mask[b], wl.N, wl.sampler_seed + b)
+    else:
+        anchors, keep = wl.anchors, wl.keep
+    L = len(wl.layers)
+    tensors = [upload_layer(wl, i) for i in range(L)]
+    a_dev, k_dev = upload_anchors(anchors, keep)
+    desc = sd.make_desc(B=wl.B, S=wl.S, N=wl.N, window=wl.W, n_heads=wl.H, d_latent=wl.D,
+                        d_nope=wl.d_c, d_rope=wl.d_r, d_v=wl.d_v, rope_base=wl.rope_base,
+                        dtype=wl.dtype)
+    outs = [torch.empty((wl.B, wl.q_len, wl.H, wl.d_v), dtype=torch.bfloat16, device="cuda")
+            for _ in range(L)]
+    ws = torch.empty(sd.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sptr = int(stream.cuda_stream)
+    hip = HipEvents()
+    K = args.steps
+    ev = hip.create(K * L * 5)
+
+    def step(i, events=True):
+        for l in range(L):
+            t = tensors[l]
+            se = ev[(i * L + l) * 5:(i * L + l + 1) * 5] if events else None
+            sd.attn_fwd(desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"],
+                        t["kr_blk"], t["w_uk"], t["w_uv"], a_dev, k_dev, outs[l], ws,
+                        stream=sptr, stage_events=se)
+
+    for _ in range(args.warmup):
+        step(0, events=False)
+    st, fb = sd.read_device_status(ws, stream=sptr)
+    assert st == 0, sd.last_error()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_stage = {s: [] for s in STAGES}
+    call_ms = []
+    for i in range(K * L):
+        e = ev[i * 5:(i + 1) * 5]
+        call_ms.append(hip.elapsed_ms(e[0], e[4]))
+        for s_i, s in enumerate(STAGES):
+            per_stage[s].append(hip.elapsed_ms(e[s_i], e[s_i + 1]))
+    hip.destroy(ev)
+
+    flop = useful_flop(anchors, keep, wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v) * L
+    kept_blocks = int(keep.sum()) * L
+    ms_per_step = wall / K * 1e3
+    value = flop / (wall / K) / 1e12
+    stage_avg_us = {s: float(np.mean(v)) * 1e3 for s, v in per_stage.items()}
+    sbytes = stage_bytes(wl, anchors, keep)
+    dom = max(("absorb", "attention", "w_uv"), key=lambda s: stage_avg_us[s])
+    achieved = sbytes[dom] / (stage_avg_us[dom] * 1e-6) / 1e9
+    result = {
+        "metric": "DSpark draft-attn fwd useful TFLOP/s + blocks/s at S=32K, N=1024 (1 GPU)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "S": wl.S, "N": wl.N, "W": wl.W,
+                   "heads": wl.H, "layers": L, "kept_blocks_per_layer": int(keep.sum()),
+                   "parallelism": "none (1 GPU)"},
+        "blocks_per_s": round(kept_blocks / (wall / K), 1),
+        "frac_of_bf16_peak": round(value / MI355X_BF16_PEAK_TFLOPS, 4),
+        "useful_gflop_per_step": round(flop / 1e9, 3),
+        "gpu_event_us_per_call": round(float(np.mean(call_ms)) * 1e3, 2),
+        "stage_us": {s: round(v, 2) for s, v in stage_avg_us.items()},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": MI355X_HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / MI355X_HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes": sbytes[dom]},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, anchors, keep, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
