@@ -85,7 +85,9 @@ typedef struct dspark_attn_desc {
  * descriptor; see dspark_last_error).  The workspace holds the per-block
  * index records, the compacted list of kept blocks, a small status area, the
  * RoPE cos/sin table and, on the MFMA path, the bf16 latent intermediates
- * q_abs and o_lat ([H, 5*B*N, D] each).  It must be 256-byte aligned. */
+ * q_abs and o_lat of one chunk of kept blocks ([H, 5*chunk, D] each; the
+ * size covers the largest chunk any opts->chunk_blocks can ask for, i.e. all
+ * B*N blocks).  It must be 256-byte aligned. */
 size_t dspark_attn_workspace_size(const dspark_attn_desc* desc);
 
 /* The masked MLA attention forward of one draft layer.
@@ -116,15 +118,29 @@ dspark_status dspark_attn_fwd(const dspark_attn_desc* desc,
 
 /* Extra controls for dspark_attn_fwd_ex (zero-initialise, then set fields). */
 typedef struct dspark_attn_opts {
-    /* NULL, or n_stage_events hipEvent_t handles recorded on `stream` at the
-     * stage boundaries: [0] before the index build, [1] after it, [2] after
-     * the q_abs absorb, [3] after the attention kernel, [4] after the W_UV
-     * projection (generic path: [2] and [3] coincide with [1]). */
+    /* NULL, or hipEvent_t handles recorded on `stream` between the kernels
+     * of the call, in launch order: [0] before the index build, [1] after
+     * the index build, RoPE table and padding fill, then for chunk c (see
+     * dspark_attn_plan) [2 + 3c] after its absorb, [3 + 3c] after its
+     * attention kernel, [4 + 3c] after its W_UV projection.  The generic path
+     * records [0] and [1] only, and [2] after its single kernel. */
     void* const* stage_events;
-    int32_t n_stage_events;   /* 0 or 5 */
+    int32_t n_stage_events;   /* at least the count dspark_attn_plan reports */
     int32_t force_generic;    /* nonzero: use the generic fp32 kernels even
                                  where the MFMA path applies */
+    int32_t chunk_blocks;     /* > 0: kept blocks per kernel round on the MFMA
+                                 path (the bf16 intermediates of one round
+                                 are 640 KiB per block); 0: one round over
+                                 all B*N blocks */
 } dspark_attn_opts;
+
+/* Launch plan of dspark_attn_fwd_ex for (desc, opts) (opts may be NULL):
+ * *n_chunks kernel rounds of *chunk_blocks kept blocks each (the count is an
+ * upper bound: chunks past the number of kept blocks exit at once), and
+ * *n_events stage events recorded when opts->stage_events is given.  Any
+ * output pointer may be NULL. */
+dspark_status dspark_attn_plan(const dspark_attn_desc* desc, const dspark_attn_opts* opts,
+                               int32_t* n_chunks, int32_t* chunk_blocks, int32_t* n_events);
 
 /* dspark_attn_fwd with options; opts may be NULL. */
 dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc,

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     Desc,
     DSparkError,
     abi_version,
+    attn_plan,
     attn_fwd,
     build_index,
     last_error,

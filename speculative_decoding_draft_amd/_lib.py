@@ -28,7 +28,7 @@ STATUS_NAMES = {0: "DSPARK_OK", -1: "DSPARK_EINVAL", -2: "DSPARK_EUNSUPPORTED",
 DSPARK_F32 = 0
 DSPARK_BF16 = 1
 
-EXPORTS = ("dspark_attn_workspace_size", "dspark_attn_fwd", "dspark_attn_fwd_ex",
+EXPORTS = ("dspark_attn_workspace_size", "dspark_attn_fwd", "dspark_attn_fwd_ex", "dspark_attn_plan",
            "dspark_build_index", "dspark_select_anchors_host", "dspark_read_device_status",
            "dspark_last_error", "dspark_abi_version")
 
@@ -50,7 +50,8 @@ class Desc(ctypes.Structure):
 
 class Opts(ctypes.Structure):
     _fields_ = [("stage_events", ctypes.POINTER(ctypes.c_void_p)),
-                ("n_stage_events", ctypes.c_int32), ("force_generic", ctypes.c_int32)]
+                ("n_stage_events", ctypes.c_int32), ("force_generic", ctypes.c_int32),
+                ("chunk_blocks", ctypes.c_int32)]
 
 
 def _load():
@@ -71,6 +72,8 @@ def _load():
     lib.dspark_attn_fwd.restype = i32
     lib.dspark_attn_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(Opts)]
     lib.dspark_attn_fwd_ex.restype = i32
+    lib.dspark_attn_plan.argtypes = [pd, ctypes.POINTER(Opts)] + [ctypes.POINTER(i32)] * 3
+    lib.dspark_attn_plan.restype = i32
     lib.dspark_build_index.argtypes = [pd, vp, vp, vp, vp, sz, vp]
     lib.dspark_build_index.restype = i32
     lib.dspark_select_anchors_host.argtypes = [vp, i32, i32, u64, vp, vp]
@@ -129,24 +132,41 @@ def _stream(stream) -> Optional[int]:
     return int(stream.cuda_stream)
 
 
+def _opts(stage_events=None, force_generic=False, chunk_blocks=0):
+    opts = Opts()
+    keep = None
+    if stage_events is not None:
+        keep = (ctypes.c_void_p * len(stage_events))(*stage_events)
+        opts.stage_events = ctypes.cast(keep, ctypes.POINTER(ctypes.c_void_p))
+        opts.n_stage_events = len(stage_events)
+    opts.force_generic = 1 if force_generic else 0
+    opts.chunk_blocks = int(chunk_blocks)
+    return opts, keep
+
+
+def attn_plan(desc: Desc, force_generic: bool = False, chunk_blocks: int = 0):
+    """dspark_attn_plan: (n_chunks, chunk_blocks, n_events)."""
+    opts, _ = _opts(None, force_generic, chunk_blocks)
+    nc, cb, ne = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.dspark_attn_plan(ctypes.byref(desc), ctypes.byref(opts), ctypes.byref(nc),
+                                ctypes.byref(cb), ctypes.byref(ne)))
+    return nc.value, cb.value, ne.value
+
+
 def attn_fwd(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
              anchors, keep, out, workspace, stream=None,
-             stage_events: Optional[Sequence[int]] = None, force_generic: bool = False) -> None:
+             stage_events: Optional[Sequence[int]] = None, force_generic: bool = False,
+             chunk_blocks: int = 0) -> None:
     """dspark_attn_fwd / dspark_attn_fwd_ex; raises DSparkError on a non-OK status."""
     args = [ctypes.byref(desc)] + [_ptr(t) for t in (q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk,
                                                      kr_blk, w_uk, w_uv, anchors, keep, out,
                                                      workspace)]
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args += [ws_bytes, _stream(stream)]
-    if stage_events is None and not force_generic:
+    if stage_events is None and not force_generic and not chunk_blocks:
         _check(lib.dspark_attn_fwd(*args))
         return
-    opts = Opts()
-    if stage_events is not None:
-        arr = (ctypes.c_void_p * len(stage_events))(*stage_events)
-        opts.stage_events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
-        opts.n_stage_events = len(stage_events)
-    opts.force_generic = 1 if force_generic else 0
+    opts, _arr = _opts(stage_events, force_generic, chunk_blocks)
     _check(lib.dspark_attn_fwd_ex(*args, ctypes.byref(opts)))
 
 

@@ -14,7 +14,8 @@
 // Work split: a workgroup owns one head, one half of the 512 output dims and
 // a strided range of 128-row iterations.  The 192 x 256 weight slice stays in
 // LDS for the workgroup's lifetime; its transposed MFMA fragments are read
-// with ds_read_b64_tr_b16.  Each wave computes 128 dims x 64 rows.
+// with ds_read_b64_tr_b16 once per wave into registers.  Each wave computes
+// 128 dims x 64 rows per iteration.
 #include "kernels.hpp"
 
 namespace dspark {
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
                                                      const int32_t* __restrict__ kept,
                                                      const int32_t* __restrict__ status,
                                                      bf16* __restrict__ q_abs, int N, int L5,
-                                                     int rows_max) {
+                                                     int lat_rows, int slot0, int nslots) {
     __shared__ __attribute__((aligned(16))) bf16 wl[kDc * kAbsStride];
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int dh = lid & 1;
@@ -42,61 +43,110 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
     for (int e = tid; e < kDc * 32; e += 256) {
         const int c = e >> 5, ch = e & 31;
         st16(&wl[c * kAbsStride + ch * 8],
-             ld16(w_uk + ((size_t)h * kDc + c) * kD + dh * 256 + ch * 8));
+             gld16(w_uk + ((size_t)h * kDc + c) * kD + dh * 256 + ch * 8));
     }
     __syncthreads();
 
-    const int rows = kBlock * status[kStKeptCount];
+    // rows of this chunk: kept slots [slot0, slot0 + nslots); local row r is
+    // query r % 5 of slot slot0 + r / 5
+    const int rows = kBlock * max(0, min(nslots, status[kStKeptCount] - slot0));
+    const int n_iter = (rows + kAbsRowsPerIter - 1) / kAbsRowsPerIter;
     const int wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
     const int wd = wave & 1;      // 128-dim quarter inside the half
     const int wr = wave >> 1;     // 64-row group inside the iteration
+    if (rg >= n_iter) return;
 
-    for (int it = rg; it * kAbsRowsPerIter < rows; it += kAbsRowGroups) {
-        const int row0 = it * kAbsRowsPerIter + wr * 64;
-        const bf16* qp[4];
-        for (int t = 0; t < 4; ++t) {
-            int r = row0 + t * 16 + l16;
-            r = (r < rows) ? r : rows - 1;
-            const int slot = r / kBlock, j = r % kBlock;
-            const int blk = kept[slot];
-            const int b = blk / N, n = blk % N;
-            qp[t] = q_nope + (((size_t)b * L5 + (size_t)kBlock * n + j) * kH + h) * kDc + g * 8;
-        }
-        f32x4 acc[8][4];
+    // row r of iteration `it`, tile t (clamped; rows past the end are computed
+    // on a duplicate row and not stored)
+    auto row_of = [&](int it, int t) {
+        const int r = it * kAbsRowsPerIter + wr * 64 + t * 16 + l16;
+        return (r < rows) ? r : rows - 1;
+    };
+    auto q_ptr = [&](int r, int blk) {
+        const int j = r % kBlock;
+        const int b = blk / N, n = blk % N;
+        return q_nope + (((size_t)b * L5 + (size_t)kBlock * n + j) * kH + h) * kDc + g * 8;
+    };
+    constexpr int kKs = kDc / 32;     // 6 k-steps per iteration
+
+    // The wave's A operand (its 128 x 192 slice of W_UK[h]^T) is the same in
+    // every iteration: read it out of LDS once, transposed, and keep it in
+    // registers (48 fragments, 192 VGPRs), so the main loop has no LDS reads.
+    // Fragment (ks, dt): rows d = wd*128 + dt*16 + l16, k-values
+    // c = ks*32 + g*8 + 0..7.
+    bf16x8 afr[kKs][8];
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) {
+        const bf16* abase = wl + (ks * 32 + g * 8 + (l16 >> 2)) * kAbsStride + wd * 128 +
+                            (l16 & 3) * 4;
+#pragma unroll
         for (int dt = 0; dt < 8; ++dt)
+            afr[ks][dt] = cat(lds_read_tr(abase + dt * 16), lds_read_tr(abase + 4 * kAbsStride + dt * 16));
+    }
+
+    // B fragments: a ring of kPf k-steps; consuming k-step ks frees slot
+    // ks % kPf, which is refilled with k-step ks + kPf (of this iteration or,
+    // wrapping, of the next one)
+    constexpr int kPf = 3;            // divides kKs
+    bf16x8 ring[kPf][4];
+    const bf16* qp[4];
+    int blk_next[4];
+    for (int t = 0; t < 4; ++t) {
+        const int r = row_of(rg, t);
+        qp[t] = q_ptr(r, kept[slot0 + r / kBlock]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kPf; ++ks)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ring[ks][t] = gld16(qp[t] + ks * 32);
+    for (int t = 0; t < 4; ++t) blk_next[t] = kept[slot0 + row_of(rg + kAbsRowGroups, t) / kBlock];
+
+    // The loop body is branch-free so that the compiler's wait counts stay
+    // exact across iterations: past the last iteration the prefetches and
+    // kept-list reads re-read clamped (valid) rows, and rows past the end are
+    // computed on a duplicate of the last row and stored onto it (same value).
+    for (int it = rg; it < n_iter; it += kAbsRowGroups) {
+        const int nxt = it + kAbsRowGroups;
+        const bf16* np[4];
+        for (int t = 0; t < 4; ++t) np[t] = q_ptr(row_of(nxt, t), blk_next[t]);
+        for (int t = 0; t < 4; ++t) blk_next[t] = kept[slot0 + row_of(nxt + kAbsRowGroups, t) / kBlock];
+        f32x4 acc[8][4];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
             for (int t = 0; t < 4; ++t) acc[dt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-        for (int ks = 0; ks < kDc / 32; ++ks) {
+        for (int ks = 0; ks < kKs; ++ks) {
             bf16x8 bq[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) bq[t] = ld16(qp[t] + ks * 32);
-            // A fragment rows: dims wd*128 + dt*16 + l16; k-values c = ks*32 + g*8 + 0..7
-            const bf16* abase = wl + (ks * 32 + g * 8 + (l16 >> 2)) * kAbsStride + wd * 128 +
-                                (l16 & 3) * 4;
+            for (int t = 0; t < 4; ++t) bq[t] = ring[ks % kPf][t];
+            if (ks + kPf < kKs) {
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const bf16x4 lo = lds_read_tr(abase + dt * 16);
-                const bf16x4 hi = lds_read_tr(abase + 4 * kAbsStride + dt * 16);
-                const bf16x8 af = cat(lo, hi);
+                for (int t = 0; t < 4; ++t) ring[ks % kPf][t] = gld16(qp[t] + (ks + kPf) * 32);
+            } else {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) acc[dt][t] = mfma_16x16x32(af, bq[t], acc[dt][t]);
+                for (int t = 0; t < 4; ++t) ring[ks % kPf][t] = gld16(np[t] + (ks + kPf - kKs) * 32);
             }
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc[dt][t] = mfma_16x16x32(afr[ks][dt], bq[t], acc[dt][t]);
         }
-        // lane holds dims dcol + 4g + i of tile pair (2p, 2p+1) for row row0 + 16t + l16
+        for (int t = 0; t < 4; ++t) qp[t] = np[t];
+        // lane holds dims dcol + 4g + i of tile pair (2p, 2p+1) for row it*128 + wr*64 + 16t + l16
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int r = row0 + t * 16 + l16;
-            if (r >= rows) continue;
-            bf16* dst = q_abs + ((size_t)h * rows_max + r) * kD + dh * 256 + wd * 128 + g * 8;
+            const int r = row_of(it, t);
+            bf16* dst = q_abs + ((size_t)h * lat_rows + r) * kD + dh * 256 + wd * 128 + g * 8;
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const f32x4 a0 = acc[2 * pp][t], a1 = acc[2 * pp + 1][t];
                 bf16x8 v;
                 v[0] = (bf16)a0[0]; v[1] = (bf16)a0[1]; v[2] = (bf16)a0[2]; v[3] = (bf16)a0[3];
                 v[4] = (bf16)a1[0]; v[5] = (bf16)a1[1]; v[6] = (bf16)a1[2]; v[7] = (bf16)a1[3];
-                st16(dst + pp * 32, v);
+                gst16(dst + pp * 32, v);
             }
         }
     }
@@ -104,10 +154,12 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
 
 }  // namespace
 
-hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws, hipStream_t s) {
+hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
+                         hipStream_t s) {
     const int grid = kH * 2 * kAbsRowGroups;
     hipLaunchKernelGGL(absorb_kernel, dim3(grid), dim3(256), 0, s, (const bf16*)in.q_nope,
-                       (const bf16*)in.w_uk, ws.kept, ws.status, ws.qabs, p.N, p.L5, p.rows_max);
+                       (const bf16*)in.w_uk, ws.kept, ws.status, ws.qabs, p.N, p.L5, p.lat_rows,
+                       c.slot0, c.nslots);
     return hipGetLastError();
 }
 

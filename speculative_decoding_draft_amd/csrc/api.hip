@@ -63,12 +63,23 @@ dspark_status check_desc(const dspark_attn_desc* d, bool* empty) {
     return DSPARK_OK;
 }
 
+// Kept blocks per kernel round.  By default one round covers every block:
+// each kernel's grid is sized for the whole problem, and smaller rounds
+// (which would keep a round's q_abs / o_lat, 640 KiB per block, inside the
+// 256 MB Infinity Cache) leave the 256 CUs under-filled and pay each
+// launch's weight staging again, which costs more than the cache saves.
+int chunk_blocks(const dspark_attn_desc& d, const dspark_attn_opts* opts) {
+    const int blocks = d.B * d.N;
+    const int c = (opts && opts->chunk_blocks > 0) ? opts->chunk_blocks : blocks;
+    return c < blocks ? c : blocks;
+}
+
 Problem make_problem(const dspark_attn_desc& d) {
     Problem p;
     p.B = d.B; p.S = d.S; p.N = d.N; p.W = d.window; p.H = d.n_heads;
     p.D = d.d_latent; p.dc = d.d_nope; p.dr = d.d_rope; p.dv = d.d_v;
     p.L5 = kBlock * d.N;
-    p.rows_max = kBlock * d.B * d.N;
+    p.lat_rows = kBlock * d.B * d.N;   // narrowed to the chunk by the caller
     p.scale = (float)(d.softmax_scale > 0.0 ? d.softmax_scale
                                             : 1.0 / std::sqrt((double)(d.d_nope + d.d_rope)));
     return p;
@@ -147,8 +158,6 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
         if (ptrs[i] && i != 9 && !aligned16(ptrs[i]))
             return fail(DSPARK_EINVAL, "%s must be 16-byte aligned", names[i]);
     }
-    if (opts && opts->stage_events && opts->n_stage_events != 5)
-        return fail(DSPARK_EINVAL, "n_stage_events must be 5 when stage_events is given");
     const bool fast = is_fast_path(d) && !(opts && opts->force_generic);
     const WsLayout L = ws_layout(d, fast);
     st = check_workspace(workspace, ws_bytes, L.total);
@@ -169,26 +178,55 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
         return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[k]), s) : hipSuccess;
     };
 
+    const int chunk = chunk_blocks(d, opts);
+    const int n_chunks = fast ? (d.B * d.N + chunk - 1) / chunk : 0;
+    const int n_events = fast ? 2 + 3 * n_chunks : 3;
+    if (ev && opts->n_stage_events < n_events)
+        return fail(DSPARK_EINVAL, "this call records %d stage events; n_stage_events is %d",
+                    n_events, opts->n_stage_events);
+    Problem pc = p;
+    pc.lat_rows = kBlock * chunk;
+
     hipError_t e;
     if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = launch_index(p, anchors, keep, ws, nullptr, s)) != hipSuccess)
         return hip_fail(e, "index kernel launch");
     if ((e = launch_rope_table(p, L.rope_rows, make_theta(d), ws, s)) != hipSuccess)
         return hip_fail(e, "rope table launch");
+    if (fast && (e = launch_fill(p, in, ws, s)) != hipSuccess)
+        return hip_fail(e, "padding fill launch");
     if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if (fast) {
-        if ((e = launch_absorb(p, in, ws, s)) != hipSuccess) return hip_fail(e, "absorb launch");
-        if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-        if ((e = launch_attn(p, in, ws, s)) != hipSuccess) return hip_fail(e, "attention launch");
-        if ((e = mark(3)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-        if ((e = launch_uv(p, in, ws, s)) != hipSuccess) return hip_fail(e, "W_UV launch");
+        for (int c = 0; c < n_chunks; ++c) {
+            const Chunk ch{c * chunk, chunk};
+            if ((e = launch_absorb(pc, in, ws, ch, s)) != hipSuccess)
+                return hip_fail(e, "absorb launch");
+            if ((e = mark(2 + 3 * c)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+            if ((e = launch_attn(pc, in, ws, ch, s)) != hipSuccess)
+                return hip_fail(e, "attention launch");
+            if ((e = mark(3 + 3 * c)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+            if ((e = launch_uv(pc, in, ws, ch, s)) != hipSuccess) return hip_fail(e, "W_UV launch");
+            if ((e = mark(4 + 3 * c)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        }
     } else {
-        if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-        if ((e = mark(3)) != hipSuccess) return hip_fail(e, "hipEventRecord");
         if ((e = launch_generic(p, d.dtype == DSPARK_BF16, in, ws, s)) != hipSuccess)
             return hip_fail(e, "generic kernel launch");
+        if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
-    if ((e = mark(4)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    return ok();
+}
+
+dspark_status dspark_attn_plan(const dspark_attn_desc* desc, const dspark_attn_opts* opts,
+                               int32_t* n_chunks, int32_t* chunk_out, int32_t* n_events) {
+    bool empty = false;
+    dspark_status st = check_desc(desc, &empty);
+    if (st != DSPARK_OK) return st;
+    const bool fast = is_fast_path(*desc) && !(opts && opts->force_generic) && !empty;
+    const int chunk = empty ? 0 : chunk_blocks(*desc, opts);
+    const int nc = fast ? (desc->B * desc->N + chunk - 1) / chunk : 0;
+    if (n_chunks) *n_chunks = nc;
+    if (chunk_out) *chunk_out = fast ? chunk : 0;
+    if (n_events) *n_events = empty ? 0 : (fast ? 2 + 3 * nc : 3);
     return ok();
 }
 

@@ -32,9 +32,10 @@ template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     const bf16* __restrict__ q_rope, const bf16* __restrict__ ckv_ctx,
     const bf16* __restrict__ kr_ctx, const bf16* __restrict__ ckv_blk,
-    const bf16* __restrict__ kr_blk, bf16* __restrict__ out, const int4* __restrict__ idx,
+    const bf16* __restrict__ kr_blk, const int4* __restrict__ idx,
+    const int32_t* __restrict__ kept, const int32_t* __restrict__ status,
     const float2* __restrict__ rope, const bf16* __restrict__ q_abs, bf16* __restrict__ o_lat,
-    int S, int N, int L5, int total_blocks, int rows_max, float scale) {
+    int S, int N, int L5, int lat_rows, int slot0, int nslots, float scale) {
     __shared__ __attribute__((aligned(16))) bf16 ckv_l[kMaxKeys * kCkvStride];
     __shared__ __attribute__((aligned(16))) bf16 kr_l[kMaxKeys * kKrStride];
     __shared__ float2 qcs[kBlock * (kDr / 2)];
@@ -42,62 +43,95 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     constexpr int kThreads = WAVES * 64;
     constexpr int kGroups = 4 / WAVES;        // workgroups per block
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int blk = lid / kGroups;
-    if (blk >= total_blocks) return;
+    const int local = lid / kGroups;          // slot within the chunk
+    const int n_here = min(nslots, status[kStKeptCount] - slot0);
+    if (local >= n_here) return;
     const int hg0 = (lid % kGroups) * WAVES;  // first 16-head group of this workgroup
     const int tid = threadIdx.x;
+    const int blk = kept[slot0 + local];
     const int b = blk / N, n = blk % N;
     const size_t qrow0 = (size_t)b * L5 + (size_t)kBlock * n;
     const int4 rec = idx[blk];
-
-    if (rec.w < 0) {   // padding block -> 0, kept block with a bad anchor -> NaN
-        const bf16 fill = (rec.w == -1) ? (bf16)0.0f : (bf16)__builtin_nanf("");
-        bf16x8 fv;
-        for (int e = 0; e < 8; ++e) fv[e] = fill;
-        constexpr int kChunks = WAVES * 16 * kDv / 8;    // 16-byte chunks per query row
-        for (int e = tid; e < kBlock * kChunks; e += kThreads) {
-            const int j = e / kChunks, c = e % kChunks;
-            st16(out + ((qrow0 + j) * kH + hg0 * 16) * kDv + (size_t)c * 8, fv);
-        }
-        return;
-    }
-    const int ctx_lo = rec.x, ctx_len = rec.y, pos0 = rec.z, slot = rec.w;
+    const int ctx_lo = rec.x, ctx_len = rec.y, pos0 = rec.z;
     const int nkeys = ctx_len + kBlock;
-
-    // ---- stage the keys: slot s < ctx_len is context row ctx_lo + s, the
-    // rest are the block's own positions; k^R is rotated on the way in
-    for (int e = tid; e < nkeys * (kD / 8); e += kThreads) {
-        const int s = e / (kD / 8), ch = e % (kD / 8);
-        const bf16* src = (s < ctx_len)
-                              ? ckv_ctx + ((size_t)b * S + ctx_lo + s) * kD
-                              : ckv_blk + (qrow0 + (s - ctx_len)) * kD;
-        st16(&ckv_l[s * kCkvStride + ch * 8], ld16(src + ch * 8));
-    }
-    for (int e = tid; e < nkeys * (kDr / 8); e += kThreads) {
-        const int s = e / (kDr / 8), ch = e % (kDr / 8);
-        const bool is_ctx = s < ctx_len;
-        const bf16* src = is_ctx ? kr_ctx + ((size_t)b * S + ctx_lo + s) * kDr
-                                 : kr_blk + (qrow0 + (s - ctx_len)) * kDr;
-        const int pos = is_ctx ? ctx_lo + s : pos0 + (s - ctx_len);
-        const bf16x8 x = ld16(src + ch * 8);
-        bf16x8 y;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float2 cs = rope[(size_t)pos * (kDr / 2) + ch * 4 + q];
-            const float x0 = (float)x[2 * q], x1 = (float)x[2 * q + 1];
-            y[2 * q] = (bf16)(x0 * cs.x - x1 * cs.y);
-            y[2 * q + 1] = (bf16)(x0 * cs.y + x1 * cs.x);
-        }
-        st16(&kr_l[s * kKrStride + ch * 8], y);
-    }
-    for (int e = tid; e < kBlock * (kDr / 2); e += kThreads)
-        qcs[e] = rope[(size_t)(pos0 + e / (kDr / 2)) * (kDr / 2) + e % (kDr / 2)];
-    __syncthreads();
-
     const int wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
     const int head = (hg0 + wave) * 16 + l16;   // this lane's head (B-operand column)
-    const int nkt = (nkeys + 15) >> 4;
+
+    // ---- stage the keys: slot s < ctx_len is context row ctx_lo + s, the
+    // rest are the block's own positions.  c^KV rows go straight to LDS, one
+    // wave instruction per 1 KB row.
+    for (int s = wave; s < nkeys; s += WAVES) {
+        const bf16* src = (s < ctx_len) ? ckv_ctx + ((size_t)b * S + ctx_lo + s) * kD
+                                        : ckv_blk + (qrow0 + (s - ctx_len)) * kD;
+        async_copy_16(src + lane * 8, &ckv_l[s * kCkvStride]);
+    }
+
+    // Q fragments of the first k-steps are requested while the keys stream in
+    constexpr int kKs = (kD + kDr) / 32;           // 18 k-steps: 16 latent + 2 rope
+    constexpr int kPf = 3;                         // prefetch distance (k-steps)
+    const bf16* qa = q_abs + ((size_t)head * lat_rows + (size_t)kBlock * local) * kD + g * 8;
+    const bf16* qr = q_rope + (qrow0 * kH + head) * kDr + g * 8;
+    auto q_frag = [&](int ks, int t) -> bf16x8 {
+        return (ks < kD / 32) ? gld16(qa + t * kD + ks * 32)
+                              : gld16(qr + (size_t)t * kH * kDr + (ks - kD / 32) * 32);
+    };
+    bf16x8 qbuf[kPf][kBlock];
+#pragma unroll
+    for (int p = 0; p < kPf; ++p)
+#pragma unroll
+        for (int t = 0; t < kBlock; ++t) qbuf[p][t] = q_frag(p, t);
+
+    // k^R is rotated on the way in: batch the loads, then rotate and store
+    constexpr int kKrChunks = kDr / 8;             // 16-byte chunks per k^R row
+    constexpr int kKrBatch = 5;
+    constexpr int kKrIters =                       // 1 with four waves
+        (kMaxKeys * kKrChunks + kThreads * kKrBatch - 1) / (kThreads * kKrBatch);
+#pragma unroll
+    for (int bi = 0; bi < kKrIters; ++bi) {
+        const int base = bi * kThreads * kKrBatch;
+        bf16x8 xr[kKrBatch];
+        float4 cs01[kKrBatch], cs23[kKrBatch];
+#pragma unroll
+        for (int u = 0; u < kKrBatch; ++u) {
+            // unconditional (clamped) loads so that the batch is issued back to back
+            int e = base + u * kThreads + tid;
+            e = (e < nkeys * kKrChunks) ? e : nkeys * kKrChunks - 1;
+            {
+                const int s = e / kKrChunks, ch = e % kKrChunks;
+                const bool is_ctx = s < ctx_len;
+                const bf16* src = is_ctx ? kr_ctx + ((size_t)b * S + ctx_lo + s) * kDr
+                                         : kr_blk + (qrow0 + (s - ctx_len)) * kDr;
+                const int pos = is_ctx ? ctx_lo + s : pos0 + (s - ctx_len);
+                const float4* tb =
+                    reinterpret_cast<const float4*>(rope + (size_t)pos * (kDr / 2) + ch * 4);
+                xr[u] = gld16(src + ch * 8);
+                cs01[u] = tb[0];
+                cs23[u] = tb[1];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kKrBatch; ++u) {
+            const int e = base + u * kThreads + tid;
+            if (e < nkeys * kKrChunks) {
+                const int s = e / kKrChunks, ch = e % kKrChunks;
+                const float c[4] = {cs01[u].x, cs01[u].z, cs23[u].x, cs23[u].z};
+                const float sn[4] = {cs01[u].y, cs01[u].w, cs23[u].y, cs23[u].w};
+                bf16x8 y;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float x0 = (float)xr[u][2 * q], x1 = (float)xr[u][2 * q + 1];
+                    y[2 * q] = (bf16)(x0 * c[q] - x1 * sn[q]);
+                    y[2 * q + 1] = (bf16)(x0 * sn[q] + x1 * c[q]);
+                }
+                st16(&kr_l[s * kKrStride + ch * 8], y);
+            }
+        }
+    }
+    for (int e = tid; e < kBlock * (kDr / 2); e += kThreads)
+        qcs[e] = rope[(size_t)(pos0 + e / (kDr / 2)) * (kDr / 2) + e % (kDr / 2)];
+    __builtin_amdgcn_s_waitcnt(0);     // the LDS copies are counted by vmcnt
+    __syncthreads();
 
     // ---- scores, transposed: St[kt][t] = keys (16 kt + 4g + i) x head, query t
     f32x4 st[kMaxKt][kBlock];
@@ -113,47 +147,57 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
         krow[kt] = (r < nkeys) ? r : nkeys - 1;    // rows past the end are masked below
     }
 
-    // latent part: 16 k-steps of 32 dims; q_abs is stored in the permuted
-    // order that matches the two 8-byte c^KV reads below
-    const bf16* qa = q_abs + ((size_t)head * rows_max + (size_t)kBlock * slot) * kD + g * 8;
-#pragma unroll 2
-    for (int ks = 0; ks < kD / 32; ++ks) {
+    // latent k-steps read c^KV in the permuted order q_abs is stored in (two
+    // 8-byte pieces: dims 32ks + 4g + 0..3 and 32ks + 16 + 4g + 0..3); rope
+    // k-steps read k^R in natural order and rotate q^R in registers.  All 9
+    // key tiles are always processed (rows past the end are masked), so the
+    // A fragments of k-step ks + 1 can be read while k-step ks computes.
+    auto a_frag = [&](int ks, int kt) -> bf16x8 {
+        if (ks < kD / 32) {
+            const bf16* ap = &ckv_l[krow[kt] * kCkvStride + ks * 32 + g * 4];
+            return cat(ld8(ap), ld8(ap + 16));
+        }
+        return ld16(&kr_l[krow[kt] * kKrStride + (ks - kD / 32) * 32 + g * 8]);
+    };
+    bf16x8 acur[kMaxKt];
+#pragma unroll
+    for (int kt = 0; kt < kMaxKt; ++kt) acur[kt] = a_frag(0, kt);
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) {
         bf16x8 bq[kBlock];
 #pragma unroll
-        for (int t = 0; t < kBlock; ++t) bq[t] = ld16(qa + t * kD + ks * 32);
+        for (int t = 0; t < kBlock; ++t) bq[t] = qbuf[ks % kPf][t];
+        if (ks + kPf < kKs) {
 #pragma unroll
-        for (int kt = 0; kt < kMaxKt; ++kt) {
-            if (kt < nkt) {
-                const bf16* ap = &ckv_l[krow[kt] * kCkvStride + ks * 32 + g * 4];
-                const bf16x8 af = cat(ld8(ap), ld8(ap + 16));
+            for (int t = 0; t < kBlock; ++t) qbuf[ks % kPf][t] = q_frag(ks + kPf, t);
+        }
+        if (ks >= kD / 32) {
+            const int kr = ks - kD / 32;
 #pragma unroll
-                for (int t = 0; t < kBlock; ++t) st[kt][t] = mfma_16x16x32(af, bq[t], st[kt][t]);
+            for (int t = 0; t < kBlock; ++t) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float2 cs = qcs[t * (kDr / 2) + kr * 16 + g * 4 + q];
+                    const float x0 = (float)bq[t][2 * q], x1 = (float)bq[t][2 * q + 1];
+                    bq[t][2 * q] = (bf16)(x0 * cs.x - x1 * cs.y);
+                    bq[t][2 * q + 1] = (bf16)(x0 * cs.y + x1 * cs.x);
+                }
             }
         }
-    }
-    // rope part: 2 k-steps of 32 dims, q^R rotated in registers
-    const bf16* qr = q_rope + (qrow0 * kH + head) * kDr + g * 8;
+        bf16x8 anext[kMaxKt];
+        if (ks + 1 < kKs) {
 #pragma unroll
-    for (int ks = 0; ks < kDr / 32; ++ks) {
-        bf16x8 bq[kBlock];
-#pragma unroll
-        for (int t = 0; t < kBlock; ++t) {
-            const bf16x8 x = ld16(qr + (size_t)t * kH * kDr + ks * 32);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float2 cs = qcs[t * (kDr / 2) + ks * 16 + g * 4 + q];
-                const float x0 = (float)x[2 * q], x1 = (float)x[2 * q + 1];
-                bq[t][2 * q] = (bf16)(x0 * cs.x - x1 * cs.y);
-                bq[t][2 * q + 1] = (bf16)(x0 * cs.y + x1 * cs.x);
-            }
+            for (int kt = 0; kt < kMaxKt; ++kt) anext[kt] = a_frag(ks + 1, kt);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kt = 0; kt < kMaxKt; ++kt) {
-            if (kt < nkt) {
-                const bf16x8 af = ld16(&kr_l[krow[kt] * kKrStride + ks * 32 + g * 8]);
+        for (int kt = 0; kt < kMaxKt; ++kt)
 #pragma unroll
-                for (int t = 0; t < kBlock; ++t) st[kt][t] = mfma_16x16x32(af, bq[t], st[kt][t]);
-            }
+            for (int t = 0; t < kBlock; ++t) st[kt][t] = mfma_16x16x32(acur[kt], bq[t], st[kt][t]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + 1 < kKs) {
+#pragma unroll
+            for (int kt = 0; kt < kMaxKt; ++kt) acur[kt] = anext[kt];
         }
     }
 
@@ -167,14 +211,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
         float m = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < kMaxKt; ++kt) {
-            if (kt < nkt) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = kt * 16 + g * 4 + i;
-                    const float x = (key < nkeys) ? st[kt][t][i] : -INFINITY;
-                    st[kt][t][i] = x;
-                    m = fmaxf(m, x);
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int key = kt * 16 + g * 4 + i;
+                const float x = (key < nkeys) ? st[kt][t][i] : -INFINITY;
+                st[kt][t][i] = x;
+                m = fmaxf(m, x);
             }
         }
         m = fmaxf(m, __shfl_xor(m, 16));
@@ -183,15 +225,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
         float sum = 0.f;
 #pragma unroll
         for (int kt = 0; kt < kMaxKt; ++kt) {
-            if (kt < nkt) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = exp2f(fmaf(st[kt][t][i], c2, -mc));
-                    pr[kt][t][i] = (bf16)p;
-                    sum += p;
-                }
-            } else {
-                pr[kt][t] = bf16x4{(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+            for (int i = 0; i < 4; ++i) {
+                const float p = exp2f(fmaf(st[kt][t][i], c2, -mc));   // masked keys: 0
+                pr[kt][t][i] = (bf16)p;
+                sum += p;
             }
         }
         sum += __shfl_xor(sum, 16);
@@ -201,10 +239,31 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
 
     // ---- o_lat^T = c^KV^T P^T in 64-dim chunks; lane holds dims
     // 64c + 16mt + 4g + i of head `head`, query t
-    bf16* ol = o_lat + ((size_t)head * rows_max + (size_t)kBlock * slot) * kD + g * 8;
+    bf16* ol = o_lat + ((size_t)head * lat_rows + (size_t)kBlock * local) * kD + g * 8;
     const int tr_row = g * 4 + (l16 >> 2);      // transpose-read row inside a 16-key group
     const int tr_col = (l16 & 3) * 4;
-#pragma unroll 1
+    // A (V^T) fragments of step (c, kk) + 1 are read while step (c, kk)
+    // computes; kk < 4 covers keys 32kk .. 32kk + 31 (16x16x32), kk = 4 the
+    // last tile, keys 128 .. 143 (16x16x16)
+    constexpr int kKk = (kMaxKt + 1) / 2;      // 5
+    auto v_rows = [&](int kk, int& r0, int& r1) {
+        r0 = 32 * kk + tr_row;
+        r1 = r0 + 16;
+        r0 = (r0 < nkeys) ? r0 : nkeys - 1;
+        r1 = (r1 < nkeys) ? r1 : nkeys - 1;
+    };
+    auto v_frag = [&](int c, int kk, int mt) -> bf16x8 {
+        int r0, r1;
+        v_rows(kk, r0, r1);
+        const int col = c * 64 + mt * 16 + tr_col;
+        const bf16x4 lo = lds_read_tr(&ckv_l[r0 * kCkvStride + col]);
+        if (kk == kKk - 1) return cat(lo, lo);          // upper half unused
+        return cat(lo, lds_read_tr(&ckv_l[r1 * kCkvStride + col]));
+    };
+    bf16x8 vcur[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) vcur[mt] = v_frag(0, 0, mt);
+#pragma unroll
     for (int c = 0; c < kD / 64; ++c) {
         f32x4 o[4][kBlock];
 #pragma unroll
@@ -212,30 +271,34 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
 #pragma unroll
             for (int t = 0; t < kBlock; ++t) o[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < (kMaxKt + 1) / 2; ++kk) {
-            if (2 * kk + 1 < nkt) {
-                int r0 = 32 * kk + tr_row, r1 = r0 + 16;
-                r0 = (r0 < nkeys) ? r0 : nkeys - 1;
-                r1 = (r1 < nkeys) ? r1 : nkeys - 1;
+        for (int kk = 0; kk < kKk; ++kk) {
+            const bool last = (c == kD / 64 - 1) && (kk == kKk - 1);
+            const int nc = (kk == kKk - 1) ? c + 1 : c;
+            const int nkk = (kk == kKk - 1) ? 0 : kk + 1;
+            bf16x8 vnext[4];
+            if (!last) {
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const int col = c * 64 + mt * 16 + tr_col;
-                    const bf16x8 af = cat(lds_read_tr(&ckv_l[r0 * kCkvStride + col]),
-                                          lds_read_tr(&ckv_l[r1 * kCkvStride + col]));
+                for (int mt = 0; mt < 4; ++mt) vnext[mt] = v_frag(nc, nkk, mt);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (kk < kKk - 1) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int t = 0; t < kBlock; ++t)
-                        o[mt][t] = mfma_16x16x32(af, cat(pr[2 * kk][t], pr[2 * kk + 1][t]), o[mt][t]);
-                }
-            } else if (2 * kk < nkt) {
-                int r0 = 32 * kk + tr_row;
-                r0 = (r0 < nkeys) ? r0 : nkeys - 1;
+                        o[mt][t] = mfma_16x16x32(vcur[mt], cat(pr[2 * kk][t], pr[2 * kk + 1][t]), o[mt][t]);
+            } else {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
-                    const int col = c * 64 + mt * 16 + tr_col;
-                    const bf16x4 af = lds_read_tr(&ckv_l[r0 * kCkvStride + col]);
+                    const bf16x4 lo = __builtin_shufflevector(vcur[mt], vcur[mt], 0, 1, 2, 3);
 #pragma unroll
-                    for (int t = 0; t < kBlock; ++t) o[mt][t] = mfma_16x16x16(af, pr[2 * kk][t], o[mt][t]);
+                    for (int t = 0; t < kBlock; ++t) o[mt][t] = mfma_16x16x16(lo, pr[2 * kk][t], o[mt][t]);
                 }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (!last) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) vcur[mt] = vnext[mt];
             }
         }
 #pragma unroll
@@ -249,32 +312,57 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
                     v[i] = (bf16)(a0[i] * inv[t]);
                     v[4 + i] = (bf16)(a1[i] * inv[t]);
                 }
-                st16(ol + t * kD + c * 64 + pp * 32, v);
+                gst16(ol + t * kD + c * 64 + pp * 32, v);
             }
         }
     }
 }
 
+// Rows of padding blocks are written as 0 and rows of kept blocks with a bad
+// anchor as NaN; kept blocks are left to the attention path.
+__global__ __launch_bounds__(256) void fill_kernel(const int4* __restrict__ idx,
+                                                   bf16* __restrict__ out, int L5, int N,
+                                                   int H, int dv) {
+    const int blk = blockIdx.x;
+    const int4 rec = idx[blk];
+    if (rec.w >= 0) return;
+    const bf16 fill = (rec.w == -1) ? (bf16)0.0f : (bf16)__builtin_nanf("");
+    bf16x8 fv;
+    for (int e = 0; e < 8; ++e) fv[e] = fill;
+    const int b = blk / N, n = blk % N;
+    bf16* base = out + ((size_t)b * L5 + (size_t)kBlock * n) * H * dv;
+    const int chunks = kBlock * H * dv / 8;   // the block's rows are contiguous
+    for (int e = threadIdx.x; e < chunks; e += 256) gst16(base + (size_t)e * 8, fv);
+}
+
 }  // namespace
 
-hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, hipStream_t s) {
-    const int total = p.B * p.N;
-    // small batches: split the 64 heads over four single-wave workgroups so
-    // that more compute units take part
-    const bool split = total < 512;
+hipError_t launch_fill(const Problem& p, const Inputs& in, const Workspace& ws, hipStream_t s) {
+    hipLaunchKernelGGL(fill_kernel, dim3(p.B * p.N), dim3(256), 0, s, ws.idx, (bf16*)in.out, p.L5,
+                       p.N, p.H, p.dv);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
+                       hipStream_t s) {
+    // few blocks: split the 64 heads over four single-wave workgroups so that
+    // more compute units take part
+    const bool split = c.nslots < 160;
     const int groups = split ? 4 : 1;
-    int grid = total * groups;
+    int grid = c.nslots * groups;
     grid = (grid + 7) / 8 * 8;
     if (split) {
         hipLaunchKernelGGL(attn_kernel<1>, dim3(grid), dim3(64), 0, s, (const bf16*)in.q_rope,
                            (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
-                           (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, (bf16*)in.out, ws.idx,
-                           ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5, total, p.rows_max, p.scale);
+                           (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.idx, ws.kept,
+                           ws.status, ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5, p.lat_rows,
+                           c.slot0, c.nslots, p.scale);
     } else {
         hipLaunchKernelGGL(attn_kernel<4>, dim3(grid), dim3(256), 0, s, (const bf16*)in.q_rope,
                            (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
-                           (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, (bf16*)in.out, ws.idx,
-                           ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5, total, p.rows_max, p.scale);
+                           (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.idx, ws.kept,
+                           ws.status, ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5, p.lat_rows,
+                           c.slot0, c.nslots, p.scale);
     }
     return hipGetLastError();
 }

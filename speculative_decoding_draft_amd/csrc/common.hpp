@@ -77,6 +77,17 @@ __device__ inline int xcd_remap(int id, int grid) {
     return (id % 8) * (grid / 8) + id / 8;
 }
 
+// Global-memory accesses go through address-space-1 pointers so that they
+// compile to global_load/global_store: a generic (flat) access also counts
+// against lgkmcnt and turns every LDS wait into a wait for memory as well.
+typedef __attribute__((address_space(1))) bf16x8 gbf16x8;
+typedef __attribute__((address_space(1))) bf16x4 gbf16x4;
+__device__ inline bf16x8 gld16(const bf16* p) { return *(const gbf16x8*)(p); }
+__device__ inline bf16x4 gld8(const bf16* p) { return *(const gbf16x4*)(p); }
+__device__ inline void gst16(bf16* p, bf16x8 v) { *(gbf16x8*)(p) = v; }
+__device__ inline void gst8(bf16* p, bf16x4 v) { *(gbf16x4*)(p) = v; }
+
+// LDS accesses (pointers into __shared__ arrays)
 __device__ inline bf16x8 ld16(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ inline void st16(bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
 __device__ inline bf16x4 ld8(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
@@ -97,6 +108,15 @@ __device__ inline f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ inline f32x4 mfma_16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a),
                                                      __builtin_bit_cast(short4v, b), c, 0, 0, 0);
+}
+
+// Asynchronous 16-byte-per-lane copy global -> LDS (gfx950
+// global_load_lds_dwordx4): lane i's 16 bytes land at lds_base + 16 * i, so
+// one wave moves 1 KB into a contiguous LDS range.  lds_base must be the same
+// for every lane of the wave.  Completion is tracked by vmcnt.
+__device__ inline void async_copy_16(const void* gsrc, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(lds_base),
+                                     16, 0, 0);
 }
 
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16

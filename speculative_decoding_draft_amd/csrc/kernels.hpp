@@ -9,7 +9,7 @@ namespace dspark {
 struct Problem {
     int B, S, N, W, H, D, dc, dr, dv;
     int L5;          // 5 * N queries per sample
-    int rows_max;    // 5 * B * N kept-row capacity of the latent buffers
+    int lat_rows;    // row capacity of the latent buffers: 5 * (slots per chunk)
     float scale;     // softmax scale
 };
 
@@ -41,8 +41,19 @@ hipError_t launch_rope_table(const Problem& p, int rope_rows, const RopeTheta& t
 hipError_t launch_generic(const Problem& p, bool bf16_io, const Inputs& in,
                           const Workspace& ws, hipStream_t s);
 size_t generic_lds_bytes(const Problem& p);
-hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws, hipStream_t s);
-hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, hipStream_t s);
-hipError_t launch_uv(const Problem& p, const Inputs& in, const Workspace& ws, hipStream_t s);
+// A chunk is the range [slot0, slot0 + nslots) of kept-block slots; its
+// latent rows are 5 * (slot - slot0) + j in the latent buffers.
+struct Chunk {
+    int slot0;
+    int nslots;
+};
+
+hipError_t launch_fill(const Problem& p, const Inputs& in, const Workspace& ws, hipStream_t s);
+hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
+                         hipStream_t s);
+hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
+                       hipStream_t s);
+hipError_t launch_uv(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
+                     hipStream_t s);
 
 }  // namespace dspark

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
                                                  const int32_t* __restrict__ kept,
                                                  const int32_t* __restrict__ status,
                                                  bf16* __restrict__ out, int N, int L5,
-                                                 int rows_max) {
+                                                 int lat_rows, int slot0, int nslots) {
     __shared__ __attribute__((aligned(16))) bf16 wl[128 * kUvStride];
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int vh = lid & 1;
@@ -40,63 +40,114 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
     for (int e = tid; e < 128 * (kD / 8); e += 256) {
         const int v = e / (kD / 8), ch = e % (kD / 8);
         st16(&wl[v * kUvStride + ch * 8],
-             ld16(w_uv + ((size_t)h * kDv + vh * 128 + v) * kD + ch * 8));
+             gld16(w_uv + ((size_t)h * kDv + vh * 128 + v) * kD + ch * 8));
     }
     __syncthreads();
 
-    const int rows = kBlock * status[kStKeptCount];
+    // rows of this chunk (kept slots [slot0, slot0 + nslots))
+    const int rows = kBlock * max(0, min(nslots, status[kStKeptCount] - slot0));
+    const int n_iter = (rows + kUvRowsPerIter - 1) / kUvRowsPerIter;
     const int wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
+    if (rg >= n_iter) return;
 
-    for (int it = rg; it * kUvRowsPerIter < rows; it += kUvRowGroups) {
-        const int row0 = it * kUvRowsPerIter + wave * 64;
-        if (row0 >= rows) continue;
-        const bf16* op[4];
-        for (int t = 0; t < 4; ++t) {
-            int r = row0 + t * 16 + l16;
-            r = (r < rows) ? r : rows - 1;
-            op[t] = o_lat + ((size_t)h * rows_max + r) * kD + g * 8;
-        }
+    auto row_of = [&](int it, int t) {
+        const int r = it * kUvRowsPerIter + wave * 64 + t * 16 + l16;
+        return (r < rows) ? r : rows - 1;     // duplicate rows are computed, not stored
+    };
+    constexpr int kKs = kD / 32;     // 16 k-steps
+    // A fragment (ks, vt): rows v = vt*16 + l16 of the slice, k-values in the
+    // permuted o_lat order (dims 32ks + 4g + 0..3 and 32ks + 16 + 4g + 0..3)
+    auto a_frag = [&](int ks, int vt) -> bf16x8 {
+        const bf16* ap = &wl[(vt * 16 + l16) * kUvStride + ks * 32 + g * 4];
+        return cat(ld8(ap), ld8(ap + 16));
+    };
+    constexpr int kPf = 8;           // prefetch distance in k-steps (divides kKs)
+    const bf16* op[4];
+    for (int t = 0; t < 4; ++t) op[t] = o_lat + ((size_t)h * lat_rows + row_of(rg, t)) * kD + g * 8;
+    bf16x8 ring[kPf][4];
+#pragma unroll
+    for (int ks = 0; ks < kPf; ++ks)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ring[ks][t] = gld16(op[t] + ks * 32);
+
+    for (int it = rg; it < n_iter; it += kUvRowGroups) {
+        // keep the weight fragments in LDS: without this compiler barrier the
+        // loop-invariant LDS reads are hoisted into (and overflow) registers
+        __asm__ volatile("" ::: "memory");
+        const int nxt = it + kUvRowGroups;
+        const bf16* np[4];
+        for (int t = 0; t < 4; ++t)
+            np[t] = o_lat + ((size_t)h * lat_rows + row_of(nxt, t)) * kD + g * 8;
+        int blk[4];
+        for (int t = 0; t < 4; ++t) blk[t] = kept[slot0 + row_of(it, t) / kBlock];
+
         f32x4 acc[8][4];
+#pragma unroll
         for (int vt = 0; vt < 8; ++vt)
+#pragma unroll
             for (int t = 0; t < 4; ++t) acc[vt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-        for (int ks = 0; ks < kD / 32; ++ks) {
+        // A fragments of k-step ks + 1 are read from LDS while the MFMAs of
+        // k-step ks run; sched_barrier keeps the reads ahead of the MFMAs
+        bf16x8 acur[8];
+#pragma unroll
+        for (int vt = 0; vt < 8; ++vt) acur[vt] = a_frag(0, vt);
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) {
             bf16x8 bo[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) bo[t] = ld16(op[t] + ks * 32);
+            for (int t = 0; t < 4; ++t) bo[t] = ring[ks % kPf][t];
+            // without a next iteration np points at the current rows: the
+            // loads stay unconditional so that the wait counts stay exact
+            if (ks + kPf < kKs) {
 #pragma unroll
-            for (int vt = 0; vt < 8; ++vt) {
-                const bf16* ap = &wl[(vt * 16 + l16) * kUvStride + ks * 32 + g * 4];
-                const bf16x8 af = cat(ld8(ap), ld8(ap + 16));
+                for (int t = 0; t < 4; ++t) ring[ks % kPf][t] = gld16(op[t] + (ks + kPf) * 32);
+            } else {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) acc[vt][t] = mfma_16x16x32(af, bo[t], acc[vt][t]);
+                for (int t = 0; t < 4; ++t) ring[ks % kPf][t] = gld16(np[t] + (ks + kPf - kKs) * 32);
+            }
+            bf16x8 anext[8];
+            if (ks + 1 < kKs) {
+#pragma unroll
+                for (int vt = 0; vt < 8; ++vt) anext[vt] = a_frag(ks + 1, vt);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int vt = 0; vt < 8; ++vt)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) acc[vt][t] = mfma_16x16x32(acur[vt], bo[t], acc[vt][t]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < kKs) {
+#pragma unroll
+                for (int vt = 0; vt < 8; ++vt) acur[vt] = anext[vt];
             }
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const int r = row0 + t * 16 + l16;
-            if (r >= rows) continue;
-            const int slot = r / kBlock, j = r % kBlock;
-            const int blk = kept[slot];
-            const int b = blk / N, n = blk % N;
+            // rows past the end repeat the last row (same values, same place)
+            const int r = row_of(it, t);
+            const int j = r % kBlock;
+            const int b = blk[t] / N, n = blk[t] % N;
             bf16* dst = out + (((size_t)b * L5 + (size_t)kBlock * n + j) * kH + h) * kDv +
                         vh * 128 + g * 4;
 #pragma unroll
             for (int vt = 0; vt < 8; ++vt) {
                 const f32x4 a = acc[vt][t];
-                st8(dst + vt * 16, bf16x4{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]});
+                gst8(dst + vt * 16, bf16x4{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]});
             }
         }
+        for (int t = 0; t < 4; ++t) op[t] = np[t];
     }
 }
 
 }  // namespace
 
-hipError_t launch_uv(const Problem& p, const Inputs& in, const Workspace& ws, hipStream_t s) {
+hipError_t launch_uv(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
+                     hipStream_t s) {
     const int grid = kH * 2 * kUvRowGroups;
     hipLaunchKernelGGL(uv_kernel, dim3(grid), dim3(256), 0, s, (const bf16*)in.w_uv, ws.olat,
-                       ws.kept, ws.status, (bf16*)in.out, p.N, p.L5, p.rows_max);
+                       ws.kept, ws.status, (bf16*)in.out, p.N, p.L5, p.lat_rows, c.slot0,
+                       c.nslots);
     return hipGetLastError();
 }
 

@@ -116,6 +116,19 @@ def test_empty_problem_is_a_no_op():
     assert sd._lib.lib.dspark_attn_fwd(ctypes.byref(d), *([None] * 12), 0, None) == sd.DSPARK_OK
 
 
+def test_launch_plan():
+    d = glm_desc(B=2, N=1000)
+    assert sd.attn_plan(d) == (1, 2000, 5)
+    assert sd.attn_plan(d, chunk_blocks=1) == (2000, 1, 2 + 3 * 2000)
+    assert sd.attn_plan(d, chunk_blocks=300) == (7, 300, 23)
+    assert sd.attn_plan(d, chunk_blocks=10**6) == (1, 2000, 5)    # capped at B*N
+    assert sd.attn_plan(d, force_generic=True) == (0, 0, 3)
+    assert sd.attn_plan(glm_desc(dtype="f32")) == (0, 0, 3)
+    assert sd.attn_plan(glm_desc(N=0)) == (0, 0, 0)
+    with pytest.raises(sd.DSparkError):
+        sd.attn_plan(glm_desc(window=0))
+
+
 def test_generic_lds_limit_is_reported():
     d = glm_desc(dtype="f32", window=4000, d_latent=2048)
     need = sd.workspace_size(d)

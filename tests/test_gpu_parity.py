@@ -20,10 +20,12 @@ def sd():
     return sd
 
 
-def check_full(wl, form="dense", layer=0, force_generic=False, tol=None, guard=0):
+def check_full(wl, form="dense", layer=0, force_generic=False, tol=None, guard=0,
+               chunk_blocks=0):
     ga, gk, oa, ok = anchors_for(wl)
     assert np.array_equal(ga, oa) and np.array_equal(gk, ok), "anchor selection differs"
-    run = GpuRun(wl, layer, ga, gk, guard=guard, force_generic=force_generic).run()
+    run = GpuRun(wl, layer, ga, gk, guard=guard, force_generic=force_generic,
+                 chunk_blocks=chunk_blocks).run()
     gpu = run.result()
     ref = O.forward(wl, layer, oa, ok, form=form)
     if tol is None:
@@ -139,6 +141,51 @@ def test_cfg4_recipe_small(sd):
 def test_cfg4_recipe_four_wave_launch(sd):
     log("cfg4 recipe B1 S4096 N600 (one workgroup per block)")
     check_full(wk.scaled(4, S=4096, N=600), form="gathered")
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 64, 159, 160, 100000])
+def test_chunk_sizes(sd, chunk):
+    """Kept blocks processed in rounds of `chunk` (ragged last round, rounds
+    past the kept count, the one-wave / four-wave attention launch switch)."""
+    wl = wk.scaled(4, S=4096, N=224)
+    log(f"cfg4 recipe B1 S4096 N224, chunk {chunk}")
+    check_full(wl, form="gathered", guard=2048, chunk_blocks=chunk)
+
+
+def test_stage_events_are_recorded_in_order(sd):
+    import ctypes
+    import torch
+    wl = wk.scaled(4, S=2048, N=100)
+    run = GpuRun(wl, 0, wl.anchors, wl.keep, chunk_blocks=16)
+    n_chunks, chunk, n_ev = sd.attn_plan(run.desc, chunk_blocks=16)
+    assert (n_chunks, chunk, n_ev) == (7, 16, 2 + 3 * 7)
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(n_ev):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    t = run.t
+    with pytest.raises(sd.DSparkError):   # too few events is refused up front
+        sd.attn_fwd(run.desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"],
+                    t["kr_blk"], t["w_uk"], t["w_uv"], run.anchors, run.keep, run.out, run.ws,
+                    stage_events=evs[:-1], chunk_blocks=16)
+    sd.attn_fwd(run.desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"],
+                t["kr_blk"], t["w_uk"], t["w_uv"], run.anchors, run.keep, run.out, run.ws,
+                stage_events=evs, chunk_blocks=16)
+    torch.cuda.synchronize()
+    ms = ctypes.c_float()
+    for a, b in zip(evs[:-1], evs[1:]):
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        assert ms.value >= 0.0
+    for e in evs:
+        hip.hipEventDestroy(e)
+    compare(run.result(), O.forward(wl, 0, form="gathered"), wl.keep, BF16_MAX_ABS, BF16_REL_L2,
+            what="with stage events")
 
 
 @pytest.mark.parametrize("W", [1, 2, 16, 127, 128])
