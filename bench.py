@@ -29,6 +29,33 @@ sys.path.insert(0, ROOT)
 MI355X_BF16_PEAK_TFLOPS = 2516.6     # 256 CU * 2.4 GHz * 4096 FLOP/CU/clk, dense
 MI355X_HBM_PEAK_GBS = 8000.0
 STAGES = ("index+rope+fill", "absorb", "attention", "w_uv")
+KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.hip"}
+# Measured HBM bytes per launch on the headline workload (one round of all
+# blocks): rocprofv3 --pmc FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors from a
+# plain 256 MiB device copy), with the digest of the kernel's sources when the
+# counters were taken.  A kernel whose sources changed since reports null.
+PMC_TRAFFIC = {
+    "absorb": (360_095_442, "f1bf3ce30aa94d20"),
+    "attention": (587_912_448, "19d67061615e6f5a"),
+    "w_uv": (394_475_685, "ecf5271f60ef0594"),
+}
+
+
+def kernel_digest(stage: str) -> str:
+    import hashlib
+    csrc = os.path.join(ROOT, "speculative_decoding_draft_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[stage], "common.hpp", "kernels.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(stage: str, workload: str, chunk_blocks: int, n_blocks: int):
+    if stage not in PMC_TRAFFIC or not workload.startswith("headline") or chunk_blocks < n_blocks:
+        return None
+    nbytes, digest = PMC_TRAFFIC[stage]
+    return nbytes if kernel_digest(stage) == digest else None
 
 
 def useful_flop(anchors, keep, W, H, D, d_c, d_r, d_v, block=5) -> int:
@@ -263,7 +290,8 @@ def main():
         "chunks": {"chunk_blocks": chunk_blocks, "launches_per_kernel": live},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": MI355X_HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / MI355X_HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / MI355X_HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(dom, wl.name, chunk_blocks, wl.B * wl.N),
                      "avg_launch_us": round(avg_launch_us, 2),
                      "algorithmic_bytes_per_launch": round(avg_launch_bytes)},
         "cpu_baseline": None,
