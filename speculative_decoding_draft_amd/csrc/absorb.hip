@@ -14,8 +14,9 @@
 // Work split: a workgroup owns one head, one half of the 512 output dims and
 // a strided range of 128-row iterations.  The 192 x 256 weight slice stays in
 // LDS for the workgroup's lifetime; its transposed MFMA fragments are read
-// with ds_read_b64_tr_b16 once per wave into registers.  Each wave computes
-// 128 dims x 64 rows per iteration.
+// with ds_read_b64_tr_b16 one k-step ahead of their use.  Each wave computes
+// 128 dims x 64 rows per iteration and keeps a whole iteration of q^C rows in
+// flight.
 #include "kernels.hpp"
 
 namespace dspark {
@@ -70,25 +71,19 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
     };
     constexpr int kKs = kDc / 32;     // 6 k-steps per iteration
 
-    // The wave's A operand (its 128 x 192 slice of W_UK[h]^T) is the same in
-    // every iteration: read it out of LDS once, transposed, and keep it in
-    // registers (48 fragments, 192 VGPRs), so the main loop has no LDS reads.
-    // Fragment (ks, dt): rows d = wd*128 + dt*16 + l16, k-values
-    // c = ks*32 + g*8 + 0..7.
-    bf16x8 afr[kKs][8];
-#pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
+    // A operand (the wave's 128 x 192 slice of W_UK[h]^T): fragment (ks, dt)
+    // holds rows d = wd*128 + dt*16 + l16 and k-values c = ks*32 + g*8 + 0..7,
+    // read transposed out of the [c][d] LDS slice with ds_read_b64_tr_b16.
+    auto a_frag = [&](int ks, int dt) -> bf16x8 {
         const bf16* abase = wl + (ks * 32 + g * 8 + (l16 >> 2)) * kAbsStride + wd * 128 +
-                            (l16 & 3) * 4;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-            afr[ks][dt] = cat(lds_read_tr(abase + dt * 16), lds_read_tr(abase + 4 * kAbsStride + dt * 16));
-    }
+                            (l16 & 3) * 4 + dt * 16;
+        return cat(lds_read_tr(abase), lds_read_tr(abase + 4 * kAbsStride));
+    };
 
-    // B fragments: a ring of kPf k-steps; consuming k-step ks frees slot
-    // ks % kPf, which is refilled with k-step ks + kPf (of this iteration or,
-    // wrapping, of the next one)
-    constexpr int kPf = 3;            // divides kKs
+    // B fragments: a ring of kPf k-steps (one whole iteration); consuming
+    // k-step ks frees slot ks % kPf, which is refilled with the same k-step
+    // of the next iteration.
+    constexpr int kPf = kKs;
     bf16x8 ring[kPf][4];
     const bf16* qp[4];
     int blk_next[4];
@@ -106,7 +101,13 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
     // exact across iterations: past the last iteration the prefetches and
     // kept-list reads re-read clamped (valid) rows, and rows past the end are
     // computed on a duplicate of the last row and stored onto it (same value).
-    for (int it = rg; it < n_iter; it += kAbsRowGroups) {
+    // Results of one iteration are stored at the start of the next one, so
+    // that the loop header sees the same operations in flight from both sides
+    // and no wait for a prefetched row also waits for fresh stores.
+    bf16x8 pend[4][4];
+    bf16* pdst[4];
+    auto compute = [&](int it) {
+        __asm__ volatile("" ::: "memory");
         const int nxt = it + kAbsRowGroups;
         const bf16* np[4];
         for (int t = 0; t < 4; ++t) np[t] = q_ptr(row_of(nxt, t), blk_next[t]);
@@ -116,40 +117,60 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[dt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+        bf16x8 acur[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acur[dt] = a_frag(0, dt);
 #pragma unroll
         for (int ks = 0; ks < kKs; ++ks) {
             bf16x8 bq[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) bq[t] = ring[ks % kPf][t];
-            if (ks + kPf < kKs) {
+            for (int t = 0; t < 4; ++t) bq[t] = ring[ks][t];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) ring[ks % kPf][t] = gld16(qp[t] + (ks + kPf) * 32);
-            } else {
+            for (int t = 0; t < 4; ++t) ring[ks][t] = gld16(np[t] + ks * 32);
+            bf16x8 anext[8];
+            if (ks + 1 < kKs) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) ring[ks % kPf][t] = gld16(np[t] + (ks + kPf - kKs) * 32);
+                for (int dt = 0; dt < 8; ++dt) anext[dt] = a_frag(ks + 1, dt);
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) acc[dt][t] = mfma_16x16x32(afr[ks][dt], bq[t], acc[dt][t]);
+                for (int t = 0; t < 4; ++t) acc[dt][t] = mfma_16x16x32(acur[dt], bq[t], acc[dt][t]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < kKs) {
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) acur[dt] = anext[dt];
+            }
         }
-        for (int t = 0; t < 4; ++t) qp[t] = np[t];
         // lane holds dims dcol + 4g + i of tile pair (2p, 2p+1) for row it*128 + wr*64 + 16t + l16
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int r = row_of(it, t);
-            bf16* dst = q_abs + ((size_t)h * lat_rows + r) * kD + dh * 256 + wd * 128 + g * 8;
+            pdst[t] = q_abs + ((size_t)h * lat_rows + r) * kD + dh * 256 + wd * 128 + g * 8;
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const f32x4 a0 = acc[2 * pp][t], a1 = acc[2 * pp + 1][t];
                 bf16x8 v;
                 v[0] = (bf16)a0[0]; v[1] = (bf16)a0[1]; v[2] = (bf16)a0[2]; v[3] = (bf16)a0[3];
                 v[4] = (bf16)a1[0]; v[5] = (bf16)a1[1]; v[6] = (bf16)a1[2]; v[7] = (bf16)a1[3];
-                gst16(dst + pp * 32, v);
+                pend[t][pp] = v;
             }
         }
+    };
+    auto flush = [&]() {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) gst16(pdst[t] + pp * 32, pend[t][pp]);
+    };
+
+    compute(rg);
+    for (int it = rg + kAbsRowGroups; it < n_iter; it += kAbsRowGroups) {
+        flush();
+        compute(it);
     }
+    flush();
 }
 
 }  // namespace

@@ -42,10 +42,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
 
     constexpr int kThreads = WAVES * 64;
     constexpr int kGroups = 4 / WAVES;        // workgroups per block
-    const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int local = lid / kGroups;          // slot within the chunk
+    // live slots of this chunk; the grid covers the chunk's capacity, so
+    // spread the live ones evenly over the XCDs
     const int n_here = min(nslots, status[kStKeptCount] - slot0);
-    if (local >= n_here) return;
+    const int lid = xcd_balance(blockIdx.x, n_here * kGroups);
+    if (lid < 0) return;
+    const int local = lid / kGroups;          // slot within the chunk
     const int hg0 = (lid % kGroups) * WAVES;  // first 16-head group of this workgroup
     const int tid = threadIdx.x;
     const int blk = kept[slot0 + local];

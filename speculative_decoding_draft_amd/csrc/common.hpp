@@ -77,6 +77,18 @@ __device__ inline int xcd_remap(int id, int grid) {
     return (id % 8) * (grid / 8) + id / 8;
 }
 
+// The same for a grid of which only the first n_live logical ids have work
+// (the count is known on the device only): each XCD gets an equal share of
+// the live ids, again as a contiguous range.  Returns -1 for ids without
+// work.  Requires grid % 8 == 0 and n_live <= grid.
+__device__ inline int xcd_balance(int id, int n_live) {
+    const int share = (n_live + 7) / 8;
+    const int x = id % 8, k = id / 8;
+    if (k >= share) return -1;
+    const int lid = x * share + k;
+    return lid < n_live ? lid : -1;
+}
+
 // Global-memory accesses go through address-space-1 pointers so that they
 // compile to global_load/global_store: a generic (flat) access also counts
 // against lgkmcnt and turns every LDS wait into a wait for memory as well.

@@ -11,9 +11,9 @@
 // fragments are read in the same order, two 8-byte pieces per lane.
 //
 // Work split: a workgroup owns one head, one half of the 256 output dims
-// (a 128 x 512 weight slice resident in LDS) and a strided range of 256-row
-// iterations; each wave computes 128 dims x 64 rows, transposed (dims x rows),
-// and writes 4 consecutive output dims per lane.
+// (a 128 x 512 weight slice resident in LDS, rows permuted) and a strided
+// range of 256-row iterations; each wave computes 128 dims x 64 rows,
+// transposed (dims x rows), and writes 8 consecutive output dims per lane.
 #include "kernels.hpp"
 
 namespace dspark {
@@ -37,9 +37,16 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
     const int h = (lid >> 1) / kUvRowGroups;
     const int tid = threadIdx.x;
 
+    // LDS row R = 16 * vt + m of the slice holds output dim
+    // 32 * (vt / 2) + 8 * (m / 4) + 4 * (vt % 2) + m % 4, so that after the
+    // transposed MFMAs the lane with k-group g holds the 8 consecutive dims
+    // 32p + 8g .. 32p + 8g + 7 of tile pair p and writes them as one 16-byte
+    // store (4 lanes cover 64 contiguous bytes of a row).
     for (int e = tid; e < 128 * (kD / 8); e += 256) {
-        const int v = e / (kD / 8), ch = e % (kD / 8);
-        st16(&wl[v * kUvStride + ch * 8],
+        const int R = e / (kD / 8), ch = e % (kD / 8);
+        const int vt = R >> 4, m = R & 15;
+        const int v = 32 * (vt >> 1) + 8 * (m >> 2) + 4 * (vt & 1) + (m & 3);
+        st16(&wl[R * kUvStride + ch * 8],
              gld16(w_uv + ((size_t)h * kDv + vh * 128 + v) * kD + ch * 8));
     }
     __syncthreads();
@@ -56,8 +63,8 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
         return (r < rows) ? r : rows - 1;     // duplicate rows are computed, not stored
     };
     constexpr int kKs = kD / 32;     // 16 k-steps
-    // A fragment (ks, vt): rows v = vt*16 + l16 of the slice, k-values in the
-    // permuted o_lat order (dims 32ks + 4g + 0..3 and 32ks + 16 + 4g + 0..3)
+    // A fragment (ks, vt): LDS rows 16 vt + l16, k-values in the permuted
+    // o_lat order (dims 32ks + 4g + 0..3 and 32ks + 16 + 4g + 0..3)
     auto a_frag = [&](int ks, int vt) -> bf16x8 {
         const bf16* ap = &wl[(vt * 16 + l16) * kUvStride + ks * 32 + g * 4];
         return cat(ld8(ap), ld8(ap + 16));
@@ -71,9 +78,13 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
 #pragma unroll
         for (int t = 0; t < 4; ++t) ring[ks][t] = gld16(op[t] + ks * 32);
 
-    for (int it = rg; it < n_iter; it += kUvRowGroups) {
-        // keep the weight fragments in LDS: without this compiler barrier the
-        // loop-invariant LDS reads are hoisted into (and overflow) registers
+    // Results of one iteration are stored at the start of the next one: the
+    // loop then enters its header with the same kinds of memory operations in
+    // flight from both sides, and the stores have the whole prefetch distance
+    // to complete before any load issued after them is waited for.
+    bf16x8 pend[4][4];               // [row tile][tile pair]
+    bf16* pdst[4];
+    auto compute = [&](int it) {
         __asm__ volatile("" ::: "memory");
         const int nxt = it + kUvRowGroups;
         const bf16* np[4];
@@ -128,16 +139,32 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
             const int r = row_of(it, t);
             const int j = r % kBlock;
             const int b = blk[t] / N, n = blk[t] % N;
-            bf16* dst = out + (((size_t)b * L5 + (size_t)kBlock * n + j) * kH + h) * kDv +
-                        vh * 128 + g * 4;
+            pdst[t] = out + (((size_t)b * L5 + (size_t)kBlock * n + j) * kH + h) * kDv +
+                      vh * 128 + g * 8;
 #pragma unroll
-            for (int vt = 0; vt < 8; ++vt) {
-                const f32x4 a = acc[vt][t];
-                gst8(dst + vt * 16, bf16x4{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]});
+            for (int pp = 0; pp < 4; ++pp) {
+                const f32x4 a0 = acc[2 * pp][t], a1 = acc[2 * pp + 1][t];
+                bf16x8 v;
+                v[0] = (bf16)a0[0]; v[1] = (bf16)a0[1]; v[2] = (bf16)a0[2]; v[3] = (bf16)a0[3];
+                v[4] = (bf16)a1[0]; v[5] = (bf16)a1[1]; v[6] = (bf16)a1[2]; v[7] = (bf16)a1[3];
+                pend[t][pp] = v;
             }
         }
         for (int t = 0; t < 4; ++t) op[t] = np[t];
+    };
+    auto flush = [&]() {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) gst16(pdst[t] + pp * 32, pend[t][pp]);
+    };
+
+    compute(rg);
+    for (int it = rg + kUvRowGroups; it < n_iter; it += kUvRowGroups) {
+        flush();
+        compute(it);
     }
+    flush();
 }
 
 }  // namespace
