@@ -31,7 +31,7 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-SOURCES = ["index_rope.hip", "generic.hip", "absorb.hip", "attn.hip", "uv.hip", "api.hip",
+SOURCES = ["prep.hip", "generic.hip", "absorb.hip", "attn.hip", "uv.hip", "api.hip",
            "sampler.cpp"]
 
 

@@ -41,10 +41,20 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
     const int tid = threadIdx.x;
 
     // weight slice W_UK[h][0:192][dh*256 : dh*256+256]
-    for (int e = tid; e < kDc * 32; e += 256) {
-        const int c = e >> 5, ch = e & 31;
-        st16(&wl[c * kAbsStride + ch * 8],
-             gld16(w_uk + ((size_t)h * kDc + c) * kD + dh * 256 + ch * 8));
+    // one 512-byte weight row per half-wave instruction, straight into LDS
+    {
+        const int wave = tid >> 6, lane = tid & 63;
+        const int half = lane >> 5;
+        for (int c0 = 2 * wave; c0 < kDc; c0 += 8) {
+            const int c = c0 + half;
+            if (half == 0)
+                async_copy_16(w_uk + ((size_t)h * kDc + c) * kD + dh * 256 + lane * 8,
+                              &wl[c0 * kAbsStride]);
+            else
+                async_copy_16(w_uk + ((size_t)h * kDc + c) * kD + dh * 256 + (lane - 32) * 8,
+                              &wl[c0 * kAbsStride + kAbsStride - 256]);
+        }
+        __builtin_amdgcn_s_waitcnt(0);     // the LDS copies are counted by vmcnt
     }
     __syncthreads();
 

@@ -189,12 +189,10 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
 
     hipError_t e;
     if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    if ((e = launch_index(p, anchors, keep, ws, nullptr, s)) != hipSuccess)
-        return hip_fail(e, "index kernel launch");
-    if ((e = launch_rope_table(p, L.rope_rows, make_theta(d), ws, s)) != hipSuccess)
-        return hip_fail(e, "rope table launch");
-    if (fast && (e = launch_fill(p, in, ws, s)) != hipSuccess)
-        return hip_fail(e, "padding fill launch");
+    const RopeTheta theta = make_theta(d);
+    if ((e = launch_prep(p, anchors, keep, ws, nullptr, L.rope_rows, &theta,
+                         fast ? out : nullptr, s)) != hipSuccess)
+        return hip_fail(e, "index / RoPE table / fill launch");
     if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if (fast) {
         for (int c = 0; c < n_chunks; ++c) {
@@ -256,7 +254,8 @@ dspark_status dspark_build_index(const dspark_attn_desc* desc, const int32_t* an
     if (st != DSPARK_OK) return st;
     const Problem p = make_problem(*desc);
     const Workspace ws = carve(workspace, L);
-    hipError_t e = launch_index(p, anchors, keep, ws, index_out, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_prep(p, anchors, keep, ws, index_out, 0, nullptr, nullptr,
+                               static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "index kernel launch");
     return ok();
 }

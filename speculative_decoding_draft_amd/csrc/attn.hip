@@ -320,30 +320,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     }
 }
 
-// Rows of padding blocks are written as 0 and rows of kept blocks with a bad
-// anchor as NaN; kept blocks are left to the attention path.
-__global__ __launch_bounds__(256) void fill_kernel(const int4* __restrict__ idx,
-                                                   bf16* __restrict__ out, int L5, int N,
-                                                   int H, int dv) {
-    const int blk = blockIdx.x;
-    const int4 rec = idx[blk];
-    if (rec.w >= 0) return;
-    const bf16 fill = (rec.w == -1) ? (bf16)0.0f : (bf16)__builtin_nanf("");
-    bf16x8 fv;
-    for (int e = 0; e < 8; ++e) fv[e] = fill;
-    const int b = blk / N, n = blk % N;
-    bf16* base = out + ((size_t)b * L5 + (size_t)kBlock * n) * H * dv;
-    const int chunks = kBlock * H * dv / 8;   // the block's rows are contiguous
-    for (int e = threadIdx.x; e < chunks; e += 256) gst16(base + (size_t)e * 8, fv);
-}
-
 }  // namespace
-
-hipError_t launch_fill(const Problem& p, const Inputs& in, const Workspace& ws, hipStream_t s) {
-    hipLaunchKernelGGL(fill_kernel, dim3(p.B * p.N), dim3(256), 0, s, ws.idx, (bf16*)in.out, p.L5,
-                       p.N, p.H, p.dv);
-    return hipGetLastError();
-}
 
 hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
                        hipStream_t s) {

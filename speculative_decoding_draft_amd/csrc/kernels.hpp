@@ -34,10 +34,11 @@ struct Workspace {
     bf16* olat;
 };
 
-hipError_t launch_index(const Problem& p, const int32_t* anchors, const uint8_t* keep,
-                        const Workspace& ws, int32_t* index_copy, hipStream_t s);
-hipError_t launch_rope_table(const Problem& p, int rope_rows, const RopeTheta& th,
-                             const Workspace& ws, hipStream_t s);
+// Index build, and optionally (th != nullptr) the RoPE table and (out !=
+// nullptr) the rows of padding / invalid-anchor blocks, in one launch.
+hipError_t launch_prep(const Problem& p, const int32_t* anchors, const uint8_t* keep,
+                       const Workspace& ws, int32_t* index_copy, int rope_rows,
+                       const RopeTheta* th, void* out, hipStream_t s);
 hipError_t launch_generic(const Problem& p, bool bf16_io, const Inputs& in,
                           const Workspace& ws, hipStream_t s);
 size_t generic_lds_bytes(const Problem& p);
@@ -48,7 +49,6 @@ struct Chunk {
     int nslots;
 };
 
-hipError_t launch_fill(const Problem& p, const Inputs& in, const Workspace& ws, hipStream_t s);
 hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
                          hipStream_t s);
 hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,

@@ -42,12 +42,16 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
     // transposed MFMAs the lane with k-group g holds the 8 consecutive dims
     // 32p + 8g .. 32p + 8g + 7 of tile pair p and writes them as one 16-byte
     // store (4 lanes cover 64 contiguous bytes of a row).
-    for (int e = tid; e < 128 * (kD / 8); e += 256) {
-        const int R = e / (kD / 8), ch = e % (kD / 8);
-        const int vt = R >> 4, m = R & 15;
-        const int v = 32 * (vt >> 1) + 8 * (m >> 2) + 4 * (vt & 1) + (m & 3);
-        st16(&wl[R * kUvStride + ch * 8],
-             gld16(w_uv + ((size_t)h * kDv + vh * 128 + v) * kD + ch * 8));
+    // one 1 KB weight row per wave instruction, straight into LDS
+    {
+        const int wave = tid >> 6, lane = tid & 63;
+        for (int R = wave; R < 128; R += 4) {
+            const int vt = R >> 4, m = R & 15;
+            const int v = 32 * (vt >> 1) + 8 * (m >> 2) + 4 * (vt & 1) + (m & 3);
+            async_copy_16(w_uv + ((size_t)h * kDv + vh * 128 + v) * kD + lane * 8,
+                          &wl[R * kUvStride]);
+        }
+        __builtin_amdgcn_s_waitcnt(0);     // the LDS copies are counted by vmcnt
     }
     __syncthreads();
 
