@@ -131,6 +131,25 @@ __device__ inline void async_copy_16(const void* gsrc, void* lds_base) {
                                      16, 0, 0);
 }
 
+// Buffer resource over a whole tensor (raw, untyped access; reads past
+// num_bytes return 0) and a 16-byte copy through it into LDS.  Unlike the
+// global form, the buffer form is counted by vmcnt only, so LDS reads issued
+// after it keep exact lgkmcnt waits.  Offsets are 32-bit: tensors below 4 GiB.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t num_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)num_bytes,
+                                             0x00020000);
+}
+__device__ inline void buffer_copy_16(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte_offset,
+                                      void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(lds_base), 16, (int)byte_offset, 0, 0, 0);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]); the counters not named are left unconstrained.
+constexpr int kWaitVm0 = 0x0F70;     // vmcnt(0): this wave's global loads, stores, LDS DMA
+constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0): this wave's LDS operations
+
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane r*4 + c points at 4 consecutive 16-bit elements of "row" r
 // (r = 0..3); lane j of the group receives element j%4 of the chunk held by
