@@ -204,7 +204,24 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     }
 
     // ---- softmax per (query t, head): keys are spread over i, kt and the
-    // four lane groups g (lanes l, l^16, l^32, l^48)
+    // four lane groups g (lanes l, l^16, l^32, l^48).  Keys at or past nkeys
+    // are masked: inline for the last tile, and in a separate pass over the
+    // other tiles when the window is clamped (nkeys < 128).  exp2 is the
+    // hardware instruction: arguments are <= 0 and results below 2^-126
+    // (relative to the row maximum, which contributes 1) flush to 0.
+    if (nkeys < (kMaxKt - 1) * 16) {
+#pragma unroll
+        for (int kt = 0; kt < kMaxKt - 1; ++kt)
+#pragma unroll
+            for (int t = 0; t < kBlock; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (kt * 16 + g * 4 + i >= nkeys) st[kt][t][i] = -INFINITY;
+    }
+    auto score = [&](int kt, int t, int i) -> float {
+        if (kt == kMaxKt - 1 && kt * 16 + g * 4 + i >= nkeys) return -INFINITY;
+        return st[kt][t][i];
+    };
     const float c2 = scale * kLog2e;
     float inv[kBlock];
     bf16x4 pr[kMaxKt][kBlock];
@@ -212,15 +229,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     for (int t = 0; t < kBlock; ++t) {
         float m = -INFINITY;
 #pragma unroll
-        for (int kt = 0; kt < kMaxKt; ++kt) {
+        for (int kt = 0; kt < kMaxKt; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = kt * 16 + g * 4 + i;
-                const float x = (key < nkeys) ? st[kt][t][i] : -INFINITY;
-                st[kt][t][i] = x;
-                m = fmaxf(m, x);
-            }
-        }
+            for (int i = 0; i < 4; ++i) m = fmaxf(m, score(kt, t, i));
         m = fmaxf(m, __shfl_xor(m, 16));
         m = fmaxf(m, __shfl_xor(m, 32));
         const float mc = m * c2;
@@ -229,14 +240,14 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
         for (int kt = 0; kt < kMaxKt; ++kt) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = exp2f(fmaf(st[kt][t][i], c2, -mc));   // masked keys: 0
+                const float p = __builtin_amdgcn_exp2f(fmaf(score(kt, t, i), c2, -mc));
                 pr[kt][t][i] = (bf16)p;
                 sum += p;
             }
         }
         sum += __shfl_xor(sum, 16);
         sum += __shfl_xor(sum, 32);
-        inv[t] = 1.0f / sum;
+        inv[t] = __builtin_amdgcn_rcpf(sum);    // sum >= 1
     }
 
     // ---- o_lat^T = c^KV^T P^T in 64-dim chunks; lane holds dims
