@@ -12,7 +12,7 @@
 //
 // Work split: a workgroup owns one head, one half of the 256 output dims
 // (a 128 x 512 weight slice resident in LDS, rows permuted) and a strided
-// range of 256-row iterations; each wave computes 128 dims x 64 rows,
+// range of 128-row iterations; each wave computes 128 dims x 32 rows,
 // transposed (dims x rows), and writes 8 consecutive output dims per lane.
 #include "kernels.hpp"
 
@@ -22,7 +22,8 @@ namespace {
 
 constexpr int kUvRowGroups = 2;
 constexpr int kUvStride = kD + 8;        // bf16 per LDS weight row (1040 B)
-constexpr int kUvRowsPerIter = 256;
+constexpr int kUvTiles = 2;             // 16-row tiles per wave and iteration
+constexpr int kUvRowsPerIter = 4 * 16 * kUvTiles;
 
 __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
                                                  const bf16* __restrict__ o_lat,
@@ -51,19 +52,20 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
             async_copy_16(w_uv + ((size_t)h * kDv + vh * 128 + v) * kD + lane * 8,
                           &wl[R * kUvStride]);
         }
-        __builtin_amdgcn_s_waitcnt(0);     // the LDS copies are counted by vmcnt
     }
-    __syncthreads();
 
     // rows of this chunk (kept slots [slot0, slot0 + nslots))
     const int rows = kBlock * max(0, min(nslots, status[kStKeptCount] - slot0));
     const int n_iter = (rows + kUvRowsPerIter - 1) / kUvRowsPerIter;
     const int wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
-    if (rg >= n_iter) return;
+    if (rg >= n_iter) {
+        __builtin_amdgcn_s_waitcnt(0);     // no LDS copy left in flight
+        return;
+    }
 
     auto row_of = [&](int it, int t) {
-        const int r = it * kUvRowsPerIter + wave * 64 + t * 16 + l16;
+        const int r = it * kUvRowsPerIter + wave * 16 * kUvTiles + t * 16 + l16;
         return (r < rows) ? r : rows - 1;     // duplicate rows are computed, not stored
     };
     constexpr int kKs = kD / 32;     // 16 k-steps
@@ -74,34 +76,38 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
         return cat(ld8(ap), ld8(ap + 16));
     };
     constexpr int kPf = 8;           // prefetch distance in k-steps (divides kKs)
-    const bf16* op[4];
-    for (int t = 0; t < 4; ++t) op[t] = o_lat + ((size_t)h * lat_rows + row_of(rg, t)) * kD + g * 8;
-    bf16x8 ring[kPf][4];
+    const bf16* op[kUvTiles];
+    for (int t = 0; t < kUvTiles; ++t)
+        op[t] = o_lat + ((size_t)h * lat_rows + row_of(rg, t)) * kD + g * 8;
+    bf16x8 ring[kPf][kUvTiles];
 #pragma unroll
     for (int ks = 0; ks < kPf; ++ks)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) ring[ks][t] = gld16(op[t] + ks * 32);
+        for (int t = 0; t < kUvTiles; ++t) ring[ks][t] = gld16(op[t] + ks * 32);
+    // the weight copies and the first rows are in flight together
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
     // Results of one iteration are stored at the start of the next one: the
     // loop then enters its header with the same kinds of memory operations in
     // flight from both sides, and the stores have the whole prefetch distance
     // to complete before any load issued after them is waited for.
-    bf16x8 pend[4][4];               // [row tile][tile pair]
-    bf16* pdst[4];
+    bf16x8 pend[kUvTiles][4];        // [row tile][tile pair]
+    bf16* pdst[kUvTiles];
     auto compute = [&](int it) {
         __asm__ volatile("" ::: "memory");
         const int nxt = it + kUvRowGroups;
-        const bf16* np[4];
-        for (int t = 0; t < 4; ++t)
+        const bf16* np[kUvTiles];
+        for (int t = 0; t < kUvTiles; ++t)
             np[t] = o_lat + ((size_t)h * lat_rows + row_of(nxt, t)) * kD + g * 8;
-        int blk[4];
-        for (int t = 0; t < 4; ++t) blk[t] = kept[slot0 + row_of(it, t) / kBlock];
+        int blk[kUvTiles];
+        for (int t = 0; t < kUvTiles; ++t) blk[t] = kept[slot0 + row_of(it, t) / kBlock];
 
-        f32x4 acc[8][4];
+        f32x4 acc[8][kUvTiles];
 #pragma unroll
         for (int vt = 0; vt < 8; ++vt)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[vt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < kUvTiles; ++t) acc[vt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         // A fragments of k-step ks + 1 are read from LDS while the MFMAs of
         // k-step ks run; sched_barrier keeps the reads ahead of the MFMAs
         bf16x8 acur[8];
@@ -109,17 +115,17 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
         for (int vt = 0; vt < 8; ++vt) acur[vt] = a_frag(0, vt);
 #pragma unroll
         for (int ks = 0; ks < kKs; ++ks) {
-            bf16x8 bo[4];
+            bf16x8 bo[kUvTiles];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) bo[t] = ring[ks % kPf][t];
+            for (int t = 0; t < kUvTiles; ++t) bo[t] = ring[ks % kPf][t];
             // without a next iteration np points at the current rows: the
             // loads stay unconditional so that the wait counts stay exact
             if (ks + kPf < kKs) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) ring[ks % kPf][t] = gld16(op[t] + (ks + kPf) * 32);
+                for (int t = 0; t < kUvTiles; ++t) ring[ks % kPf][t] = gld16(op[t] + (ks + kPf) * 32);
             } else {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) ring[ks % kPf][t] = gld16(np[t] + (ks + kPf - kKs) * 32);
+                for (int t = 0; t < kUvTiles; ++t) ring[ks % kPf][t] = gld16(np[t] + (ks + kPf - kKs) * 32);
             }
             bf16x8 anext[8];
             if (ks + 1 < kKs) {
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
 #pragma unroll
             for (int vt = 0; vt < 8; ++vt)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) acc[vt][t] = mfma_16x16x32(acur[vt], bo[t], acc[vt][t]);
+                for (int t = 0; t < kUvTiles; ++t) acc[vt][t] = mfma_16x16x32(acur[vt], bo[t], acc[vt][t]);
             __builtin_amdgcn_sched_barrier(0);
             if (ks + 1 < kKs) {
 #pragma unroll
@@ -138,7 +144,7 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
             }
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < kUvTiles; ++t) {
             // rows past the end repeat the last row (same values, same place)
             const int r = row_of(it, t);
             const int j = r % kBlock;
@@ -154,11 +160,11 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
                 pend[t][pp] = v;
             }
         }
-        for (int t = 0; t < 4; ++t) op[t] = np[t];
+        for (int t = 0; t < kUvTiles; ++t) op[t] = np[t];
     };
     auto flush = [&]() {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < kUvTiles; ++t)
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) gst16(pdst[t] + pp * 32, pend[t][pp]);
     };
