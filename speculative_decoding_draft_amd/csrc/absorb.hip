@@ -27,10 +27,12 @@ namespace {
 
 constexpr int kAbsRowGroups = 2;        // workgroups per (head, dim half)
 constexpr int kAbsStride = 256 + 16;    // LDS row stride (bf16) of the weight slice
-constexpr int kAbsRowsPerIter = 128;
+constexpr int kAbsTiles = 4;                         // 16-row tiles per wave and iteration
+constexpr int kAbsRowsPerIter = 2 * 16 * kAbsTiles;  // two row groups per workgroup
+constexpr int kAbsCopyTiles = 2 * kAbsTiles / 4;     // tiles each wave copies per iteration
 
 constexpr int kAbsKs = kDc / 32;                        // 6 k-steps
-constexpr int kAbsFrags = (kAbsRowsPerIter / 16) * kAbsKs;  // 48 B fragments per iteration
+constexpr int kAbsFrags = (kAbsRowsPerIter / 16) * kAbsKs;  // B fragments per iteration
 
 __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_nope,
                                                      const bf16* __restrict__ w_uk,
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
     const int rows = kBlock * max(0, min(nslots, status[kStKeptCount] - slot0));
     const int n_iter = (rows + kAbsRowsPerIter - 1) / kAbsRowsPerIter;
     const int wd = wave & 1;      // 128-dim quarter inside the half
-    const int wr = wave >> 1;     // 64-row group inside the iteration
+    const int wr = wave >> 1;     // row group inside the iteration
     if (rg >= n_iter) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);   // no LDS copy left in flight
         return;
@@ -82,25 +84,27 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
         const int b = blk / N, n = blk % N;
         return q_nope + (((size_t)b * L5 + (size_t)kBlock * n + j) * kH + h) * kDc + g * 8;
     };
-    // Copy side: this wave copies row tiles 2*wave and 2*wave + 1 of an
+    // Copy side: this wave copies row tiles kAbsCopyTiles*wave + u of an
     // iteration (all k-steps).  Rows past the end copy the last row.
     auto copy_row = [&](int it, int u) {
-        return clamp_row(it * kAbsRowsPerIter + (2 * wave + u) * 16 + l16);
+        return clamp_row(it * kAbsRowsPerIter + (kAbsCopyTiles * wave + u) * 16 + l16);
     };
     const __amdgpu_buffer_rsrc_t q_rsrc = buffer_rsrc(q_nope, q_bytes);
     auto stage = [&](int it, const int* blk) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < kAbsCopyTiles; ++u) {
             const uint32_t off = (uint32_t)((q_ptr(copy_row(it, u), blk[u]) - q_nope) * 2);
 #pragma unroll
             for (int ks = 0; ks < kAbsKs; ++ks)
-                buffer_copy_16(q_rsrc, off + ks * 64, &qs[((2 * wave + u) * kAbsKs + ks) * 512]);
+                buffer_copy_16(q_rsrc, off + ks * 64,
+                               &qs[((kAbsCopyTiles * wave + u) * kAbsKs + ks) * 512]);
         }
     };
-    int cblk[2];
-    for (int u = 0; u < 2; ++u) cblk[u] = kept[slot0 + copy_row(rg, u) / kBlock];
+    int cblk[kAbsCopyTiles];
+    for (int u = 0; u < kAbsCopyTiles; ++u) cblk[u] = kept[slot0 + copy_row(rg, u) / kBlock];
     stage(rg, cblk);
-    for (int u = 0; u < 2; ++u) cblk[u] = kept[slot0 + copy_row(rg + kAbsRowGroups, u) / kBlock];
+    for (int u = 0; u < kAbsCopyTiles; ++u)
+        cblk[u] = kept[slot0 + copy_row(rg + kAbsRowGroups, u) / kBlock];
 
     // A operand (the wave's 128 x 192 slice of W_UK[h]^T): fragment (ks, dt)
     // holds rows d = wd*128 + dt*16 + l16 and k-values c = ks*32 + g*8 + 0..7,
@@ -116,34 +120,34 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
     // buffer, store the previous iteration's results, start the next copy,
     // then compute.  Everything waited for at the top of an iteration was
     // issued before the previous iteration's MFMAs.
-    bf16x8 pend[4][4];
-    bf16* pdst[4];
+    bf16x8 pend[kAbsTiles][4];
+    bf16* pdst[kAbsTiles];
     for (int it = rg; it < n_iter; it += kAbsRowGroups) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();
-        bf16x8 bq[kAbsKs][4];
+        bf16x8 bq[kAbsKs][kAbsTiles];
 #pragma unroll
         for (int ks = 0; ks < kAbsKs; ++ks)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                bq[ks][t] = ld16(&qs[((wr * 4 + t) * kAbsKs + ks) * 512 + lane * 8]);
+            for (int t = 0; t < kAbsTiles; ++t)
+                bq[ks][t] = ld16(&qs[((wr * kAbsTiles + t) * kAbsKs + ks) * 512 + lane * 8]);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __syncthreads();
         if (it != rg) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < kAbsTiles; ++t)
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) gst16(pdst[t] + pp * 32, pend[t][pp]);
         }
         stage(it + kAbsRowGroups, cblk);
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < kAbsCopyTiles; ++u)
             cblk[u] = kept[slot0 + copy_row(it + 2 * kAbsRowGroups, u) / kBlock];
 
-        f32x4 acc[8][4];
+        f32x4 acc[8][kAbsTiles];
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[dt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < kAbsTiles; ++t) acc[dt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         // A fragments of k-step ks + 1 are read in two halves, each while 16
         // MFMAs of k-step ks run, so that at most 8 LDS reads (16 counted
         // operations would overflow lgkmcnt) separate a fragment from its use.
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
 #pragma unroll
                 for (int dt = 4 * hf; dt < 4 * hf + 4; ++dt)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
+                    for (int t = 0; t < kAbsTiles; ++t)
                         acc[dt][t] = mfma_16x16x32(acur[dt], bq[ks][t], acc[dt][t]);
                 __builtin_amdgcn_sched_barrier(0);
                 if (ks + 1 < kAbsKs) {
@@ -174,11 +178,11 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
             }
         }
         // lane holds dims dcol + 4g + i of tile pair (2p, 2p+1) for row
-        // it*128 + wr*64 + 16t + l16; rows past the end repeat the last row
-        // (same values, same place)
+        // it*rows_per_iter + (wr*kAbsTiles + t)*16 + l16; rows past the end
+        // repeat the last row (same values, same place)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int r = clamp_row(it * kAbsRowsPerIter + wr * 64 + t * 16 + l16);
+        for (int t = 0; t < kAbsTiles; ++t) {
+            const int r = clamp_row(it * kAbsRowsPerIter + (wr * kAbsTiles + t) * 16 + l16);
             pdst[t] = q_abs + ((size_t)h * lat_rows + r) * kD + dh * 256 + wd * 128 + g * 8;
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
         }
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < kAbsTiles; ++t)
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) gst16(pdst[t] + pp * 32, pend[t][pp]);
     // the copy started by the last iteration is not used; let it land before
