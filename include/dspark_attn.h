@@ -72,8 +72,8 @@ typedef enum dspark_dtype {
  *   dtype     a dspark_dtype
  * Supported: any positive dims with d_rope even (generic kernels, fp32
  * arithmetic); the MFMA fast path is taken for dtype BF16 with H = 64,
- * D = 512, d_c = 192, d_r = 64, d_v = 256, window <= 128 and q_nope below
- * 4 GiB (B * 5N <= 174762). */
+ * D = 512, d_c = 192, d_r = 64, d_v = 256, window <= 128, and q_nope and
+ * ckv_ctx each below 4 GiB (B * 5N <= 174762, B * S < 4194304). */
 typedef struct dspark_attn_desc {
     int32_t B, S, N, block, window;
     int32_t n_heads, d_latent, d_nope, d_rope, d_v;

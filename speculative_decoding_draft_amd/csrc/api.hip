@@ -30,12 +30,15 @@ dspark_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// The MFMA path addresses q^C through a buffer resource with 32-bit byte
-// offsets, so q^C must stay below 4 GiB (B * 5N <= 174762 query rows).
+// The MFMA path addresses q^C and c^KV through buffer resources with 32-bit
+// byte offsets, so each must stay below 4 GiB (B * 5N <= 174762 query rows,
+// B * S < 4M context rows).
 bool is_fast_path(const dspark_attn_desc& d) {
     const size_t q_bytes = (size_t)d.B * kBlock * d.N * kH * kDc * 2;
+    const size_t ctx_bytes = (size_t)d.B * d.S * kD * 2;
     return d.dtype == DSPARK_BF16 && d.n_heads == kH && d.d_latent == kD && d.d_nope == kDc &&
-           d.d_rope == kDr && d.d_v == kDv && d.window <= kMaxWindow && q_bytes < (1ull << 32);
+           d.d_rope == kDr && d.d_v == kDv && d.window <= kMaxWindow &&
+           q_bytes < (1ull << 32) && ctx_bytes < (1ull << 32);
 }
 
 // Validates the descriptor; `empty` is set when there is nothing to compute.

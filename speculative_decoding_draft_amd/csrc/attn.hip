@@ -35,7 +35,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     const bf16* __restrict__ kr_blk, const int4* __restrict__ idx,
     const int32_t* __restrict__ kept, const int32_t* __restrict__ status,
     const float2* __restrict__ rope, const bf16* __restrict__ q_abs, bf16* __restrict__ o_lat,
-    int S, int N, int L5, int lat_rows, int slot0, int nslots, float scale) {
+    int S, int N, int L5, int lat_rows, int slot0, int nslots, float scale, uint32_t ctx_bytes,
+    uint32_t blk_bytes) {
     __shared__ __attribute__((aligned(16))) bf16 ckv_l[kMaxKeys * kCkvStride];
     __shared__ __attribute__((aligned(16))) bf16 kr_l[kMaxKeys * kKrStride];
     __shared__ float2 qcs[kBlock * (kDr / 2)];
@@ -56,62 +57,43 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     const int4 rec = idx[blk];
     const int ctx_lo = rec.x, ctx_len = rec.y, pos0 = rec.z;
     const int nkeys = ctx_len + kBlock;
-    const int wave = tid >> 6, lane = tid & 63;
+    // wave index as a scalar: the key staging below selects its source
+    // tensor per wave, which must be visible to the compiler as uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
     const int head = (hg0 + wave) * 16 + l16;   // this lane's head (B-operand column)
 
-    // ---- stage the keys: slot s < ctx_len is context row ctx_lo + s, the
-    // rest are the block's own positions.  c^KV rows go straight to LDS, one
-    // wave instruction per 1 KB row.
-    for (int s = wave; s < nkeys; s += WAVES) {
-        const bf16* src = (s < ctx_len) ? ckv_ctx + ((size_t)b * S + ctx_lo + s) * kD
-                                        : ckv_blk + (qrow0 + (s - ctx_len)) * kD;
-        async_copy_16(src + lane * 8, &ckv_l[s * kCkvStride]);
-    }
-
-    // Q fragments of the first k-steps are requested while the keys stream in
-    constexpr int kKs = (kD + kDr) / 32;           // 18 k-steps: 16 latent + 2 rope
-    constexpr int kPf = 3;                         // prefetch distance (k-steps)
-    const bf16* qa = q_abs + ((size_t)head * lat_rows + (size_t)kBlock * local) * kD + g * 8;
-    const bf16* qr = q_rope + (qrow0 * kH + head) * kDr + g * 8;
-    auto q_frag = [&](int ks, int t) -> bf16x8 {
-        return (ks < kD / 32) ? gld16(qa + t * kD + ks * 32)
-                              : gld16(qr + (size_t)t * kH * kDr + (ks - kD / 32) * 32);
-    };
-    bf16x8 qbuf[kPf][kBlock];
-#pragma unroll
-    for (int p = 0; p < kPf; ++p)
-#pragma unroll
-        for (int t = 0; t < kBlock; ++t) qbuf[p][t] = q_frag(p, t);
-
-    // k^R is rotated on the way in: batch the loads, then rotate and store
+    // k^R is rotated on the way in: batch the loads, then rotate and store.
+    // With four waves one batch covers every key; its loads are issued before
+    // the c^KV copies so that the rotation only waits for them (vmcnt retires
+    // in order) and overlaps the copies.
     constexpr int kKrChunks = kDr / 8;             // 16-byte chunks per k^R row
     constexpr int kKrBatch = 5;
     constexpr int kKrIters =                       // 1 with four waves
         (kMaxKeys * kKrChunks + kThreads * kKrBatch - 1) / (kThreads * kKrBatch);
-#pragma unroll
-    for (int bi = 0; bi < kKrIters; ++bi) {
+    bf16x8 xr[kKrBatch];
+    float4 cs01[kKrBatch], cs23[kKrBatch];
+    auto kr_load = [&](int bi) {
         const int base = bi * kThreads * kKrBatch;
-        bf16x8 xr[kKrBatch];
-        float4 cs01[kKrBatch], cs23[kKrBatch];
 #pragma unroll
         for (int u = 0; u < kKrBatch; ++u) {
             // unconditional (clamped) loads so that the batch is issued back to back
             int e = base + u * kThreads + tid;
             e = (e < nkeys * kKrChunks) ? e : nkeys * kKrChunks - 1;
-            {
-                const int s = e / kKrChunks, ch = e % kKrChunks;
-                const bool is_ctx = s < ctx_len;
-                const bf16* src = is_ctx ? kr_ctx + ((size_t)b * S + ctx_lo + s) * kDr
-                                         : kr_blk + (qrow0 + (s - ctx_len)) * kDr;
-                const int pos = is_ctx ? ctx_lo + s : pos0 + (s - ctx_len);
-                const float4* tb =
-                    reinterpret_cast<const float4*>(rope + (size_t)pos * (kDr / 2) + ch * 4);
-                xr[u] = gld16(src + ch * 8);
-                cs01[u] = tb[0];
-                cs23[u] = tb[1];
-            }
+            const int s = e / kKrChunks, ch = e % kKrChunks;
+            const bool is_ctx = s < ctx_len;
+            const bf16* src = is_ctx ? kr_ctx + ((size_t)b * S + ctx_lo + s) * kDr
+                                     : kr_blk + (qrow0 + (s - ctx_len)) * kDr;
+            const int pos = is_ctx ? ctx_lo + s : pos0 + (s - ctx_len);
+            const float4* tb =
+                reinterpret_cast<const float4*>(rope + (size_t)pos * (kDr / 2) + ch * 4);
+            xr[u] = gld16(src + ch * 8);
+            cs01[u] = tb[0];
+            cs23[u] = tb[1];
         }
+    };
+    auto kr_store = [&](int bi) {
+        const int base = bi * kThreads * kKrBatch;
 #pragma unroll
         for (int u = 0; u < kKrBatch; ++u) {
             const int e = base + u * kThreads + tid;
@@ -129,10 +111,70 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
                 st16(&kr_l[s * kKrStride + ch * 8], y);
             }
         }
+    };
+    // cos/sin of the block's 5 query positions (q^R is rotated in registers)
+    constexpr int kQcsPer = (kBlock * (kDr / 2) + kThreads - 1) / kThreads;
+    float2 qcs_r[kQcsPer];
+#pragma unroll
+    for (int u = 0; u < kQcsPer; ++u) {
+        const int e = min(tid + u * kThreads, kBlock * (kDr / 2) - 1);
+        qcs_r[u] = rope[(size_t)(pos0 + e / (kDr / 2)) * (kDr / 2) + e % (kDr / 2)];
     }
-    for (int e = tid; e < kBlock * (kDr / 2); e += kThreads)
-        qcs[e] = rope[(size_t)(pos0 + e / (kDr / 2)) * (kDr / 2) + e % (kDr / 2)];
-    __builtin_amdgcn_s_waitcnt(0);     // the LDS copies are counted by vmcnt
+    if constexpr (kKrIters == 1) kr_load(0);
+
+    // ---- stage the keys: slot s < ctx_len is context row ctx_lo + s, the
+    // rest are the block's own positions.  c^KV rows go straight to LDS, one
+    // wave instruction per 1 KB row.
+    // A fixed number of copies per wave (slots past the last key receive a
+    // copy of the last key and are never read) keeps the wait counts after
+    // this loop exact.  The buffer form of the copy is counted by vmcnt only.
+    static_assert(kMaxKeys % WAVES == 0, "slots per wave");
+    const __amdgpu_buffer_rsrc_t ctx_rsrc = buffer_rsrc(ckv_ctx, ctx_bytes);
+    const __amdgpu_buffer_rsrc_t blk_rsrc = buffer_rsrc(ckv_blk, blk_bytes);
+#pragma unroll
+    for (int i = 0; i < kMaxKeys / WAVES; ++i) {
+        const int slot = wave + i * WAVES;
+        const int s = (slot < nkeys) ? slot : nkeys - 1;
+        const bool is_ctx = s < ctx_len;
+        const uint32_t row =
+            is_ctx ? (uint32_t)(b * S + ctx_lo + s) : (uint32_t)(qrow0 + (s - ctx_len));
+        buffer_copy_16(is_ctx ? ctx_rsrc : blk_rsrc, (row * kD + lane * 8) * 2,
+                       &ckv_l[slot * kCkvStride]);
+    }
+
+    // Q fragments of the first k-steps are requested while the keys stream in
+    constexpr int kKs = (kD + kDr) / 32;           // 18 k-steps: 16 latent + 2 rope
+    constexpr int kPf = 3;                         // prefetch distance (k-steps)
+    const bf16* qa = q_abs + ((size_t)head * lat_rows + (size_t)kBlock * local) * kD + g * 8;
+    const bf16* qr = q_rope + (qrow0 * kH + head) * kDr + g * 8;
+    auto q_frag = [&](int ks, int t) -> bf16x8 {
+        return (ks < kD / 32) ? gld16(qa + t * kD + ks * 32)
+                              : gld16(qr + (size_t)t * kH * kDr + (ks - kD / 32) * 32);
+    };
+    bf16x8 qbuf[kPf][kBlock];
+#pragma unroll
+    for (int p = 0; p < kPf; ++p)
+#pragma unroll
+        for (int t = 0; t < kBlock; ++t) qbuf[p][t] = q_frag(p, t);
+
+    if constexpr (kKrIters == 1) {
+        kr_store(0);
+    } else {
+#pragma unroll
+        for (int bi = 0; bi < kKrIters; ++bi) {
+            kr_load(bi);
+            kr_store(bi);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kQcsPer; ++u) {
+        const int e = tid + u * kThreads;
+        if (e < kBlock * (kDr / 2)) qcs[e] = qcs_r[u];
+    }
+    // the c^KV copies are counted by vmcnt; only the q fragment prefetches
+    // (kPf * kBlock loads, issued after them) may still be in flight
+    static_assert(kPf * kBlock == 15, "wait count below");
+    __builtin_amdgcn_s_waitcnt(kWaitVm15Lgkm0);
     __syncthreads();
 
     // ---- scores, transposed: St[kt][t] = keys (16 kt + 4g + i) x head, query t
@@ -337,6 +379,8 @@ hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, 
                        hipStream_t s) {
     // few blocks: split the 64 heads over four single-wave workgroups so that
     // more compute units take part
+    const uint32_t ctx_bytes = (uint32_t)((size_t)p.B * p.S * kD * sizeof(bf16));
+    const uint32_t blk_bytes = (uint32_t)((size_t)p.B * p.L5 * kD * sizeof(bf16));
     const bool split = c.nslots < 160;
     const int groups = split ? 4 : 1;
     int grid = c.nslots * groups;
@@ -346,13 +390,13 @@ hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, 
                            (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
                            (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.idx, ws.kept,
                            ws.status, ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5, p.lat_rows,
-                           c.slot0, c.nslots, p.scale);
+                           c.slot0, c.nslots, p.scale, ctx_bytes, blk_bytes);
     } else {
         hipLaunchKernelGGL(attn_kernel<4>, dim3(grid), dim3(256), 0, s, (const bf16*)in.q_rope,
                            (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
                            (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.idx, ws.kept,
                            ws.status, ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5, p.lat_rows,
-                           c.slot0, c.nslots, p.scale);
+                           c.slot0, c.nslots, p.scale, ctx_bytes, blk_bytes);
     }
     return hipGetLastError();
 }

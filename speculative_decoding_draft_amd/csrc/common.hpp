@@ -149,6 +149,7 @@ __device__ inline void buffer_copy_16(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte
 // [6:4], lgkmcnt [11:8]); the counters not named are left unconstrained.
 constexpr int kWaitVm0 = 0x0F70;     // vmcnt(0): this wave's global loads, stores, LDS DMA
 constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0): this wave's LDS operations
+constexpr int kWaitVm15Lgkm0 = 0x007F;  // vmcnt(15) and lgkmcnt(0)
 
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane r*4 + c points at 4 consecutive 16-bit elements of "row" r
