@@ -8,6 +8,13 @@ default workload is the S=32768, N=1024 headline configuration (25% padding
 blocks, 5% clamped windows, synthetic N(0,1) activations and N(0,1/512)
 weights).  Prints one JSON line.
 
+Timing: warm-up steps (at least W and at least 100 ms of them: the clocks
+take tens of milliseconds to settle), then K timed steps between two
+synchronisations.
+Per-kernel durations come from HIP events that the library records on the
+launch stream between its kernels; they are recorded on every 10th timed step
+only (--event-every), since each event orders the kernels around it.
+
 Useful FLOP count only what the absorbed method must compute for kept blocks
 and visible keys: per kept block 5*H*(2*d_c*D + 2*(D+d_r)*v + 2*D*v + 2*D*d_v)
 with v = min(A, W-1) + 5.
@@ -35,9 +42,9 @@ KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.h
 # plain 256 MiB device copy), with the digest of the kernel's sources when the
 # counters were taken.  A kernel whose sources changed since reports null.
 PMC_TRAFFIC = {
-    "absorb": (360_095_442, "f1bf3ce30aa94d20"),
-    "attention": (587_912_448, "19d67061615e6f5a"),
-    "w_uv": (394_475_685, "ecf5271f60ef0594"),
+    "absorb": (358_861_632, "d38077a144262d1f"),
+    "attention": (587_350_857, "c63690ea55af4614"),
+    "w_uv": (394_515_483, "5189f21b2c607300"),
 }
 
 
@@ -160,10 +167,14 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--min-warmup-ms", type=float, default=100.0,
+                    help="keep warming up until this much time has passed")
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--chunk-blocks", type=int, default=0,
                     help="kept blocks per kernel round (0: the library default)")
+    ap.add_argument("--event-every", type=int, default=10,
+                    help="record per-kernel stage events on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
@@ -213,32 +224,48 @@ def main():
     n_chunks, chunk_blocks, n_ev = sd.attn_plan(desc, chunk_blocks=args.chunk_blocks)
     # chunks past the number of kept blocks exit at once; time only real ones
     live = min(n_chunks, -(-int(keep.sum()) // chunk_blocks))
-    ev = hip.create(K * L * n_ev)
+    calls = [sd.BoundFwd(desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"],
+                         t["kr_blk"], t["w_uk"], t["w_uv"], a_dev, k_dev, outs[l], ws, stream=sptr,
+                         chunk_blocks=args.chunk_blocks, n_stage_events=n_ev)
+             for l, t in enumerate(tensors)]
+    # Stage events are recorded on every `event_every`-th timed step only:
+    # each event is a barrier between kernels, so recording them on every
+    # step would lengthen the steps being timed.
+    ev_steps = list(range(0, K, max(1, args.event_every)))
+    ev = hip.create(len(ev_steps) * L * n_ev)
 
-    def step(i, events=True):
-        for l in range(L):
-            t = tensors[l]
-            se = ev[(i * L + l) * n_ev:(i * L + l + 1) * n_ev] if events else None
-            sd.attn_fwd(desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"],
-                        t["kr_blk"], t["w_uk"], t["w_uv"], a_dev, k_dev, outs[l], ws,
-                        stream=sptr, stage_events=se, chunk_blocks=args.chunk_blocks)
-
-    for _ in range(args.warmup):
-        step(0, events=False)
+    # warm-up: at least W steps and at least --min-warmup-ms of them, so that
+    # the timed steps run at the clocks the GPU settles at under this load
+    warm_steps, warm_t0 = 0, time.perf_counter()
+    while (warm_steps < args.warmup or
+           (time.perf_counter() - warm_t0) * 1e3 < args.min_warmup_ms):
+        for call in calls:
+            call()
+        warm_steps += 1
+        if warm_steps % 10 == 0:
+            torch.cuda.synchronize()
     st, fb = sd.read_device_status(ws, stream=sptr)
     assert st == 0, sd.last_error()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e_i = 0
     for i in range(K):
-        step(i)
+        if e_i < len(ev_steps) and ev_steps[e_i] == i:
+            for l, call in enumerate(calls):
+                call.with_events(ev[(e_i * L + l) * n_ev:(e_i * L + l + 1) * n_ev])
+            e_i += 1
+        else:
+            for call in calls:
+                call()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # per call: stage time summed over its chunks; per launch: each chunk's
+    # per instrumented call: stage time summed over its chunks; per launch:
+    # each chunk's
     launch_us = {s: [[] for _ in range(live)] for s in STAGES[1:]}
     per_stage = {s: [] for s in STAGES}
     call_ms = []
-    for i in range(K * L):
+    for i in range(len(ev_steps) * L):
         e = ev[i * n_ev:(i + 1) * n_ev]
         call_ms.append(hip.elapsed_ms(e[0], e[-1]))
         per_stage[STAGES[0]].append(hip.elapsed_ms(e[0], e[1]))
@@ -272,7 +299,8 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warm_steps,
+        "warmup_requested": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -286,6 +314,7 @@ def main():
         "frac_of_bf16_peak": round(value / MI355X_BF16_PEAK_TFLOPS, 4),
         "useful_gflop_per_step": round(flop / 1e9, 3),
         "gpu_event_us_per_call": round(float(np.mean(call_ms)) * 1e3, 2),
+        "event_steps": len(ev_steps),
         "stage_us": {s: round(v, 2) for s, v in stage_avg_us.items()},
         "chunks": {"chunk_blocks": chunk_blocks, "launches_per_kernel": live},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),

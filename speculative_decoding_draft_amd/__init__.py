@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     DSPARK_EWORKSPACE,
     DSPARK_F32,
     DSPARK_OK,
+    BoundFwd,
     EXPORTS,
     LIB_PATH,
     Desc,

@@ -170,6 +170,45 @@ def attn_fwd(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk,
     _check(lib.dspark_attn_fwd_ex(*args, ctypes.byref(opts)))
 
 
+class BoundFwd:
+    """dspark_attn_fwd with its arguments marshalled once, for callers that
+    issue the same call many times (a training loop, a benchmark).  The
+    tensors must stay alive and in place while the object is used."""
+
+    def __init__(self, desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
+                 anchors, keep, out, workspace, stream=None, chunk_blocks: int = 0,
+                 n_stage_events: int = 0):
+        self._desc = desc
+        ws_bytes = workspace.numel() * workspace.element_size()
+        self._args = (ctypes.byref(desc),) + tuple(
+            ctypes.c_void_p(_ptr(t)) for t in (q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk,
+                                                w_uk, w_uv, anchors, keep, out, workspace)) + (
+            ctypes.c_size_t(ws_bytes), ctypes.c_void_p(_stream(stream)))
+        self._plain = lib.dspark_attn_fwd
+        self._ex = lib.dspark_attn_fwd_ex
+        self._opts, _ = _opts(None, False, chunk_blocks)
+        self._opts_ref = ctypes.byref(self._opts)
+        self._events = (ctypes.c_void_p * max(1, n_stage_events))()
+        self._opts_ev = Opts()
+        self._opts_ev.stage_events = ctypes.cast(self._events, ctypes.POINTER(ctypes.c_void_p))
+        self._opts_ev.n_stage_events = n_stage_events
+        self._opts_ev.chunk_blocks = int(chunk_blocks)
+        self._opts_ev_ref = ctypes.byref(self._opts_ev)
+
+    def __call__(self) -> None:
+        st = self._ex(*self._args, self._opts_ref)
+        if st != DSPARK_OK:
+            _check(st)
+
+    def with_events(self, events: Sequence[int]) -> None:
+        """The same call, recording stage events (see dspark_attn_opts)."""
+        for i, e in enumerate(events):
+            self._events[i] = e
+        st = self._ex(*self._args, self._opts_ev_ref)
+        if st != DSPARK_OK:
+            _check(st)
+
+
 def build_index(desc: Desc, anchors, keep, index_out, workspace, stream=None) -> None:
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib.dspark_build_index(ctypes.byref(desc), _ptr(anchors), _ptr(keep), _ptr(index_out),

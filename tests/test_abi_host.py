@@ -116,6 +116,18 @@ def test_empty_problem_is_a_no_op():
     assert sd._lib.lib.dspark_attn_fwd(ctypes.byref(d), *([None] * 12), 0, None) == sd.DSPARK_OK
 
 
+def test_mfma_path_needs_32bit_offsets():
+    """The MFMA path addresses q_nope and ckv_ctx with 32-bit byte offsets:
+    beyond 4 GiB the generic path (no latent buffers) is planned instead."""
+    fast = glm_desc(S=4096, N=64)
+    assert sd.attn_plan(fast)[0] == 1
+    big_ctx = glm_desc(S=4 * 2**20, N=64)          # ckv_ctx = 4 GiB
+    assert sd.attn_plan(big_ctx) == (0, 0, 3)
+    assert sd.workspace_size(big_ctx) < sd.workspace_size(glm_desc(S=4 * 2**20 - 8, N=64))
+    big_q = glm_desc(B=2, S=256, N=20000)          # q_nope = 2 * 100000 rows * 24 KiB > 4 GiB
+    assert sd.attn_plan(big_q) == (0, 0, 3)
+
+
 def test_launch_plan():
     d = glm_desc(B=2, N=1000)
     assert sd.attn_plan(d) == (1, 2000, 5)

@@ -188,6 +188,24 @@ def test_stage_events_are_recorded_in_order(sd):
             what="with stage events")
 
 
+def test_bound_call_matches_plain_call(sd):
+    """BoundFwd (arguments marshalled once) runs the same forward."""
+    import torch
+    wl = wk.scaled(4, S=2048, N=96)
+    r = GpuRun(wl, 0, wl.anchors, wl.keep)
+    ref = r.run().result()
+    r.out.fill_(float("nan"))
+    t = r.t
+    n_chunks, chunk, n_ev = sd.attn_plan(r.desc, chunk_blocks=32)
+    call = sd.BoundFwd(r.desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"],
+                       t["kr_blk"], t["w_uk"], t["w_uv"], r.anchors, r.keep, r.out, r.ws,
+                       chunk_blocks=32, n_stage_events=n_ev)
+    call()
+    got = r.result()
+    assert np.array_equal(np.nan_to_num(got, nan=7.0), np.nan_to_num(ref, nan=7.0))
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("W", [1, 2, 16, 127, 128])
 def test_window_sizes_on_mfma_path(sd, W):
     dims = dict(wk.GLM_DIMS, W=W)
