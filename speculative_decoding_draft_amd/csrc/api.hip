@@ -96,6 +96,7 @@ Workspace carve(void* base, const WsLayout& L) {
     Workspace w;
     w.idx = reinterpret_cast<int4*>(c + L.idx);
     w.kept = reinterpret_cast<int32_t*>(c + L.kept);
+    w.srec = reinterpret_cast<int4*>(c + L.srec);
     w.status = reinterpret_cast<int32_t*>(c + L.status);
     w.rope = reinterpret_cast<float2*>(c + L.rope);
     w.qabs = L.qabs ? reinterpret_cast<bf16*>(c + L.qabs) : nullptr;
@@ -255,7 +256,8 @@ dspark_status dspark_build_index(const dspark_attn_desc* desc, const int32_t* an
     if (!aligned16(anchors) || !aligned16(index_out))
         return fail(DSPARK_EINVAL, "anchors and index_out must be 16-byte aligned");
     const WsLayout L = ws_layout(*desc, is_fast_path(*desc));
-    // the index build touches only the status, index and kept-list areas
+    // the index build touches only the status, index, kept-list and slot
+    // record areas
     st = check_workspace(workspace, ws_bytes, L.rope);
     if (st != DSPARK_OK) return st;
     const Problem p = make_problem(*desc);

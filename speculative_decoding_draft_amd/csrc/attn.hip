@@ -32,8 +32,8 @@ template <int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     const bf16* __restrict__ q_rope, const bf16* __restrict__ ckv_ctx,
     const bf16* __restrict__ kr_ctx, const bf16* __restrict__ ckv_blk,
-    const bf16* __restrict__ kr_blk, const int4* __restrict__ idx,
-    const int32_t* __restrict__ kept, const int32_t* __restrict__ status,
+    const bf16* __restrict__ kr_blk, const int4* __restrict__ srec,
+    const int32_t* __restrict__ status,
     const float2* __restrict__ rope, const bf16* __restrict__ q_abs, bf16* __restrict__ o_lat,
     int S, int N, int L5, int lat_rows, int slot0, int nslots, float scale, uint32_t ctx_bytes,
     uint32_t blk_bytes) {
@@ -51,17 +51,30 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     const int local = lid / kGroups;          // slot within the chunk
     const int hg0 = (lid % kGroups) * WAVES;  // first 16-head group of this workgroup
     const int tid = threadIdx.x;
-    const int blk = kept[slot0 + local];
-    const int b = blk / N, n = blk % N;
-    const size_t qrow0 = (size_t)b * L5 + (size_t)kBlock * n;
-    const int4 rec = idx[blk];
-    const int ctx_lo = rec.x, ctx_len = rec.y, pos0 = rec.z;
-    const int nkeys = ctx_len + kBlock;
     // wave index as a scalar: the key staging below selects its source
     // tensor per wave, which must be visible to the compiler as uniform
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
     const int head = (hg0 + wave) * 16 + l16;   // this lane's head (B-operand column)
+
+    // Q fragments of the first k-steps (all latent) are requested first:
+    // they depend on the slot only
+    constexpr int kKs = (kD + kDr) / 32;           // 18 k-steps: 16 latent + 2 rope
+    constexpr int kPf = 3;                         // prefetch distance (k-steps)
+    static_assert(kPf <= kD / 32, "prefetched k-steps are latent ones");
+    const bf16* qa = q_abs + ((size_t)head * lat_rows + (size_t)kBlock * local) * kD + g * 8;
+    bf16x8 qbuf[kPf][kBlock];
+#pragma unroll
+    for (int p = 0; p < kPf; ++p)
+#pragma unroll
+        for (int t = 0; t < kBlock; ++t) qbuf[p][t] = gld16(qa + t * kD + p * 32);
+
+    const int4 rec = srec[slot0 + local];      // {ctx_lo, ctx_len, pos0, block}
+    const int blk = rec.w;
+    const int b = blk / N, n = blk % N;
+    const size_t qrow0 = (size_t)b * L5 + (size_t)kBlock * n;
+    const int ctx_lo = rec.x, ctx_len = rec.y, pos0 = rec.z;
+    const int nkeys = ctx_len + kBlock;
 
     // k^R is rotated on the way in: batch the loads, then rotate and store.
     // With four waves one batch covers every key; its loads are issued before
@@ -142,20 +155,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
                        &ckv_l[slot * kCkvStride]);
     }
 
-    // Q fragments of the first k-steps are requested while the keys stream in
-    constexpr int kKs = (kD + kDr) / 32;           // 18 k-steps: 16 latent + 2 rope
-    constexpr int kPf = 3;                         // prefetch distance (k-steps)
-    const bf16* qa = q_abs + ((size_t)head * lat_rows + (size_t)kBlock * local) * kD + g * 8;
     const bf16* qr = q_rope + (qrow0 * kH + head) * kDr + g * 8;
     auto q_frag = [&](int ks, int t) -> bf16x8 {
         return (ks < kD / 32) ? gld16(qa + t * kD + ks * 32)
                               : gld16(qr + (size_t)t * kH * kDr + (ks - kD / 32) * 32);
     };
-    bf16x8 qbuf[kPf][kBlock];
-#pragma unroll
-    for (int p = 0; p < kPf; ++p)
-#pragma unroll
-        for (int t = 0; t < kBlock; ++t) qbuf[p][t] = q_frag(p, t);
 
     if constexpr (kKrIters == 1) {
         kr_store(0);
@@ -171,10 +175,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
         const int e = tid + u * kThreads;
         if (e < kBlock * (kDr / 2)) qcs[e] = qcs_r[u];
     }
-    // the c^KV copies are counted by vmcnt; only the q fragment prefetches
-    // (kPf * kBlock loads, issued after them) may still be in flight
-    static_assert(kPf * kBlock == 15, "wait count below");
-    __builtin_amdgcn_s_waitcnt(kWaitVm15Lgkm0);
+    // the c^KV copies (the last memory operations issued) are counted by vmcnt
+    __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
     __syncthreads();
 
     // ---- scores, transposed: St[kt][t] = keys (16 kt + 4g + i) x head, query t
@@ -388,13 +390,13 @@ hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, 
     if (split) {
         hipLaunchKernelGGL(attn_kernel<1>, dim3(grid), dim3(64), 0, s, (const bf16*)in.q_rope,
                            (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
-                           (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.idx, ws.kept,
+                           (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.srec,
                            ws.status, ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5, p.lat_rows,
                            c.slot0, c.nslots, p.scale, ctx_bytes, blk_bytes);
     } else {
         hipLaunchKernelGGL(attn_kernel<4>, dim3(grid), dim3(256), 0, s, (const bf16*)in.q_rope,
                            (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
-                           (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.idx, ws.kept,
+                           (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.srec,
                            ws.status, ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5, p.lat_rows,
                            c.slot0, c.nslots, p.scale, ctx_bytes, blk_bytes);
     }

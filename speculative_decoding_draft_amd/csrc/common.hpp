@@ -38,6 +38,7 @@ struct WsLayout {
     size_t status = 0;   // int32 [kStWords]
     size_t idx = 0;      // int4 [B*N]       {ctx_lo, ctx_len, pos0, slot}
     size_t kept = 0;     // int32 [B*N]      slot -> b*N + n
+    size_t srec = 0;     // int4 [B*N]       slot -> {ctx_lo, ctx_len, pos0, b*N + n}
     size_t rope = 0;     // float2 [S + 8][d_r/2]  (cos, sin)
     size_t qabs = 0;     // bf16 [H][5*B*N][D]  (MFMA path)
     size_t olat = 0;     // bf16 [H][5*B*N][D]  (MFMA path)
@@ -54,6 +55,7 @@ inline WsLayout ws_layout(const dspark_attn_desc& d, bool mfma) {
     w.status = off; off = align256(off + kStWords * 4);
     w.idx = off;    off = align256(off + blocks * 16);
     w.kept = off;   off = align256(off + blocks * 4);
+    w.srec = off;   off = align256(off + blocks * 16);
     w.rope_rows = d.S + 8;
     w.rope = off;   off = align256(off + size_t(w.rope_rows) * size_t(d.d_rope / 2) * 8);
     if (mfma) {
@@ -149,7 +151,7 @@ __device__ inline void buffer_copy_16(__amdgpu_buffer_rsrc_t rsrc, uint32_t byte
 // [6:4], lgkmcnt [11:8]); the counters not named are left unconstrained.
 constexpr int kWaitVm0 = 0x0F70;     // vmcnt(0): this wave's global loads, stores, LDS DMA
 constexpr int kWaitLgkm0 = 0xC07F;   // lgkmcnt(0): this wave's LDS operations
-constexpr int kWaitVm15Lgkm0 = 0x007F;  // vmcnt(15) and lgkmcnt(0)
+constexpr int kWaitVm0Lgkm0 = 0x0070;   // vmcnt(0) and lgkmcnt(0)
 
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane r*4 + c points at 4 consecutive 16-bit elements of "row" r

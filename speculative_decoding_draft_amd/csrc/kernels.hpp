@@ -28,6 +28,7 @@ struct Inputs {
 struct Workspace {
     int4* idx;
     int32_t* kept;
+    int4* srec;
     int32_t* status;
     float2* rope;
     bf16* qabs;

@@ -33,8 +33,8 @@ constexpr int kIndexThreads = kPrepThreads;
 // ranks of the kept blocks in (b, n) order.
 __device__ void build_index(int total, int S, int W, const int32_t* __restrict__ anchors,
                             const uint8_t* __restrict__ keep, int4* __restrict__ idx,
-                            int32_t* __restrict__ kept, int32_t* __restrict__ status,
-                            int4* __restrict__ idx_copy) {
+                            int32_t* __restrict__ kept, int4* __restrict__ srec,
+                            int32_t* __restrict__ status, int4* __restrict__ idx_copy) {
     __shared__ int wave_count[kIndexThreads / 64];
     __shared__ int first_bad_sh;
     const int tid = threadIdx.x;
@@ -74,6 +74,7 @@ __device__ void build_index(int total, int S, int W, const int32_t* __restrict__
         if (state == 1) {
             rec.w = before + before_in_wave;
             kept[rec.w] = i;
+            srec[rec.w] = make_int4(rec.x, rec.y, rec.z, i);
         }
         if (i < total) {
             idx[i] = rec;
@@ -133,11 +134,12 @@ __device__ void fill_block(int blk, int S, int N, int L5, int H, int dv,
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     int total, int S, int W, const int32_t* __restrict__ anchors,
     const uint8_t* __restrict__ keep, int4* __restrict__ idx, int32_t* __restrict__ kept,
-    int32_t* __restrict__ status, int4* __restrict__ idx_copy, long long rope_n, int pairs,
+    int4* __restrict__ srec, int32_t* __restrict__ status, int4* __restrict__ idx_copy,
+    long long rope_n, int pairs,
     RopeTheta th, float2* __restrict__ table, int rope_wgs, bf16* __restrict__ out, int N,
     int L5, int H, int dv) {
     if (blockIdx.x == 0) {
-        build_index(total, S, W, anchors, keep, idx, kept, status, idx_copy);
+        build_index(total, S, W, anchors, keep, idx, kept, srec, status, idx_copy);
         return;
     }
     const int r = blockIdx.x - 1;
@@ -161,7 +163,7 @@ hipError_t launch_prep(const Problem& p, const int32_t* anchors, const uint8_t* 
     const int fill_wgs = out ? p.B * p.N : 0;
     RopeTheta none{};
     hipLaunchKernelGGL(prep_kernel, dim3(1 + rope_wgs + fill_wgs), dim3(kPrepThreads), 0, s,
-                       p.B * p.N, p.S, p.W, anchors, keep, ws.idx, ws.kept, ws.status,
+                       p.B * p.N, p.S, p.W, anchors, keep, ws.idx, ws.kept, ws.srec, ws.status,
                        reinterpret_cast<int4*>(index_copy), rope_n, pairs > 0 ? pairs : 1,
                        th ? *th : none, ws.rope, rope_wgs, static_cast<bf16*>(out), p.N, p.L5,
                        p.H, p.dv);
