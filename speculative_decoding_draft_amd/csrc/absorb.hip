@@ -1,11 +1,12 @@
-// Absorb: q_abs[h][r] = W_UK[h]^T q^C[r, h]  (192 -> 512) for every kept
+// Absorb: q_abs[r][h] = W_UK[h]^T q^C[r, h]  (192 -> 512) for every kept
 // query row r, bf16 MFMA with fp32 accumulation.
 //
 // Absorption is the identity q^C . (W_UK[h] c) = (W_UK[h]^T q^C) . c (design
 // page §4 "MLA Projection": k^C_h = W_UK[h] c^KV), so the attention can score
 // the 512 cached latent numbers directly.
 //
-// Output layout (consumed by the attention kernel): q_abs[h][r][512] bf16 with
+// Output layout (consumed by the attention kernel): q_abs[r][h][512] bf16
+// (block-major: the 5 rows x 64 heads of a kept block are contiguous), with
 // the latent dims permuted inside every 32-dim group: stored position
 // 32*k + 8*g + s holds dim 32*k + 4*g + s for s < 4 and 32*k + 16 + 4*g + (s-4)
 // for s >= 4.  That is exactly what one lane of a 16x16 MFMA output tile pair
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
                                                      const int32_t* __restrict__ kept,
                                                      const int32_t* __restrict__ status,
                                                      bf16* __restrict__ q_abs, int N, int L5,
-                                                     int lat_rows, int slot0, int nslots,
+                                                     int slot0, int nslots,
                                                      uint32_t q_bytes) {
     __shared__ __attribute__((aligned(16))) bf16 wl[kDc * kAbsStride];
     // B fragments of one iteration: [row tile][k-step][lane][8]
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
 #pragma unroll
         for (int t = 0; t < kAbsTiles; ++t) {
             const int r = clamp_row(it * kAbsRowsPerIter + (wr * kAbsTiles + t) * 16 + l16);
-            pdst[t] = q_abs + ((size_t)h * lat_rows + r) * kD + dh * 256 + wd * 128 + g * 8;
+            pdst[t] = q_abs + ((size_t)r * kH + h) * kD + dh * 256 + wd * 128 + g * 8;
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const f32x4 a0 = acc[2 * pp][t], a1 = acc[2 * pp + 1][t];
@@ -209,7 +210,7 @@ hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws
                          hipStream_t s) {
     const int grid = kH * 2 * kAbsRowGroups;
     hipLaunchKernelGGL(absorb_kernel, dim3(grid), dim3(256), 0, s, (const bf16*)in.q_nope,
-                       (const bf16*)in.w_uk, ws.kept, ws.status, ws.qabs, p.N, p.L5, p.lat_rows,
+                       (const bf16*)in.w_uk, ws.kept, ws.status, ws.qabs, p.N, p.L5,
                        c.slot0, c.nslots,
                        (uint32_t)((size_t)p.B * p.L5 * kH * kDc * sizeof(bf16)));
     return hipGetLastError();

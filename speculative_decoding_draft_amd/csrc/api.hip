@@ -85,7 +85,6 @@ Problem make_problem(const dspark_attn_desc& d) {
     p.B = d.B; p.S = d.S; p.N = d.N; p.W = d.window; p.H = d.n_heads;
     p.D = d.d_latent; p.dc = d.d_nope; p.dr = d.d_rope; p.dv = d.d_v;
     p.L5 = kBlock * d.N;
-    p.lat_rows = kBlock * d.B * d.N;   // narrowed to the chunk by the caller
     p.scale = (float)(d.softmax_scale > 0.0 ? d.softmax_scale
                                             : 1.0 / std::sqrt((double)(d.d_nope + d.d_rope)));
     return p;
@@ -191,8 +190,7 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
     if (ev && opts->n_stage_events < n_events)
         return fail(DSPARK_EINVAL, "this call records %d stage events; n_stage_events is %d",
                     n_events, opts->n_stage_events);
-    Problem pc = p;
-    pc.lat_rows = kBlock * chunk;
+    const Problem& pc = p;
 
     hipError_t e;
     if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     const bf16* __restrict__ kr_blk, const int4* __restrict__ srec,
     const int32_t* __restrict__ status,
     const float2* __restrict__ rope, const bf16* __restrict__ q_abs, bf16* __restrict__ o_lat,
-    int S, int N, int L5, int lat_rows, int slot0, int nslots, float scale, uint32_t ctx_bytes,
+    int S, int N, int L5, int slot0, int nslots, float scale, uint32_t ctx_bytes,
     uint32_t blk_bytes) {
     __shared__ __attribute__((aligned(16))) bf16 ckv_l[kMaxKeys * kCkvStride];
     __shared__ __attribute__((aligned(16))) bf16 kr_l[kMaxKeys * kKrStride];
@@ -62,12 +62,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     constexpr int kKs = (kD + kDr) / 32;           // 18 k-steps: 16 latent + 2 rope
     constexpr int kPf = 3;                         // prefetch distance (k-steps)
     static_assert(kPf <= kD / 32, "prefetched k-steps are latent ones");
-    const bf16* qa = q_abs + ((size_t)head * lat_rows + (size_t)kBlock * local) * kD + g * 8;
+    const bf16* qa = q_abs + ((size_t)kBlock * local * kH + head) * kD + g * 8;
     bf16x8 qbuf[kPf][kBlock];
 #pragma unroll
     for (int p = 0; p < kPf; ++p)
 #pragma unroll
-        for (int t = 0; t < kBlock; ++t) qbuf[p][t] = gld16(qa + t * kD + p * 32);
+        for (int t = 0; t < kBlock; ++t) qbuf[p][t] = gld16(qa + (size_t)t * kH * kD + p * 32);
 
     const int4 rec = srec[slot0 + local];      // {ctx_lo, ctx_len, pos0, block}
     const int blk = rec.w;
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
 
     const bf16* qr = q_rope + (qrow0 * kH + head) * kDr + g * 8;
     auto q_frag = [&](int ks, int t) -> bf16x8 {
-        return (ks < kD / 32) ? gld16(qa + t * kD + ks * 32)
+        return (ks < kD / 32) ? gld16(qa + (size_t)t * kH * kD + ks * 32)
                               : gld16(qr + (size_t)t * kH * kDr + (ks - kD / 32) * 32);
     };
 
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
 
     // ---- o_lat^T = c^KV^T P^T in 64-dim chunks; lane holds dims
     // 64c + 16mt + 4g + i of head `head`, query t
-    bf16* ol = o_lat + ((size_t)head * lat_rows + (size_t)kBlock * local) * kD + g * 8;
+    bf16* ol = o_lat + ((size_t)kBlock * local * kH + head) * kD + g * 8;
     const int tr_row = g * 4 + (l16 >> 2);      // transpose-read row inside a 16-key group
     const int tr_col = (l16 & 3) * 4;
     // A (V^T) fragments of step (c, kk) + 1 are read while step (c, kk)
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
                     v[i] = (bf16)(a0[i] * inv[t]);
                     v[4 + i] = (bf16)(a1[i] * inv[t]);
                 }
-                gst16(ol + t * kD + c * 64 + pp * 32, v);
+                gst16(ol + (size_t)t * kH * kD + c * 64 + pp * 32, v);
             }
         }
     }
@@ -391,13 +391,13 @@ hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, 
         hipLaunchKernelGGL(attn_kernel<1>, dim3(grid), dim3(64), 0, s, (const bf16*)in.q_rope,
                            (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
                            (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.srec,
-                           ws.status, ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5, p.lat_rows,
+                           ws.status, ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5,
                            c.slot0, c.nslots, p.scale, ctx_bytes, blk_bytes);
     } else {
         hipLaunchKernelGGL(attn_kernel<4>, dim3(grid), dim3(256), 0, s, (const bf16*)in.q_rope,
                            (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
                            (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.srec,
-                           ws.status, ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5, p.lat_rows,
+                           ws.status, ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5,
                            c.slot0, c.nslots, p.scale, ctx_bytes, blk_bytes);
     }
     return hipGetLastError();

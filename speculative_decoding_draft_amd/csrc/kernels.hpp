@@ -9,7 +9,6 @@ namespace dspark {
 struct Problem {
     int B, S, N, W, H, D, dc, dr, dv;
     int L5;          // 5 * N queries per sample
-    int lat_rows;    // row capacity of the latent buffers: 5 * (slots per chunk)
     float scale;     // softmax scale
 };
 

@@ -1,11 +1,11 @@
-// W_UV up-projection: out[b, q, h, :] = W_UV[h] o_lat[h][r]  (512 -> 256) for
+// W_UV up-projection: out[b, q, h, :] = W_UV[h] o_lat[r][h]  (512 -> 256) for
 // every kept query row r, bf16 MFMA with fp32 accumulation.
 //
 // Design page §4 "MLA Projection": v_h = W_UV[h] c^KV; because the attention
 // weights sum to one per row, sum_k p_k v_h(k) = W_UV[h] (sum_k p_k c^KV_k),
 // so the value up-projection is applied once per (query, head) to o_lat.
 //
-// o_lat[h][r][512] comes from the attention kernel with the latent dims
+// o_lat[r][h][512] (block-major) comes from the attention kernel with the latent dims
 // permuted inside each 32-dim group (stored position 32k + 8g + s is dim
 // 32k + 4g + s for s < 4, 32k + 16 + 4g + (s-4) for s >= 4); the weight
 // fragments are read in the same order, two 8-byte pieces per lane.
@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
                                                  const int32_t* __restrict__ kept,
                                                  const int32_t* __restrict__ status,
                                                  bf16* __restrict__ out, int N, int L5,
-                                                 int lat_rows, int slot0, int nslots) {
+                                                 int slot0, int nslots) {
     __shared__ __attribute__((aligned(16))) bf16 wl[128 * kUvStride];
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int vh = lid & 1;
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
     constexpr int kPf = 8;           // prefetch distance in k-steps (divides kKs)
     const bf16* op[kUvTiles];
     for (int t = 0; t < kUvTiles; ++t)
-        op[t] = o_lat + ((size_t)h * lat_rows + row_of(rg, t)) * kD + g * 8;
+        op[t] = o_lat + ((size_t)row_of(rg, t) * kH + h) * kD + g * 8;
     bf16x8 ring[kPf][kUvTiles];
 #pragma unroll
     for (int ks = 0; ks < kPf; ++ks)
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
         const int nxt = it + kUvRowGroups;
         const bf16* np[kUvTiles];
         for (int t = 0; t < kUvTiles; ++t)
-            np[t] = o_lat + ((size_t)h * lat_rows + row_of(nxt, t)) * kD + g * 8;
+            np[t] = o_lat + ((size_t)row_of(nxt, t) * kH + h) * kD + g * 8;
         int blk[kUvTiles];
         for (int t = 0; t < kUvTiles; ++t) blk[t] = kept[slot0 + row_of(it, t) / kBlock];
 
@@ -183,7 +183,7 @@ hipError_t launch_uv(const Problem& p, const Inputs& in, const Workspace& ws, Ch
                      hipStream_t s) {
     const int grid = kH * 2 * kUvRowGroups;
     hipLaunchKernelGGL(uv_kernel, dim3(grid), dim3(256), 0, s, (const bf16*)in.w_uv, ws.olat,
-                       ws.kept, ws.status, (bf16*)in.out, p.N, p.L5, p.lat_rows, c.slot0,
+                       ws.kept, ws.status, (bf16*)in.out, p.N, p.L5, c.slot0,
                        c.nslots);
     return hipGetLastError();
 }
