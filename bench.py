@@ -173,6 +173,8 @@ def main():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--chunk-blocks", type=int, default=0,
                     help="kept blocks per kernel round (0: the library default)")
+    ap.add_argument("--aux-stream", action="store_true",
+                    help="run odd kernel rounds on a second stream (with --chunk-blocks)")
     ap.add_argument("--event-every", type=int, default=10,
                     help="record per-kernel stage events on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -224,9 +226,14 @@ def main():
     n_chunks, chunk_blocks, n_ev = sd.attn_plan(desc, chunk_blocks=args.chunk_blocks)
     # chunks past the number of kept blocks exit at once; time only real ones
     live = min(n_chunks, -(-int(keep.sum()) // chunk_blocks))
+    aux, aux_ev = None, None
+    if args.aux_stream and n_chunks > 1:
+        aux = torch.cuda.Stream()
+        aux_ev = hip.create(2)
     calls = [sd.BoundFwd(desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"],
                          t["kr_blk"], t["w_uk"], t["w_uv"], a_dev, k_dev, outs[l], ws, stream=sptr,
-                         chunk_blocks=args.chunk_blocks, n_stage_events=n_ev)
+                         chunk_blocks=args.chunk_blocks, n_stage_events=n_ev, aux_stream=aux,
+                         aux_events=aux_ev)
              for l, t in enumerate(tensors)]
     # Stage events are recorded on every `event_every`-th timed step only:
     # each event is a barrier between kernels, so recording them on every
@@ -267,11 +274,11 @@ def main():
     call_ms = []
     for i in range(len(ev_steps) * L):
         e = ev[i * n_ev:(i + 1) * n_ev]
-        call_ms.append(hip.elapsed_ms(e[0], e[-1]))
+        call_ms.append(max(hip.elapsed_ms(e[0], e[5 + 4 * c]) for c in range(n_chunks)))
         per_stage[STAGES[0]].append(hip.elapsed_ms(e[0], e[1]))
         tot = {s: 0.0 for s in STAGES[1:]}
         for c in range(n_chunks):
-            marks = (e[1 + 3 * c], e[2 + 3 * c], e[3 + 3 * c], e[4 + 3 * c])
+            marks = (e[2 + 4 * c], e[3 + 4 * c], e[4 + 4 * c], e[5 + 4 * c])
             for k, s in enumerate(STAGES[1:]):
                 ms = hip.elapsed_ms(marks[k], marks[k + 1])
                 tot[s] += ms
@@ -280,6 +287,8 @@ def main():
         for s in STAGES[1:]:
             per_stage[s].append(tot[s])
     hip.destroy(ev)
+    if aux_ev:
+        hip.destroy(aux_ev)
 
     flop = useful_flop(anchors, keep, wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v) * L
     kept_blocks = int(keep.sum()) * L
@@ -316,7 +325,8 @@ def main():
         "gpu_event_us_per_call": round(float(np.mean(call_ms)) * 1e3, 2),
         "event_steps": len(ev_steps),
         "stage_us": {s: round(v, 2) for s, v in stage_avg_us.items()},
-        "chunks": {"chunk_blocks": chunk_blocks, "launches_per_kernel": live},
+        "chunks": {"chunk_blocks": chunk_blocks, "launches_per_kernel": live,
+                   "streams": 2 if aux is not None else 1},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": MI355X_HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / MI355X_HBM_PEAK_GBS, 4),

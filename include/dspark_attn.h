@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 1
+#define DSPARK_ABI_VERSION 2
 
 typedef enum dspark_status {
     DSPARK_OK = 0,
@@ -86,9 +86,8 @@ typedef struct dspark_attn_desc {
  * descriptor; see dspark_last_error).  The workspace holds the per-block
  * index records, the compacted list of kept blocks, a small status area, the
  * RoPE cos/sin table and, on the MFMA path, the bf16 latent intermediates
- * q_abs and o_lat of one chunk of kept blocks ([H, 5*chunk, D] each; the
- * size covers the largest chunk any opts->chunk_blocks can ask for, i.e. all
- * B*N blocks).  It must be 256-byte aligned. */
+ * q_abs and o_lat of every kept block ([5*B*N, H, D] each, row = 5 * slot +
+ * query).  It must be 256-byte aligned. */
 size_t dspark_attn_workspace_size(const dspark_attn_desc* desc);
 
 /* The masked MLA attention forward of one draft layer.
@@ -119,20 +118,30 @@ dspark_status dspark_attn_fwd(const dspark_attn_desc* desc,
 
 /* Extra controls for dspark_attn_fwd_ex (zero-initialise, then set fields). */
 typedef struct dspark_attn_opts {
-    /* NULL, or hipEvent_t handles recorded on `stream` between the kernels
-     * of the call, in launch order: [0] before the index build, [1] after
-     * the index build, RoPE table and padding fill, then for chunk c (see
-     * dspark_attn_plan) [2 + 3c] after its absorb, [3 + 3c] after its
-     * attention kernel, [4 + 3c] after its W_UV projection.  The generic path
-     * records [0] and [1] only, and [2] after its single kernel. */
+    /* NULL, or hipEvent_t handles recorded between the kernels of the call,
+     * in launch order: [0] before the index build, [1] after the index
+     * build, RoPE table and padding fill (both on `stream`), then for round c
+     * (see dspark_attn_plan), on the stream that runs the round: [2 + 4c]
+     * before its absorb, [3 + 4c] after it, [4 + 4c] after its attention
+     * kernel, [5 + 4c] after its W_UV projection.  The generic path records
+     * [0], [1] and [2] after its single kernel. */
     void* const* stage_events;
     int32_t n_stage_events;   /* at least the count dspark_attn_plan reports */
     int32_t force_generic;    /* nonzero: use the generic fp32 kernels even
                                  where the MFMA path applies */
     int32_t chunk_blocks;     /* > 0: kept blocks per kernel round on the MFMA
-                                 path (the bf16 intermediates of one round
-                                 are 640 KiB per block); 0: one round over
-                                 all B*N blocks */
+                                 path; 0: one round over all B*N blocks */
+    /* NULL, or a second hipStream_t.  With two or more rounds, odd rounds
+     * run on aux_stream and even rounds on `stream`, so that a round's
+     * kernels overlap the ramp-up and tail of the other stream's; the call
+     * records aux_events[0] on `stream` after the preparation launch and
+     * makes aux_stream wait for it, records aux_events[1] on aux_stream after
+     * its last round and makes `stream` wait for it, so work enqueued on
+     * `stream` afterwards sees the whole result.  Both events are created by
+     * the caller (timing may be disabled) and must not be in use elsewhere
+     * during the call.  aux_stream must not be `stream`. */
+    void* aux_stream;
+    void* aux_events[2];
 } dspark_attn_opts;
 
 /* Launch plan of dspark_attn_fwd_ex for (desc, opts) (opts may be NULL):

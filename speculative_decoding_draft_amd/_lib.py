@@ -51,7 +51,8 @@ class Desc(ctypes.Structure):
 class Opts(ctypes.Structure):
     _fields_ = [("stage_events", ctypes.POINTER(ctypes.c_void_p)),
                 ("n_stage_events", ctypes.c_int32), ("force_generic", ctypes.c_int32),
-                ("chunk_blocks", ctypes.c_int32)]
+                ("chunk_blocks", ctypes.c_int32), ("aux_stream", ctypes.c_void_p),
+                ("aux_events", ctypes.c_void_p * 2)]
 
 
 def _load():
@@ -132,8 +133,12 @@ def _stream(stream) -> Optional[int]:
     return int(stream.cuda_stream)
 
 
-def _opts(stage_events=None, force_generic=False, chunk_blocks=0):
+def _opts(stage_events=None, force_generic=False, chunk_blocks=0, aux_stream=None,
+          aux_events=None):
     opts = Opts()
+    if aux_stream is not None:
+        opts.aux_stream = _stream(aux_stream)
+        opts.aux_events[0], opts.aux_events[1] = aux_events
     keep = None
     if stage_events is not None:
         keep = (ctypes.c_void_p * len(stage_events))(*stage_events)
@@ -156,17 +161,20 @@ def attn_plan(desc: Desc, force_generic: bool = False, chunk_blocks: int = 0):
 def attn_fwd(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
              anchors, keep, out, workspace, stream=None,
              stage_events: Optional[Sequence[int]] = None, force_generic: bool = False,
-             chunk_blocks: int = 0) -> None:
-    """dspark_attn_fwd / dspark_attn_fwd_ex; raises DSparkError on a non-OK status."""
+             chunk_blocks: int = 0, aux_stream=None,
+             aux_events: Optional[Sequence[int]] = None) -> None:
+    """dspark_attn_fwd / dspark_attn_fwd_ex; raises DSparkError on a non-OK
+    status.  aux_stream / aux_events (two hipEvent_t handles) run odd rounds
+    on a second stream (see dspark_attn_opts)."""
     args = [ctypes.byref(desc)] + [_ptr(t) for t in (q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk,
                                                      kr_blk, w_uk, w_uv, anchors, keep, out,
                                                      workspace)]
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args += [ws_bytes, _stream(stream)]
-    if stage_events is None and not force_generic and not chunk_blocks:
+    if stage_events is None and not force_generic and not chunk_blocks and aux_stream is None:
         _check(lib.dspark_attn_fwd(*args))
         return
-    opts, _arr = _opts(stage_events, force_generic, chunk_blocks)
+    opts, _arr = _opts(stage_events, force_generic, chunk_blocks, aux_stream, aux_events)
     _check(lib.dspark_attn_fwd_ex(*args, ctypes.byref(opts)))
 
 
@@ -177,7 +185,8 @@ class BoundFwd:
 
     def __init__(self, desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
                  anchors, keep, out, workspace, stream=None, chunk_blocks: int = 0,
-                 n_stage_events: int = 0):
+                 n_stage_events: int = 0, aux_stream=None,
+                 aux_events: Optional[Sequence[int]] = None):
         self._desc = desc
         ws_bytes = workspace.numel() * workspace.element_size()
         self._args = (ctypes.byref(desc),) + tuple(
@@ -186,13 +195,12 @@ class BoundFwd:
             ctypes.c_size_t(ws_bytes), ctypes.c_void_p(_stream(stream)))
         self._plain = lib.dspark_attn_fwd
         self._ex = lib.dspark_attn_fwd_ex
-        self._opts, _ = _opts(None, False, chunk_blocks)
+        self._opts, _ = _opts(None, False, chunk_blocks, aux_stream, aux_events)
         self._opts_ref = ctypes.byref(self._opts)
         self._events = (ctypes.c_void_p * max(1, n_stage_events))()
-        self._opts_ev = Opts()
+        self._opts_ev, _ = _opts(None, False, chunk_blocks, aux_stream, aux_events)
         self._opts_ev.stage_events = ctypes.cast(self._events, ctypes.POINTER(ctypes.c_void_p))
         self._opts_ev.n_stage_events = n_stage_events
-        self._opts_ev.chunk_blocks = int(chunk_blocks)
         self._opts_ev_ref = ctypes.byref(self._opts_ev)
 
     def __call__(self) -> None:

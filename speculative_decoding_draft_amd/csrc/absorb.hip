@@ -184,7 +184,8 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
 #pragma unroll
         for (int t = 0; t < kAbsTiles; ++t) {
             const int r = clamp_row(it * kAbsRowsPerIter + (wr * kAbsTiles + t) * 16 + l16);
-            pdst[t] = q_abs + ((size_t)r * kH + h) * kD + dh * 256 + wd * 128 + g * 8;
+            pdst[t] = q_abs + ((size_t)(kBlock * slot0 + r) * kH + h) * kD + dh * 256 + wd * 128 +
+                      g * 8;
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const f32x4 a0 = acc[2 * pp][t], a1 = acc[2 * pp + 1][t];

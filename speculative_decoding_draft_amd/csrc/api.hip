@@ -186,11 +186,20 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
 
     const int chunk = chunk_blocks(d, opts);
     const int n_chunks = fast ? (d.B * d.N + chunk - 1) / chunk : 0;
-    const int n_events = fast ? 2 + 3 * n_chunks : 3;
+    const int n_events = fast ? 2 + 4 * n_chunks : 3;
     if (ev && opts->n_stage_events < n_events)
         return fail(DSPARK_EINVAL, "this call records %d stage events; n_stage_events is %d",
                     n_events, opts->n_stage_events);
-    const Problem& pc = p;
+    hipStream_t aux = (opts && fast && n_chunks > 1) ? static_cast<hipStream_t>(opts->aux_stream)
+                                                     : nullptr;
+    if (aux) {
+        if (aux == s) return fail(DSPARK_EINVAL, "aux_stream must differ from stream");
+        if (!opts->aux_events[0] || !opts->aux_events[1])
+            return fail(DSPARK_EINVAL, "aux_stream needs two events in aux_events");
+    }
+    auto mark_on = [&](int k, hipStream_t st) -> hipError_t {
+        return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[k]), st) : hipSuccess;
+    };
 
     hipError_t e;
     if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -200,16 +209,33 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
         return hip_fail(e, "index / RoPE table / fill launch");
     if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if (fast) {
+        hipEvent_t fork = aux ? static_cast<hipEvent_t>(opts->aux_events[0]) : nullptr;
+        hipEvent_t join = aux ? static_cast<hipEvent_t>(opts->aux_events[1]) : nullptr;
+        if (aux) {
+            if ((e = hipEventRecord(fork, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+            if ((e = hipStreamWaitEvent(aux, fork, 0)) != hipSuccess)
+                return hip_fail(e, "hipStreamWaitEvent");
+        }
         for (int c = 0; c < n_chunks; ++c) {
+            // rounds write disjoint latent rows (row = 5 * slot + query), so
+            // rounds on different streams do not interfere
+            hipStream_t st = (aux && (c & 1)) ? aux : s;
             const Chunk ch{c * chunk, chunk};
-            if ((e = launch_absorb(pc, in, ws, ch, s)) != hipSuccess)
+            if ((e = mark_on(2 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+            if ((e = launch_absorb(p, in, ws, ch, st)) != hipSuccess)
                 return hip_fail(e, "absorb launch");
-            if ((e = mark(2 + 3 * c)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-            if ((e = launch_attn(pc, in, ws, ch, s)) != hipSuccess)
+            if ((e = mark_on(3 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+            if ((e = launch_attn(p, in, ws, ch, st)) != hipSuccess)
                 return hip_fail(e, "attention launch");
-            if ((e = mark(3 + 3 * c)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-            if ((e = launch_uv(pc, in, ws, ch, s)) != hipSuccess) return hip_fail(e, "W_UV launch");
-            if ((e = mark(4 + 3 * c)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+            if ((e = mark_on(4 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+            if ((e = launch_uv(p, in, ws, ch, st)) != hipSuccess)
+                return hip_fail(e, "W_UV launch");
+            if ((e = mark_on(5 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        }
+        if (aux) {
+            if ((e = hipEventRecord(join, aux)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+            if ((e = hipStreamWaitEvent(s, join, 0)) != hipSuccess)
+                return hip_fail(e, "hipStreamWaitEvent");
         }
     } else {
         if ((e = launch_generic(p, d.dtype == DSPARK_BF16, in, ws, s)) != hipSuccess)
@@ -229,7 +255,7 @@ dspark_status dspark_attn_plan(const dspark_attn_desc* desc, const dspark_attn_o
     const int nc = fast ? (desc->B * desc->N + chunk - 1) / chunk : 0;
     if (n_chunks) *n_chunks = nc;
     if (chunk_out) *chunk_out = fast ? chunk : 0;
-    if (n_events) *n_events = empty ? 0 : (fast ? 2 + 3 * nc : 3);
+    if (n_events) *n_events = empty ? 0 : (fast ? 2 + 4 * nc : 3);
     return ok();
 }
 

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     constexpr int kKs = (kD + kDr) / 32;           // 18 k-steps: 16 latent + 2 rope
     constexpr int kPf = 3;                         // prefetch distance (k-steps)
     static_assert(kPf <= kD / 32, "prefetched k-steps are latent ones");
-    const bf16* qa = q_abs + ((size_t)kBlock * local * kH + head) * kD + g * 8;
+    const bf16* qa = q_abs + ((size_t)kBlock * (slot0 + local) * kH + head) * kD + g * 8;
     bf16x8 qbuf[kPf][kBlock];
 #pragma unroll
     for (int p = 0; p < kPf; ++p)
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
 
     // ---- o_lat^T = c^KV^T P^T in 64-dim chunks; lane holds dims
     // 64c + 16mt + 4g + i of head `head`, query t
-    bf16* ol = o_lat + ((size_t)kBlock * local * kH + head) * kD + g * 8;
+    bf16* ol = o_lat + ((size_t)kBlock * (slot0 + local) * kH + head) * kD + g * 8;
     const int tr_row = g * 4 + (l16 >> 2);      // transpose-read row inside a 16-key group
     const int tr_col = (l16 & 3) * 4;
     // A (V^T) fragments of step (c, kk) + 1 are read while step (c, kk)

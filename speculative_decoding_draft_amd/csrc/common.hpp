@@ -40,7 +40,8 @@ struct WsLayout {
     size_t kept = 0;     // int32 [B*N]      slot -> b*N + n
     size_t srec = 0;     // int4 [B*N]       slot -> {ctx_lo, ctx_len, pos0, b*N + n}
     size_t rope = 0;     // float2 [S + 8][d_r/2]  (cos, sin)
-    size_t qabs = 0;     // bf16 [5*B*N][H][D]  (MFMA path; row = 5*slot + query)
+    size_t qabs = 0;     // bf16 [5*B*N][H][D]  (MFMA path; row = 5*slot + query,
+                         // the same rows whatever the round size)
     size_t olat = 0;     // bf16 [5*B*N][H][D]  (MFMA path)
     size_t total = 0;
     int rope_rows = 0;   // S + 8

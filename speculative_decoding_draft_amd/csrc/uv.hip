@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
     constexpr int kPf = 8;           // prefetch distance in k-steps (divides kKs)
     const bf16* op[kUvTiles];
     for (int t = 0; t < kUvTiles; ++t)
-        op[t] = o_lat + ((size_t)row_of(rg, t) * kH + h) * kD + g * 8;
+        op[t] = o_lat + ((size_t)(kBlock * slot0 + row_of(rg, t)) * kH + h) * kD + g * 8;
     bf16x8 ring[kPf][kUvTiles];
 #pragma unroll
     for (int ks = 0; ks < kPf; ++ks)
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
         const int nxt = it + kUvRowGroups;
         const bf16* np[kUvTiles];
         for (int t = 0; t < kUvTiles; ++t)
-            np[t] = o_lat + ((size_t)row_of(nxt, t) * kH + h) * kD + g * 8;
+            np[t] = o_lat + ((size_t)(kBlock * slot0 + row_of(nxt, t)) * kH + h) * kD + g * 8;
         int blk[kUvTiles];
         for (int t = 0; t < kUvTiles; ++t) blk[t] = kept[slot0 + row_of(it, t) / kBlock];
 

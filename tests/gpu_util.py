@@ -20,6 +20,27 @@ F32_MAX_ABS = 1e-4
 F32_REL_L2 = 2e-5
 
 
+class HipEventPool:
+    """Raw hipEvent_t handles from the HIP runtime torch loaded."""
+
+    def __init__(self, n: int, timing: bool = True):
+        import ctypes
+        import torch  # noqa: F401  (loads the runtime)
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreateWithFlags(ctypes.byref(e), 0 if timing else 2) == 0
+            self.handles.append(e.value)
+
+    def close(self) -> None:
+        for e in self.handles:
+            self.hip.hipEventDestroy(e)
+        self.handles = []
+
+
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()

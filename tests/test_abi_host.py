@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert set(sd.EXPORTS) == declared
-    assert sd.abi_version() == 1
+    assert sd.abi_version() == 2
 
 
 def glm_desc(**kw):
@@ -128,12 +128,32 @@ def test_mfma_path_needs_32bit_offsets():
     assert sd.attn_plan(big_q) == (0, 0, 3)
 
 
+def test_opts_struct_matches_header():
+    """The binding's dspark_attn_opts has the header's layout (x86-64)."""
+    assert ctypes.sizeof(sd._lib.Opts) == 8 + 4 * 3 + 4 + 8 + 16
+    assert sd._lib.Opts.aux_stream.offset == 24 and sd._lib.Opts.aux_events.offset == 32
+
+
+def test_aux_stream_is_validated():
+    d = glm_desc(N=64)
+    need = sd.workspace_size(d)
+    p = [0x10000 * (i + 1) for i in range(11)]
+    lib = sd._lib.lib
+    opts = sd._lib.Opts()
+    opts.chunk_blocks = 16
+    opts.aux_stream = 0x1234
+    st = lib.dspark_attn_fwd_ex(ctypes.byref(d), *p, 0x7000000, need, None, ctypes.byref(opts))
+    assert st == sd.DSPARK_EINVAL and "aux_events" in sd.last_error()
+    opts.aux_stream = None
+    opts.aux_events[0] = opts.aux_events[1] = 0x10
+
+
 def test_launch_plan():
     d = glm_desc(B=2, N=1000)
-    assert sd.attn_plan(d) == (1, 2000, 5)
-    assert sd.attn_plan(d, chunk_blocks=1) == (2000, 1, 2 + 3 * 2000)
-    assert sd.attn_plan(d, chunk_blocks=300) == (7, 300, 23)
-    assert sd.attn_plan(d, chunk_blocks=10**6) == (1, 2000, 5)    # capped at B*N
+    assert sd.attn_plan(d) == (1, 2000, 6)
+    assert sd.attn_plan(d, chunk_blocks=1) == (2000, 1, 2 + 4 * 2000)
+    assert sd.attn_plan(d, chunk_blocks=300) == (7, 300, 30)
+    assert sd.attn_plan(d, chunk_blocks=10**6) == (1, 2000, 6)    # capped at B*N
     assert sd.attn_plan(d, force_generic=True) == (0, 0, 3)
     assert sd.attn_plan(glm_desc(dtype="f32")) == (0, 0, 3)
     assert sd.attn_plan(glm_desc(N=0)) == (0, 0, 0)

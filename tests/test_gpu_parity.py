@@ -6,8 +6,8 @@ import pytest
 
 import oracle as O
 import workloads as wk
-from gpu_util import (BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS, F32_REL_L2, GpuRun, anchors_for,
-                      compare, desc_for, log, sample_blocks)
+from gpu_util import (BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS, F32_REL_L2, GpuRun, HipEventPool,
+                      anchors_for, compare, desc_for, log, sample_blocks)
 
 pytestmark = pytest.mark.gpu
 
@@ -152,13 +152,37 @@ def test_chunk_sizes(sd, chunk):
     check_full(wl, form="gathered", guard=2048, chunk_blocks=chunk)
 
 
+@pytest.mark.parametrize("chunk", [7, 48, 100])
+def test_rounds_on_two_streams(sd, chunk):
+    """Odd rounds on a second stream (joined back before the result is
+    read): same output as one stream, within tolerance of the oracle."""
+    import torch
+    wl = wk.scaled(4, S=4096, N=224)
+    log(f"cfg4 recipe B1 S4096 N224, chunk {chunk}, two streams")
+    run = GpuRun(wl, 0, wl.anchors, wl.keep, guard=2048)
+    single = run.run().result()
+    run.out.fill_(float("nan"))
+    aux = torch.cuda.Stream()
+    ev = HipEventPool(2, timing=False)
+    t = run.t
+    sd.attn_fwd(run.desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"],
+                t["kr_blk"], t["w_uk"], t["w_uv"], run.anchors, run.keep, run.out, run.ws,
+                chunk_blocks=chunk, aux_stream=aux, aux_events=ev.handles)
+    got = run.result()
+    ev.close()
+    assert run.guards_intact()
+    ref = O.forward(wl, 0, form="gathered")
+    compare(got, ref, wl.keep, BF16_MAX_ABS, BF16_REL_L2, what=f"two streams, chunk {chunk}")
+    assert np.array_equal(np.nan_to_num(got, nan=7.0), np.nan_to_num(single, nan=7.0))
+
+
 def test_stage_events_are_recorded_in_order(sd):
     import ctypes
     import torch
     wl = wk.scaled(4, S=2048, N=100)
     run = GpuRun(wl, 0, wl.anchors, wl.keep, chunk_blocks=16)
     n_chunks, chunk, n_ev = sd.attn_plan(run.desc, chunk_blocks=16)
-    assert (n_chunks, chunk, n_ev) == (7, 16, 2 + 3 * 7)
+    assert (n_chunks, chunk, n_ev) == (7, 16, 2 + 4 * 7)
     hip = ctypes.CDLL("libamdhip64.so.7")
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
