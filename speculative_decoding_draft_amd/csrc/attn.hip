@@ -48,7 +48,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     const int n_here = min(nslots, status[kStKeptCount] - slot0);
     const int lid = xcd_balance(blockIdx.x, n_here * kGroups);
     if (lid < 0) return;
-    const int local = lid / kGroups;          // slot within the chunk
+    // slots are taken in descending order: W_UV then walks its rows upwards
+    // and first reads the o_lat rows written last (still in the Infinity
+    // Cache)
+    const int local = n_here - 1 - lid / kGroups;   // slot within the chunk
     const int hg0 = (lid % kGroups) * WAVES;  // first 16-head group of this workgroup
     const int tid = threadIdx.x;
     // wave index as a scalar: the key staging below selects its source
