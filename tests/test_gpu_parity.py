@@ -251,6 +251,35 @@ def test_all_padding_and_anchor_zero(sd):
     check_full(wl, form="gathered")
 
 
+def test_anchor_at_last_valid_position_and_single_block(sd):
+    """A = S - 2 (block positions up to S + 2, the top of the RoPE table)
+    and N = 1 on the MFMA path."""
+    wl = wk.make_workload("edge-top", B=1, S=300, N=1, dims=wk.GLM_DIMS, dtype="bf16",
+                          recipe="uniform", seed=81)
+    wl.anchors[0, 0] = 298
+    wl.loss_mask[0, 298] = wl.loss_mask[0, 299] = 1
+    check_full(wl, form="dense")
+
+
+def test_three_samples_mixed_blocks(sd):
+    """B = 3 with padding, clamped and full windows mixed in every sample."""
+    wl = wk.make_workload("mixed-B3", B=3, S=700, N=37, dims=wk.GLM_DIMS, dtype="bf16",
+                          recipe="headline", seed=82, recipe_args=dict(pad_frac=0.3, low_frac=0.2))
+    check_full(wl, form="gathered", guard=1024)
+
+
+def test_everything_padding_on_mfma_path(sd):
+    wl = wk.make_workload("all-pad", B=2, S=256, N=50, dims=wk.GLM_DIMS, dtype="bf16",
+                          recipe="uniform", seed=83)
+    wl.keep[:] = 0
+    wl.anchors[:] = -3
+    run = GpuRun(wl, 0, wl.anchors, wl.keep, guard=512).run()
+    gpu = run.result()
+    assert np.all(gpu == 0) and run.guards_intact()
+    st, fb = sd.read_device_status(run.ws)
+    assert st == sd.DSPARK_OK and fb == -1
+
+
 def test_bad_anchor_rows_are_nan_and_reported(sd):
     wl = wk.make_workload("badfwd", B=1, S=512, N=20, dims=wk.GLM_DIMS, dtype="bf16",
                           recipe="uniform", seed=9)
