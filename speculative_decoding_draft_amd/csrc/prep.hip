@@ -18,6 +18,7 @@
 //
 // Workgroup 0 builds the index; the next ones fill the RoPE table, the rest
 // fill rows, so the three parts run side by side.
+#include <algorithm>
 #include <climits>
 
 #include "kernels.hpp"
@@ -131,6 +132,8 @@ __device__ void fill_block(int blk, int S, int N, int L5, int H, int dv,
 }
 
 // grid = 1 + rope_wgs + fill_wgs; out == nullptr (fill_wgs = 0) skips the fill.
+// The RoPE and fill parts loop with a grid stride, so a few hundred
+// workgroups cover any problem size.
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     int total, int S, int W, const int32_t* __restrict__ anchors,
     const uint8_t* __restrict__ keep, int4* __restrict__ idx, int32_t* __restrict__ kept,
@@ -144,12 +147,16 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     }
     const int r = blockIdx.x - 1;
     if (r < rope_wgs) {
-        const long long e = (long long)r * kPrepThreads + threadIdx.x;
-        if (e < rope_n) rope_entry(e, pairs, th, table);
+        for (long long e = (long long)r * kPrepThreads + threadIdx.x; e < rope_n;
+             e += (long long)rope_wgs * kPrepThreads)
+            rope_entry(e, pairs, th, table);
         return;
     }
-    // fill workgroups handle every block; kept blocks with valid anchors exit
-    fill_block(r - rope_wgs, S, N, L5, H, dv, anchors, keep, out);
+    // fill workgroups visit every block; kept blocks with valid anchors are
+    // skipped (the test is uniform per block)
+    const int fill_wgs = gridDim.x - 1 - rope_wgs;
+    for (int blk = r - rope_wgs; blk < total; blk += fill_wgs)
+        fill_block(blk, S, N, L5, H, dv, anchors, keep, out);
 }
 
 }  // namespace
@@ -159,8 +166,9 @@ hipError_t launch_prep(const Problem& p, const int32_t* anchors, const uint8_t* 
                        const RopeTheta* th, void* out, hipStream_t s) {
     const int pairs = p.dr / 2;
     const long long rope_n = (th && pairs > 0) ? (long long)rope_rows * pairs : 0;
-    const int rope_wgs = (int)((rope_n + kPrepThreads - 1) / kPrepThreads);
-    const int fill_wgs = out ? p.B * p.N : 0;
+    constexpr long long kRopeWgs = 128, kFillWgs = 256;
+    const int rope_wgs = (int)std::min(kRopeWgs, (rope_n + kPrepThreads - 1) / kPrepThreads);
+    const int fill_wgs = out ? (int)std::min<long long>(kFillWgs, (long long)p.B * p.N) : 0;
     RopeTheta none{};
     hipLaunchKernelGGL(prep_kernel, dim3(1 + rope_wgs + fill_wgs), dim3(kPrepThreads), 0, s,
                        p.B * p.N, p.S, p.W, anchors, keep, ws.idx, ws.kept, ws.srec, ws.status,
