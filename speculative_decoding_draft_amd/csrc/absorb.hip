@@ -19,7 +19,9 @@
 // 128 dims x 64 rows per iteration.  The q^C rows of an iteration are copied
 // into LDS once per workgroup (LDS DMA, laid out as MFMA B fragments) and
 // read by both waves that need them; the copy for the next iteration runs
-// while the current one computes.
+// while the current one computes.  Results are transposed through LDS so
+// that each store instruction writes 4 rows x 256 B of q_abs: with 16 rows x
+// 64 B per instruction (the MFMA tile layout) the stores ran ~20% slower.
 #include "kernels.hpp"
 
 namespace dspark {
@@ -117,12 +119,47 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
     };
 
     // Per iteration: wait for this iteration's copy (issued one iteration
-    // earlier), read the wave's B fragments into registers, release the
-    // buffer, store the previous iteration's results, start the next copy,
-    // then compute.  Everything waited for at the top of an iteration was
-    // issued before the previous iteration's MFMAs.
+    // earlier), read the wave's B fragments into registers, store the
+    // previous iteration's results, start the next copy, then compute.
+    // Everything waited for at the top of an iteration was issued before the
+    // previous iteration's MFMAs.
+    //
+    // Results leave through LDS while the q^C buffer is free (after the
+    // B-fragment reads, before the next copy): each wave writes its rows
+    // there as they sit in the MFMA tiles (16 rows per instruction), reads
+    // them back as 4 rows x 256 B per instruction and stores those, so that
+    // a store instruction touches 4 rows of q_abs instead of 16.
+    constexpr int kEpiStride = 256 + 16;      // bytes per row (16 B pad: no bank conflicts)
+    constexpr int kEpiRows = 32;              // rows per pass (two row tiles)
+    static_assert(4 * kEpiRows * kEpiStride <= (int)sizeof(qs), "epilogue area");
+    char* const epi = reinterpret_cast<char*>(qs) + wave * kEpiRows * kEpiStride;
     bf16x8 pend[kAbsTiles][4];
-    bf16* pdst[kAbsTiles];
+    int prow0 = 0;        // chunk-local row of the wave's first pending result
+    auto flush = [&]() {
+#pragma unroll
+        for (int hf = 0; hf < kAbsTiles / 2; ++hf) {
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp)
+                    *reinterpret_cast<bf16x8*>(epi + (t2 * 16 + l16) * kEpiStride +
+                                               (pp * 4 + g) * 16) = pend[2 * hf + t2][pp];
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            bf16x8 w[kEpiRows / 4];
+#pragma unroll
+            for (int j = 0; j < kEpiRows / 4; ++j)
+                w[j] = *reinterpret_cast<const bf16x8*>(epi + (4 * j + (lane >> 4)) * kEpiStride +
+                                                        (lane & 15) * 16);
+#pragma unroll
+            for (int j = 0; j < kEpiRows / 4; ++j) {
+                const int r = clamp_row(prow0 + hf * kEpiRows + 4 * j + (lane >> 4));
+                gst16(q_abs + ((size_t)(kBlock * slot0 + r) * kH + h) * kD + dh * 256 + wd * 128 +
+                          (lane & 15) * 8,
+                      w[j]);
+            }
+        }
+    };
     for (int it = rg; it < n_iter; it += kAbsRowGroups) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();
@@ -135,10 +172,8 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __syncthreads();
         if (it != rg) {
-#pragma unroll
-            for (int t = 0; t < kAbsTiles; ++t)
-#pragma unroll
-                for (int pp = 0; pp < 4; ++pp) gst16(pdst[t] + pp * 32, pend[t][pp]);
+            flush();
+            __syncthreads();   // every wave is done with its part of the buffer
         }
         stage(it + kAbsRowGroups, cblk);
         for (int u = 0; u < kAbsCopyTiles; ++u)
@@ -181,11 +216,9 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
         // lane holds dims dcol + 4g + i of tile pair (2p, 2p+1) for row
         // it*rows_per_iter + (wr*kAbsTiles + t)*16 + l16; rows past the end
         // repeat the last row (same values, same place)
+        prow0 = it * kAbsRowsPerIter + wr * kAbsTiles * 16;
 #pragma unroll
         for (int t = 0; t < kAbsTiles; ++t) {
-            const int r = clamp_row(it * kAbsRowsPerIter + (wr * kAbsTiles + t) * 16 + l16);
-            pdst[t] = q_abs + ((size_t)(kBlock * slot0 + r) * kH + h) * kD + dh * 256 + wd * 128 +
-                      g * 8;
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const f32x4 a0 = acc[2 * pp][t], a1 = acc[2 * pp + 1][t];
@@ -196,13 +229,11 @@ __global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_
             }
         }
     }
-#pragma unroll
-    for (int t = 0; t < kAbsTiles; ++t)
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) gst16(pdst[t] + pp * 32, pend[t][pp]);
-    // the copy started by the last iteration is not used; let it land before
-    // the workgroup's LDS is released
+    // the copy started by the last iteration is not used; it must land
+    // before the buffer holds the last results
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    flush();
 }
 
 }  // namespace
