@@ -10,20 +10,61 @@
 // 32k + 4g + s for s < 4, 32k + 16 + 4g + (s-4) for s >= 4); the weight
 // fragments are read in the same order, two 8-byte pieces per lane.
 //
-// Work split: a workgroup owns one head, one half of the 256 output dims
-// (a 128 x 512 weight slice resident in LDS, rows permuted) and a strided
-// range of 128-row iterations; each wave computes 128 dims x 32 rows,
-// transposed (dims x rows), and writes 8 consecutive output dims per lane.
+// Work split: a workgroup owns one head, one half of the 256 output dims and
+// a strided range of 32-row iterations; wave w computes output dims
+// 32w .. 32w+31 of the half, transposed (dims x rows), with its 32 x 512
+// slice of W_UV[h] resident in registers.  The o_lat rows of an iteration
+// are copied into LDS one 1 KB row per instruction (LDS DMA) through a ring
+// of four slots, three iterations ahead of their use, and every wave reads
+// its B fragments from there.  Results are transposed through LDS and
+// stored as 4 rows x 256 B per instruction.  Reading o_lat as MFMA
+// fragments straight from memory (16 rows x 64 B per instruction) and
+// storing in the tile layout made this kernel ~30% slower.
 #include "kernels.hpp"
 
 namespace dspark {
 
 namespace {
 
-constexpr int kUvRowGroups = 2;
-constexpr int kUvStride = kD + 8;        // bf16 per LDS weight row (1040 B)
-constexpr int kUvTiles = 2;             // 16-row tiles per wave and iteration
-constexpr int kUvRowsPerIter = 4 * 16 * kUvTiles;
+constexpr int kUvRowGroups = 2;               // workgroups per (head, dim half)
+constexpr int kUvRows = 32;                   // o_lat rows per iteration
+constexpr int kUvCopies = kUvRows / 4;        // copy instructions per wave and iteration
+constexpr int kUvLdsStride = kD * 2 + 16;     // bytes per staged o_lat row (pad: no bank conflicts)
+constexpr int kUvSlot = kUvRows * kUvLdsStride;
+constexpr int kUvEpiStride = 128 * 2 + 16;    // bytes per row of the output transpose
+constexpr int kUvStores = kUvRows / 16;       // store instructions per wave and iteration
+constexpr int kUvKs = kD / 32;                // 16 k-steps
+
+// s_waitcnt vmcnt(n), other counters unconstrained (gfx9 encoding)
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Words of a raw buffer resource over num_bytes from base (the fields
+// buffer_rsrc() sets), made wave-uniform so that they live in SGPRs.
+__device__ inline i32x4 rsrc_words(const void* base, uint32_t num_bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFF)), (int)num_bytes,
+                 0x00020000};
+}
+
+// 16-byte-per-lane LDS DMA (lane i's bytes land at lds + 16 i) issued from
+// inline asm.  The compiler does not see it, so it adds no waits of its own
+// for it (its alias tracking would otherwise make every LDS read wait for
+// all copies in flight); the caller waits with vmcnt before the destination
+// is read.  `lds` must be the same for every lane.
+// M0 is reserved by the compiler, which sets it itself before every use; the
+// clobber tells it that the value does not survive this statement.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void copy_16_untracked(i32x4 rsrc, uint32_t byte_offset, const char* lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(lds));
+    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(m0), "v"(byte_offset), "s"(rsrc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
                                                  const bf16* __restrict__ o_lat,
@@ -31,150 +72,174 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
                                                  const int32_t* __restrict__ status,
                                                  bf16* __restrict__ out, int N, int L5,
                                                  int slot0, int nslots) {
-    __shared__ __attribute__((aligned(16))) bf16 wl[128 * kUvStride];
+    // the ring slots are separate arrays so that the compiler sees that a
+    // copy into one slot does not touch the slot being read
+    __shared__ __attribute__((aligned(16))) char s0[kUvSlot];
+    __shared__ __attribute__((aligned(16))) char s1[kUvSlot];
+    __shared__ __attribute__((aligned(16))) char s2[kUvSlot];
+    __shared__ __attribute__((aligned(16))) char s3[kUvSlot];
+    __shared__ __attribute__((aligned(16))) char epi[kUvRows * kUvEpiStride];
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int vh = lid & 1;
     const int rg = (lid >> 1) % kUvRowGroups;
     const int h = (lid >> 1) / kUvRowGroups;
     const int tid = threadIdx.x;
-
-    // LDS row R = 16 * vt + m of the slice holds output dim
-    // 32 * (vt / 2) + 8 * (m / 4) + 4 * (vt % 2) + m % 4, so that after the
-    // transposed MFMAs the lane with k-group g holds the 8 consecutive dims
-    // 32p + 8g .. 32p + 8g + 7 of tile pair p and writes them as one 16-byte
-    // store (4 lanes cover 64 contiguous bytes of a row).
-    // one 1 KB weight row per wave instruction, straight into LDS
-    {
-        const int wave = tid >> 6, lane = tid & 63;
-        for (int R = wave; R < 128; R += 4) {
-            const int vt = R >> 4, m = R & 15;
-            const int v = 32 * (vt >> 1) + 8 * (m >> 2) + 4 * (vt & 1) + (m & 3);
-            async_copy_16(w_uv + ((size_t)h * kDv + vh * 128 + v) * kD + lane * 8,
-                          &wl[R * kUvStride]);
-        }
-    }
-
-    // rows of this chunk (kept slots [slot0, slot0 + nslots))
-    const int rows = kBlock * max(0, min(nslots, status[kStKeptCount] - slot0));
-    const int n_iter = (rows + kUvRowsPerIter - 1) / kUvRowsPerIter;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
-    if (rg >= n_iter) {
-        __builtin_amdgcn_s_waitcnt(0);     // no LDS copy left in flight
-        return;
+
+    // rows of this chunk (kept slots [slot0, slot0 + nslots)); local row r is
+    // query r % 5 of slot slot0 + r / 5
+    const int rows = kBlock * max(0, min(nslots, status[kStKeptCount] - slot0));
+    const int n_iter = (rows + kUvRows - 1) / kUvRows;
+    if (rg >= n_iter) return;
+    const int n_mine = (n_iter - rg + kUvRowGroups - 1) / kUvRowGroups;   // iterations here
+
+    // A fragments: tile vt, row m = l16 is output dim
+    // vh*128 + 32*wave + 8*(m/4) + 4*vt + m%4, so that after the transposed
+    // MFMAs the lane with k-group g holds the 8 consecutive dims
+    // 32*wave + 8g .. 32*wave + 8g + 7; k-values follow the permuted o_lat
+    // order (dims 32ks + 4g + 0..3 and 32ks + 16 + 4g + 0..3).
+    bf16x8 a[kUvKs][2];
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt) {
+        const bf16* wrow = w_uv +
+                           ((size_t)h * kDv + vh * 128 + 32 * wave + 8 * (l16 >> 2) + 4 * vt +
+                            (l16 & 3)) * kD + 4 * g;
+#pragma unroll
+        for (int ks = 0; ks < kUvKs; ++ks) a[ks][vt] = cat(gld8(wrow + 32 * ks), gld8(wrow + 32 * ks + 16));
     }
+    // complete here, before any copy is in flight: a wait for these inside
+    // the loop would also wait for every copy issued before it
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
-    auto row_of = [&](int it, int t) {
-        const int r = it * kUvRowsPerIter + wave * 16 * kUvTiles + t * 16 + l16;
-        return (r < rows) ? r : rows - 1;     // duplicate rows are computed, not stored
-    };
-    constexpr int kKs = kD / 32;     // 16 k-steps
-    // A fragment (ks, vt): LDS rows 16 vt + l16, k-values in the permuted
-    // o_lat order (dims 32ks + 4g + 0..3 and 32ks + 16 + 4g + 0..3)
-    auto a_frag = [&](int ks, int vt) -> bf16x8 {
-        const bf16* ap = &wl[(vt * 16 + l16) * kUvStride + ks * 32 + g * 4];
-        return cat(ld8(ap), ld8(ap + 16));
-    };
-    constexpr int kPf = 8;           // prefetch distance in k-steps (divides kKs)
-    const bf16* op[kUvTiles];
-    for (int t = 0; t < kUvTiles; ++t)
-        op[t] = o_lat + ((size_t)(kBlock * slot0 + row_of(rg, t)) * kH + h) * kD + g * 8;
-    bf16x8 ring[kPf][kUvTiles];
+    // Copy of the workgroup's k-th iteration into `dst`: wave w copies rows
+    // 8w .. 8w+7, one o_lat row (1 KB) per instruction; rows past the end
+    // copy the last row.  Iterations past the last one are still issued (so
+    // that every iteration issues the same memory operations) but read
+    // nothing: their offsets fall outside the buffer resource, and such
+    // reads return zeros without touching memory.
+    auto stage = [&](int k, char* dst) {
+        const int r0 = (rg + k * kUvRowGroups) * kUvRows;
+        const i32x4 rs = rsrc_words(o_lat + ((size_t)kBlock * slot0 + r0) * kH * kD,
+                                    (uint32_t)(kUvRows * kH * kD * sizeof(bf16)));
 #pragma unroll
-    for (int ks = 0; ks < kPf; ++ks)
-#pragma unroll
-        for (int t = 0; t < kUvTiles; ++t) ring[ks][t] = gld16(op[t] + ks * 32);
-    // the weight copies and the first rows are in flight together
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    // Results of one iteration are stored at the start of the next one: the
-    // loop then enters its header with the same kinds of memory operations in
-    // flight from both sides, and the stores have the whole prefetch distance
-    // to complete before any load issued after them is waited for.
-    bf16x8 pend[kUvTiles][4];        // [row tile][tile pair]
-    bf16* pdst[kUvTiles];
-    auto compute = [&](int it) {
-        __asm__ volatile("" ::: "memory");
-        const int nxt = it + kUvRowGroups;
-        const bf16* np[kUvTiles];
-        for (int t = 0; t < kUvTiles; ++t)
-            np[t] = o_lat + ((size_t)(kBlock * slot0 + row_of(nxt, t)) * kH + h) * kD + g * 8;
-        int blk[kUvTiles];
-        for (int t = 0; t < kUvTiles; ++t) blk[t] = kept[slot0 + row_of(it, t) / kBlock];
-
-        f32x4 acc[8][kUvTiles];
-#pragma unroll
-        for (int vt = 0; vt < 8; ++vt)
-#pragma unroll
-            for (int t = 0; t < kUvTiles; ++t) acc[vt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // A fragments of k-step ks + 1 are read from LDS while the MFMAs of
-        // k-step ks run; sched_barrier keeps the reads ahead of the MFMAs
-        bf16x8 acur[8];
-#pragma unroll
-        for (int vt = 0; vt < 8; ++vt) acur[vt] = a_frag(0, vt);
-#pragma unroll
-        for (int ks = 0; ks < kKs; ++ks) {
-            bf16x8 bo[kUvTiles];
-#pragma unroll
-            for (int t = 0; t < kUvTiles; ++t) bo[t] = ring[ks % kPf][t];
-            // without a next iteration np points at the current rows: the
-            // loads stay unconditional so that the wait counts stay exact
-            if (ks + kPf < kKs) {
-#pragma unroll
-                for (int t = 0; t < kUvTiles; ++t) ring[ks % kPf][t] = gld16(op[t] + (ks + kPf) * 32);
-            } else {
-#pragma unroll
-                for (int t = 0; t < kUvTiles; ++t) ring[ks % kPf][t] = gld16(np[t] + (ks + kPf - kKs) * 32);
-            }
-            bf16x8 anext[8];
-            if (ks + 1 < kKs) {
-#pragma unroll
-                for (int vt = 0; vt < 8; ++vt) anext[vt] = a_frag(ks + 1, vt);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int vt = 0; vt < 8; ++vt)
-#pragma unroll
-                for (int t = 0; t < kUvTiles; ++t) acc[vt][t] = mfma_16x16x32(acur[vt], bo[t], acc[vt][t]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (ks + 1 < kKs) {
-#pragma unroll
-                for (int vt = 0; vt < 8; ++vt) acur[vt] = anext[vt];
-            }
+        for (int q = 0; q < kUvCopies; ++q) {
+            const int lr = kUvCopies * wave + q;
+            const int r = min(r0 + lr, rows - 1) - r0;      // negative past the end
+            const uint32_t off = (r >= 0) ? (uint32_t)((r * kH + h) * kD * sizeof(bf16) + lane * 16)
+                                          : 0xFFFFFFF0u;
+            copy_16_untracked(rs, off, dst + lr * kUvLdsStride);
         }
-#pragma unroll
-        for (int t = 0; t < kUvTiles; ++t) {
-            // rows past the end repeat the last row (same values, same place)
-            const int r = row_of(it, t);
-            const int j = r % kBlock;
-            const int b = blk[t] / N, n = blk[t] % N;
-            pdst[t] = out + (((size_t)b * L5 + (size_t)kBlock * n + j) * kH + h) * kDv +
-                      vh * 128 + g * 8;
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const f32x4 a0 = acc[2 * pp][t], a1 = acc[2 * pp + 1][t];
-                bf16x8 v;
-                v[0] = (bf16)a0[0]; v[1] = (bf16)a0[1]; v[2] = (bf16)a0[2]; v[3] = (bf16)a0[3];
-                v[4] = (bf16)a1[0]; v[5] = (bf16)a1[1]; v[6] = (bf16)a1[2]; v[7] = (bf16)a1[3];
-                pend[t][pp] = v;
-            }
-        }
-        for (int t = 0; t < kUvTiles; ++t) op[t] = np[t];
     };
+
+    // B fragment (t, ks): row 16t + l16 of the staged tile, stored o_lat
+    // positions 32ks + 8g .. 32ks + 8g + 7
+    auto b_frag = [&](const char* src, int t, int ks) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(src + (16 * t + l16) * kUvLdsStride + ks * 64 +
+                                                g * 16);
+    };
+
+    // Output transpose: every wave writes its 64 B of each of the 32 rows,
+    // then wave w stores rows 8w .. 8w+7 as 4 rows x 256 B per instruction.
+    // Rows past the end repeat the last row (same values, same place).  The
+    // kept blocks of those rows (at most 3 slots) are read with scalar loads.
+    bf16x8 pend[2];
+    int pk[3];            // kept[] of the 3 slots from pslot on
+    int pslot = 0, prow0 = 0;
+    auto out_row = [&](int j) { return 8 * wave + 4 * j + (lane >> 4); };
     auto flush = [&]() {
 #pragma unroll
-        for (int t = 0; t < kUvTiles; ++t)
+        for (int t = 0; t < 2; ++t)
+            *reinterpret_cast<bf16x8*>(&epi[(16 * t + l16) * kUvEpiStride + 64 * wave + 16 * g]) =
+                pend[t];
+        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) gst16(pdst[t] + pp * 32, pend[t][pp]);
+        for (int j = 0; j < kUvStores; ++j) {
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(
+                &epi[out_row(j) * kUvEpiStride + (lane & 15) * 16]);
+            const int r = min(prow0 + out_row(j), rows - 1);
+            const int d = r / kBlock - pslot;
+            const int blk = (d == 0) ? pk[0] : (d == 1) ? pk[1] : pk[2];
+            const int b = blk / N, n = blk % N;
+            gst16(out + (((size_t)b * L5 + (size_t)kBlock * n + r % kBlock) * kH + h) * kDv +
+                      vh * 128 + (lane & 15) * 8,
+                  v);
+        }
     };
 
-    compute(rg);
-    for (int it = rg + kUvRowGroups; it < n_iter; it += kUvRowGroups) {
-        flush();
-        compute(it);
+    // Iteration k: wait for its copy (issued three iterations earlier), start
+    // the copy three iterations ahead into the slot freed by iteration k-1,
+    // store iteration k-1's results, compute.  vmcnt retires in issue order,
+    // stores included; the operations issued after the copy of iteration k
+    // are the copies of k+1 and k+2 (kUvCopies each) and the stores of
+    // iterations k-4 .. k-2 (none before the first iteration).
+    auto iteration = [&](int k, const char* cur, char* ahead) {
+        if (k >= 4) __builtin_amdgcn_s_waitcnt(wait_vm(2 * kUvCopies + 3 * kUvStores));
+        else if (k == 3) __builtin_amdgcn_s_waitcnt(wait_vm(2 * kUvCopies + 2 * kUvStores));
+        else if (k == 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * kUvCopies + kUvStores));
+        else __builtin_amdgcn_s_waitcnt(wait_vm(2 * kUvCopies));
+        __asm__ volatile("s_barrier" ::: "memory");
+        stage(k + 3, ahead);
+        if (k > 0) flush();
+
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) acc[vt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // B fragments of k-step ks + 1 are read while the MFMAs of ks run
+        bf16x8 bcur[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) bcur[t] = b_frag(cur, t, 0);
+#pragma unroll
+        for (int ks = 0; ks < kUvKs; ++ks) {
+            bf16x8 bnext[2];
+            if (ks + 1 < kUvKs) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) bnext[t] = b_frag(cur, t, ks + 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) acc[vt][t] = mfma_16x16x32(a[ks][vt], bcur[t], acc[vt][t]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < kUvKs) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) bcur[t] = bnext[t];
+            }
+        }
+        prow0 = (rg + k * kUvRowGroups) * kUvRows;
+        pslot = min(prow0 + 8 * wave, rows - 1) / kBlock;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) pk[i] = kept[slot0 + min(pslot + i, (rows - 1) / kBlock)];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            bf16x8 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[i] = (bf16)acc[0][t][i];
+                v[4 + i] = (bf16)acc[1][t][i];
+            }
+            pend[t] = v;
+        }
+    };
+
+    stage(0, s0);
+    stage(1, s1);
+    stage(2, s2);
+    for (int k = 0; k < n_mine; k += 4) {
+        iteration(k, s0, s3);
+        if (k + 1 < n_mine) iteration(k + 1, s1, s0);
+        if (k + 2 < n_mine) iteration(k + 2, s2, s1);
+        if (k + 3 < n_mine) iteration(k + 3, s3, s2);
     }
+    // every wave is done with the transpose area of the previous store
+    __asm__ volatile("s_barrier" ::: "memory");
     flush();
+    // copies issued past the last iteration must land before the
+    // workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
 
 }  // namespace
