@@ -85,7 +85,9 @@ typedef struct dspark_attn_desc {
 /* Bytes of workspace dspark_attn_fwd needs for `desc` (0 on an invalid
  * descriptor; see dspark_last_error).  The workspace holds the per-block
  * index records, the compacted list of kept blocks, a small status area, the
- * RoPE cos/sin table and, on the MFMA path, the bf16 latent intermediates
+ * RoPE cos/sin table (written and read by the generic path only; the MFMA
+ * path evaluates RoPE inside its attention kernel) and, on the MFMA path,
+ * the bf16 latent intermediates
  * q_abs and o_lat of every kept block ([5*B*N, H, D] each, row = 5 * slot +
  * query).  It must be 256-byte aligned. */
 size_t dspark_attn_workspace_size(const dspark_attn_desc* desc);
@@ -120,7 +122,8 @@ dspark_status dspark_attn_fwd(const dspark_attn_desc* desc,
 typedef struct dspark_attn_opts {
     /* NULL, or hipEvent_t handles recorded between the kernels of the call,
      * in launch order: [0] before the index build, [1] after the index
-     * build, RoPE table and padding fill (both on `stream`), then for round c
+     * build, padding fill and (generic path) RoPE table, both on `stream`,
+     * then for round c
      * (see dspark_attn_plan), on the stream that runs the round: [2 + 4c]
      * before its absorb, [3 + 4c] after it, [4 + 4c] after its attention
      * kernel, [5 + 4c] after its W_UV projection.  The generic path records

@@ -204,7 +204,9 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
     hipError_t e;
     if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     const RopeTheta theta = make_theta(d);
-    if ((e = launch_prep(p, anchors, keep, ws, nullptr, L.rope_rows, &theta,
+    // the MFMA path evaluates RoPE inside the attention kernel; only the
+    // generic path reads the table
+    if ((e = launch_prep(p, anchors, keep, ws, nullptr, L.rope_rows, fast ? nullptr : &theta,
                          fast ? out : nullptr, s)) != hipSuccess)
         return hip_fail(e, "index / RoPE table / fill launch");
     if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -225,7 +227,7 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
             if ((e = launch_absorb(p, in, ws, ch, st)) != hipSuccess)
                 return hip_fail(e, "absorb launch");
             if ((e = mark_on(3 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-            if ((e = launch_attn(p, in, ws, ch, st)) != hipSuccess)
+            if ((e = launch_attn(p, in, ws, ch, theta, st)) != hipSuccess)
                 return hip_fail(e, "attention launch");
             if ((e = mark_on(4 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
             if ((e = launch_uv(p, in, ws, ch, st)) != hipSuccess)

@@ -24,6 +24,18 @@ namespace dspark {
 namespace {
 
 constexpr int kCkvStride = kD + 8;    // bf16 per staged c^KV row (1040 B)
+
+// RoPE (cos, sin) of pair i at position pos (design page §4 "RoPE": angle
+// pos * theta_i).  The angle is formed in fp64 as turns, pos * theta_i / 2pi
+// (turns[i] = theta_i / 2pi, in LDS), reduced to [-1/2, 1/2] and evaluated
+// with the hardware sin/cos, which take turns (absolute error ~1e-7, far
+// below bf16 resolution).  An fp32 angle at position ~1e5 would be off by up
+// to ~4e-3 rad.
+__device__ inline float2 rope_cs(const double* turns, int pos, int i) {
+    const double a = (double)pos * turns[i];
+    const float f = (float)(a - __builtin_rint(a));
+    return make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+}
 constexpr int kKrStride = kDr + 8;    // bf16 per staged k^R row (144 B)
 constexpr int kMaxKt = (kMaxKeys + 15) / 16;   // 9 key tiles
 constexpr float kLog2e = 1.4426950408889634f;
@@ -34,12 +46,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     const bf16* __restrict__ kr_ctx, const bf16* __restrict__ ckv_blk,
     const bf16* __restrict__ kr_blk, const int4* __restrict__ srec,
     const int32_t* __restrict__ status,
-    const float2* __restrict__ rope, const bf16* __restrict__ q_abs, bf16* __restrict__ o_lat,
+    const bf16* __restrict__ q_abs, bf16* __restrict__ o_lat,
     int S, int N, int L5, int slot0, int nslots, float scale, uint32_t ctx_bytes,
-    uint32_t blk_bytes) {
+    uint32_t blk_bytes, RopeTheta turns_per_pos) {
     __shared__ __attribute__((aligned(16))) bf16 ckv_l[kMaxKeys * kCkvStride];
     __shared__ __attribute__((aligned(16))) bf16 kr_l[kMaxKeys * kKrStride];
     __shared__ float2 qcs[kBlock * (kDr / 2)];
+    __shared__ double turns[kDr / 2];        // theta_i / 2pi
 
     constexpr int kThreads = WAVES * 64;
     constexpr int kGroups = 4 / WAVES;        // workgroups per block
@@ -59,6 +72,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
     const int head = (hg0 + wave) * 16 + l16;   // this lane's head (B-operand column)
+    for (int i = tid; i < kDr / 2; i += kThreads) turns[i] = turns_per_pos.t[i];
+    __syncthreads();
 
     // Q fragments of the first k-steps (all latent) are requested first:
     // they depend on the slot only
@@ -88,7 +103,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     constexpr int kKrIters =                       // 1 with four waves
         (kMaxKeys * kKrChunks + kThreads * kKrBatch - 1) / (kThreads * kKrBatch);
     bf16x8 xr[kKrBatch];
-    float4 cs01[kKrBatch], cs23[kKrBatch];
+    int xpos[kKrBatch];
     auto kr_load = [&](int bi) {
         const int base = bi * kThreads * kKrBatch;
 #pragma unroll
@@ -100,12 +115,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
             const bool is_ctx = s < ctx_len;
             const bf16* src = is_ctx ? kr_ctx + ((size_t)b * S + ctx_lo + s) * kDr
                                      : kr_blk + (qrow0 + (s - ctx_len)) * kDr;
-            const int pos = is_ctx ? ctx_lo + s : pos0 + (s - ctx_len);
-            const float4* tb =
-                reinterpret_cast<const float4*>(rope + (size_t)pos * (kDr / 2) + ch * 4);
+            xpos[u] = is_ctx ? ctx_lo + s : pos0 + (s - ctx_len);
             xr[u] = gld16(src + ch * 8);
-            cs01[u] = tb[0];
-            cs23[u] = tb[1];
         }
     };
     auto kr_store = [&](int bi) {
@@ -115,27 +126,18 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
             const int e = base + u * kThreads + tid;
             if (e < nkeys * kKrChunks) {
                 const int s = e / kKrChunks, ch = e % kKrChunks;
-                const float c[4] = {cs01[u].x, cs01[u].z, cs23[u].x, cs23[u].z};
-                const float sn[4] = {cs01[u].y, cs01[u].w, cs23[u].y, cs23[u].w};
                 bf16x8 y;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
+                    const float2 cs = rope_cs(turns, xpos[u], ch * 4 + q);
                     const float x0 = (float)xr[u][2 * q], x1 = (float)xr[u][2 * q + 1];
-                    y[2 * q] = (bf16)(x0 * c[q] - x1 * sn[q]);
-                    y[2 * q + 1] = (bf16)(x0 * sn[q] + x1 * c[q]);
+                    y[2 * q] = (bf16)(x0 * cs.x - x1 * cs.y);
+                    y[2 * q + 1] = (bf16)(x0 * cs.y + x1 * cs.x);
                 }
                 st16(&kr_l[s * kKrStride + ch * 8], y);
             }
         }
     };
-    // cos/sin of the block's 5 query positions (q^R is rotated in registers)
-    constexpr int kQcsPer = (kBlock * (kDr / 2) + kThreads - 1) / kThreads;
-    float2 qcs_r[kQcsPer];
-#pragma unroll
-    for (int u = 0; u < kQcsPer; ++u) {
-        const int e = min(tid + u * kThreads, kBlock * (kDr / 2) - 1);
-        qcs_r[u] = rope[(size_t)(pos0 + e / (kDr / 2)) * (kDr / 2) + e % (kDr / 2)];
-    }
     if constexpr (kKrIters == 1) kr_load(0);
 
     // ---- stage the keys: slot s < ctx_len is context row ctx_lo + s, the
@@ -173,11 +175,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
             kr_store(bi);
         }
     }
-#pragma unroll
-    for (int u = 0; u < kQcsPer; ++u) {
-        const int e = tid + u * kThreads;
-        if (e < kBlock * (kDr / 2)) qcs[e] = qcs_r[u];
-    }
+    // cos/sin of the block's 5 query positions (q^R is rotated in registers)
+    for (int e = tid; e < kBlock * (kDr / 2); e += kThreads)
+        qcs[e] = rope_cs(turns, pos0 + e / (kDr / 2), e % (kDr / 2));
     // the c^KV copies (the last memory operations issued) are counted by vmcnt
     __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
     __syncthreads();
@@ -381,11 +381,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
 }  // namespace
 
 hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
-                       hipStream_t s) {
+                       const RopeTheta& th, hipStream_t s) {
     // few blocks: split the 64 heads over four single-wave workgroups so that
     // more compute units take part
     const uint32_t ctx_bytes = (uint32_t)((size_t)p.B * p.S * kD * sizeof(bf16));
     const uint32_t blk_bytes = (uint32_t)((size_t)p.B * p.L5 * kD * sizeof(bf16));
+    RopeTheta turns{};
+    for (int k = 0; k < kDr / 2; ++k) turns.t[k] = th.t[k] * 0.15915494309189533577;  // 1 / 2pi
     const bool split = c.nslots < 160;
     const int groups = split ? 4 : 1;
     int grid = c.nslots * groups;
@@ -394,14 +396,14 @@ hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, 
         hipLaunchKernelGGL(attn_kernel<1>, dim3(grid), dim3(64), 0, s, (const bf16*)in.q_rope,
                            (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
                            (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.srec,
-                           ws.status, ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5,
-                           c.slot0, c.nslots, p.scale, ctx_bytes, blk_bytes);
+                           ws.status, ws.qabs, ws.olat, p.S, p.N, p.L5,
+                           c.slot0, c.nslots, p.scale, ctx_bytes, blk_bytes, turns);
     } else {
         hipLaunchKernelGGL(attn_kernel<4>, dim3(grid), dim3(256), 0, s, (const bf16*)in.q_rope,
                            (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
                            (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.srec,
-                           ws.status, ws.rope, ws.qabs, ws.olat, p.S, p.N, p.L5,
-                           c.slot0, c.nslots, p.scale, ctx_bytes, blk_bytes);
+                           ws.status, ws.qabs, ws.olat, p.S, p.N, p.L5,
+                           c.slot0, c.nslots, p.scale, ctx_bytes, blk_bytes, turns);
     }
     return hipGetLastError();
 }

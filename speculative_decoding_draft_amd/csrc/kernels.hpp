@@ -52,7 +52,7 @@ struct Chunk {
 hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
                          hipStream_t s);
 hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
-                       hipStream_t s);
+                       const RopeTheta& th, hipStream_t s);
 hipError_t launch_uv(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
                      hipStream_t s);
 

@@ -35,36 +35,6 @@ constexpr int kUvEpiStride = 128 * 2 + 16;    // bytes per row of the output tra
 constexpr int kUvStores = kUvRows / 16;       // store instructions per wave and iteration
 constexpr int kUvKs = kD / 32;                // 16 k-steps
 
-// s_waitcnt vmcnt(n), other counters unconstrained (gfx9 encoding)
-constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Words of a raw buffer resource over num_bytes from base (the fields
-// buffer_rsrc() sets), made wave-uniform so that they live in SGPRs.
-__device__ inline i32x4 rsrc_words(const void* base, uint32_t num_bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
-                 __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFF)), (int)num_bytes,
-                 0x00020000};
-}
-
-// 16-byte-per-lane LDS DMA (lane i's bytes land at lds + 16 i) issued from
-// inline asm.  The compiler does not see it, so it adds no waits of its own
-// for it (its alias tracking would otherwise make every LDS read wait for
-// all copies in flight); the caller waits with vmcnt before the destination
-// is read.  `lds` must be the same for every lane.
-// M0 is reserved by the compiler, which sets it itself before every use; the
-// clobber tells it that the value does not survive this statement.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ inline void copy_16_untracked(i32x4 rsrc, uint32_t byte_offset, const char* lds) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(lds));
-    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                     :: "s"(m0), "v"(byte_offset), "s"(rsrc) : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
                                                  const bf16* __restrict__ o_lat,

@@ -155,11 +155,12 @@ def test_chunk_sizes(sd, chunk):
 @pytest.mark.parametrize("chunk", [7, 48, 100])
 def test_rounds_on_two_streams(sd, chunk):
     """Odd rounds on a second stream (joined back before the result is
-    read): same output as one stream, within tolerance of the oracle."""
+    read): bit for bit the output of the same rounds on one stream, and
+    within tolerance of the oracle."""
     import torch
     wl = wk.scaled(4, S=4096, N=224)
     log(f"cfg4 recipe B1 S4096 N224, chunk {chunk}, two streams")
-    run = GpuRun(wl, 0, wl.anchors, wl.keep, guard=2048)
+    run = GpuRun(wl, 0, wl.anchors, wl.keep, guard=2048, chunk_blocks=chunk)
     single = run.run().result()
     run.out.fill_(float("nan"))
     aux = torch.cuda.Stream()
