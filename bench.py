@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
 
-A step is one dspark_attn_fwd call (index build, RoPE table, absorb,
+A step is one dspark_attn_fwd call (index build and padding fill, absorb,
 attention, W_UV) over the whole workload, with inputs resident in HBM.  The
 default workload is the S=32768, N=1024 headline configuration (25% padding
 blocks, 5% clamped windows, synthetic N(0,1) activations and N(0,1/512)
@@ -35,16 +35,16 @@ sys.path.insert(0, ROOT)
 
 MI355X_BF16_PEAK_TFLOPS = 2516.6     # 256 CU * 2.4 GHz * 4096 FLOP/CU/clk, dense
 MI355X_HBM_PEAK_GBS = 8000.0
-STAGES = ("index+rope+fill", "absorb", "attention", "w_uv")
+STAGES = ("index+fill", "absorb", "attention", "w_uv")
 KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.hip"}
 # Measured HBM bytes per launch on the headline workload (one round of all
 # blocks): rocprofv3 --pmc FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors from a
 # plain 256 MiB device copy), with the digest of the kernel's sources when the
 # counters were taken.  A kernel whose sources changed since reports null.
 PMC_TRAFFIC = {
-    "absorb": (358_861_632, "d38077a144262d1f"),
-    "attention": (587_350_857, "c63690ea55af4614"),
-    "w_uv": (394_515_483, "5189f21b2c607300"),
+    "absorb": (358_810_781, "00f4a3912e17c349"),
+    "attention": (583_772_378, "0720d3e19e76e1a3"),
+    "w_uv": (394_547_878, "c26d3b801c8c6e86"),
 }
 
 
