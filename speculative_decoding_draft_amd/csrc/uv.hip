@@ -10,10 +10,13 @@
 // 32k + 4g + s for s < 4, 32k + 16 + 4g + (s-4) for s >= 4); the weight
 // fragments are read in the same order, two 8-byte pieces per lane.
 //
-// Work split: a workgroup owns one head, one half of the 256 output dims and
-// a strided range of 32-row iterations; wave w computes output dims
-// 32w .. 32w+31 of the half, transposed (dims x rows), with its 32 x 512
-// slice of W_UV[h] resident in registers.  The o_lat rows of an iteration
+// Work split: a workgroup (8 waves, two per SIMD) owns one head and a
+// strided range of 32-row iterations; wave w computes output dims
+// 32w .. 32w+31, transposed (dims x rows), with its 32 x 512 slice of
+// W_UV[h] resident in registers.  One workgroup covering all 256 dims reads
+// every o_lat row once: splitting the dims over two workgroups made both
+// read it (the second read hits L2, but a read-only probe of this pattern
+// takes 47 us with two readers against 36 with one).  The o_lat rows of an iteration
 // are copied into LDS one 1 KB row per instruction (LDS DMA) through a ring
 // of four slots, three iterations ahead of their use, and every wave reads
 // its B fragments from there.  Results are transposed through LDS and
@@ -26,17 +29,18 @@ namespace dspark {
 
 namespace {
 
-constexpr int kUvRowGroups = 2;               // workgroups per (head, dim half)
+constexpr int kUvWaves = 8;                   // one per 32 output dims
+constexpr int kUvRowGroups = 4;               // workgroups per head
 constexpr int kUvRows = 32;                   // o_lat rows per iteration
-constexpr int kUvCopies = kUvRows / 4;        // copy instructions per wave and iteration
+constexpr int kUvCopies = kUvRows / kUvWaves; // copy instructions per wave and iteration
 constexpr int kUvLdsStride = kD * 2 + 16;     // bytes per staged o_lat row (pad: no bank conflicts)
 constexpr int kUvSlot = kUvRows * kUvLdsStride;
-constexpr int kUvEpiStride = 128 * 2 + 16;    // bytes per row of the output transpose
-constexpr int kUvStores = kUvRows / 16;       // store instructions per wave and iteration
+constexpr int kUvEpiStride = kDv * 2 + 16;    // bytes per row of the output transpose
+constexpr int kUvStores = kUvRows * kDv * 2 / 1024 / kUvWaves;   // 1 KB stores per wave and iteration
 constexpr int kUvKs = kD / 32;                // 16 k-steps
 
 
-__global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
+__global__ __launch_bounds__(kUvWaves * 64) void uv_kernel(const bf16* __restrict__ w_uv,
                                                  const bf16* __restrict__ o_lat,
                                                  const int32_t* __restrict__ kept,
                                                  const int32_t* __restrict__ status,
@@ -50,9 +54,8 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
     __shared__ __attribute__((aligned(16))) char s3[kUvSlot];
     __shared__ __attribute__((aligned(16))) char epi[kUvRows * kUvEpiStride];
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int vh = lid & 1;
-    const int rg = (lid >> 1) % kUvRowGroups;
-    const int h = (lid >> 1) / kUvRowGroups;
+    const int rg = lid % kUvRowGroups;
+    const int h = lid / kUvRowGroups;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
     const int n_mine = (n_iter - rg + kUvRowGroups - 1) / kUvRowGroups;   // iterations here
 
     // A fragments: tile vt, row m = l16 is output dim
-    // vh*128 + 32*wave + 8*(m/4) + 4*vt + m%4, so that after the transposed
+    // 32*wave + 8*(m/4) + 4*vt + m%4, so that after the transposed
     // MFMAs the lane with k-group g holds the 8 consecutive dims
     // 32*wave + 8g .. 32*wave + 8g + 7; k-values follow the permuted o_lat
     // order (dims 32ks + 4g + 0..3 and 32ks + 16 + 4g + 0..3).
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
 #pragma unroll
     for (int vt = 0; vt < 2; ++vt) {
         const bf16* wrow = w_uv +
-                           ((size_t)h * kDv + vh * 128 + 32 * wave + 8 * (l16 >> 2) + 4 * vt +
+                           ((size_t)h * kDv + 32 * wave + 8 * (l16 >> 2) + 4 * vt +
                             (l16 & 3)) * kD + 4 * g;
 #pragma unroll
         for (int ks = 0; ks < kUvKs; ++ks) a[ks][vt] = cat(gld8(wrow + 32 * ks), gld8(wrow + 32 * ks + 16));
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
     // Copy of the workgroup's k-th iteration into `dst`: wave w copies rows
-    // 8w .. 8w+7, one o_lat row (1 KB) per instruction; rows past the end
+    // 4w .. 4w+3, one o_lat row (1 KB) per instruction; rows past the end
     // copy the last row.  Iterations past the last one are still issued (so
     // that every iteration issues the same memory operations) but read
     // nothing: their offsets fall outside the buffer resource, and such
@@ -110,13 +113,13 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
     };
 
     // Output transpose: every wave writes its 64 B of each of the 32 rows,
-    // then wave w stores rows 8w .. 8w+7 as 4 rows x 256 B per instruction.
+    // then wave w stores rows 4w .. 4w+3 as 2 rows x 512 B per instruction.
     // Rows past the end repeat the last row (same values, same place).  The
-    // kept blocks of those rows (at most 3 slots) are read with scalar loads.
+    // kept blocks of those rows (at most 2 slots) are read with scalar loads.
     bf16x8 pend[2];
-    int pk[3];            // kept[] of the 3 slots from pslot on
+    int pk[2];            // kept[] of the 2 slots from pslot on
     int pslot = 0, prow0 = 0;
-    auto out_row = [&](int j) { return 8 * wave + 4 * j + (lane >> 4); };
+    auto out_row = [&](int j) { return 4 * wave + 2 * j + (lane >> 5); };
     auto flush = [&]() {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -126,13 +129,12 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
 #pragma unroll
         for (int j = 0; j < kUvStores; ++j) {
             const bf16x8 v = *reinterpret_cast<const bf16x8*>(
-                &epi[out_row(j) * kUvEpiStride + (lane & 15) * 16]);
+                &epi[out_row(j) * kUvEpiStride + (lane & 31) * 16]);
             const int r = min(prow0 + out_row(j), rows - 1);
-            const int d = r / kBlock - pslot;
-            const int blk = (d == 0) ? pk[0] : (d == 1) ? pk[1] : pk[2];
+            const int blk = (r / kBlock == pslot) ? pk[0] : pk[1];
             const int b = blk / N, n = blk % N;
             gst16(out + (((size_t)b * L5 + (size_t)kBlock * n + r % kBlock) * kH + h) * kDv +
-                      vh * 128 + (lane & 15) * 8,
+                      (lane & 31) * 8,
                   v);
         }
     };
@@ -180,9 +182,9 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
             }
         }
         prow0 = (rg + k * kUvRowGroups) * kUvRows;
-        pslot = min(prow0 + 8 * wave, rows - 1) / kBlock;
+        pslot = min(prow0 + 4 * wave, rows - 1) / kBlock;
 #pragma unroll
-        for (int i = 0; i < 3; ++i) pk[i] = kept[slot0 + min(pslot + i, (rows - 1) / kBlock)];
+        for (int i = 0; i < 2; ++i) pk[i] = kept[slot0 + min(pslot + i, (rows - 1) / kBlock)];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             bf16x8 v;
@@ -216,8 +218,8 @@ __global__ __launch_bounds__(256) void uv_kernel(const bf16* __restrict__ w_uv,
 
 hipError_t launch_uv(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
                      hipStream_t s) {
-    const int grid = kH * 2 * kUvRowGroups;
-    hipLaunchKernelGGL(uv_kernel, dim3(grid), dim3(256), 0, s, (const bf16*)in.w_uv, ws.olat,
+    const int grid = kH * kUvRowGroups;
+    hipLaunchKernelGGL(uv_kernel, dim3(grid), dim3(kUvWaves * 64), 0, s, (const bf16*)in.w_uv, ws.olat,
                        ws.kept, ws.status, (bf16*)in.out, p.N, p.L5, c.slot0,
                        c.nslots);
     return hipGetLastError();
