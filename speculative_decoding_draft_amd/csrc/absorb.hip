@@ -12,236 +12,224 @@
 // for s >= 4.  That is exactly what one lane of a 16x16 MFMA output tile pair
 // holds, and the attention kernel reads c^KV in the same order.
 //
-// Work split: a workgroup owns one head, one half of the 512 output dims and
-// a strided range of 128-row iterations.  The 192 x 256 weight slice stays in
-// LDS for the workgroup's lifetime; its transposed MFMA fragments are read
-// with ds_read_b64_tr_b16 one k-step ahead of their use.  Each wave computes
-// 128 dims x 64 rows per iteration.  The q^C rows of an iteration are copied
-// into LDS once per workgroup (LDS DMA, laid out as MFMA B fragments) and
-// read by both waves that need them; the copy for the next iteration runs
-// while the current one computes.  Results are transposed through LDS so
-// that each store instruction writes 4 rows x 256 B of q_abs: with 16 rows x
-// 64 B per instruction (the MFMA tile layout) the stores ran ~20% slower.
+// Work split: a workgroup (8 waves, two per SIMD) owns one head and a
+// strided range of 64-row iterations; wave w computes output dims
+// 64w .. 64w+63, transposed (dims x rows), with its 64 x 192 slice of
+// W_UK[h]^T in registers.  One workgroup covering all 512 dims copies every
+// q^C row into LDS once (splitting the dims over two workgroups made both
+// copy it).  W_UK[h] is staged through LDS at start, in two halves of 256
+// dims, and read transposed with ds_read_b64_tr_b16.  The q^C rows of an
+// iteration are copied into LDS already laid out as MFMA B fragments (LDS
+// DMA, double buffered: the copy for the next iteration overlaps the
+// current MFMAs) and read by all eight waves.  Results are transposed
+// through LDS (the weight staging area, free after start) and stored one
+// 1 KB q_abs row per instruction: in the MFMA tile layout (16 rows x 64 B
+// per instruction) the stores ran ~20% slower.
 #include "kernels.hpp"
 
 namespace dspark {
 
 namespace {
 
-constexpr int kAbsRowGroups = 2;        // workgroups per (head, dim half)
-constexpr int kAbsStride = 256 + 16;    // LDS row stride (bf16) of the weight slice
-constexpr int kAbsTiles = 4;                         // 16-row tiles per wave and iteration
-constexpr int kAbsRowsPerIter = 2 * 16 * kAbsTiles;  // two row groups per workgroup
-constexpr int kAbsCopyTiles = 2 * kAbsTiles / 4;     // tiles each wave copies per iteration
-
+constexpr int kAbsWaves = 8;                            // 64 output dims each
+constexpr int kAbsRowGroups = 4;                        // workgroups per head
+constexpr int kAbsRowsPerIter = 64;
+constexpr int kAbsTiles = kAbsRowsPerIter / 16;         // row tiles per iteration
 constexpr int kAbsKs = kDc / 32;                        // 6 k-steps
-constexpr int kAbsFrags = (kAbsRowsPerIter / 16) * kAbsKs;  // B fragments per iteration
+constexpr int kAbsDt = 4;                               // 16-dim tiles per wave
+constexpr int kAbsFrags = kAbsTiles * kAbsKs;           // 1 KB B fragments per iteration
+constexpr int kAbsCopies = kAbsFrags / kAbsWaves;       // copy instructions per wave
+constexpr int kAbsStride = 256 + 16;                    // weight staging row (bf16)
+constexpr int kAbsEpiStride = kD * 2 + 16;              // bytes per row of the output transpose
+constexpr int kAbsStoreRows = kAbsRowsPerIter / kAbsWaves;   // q_abs rows each wave stores
+constexpr int kAbsShared = (kDc * kAbsStride * 2 > kAbsRowsPerIter * kAbsEpiStride)
+                               ? kDc * kAbsStride * 2 : kAbsRowsPerIter * kAbsEpiStride;
+static_assert(kAbsCopies * kAbsWaves == kAbsFrags && kAbsKs % kAbsCopies == 0,
+              "each wave copies k-steps of one row tile");
 
-__global__ __launch_bounds__(256) void absorb_kernel(const bf16* __restrict__ q_nope,
-                                                     const bf16* __restrict__ w_uk,
-                                                     const int32_t* __restrict__ kept,
-                                                     const int32_t* __restrict__ status,
-                                                     bf16* __restrict__ q_abs, int N, int L5,
-                                                     int slot0, int nslots,
-                                                     uint32_t q_bytes) {
-    __shared__ __attribute__((aligned(16))) bf16 wl[kDc * kAbsStride];
-    // B fragments of one iteration: [row tile][k-step][lane][8]
-    __shared__ __attribute__((aligned(16))) bf16 qs[kAbsFrags * 512];
+__global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
+    const bf16* __restrict__ q_nope, const bf16* __restrict__ w_uk,
+    const int32_t* __restrict__ kept, const int32_t* __restrict__ status,
+    bf16* __restrict__ q_abs, int N, int L5, int slot0, int nslots, uint32_t q_bytes) {
+    // weight staging at start, then the output transpose
+    __shared__ __attribute__((aligned(16))) char shared_area[kAbsShared];
+    // the two q^C buffers are separate arrays: the compiler then sees that a
+    // copy into one does not touch the other
+    __shared__ __attribute__((aligned(16))) char qa_s[kAbsFrags * 1024];
+    __shared__ __attribute__((aligned(16))) char qb_s[kAbsFrags * 1024];
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int dh = lid & 1;
-    const int rg = (lid >> 1) % kAbsRowGroups;
-    const int h = (lid >> 1) / kAbsRowGroups;
+    const int rg = lid % kAbsRowGroups;
+    const int h = lid / kAbsRowGroups;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
-
-    // weight slice W_UK[h][0:192][dh*256 : dh*256+256]
-    // one 512-byte weight row per half-wave instruction, straight into LDS
-    {
-        const int half = lane >> 5;
-        for (int c0 = 2 * wave; c0 < kDc; c0 += 8) {
-            const int c = c0 + half;
-            if (half == 0)
-                async_copy_16(w_uk + ((size_t)h * kDc + c) * kD + dh * 256 + lane * 8,
-                              &wl[c0 * kAbsStride]);
-            else
-                async_copy_16(w_uk + ((size_t)h * kDc + c) * kD + dh * 256 + (lane - 32) * 8,
-                              &wl[c0 * kAbsStride + kAbsStride - 256]);
-        }
-    }
 
     // rows of this chunk: kept slots [slot0, slot0 + nslots); local row r is
     // query r % 5 of slot slot0 + r / 5
     const int rows = kBlock * max(0, min(nslots, status[kStKeptCount] - slot0));
     const int n_iter = (rows + kAbsRowsPerIter - 1) / kAbsRowsPerIter;
-    const int wd = wave & 1;      // 128-dim quarter inside the half
-    const int wr = wave >> 1;     // row group inside the iteration
-    if (rg >= n_iter) {
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);   // no LDS copy left in flight
-        return;
+    if (rg >= n_iter) return;
+
+    // ---- A operand: fragment (ks, dt) holds output dims 64w + 16dt + l16
+    // and k-values c = 32ks + 8g .. +7, read transposed out of the [c][d]
+    // staging copy of one half of W_UK[h] (waves 0-3 take the first half).
+    bf16x8 a[kAbsKs][kAbsDt];
+    {
+        bf16* wl = reinterpret_cast<bf16*>(shared_area);
+        const int hl = lane >> 5;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            // one 512-byte weight row per half-wave instruction, straight into LDS
+            for (int c0 = 2 * wave; c0 < kDc; c0 += 2 * kAbsWaves) {
+                const int c = c0 + hl;
+                if (hl == 0)
+                    async_copy_16(w_uk + ((size_t)h * kDc + c) * kD + half * 256 + lane * 8,
+                                  &wl[c0 * kAbsStride]);
+                else
+                    async_copy_16(w_uk + ((size_t)h * kDc + c) * kD + half * 256 + (lane - 32) * 8,
+                                  &wl[c0 * kAbsStride + kAbsStride - 256]);
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+            __syncthreads();
+            if ((wave >> 2) == half) {
+                const int wd = wave & 3;
+#pragma unroll
+                for (int ks = 0; ks < kAbsKs; ++ks)
+#pragma unroll
+                    for (int dt = 0; dt < kAbsDt; ++dt) {
+                        const bf16* ab = wl + (ks * 32 + g * 8 + (l16 >> 2)) * kAbsStride + wd * 64 +
+                                         (l16 & 3) * 4 + dt * 16;
+                        a[ks][dt] = cat(lds_read_tr(ab), lds_read_tr(ab + 4 * kAbsStride));
+                    }
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            __syncthreads();
+        }
     }
 
+    // ---- q^C copies: fragment f = T * 6 + ks of an iteration holds rows
+    // 16T + l16 and k-values 32ks + 8g .. +7 (16 rows x 64 B); wave w copies
+    // fragments 3w .. 3w+2, all of row tile w / 2.  Rows past the end copy
+    // the last row.  The copies are issued from inline asm (waited for at the
+    // top of every iteration) so that the compiler adds no waits of its own.
     auto clamp_row = [&](int r) { return (r < rows) ? r : rows - 1; };
-    auto q_ptr = [&](int r, int blk) {
-        const int j = r % kBlock;
+    const int copy_tile = (kAbsCopies * wave) / kAbsKs;
+    auto copy_row = [&](int it) { return clamp_row(it * kAbsRowsPerIter + 16 * copy_tile + l16); };
+    const i32x4 q_rs = rsrc_words(q_nope, q_bytes);
+    auto stage = [&](int it, int blk, char* dst) {
+        const int r = copy_row(it);
         const int b = blk / N, n = blk % N;
-        return q_nope + (((size_t)b * L5 + (size_t)kBlock * n + j) * kH + h) * kDc + g * 8;
-    };
-    // Copy side: this wave copies row tiles kAbsCopyTiles*wave + u of an
-    // iteration (all k-steps).  Rows past the end copy the last row.
-    auto copy_row = [&](int it, int u) {
-        return clamp_row(it * kAbsRowsPerIter + (kAbsCopyTiles * wave + u) * 16 + l16);
-    };
-    const __amdgpu_buffer_rsrc_t q_rsrc = buffer_rsrc(q_nope, q_bytes);
-    auto stage = [&](int it, const int* blk) {
+        const uint32_t off = (uint32_t)(
+            ((((size_t)b * L5 + (size_t)kBlock * n + r % kBlock) * kH + h) * kDc + g * 8) *
+            sizeof(bf16));
 #pragma unroll
-        for (int u = 0; u < kAbsCopyTiles; ++u) {
-            const uint32_t off = (uint32_t)((q_ptr(copy_row(it, u), blk[u]) - q_nope) * 2);
-#pragma unroll
-            for (int ks = 0; ks < kAbsKs; ++ks)
-                buffer_copy_16(q_rsrc, off + ks * 64,
-                               &qs[((kAbsCopyTiles * wave + u) * kAbsKs + ks) * 512]);
+        for (int j = 0; j < kAbsCopies; ++j) {
+            const int f = kAbsCopies * wave + j;
+            copy_16_untracked(q_rs, off + (f % kAbsKs) * 64, dst + f * 1024);
         }
     };
-    int cblk[kAbsCopyTiles];
-    for (int u = 0; u < kAbsCopyTiles; ++u) cblk[u] = kept[slot0 + copy_row(rg, u) / kBlock];
-    stage(rg, cblk);
-    for (int u = 0; u < kAbsCopyTiles; ++u)
-        cblk[u] = kept[slot0 + copy_row(rg + kAbsRowGroups, u) / kBlock];
 
-    // A operand (the wave's 128 x 192 slice of W_UK[h]^T): fragment (ks, dt)
-    // holds rows d = wd*128 + dt*16 + l16 and k-values c = ks*32 + g*8 + 0..7,
-    // read transposed out of the [c][d] LDS slice with ds_read_b64_tr_b16.
-    auto a_frag = [&](int ks, int dt) -> bf16x8 {
-        const bf16* abase = wl + (ks * 32 + g * 8 + (l16 >> 2)) * kAbsStride + wd * 128 +
-                            (l16 & 3) * 4 + dt * 16;
-        return cat(lds_read_tr(abase), lds_read_tr(abase + 4 * kAbsStride));
-    };
-
-    // Per iteration: wait for this iteration's copy (issued one iteration
-    // earlier), read the wave's B fragments into registers, store the
-    // previous iteration's results, start the next copy, then compute.
-    // Everything waited for at the top of an iteration was issued before the
-    // previous iteration's MFMAs.
-    //
-    // Results leave through LDS while the q^C buffer is free (after the
-    // B-fragment reads, before the next copy): each wave writes its rows
-    // there as they sit in the MFMA tiles (16 rows per instruction), reads
-    // them back as 4 rows x 256 B per instruction and stores those, so that
-    // a store instruction touches 4 rows of q_abs instead of 16.
-    constexpr int kEpiStride = 256 + 16;      // bytes per row (16 B pad: no bank conflicts)
-    constexpr int kEpiRows = 32;              // rows per pass (two row tiles)
-    static_assert(4 * kEpiRows * kEpiStride <= (int)sizeof(qs), "epilogue area");
-    char* const epi = reinterpret_cast<char*>(qs) + wave * kEpiRows * kEpiStride;
-    bf16x8 pend[kAbsTiles][4];
-    int prow0 = 0;        // chunk-local row of the wave's first pending result
+    // ---- output transpose: every wave writes its 64 dims (128 B) of each of
+    // the 64 rows, then wave w stores rows 8w .. 8w+7, one 1 KB row per
+    // instruction.  Rows past the end repeat the last row (same values, same
+    // place).
+    char* const epi = shared_area;
+    bf16x8 pend[kAbsTiles][2];       // [row tile][dim-tile pair]
+    int pit = 0;                     // iteration of the pending results
     auto flush = [&]() {
 #pragma unroll
-        for (int hf = 0; hf < kAbsTiles / 2; ++hf) {
-            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        for (int t = 0; t < kAbsTiles; ++t)
 #pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2)
+            for (int pp = 0; pp < 2; ++pp)
+                *reinterpret_cast<bf16x8*>(epi + (16 * t + l16) * kAbsEpiStride + 128 * wave +
+                                           (4 * pp + g) * 16) = pend[t][pp];
+        __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-                for (int pp = 0; pp < 4; ++pp)
-                    *reinterpret_cast<bf16x8*>(epi + (t2 * 16 + l16) * kEpiStride +
-                                               (pp * 4 + g) * 16) = pend[2 * hf + t2][pp];
-            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            bf16x8 w[kEpiRows / 4];
-#pragma unroll
-            for (int j = 0; j < kEpiRows / 4; ++j)
-                w[j] = *reinterpret_cast<const bf16x8*>(epi + (4 * j + (lane >> 4)) * kEpiStride +
-                                                        (lane & 15) * 16);
-#pragma unroll
-            for (int j = 0; j < kEpiRows / 4; ++j) {
-                const int r = clamp_row(prow0 + hf * kEpiRows + 4 * j + (lane >> 4));
-                gst16(q_abs + ((size_t)(kBlock * slot0 + r) * kH + h) * kD + dh * 256 + wd * 128 +
-                          (lane & 15) * 8,
-                      w[j]);
-            }
+        for (int j = 0; j < kAbsStoreRows; ++j) {
+            const int lr = kAbsStoreRows * wave + j;
+            const bf16x8 v = *reinterpret_cast<const bf16x8*>(epi + lr * kAbsEpiStride + lane * 16);
+            const int r = clamp_row(pit * kAbsRowsPerIter + lr);
+            gst16(q_abs + ((size_t)(kBlock * slot0 + r) * kH + h) * kD + lane * 8, v);
         }
     };
-    for (int it = rg; it < n_iter; it += kAbsRowGroups) {
+
+    // Iteration: wait for its copy (issued one iteration earlier) and the
+    // block index of the next copy, start that copy into the other buffer,
+    // store the previous iteration's results, compute.
+    int cblk = kept[slot0 + copy_row(rg) / kBlock];
+    stage(rg, cblk, qa_s);
+    cblk = kept[slot0 + copy_row(rg + kAbsRowGroups) / kBlock];
+    auto iteration = [&](int it, const char* cur, char* other) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();
-        bf16x8 bq[kAbsKs][kAbsTiles];
-#pragma unroll
-        for (int ks = 0; ks < kAbsKs; ++ks)
-#pragma unroll
-            for (int t = 0; t < kAbsTiles; ++t)
-                bq[ks][t] = ld16(&qs[((wr * kAbsTiles + t) * kAbsKs + ks) * 512 + lane * 8]);
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __syncthreads();
-        if (it != rg) {
-            flush();
-            __syncthreads();   // every wave is done with its part of the buffer
-        }
-        stage(it + kAbsRowGroups, cblk);
-        for (int u = 0; u < kAbsCopyTiles; ++u)
-            cblk[u] = kept[slot0 + copy_row(it + 2 * kAbsRowGroups, u) / kBlock];
+        stage(it + kAbsRowGroups, cblk, other);
+        cblk = kept[slot0 + copy_row(it + 2 * kAbsRowGroups) / kBlock];
+        if (it != rg) flush();
 
-        f32x4 acc[8][kAbsTiles];
+        f32x4 acc[kAbsDt][kAbsTiles];
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
+        for (int dt = 0; dt < kAbsDt; ++dt)
 #pragma unroll
             for (int t = 0; t < kAbsTiles; ++t) acc[dt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // A fragments of k-step ks + 1 are read in two halves, each while 16
-        // MFMAs of k-step ks run, so that at most 8 LDS reads (16 counted
-        // operations would overflow lgkmcnt) separate a fragment from its use.
-        bf16x8 acur[8];
+        // B fragments of k-step ks + 1 are read while the MFMAs of ks run
+        auto b_frag = [&](int t, int ks) {
+            return *reinterpret_cast<const bf16x8*>(cur + (t * kAbsKs + ks) * 1024 + lane * 16);
+        };
+        bf16x8 bcur[kAbsTiles];
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acur[dt] = a_frag(0, dt);
+        for (int t = 0; t < kAbsTiles; ++t) bcur[t] = b_frag(t, 0);
 #pragma unroll
         for (int ks = 0; ks < kAbsKs; ++ks) {
-            bf16x8 anext[8];
+            bf16x8 bnext[kAbsTiles];
+            if (ks + 1 < kAbsKs) {
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int dt = 4 * hf; dt < 4 * hf + 4; ++dt)
-#pragma unroll
-                    for (int t = 0; t < kAbsTiles; ++t)
-                        acc[dt][t] = mfma_16x16x32(acur[dt], bq[ks][t], acc[dt][t]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (ks + 1 < kAbsKs) {
-#pragma unroll
-                    for (int dt = 4 * hf; dt < 4 * hf + 4; ++dt) anext[dt] = a_frag(ks + 1, dt);
-                }
+                for (int t = 0; t < kAbsTiles; ++t) bnext[t] = b_frag(t, ks + 1);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int dt = 0; dt < kAbsDt; ++dt)
+#pragma unroll
+                for (int t = 0; t < kAbsTiles; ++t)
+                    acc[dt][t] = mfma_16x16x32(a[ks][dt], bcur[t], acc[dt][t]);
             __builtin_amdgcn_sched_barrier(0);
             if (ks + 1 < kAbsKs) {
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt) acur[dt] = anext[dt];
+                for (int t = 0; t < kAbsTiles; ++t) bcur[t] = bnext[t];
             }
         }
-        // lane holds dims dcol + 4g + i of tile pair (2p, 2p+1) for row
-        // it*rows_per_iter + (wr*kAbsTiles + t)*16 + l16; rows past the end
-        // repeat the last row (same values, same place)
-        prow0 = it * kAbsRowsPerIter + wr * kAbsTiles * 16;
+        // lane holds dims 32pp + 4g + i (tile 2pp) and 32pp + 16 + 4g + i
+        // (tile 2pp + 1) of the wave's 64, row 16t + l16: stored positions
+        // 32pp + 8g .. +7 of the permuted layout
+        pit = it;
 #pragma unroll
-        for (int t = 0; t < kAbsTiles; ++t) {
+        for (int t = 0; t < kAbsTiles; ++t)
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
+            for (int pp = 0; pp < 2; ++pp) {
                 const f32x4 a0 = acc[2 * pp][t], a1 = acc[2 * pp + 1][t];
                 bf16x8 v;
                 v[0] = (bf16)a0[0]; v[1] = (bf16)a0[1]; v[2] = (bf16)a0[2]; v[3] = (bf16)a0[3];
                 v[4] = (bf16)a1[0]; v[5] = (bf16)a1[1]; v[6] = (bf16)a1[2]; v[7] = (bf16)a1[3];
                 pend[t][pp] = v;
             }
-        }
+    };
+    for (int it = rg; it < n_iter; it += 2 * kAbsRowGroups) {
+        iteration(it, qa_s, qb_s);
+        if (it + kAbsRowGroups < n_iter) iteration(it + kAbsRowGroups, qb_s, qa_s);
     }
-    // the copy started by the last iteration is not used; it must land
-    // before the buffer holds the last results
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // every wave is done with the transpose area of the previous store
     __syncthreads();
     flush();
+    // the copy started by the last iteration is not used; let it land before
+    // the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
 }
 
 }  // namespace
 
 hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
                          hipStream_t s) {
-    const int grid = kH * 2 * kAbsRowGroups;
-    hipLaunchKernelGGL(absorb_kernel, dim3(grid), dim3(256), 0, s, (const bf16*)in.q_nope,
+    const int grid = kH * kAbsRowGroups;
+    hipLaunchKernelGGL(absorb_kernel, dim3(grid), dim3(kAbsWaves * 64), 0, s, (const bf16*)in.q_nope,
                        (const bf16*)in.w_uk, ws.kept, ws.status, ws.qabs, p.N, p.L5,
                        c.slot0, c.nslots,
                        (uint32_t)((size_t)p.B * p.L5 * kH * kDc * sizeof(bf16)));
