@@ -42,9 +42,9 @@ KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.h
 # plain 256 MiB device copy), with the digest of the kernel's sources when the
 # counters were taken.  A kernel whose sources changed since reports null.
 PMC_TRAFFIC = {
-    "absorb": (358_784_590, "96e36b4a54c5e81d"),
-    "attention": (583_783_532, "0720d3e19e76e1a3"),
-    "w_uv": (394_498_134, "58535103a0148018"),
+    "absorb": (358_784_632, "aab74b0beb040176"),
+    "attention": (583_677_729, "9a8efa059feee454"),
+    "w_uv": (394_498_142, "8759cdadabfffc32"),
 }
 
 

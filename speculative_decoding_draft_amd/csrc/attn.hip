@@ -25,17 +25,6 @@ namespace {
 
 constexpr int kCkvStride = kD + 8;    // bf16 per staged c^KV row (1040 B)
 
-// RoPE (cos, sin) of pair i at position pos (design page §4 "RoPE": angle
-// pos * theta_i).  The angle is formed in fp64 as turns, pos * theta_i / 2pi
-// (turns[i] = theta_i / 2pi, in LDS), reduced to [-1/2, 1/2] and evaluated
-// with the hardware sin/cos, which take turns (absolute error ~1e-7, far
-// below bf16 resolution).  An fp32 angle at position ~1e5 would be off by up
-// to ~4e-3 rad.
-__device__ inline float2 rope_cs(const double* turns, int pos, int i) {
-    const double a = (double)pos * turns[i];
-    const float f = (float)(a - __builtin_rint(a));
-    return make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
-}
 constexpr int kKrStride = kDr + 8;    // bf16 per staged k^R row (144 B)
 constexpr int kMaxKt = (kMaxKeys + 15) / 16;   // 9 key tiles
 constexpr float kLog2e = 1.4426950408889634f;

@@ -185,6 +185,18 @@ __device__ inline void copy_16_untracked(i32x4 rsrc, uint32_t byte_offset, const
 }
 #pragma clang diagnostic pop
 
+// RoPE (cos, sin) of pair i at position pos (design page §4 "RoPE": angle
+// pos * theta_i).  The angle is formed in fp64 as turns, pos * theta_i / 2pi
+// (turns[i] = theta_i / 2pi, in LDS), reduced to [-1/2, 1/2] and evaluated
+// with the hardware sin/cos, which take turns (absolute error ~1e-7, far
+// below bf16 resolution).  An fp32 angle at position ~1e5 would be off by up
+// to ~4e-3 rad.
+__device__ inline float2 rope_cs(const double* turns, int pos, int i) {
+    const double a = (double)pos * turns[i];
+    const float f = (float)(a - __builtin_rint(a));
+    return make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+}
+
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane r*4 + c points at 4 consecutive 16-bit elements of "row" r
 // (r = 0..3); lane j of the group receives element j%4 of the chunk held by
