@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the GLM-5.2 DSpark draft-attention forward.
+"""fp64 CPU oracle for the GLM-5.2 DSpark draft-attention forward and its
+backward.
 
 TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
@@ -29,4 +30,7 @@ from .dspark_oracle import (  # noqa: F401
     forward_absorbed,
     block_index_records,
     row_index_sets,
+    rope_interleaved_transpose,
+    backward,
+    loss,
 )

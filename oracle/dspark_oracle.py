@@ -29,6 +29,10 @@ notes of the repository):
 
 Everything is fp64.  bf16 inputs arrive as raw uint16 bit patterns and are
 decoded exactly.
+
+``backward`` returns the gradients of the same forward (chain rule on the
+expanded form); it is pinned by central finite differences of ``loss``, by
+closed forms and by torch's autograd of its masked SDPA in a special case.
 """
 from __future__ import annotations
 
@@ -373,3 +377,127 @@ def forward_absorbed(wl, layer_idx: int = 0, anchors=None, keep=None, scale=None
                 o_lat = p @ ckv_all[cols]
                 out[b, r, h] = x["w_uv"][h] @ o_lat
     return out
+
+
+# ---------------------------------------------------------------------------
+# backward  (gradient of the same masked attention; chain rule on the
+# expanded form of §4 "MLA Projection" and the appendix equation)
+# ---------------------------------------------------------------------------
+
+def rope_interleaved_transpose(y: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """R(pos)^T y: the adjoint of ``rope_interleaved`` (rotation by -phi), which
+    carries a gradient w.r.t. rotated vectors back to the unrotated ones."""
+    y = np.asarray(y, dtype=np.float64)
+    d_r = y.shape[-1]
+    phi = np.asarray(pos, dtype=np.float64)[:, None] * rope_theta(d_r, base)[None, :]
+    c, s = np.cos(phi), np.sin(phi)
+    y0, y1 = y[..., 0::2], y[..., 1::2]
+    x = np.empty_like(y)
+    x[..., 0::2] = y0 * c + y1 * s
+    x[..., 1::2] = -y0 * s + y1 * c
+    return x
+
+
+def backward(wl, dout, layer_idx: int = 0, anchors=None, keep=None, form: str = "dense",
+             blocks=None, scale=None):
+    """Gradients of L = sum over kept rows of <dout, out> w.r.t. every input
+    of the forward (fp64).
+
+    The forward is softmax(scale * Q_h K_h^T + Lambda(M)) V_h per head with
+    K_h = [c^KV W_UK[h]^T ; R k^R], V_h = c^KV W_UV[h]^T and
+    Q_h = [q^C_h ; R q^R_h] (§4 "MLA Projection", appendix equation).  With
+    G = dout (rows of padding blocks have no defined output and carry no
+    gradient), the chain rule gives, per head:
+      dV = P^T G,  dP = G V^T,  dS = P * (dP - rowsum(P * dP)),
+      dQ = scale dS K,  dK = scale dS^T Q,
+      dc^KV += dK[:, :d_c] W_UK[h] + dV W_UV[h],
+      dW_UK[h] += dK[:, :d_c]^T c^KV,  dW_UV[h] += dV^T c^KV,
+      d(R k^R) += dK[:, d_c:],  dq^C_h = dQ[:, :d_c],  d(R q^R_h) = dQ[:, d_c:],
+    and the rotations are undone with R^T.
+
+    dout: [B, 5N, H, d_v] in the workload's storage (bf16 bits or float).
+    form: "dense" (the whole KV axis) or "gathered" (only the columns some
+    computed row sees; identical because masked entries have P = 0).
+    blocks: None for every block, else the (b, n) pairs whose rows carry
+    gradient (the others are taken as dout = 0).
+    Returns a dict of fp64 arrays named like the inputs with a "d" prefix.
+    """
+    scale = softmax_scale(wl.d_c, wl.d_r) if scale is None else float(scale)
+    anchors = wl.anchors if anchors is None else anchors
+    keep = wl.keep if keep is None else keep
+    B, S, N, W, H, bl = wl.B, wl.S, wl.N, wl.W, wl.H, wl.block
+    D, d_c, d_r, d_v = wl.D, wl.d_c, wl.d_r, wl.d_v
+    x = _layer_f64(wl, wl.layers[layer_idx])
+    G_all = _f64(dout, wl.dtype)
+    L5 = bl * N
+    g = {"dq_nope": np.zeros((B, L5, H, d_c)), "dq_rope": np.zeros((B, L5, H, d_r)),
+         "dckv_ctx": np.zeros((B, S, D)), "dkr_ctx": np.zeros((B, S, d_r)),
+         "dckv_blk": np.zeros((B, L5, D)), "dkr_blk": np.zeros((B, L5, d_r)),
+         "dw_uk": np.zeros((H, d_c, D)), "dw_uv": np.zeros((H, d_v, D))}
+    by_sample = {}
+    if blocks is not None:
+        for (b, n) in blocks:
+            by_sample.setdefault(int(b), set()).add(int(n))
+    for b in range(B):
+        ns = sorted(by_sample.get(b, ())) if blocks is not None else list(range(N))
+        ns = [n for n in ns if keep[b][n]]
+        if not ns:
+            continue
+        pos_kv, pos_q = positions(S, anchors[b], bl)
+        ckv_all = np.concatenate([x["ckv_ctx"][b], x["ckv_blk"][b]], axis=0)
+        kr_rot = rope_interleaved(np.concatenate([x["kr_ctx"][b], x["kr_blk"][b]], axis=0),
+                                  pos_kv, wl.rope_base)
+        qr_rot = rope_interleaved(x["q_rope"][b].transpose(1, 0, 2), pos_q, wl.rope_base)
+        M = np.concatenate([mask_rows(S, N, W, anchors[b], keep[b], n, bl) for n in ns], 0)
+        rows = np.array([bl * n + j for n in ns for j in range(bl)])
+        if form == "dense":
+            cols = np.arange(S + L5)
+        elif form == "gathered":
+            cols = np.nonzero(M.any(axis=0))[0]
+        else:
+            raise ValueError(form)
+        Mc, C, KR = M[:, cols], ckv_all[cols], kr_rot[cols]
+        dC = np.zeros_like(C)
+        dKR = np.zeros_like(KR)
+        dqr_rot = np.zeros((H, L5, d_r))
+        for h in range(H):
+            Kc = C @ x["w_uk"][h].T
+            K = np.concatenate([Kc, KR], axis=1)
+            V = C @ x["w_uv"][h].T
+            Q = np.concatenate([x["q_nope"][b][rows, h, :], qr_rot[h][rows]], axis=1)
+            logits = np.where(Mc, scale * (Q @ K.T), -np.inf)
+            P = np.zeros_like(logits)
+            live = Mc.any(axis=1)
+            P[live] = _softmax_rows(logits[live])
+            Gh = G_all[b][rows, h, :]
+            dV = P.T @ Gh
+            dP = Gh @ V.T
+            dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+            dQ = scale * (dS @ K)
+            dK = scale * (dS.T @ Q)
+            dKc = dK[:, :d_c]
+            dC += dKc @ x["w_uk"][h] + dV @ x["w_uv"][h]
+            g["dw_uk"][h] += dKc.T @ C
+            g["dw_uv"][h] += dV.T @ C
+            dKR += dK[:, d_c:]
+            g["dq_nope"][b][rows, h, :] = dQ[:, :d_c]
+            dqr_rot[h][rows] = dQ[:, d_c:]
+        g["dq_rope"][b][rows] = rope_interleaved_transpose(dqr_rot[:, rows], pos_q[rows],
+                                                           wl.rope_base).transpose(1, 0, 2)
+        dkr_un = rope_interleaved_transpose(dKR, pos_kv[cols], wl.rope_base)
+        ctx = cols < S
+        g["dckv_ctx"][b][cols[ctx]] += dC[ctx]
+        g["dkr_ctx"][b][cols[ctx]] += dkr_un[ctx]
+        g["dckv_blk"][b][cols[~ctx] - S] += dC[~ctx]
+        g["dkr_blk"][b][cols[~ctx] - S] += dkr_un[~ctx]
+    return g
+
+
+def loss(wl, dout, layer_idx: int = 0, anchors=None, keep=None, scale=None) -> float:
+    """L = sum over kept rows of <dout, out>: the scalar whose gradient
+    ``backward`` returns (used to pin it by finite differences)."""
+    keep = wl.keep if keep is None else keep
+    out = forward(wl, layer_idx, anchors, keep, form="dense", scale=scale)
+    G = _f64(dout, wl.dtype)
+    rows_kept = np.repeat(np.asarray(keep, dtype=bool), wl.block, axis=1)   # [B, 5N]
+    return float(np.sum(np.where(rows_kept[:, :, None, None], out * G, 0.0)))

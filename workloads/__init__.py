@@ -267,3 +267,11 @@ def scaled(k: int, *, S: int, N: int, B: Optional[int] = None, seed: Optional[in
     return make_workload(f"cfg{k}-scaled B{B or Bd} S{S} N{N}", B=B or Bd, S=S, N=N, dims=dims,
                          dtype=dtype, recipe=recipe, seed=seed, recipe_args=args,
                          layers=3 if k == 5 else 1)
+
+
+def make_dout(wl: Workload, seed: int = 7) -> np.ndarray:
+    """Upstream gradient of the attention output, [B, 5N, H, d_v], N(0, 1) in
+    the workload's storage type (the input of a backward pass).  Drawn from
+    its own seeded stream so that the forward inputs stay as they are."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, wl.B, wl.S, wl.N])))
+    return _normal(rng, (wl.B, wl.block * wl.N, wl.H, wl.d_v), 1.0, wl.dtype)
