@@ -1,6 +1,6 @@
 /*
  * dspark_attn.h -- C ABI of libdspark_attn.so, the MI355X (gfx950) DSpark
- * draft-attention forward.
+ * draft-attention forward and its backward.
  *
  * What is computed (GLM 5.2 DSpark training-design page, "GLM 5.2 DSpark
  * 投机训练设计"): for every draft block n of every sample b, anchored at
@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 2
+#define DSPARK_ABI_VERSION 3
 
 typedef enum dspark_status {
     DSPARK_OK = 0,
@@ -192,8 +192,80 @@ dspark_status dspark_select_anchors_host(const uint8_t* loss_mask, int32_t S,
                                          int32_t num_anchors, uint64_t seed,
                                          int32_t* anchors, uint8_t* keep);
 
+/* ---- backward ----------------------------------------------------------
+ * Gradients of the same forward: with L = sum over the rows of kept blocks of
+ * <dout, out>, the chain rule on softmax(scale * Q K^T + Lambda(M)) V
+ * (appendix "Attention implementation") with the keys, values and queries of
+ * §4 "MLA Projection" and the rotations of §4 "RoPE".  The forward is
+ * recomputed inside the call (no forward state is kept between calls). */
+
+/* Bytes of workspace dspark_attn_bwd needs for `desc` (0 on an invalid
+ * descriptor).  Besides the forward's index area it holds fp32 accumulators
+ * [B, S + 5N, D + d_r] for the sums over blocks and heads of dc^KV and d k^R
+ * (and, on the generic path, [H, d_c + d_v, D] for the weight gradients), and
+ * on the MFMA path the bf16 latent intermediates of every kept block (q_abs,
+ * W_UV^T dout, o_lat, dq_abs: [5*B*N, H, D] each; rotated q^R; the softmax
+ * weights and scaled score gradients, [B*N, 5*H, 144] each).  The size
+ * covers both paths (force_generic included).  It must be 256-byte
+ * aligned. */
+size_t dspark_attn_bwd_workspace_size(const dspark_attn_desc* desc);
+
+/* The backward of dspark_attn_fwd for one draft layer.
+ *   q_nope ... keep   the forward's inputs, as in dspark_attn_fwd
+ *   dout   [B, 5N, H, d_v]  dL/d out; rows of padding blocks are ignored
+ * Outputs (every element written; same dtype as the inputs):
+ *   dq_nope [B, 5N, H, d_c]   dq_rope [B, 5N, H, d_r]  (w.r.t. the UNrotated q^R)
+ *   dckv_ctx [B, S, D]        dkr_ctx [B, S, d_r]      (w.r.t. the unrotated k^R)
+ *   dckv_blk [B, 5N, D]       dkr_blk [B, 5N, d_r]
+ *   dw_uk [H, d_c, D]         dw_uv [H, d_v, D]
+ * Rows no kept block reaches (padding blocks' queries and keys, context rows
+ * outside every window) are 0.  The query rows of a kept block whose anchor
+ * lies outside [0, S-2] are NaN and the block contributes nothing else
+ * (dspark_read_device_status reports DSPARK_EANCHOR).  Sums over blocks and
+ * heads (c^KV, k^R) are accumulated in fp32 with device atomics, so their
+ * last bits can differ from run to run; everything else is deterministic.
+ * d_rope = 0 allows NULL for q_rope, kr_ctx, kr_blk, dq_rope, dkr_ctx,
+ * dkr_blk.  Outputs must not alias inputs, each other or the workspace. */
+dspark_status dspark_attn_bwd(const dspark_attn_desc* desc,
+                              const void* q_nope, const void* q_rope,
+                              const void* ckv_ctx, const void* kr_ctx,
+                              const void* ckv_blk, const void* kr_blk,
+                              const void* w_uk, const void* w_uv,
+                              const int32_t* anchors, const uint8_t* keep,
+                              const void* dout,
+                              void* dq_nope, void* dq_rope,
+                              void* dckv_ctx, void* dkr_ctx,
+                              void* dckv_blk, void* dkr_blk,
+                              void* dw_uk, void* dw_uv,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* dspark_attn_bwd with options (opts may be NULL).  Used fields:
+ * force_generic, and stage_events: event [0] is recorded before the first
+ * launch and event [k] after the k-th, all on `stream`; the MFMA path makes
+ * 9 launches (accumulator clear, index, absorb, W_UV^T dout, attention
+ * backward, dc^KV / dk^R products, dq^C, weight gradients, final pass), the
+ * generic path 4 (clear, index and RoPE table, generic kernel, final pass).
+ * chunk_blocks and aux_stream are ignored: the backward runs as one round. */
+dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc,
+                                 const void* q_nope, const void* q_rope,
+                                 const void* ckv_ctx, const void* kr_ctx,
+                                 const void* ckv_blk, const void* kr_blk,
+                                 const void* w_uk, const void* w_uv,
+                                 const int32_t* anchors, const uint8_t* keep,
+                                 const void* dout,
+                                 void* dq_nope, void* dq_rope,
+                                 void* dckv_ctx, void* dkr_ctx,
+                                 void* dckv_blk, void* dkr_blk,
+                                 void* dw_uk, void* dw_uv,
+                                 void* workspace, size_t ws_bytes, void* stream,
+                                 const dspark_attn_opts* opts);
+
+/* Number of stage events dspark_attn_bwd_ex records for (desc, opts). */
+dspark_status dspark_attn_bwd_plan(const dspark_attn_desc* desc, const dspark_attn_opts* opts,
+                                   int32_t* n_events);
+
 /* Synchronises `stream`, then reads the status area of a workspace used by
- * the last dspark_attn_fwd / dspark_build_index on it.  Returns DSPARK_OK, or
+ * the last dspark_attn_fwd / dspark_attn_bwd / dspark_build_index on it.  Returns DSPARK_OK, or
  * DSPARK_EANCHOR with *first_bad_block = b*N + n of the first kept block
  * whose anchor was outside [0, S-2] (-1 when none).  first_bad_block may be
  * NULL. */

@@ -1,4 +1,4 @@
-"""MI355X (gfx950) DSpark draft-attention forward.
+"""MI355X (gfx950) DSpark draft-attention forward and backward.
 
 The compute lives in libdspark_attn.so (hand-written HIP kernels behind the C
 ABI of include/dspark_attn.h); this package is its Python binding.  Build the
@@ -21,6 +21,10 @@ from ._lib import (  # noqa: F401
     abi_version,
     attn_plan,
     attn_fwd,
+    attn_bwd,
+    bwd_plan,
+    bwd_workspace_size,
+    BWD_GRADS,
     build_index,
     last_error,
     make_desc,

@@ -3,7 +3,8 @@
 Every function mirrors an ``extern "C"`` entry point of
 ``include/dspark_attn.h``; tensors are torch tensors that live on the GPU
 (torch supplies device memory and the current HIP stream), except where the
-header says "host".  Nothing here computes any part of the forward; if the
+header says "host".  Nothing here computes any part of the forward or the
+backward; if the
 library is missing, importing this module raises.
 """
 from __future__ import annotations
@@ -29,8 +30,9 @@ DSPARK_F32 = 0
 DSPARK_BF16 = 1
 
 EXPORTS = ("dspark_attn_workspace_size", "dspark_attn_fwd", "dspark_attn_fwd_ex", "dspark_attn_plan",
-           "dspark_build_index", "dspark_select_anchors_host", "dspark_read_device_status",
-           "dspark_last_error", "dspark_abi_version")
+           "dspark_attn_bwd_workspace_size", "dspark_attn_bwd", "dspark_attn_bwd_ex",
+           "dspark_attn_bwd_plan", "dspark_build_index", "dspark_select_anchors_host",
+           "dspark_read_device_status", "dspark_last_error", "dspark_abi_version")
 
 
 class DSparkError(RuntimeError):
@@ -75,6 +77,15 @@ def _load():
     lib.dspark_attn_fwd_ex.restype = i32
     lib.dspark_attn_plan.argtypes = [pd, ctypes.POINTER(Opts)] + [ctypes.POINTER(i32)] * 3
     lib.dspark_attn_plan.restype = i32
+    lib.dspark_attn_bwd_workspace_size.argtypes = [pd]
+    lib.dspark_attn_bwd_workspace_size.restype = sz
+    bwd_args = [pd] + [vp] * 8 + [vp, vp, vp] + [vp] * 8 + [vp, sz, vp]
+    lib.dspark_attn_bwd.argtypes = bwd_args
+    lib.dspark_attn_bwd.restype = i32
+    lib.dspark_attn_bwd_ex.argtypes = bwd_args + [ctypes.POINTER(Opts)]
+    lib.dspark_attn_bwd_ex.restype = i32
+    lib.dspark_attn_bwd_plan.argtypes = [pd, ctypes.POINTER(Opts), ctypes.POINTER(i32)]
+    lib.dspark_attn_bwd_plan.restype = i32
     lib.dspark_build_index.argtypes = [pd, vp, vp, vp, vp, sz, vp]
     lib.dspark_build_index.restype = i32
     lib.dspark_select_anchors_host.argtypes = [vp, i32, i32, u64, vp, vp]
@@ -215,6 +226,42 @@ class BoundFwd:
         st = self._ex(*self._args, self._opts_ev_ref)
         if st != DSPARK_OK:
             _check(st)
+
+
+def bwd_workspace_size(desc: Desc) -> int:
+    n = int(lib.dspark_attn_bwd_workspace_size(ctypes.byref(desc)))
+    if n == 0:
+        raise DSparkError(DSPARK_EINVAL, last_error())
+    return n
+
+
+def bwd_plan(desc: Desc, force_generic: bool = False) -> int:
+    """dspark_attn_bwd_plan: the number of stage events the call records."""
+    opts, _ = _opts(None, force_generic, 0)
+    ne = ctypes.c_int32()
+    _check(lib.dspark_attn_bwd_plan(ctypes.byref(desc), ctypes.byref(opts), ctypes.byref(ne)))
+    return ne.value
+
+
+BWD_GRADS = ("dq_nope", "dq_rope", "dckv_ctx", "dkr_ctx", "dckv_blk", "dkr_blk", "dw_uk", "dw_uv")
+
+
+def attn_bwd(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
+             anchors, keep, dout, grads, workspace, stream=None,
+             stage_events: Optional[Sequence[int]] = None, force_generic: bool = False) -> None:
+    """dspark_attn_bwd / dspark_attn_bwd_ex.  grads: a mapping with the
+    output tensors named as in BWD_GRADS; raises DSparkError on a non-OK
+    status."""
+    args = [ctypes.byref(desc)] + [_ptr(t) for t in (q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk,
+                                                     kr_blk, w_uk, w_uv, anchors, keep, dout)]
+    args += [_ptr(grads[k]) for k in BWD_GRADS]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    args += [_ptr(workspace), ws_bytes, _stream(stream)]
+    if stage_events is None and not force_generic:
+        _check(lib.dspark_attn_bwd(*args))
+        return
+    opts, _arr = _opts(stage_events, force_generic, 0)
+    _check(lib.dspark_attn_bwd_ex(*args, ctypes.byref(opts)))
 
 
 def build_index(desc: Desc, anchors, keep, index_out, workspace, stream=None) -> None:

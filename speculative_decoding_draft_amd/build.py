@@ -32,7 +32,7 @@ COMMON_FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 SOURCES = ["prep.hip", "generic.hip", "absorb.hip", "attn.hip", "uv.hip", "api.hip",
-           "sampler.cpp"]
+           "sampler.cpp", "bwd_misc.hip", "bwd_gemm.hip", "bwd_attn.hip"]
 
 
 def _hipcc() -> str:

@@ -6,6 +6,7 @@
 #include <cstring>
 #include <string>
 
+#include "bwd.hpp"
 #include "kernels.hpp"
 
 namespace dspark {
@@ -116,6 +117,26 @@ dspark_status check_workspace(const void* ws, size_t ws_bytes, size_t need) {
 dspark_status hip_fail(hipError_t e, const char* what) {
     return fail(DSPARK_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+BwdWork carve_bwd(void* base, const BwdLayout& L) {
+    char* c = static_cast<char*>(base);
+    BwdWork w;
+    w.fwd = carve(base, L.fwd);
+    auto at = [&](size_t off) { return off ? c + off : nullptr; };
+    w.dolat = reinterpret_cast<bf16*>(at(L.dolat));
+    w.dqabs = reinterpret_cast<bf16*>(at(L.dqabs));
+    w.qrot = reinterpret_cast<bf16*>(at(L.qrot));
+    w.pmat = reinterpret_cast<bf16*>(at(L.pmat));
+    w.dsmat = reinterpret_cast<bf16*>(at(L.dsmat));
+    w.acc = reinterpret_cast<float*>(c + L.acc);
+    w.wacc = reinterpret_cast<float*>(at(L.wacc));
+    return w;
+}
+
+// launches of dspark_attn_bwd_ex: zero, index, absorb, d_olat, attention,
+// dc^KV, dq^C, dW, final (MFMA path); zero, index + RoPE table, generic
+// kernel, final (generic path)
+constexpr int kBwdLaunchesFast = 9, kBwdLaunchesGeneric = 4;
 
 RopeTheta make_theta(const dspark_attn_desc& d) {
     RopeTheta th;
@@ -292,6 +313,118 @@ dspark_status dspark_build_index(const dspark_attn_desc* desc, const int32_t* an
                                static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "index kernel launch");
     return ok();
+}
+
+size_t dspark_attn_bwd_workspace_size(const dspark_attn_desc* desc) {
+    bool empty = false;
+    if (check_desc(desc, &empty) != DSPARK_OK) return 0;
+    g_last_error.clear();
+    // enough for either path, so that opts->force_generic needs no other size
+    const size_t generic = bwd_layout(*desc, false).total;
+    const size_t fast = is_fast_path(*desc) ? bwd_layout(*desc, true).total : 0;
+    return generic > fast ? generic : fast;
+}
+
+dspark_status dspark_attn_bwd_plan(const dspark_attn_desc* desc, const dspark_attn_opts* opts,
+                                   int32_t* n_events) {
+    bool empty = false;
+    dspark_status st = check_desc(desc, &empty);
+    if (st != DSPARK_OK) return st;
+    const bool fast = is_fast_path(*desc) && !(opts && opts->force_generic);
+    if (n_events) *n_events = empty ? 0 : 1 + (fast ? kBwdLaunchesFast : kBwdLaunchesGeneric);
+    return ok();
+}
+
+dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc, const void* q_nope,
+                                 const void* q_rope, const void* ckv_ctx, const void* kr_ctx,
+                                 const void* ckv_blk, const void* kr_blk, const void* w_uk,
+                                 const void* w_uv, const int32_t* anchors, const uint8_t* keep,
+                                 const void* dout, void* dq_nope, void* dq_rope, void* dckv_ctx,
+                                 void* dkr_ctx, void* dckv_blk, void* dkr_blk, void* dw_uk,
+                                 void* dw_uv, void* workspace, size_t ws_bytes, void* stream,
+                                 const dspark_attn_opts* opts) {
+    bool empty = false;
+    dspark_status st = check_desc(desc, &empty);
+    if (st != DSPARK_OK) return st;
+    if (empty) return ok();
+    const dspark_attn_desc& d = *desc;
+    const void* ptrs[] = {q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
+                          anchors, keep, dout, dq_nope, dq_rope, dckv_ctx, dkr_ctx,
+                          dckv_blk, dkr_blk, dw_uk, dw_uv};
+    const char* names[] = {"q_nope", "q_rope", "ckv_ctx", "kr_ctx", "ckv_blk", "kr_blk",
+                           "w_uk", "w_uv", "anchors", "keep", "dout", "dq_nope", "dq_rope",
+                           "dckv_ctx", "dkr_ctx", "dckv_blk", "dkr_blk", "dw_uk", "dw_uv"};
+    for (int i = 0; i < 19; ++i) {
+        const bool rope_arg = i == 1 || i == 3 || i == 5 || i == 12 || i == 14 || i == 16;
+        const bool may_be_null = rope_arg && d.d_rope == 0;
+        if (!ptrs[i] && !may_be_null) return fail(DSPARK_EINVAL, "%s is NULL", names[i]);
+        if (ptrs[i] && i != 9 && !aligned16(ptrs[i]))
+            return fail(DSPARK_EINVAL, "%s must be 16-byte aligned", names[i]);
+    }
+    const bool fast = is_fast_path(d) && !(opts && opts->force_generic);
+    const BwdLayout L = bwd_layout(d, fast);
+    st = check_workspace(workspace, ws_bytes, L.total);
+    if (st != DSPARK_OK) return st;
+    const Problem p = make_problem(d);
+    if (!fast && bwd_generic_lds_bytes(p) > 64 * 1024)
+        return fail(DSPARK_EUNSUPPORTED,
+                    "shape needs %zu bytes of LDS in the generic backward kernel (max 65536)",
+                    bwd_generic_lds_bytes(p));
+    const int n_events = 1 + (fast ? kBwdLaunchesFast : kBwdLaunchesGeneric);
+    void* const* ev = (opts && opts->stage_events) ? opts->stage_events : nullptr;
+    if (ev && opts->n_stage_events < n_events)
+        return fail(DSPARK_EINVAL, "this call records %d stage events; n_stage_events is %d",
+                    n_events, opts->n_stage_events);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int k_ev = 0;
+    auto mark = [&]() -> hipError_t {
+        return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[k_ev++]), s) : hipSuccess;
+    };
+    const BwdWork w = carve_bwd(workspace, L);
+    const Inputs in{q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv, nullptr};
+    const BwdGrads g{dout, dq_nope, dq_rope, dckv_ctx, dkr_ctx, dckv_blk, dkr_blk, dw_uk, dw_uv};
+    const RopeTheta theta = make_theta(d);
+    hipError_t e;
+#define DSPARK_STEP(call, what)                                   \
+    do {                                                          \
+        if ((e = (call)) != hipSuccess) return hip_fail(e, what); \
+        if ((e = mark()) != hipSuccess) return hip_fail(e, "hipEventRecord"); \
+    } while (0)
+    if ((e = mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    size_t zero_n = L.acc_rows * size_t(d.d_latent + d.d_rope);
+    if (!fast) zero_n = (L.total - L.acc) / 4;     // accumulators, then the weight ones
+    DSPARK_STEP(launch_bwd_zero(w.acc, zero_n, s), "accumulator clear launch");
+    DSPARK_STEP(launch_prep(p, anchors, keep, w.fwd, nullptr, L.fwd.rope_rows,
+                            fast ? nullptr : &theta, nullptr, s),
+                "index launch");
+    if (fast) {
+        DSPARK_STEP(launch_absorb(p, in, w.fwd, Chunk{0, d.B * d.N}, s), "absorb launch");
+        DSPARK_STEP(launch_bwd_dolat(p, in, g, w, s), "d_olat launch");
+        DSPARK_STEP(launch_bwd_attn(p, in, g, w, theta, s), "backward attention launch");
+        DSPARK_STEP(launch_bwd_dkv(p, w, s), "dc^KV launch");
+        DSPARK_STEP(launch_bwd_dqnope(p, in, g, w, s), "dq^C launch");
+        DSPARK_STEP(launch_bwd_dw(p, in, g, w, s), "weight-gradient launch");
+    } else {
+        DSPARK_STEP(launch_bwd_generic(p, d.dtype == DSPARK_BF16, in, g, w, s),
+                    "generic backward launch");
+    }
+    DSPARK_STEP(launch_bwd_finalize(p, d.dtype == DSPARK_BF16, g, w, w.fwd.idx,
+                                    fast ? nullptr : w.fwd.rope, theta, !fast, s),
+                "final backward launch");
+#undef DSPARK_STEP
+    return ok();
+}
+
+dspark_status dspark_attn_bwd(const dspark_attn_desc* desc, const void* q_nope,
+                              const void* q_rope, const void* ckv_ctx, const void* kr_ctx,
+                              const void* ckv_blk, const void* kr_blk, const void* w_uk,
+                              const void* w_uv, const int32_t* anchors, const uint8_t* keep,
+                              const void* dout, void* dq_nope, void* dq_rope, void* dckv_ctx,
+                              void* dkr_ctx, void* dckv_blk, void* dkr_blk, void* dw_uk,
+                              void* dw_uv, void* workspace, size_t ws_bytes, void* stream) {
+    return dspark_attn_bwd_ex(desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
+                              anchors, keep, dout, dq_nope, dq_rope, dckv_ctx, dkr_ctx, dckv_blk,
+                              dkr_blk, dw_uk, dw_uv, workspace, ws_bytes, stream, nullptr);
 }
 
 dspark_status dspark_read_device_status(const void* workspace, void* stream,

@@ -1,0 +1,109 @@
+// Backward of the masked latent attention: workspace layout and launch
+// wrappers (internal to libdspark_attn.so).
+#pragma once
+
+#include "kernels.hpp"
+
+namespace dspark {
+
+// Workspace of dspark_attn_bwd.  The first five areas have the forward's
+// layout (status at offset 0), so the index builder is shared.
+//
+// MFMA path, per kept block (slot) s and query t, latent row R = 5 s + t:
+//   qabs  bf16 [5*B*N][H][D]   W_UK[h]^T q^C         (permuted 32-dim groups)
+//   dolat bf16 [5*B*N][H][D]   W_UV[h]^T dout        (permuted)
+//   olat  bf16 [5*B*N][H][D]   softmax-weighted c^KV (permuted)
+//   dqabs bf16 [5*B*N][H][D]   scale * sum_k dS_k c^KV_k (permuted)
+//   qrot  bf16 [5*B*N][H][d_r] rotated q^R
+//   pmat  bf16 [B*N][5H][144]  softmax weights, row = t*H + h, column = key slot
+//   dsmat bf16 [B*N][5H][144]  scale * dS, same layout
+// Both paths:
+//   acc   f32 [B][S + 5N][D + d_r]  sums over blocks and heads of dc^KV and of
+//                                   d(rotated k^R), context rows then block rows
+//   wacc  f32 [H][d_c + d_v][D]     generic path: dW_UK then dW_UV
+// "Permuted" is the order the attention kernels read and write latent rows
+// in: inside every 32-dim group, position 8g + e holds dim 16(e/4) + 4g + e%4.
+struct BwdLayout {
+    WsLayout fwd;
+    size_t dolat = 0, dqabs = 0, qrot = 0, pmat = 0, dsmat = 0, acc = 0, wacc = 0;
+    size_t acc_rows = 0;   // B * (S + 5N)
+    size_t total = 0;
+};
+
+constexpr int kKeySlots = 144;   // key slots of a block's P / dS rows (9 tiles of 16)
+
+inline BwdLayout bwd_layout(const dspark_attn_desc& d, bool mfma) {
+    BwdLayout L;
+    L.fwd = ws_layout(d, mfma);
+    size_t off = L.fwd.total;
+    const size_t blocks = size_t(d.B) * size_t(d.N);
+    if (mfma) {
+        const size_t lat = size_t(d.n_heads) * kBlock * blocks * size_t(d.d_latent) * 2;
+        L.dolat = off; off = align256(off + lat);
+        L.dqabs = off; off = align256(off + lat);
+        L.qrot = off;  off = align256(off + size_t(d.n_heads) * kBlock * blocks * d.d_rope * 2);
+        const size_t pm = blocks * kBlock * size_t(d.n_heads) * kKeySlots * 2;
+        L.pmat = off;  off = align256(off + pm);
+        L.dsmat = off; off = align256(off + pm);
+    }
+    L.acc_rows = size_t(d.B) * (size_t(d.S) + size_t(kBlock) * d.N);
+    L.acc = off; off = align256(off + L.acc_rows * size_t(d.d_latent + d.d_rope) * 4);
+    if (!mfma) {
+        L.wacc = off;
+        off = align256(off + size_t(d.n_heads) * (d.d_nope + d.d_v) * size_t(d.d_latent) * 4);
+    }
+    L.total = off;
+    return L;
+}
+
+struct BwdGrads {
+    const void* dout;
+    void* dq_nope;
+    void* dq_rope;
+    void* dckv_ctx;
+    void* dkr_ctx;
+    void* dckv_blk;
+    void* dkr_blk;
+    void* dw_uk;
+    void* dw_uv;
+};
+
+struct BwdWork {
+    Workspace fwd;
+    bf16* dolat;
+    bf16* dqabs;
+    bf16* qrot;
+    bf16* pmat;
+    bf16* dsmat;
+    float* acc;
+    float* wacc;
+};
+
+// Zero the fp32 accumulators (and, on the generic path, the weight ones).
+hipError_t launch_bwd_zero(float* p, size_t n, hipStream_t s);
+// Generic path: one workgroup per (block, head), fp32 arithmetic, atomics
+// into the accumulators.
+hipError_t launch_bwd_generic(const Problem& p, bool bf16_io, const Inputs& in,
+                              const BwdGrads& g, const BwdWork& w, hipStream_t s);
+size_t bwd_generic_lds_bytes(const Problem& p);
+// Accumulators -> dc^KV / dk^R outputs (R^T applied to dk^R); rows of query
+// gradients of blocks that are not computed (0 for padding, NaN for a kept
+// block with a bad anchor); on the generic path also the weight gradients.
+// table: the RoPE table (generic path) or nullptr (angles evaluated from
+// th, the theta_i of the descriptor).
+hipError_t launch_bwd_finalize(const Problem& p, bool bf16_io, const BwdGrads& g,
+                               const BwdWork& w, const int4* idx, const float2* table,
+                               const RopeTheta& th, bool weights, hipStream_t s);
+
+// MFMA path (bf16, GLM dims).
+hipError_t launch_bwd_dolat(const Problem& p, const Inputs& in, const BwdGrads& g,
+                            const BwdWork& w, hipStream_t s);
+hipError_t launch_bwd_attn(const Problem& p, const Inputs& in, const BwdGrads& g,
+                           const BwdWork& w, const RopeTheta& th, hipStream_t s);
+hipError_t launch_bwd_dkv(const Problem& p, const BwdWork& w, hipStream_t s);
+hipError_t launch_bwd_dqnope(const Problem& p, const Inputs& in, const BwdGrads& g,
+                             const BwdWork& w, hipStream_t s);
+hipError_t launch_bwd_dw(const Problem& p, const Inputs& in, const BwdGrads& g,
+                         const BwdWork& w, hipStream_t s);
+
+}  // namespace dspark

@@ -1,0 +1,408 @@
+// Backward of the masked latent attention, MFMA path: the dense products
+// around the attention kernel, as tiled bf16 MFMA GEMMs with fp32
+// accumulation.
+//
+//   d_olat = W_UV[h]^T dout              per head, over the kept query rows
+//   dq^C   = W_UK[h] dq_abs              per head
+//   dW_UV[h] = sum_rows dout (o_lat)^T   per head, reduction over every row
+//   dW_UK[h] = sum_rows q^C (dq_abs)^T   per head
+//   dc_k  = sum_rows P d_olat + dS' q_abs, d(R k^R)_k = sum_rows dS' (R q^R)
+//                                         per block, over its 5 x 64 rows
+// (the chain rule on the design page's attention in absorbed form: the
+// relations are listed at the top of bwd_misc.hip).
+//
+// One workgroup computes a BM x BN tile of C = A B (A: M x K, B: K x N) with
+// 4 waves.  Operands go through LDS 32 k at a time, double buffered (one
+// barrier per step); the global loads of step s + 1 are issued before the
+// MFMAs of step s.  An operand is either K-contiguous in memory (its rows
+// are M or N indices; read with 16-byte LDS loads) or M/N-contiguous (its
+// rows are k indices; read with the gfx950 transposing LDS load).  Every
+// fragment carries its 8 k values in the order the transposing load
+// produces: inside each 32-group, k-slot 8g + e holds k = 16(e/4) + 4g + e%4
+// for k-group g.  That is also the order the latent rows are stored in
+// ("permuted"), so a K-contiguous latent operand is read with plain 16-byte
+// loads and a K-contiguous natural-order operand with two 8-byte loads.
+//
+// The M side is always the output's contiguous dimension: lane l of a wave
+// receives C[4(l/16) + i][l%16], i = 0..3, i.e. 4 consecutive output elements.
+#include "bwd.hpp"
+
+namespace dspark {
+
+namespace {
+
+// dim of position p (0..31) of a permuted 32-group, and the inverse
+__device__ inline int perm_dim(int p) { return 16 * ((p & 7) >> 2) + 4 * (p >> 3) + (p & 3); }
+__device__ inline int perm_pos(int d) { return 8 * ((d & 15) >> 2) + 4 * (d >> 4) + (d & 3); }
+
+// the first of 4 consecutive dims held at permuted positions pos .. pos+3
+__device__ inline int dim_of_pos4(int pos) { return (pos & ~31) + perm_dim(pos & 31); }
+__device__ inline int pos_of_dim4(int dim) { return (dim & ~31) + perm_pos(dim & 31); }
+
+template <int BM_, int BN_, int WM_, int WN_, bool A_TR_, bool A_PERM_, bool B_TR_, bool B_PERM_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr bool A_TR = A_TR_, A_PERM = A_PERM_, B_TR = B_TR_, B_PERM = B_PERM_;
+    static_assert(WM * WN == 4, "4 waves");
+    static constexpr int MT = BM / WM / 16, NT = BN / WN / 16;
+    static_assert(MT * WM * 16 == BM && NT * WN * 16 == BN, "16-row tiles");
+    static constexpr int A_LD = A_TR ? BM + 8 : 40;     // LDS row stride (bf16)
+    static constexpr int B_LD = B_TR ? BN + 8 : 40;
+    static constexpr int A_SZ = A_TR ? 32 * A_LD : BM * A_LD;
+    static constexpr int B_SZ = B_TR ? 32 * B_LD : BN * B_LD;
+    static constexpr int A_CH = BM * 4, B_CH = BN * 4;  // 16-byte chunks per 32-k tile
+    static constexpr int A_PT = (A_CH + 255) / 256, B_PT = (B_CH + 255) / 256;
+    static constexpr int STAGE = A_SZ + B_SZ;
+    static constexpr int LDS_ELEMS = 2 * STAGE;
+};
+
+// K-contiguous operand: row(r) is the start of row r (r < BM or BN), or
+// nullptr (zeros).  Transposed operand: row(k) is the element (k, tile
+// column 0) of k-row k, or nullptr (zeros).
+template <class C, class AF, class BF>
+__device__ inline void gemm_tile(const AF& arow, const BF& brow, int s0, int s1, bf16* lds,
+                                 f32x4 (&acc)[C::MT][C::NT]) {
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const bf16x8 zero8 = {};
+#pragma unroll
+    for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const bf16* apr[C::A_PT];
+    const bf16* bpr[C::B_PT];
+    if constexpr (!C::A_TR) {
+#pragma unroll
+        for (int i = 0; i < C::A_PT; ++i) {
+            const int c = tid + 256 * i;
+            apr[i] = (c < C::A_CH) ? arow(c >> 2) : nullptr;
+        }
+    }
+    if constexpr (!C::B_TR) {
+#pragma unroll
+        for (int i = 0; i < C::B_PT; ++i) {
+            const int c = tid + 256 * i;
+            bpr[i] = (c < C::B_CH) ? brow(c >> 2) : nullptr;
+        }
+    }
+    bf16x8 ra[C::A_PT], rb[C::B_PT];
+    auto load = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < C::A_PT; ++i) {
+            const int c = tid + 256 * i;
+            const bf16* p = nullptr;
+            if (c < C::A_CH) {
+                if constexpr (C::A_TR) {
+                    constexpr int per = C::BM / 8;
+                    p = arow(32 * s + c / per);
+                    if (p) p += 8 * (c % per);
+                } else {
+                    p = apr[i];
+                    if (p) p += 32 * s + 8 * (c & 3);
+                }
+            }
+            ra[i] = p ? gld16(p) : zero8;
+        }
+#pragma unroll
+        for (int i = 0; i < C::B_PT; ++i) {
+            const int c = tid + 256 * i;
+            const bf16* p = nullptr;
+            if (c < C::B_CH) {
+                if constexpr (C::B_TR) {
+                    constexpr int per = C::BN / 8;
+                    p = brow(32 * s + c / per);
+                    if (p) p += 8 * (c % per);
+                } else {
+                    p = bpr[i];
+                    if (p) p += 32 * s + 8 * (c & 3);
+                }
+            }
+            rb[i] = p ? gld16(p) : zero8;
+        }
+    };
+    auto store = [&](bf16* st) {
+#pragma unroll
+        for (int i = 0; i < C::A_PT; ++i) {
+            const int c = tid + 256 * i;
+            if (c < C::A_CH) {
+                constexpr int per = C::BM / 8;
+                const int off = C::A_TR ? (c / per) * C::A_LD + 8 * (c % per)
+                                        : (c >> 2) * C::A_LD + 8 * (c & 3);
+                st16(st + off, ra[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::B_PT; ++i) {
+            const int c = tid + 256 * i;
+            if (c < C::B_CH) {
+                constexpr int per = C::BN / 8;
+                const int off = C::B_TR ? (c / per) * C::B_LD + 8 * (c % per)
+                                        : (c >> 2) * C::B_LD + 8 * (c & 3);
+                st16(st + C::A_SZ + off, rb[i]);
+            }
+        }
+    };
+    auto frag = [&](const bf16* base, int ld, bool tr, bool perm, int r0) -> bf16x8 {
+        if (tr) {
+            const int col = r0 + 4 * (l16 & 3);
+            const int rr = 4 * g + (l16 >> 2);
+            return cat(lds_read_tr(base + rr * ld + col), lds_read_tr(base + (rr + 16) * ld + col));
+        }
+        const bf16* row = base + (r0 + l16) * ld;
+        return perm ? ld16(row + 8 * g) : cat(ld8(row + 4 * g), ld8(row + 16 + 4 * g));
+    };
+    if (s0 >= s1) return;
+    load(s0);
+    for (int s = s0; s < s1; ++s) {
+        bf16* st = lds + ((s - s0) & 1) * C::STAGE;
+        store(st);
+        __syncthreads();
+        if (s + 1 < s1) load(s + 1);
+        bf16x8 af[C::MT], bfr[C::NT];
+#pragma unroll
+        for (int i = 0; i < C::MT; ++i)
+            af[i] = frag(st, C::A_LD, C::A_TR, C::A_PERM, wm * (C::BM / C::WM) + 16 * i);
+#pragma unroll
+        for (int j = 0; j < C::NT; ++j)
+            bfr[j] = frag(st + C::A_SZ, C::B_LD, C::B_TR, C::B_PERM, wn * (C::BN / C::WN) + 16 * j);
+#pragma unroll
+        for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NT; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+    }
+}
+
+// input row (b * 5N + 5n + t) of latent row R = 5 * slot + t
+__device__ inline size_t input_row(const int4* srec, int R, int N, int L5) {
+    const int blk = srec[R / kBlock].w;
+    return (size_t)(blk / N) * L5 + (size_t)kBlock * (blk % N) + R % kBlock;
+}
+
+__device__ inline bf16x4 to_bf16x4(f32x4 v) {
+    return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+
+// ---- d_olat[R][h] = W_UV[h]^T dout[R][h]: M = D (dims, natural), N = rows,
+// K = d_v.  A = W_UV[h] read transposed, B = dout rows.
+using CfgDolat = Cfg<128, 64, 2, 2, true, false, false, false>;
+__global__ __launch_bounds__(256) void dolat_kernel(const bf16* __restrict__ dout,
+                                                    const bf16* __restrict__ w_uv,
+                                                    const int4* __restrict__ srec,
+                                                    const int32_t* __restrict__ status,
+                                                    bf16* __restrict__ dolat, int N, int L5) {
+    __shared__ __attribute__((aligned(16))) bf16 lds[CfgDolat::LDS_ELEMS];
+    const int rows = kBlock * status[kStKeptCount];
+    const int m0 = blockIdx.x * CfgDolat::BM, n0 = blockIdx.y * CfgDolat::BN, h = blockIdx.z;
+    if (n0 >= rows) return;
+    const bf16* wh = w_uv + (size_t)h * kDv * kD + m0;
+    auto arow = [&](int k) -> const bf16* { return wh + (size_t)k * kD; };
+    auto brow = [&](int r) -> const bf16* {
+        const int R = n0 + r;
+        return R < rows ? dout + (input_row(srec, R, N, L5) * kH + h) * kDv : nullptr;
+    };
+    f32x4 acc[CfgDolat::MT][CfgDolat::NT];
+    gemm_tile<CfgDolat>(arow, brow, 0, kDv / 32, lds, acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
+    const int wm = wave / CfgDolat::WN, wn = wave % CfgDolat::WN;
+#pragma unroll
+    for (int j = 0; j < CfgDolat::NT; ++j) {
+        const int R = n0 + wn * (CfgDolat::BN / 2) + 16 * j + l16;
+        if (R >= rows) continue;
+        bf16* dst = dolat + ((size_t)R * kH + h) * kD;
+#pragma unroll
+        for (int i = 0; i < CfgDolat::MT; ++i) {
+            const int d = m0 + wm * (CfgDolat::BM / 2) + 16 * i + 4 * g;
+            gst8(dst + pos_of_dim4(d), to_bf16x4(acc[i][j]));
+        }
+    }
+}
+
+// ---- dq^C[R][h] = W_UK[h] dq_abs[R][h]: M = d_c, N = rows, K = D.
+// A = W_UK[h] rows (natural), B = dq_abs rows (permuted).
+using CfgDqn = Cfg<192, 64, 2, 2, false, false, false, true>;
+__global__ __launch_bounds__(256) void dqnope_kernel(const bf16* __restrict__ dqabs,
+                                                     const bf16* __restrict__ w_uk,
+                                                     const int4* __restrict__ srec,
+                                                     const int32_t* __restrict__ status,
+                                                     bf16* __restrict__ dq_nope, int N, int L5) {
+    __shared__ __attribute__((aligned(16))) bf16 lds[CfgDqn::LDS_ELEMS];
+    const int rows = kBlock * status[kStKeptCount];
+    const int n0 = blockIdx.y * CfgDqn::BN, h = blockIdx.z;
+    if (n0 >= rows) return;
+    const bf16* wh = w_uk + (size_t)h * kDc * kD;
+    auto arow = [&](int r) -> const bf16* { return wh + (size_t)r * kD; };
+    auto brow = [&](int r) -> const bf16* {
+        const int R = n0 + r;
+        return R < rows ? dqabs + ((size_t)R * kH + h) * kD : nullptr;
+    };
+    f32x4 acc[CfgDqn::MT][CfgDqn::NT];
+    gemm_tile<CfgDqn>(arow, brow, 0, kD / 32, lds, acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
+    const int wm = wave / CfgDqn::WN, wn = wave % CfgDqn::WN;
+#pragma unroll
+    for (int j = 0; j < CfgDqn::NT; ++j) {
+        const int R = n0 + wn * (CfgDqn::BN / 2) + 16 * j + l16;
+        if (R >= rows) continue;
+        bf16* dst = dq_nope + (input_row(srec, R, N, L5) * kH + h) * kDc;
+#pragma unroll
+        for (int i = 0; i < CfgDqn::MT; ++i)
+            gst8(dst + wm * (CfgDqn::BM / 2) + 16 * i + 4 * g, to_bf16x4(acc[i][j]));
+    }
+}
+
+// ---- weight gradients, a reduction over every kept row: M = D (latent
+// positions, permuted), N = d_v or d_c, K = rows.  Both operands transposed.
+// The 8 (dW_UV) or 4 (dW_UK) tiles of a head are consecutive in the
+// XCD-remapped order, so they share the rows they stream through one L2.
+using CfgDwuv = Cfg<128, 128, 2, 2, true, false, true, false>;
+using CfgDwuk = Cfg<128, 192, 2, 2, true, false, true, false>;
+
+template <class C, int NOUT>
+__device__ inline void dw_tile(const bf16* __restrict__ lat, const bf16* __restrict__ rowsrc,
+                               const int4* __restrict__ srec, int rows, int h, int m0, int n0,
+                               int N, int L5, bf16* __restrict__ dw, bf16* lds) {
+    auto arow = [&](int k) -> const bf16* {
+        return k < rows ? lat + ((size_t)k * kH + h) * kD + m0 : nullptr;
+    };
+    auto brow = [&](int k) -> const bf16* {
+        return k < rows ? rowsrc + (input_row(srec, k, N, L5) * kH + h) * NOUT + n0 : nullptr;
+    };
+    f32x4 acc[C::MT][C::NT];
+    gemm_tile<C>(arow, brow, 0, (rows + 31) / 32, lds, acc);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+#pragma unroll
+    for (int j = 0; j < C::NT; ++j) {
+        const int o = n0 + wn * (C::BN / C::WN) + 16 * j + l16;
+        bf16* dst = dw + ((size_t)h * NOUT + o) * kD;
+#pragma unroll
+        for (int i = 0; i < C::MT; ++i) {
+            const int pos = m0 + wm * (C::BM / C::WM) + 16 * i + 4 * g;
+            gst8(dst + dim_of_pos4(pos), to_bf16x4(acc[i][j]));
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void dw_kernel(const bf16* __restrict__ olat,
+                                                 const bf16* __restrict__ dout,
+                                                 const bf16* __restrict__ dqabs,
+                                                 const bf16* __restrict__ q_nope,
+                                                 const int4* __restrict__ srec,
+                                                 const int32_t* __restrict__ status,
+                                                 bf16* __restrict__ dw_uv, bf16* __restrict__ dw_uk,
+                                                 int N, int L5) {
+    constexpr int kUvTiles = (kD / CfgDwuv::BM) * (kDv / CfgDwuv::BN);   // 8 per head
+    constexpr int kUkTiles = (kD / CfgDwuk::BM) * (kDc / CfgDwuk::BN);   // 4 per head
+    constexpr int kLds = CfgDwuv::LDS_ELEMS > CfgDwuk::LDS_ELEMS ? CfgDwuv::LDS_ELEMS
+                                                                  : CfgDwuk::LDS_ELEMS;
+    __shared__ __attribute__((aligned(16))) bf16 lds[kLds];
+    const int rows = kBlock * status[kStKeptCount];
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = lid / (kUvTiles + kUkTiles), t = lid % (kUvTiles + kUkTiles);
+    if (t < kUvTiles) {
+        const int m0 = (t / (kDv / CfgDwuv::BN)) * CfgDwuv::BM;
+        const int n0 = (t % (kDv / CfgDwuv::BN)) * CfgDwuv::BN;
+        dw_tile<CfgDwuv, kDv>(olat, dout, srec, rows, h, m0, n0, N, L5, dw_uv, lds);
+    } else {
+        const int m0 = (t - kUvTiles) * CfgDwuk::BM;
+        dw_tile<CfgDwuk, kDc>(dqabs, q_nope, srec, rows, h, m0, 0, N, L5, dw_uk, lds);
+    }
+}
+
+// ---- per block: dc_k (M = D, permuted positions) and d(R k^R)_k (M = d_r,
+// natural) for its key slots (N = 144), K = its 320 rows taken twice
+// (P with d_olat, then dS' with q_abs; the k^R part only dS' with R q^R).
+// The sums over blocks that share a context row go to the fp32 accumulator
+// with atomics; a block's own 5 keys are its alone.
+using CfgDkv = Cfg<64, kKeySlots, 4, 1, true, false, true, false>;
+__global__ __launch_bounds__(256) void dkv_kernel(const bf16* __restrict__ dolat,
+                                                  const bf16* __restrict__ qabs,
+                                                  const bf16* __restrict__ qrot,
+                                                  const bf16* __restrict__ pmat,
+                                                  const bf16* __restrict__ dsmat,
+                                                  const int4* __restrict__ srec,
+                                                  const int32_t* __restrict__ status,
+                                                  float* __restrict__ acc, int S, int N, int L5) {
+    __shared__ __attribute__((aligned(16))) bf16 lds[CfgDkv::LDS_ELEMS];
+    constexpr int kTiles = (kD + kDr) / CfgDkv::BM;    // 9
+    constexpr int kRows = kBlock * kH;                 // 320
+    const int n_live = status[kStKeptCount];
+    const int lid = xcd_balance(blockIdx.x, n_live * kTiles);
+    if (lid < 0) return;
+    const int slot = lid / kTiles, mt = lid % kTiles;
+    const int m0 = mt * CfgDkv::BM;
+    const size_t lat0 = (size_t)kBlock * slot * kH;    // first latent row (t = 0, h = 0)
+    const bf16* pm = pmat + (size_t)slot * kRows * kKeySlots;
+    const bf16* ds = dsmat + (size_t)slot * kRows * kKeySlots;
+    const bool rope_tile = m0 >= kD;
+    auto arow = [&](int k) -> const bf16* {
+        if (rope_tile) return qrot + (lat0 + (k - kRows)) * kDr;
+        return (k < kRows) ? dolat + (lat0 + k) * kD + m0 : qabs + (lat0 + k - kRows) * kD + m0;
+    };
+    auto brow = [&](int k) -> const bf16* {
+        return (k < kRows) ? pm + (size_t)k * kKeySlots : ds + (size_t)(k - kRows) * kKeySlots;
+    };
+    f32x4 a[CfgDkv::MT][CfgDkv::NT];
+    gemm_tile<CfgDkv>(arow, brow, rope_tile ? kRows / 32 : 0, 2 * kRows / 32, lds, a);
+
+    const int4 rec = srec[slot];
+    const int blk = rec.w, b = blk / N, n = blk % N;
+    const int ctx_lo = rec.x, ctx_len = rec.y, nkeys = ctx_len + kBlock;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
+    const size_t arow0 = (size_t)b * (S + L5);
+    const int pos = wave * 16 + 4 * g;                  // CfgDkv: WM = 4, MT = 1
+    const int dim = rope_tile ? kD + pos : dim_of_pos4(m0 + pos);
+#pragma unroll
+    for (int j = 0; j < CfgDkv::NT; ++j) {
+        const int key = 16 * j + l16;
+        if (key >= nkeys) continue;
+        const size_t r = arow0 + ((key < ctx_len) ? (size_t)(ctx_lo + key)
+                                                  : (size_t)S + kBlock * n + (key - ctx_len));
+        float* dst = acc + r * (kD + kDr) + dim;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) atomicAdd(dst + i, a[0][j][i]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dolat(const Problem& p, const Inputs& in, const BwdGrads& g,
+                            const BwdWork& w, hipStream_t s) {
+    const int rows = kBlock * p.B * p.N;
+    const dim3 grid(kD / CfgDolat::BM, (rows + CfgDolat::BN - 1) / CfgDolat::BN, kH);
+    hipLaunchKernelGGL(dolat_kernel, grid, dim3(256), 0, s, (const bf16*)g.dout,
+                       (const bf16*)in.w_uv, w.fwd.srec, w.fwd.status, w.dolat, p.N, p.L5);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dqnope(const Problem& p, const Inputs& in, const BwdGrads& g,
+                             const BwdWork& w, hipStream_t s) {
+    const int rows = kBlock * p.B * p.N;
+    const dim3 grid(1, (rows + CfgDqn::BN - 1) / CfgDqn::BN, kH);
+    hipLaunchKernelGGL(dqnope_kernel, grid, dim3(256), 0, s, w.dqabs, (const bf16*)in.w_uk,
+                       w.fwd.srec, w.fwd.status, (bf16*)g.dq_nope, p.N, p.L5);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dw(const Problem& p, const Inputs& in, const BwdGrads& g,
+                         const BwdWork& w, hipStream_t s) {
+    constexpr int kPerHead = (kD / CfgDwuv::BM) * (kDv / CfgDwuv::BN) +
+                             (kD / CfgDwuk::BM) * (kDc / CfgDwuk::BN);   // 12
+    hipLaunchKernelGGL(dw_kernel, dim3(kH * kPerHead), dim3(256), 0, s, w.fwd.olat,
+                       (const bf16*)g.dout, w.dqabs, (const bf16*)in.q_nope, w.fwd.srec,
+                       w.fwd.status, (bf16*)g.dw_uv, (bf16*)g.dw_uk, p.N, p.L5);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkv(const Problem& p, const BwdWork& w, hipStream_t s) {
+    constexpr int kTiles = (kD + kDr) / CfgDkv::BM;
+    int grid = p.B * p.N * kTiles;
+    grid = (grid + 7) / 8 * 8;
+    hipLaunchKernelGGL(dkv_kernel, dim3(grid), dim3(256), 0, s, w.dolat, w.fwd.qabs, w.qrot,
+                       w.pmat, w.dsmat, w.fwd.srec, w.fwd.status, w.acc, p.S, p.N, p.L5);
+    return hipGetLastError();
+}
+
+}  // namespace dspark

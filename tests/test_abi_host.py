@@ -29,12 +29,13 @@ def test_library_exports_every_declared_symbol():
     declared = header_functions()
     assert {"dspark_attn_fwd", "dspark_attn_workspace_size", "dspark_build_index",
             "dspark_select_anchors_host", "dspark_read_device_status", "dspark_last_error",
-            "dspark_abi_version", "dspark_attn_fwd_ex"} <= declared
+            "dspark_abi_version", "dspark_attn_fwd_ex", "dspark_attn_bwd",
+            "dspark_attn_bwd_ex", "dspark_attn_bwd_workspace_size", "dspark_attn_bwd_plan"} <= declared
     lib = ctypes.CDLL(sd.LIB_PATH)
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert set(sd.EXPORTS) == declared
-    assert sd.abi_version() == 2
+    assert sd.abi_version() == 3
 
 
 def glm_desc(**kw):
@@ -192,3 +193,72 @@ def test_sampler_matches_oracle_on_benchmark_masks(k):
         a_o, k_o = O.select_anchors(wl.loss_mask[b], wl.N, wl.sampler_seed + b)
         assert np.array_equal(a_c, a_o) and np.array_equal(k_c, k_o)
         assert k_c.all()
+
+
+# ---------------------------------------------------------------------------
+# backward entry points: validation before any launch
+# ---------------------------------------------------------------------------
+
+def _bwd_call(d, ptrs, ws, ws_bytes, opts=None):
+    lib = sd._lib.lib
+    if opts is None:
+        return lib.dspark_attn_bwd(ctypes.byref(d), *ptrs, ws, ws_bytes, None)
+    return lib.dspark_attn_bwd_ex(ctypes.byref(d), *ptrs, ws, ws_bytes, None, ctypes.byref(opts))
+
+
+def test_bwd_workspace_holds_forward_area_and_accumulators():
+    d = glm_desc(B=1, S=2048, N=64)
+    fwd, bwd = sd.workspace_size(d), sd.bwd_workspace_size(d)
+    rows = 5 * 64
+    acc = (2048 + rows) * (512 + 64) * 4
+    lat = rows * 64 * 512 * 2
+    pm = 64 * rows * 144 * 2
+    assert bwd >= fwd + acc + 2 * lat + rows * 64 * 64 * 2 + 2 * pm
+    g = glm_desc(dtype="f32", B=1, S=2048, N=64)
+    wacc = 64 * (192 + 256) * 512 * 4
+    assert sd.bwd_workspace_size(g) >= sd.workspace_size(g) + acc + wacc
+    # the MFMA-path size also covers force_generic (weight accumulators)
+    small = glm_desc(B=1, S=300, N=12)
+    assert sd.bwd_workspace_size(small) >= (300 + 60) * (512 + 64) * 4 + wacc
+
+
+def test_bwd_null_misaligned_and_workspace_errors_before_any_launch():
+    d = glm_desc()
+    good = [0x10000 * (i + 1) for i in range(19)]
+    need = sd.bwd_workspace_size(d)
+    ws = 0x7000000
+    for i in range(19):
+        p = list(good)
+        p[i] = None
+        assert _bwd_call(d, p, ws, need) == sd.DSPARK_EINVAL
+        assert "NULL" in sd.last_error()
+    p = list(good)
+    p[12] += 8
+    assert _bwd_call(d, p, ws, need) == sd.DSPARK_EINVAL and "aligned" in sd.last_error()
+    assert _bwd_call(d, good, ws, need - 1) == sd.DSPARK_EWORKSPACE
+    assert _bwd_call(d, good, ws + 64, need) == sd.DSPARK_EWORKSPACE
+    # d_rope = 0: the six rope pointers may be NULL (generic path, no launch
+    # happens here because the workspace is too small)
+    z = glm_desc(d_rope=0)
+    p = list(good)
+    for i in (1, 3, 5, 12, 14, 16):
+        p[i] = None
+    assert _bwd_call(z, p, ws, 0) == sd.DSPARK_EWORKSPACE
+
+
+def test_bwd_plan_and_event_count_check():
+    d = glm_desc()
+    assert sd.bwd_plan(d) == 10 and sd.bwd_plan(d, force_generic=True) == 5
+    assert sd.bwd_plan(glm_desc(dtype="f32")) == 5 and sd.bwd_plan(glm_desc(N=0)) == 0
+    opts = sd._lib.Opts()
+    ev = (ctypes.c_void_p * 3)(0x10, 0x20, 0x30)
+    opts.stage_events = ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p))
+    opts.n_stage_events = 3
+    good = [0x10000 * (i + 1) for i in range(19)]
+    st = _bwd_call(d, good, 0x7000000, sd.bwd_workspace_size(d), opts)
+    assert st == sd.DSPARK_EINVAL and "stage events" in sd.last_error()
+
+
+def test_bwd_empty_problem_is_a_no_op():
+    d = glm_desc(N=0)
+    assert sd._lib.lib.dspark_attn_bwd(ctypes.byref(d), *([None] * 20), 0, None) == sd.DSPARK_OK

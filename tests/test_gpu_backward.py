@@ -1,0 +1,210 @@
+"""Parity of the HIP backward (dspark_attn_bwd through the C ABI) with the
+fp64 oracle's backward, on the same seeded inputs and upstream gradient.
+
+Tolerances (per gradient tensor, over every element):
+  * fp32 generic path: rel-L2 <= 2e-5 and max|err| <= 1e-4 * max|ref|.
+    Every value is a short chain of fp32 dot products (<= 512 terms), an
+    fp32 softmax and an fp32 rotation; sums over blocks and heads are fp32
+    atomics in any order.  Measured errors are ~1e-6 relative.
+  * bf16 storage: every output is rounded to bf16 once (relative error
+    <= 2^-9, RMS ~1.1e-3).  The MFMA path also rounds its intermediates to
+    bf16 (q_abs, W_UV^T dout, P, dS', o_lat, dq_abs, rotated q^R: <= 4 such
+    roundings on any chain), so its error is a few times that of one
+    rounding: rel-L2 <= 1e-2 and max|err| <= 3e-2 * max|ref|, with the
+    generic bf16 path (fp32 intermediates) held to rel-L2 <= 5e-3.
+Rows that no kept block reaches must be exactly 0 (padding blocks' query
+and key rows, context rows outside every window); outputs are pre-filled
+with NaN so that an element the library does not write fails the check.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as wk
+from gpu_util import anchors_for, desc_for, log, sample_blocks
+from workloads.device import to_torch, upload_anchors, upload_layer
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq_nope", "dq_rope", "dckv_ctx", "dkr_ctx", "dckv_blk", "dkr_blk", "dw_uk", "dw_uv")
+F32_TOL = (2e-5, 1e-4)
+BF16_GENERIC_TOL = (5e-3, 2e-2)
+BF16_MFMA_TOL = (1e-2, 3e-2)
+
+
+class GpuBwd:
+    """Uploads one layer and an upstream gradient, owns the gradient outputs
+    (NaN-filled) and the workspace, runs dspark_attn_bwd."""
+
+    def __init__(self, wl, dout, anchors, keep, force_generic=False):
+        import torch
+        import speculative_decoding_draft_amd as sd
+        self.sd, self.torch, self.wl = sd, torch, wl
+        self.desc = desc_for(wl)
+        self.t = upload_layer(wl)
+        self.dout = to_torch(dout, wl.dtype, "cuda")
+        self.anchors, self.keep = upload_anchors(anchors, keep)
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        B, S, L5, H = wl.B, wl.S, wl.q_len, wl.H
+        shapes = {"dq_nope": (B, L5, H, wl.d_c), "dq_rope": (B, L5, H, wl.d_r),
+                  "dckv_ctx": (B, S, wl.D), "dkr_ctx": (B, S, wl.d_r),
+                  "dckv_blk": (B, L5, wl.D), "dkr_blk": (B, L5, wl.d_r),
+                  "dw_uk": (H, wl.d_c, wl.D), "dw_uv": (H, wl.d_v, wl.D)}
+        self.g = {k: torch.full(v, float("nan"), dtype=tdt, device="cuda")
+                  for k, v in shapes.items()}
+        self.ws = torch.empty(sd.bwd_workspace_size(self.desc), dtype=torch.uint8, device="cuda")
+        self.force_generic = force_generic
+
+    def run(self):
+        t = self.t
+        self.sd.attn_bwd(self.desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"],
+                         t["ckv_blk"], t["kr_blk"], t["w_uk"], t["w_uv"], self.anchors,
+                         self.keep, self.dout, self.g, self.ws,
+                         force_generic=self.force_generic)
+        return self
+
+    def result(self) -> dict:
+        self.torch.cuda.synchronize()
+        return {k: v.float().cpu().numpy().astype(np.float64) for k, v in self.g.items()}
+
+
+def check(gpu: dict, ref: dict, tol, what: str, names=GRADS, rows=None) -> None:
+    """rows: None, or {name: boolean mask over the leading dims} restricting
+    the comparison (elements outside are not checked)."""
+    rel_tol, abs_tol = tol
+    for k in names:
+        g, r = gpu[k], ref[k]
+        if rows is not None and k in rows:
+            g, r = g[rows[k]], r[rows[k]]
+        assert np.all(np.isfinite(g)), f"{what} {k}: non-finite values"
+        scale = np.abs(r).max()
+        if scale == 0:
+            assert np.all(g == 0), f"{what} {k}: expected all zero"
+            continue
+        err = np.abs(g - r)
+        rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+        mx = float(err.max() / scale)
+        log(f"  {what} {k}: rel_l2={rel:.3e} max_abs/max|ref|={mx:.3e} n={g.size}")
+        assert rel <= rel_tol, f"{what} {k}: rel_l2 {rel} > {rel_tol}"
+        assert mx <= abs_tol, f"{what} {k}: max_abs {mx} > {abs_tol} of max|ref|"
+
+
+def unreached_rows_are_zero(gpu: dict, wl, anchors, keep) -> None:
+    """Rows of padding blocks and context rows outside every window."""
+    for b in range(wl.B):
+        seen = np.zeros(wl.S, bool)
+        for n in range(wl.N):
+            if keep[b, n]:
+                A = int(anchors[b, n])
+                seen[max(0, A - wl.W + 1):A] = True
+            else:
+                r = slice(5 * n, 5 * n + 5)
+                for k in ("dq_nope", "dq_rope", "dckv_blk", "dkr_blk"):
+                    assert np.all(gpu[k][b, r] == 0), (k, b, n)
+        assert np.all(gpu["dckv_ctx"][b][~seen] == 0) and np.all(gpu["dkr_ctx"][b][~seen] == 0)
+
+
+def run_case(wl, force_generic=False, tol=None, form="dense"):
+    ga, gk, oa, ok = anchors_for(wl)
+    assert np.array_equal(ga, oa) and np.array_equal(gk, ok)
+    dout = wk.make_dout(wl, seed=11)
+    log(f"case {wl.name} generic={force_generic}")
+    gpu = GpuBwd(wl, dout, ga, gk, force_generic=force_generic).run().result()
+    ref = O.backward(wl, dout, anchors=oa, keep=ok, form=form)
+    check(gpu, ref, tol, wl.name)
+    unreached_rows_are_zero(gpu, wl, oa, ok)
+    return gpu
+
+
+def test_bwd_tiny_fp32_generic():
+    run_case(wk.config(1), tol=F32_TOL)
+
+
+@pytest.mark.parametrize("k,S,N", [(1, 90, 12), (4, 120, 16)])
+def test_bwd_tiny_dims_fp32_recipes(k, S, N):
+    wl = wk.scaled(k, S=S, N=N, dims=wk.TINY_DIMS, dtype="f32")
+    run_case(wl, tol=F32_TOL)
+
+
+def test_bwd_generic_bf16_glm_dims():
+    wl = wk.scaled(4, S=300, N=12)
+    run_case(wl, force_generic=True, tol=BF16_GENERIC_TOL, form="gathered")
+
+
+@pytest.mark.parametrize("k,S,N", [(2, 512, 16), (3, 640, 16), (4, 1024, 40)])
+def test_bwd_mfma_scaled(k, S, N):
+    wl = wk.scaled(k, S=S, N=N)
+    run_case(wl, tol=BF16_MFMA_TOL, form="gathered")
+
+
+def test_bwd_mfma_matches_generic_path():
+    """Both GPU paths on the same bf16 problem agree to the MFMA tolerance."""
+    wl = wk.scaled(4, S=400, N=16)
+    ga, gk, _, _ = anchors_for(wl)
+    dout = wk.make_dout(wl, seed=12)
+    fast = GpuBwd(wl, dout, ga, gk).run().result()
+    gen = GpuBwd(wl, dout, ga, gk, force_generic=True).run().result()
+    check(fast, gen, BF16_MFMA_TOL, "mfma vs generic")
+
+
+def test_bwd_repeat_runs_agree():
+    """A second call on the same workspace gives the same gradients (the
+    accumulators are cleared by every call; atomics may reorder fp32 sums)."""
+    wl = wk.scaled(2, S=512, N=16)
+    ga, gk, _, _ = anchors_for(wl)
+    run = GpuBwd(wl, wk.make_dout(wl, seed=13), ga, gk)
+    a = run.run().result()
+    b = run.run().result()
+    for k in GRADS:
+        if k in ("dckv_ctx", "dkr_ctx", "dckv_blk", "dkr_blk"):
+            np.testing.assert_allclose(b[k], a[k], rtol=1e-2, atol=1e-2 * np.abs(a[k]).max())
+        else:
+            assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_bwd_bad_anchor_rows_are_nan(generic):
+    """A kept block with an anchor outside [0, S-2]: its query-gradient rows
+    are NaN, the status reports it, and every other gradient equals the
+    oracle's with that block treated as padding."""
+    import speculative_decoding_draft_amd as sd
+    wl = wk.scaled(4, S=300, N=12)
+    anchors, keep = wl.anchors.copy(), wl.keep.copy()
+    bad = int(np.nonzero(keep[0])[0][3])
+    anchors[0, bad] = wl.S + 3
+    dout = wk.make_dout(wl, seed=14)
+    run = GpuBwd(wl, dout, anchors, keep, force_generic=generic).run()
+    gpu = run.result()
+    st, first = sd.read_device_status(run.ws)
+    assert st == sd.DSPARK_EANCHOR and first == bad
+    r = slice(5 * bad, 5 * bad + 5)
+    assert np.all(np.isnan(gpu["dq_nope"][0, r])) and np.all(np.isnan(gpu["dq_rope"][0, r]))
+    gpu["dq_nope"][0, r] = 0
+    gpu["dq_rope"][0, r] = 0
+    keep_ref = keep.copy()
+    keep_ref[0, bad] = 0
+    ref = O.backward(wl, dout, anchors=anchors, keep=keep_ref, form="gathered")
+    check(gpu, ref, BF16_GENERIC_TOL if generic else BF16_MFMA_TOL, f"bad anchor generic={generic}")
+
+
+def test_bwd_headline_full_size_sampled_blocks():
+    """Full headline size (B=1, S=32768, N=1024, 25 % padding) in the launch
+    configuration the benchmark times: the query gradients and the block-key
+    gradients of sampled blocks (every clamped-window block and random
+    others) come from that block alone and are checked against the oracle
+    block by block; every row no kept block reaches must be 0."""
+    wl = wk.config(4)
+    dout = wk.make_dout(wl, seed=15)
+    log("case headline full size")
+    gpu = GpuBwd(wl, dout, wl.anchors, wl.keep).run().result()
+    unreached_rows_are_zero(gpu, wl, wl.anchors, wl.keep)
+    for k in GRADS:
+        assert np.all(np.isfinite(gpu[k])), k
+    pick = sample_blocks(wl.keep[0], wl.anchors[0], wl.W, n_random=6, seed=3)[:14]
+    ref = O.backward(wl, dout, form="gathered", blocks=[(0, n) for n in pick])
+    rows = np.zeros((1, wl.q_len), bool)
+    for n in pick:
+        rows[0, 5 * n:5 * n + 5] = True
+    check(gpu, ref, BF16_MFMA_TOL, "headline sampled", names=("dq_nope", "dq_rope", "dckv_blk",
+                                                              "dkr_blk"),
+          rows={k: rows for k in ("dq_nope", "dq_rope", "dckv_blk", "dkr_blk")})
