@@ -1,4 +1,4 @@
-"""Benchmark of the DSpark draft-attention forward on one MI355X.
+"""Benchmark of the DSpark draft-attention forward (and backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
 
@@ -18,6 +18,11 @@ only (--event-every), since each event orders the kernels around it.
 Useful FLOP count only what the absorbed method must compute for kept blocks
 and visible keys: per kept block 5*H*(2*d_c*D + 2*(D+d_r)*v + 2*D*v + 2*D*d_v)
 with v = min(A, W-1) + 5.
+
+The same line carries a "backward" object: dspark_attn_bwd on the same
+inputs with a seeded upstream gradient (--bwd-steps timed calls), its useful
+TFLOP/s (gradient products only; see bwd_useful_flop) and per-launch times.
+The headline metric is the forward's.
 """
 from __future__ import annotations
 
@@ -96,6 +101,115 @@ def stage_bytes(wl, anchors, keep, chunk_blocks):
         out["absorb"].append(rows * H * (dc + D) * 2 + H * dc * D * 2)
         out["attention"].append(rows * H * (D + dr + D) * 2 + (union + rows) * (D + dr) * 2)
         out["w_uv"].append(rows * H * (D + dv) * 2 + H * dv * D * 2)
+    return out
+
+
+BWD_STAGES = ("index", "order", "clear", "absorb", "d_olat", "attention_bwd", "dkv",
+              "dq_nope", "dw", "final")
+
+
+def bwd_useful_flop(anchors, keep, W, H, D, d_c, d_r, d_v, block=5) -> int:
+    """Gradient products the backward must compute per kept block (the
+    forward values it recomputes -- q_abs, scores, o_lat -- are not counted):
+    per (query, head) 2 d_v D (W_UV^T dout) + 2 d_v D (dW_UV) + 2 D v (dP)
+    + 2 (D + d_r) v (dq_abs, dq^R) + 4 D v + 2 d_r v (dc^KV, dk^R)
+    + 2 d_c D (dq^C) + 2 d_c D (dW_UK); about twice the forward's count."""
+    total = 0
+    for a, k in zip(np.asarray(anchors).ravel(), np.asarray(keep).ravel()):
+        if k:
+            v = min(int(a), W - 1) + block
+            total += block * H * (4 * d_v * D + 4 * d_c * D + 8 * D * v + 4 * d_r * v)
+    return total
+
+
+def bwd_stage_bytes(wl, anchors, keep):
+    """Algorithmic HBM bytes of each backward launch (bf16 = 2 B, fp32
+    accumulators 4 B): every input read once, every output written once,
+    intermediates written by one launch and read by the next."""
+    H, D, dc, dr, dv = wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v
+    kept = [(b, int(anchors[b, n])) for b in range(wl.B) for n in range(wl.N) if keep[b, n]]
+    rows = 5 * len(kept)
+    union = 0
+    vsum = 0
+    for b in range(wl.B):
+        cover = np.zeros(wl.S, dtype=bool)
+        for bb, a in kept:
+            if bb == b:
+                cover[max(0, a - wl.W + 1):a] = True
+                vsum += min(a, wl.W - 1) + 5
+        union += int(cover.sum())
+    lat = rows * H * D * 2
+    pm = len(kept) * 5 * H * 144 * 2
+    acc = wl.B * (wl.S + 5 * wl.N) * (D + dr) * 4
+    part = vsum * (D + dr) * 4          # each block's partial rows
+    out_kv = wl.B * (wl.S + 5 * wl.N) * (D + dr) * 2
+    return {
+        "absorb": rows * H * dc * 2 + H * dc * D * 2 + lat,
+        "d_olat": rows * H * dv * 2 + H * dv * D * 2 + lat,
+        "attention_bwd": 2 * lat + rows * H * dr * 2 + (union + rows) * (D + dr) * 2
+                         + 2 * lat + rows * H * dr * 2 + 2 * pm + rows * H * dr * 2,
+        "dkv": 2 * lat + rows * H * dr * 2 + 2 * pm + part,
+        "dq_nope": lat + H * dc * D * 2 + rows * H * dc * 2,
+        "dw": 2 * lat + rows * H * (dv + dc) * 2 + H * (dc + dv) * D * 2,
+        "final": part + out_kv,
+    }
+
+
+def bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sptr, hip,
+                   steps):
+    """Times dspark_attn_bwd on the same inputs (layer 0) with a seeded
+    upstream gradient; per-launch durations from the library's stage events
+    on one extra call."""
+    import workloads as wk
+    from workloads.device import to_torch
+    t = tensors[0]
+    dout = to_torch(wk.make_dout(wl, seed=11), wl.dtype, "cuda")
+    B, S, L5, H = wl.B, wl.S, wl.q_len, wl.H
+    shapes = {"dq_nope": (B, L5, H, wl.d_c), "dq_rope": (B, L5, H, wl.d_r),
+              "dckv_ctx": (B, S, wl.D), "dkr_ctx": (B, S, wl.d_r),
+              "dckv_blk": (B, L5, wl.D), "dkr_blk": (B, L5, wl.d_r),
+              "dw_uk": (H, wl.d_c, wl.D), "dw_uv": (H, wl.d_v, wl.D)}
+    g = {k: torch.empty(v, dtype=torch.bfloat16, device="cuda") for k, v in shapes.items()}
+    ws = torch.empty(sd.bwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    args = (desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"], t["kr_blk"],
+            t["w_uk"], t["w_uv"], a_dev, k_dev, dout, g, ws)
+    w0, n_w = time.perf_counter(), 0
+    while n_w < 3 or (time.perf_counter() - w0) < 0.1:
+        sd.attn_bwd(*args, stream=sptr)
+        n_w += 1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sd.attn_bwd(*args, stream=sptr)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    n_ev = sd.bwd_plan(desc)
+    names = BWD_STAGES if n_ev == len(BWD_STAGES) + 1 else None
+    ev = hip.create(n_ev)
+    sd.attn_bwd(*args, stream=sptr, stage_events=ev)
+    torch.cuda.synchronize()
+    stage_us = {}
+    if names:
+        for i, s in enumerate(names):
+            stage_us[s] = hip.elapsed_ms(ev[i], ev[i + 1]) * 1e3
+    hip.destroy(ev)
+    flop = bwd_useful_flop(anchors, keep, wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v)
+    out = {"ms_per_step": round(wall * 1e3, 4), "steps": steps, "warmup": n_w,
+           "useful_gflop_per_step": round(flop / 1e9, 3),
+           "value": round(flop / wall / 1e12, 3), "unit": "TFLOP/s",
+           "frac_of_bf16_peak": round(flop / wall / 1e12 / MI355X_BF16_PEAK_TFLOPS, 4),
+           "stage_us": {k: round(v, 2) for k, v in stage_us.items()}}
+    if stage_us:
+        nb = bwd_stage_bytes(wl, anchors, keep)
+        dom = max(stage_us, key=lambda s: stage_us[s])
+        ach = nb[dom] / (stage_us[dom] * 1e-6) / 1e9
+        out["stage_gbs"] = {k: round(nb[k] / (v * 1e-6) / 1e9, 1) for k, v in stage_us.items()
+                            if k in nb and v > 0}
+        out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1),
+                           "peak": MI355X_HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(ach / MI355X_HBM_PEAK_GBS, 4), "traffic": None,
+                           "avg_launch_us": round(stage_us[dom], 2),
+                           "algorithmic_bytes_per_launch": nb[dom]}
     return out
 
 
@@ -178,6 +292,9 @@ def main():
     ap.add_argument("--event-every", type=int, default=10,
                     help="record per-kernel stage events on every n-th timed step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the backward measurement (the 'backward' object)")
+    ap.add_argument("--bwd-steps", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (the reference "
@@ -335,6 +452,12 @@ def main():
                      "algorithmic_bytes_per_launch": round(avg_launch_bytes)},
         "cpu_baseline": None,
     }
+    if not args.no_bwd and wl.dtype == "bf16":
+        try:
+            result["backward"] = bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors,
+                                                keep, desc, sptr, hip, args.bwd_steps)
+        except Exception as e:   # the forward line is still reported
+            result["backward"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, anchors, keep, args.cpu_budget)
     print(json.dumps(result), flush=True)

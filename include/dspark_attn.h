@@ -221,9 +221,12 @@ size_t dspark_attn_bwd_workspace_size(const dspark_attn_desc* desc);
  * Rows no kept block reaches (padding blocks' queries and keys, context rows
  * outside every window) are 0.  The query rows of a kept block whose anchor
  * lies outside [0, S-2] are NaN and the block contributes nothing else
- * (dspark_read_device_status reports DSPARK_EANCHOR).  Sums over blocks and
- * heads (c^KV, k^R) are accumulated in fp32 with device atomics, so their
- * last bits can differ from run to run; everything else is deterministic.
+ * (dspark_read_device_status reports DSPARK_EANCHOR).  Sums over heads and
+ * over the blocks whose windows share a context row are fp32.  On the MFMA
+ * path, when every sample's kept anchors ascend (as the sampler returns
+ * them), each block's share is written once and summed per row in a fixed
+ * order, so results are deterministic; otherwise (and on the generic path)
+ * the sums use device atomics and their last bits can differ between runs.
  * d_rope = 0 allows NULL for q_rope, kr_ctx, kr_blk, dq_rope, dkr_ctx,
  * dkr_blk.  Outputs must not alias inputs, each other or the workspace. */
 dspark_status dspark_attn_bwd(const dspark_attn_desc* desc,
@@ -242,9 +245,10 @@ dspark_status dspark_attn_bwd(const dspark_attn_desc* desc,
 /* dspark_attn_bwd with options (opts may be NULL).  Used fields:
  * force_generic, and stage_events: event [0] is recorded before the first
  * launch and event [k] after the k-th, all on `stream`; the MFMA path makes
- * 9 launches (accumulator clear, index, absorb, W_UV^T dout, attention
- * backward, dc^KV / dk^R products, dq^C, weight gradients, final pass), the
- * generic path 4 (clear, index and RoPE table, generic kernel, final pass).
+ * 10 launches (index, anchor-order check, accumulator clear, absorb,
+ * W_UV^T dout, attention backward, dc^KV / dk^R products, dq^C, weight
+ * gradients, final pass), the generic path 4 (index and RoPE table,
+ * accumulator clear, generic kernel, final pass).
  * chunk_blocks and aux_stream are ignored: the backward runs as one round. */
 dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc,
                                  const void* q_nope, const void* q_rope,

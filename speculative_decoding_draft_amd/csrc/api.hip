@@ -128,15 +128,17 @@ BwdWork carve_bwd(void* base, const BwdLayout& L) {
     w.qrot = reinterpret_cast<bf16*>(at(L.qrot));
     w.pmat = reinterpret_cast<bf16*>(at(L.pmat));
     w.dsmat = reinterpret_cast<bf16*>(at(L.dsmat));
+    w.part = reinterpret_cast<float*>(at(L.part));
     w.acc = reinterpret_cast<float*>(c + L.acc);
     w.wacc = reinterpret_cast<float*>(at(L.wacc));
     return w;
 }
 
-// launches of dspark_attn_bwd_ex: zero, index, absorb, d_olat, attention,
-// dc^KV, dq^C, dW, final (MFMA path); zero, index + RoPE table, generic
-// kernel, final (generic path)
-constexpr int kBwdLaunchesFast = 9, kBwdLaunchesGeneric = 4;
+// launches of dspark_attn_bwd_ex: index, anchor-order check, accumulator
+// clear (a no-op unless the anchors are unsorted), absorb, d_olat,
+// attention, dc^KV, dq^C, dW, final (MFMA path); index + RoPE table, clear,
+// generic kernel, final (generic path)
+constexpr int kBwdLaunchesFast = 10, kBwdLaunchesGeneric = 4;
 
 RopeTheta make_theta(const dspark_attn_desc& d) {
     RopeTheta th;
@@ -393,10 +395,12 @@ dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc, const void* q_nop
     if ((e = mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
     size_t zero_n = L.acc_rows * size_t(d.d_latent + d.d_rope);
     if (!fast) zero_n = (L.total - L.acc) / 4;     // accumulators, then the weight ones
-    DSPARK_STEP(launch_bwd_zero(w.acc, zero_n, s), "accumulator clear launch");
     DSPARK_STEP(launch_prep(p, anchors, keep, w.fwd, nullptr, L.fwd.rope_rows,
                             fast ? nullptr : &theta, nullptr, s),
                 "index launch");
+    if (fast) DSPARK_STEP(launch_bwd_order(p, w, s), "anchor-order launch");
+    DSPARK_STEP(launch_bwd_zero(w.acc, zero_n, fast ? w.fwd.status + kStUnsorted : nullptr, s),
+                "accumulator clear launch");
     if (fast) {
         DSPARK_STEP(launch_absorb(p, in, w.fwd, Chunk{0, d.B * d.N}, s), "absorb launch");
         DSPARK_STEP(launch_bwd_dolat(p, in, g, w, s), "d_olat launch");
@@ -408,9 +412,12 @@ dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc, const void* q_nop
         DSPARK_STEP(launch_bwd_generic(p, d.dtype == DSPARK_BF16, in, g, w, s),
                     "generic backward launch");
     }
-    DSPARK_STEP(launch_bwd_finalize(p, d.dtype == DSPARK_BF16, g, w, w.fwd.idx,
-                                    fast ? nullptr : w.fwd.rope, theta, !fast, s),
-                "final backward launch");
+    if (fast)
+        DSPARK_STEP(launch_bwd_gather(p, g, w, theta, s), "final backward launch");
+    else
+        DSPARK_STEP(launch_bwd_finalize(p, d.dtype == DSPARK_BF16, g, w, w.fwd.idx, w.fwd.rope,
+                                        theta, true, s),
+                    "final backward launch");
 #undef DSPARK_STEP
     return ok();
 }

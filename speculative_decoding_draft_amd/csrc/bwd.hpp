@@ -17,6 +17,8 @@ namespace dspark {
 //   qrot  bf16 [5*B*N][H][d_r] rotated q^R
 //   pmat  bf16 [B*N][5H][144]  softmax weights, row = t*H + h, column = key slot
 //   dsmat bf16 [B*N][5H][144]  scale * dS, same layout
+//   part  f32 [B*N][132][D + d_r]  per block: dc^KV and d(rotated k^R) of its
+//                                  key slots (summed over its 5 x 64 rows)
 // Both paths:
 //   acc   f32 [B][S + 5N][D + d_r]  sums over blocks and heads of dc^KV and of
 //                                   d(rotated k^R), context rows then block rows
@@ -25,7 +27,7 @@ namespace dspark {
 // in: inside every 32-dim group, position 8g + e holds dim 16(e/4) + 4g + e%4.
 struct BwdLayout {
     WsLayout fwd;
-    size_t dolat = 0, dqabs = 0, qrot = 0, pmat = 0, dsmat = 0, acc = 0, wacc = 0;
+    size_t dolat = 0, dqabs = 0, qrot = 0, pmat = 0, dsmat = 0, part = 0, acc = 0, wacc = 0;
     size_t acc_rows = 0;   // B * (S + 5N)
     size_t total = 0;
 };
@@ -45,6 +47,8 @@ inline BwdLayout bwd_layout(const dspark_attn_desc& d, bool mfma) {
         const size_t pm = blocks * kBlock * size_t(d.n_heads) * kKeySlots * 2;
         L.pmat = off;  off = align256(off + pm);
         L.dsmat = off; off = align256(off + pm);
+        L.part = off;
+        off = align256(off + blocks * kMaxKeys * size_t(d.d_latent + d.d_rope) * 4);
     }
     L.acc_rows = size_t(d.B) * (size_t(d.S) + size_t(kBlock) * d.N);
     L.acc = off; off = align256(off + L.acc_rows * size_t(d.d_latent + d.d_rope) * 4);
@@ -75,12 +79,28 @@ struct BwdWork {
     bf16* qrot;
     bf16* pmat;
     bf16* dsmat;
+    float* part;
     float* acc;
     float* wacc;
 };
 
+// Status word set by launch_bwd_order: nonzero when some sample's kept
+// anchors are not in ascending order (slot order).  Words 0 and 1 belong to
+// the index builder.
+constexpr int kStUnsorted = 2;
+
 // Zero the fp32 accumulators (and, on the generic path, the weight ones).
-hipError_t launch_bwd_zero(float* p, size_t n, hipStream_t s);
+// only_if: nullptr (always), or a status word -- the clear runs only when
+// that word is nonzero.
+hipError_t launch_bwd_zero(float* p, size_t n, const int32_t* only_if, hipStream_t s);
+// One workgroup: sets status[kStUnsorted] from the slot records.
+hipError_t launch_bwd_order(const Problem& p, const BwdWork& w, hipStream_t s);
+// MFMA path final pass: per row, the block partials of the windows that
+// cover it (ascending anchors) or the accumulator row (otherwise), converted
+// to the output type with R^T applied to dk^R; plus the query-gradient rows
+// of blocks that were not computed.
+hipError_t launch_bwd_gather(const Problem& p, const BwdGrads& g, const BwdWork& w,
+                             const RopeTheta& th, hipStream_t s);
 // Generic path: one workgroup per (block, head), fp32 arithmetic, atomics
 // into the accumulators.
 hipError_t launch_bwd_generic(const Problem& p, bool bf16_io, const Inputs& in,

@@ -314,8 +314,10 @@ __global__ __launch_bounds__(256) void dw_kernel(const bf16* __restrict__ olat,
 // ---- per block: dc_k (M = D, permuted positions) and d(R k^R)_k (M = d_r,
 // natural) for its key slots (N = 144), K = its 320 rows taken twice
 // (P with d_olat, then dS' with q_abs; the k^R part only dS' with R q^R).
-// The sums over blocks that share a context row go to the fp32 accumulator
-// with atomics; a block's own 5 keys are its alone.
+// When every sample's kept anchors ascend, each block writes its partial
+// rows and the final pass sums, per context row, the contiguous range of
+// blocks whose windows hold it; otherwise the sums go to the fp32
+// accumulator with atomics.  A block's own 5 keys are its alone.
 using CfgDkv = Cfg<64, kKeySlots, 4, 1, true, false, true, false>;
 __global__ __launch_bounds__(256) void dkv_kernel(const bf16* __restrict__ dolat,
                                                   const bf16* __restrict__ qabs,
@@ -324,6 +326,7 @@ __global__ __launch_bounds__(256) void dkv_kernel(const bf16* __restrict__ dolat
                                                   const bf16* __restrict__ dsmat,
                                                   const int4* __restrict__ srec,
                                                   const int32_t* __restrict__ status,
+                                                  float* __restrict__ part,
                                                   float* __restrict__ acc, int S, int N, int L5) {
     __shared__ __attribute__((aligned(16))) bf16 lds[CfgDkv::LDS_ELEMS];
     constexpr int kTiles = (kD + kDr) / CfgDkv::BM;    // 9
@@ -354,6 +357,17 @@ __global__ __launch_bounds__(256) void dkv_kernel(const bf16* __restrict__ dolat
     const size_t arow0 = (size_t)b * (S + L5);
     const int pos = wave * 16 + 4 * g;                  // CfgDkv: WM = 4, MT = 1
     const int dim = rope_tile ? kD + pos : dim_of_pos4(m0 + pos);
+    if (status[kStUnsorted] == 0) {
+        // the block's own partial rows; the final pass sums the blocks whose
+        // windows cover each context row
+        float* base = part + (size_t)slot * kMaxKeys * (kD + kDr) + dim;
+#pragma unroll
+        for (int j = 0; j < CfgDkv::NT; ++j) {
+            const int key = 16 * j + l16;
+            if (key < nkeys) *reinterpret_cast<f32x4*>(base + (size_t)key * (kD + kDr)) = a[0][j];
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < CfgDkv::NT; ++j) {
         const int key = 16 * j + l16;
@@ -401,7 +415,7 @@ hipError_t launch_bwd_dkv(const Problem& p, const BwdWork& w, hipStream_t s) {
     int grid = p.B * p.N * kTiles;
     grid = (grid + 7) / 8 * 8;
     hipLaunchKernelGGL(dkv_kernel, dim3(grid), dim3(256), 0, s, w.dolat, w.fwd.qabs, w.qrot,
-                       w.pmat, w.dsmat, w.fwd.srec, w.fwd.status, w.acc, p.S, p.N, p.L5);
+                       w.pmat, w.dsmat, w.fwd.srec, w.fwd.status, w.part, w.acc, p.S, p.N, p.L5);
     return hipGetLastError();
 }
 

@@ -31,7 +31,8 @@ template <typename T> __device__ inline void stf(T* p, size_t i, float v);
 template <> __device__ inline void stf<float>(float* p, size_t i, float v) { p[i] = v; }
 template <> __device__ inline void stf<bf16>(bf16* p, size_t i, float v) { p[i] = (bf16)v; }
 
-__global__ void zero_kernel(float4* __restrict__ p, size_t n4) {
+__global__ void zero_kernel(float4* __restrict__ p, size_t n4, const int32_t* only_if) {
+    if (only_if && *only_if == 0) return;
     const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
          i += (size_t)gridDim.x * blockDim.x)
@@ -307,9 +308,159 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(
     }
 }
 
+// status[kStUnsorted] = 1 when two consecutive kept slots of one sample have
+// descending anchors (slots are in (b, n) order).
+__global__ __launch_bounds__(1024) void order_kernel(const int4* __restrict__ srec,
+                                                     int32_t* __restrict__ status, int N) {
+    __shared__ int bad;
+    if (threadIdx.x == 0) bad = 0;
+    __syncthreads();
+    const int n_live = status[kStKeptCount];
+    int mine = 0;
+    for (int s = 1 + threadIdx.x; s < n_live; s += blockDim.x) {
+        const int4 a = srec[s - 1], c = srec[s];
+        mine |= (a.w / N == c.w / N) && (c.z < a.z);
+    }
+    if (mine) atomicOr(&bad, 1);
+    __syncthreads();
+    if (threadIdx.x == 0) status[kStUnsorted] = bad;
+}
+
+// First slot in [0, n) whose key (sample, anchor) is greater than (b, a);
+// slots are ordered by that key when the anchors ascend.
+__device__ inline int first_after(const int4* __restrict__ srec, int n, int N, int b, int a) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const int4 r = srec[mid];
+        const int rb = r.w / N;
+        if (rb > b || (rb == b && r.z > a)) hi = mid;
+        else lo = mid + 1;
+    }
+    return lo;
+}
+
+// One 64-lane group per row (4 rows per workgroup of 256).  A row is 144
+// float4: lane l holds float4 l and 64 + l (c^KV dims 4l.., 256 + 4l..), and
+// lanes 0..15 also float4 128 + l (k^R dims 4l .. 4l+3, rotated back).
+__global__ __launch_bounds__(256) void gather_kernel(
+    Problem p, const float* __restrict__ part, const float* __restrict__ acc,
+    const int4* __restrict__ srec, const int4* __restrict__ idx,
+    const int32_t* __restrict__ status, bf16* __restrict__ dckv_ctx, bf16* __restrict__ dkr_ctx,
+    bf16* __restrict__ dckv_blk, bf16* __restrict__ dkr_blk, bf16* __restrict__ dq_nope,
+    bf16* __restrict__ dq_rope, RopeTheta turns) {
+    __shared__ double tn[kDr / 2];
+    for (int i = threadIdx.x; i < kDr / 2; i += blockDim.x) tn[i] = turns.t[i];
+    __syncthreads();
+    const bool unsorted = status[kStUnsorted] != 0;
+    const int n_live = status[kStKeptCount];
+    const int lane = threadIdx.x & 63, sub = threadIdx.x >> 6;
+    const size_t rows_per_b = (size_t)p.S + p.L5;
+    const size_t n_rows = (size_t)p.B * rows_per_b;
+    for (size_t r = (size_t)blockIdx.x * 4 + sub; r < n_rows; r += (size_t)gridDim.x * 4) {
+        const int b = (int)(r / rows_per_b);
+        const int rr = (int)(r % rows_per_b);
+        float4 v[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int nv = (lane < kDr / 4) ? 3 : 2;
+        int pos = rr;
+        bf16 *ckv_out, *kr_out;
+        bool live = true;
+        if (rr < p.S) {
+            ckv_out = dckv_ctx + ((size_t)b * p.S + rr) * kD;
+            kr_out = dkr_ctx + ((size_t)b * p.S + rr) * kDr;
+        } else {
+            const int q = rr - p.S, n = q / kBlock, j = q % kBlock;
+            const int4 rec = idx[(size_t)b * p.N + n];
+            live = rec.w >= 0;
+            pos = live ? rec.z + j : 0;
+            ckv_out = dckv_blk + ((size_t)b * p.L5 + q) * kD;
+            kr_out = dkr_blk + ((size_t)b * p.L5 + q) * kDr;
+        }
+        auto add_row = [&](const float* src) {
+            const float4* s4 = reinterpret_cast<const float4*>(src);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                if (k < nv) {
+                    const float4 x = s4[lane + 64 * k];
+                    v[k].x += x.x; v[k].y += x.y; v[k].z += x.z; v[k].w += x.w;
+                }
+            }
+        };
+        if (live) {
+            if (unsorted) {
+                add_row(acc + r * (kD + kDr));
+            } else if (rr < p.S) {
+                // the blocks whose windows [A-W+1, A) hold row rr: r < A <= rr + W - 1
+                const int s0 = first_after(srec, n_live, p.N, b, rr);
+                const int s1 = first_after(srec, n_live, p.N, b, rr + p.W - 1);
+                for (int sl = s0; sl < s1; ++sl) {
+                    const int4 rec = srec[sl];
+                    add_row(part + ((size_t)sl * kMaxKeys + (rr - rec.x)) * (kD + kDr));
+                }
+            } else {
+                const int q = rr - p.S, n = q / kBlock, j = q % kBlock;
+                const int4 rec = idx[(size_t)b * p.N + n];
+                add_row(part + ((size_t)rec.w * kMaxKeys + rec.y + j) * (kD + kDr));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = 4 * (lane + 64 * k);
+            gst8(ckv_out + e, bf16x4{(bf16)v[k].x, (bf16)v[k].y, (bf16)v[k].z, (bf16)v[k].w});
+        }
+        if (nv == 3) {
+            const int e = 4 * lane;                   // k^R dims e .. e+3: pairs e/2, e/2+1
+            const float2 c0 = rope_cs(tn, pos, e / 2), c1 = rope_cs(tn, pos, e / 2 + 1);
+            const float4 y = v[2];
+            gst8(kr_out + e, bf16x4{(bf16)(y.x * c0.x + y.y * c0.y), (bf16)(-y.x * c0.y + y.y * c0.x),
+                                    (bf16)(y.z * c1.x + y.w * c1.y), (bf16)(-y.z * c1.y + y.w * c1.x)});
+        }
+    }
+    // query-gradient rows of blocks that were not computed: 0 (padding) or
+    // NaN (kept, bad anchor)
+    const size_t qw = (size_t)kH * (kDc + kDr);
+    for (size_t blk = blockIdx.x; blk < (size_t)p.B * p.N; blk += gridDim.x) {
+        const int4 rec = idx[blk];
+        if (rec.w >= 0) continue;
+        const bf16 f = (bf16)((rec.w == -1) ? 0.0f : __builtin_nanf(""));
+        const bf16x4 fill = {f, f, f, f};
+        const size_t b = blk / p.N, n = blk % p.N;
+        const size_t qrow0 = b * p.L5 + kBlock * n;
+        for (size_t e = threadIdx.x; e < kBlock * qw / 4; e += blockDim.x) {
+            const size_t j = (4 * e) / qw, w = (4 * e) % qw;
+            const size_t h = w / (kDc + kDr), c = w % (kDc + kDr);
+            if (c < (size_t)kDc)
+                gst8(dq_nope + ((qrow0 + j) * kH + h) * kDc + c, fill);
+            else
+                gst8(dq_rope + ((qrow0 + j) * kH + h) * kDr + (c - kDc), fill);
+        }
+    }
+}
+
 }  // namespace
 
-hipError_t launch_bwd_zero(float* p, size_t n, hipStream_t s) {
+hipError_t launch_bwd_order(const Problem& p, const BwdWork& w, hipStream_t s) {
+    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, s, w.fwd.srec, w.fwd.status, p.N);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_gather(const Problem& p, const BwdGrads& g, const BwdWork& w,
+                             const RopeTheta& th, hipStream_t s) {
+    RopeTheta turns{};
+    for (int k = 0; k < kDr / 2; ++k) turns.t[k] = th.t[k] * 0.15915494309189533577;  // 1 / 2pi
+    const size_t rows = (size_t)p.B * ((size_t)p.S + p.L5);
+    const size_t want = (rows + 3) / 4;
+    const int grid = (int)(want < 16384 ? want : 16384);
+    hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(256), 0, s, p, w.part, w.acc, w.fwd.srec,
+                       w.fwd.idx, w.fwd.status, (bf16*)g.dckv_ctx, (bf16*)g.dkr_ctx,
+                       (bf16*)g.dckv_blk, (bf16*)g.dkr_blk, (bf16*)g.dq_nope, (bf16*)g.dq_rope,
+                       turns);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_zero(float* p, size_t n, const int32_t* only_if, hipStream_t s) {
     // rounded up to whole float4: every workspace area starts 256-byte
     // aligned and is padded to a multiple of 256 bytes
     const size_t n4 = (n + 3) / 4;
@@ -317,7 +468,7 @@ hipError_t launch_bwd_zero(float* p, size_t n, hipStream_t s) {
     const size_t want = (n4 + 255) / 256;
     const int grid = (int)(want < 4096 ? want : 4096);
     hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<float4*>(p),
-                       n4);
+                       n4, only_if);
     return hipGetLastError();
 }
 

@@ -213,7 +213,8 @@ def test_bwd_workspace_holds_forward_area_and_accumulators():
     acc = (2048 + rows) * (512 + 64) * 4
     lat = rows * 64 * 512 * 2
     pm = 64 * rows * 144 * 2
-    assert bwd >= fwd + acc + 2 * lat + rows * 64 * 64 * 2 + 2 * pm
+    part = 64 * 132 * (512 + 64) * 4
+    assert bwd >= fwd + acc + 2 * lat + rows * 64 * 64 * 2 + 2 * pm + part
     g = glm_desc(dtype="f32", B=1, S=2048, N=64)
     wacc = 64 * (192 + 256) * 512 * 4
     assert sd.bwd_workspace_size(g) >= sd.workspace_size(g) + acc + wacc
@@ -248,7 +249,7 @@ def test_bwd_null_misaligned_and_workspace_errors_before_any_launch():
 
 def test_bwd_plan_and_event_count_check():
     d = glm_desc()
-    assert sd.bwd_plan(d) == 10 and sd.bwd_plan(d, force_generic=True) == 5
+    assert sd.bwd_plan(d) == 11 and sd.bwd_plan(d, force_generic=True) == 5
     assert sd.bwd_plan(glm_desc(dtype="f32")) == 5 and sd.bwd_plan(glm_desc(N=0)) == 0
     opts = sd._lib.Opts()
     ev = (ctypes.c_void_p * 3)(0x10, 0x20, 0x30)

@@ -208,3 +208,30 @@ def test_bwd_headline_full_size_sampled_blocks():
     check(gpu, ref, BF16_MFMA_TOL, "headline sampled", names=("dq_nope", "dq_rope", "dckv_blk",
                                                               "dkr_blk"),
           rows={k: rows for k in ("dq_nope", "dq_rope", "dckv_blk", "dkr_blk")})
+
+
+def test_bwd_unsorted_anchors_take_the_atomic_path():
+    """Kept anchors out of order within a sample: the MFMA path detects it
+    and sums the c^KV / k^R shares with atomics; the result still matches."""
+    wl = wk.scaled(3, S=640, N=16)
+    anchors, keep = wl.anchors.copy(), wl.keep.copy()
+    rng = np.random.default_rng(5)
+    for b in range(wl.B):
+        anchors[b] = anchors[b][rng.permutation(wl.N)]
+    assert any(np.any(np.diff(anchors[b][keep[b] == 1]) < 0) for b in range(wl.B))
+    dout = wk.make_dout(wl, seed=16)
+    gpu = GpuBwd(wl, dout, anchors, keep).run().result()
+    ref = O.backward(wl, dout, anchors=anchors, keep=keep, form="gathered")
+    check(gpu, ref, BF16_MFMA_TOL, "unsorted anchors")
+    unreached_rows_are_zero(gpu, wl, anchors, keep)
+
+
+def test_bwd_sorted_path_is_deterministic():
+    """Ascending anchors: every sum is taken in a fixed order, so two calls
+    give identical bits."""
+    wl = wk.scaled(4, S=1024, N=40)
+    run = GpuBwd(wl, wk.make_dout(wl, seed=17), wl.anchors, wl.keep)
+    a = run.run().result()
+    b = run.run().result()
+    for k in GRADS:
+        assert np.array_equal(a[k], b[k]), k
