@@ -35,22 +35,36 @@ constexpr int kAbsWaves = 8;                            // 64 output dims each
 constexpr int kAbsRowGroups = 4;                        // workgroups per head
 constexpr int kAbsRowsPerIter = 64;
 constexpr int kAbsTiles = kAbsRowsPerIter / 16;         // row tiles per iteration
-constexpr int kAbsKs = kDc / 32;                        // 6 k-steps
 constexpr int kAbsDt = 4;                               // 16-dim tiles per wave
-constexpr int kAbsFrags = kAbsTiles * kAbsKs;           // 1 KB B fragments per iteration
-constexpr int kAbsCopies = kAbsFrags / kAbsWaves;       // copy instructions per wave
-constexpr int kAbsStride = 256 + 16;                    // weight staging row (bf16)
 constexpr int kAbsEpiStride = kD * 2 + 16;              // bytes per row of the output transpose
 constexpr int kAbsStoreRows = kAbsRowsPerIter / kAbsWaves;   // q_abs rows each wave stores
-constexpr int kAbsShared = (kDc * kAbsStride * 2 > kAbsRowsPerIter * kAbsEpiStride)
-                               ? kDc * kAbsStride * 2 : kAbsRowsPerIter * kAbsEpiStride;
-static_assert(kAbsCopies * kAbsWaves == kAbsFrags && kAbsKs % kAbsCopies == 0,
-              "each wave copies k-steps of one row tile");
 
+// KD: input dims per row (d_c = 192 for q_abs; the backward runs the same
+// kernel with d_v = 256 for W_UV^T dout).  The weight slice is staged
+// through LDS in PARTS column parts (2 for 192 rows, 4 for 256, to fit LDS).
+template <int KD, int PARTS>
+struct AbsCfg {
+    static constexpr int Ks = KD / 32;                              // k-steps
+    static constexpr int Frags = kAbsTiles * Ks;                    // 1 KB B fragments per iteration
+    static constexpr int Copies = Frags / kAbsWaves;                // copy instructions per wave
+    static constexpr int PartCols = kD / PARTS;                     // weight columns per part
+    static constexpr int Stride = PartCols + 16;                    // weight staging row (bf16)
+    static constexpr int WavesPerPart = kAbsWaves / PARTS;
+    static constexpr int Shared = (KD * Stride * 2 > kAbsRowsPerIter * kAbsEpiStride)
+                                      ? KD * Stride * 2 : kAbsRowsPerIter * kAbsEpiStride;
+    static_assert(Copies * kAbsWaves == Frags && Ks % Copies == 0,
+                  "each wave copies k-steps of one row tile");
+    static_assert(WavesPerPart * 64 == PartCols, "a part holds whole waves' dims");
+};
+
+template <int KD, int PARTS>
 __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
     const bf16* __restrict__ q_nope, const bf16* __restrict__ w_uk,
     const int32_t* __restrict__ kept, const int32_t* __restrict__ status,
     bf16* __restrict__ q_abs, int N, int L5, int slot0, int nslots, uint32_t q_bytes) {
+    using C = AbsCfg<KD, PARTS>;
+    constexpr int kAbsKs = C::Ks, kAbsFrags = C::Frags, kAbsCopies = C::Copies;
+    constexpr int kAbsStride = C::Stride, kAbsShared = C::Shared;
     // weight staging at start, then the output transpose
     __shared__ __attribute__((aligned(16))) char shared_area[kAbsShared];
     // the two q^C buffers are separate arrays: the compiler then sees that a
@@ -72,27 +86,46 @@ __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
 
     // ---- A operand: fragment (ks, dt) holds output dims 64w + 16dt + l16
     // and k-values c = 32ks + 8g .. +7, read transposed out of the [c][d]
-    // staging copy of one half of W_UK[h] (waves 0-3 take the first half).
+    // staging copy of one column part of the weight (the waves whose dims it
+    // holds read it).
     bf16x8 a[kAbsKs][kAbsDt];
     {
         bf16* wl = reinterpret_cast<bf16*>(shared_area);
         const int hl = lane >> 5;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            // one 512-byte weight row per half-wave instruction, straight into LDS
-            for (int c0 = 2 * wave; c0 < kDc; c0 += 2 * kAbsWaves) {
-                const int c = c0 + hl;
-                if (hl == 0)
-                    async_copy_16(w_uk + ((size_t)h * kDc + c) * kD + half * 256 + lane * 8,
-                                  &wl[c0 * kAbsStride]);
-                else
-                    async_copy_16(w_uk + ((size_t)h * kDc + c) * kD + half * 256 + (lane - 32) * 8,
-                                  &wl[c0 * kAbsStride + kAbsStride - 256]);
+        for (int part = 0; part < PARTS; ++part) {
+            if constexpr (PARTS == 2) {
+                // one 512-byte weight row per half-wave instruction
+                for (int c0 = 2 * wave; c0 < KD; c0 += 2 * kAbsWaves) {
+                    const int c = c0 + hl;
+                    if (hl == 0)
+                        async_copy_16(w_uk + ((size_t)h * KD + c) * kD + part * 256 + lane * 8,
+                                      &wl[c0 * kAbsStride]);
+                    else
+                        async_copy_16(w_uk + ((size_t)h * KD + c) * kD + part * 256 +
+                                          (lane - 32) * 8,
+                                      &wl[c0 * kAbsStride + kAbsStride - 256]);
+                }
+            } else {
+                // full-wave copies that fill the padded layout contiguously, 1 KB
+                // each: lane l's 16 bytes land at byte 1024 i + 16 l, i.e. row
+                // (1024 i + 16 l) / (2 * stride); lanes that land in a row's
+                // padding fetch any element of that row
+                constexpr int kRowBytes = 2 * kAbsStride;
+                constexpr int kCopies = KD * kRowBytes / 1024;
+                static_assert(KD * kRowBytes % 1024 == 0 && kRowBytes % 16 == 0, "whole copies");
+                for (int i = wave; i < kCopies; i += kAbsWaves) {
+                    const int off = 1024 * i + 16 * lane;
+                    const int row = off / kRowBytes, cb = off % kRowBytes;
+                    const int col = (cb < 2 * C::PartCols) ? cb / 2 : 0;
+                    async_copy_16(w_uk + ((size_t)h * KD + row) * kD + part * C::PartCols + col,
+                                  shared_area + 1024 * i);
+                }
             }
             __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
             __syncthreads();
-            if ((wave >> 2) == half) {
-                const int wd = wave & 3;
+            if (wave / C::WavesPerPart == part) {
+                const int wd = wave % C::WavesPerPart;
 #pragma unroll
                 for (int ks = 0; ks < kAbsKs; ++ks)
 #pragma unroll
@@ -120,7 +153,7 @@ __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
         const int r = copy_row(it);
         const int b = blk / N, n = blk % N;
         const uint32_t off = (uint32_t)(
-            ((((size_t)b * L5 + (size_t)kBlock * n + r % kBlock) * kH + h) * kDc + g * 8) *
+            ((((size_t)b * L5 + (size_t)kBlock * n + r % kBlock) * kH + h) * KD + g * 8) *
             sizeof(bf16));
 #pragma unroll
         for (int j = 0; j < kAbsCopies; ++j) {
@@ -229,10 +262,19 @@ __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
 hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
                          hipStream_t s) {
     const int grid = kH * kAbsRowGroups;
-    hipLaunchKernelGGL(absorb_kernel, dim3(grid), dim3(kAbsWaves * 64), 0, s, (const bf16*)in.q_nope,
-                       (const bf16*)in.w_uk, ws.kept, ws.status, ws.qabs, p.N, p.L5,
-                       c.slot0, c.nslots,
+    hipLaunchKernelGGL((absorb_kernel<kDc, 2>), dim3(grid), dim3(kAbsWaves * 64), 0, s,
+                       (const bf16*)in.q_nope, (const bf16*)in.w_uk, ws.kept, ws.status, ws.qabs,
+                       p.N, p.L5, c.slot0, c.nslots,
                        (uint32_t)((size_t)p.B * p.L5 * kH * kDc * sizeof(bf16)));
+    return hipGetLastError();
+}
+
+hipError_t launch_absorb_dv(const Problem& p, const void* dout, const void* w_uv,
+                            const Workspace& ws, bf16* dolat, hipStream_t s) {
+    const int grid = kH * kAbsRowGroups;
+    hipLaunchKernelGGL((absorb_kernel<kDv, 4>), dim3(grid), dim3(kAbsWaves * 64), 0, s,
+                       (const bf16*)dout, (const bf16*)w_uv, ws.kept, ws.status, dolat, p.N, p.L5,
+                       0, p.B * p.N, (uint32_t)((size_t)p.B * p.L5 * kH * kDv * sizeof(bf16)));
     return hipGetLastError();
 }
 

@@ -116,8 +116,10 @@ hipError_t launch_bwd_finalize(const Problem& p, bool bf16_io, const BwdGrads& g
                                const RopeTheta& th, bool weights, hipStream_t s);
 
 // MFMA path (bf16, GLM dims).
-hipError_t launch_bwd_dolat(const Problem& p, const Inputs& in, const BwdGrads& g,
-                            const BwdWork& w, hipStream_t s);
+// d_olat = W_UV[h]^T dout for every kept row: the forward's absorb kernel
+// with d_v = 256 input dims (absorb.hip); written in the permuted latent order.
+hipError_t launch_absorb_dv(const Problem& p, const void* dout, const void* w_uv,
+                            const Workspace& ws, bf16* dolat, hipStream_t s);
 hipError_t launch_bwd_attn(const Problem& p, const Inputs& in, const BwdGrads& g,
                            const BwdWork& w, const RopeTheta& th, hipStream_t s);
 hipError_t launch_bwd_dkv(const Problem& p, const BwdWork& w, hipStream_t s);

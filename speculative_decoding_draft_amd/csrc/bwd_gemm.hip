@@ -1,9 +1,8 @@
 // Backward of the masked latent attention, MFMA path: the dense products
 // around the attention kernel, as tiled bf16 MFMA GEMMs with fp32
-// accumulation.
+// accumulation (W_UV^T dout runs on the forward's absorb kernel).
 //
-//   d_olat = W_UV[h]^T dout              per head, over the kept query rows
-//   dq^C   = W_UK[h] dq_abs              per head
+//   dq^C   = W_UK[h] dq_abs              per head, over the kept query rows
 //   dW_UV[h] = sum_rows dout (o_lat)^T   per head, reduction over every row
 //   dW_UK[h] = sum_rows q^C (dq_abs)^T   per head
 //   dc_k  = sum_rows P d_olat + dS' q_abs, d(R k^R)_k = sum_rows dS' (R q^R)
@@ -39,9 +38,11 @@ __device__ inline int perm_pos(int d) { return 8 * ((d & 15) >> 2) + 4 * (d >> 4
 __device__ inline int dim_of_pos4(int pos) { return (pos & ~31) + perm_dim(pos & 31); }
 __device__ inline int pos_of_dim4(int dim) { return (dim & ~31) + perm_pos(dim & 31); }
 
-template <int BM_, int BN_, int WM_, int WN_, bool A_TR_, bool A_PERM_, bool B_TR_, bool B_PERM_>
+template <int BM_, int BN_, int WM_, int WN_, bool A_TR_, bool A_PERM_, bool B_TR_, bool B_PERM_,
+          int PF_ = 1>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int PF = PF_;                      // k-steps of global loads in flight
     static constexpr bool A_TR = A_TR_, A_PERM = A_PERM_, B_TR = B_TR_, B_PERM = B_PERM_;
     static_assert(WM * WN == 4, "4 waves");
     static constexpr int MT = BM / WM / 16, NT = BN / WN / 16;
@@ -56,9 +57,20 @@ struct Cfg {
     static constexpr int LDS_ELEMS = 2 * STAGE;
 };
 
+template <class C>
+__device__ inline void gemm_zero(f32x4 (&acc)[C::MT][C::NT]) {
+#pragma unroll
+    for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// acc += the k-steps [s0, s1) of the tile product.
 // K-contiguous operand: row(r) is the start of row r (r < BM or BN), or
 // nullptr (zeros).  Transposed operand: row(k) is the element (k, tile
-// column 0) of k-row k, or nullptr (zeros).
+// column 0) of k-row k, or nullptr (zeros).  The global loads of C::PF
+// k-steps are in flight in a ring of registers; vmcnt retires in order, so
+// row() must not itself load from global memory (it may read LDS).
 template <class C, class AF, class BF>
 __device__ inline void gemm_tile(const AF& arow, const BF& brow, int s0, int s1, bf16* lds,
                                  f32x4 (&acc)[C::MT][C::NT]) {
@@ -66,10 +78,6 @@ __device__ inline void gemm_tile(const AF& arow, const BF& brow, int s0, int s1,
     const int wave = tid >> 6, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const int wm = wave / C::WN, wn = wave % C::WN;
     const bf16x8 zero8 = {};
-#pragma unroll
-    for (int i = 0; i < C::MT; ++i)
-#pragma unroll
-        for (int j = 0; j < C::NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const bf16* apr[C::A_PT];
     const bf16* bpr[C::B_PT];
@@ -87,8 +95,8 @@ __device__ inline void gemm_tile(const AF& arow, const BF& brow, int s0, int s1,
             bpr[i] = (c < C::B_CH) ? brow(c >> 2) : nullptr;
         }
     }
-    bf16x8 ra[C::A_PT], rb[C::B_PT];
-    auto load = [&](int s) {
+    bf16x8 ra[C::PF][C::A_PT], rb[C::PF][C::B_PT];
+    auto load = [&](int s, bf16x8 (&xa)[C::A_PT], bf16x8 (&xb)[C::B_PT]) {
 #pragma unroll
         for (int i = 0; i < C::A_PT; ++i) {
             const int c = tid + 256 * i;
@@ -103,7 +111,7 @@ __device__ inline void gemm_tile(const AF& arow, const BF& brow, int s0, int s1,
                     if (p) p += 32 * s + 8 * (c & 3);
                 }
             }
-            ra[i] = p ? gld16(p) : zero8;
+            xa[i] = p ? gld16(p) : zero8;
         }
 #pragma unroll
         for (int i = 0; i < C::B_PT; ++i) {
@@ -119,10 +127,10 @@ __device__ inline void gemm_tile(const AF& arow, const BF& brow, int s0, int s1,
                     if (p) p += 32 * s + 8 * (c & 3);
                 }
             }
-            rb[i] = p ? gld16(p) : zero8;
+            xb[i] = p ? gld16(p) : zero8;
         }
     };
-    auto store = [&](bf16* st) {
+    auto store = [&](bf16* st, const bf16x8 (&xa)[C::A_PT], const bf16x8 (&xb)[C::B_PT]) {
 #pragma unroll
         for (int i = 0; i < C::A_PT; ++i) {
             const int c = tid + 256 * i;
@@ -130,7 +138,7 @@ __device__ inline void gemm_tile(const AF& arow, const BF& brow, int s0, int s1,
                 constexpr int per = C::BM / 8;
                 const int off = C::A_TR ? (c / per) * C::A_LD + 8 * (c % per)
                                         : (c >> 2) * C::A_LD + 8 * (c & 3);
-                st16(st + off, ra[i]);
+                st16(st + off, xa[i]);
             }
         }
 #pragma unroll
@@ -140,7 +148,7 @@ __device__ inline void gemm_tile(const AF& arow, const BF& brow, int s0, int s1,
                 constexpr int per = C::BN / 8;
                 const int off = C::B_TR ? (c / per) * C::B_LD + 8 * (c % per)
                                         : (c >> 2) * C::B_LD + 8 * (c & 3);
-                st16(st + C::A_SZ + off, rb[i]);
+                st16(st + C::A_SZ + off, xb[i]);
             }
         }
     };
@@ -154,23 +162,33 @@ __device__ inline void gemm_tile(const AF& arow, const BF& brow, int s0, int s1,
         return perm ? ld16(row + 8 * g) : cat(ld8(row + 4 * g), ld8(row + 16 + 4 * g));
     };
     if (s0 >= s1) return;
-    load(s0);
-    for (int s = s0; s < s1; ++s) {
-        bf16* st = lds + ((s - s0) & 1) * C::STAGE;
-        store(st);
-        __syncthreads();
-        if (s + 1 < s1) load(s + 1);
-        bf16x8 af[C::MT], bfr[C::NT];
 #pragma unroll
-        for (int i = 0; i < C::MT; ++i)
-            af[i] = frag(st, C::A_LD, C::A_TR, C::A_PERM, wm * (C::BM / C::WM) + 16 * i);
+    for (int u = 0; u < C::PF; ++u)
+        if (s0 + u < s1) load(s0 + u, ra[u], rb[u]);
+    for (int s = s0; s < s1; s += C::PF) {
 #pragma unroll
-        for (int j = 0; j < C::NT; ++j)
-            bfr[j] = frag(st + C::A_SZ, C::B_LD, C::B_TR, C::B_PERM, wn * (C::BN / C::WN) + 16 * j);
+        for (int u = 0; u < C::PF; ++u) {
+            const int ss = s + u;
+            if (ss < s1) {
+                bf16* st = lds + ((ss - s0) & 1) * C::STAGE;
+                store(st, ra[u], rb[u]);
+                __syncthreads();
+                if (ss + C::PF < s1) load(ss + C::PF, ra[u], rb[u]);
+                bf16x8 af[C::MT], bfr[C::NT];
 #pragma unroll
-        for (int i = 0; i < C::MT; ++i)
+                for (int i = 0; i < C::MT; ++i)
+                    af[i] = frag(st, C::A_LD, C::A_TR, C::A_PERM, wm * (C::BM / C::WM) + 16 * i);
 #pragma unroll
-            for (int j = 0; j < C::NT; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+                for (int j = 0; j < C::NT; ++j)
+                    bfr[j] = frag(st + C::A_SZ, C::B_LD, C::B_TR, C::B_PERM,
+                                  wn * (C::BN / C::WN) + 16 * j);
+#pragma unroll
+                for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::NT; ++j)
+                        acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+            }
+        }
     }
 }
 
@@ -184,44 +202,9 @@ __device__ inline bf16x4 to_bf16x4(f32x4 v) {
     return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
 }
 
-// ---- d_olat[R][h] = W_UV[h]^T dout[R][h]: M = D (dims, natural), N = rows,
-// K = d_v.  A = W_UV[h] read transposed, B = dout rows.
-using CfgDolat = Cfg<128, 64, 2, 2, true, false, false, false>;
-__global__ __launch_bounds__(256) void dolat_kernel(const bf16* __restrict__ dout,
-                                                    const bf16* __restrict__ w_uv,
-                                                    const int4* __restrict__ srec,
-                                                    const int32_t* __restrict__ status,
-                                                    bf16* __restrict__ dolat, int N, int L5) {
-    __shared__ __attribute__((aligned(16))) bf16 lds[CfgDolat::LDS_ELEMS];
-    const int rows = kBlock * status[kStKeptCount];
-    const int m0 = blockIdx.x * CfgDolat::BM, n0 = blockIdx.y * CfgDolat::BN, h = blockIdx.z;
-    if (n0 >= rows) return;
-    const bf16* wh = w_uv + (size_t)h * kDv * kD + m0;
-    auto arow = [&](int k) -> const bf16* { return wh + (size_t)k * kD; };
-    auto brow = [&](int r) -> const bf16* {
-        const int R = n0 + r;
-        return R < rows ? dout + (input_row(srec, R, N, L5) * kH + h) * kDv : nullptr;
-    };
-    f32x4 acc[CfgDolat::MT][CfgDolat::NT];
-    gemm_tile<CfgDolat>(arow, brow, 0, kDv / 32, lds, acc);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
-    const int wm = wave / CfgDolat::WN, wn = wave % CfgDolat::WN;
-#pragma unroll
-    for (int j = 0; j < CfgDolat::NT; ++j) {
-        const int R = n0 + wn * (CfgDolat::BN / 2) + 16 * j + l16;
-        if (R >= rows) continue;
-        bf16* dst = dolat + ((size_t)R * kH + h) * kD;
-#pragma unroll
-        for (int i = 0; i < CfgDolat::MT; ++i) {
-            const int d = m0 + wm * (CfgDolat::BM / 2) + 16 * i + 4 * g;
-            gst8(dst + pos_of_dim4(d), to_bf16x4(acc[i][j]));
-        }
-    }
-}
-
 // ---- dq^C[R][h] = W_UK[h] dq_abs[R][h]: M = d_c, N = rows, K = D.
 // A = W_UK[h] rows (natural), B = dq_abs rows (permuted).
-using CfgDqn = Cfg<192, 64, 2, 2, false, false, false, true>;
+using CfgDqn = Cfg<192, 64, 2, 2, false, false, false, true, 2>;
 __global__ __launch_bounds__(256) void dqnope_kernel(const bf16* __restrict__ dqabs,
                                                      const bf16* __restrict__ w_uk,
                                                      const int4* __restrict__ srec,
@@ -238,6 +221,7 @@ __global__ __launch_bounds__(256) void dqnope_kernel(const bf16* __restrict__ dq
         return R < rows ? dqabs + ((size_t)R * kH + h) * kD : nullptr;
     };
     f32x4 acc[CfgDqn::MT][CfgDqn::NT];
+    gemm_zero<CfgDqn>(acc);
     gemm_tile<CfgDqn>(arow, brow, 0, kD / 32, lds, acc);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
     const int wm = wave / CfgDqn::WN, wn = wave % CfgDqn::WN;
@@ -256,21 +240,37 @@ __global__ __launch_bounds__(256) void dqnope_kernel(const bf16* __restrict__ dq
 // positions, permuted), N = d_v or d_c, K = rows.  Both operands transposed.
 // The 8 (dW_UV) or 4 (dW_UK) tiles of a head are consecutive in the
 // XCD-remapped order, so they share the rows they stream through one L2.
-using CfgDwuv = Cfg<128, 128, 2, 2, true, false, true, false>;
-using CfgDwuk = Cfg<128, 192, 2, 2, true, false, true, false>;
+using CfgDwuv = Cfg<128, 128, 2, 2, true, false, true, false, 4>;
+using CfgDwuk = Cfg<128, 192, 2, 2, true, false, true, false, 4>;
+constexpr int kSlotChunk = 4096;     // slots whose input rows one LDS table holds
 
 template <class C, int NOUT>
 __device__ inline void dw_tile(const bf16* __restrict__ lat, const bf16* __restrict__ rowsrc,
-                               const int4* __restrict__ srec, int rows, int h, int m0, int n0,
-                               int N, int L5, bf16* __restrict__ dw, bf16* lds) {
-    auto arow = [&](int k) -> const bf16* {
-        return k < rows ? lat + ((size_t)k * kH + h) * kD + m0 : nullptr;
-    };
-    auto brow = [&](int k) -> const bf16* {
-        return k < rows ? rowsrc + (input_row(srec, k, N, L5) * kH + h) * NOUT + n0 : nullptr;
-    };
+                               const int4* __restrict__ srec, int n_slots, int h, int m0, int n0,
+                               int N, int L5, bf16* __restrict__ dw, bf16* lds, int* rbase) {
     f32x4 acc[C::MT][C::NT];
-    gemm_tile<C>(arow, brow, 0, (rows + 31) / 32, lds, acc);
+    gemm_zero<C>(acc);
+    for (int c0 = 0; c0 < n_slots; c0 += kSlotChunk) {
+        const int nsl = min(kSlotChunk, n_slots - c0);
+        __syncthreads();                 // the previous chunk is done with the table and LDS
+        for (int i = threadIdx.x; i < nsl; i += blockDim.x) {
+            const int blk = srec[c0 + i].w;
+            rbase[i] = (blk / N) * L5 + kBlock * (blk % N);
+        }
+        __syncthreads();
+        const int k0 = kBlock * c0, k1 = kBlock * (c0 + nsl);
+        auto arow = [&](int k) -> const bf16* {
+            return (k >= k0 && k < k1) ? lat + ((size_t)k * kH + h) * kD + m0 : nullptr;
+        };
+        auto brow = [&](int k) -> const bf16* {
+            if (k < k0 || k >= k1) return nullptr;
+            const int sl = k / kBlock;
+            const size_t row = (size_t)rbase[sl - c0] + (k - kBlock * sl);
+            return rowsrc + (row * kH + h) * NOUT + n0;
+        };
+        // chunks start on a 32-row boundary (5 * 4096 = 640 * 32)
+        gemm_tile<C>(arow, brow, k0 / 32, (k1 + 31) / 32, lds, acc);
+    }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
     const int wm = wave / C::WN, wn = wave % C::WN;
 #pragma unroll
@@ -298,16 +298,17 @@ __global__ __launch_bounds__(256) void dw_kernel(const bf16* __restrict__ olat,
     constexpr int kLds = CfgDwuv::LDS_ELEMS > CfgDwuk::LDS_ELEMS ? CfgDwuv::LDS_ELEMS
                                                                   : CfgDwuk::LDS_ELEMS;
     __shared__ __attribute__((aligned(16))) bf16 lds[kLds];
-    const int rows = kBlock * status[kStKeptCount];
+    __shared__ int rbase[kSlotChunk];
+    const int n_slots = status[kStKeptCount];
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int h = lid / (kUvTiles + kUkTiles), t = lid % (kUvTiles + kUkTiles);
     if (t < kUvTiles) {
         const int m0 = (t / (kDv / CfgDwuv::BN)) * CfgDwuv::BM;
         const int n0 = (t % (kDv / CfgDwuv::BN)) * CfgDwuv::BN;
-        dw_tile<CfgDwuv, kDv>(olat, dout, srec, rows, h, m0, n0, N, L5, dw_uv, lds);
+        dw_tile<CfgDwuv, kDv>(olat, dout, srec, n_slots, h, m0, n0, N, L5, dw_uv, lds, rbase);
     } else {
         const int m0 = (t - kUvTiles) * CfgDwuk::BM;
-        dw_tile<CfgDwuk, kDc>(dqabs, q_nope, srec, rows, h, m0, 0, N, L5, dw_uk, lds);
+        dw_tile<CfgDwuk, kDc>(dqabs, q_nope, srec, n_slots, h, m0, 0, N, L5, dw_uk, lds, rbase);
     }
 }
 
@@ -348,6 +349,7 @@ __global__ __launch_bounds__(256) void dkv_kernel(const bf16* __restrict__ dolat
         return (k < kRows) ? pm + (size_t)k * kKeySlots : ds + (size_t)(k - kRows) * kKeySlots;
     };
     f32x4 a[CfgDkv::MT][CfgDkv::NT];
+    gemm_zero<CfgDkv>(a);
     gemm_tile<CfgDkv>(arow, brow, rope_tile ? kRows / 32 : 0, 2 * kRows / 32, lds, a);
 
     const int4 rec = srec[slot];
@@ -381,15 +383,6 @@ __global__ __launch_bounds__(256) void dkv_kernel(const bf16* __restrict__ dolat
 }
 
 }  // namespace
-
-hipError_t launch_bwd_dolat(const Problem& p, const Inputs& in, const BwdGrads& g,
-                            const BwdWork& w, hipStream_t s) {
-    const int rows = kBlock * p.B * p.N;
-    const dim3 grid(kD / CfgDolat::BM, (rows + CfgDolat::BN - 1) / CfgDolat::BN, kH);
-    hipLaunchKernelGGL(dolat_kernel, grid, dim3(256), 0, s, (const bf16*)g.dout,
-                       (const bf16*)in.w_uv, w.fwd.srec, w.fwd.status, w.dolat, p.N, p.L5);
-    return hipGetLastError();
-}
 
 hipError_t launch_bwd_dqnope(const Problem& p, const Inputs& in, const BwdGrads& g,
                              const BwdWork& w, hipStream_t s) {
