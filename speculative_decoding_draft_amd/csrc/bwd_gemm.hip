@@ -238,11 +238,13 @@ __global__ __launch_bounds__(256) void dqnope_kernel(const bf16* __restrict__ dq
 
 // ---- weight gradients, a reduction over every kept row: M = D (latent
 // positions, permuted), N = d_v or d_c, K = rows.  Both operands transposed.
-// The 8 (dW_UV) or 4 (dW_UK) tiles of a head are consecutive in the
-// XCD-remapped order, so they share the rows they stream through one L2.
-using CfgDwuv = Cfg<128, 128, 2, 2, true, false, true, false, 4>;
-using CfgDwuk = Cfg<128, 192, 2, 2, true, false, true, false, 4>;
-constexpr int kSlotChunk = 4096;     // slots whose input rows one LDS table holds
+// 128 x 64 tiles (16 of dW_UV and 12 of dW_UK per head; small tiles keep
+// four workgroups resident per compute unit) are consecutive per head in the
+// XCD-remapped order, so a head's tiles share the rows they stream through
+// one L2.
+using CfgDwuv = Cfg<128, 64, 2, 2, true, false, true, false, 2>;
+using CfgDwuk = Cfg<128, 64, 2, 2, true, false, true, false, 2>;
+constexpr int kSlotChunk = 2048;     // slots whose input rows one LDS table holds
 
 template <class C, int NOUT>
 __device__ inline void dw_tile(const bf16* __restrict__ lat, const bf16* __restrict__ rowsrc,
@@ -293,8 +295,9 @@ __global__ __launch_bounds__(256) void dw_kernel(const bf16* __restrict__ olat,
                                                  const int32_t* __restrict__ status,
                                                  bf16* __restrict__ dw_uv, bf16* __restrict__ dw_uk,
                                                  int N, int L5) {
-    constexpr int kUvTiles = (kD / CfgDwuv::BM) * (kDv / CfgDwuv::BN);   // 8 per head
-    constexpr int kUkTiles = (kD / CfgDwuk::BM) * (kDc / CfgDwuk::BN);   // 4 per head
+    constexpr int kUvTiles = (kD / CfgDwuv::BM) * (kDv / CfgDwuv::BN);
+    constexpr int kUkTiles = (kD / CfgDwuk::BM) * (kDc / CfgDwuk::BN);
+    static_assert(kDv % CfgDwuv::BN == 0 && kDc % CfgDwuk::BN == 0, "whole tiles");
     constexpr int kLds = CfgDwuv::LDS_ELEMS > CfgDwuk::LDS_ELEMS ? CfgDwuv::LDS_ELEMS
                                                                   : CfgDwuk::LDS_ELEMS;
     __shared__ __attribute__((aligned(16))) bf16 lds[kLds];
@@ -307,8 +310,9 @@ __global__ __launch_bounds__(256) void dw_kernel(const bf16* __restrict__ olat,
         const int n0 = (t % (kDv / CfgDwuv::BN)) * CfgDwuv::BN;
         dw_tile<CfgDwuv, kDv>(olat, dout, srec, n_slots, h, m0, n0, N, L5, dw_uv, lds, rbase);
     } else {
-        const int m0 = (t - kUvTiles) * CfgDwuk::BM;
-        dw_tile<CfgDwuk, kDc>(dqabs, q_nope, srec, n_slots, h, m0, 0, N, L5, dw_uk, lds, rbase);
+        const int m0 = ((t - kUvTiles) / (kDc / CfgDwuk::BN)) * CfgDwuk::BM;
+        const int n0 = ((t - kUvTiles) % (kDc / CfgDwuk::BN)) * CfgDwuk::BN;
+        dw_tile<CfgDwuk, kDc>(dqabs, q_nope, srec, n_slots, h, m0, n0, N, L5, dw_uk, lds, rbase);
     }
 }
 
@@ -396,7 +400,7 @@ hipError_t launch_bwd_dqnope(const Problem& p, const Inputs& in, const BwdGrads&
 hipError_t launch_bwd_dw(const Problem& p, const Inputs& in, const BwdGrads& g,
                          const BwdWork& w, hipStream_t s) {
     constexpr int kPerHead = (kD / CfgDwuv::BM) * (kDv / CfgDwuv::BN) +
-                             (kD / CfgDwuk::BM) * (kDc / CfgDwuk::BN);   // 12
+                             (kD / CfgDwuk::BM) * (kDc / CfgDwuk::BN);
     hipLaunchKernelGGL(dw_kernel, dim3(kH * kPerHead), dim3(256), 0, s, w.fwd.olat,
                        (const bf16*)g.dout, w.dqabs, (const bf16*)in.q_nope, w.fwd.srec,
                        w.fwd.status, (bf16*)g.dw_uv, (bf16*)g.dw_uk, p.N, p.L5);
