@@ -47,20 +47,51 @@ KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.h
 # plain 256 MiB device copy), with the digest of the kernel's sources when the
 # counters were taken.  A kernel whose sources changed since reports null.
 PMC_TRAFFIC = {
-    "absorb": (358_784_632, "aab74b0beb040176"),
-    "attention": (583_677_729, "9a8efa059feee454"),
-    "w_uv": (394_498_142, "8759cdadabfffc32"),
+    "absorb": (358_772_640, "1173152b9dfcdc71"),
+    "attention": (583_813_805, "9a8efa059feee454"),
+    "w_uv": (394_468_035, "8759cdadabfffc32"),
 }
 
 
-def kernel_digest(stage: str) -> str:
+# The same for the backward's launches (dspark_attn_bwd on the headline
+# workload): the source files each kernel is built from.
+BWD_KERNEL_SOURCES = {
+    "attention_bwd": ("bwd_attn.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
+    "dw": ("bwd_gemm.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
+    "dkv": ("bwd_gemm.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
+    "dq_nope": ("bwd_gemm.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
+    "d_olat": ("absorb.hip", "common.hpp", "kernels.hpp"),
+    "final": ("bwd_misc.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
+}
+BWD_PMC_TRAFFIC = {
+    "attention_bwd": (1_294_560_937, "ba86a7add3441456"),
+    "dw": (753_618_158, "e9bdb2e8cbad973d"),
+    "dkv": (971_080_342, "e9bdb2e8cbad973d"),
+    "dq_nope": (457_574_062, "e9bdb2e8cbad973d"),
+    "d_olat": (394_457_696, "1173152b9dfcdc71"),
+    "final": (311_151_167, "3f5a07842d4ad55c"),
+}
+
+
+def files_digest(files) -> str:
     import hashlib
     csrc = os.path.join(ROOT, "speculative_decoding_draft_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[stage], "common.hpp", "kernels.hpp"):
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def kernel_digest(stage: str) -> str:
+    return files_digest((KERNEL_SOURCES[stage], "common.hpp", "kernels.hpp"))
+
+
+def bwd_measured_traffic(stage: str, workload: str):
+    if stage not in BWD_PMC_TRAFFIC or not workload.startswith("headline"):
+        return None
+    nbytes, digest = BWD_PMC_TRAFFIC[stage]
+    return nbytes if files_digest(BWD_KERNEL_SOURCES[stage]) == digest else None
 
 
 def measured_traffic(stage: str, workload: str, chunk_blocks: int, n_blocks: int):
@@ -140,7 +171,11 @@ def bwd_stage_bytes(wl, anchors, keep):
         union += int(cover.sum())
     lat = rows * H * D * 2
     pm = len(kept) * 5 * H * 144 * 2
-    acc = wl.B * (wl.S + 5 * wl.N) * (D + dr) * 4
+    # with ascending anchors in every sample the accumulator is not used
+    # (per-block partials are gathered instead) and its clear is skipped
+    ascending = all(np.all(np.diff(np.asarray(anchors[b])[np.asarray(keep[b]) != 0]) >= 0)
+                    for b in range(wl.B))
+    acc = 0 if ascending else wl.B * (wl.S + 5 * wl.N) * (D + dr) * 4
     part = vsum * (D + dr) * 4          # each block's partial rows
     out_kv = wl.B * (wl.S + 5 * wl.N) * (D + dr) * 2
     return {
@@ -207,7 +242,8 @@ def bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sp
                             if k in nb and v > 0}
         out["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1),
                            "peak": MI355X_HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(ach / MI355X_HBM_PEAK_GBS, 4), "traffic": None,
+                           "frac": round(ach / MI355X_HBM_PEAK_GBS, 4),
+                           "traffic": bwd_measured_traffic(dom, wl.name),
                            "avg_launch_us": round(stage_us[dom], 2),
                            "algorithmic_bytes_per_launch": nb[dom]}
     return out
