@@ -204,7 +204,7 @@ __device__ inline bf16x4 to_bf16x4(f32x4 v) {
 
 // ---- dq^C[R][h] = W_UK[h] dq_abs[R][h]: M = d_c, N = rows, K = D.
 // A = W_UK[h] rows (natural), B = dq_abs rows (permuted).
-using CfgDqn = Cfg<192, 64, 2, 2, false, false, false, true, 2>;
+using CfgDqn = Cfg<192, 128, 2, 2, false, false, false, true, 1>;
 __global__ __launch_bounds__(256) void dqnope_kernel(const bf16* __restrict__ dqabs,
                                                      const bf16* __restrict__ w_uk,
                                                      const int4* __restrict__ srec,
@@ -212,9 +212,9 @@ __global__ __launch_bounds__(256) void dqnope_kernel(const bf16* __restrict__ dq
                                                      bf16* __restrict__ dq_nope, int N, int L5) {
     __shared__ __attribute__((aligned(16))) bf16 lds[CfgDqn::LDS_ELEMS];
     const int rows = kBlock * status[kStKeptCount];
-    const int n0 = blockIdx.y * CfgDqn::BN, h = blockIdx.z;
+    const int m0 = blockIdx.x * CfgDqn::BM, n0 = blockIdx.y * CfgDqn::BN, h = blockIdx.z;
     if (n0 >= rows) return;
-    const bf16* wh = w_uk + (size_t)h * kDc * kD;
+    const bf16* wh = w_uk + ((size_t)h * kDc + m0) * kD;
     auto arow = [&](int r) -> const bf16* { return wh + (size_t)r * kD; };
     auto brow = [&](int r) -> const bf16* {
         const int R = n0 + r;
@@ -227,12 +227,13 @@ __global__ __launch_bounds__(256) void dqnope_kernel(const bf16* __restrict__ dq
     const int wm = wave / CfgDqn::WN, wn = wave % CfgDqn::WN;
 #pragma unroll
     for (int j = 0; j < CfgDqn::NT; ++j) {
-        const int R = n0 + wn * (CfgDqn::BN / 2) + 16 * j + l16;
+        const int R = n0 + wn * (CfgDqn::BN / CfgDqn::WN) + 16 * j + l16;
         if (R >= rows) continue;
         bf16* dst = dq_nope + (input_row(srec, R, N, L5) * kH + h) * kDc;
 #pragma unroll
         for (int i = 0; i < CfgDqn::MT; ++i)
-            gst8(dst + wm * (CfgDqn::BM / 2) + 16 * i + 4 * g, to_bf16x4(acc[i][j]));
+            gst8(dst + m0 + wm * (CfgDqn::BM / CfgDqn::WM) + 16 * i + 4 * g,
+                 to_bf16x4(acc[i][j]));
     }
 }
 
@@ -391,7 +392,8 @@ __global__ __launch_bounds__(256) void dkv_kernel(const bf16* __restrict__ dolat
 hipError_t launch_bwd_dqnope(const Problem& p, const Inputs& in, const BwdGrads& g,
                              const BwdWork& w, hipStream_t s) {
     const int rows = kBlock * p.B * p.N;
-    const dim3 grid(1, (rows + CfgDqn::BN - 1) / CfgDqn::BN, kH);
+    static_assert(kDc % CfgDqn::BM == 0, "whole tiles");
+    const dim3 grid(kDc / CfgDqn::BM, (rows + CfgDqn::BN - 1) / CfgDqn::BN, kH);
     hipLaunchKernelGGL(dqnope_kernel, grid, dim3(256), 0, s, w.dqabs, (const bf16*)in.w_uk,
                        w.fwd.srec, w.fwd.status, (bf16*)g.dq_nope, p.N, p.L5);
     return hipGetLastError();
