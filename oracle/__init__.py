@@ -33,4 +33,6 @@ from .dspark_oracle import (  # noqa: F401
     rope_interleaved_transpose,
     backward,
     loss,
+    rmsnorm,
+    layer_forward,
 )

@@ -501,3 +501,55 @@ def loss(wl, dout, layer_idx: int = 0, anchors=None, keep=None, scale=None) -> f
     G = _f64(dout, wl.dtype)
     rows_kept = np.repeat(np.asarray(keep, dtype=bool), wl.block, axis=1)   # [B, 5N]
     return float(np.sum(np.where(rows_kept[:, :, None, None], out * G, 0.0)))
+
+
+# ---------------------------------------------------------------------------
+# the MLA block of one draft layer  (§4 "MLA Projection": input_layernorm,
+# q_a_proj, q_a_layernorm, q_b_proj, kv_a_proj_with_mqa over [H^ctx ; h],
+# kv_a_layernorm, the attention, o_proj added back to the residual)
+# ---------------------------------------------------------------------------
+
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * g.  The page
+    names the op (input_layernorm, q_a_layernorm, kv_a_layernorm) without a
+    formula or epsilon; this is the standard definition with eps a
+    parameter."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(g, np.float64)
+
+
+def layer_forward(wl, li, anchors=None, keep=None, scale=None, blocks=None):
+    """H^(l) + o_proj(attention) for one draft layer (fp64), in the page's
+    order (§4 "MLA Projection"):
+      h    = RMSNorm(H^(l))                               input_layernorm
+      c^Q  = RMSNorm(h W_qa^T)                            q_a_proj, q_a_layernorm
+      [q^C ; q^R] per head = c^Q W_qb^T                   q_b_proj (n_h groups of (d_c, d_r))
+      [c^KV ; k^R] = [H^ctx ; h] W_kva^T                  kv_a_proj_with_mqa
+      c^KV <- RMSNorm(c^KV)                               kv_a_layernorm
+      o    = attention(q, c^KV, k^R; W_UK, W_UV)          the forward above
+      out  = H^(l) + o W_o^T                              o_proj, residual
+    Rows of padding blocks have no attention output; they are NaN here.
+    li: a ``workloads.LayerInputs``; W_UK / W_UV come from wl.layers[0].
+    blocks: as in ``forward`` (only those blocks' rows are computed)."""
+    import copy as _copy
+    dt = wl.dtype
+    B, S, N, H = wl.B, wl.S, wl.N, wl.H
+    D, dc, dr, dv = wl.D, wl.d_c, wl.d_r, wl.d_v
+    L5 = wl.block * N
+    f = lambda a: _f64(a, dt)
+    Hd, Hc = f(li.h_draft), f(li.h_ctx)
+    h = rmsnorm(Hd, f(li.g_in), li.rms_eps)
+    cq = rmsnorm(h @ f(li.w_qa).T, f(li.g_qa), li.rms_eps)
+    q = (cq @ f(li.w_qb).T).reshape(B, L5, H, dc + dr)
+    kv_ctx = Hc @ f(li.w_kva).T
+    kv_blk = h @ f(li.w_kva).T
+    sub = _copy.copy(wl)
+    sub.dtype = "f64"
+    base = wl.layers[0]
+    sub.layers = [type(base)(
+        q_nope=q[..., :dc], q_rope=q[..., dc:],
+        ckv_ctx=rmsnorm(kv_ctx[..., :D], f(li.g_kva), li.rms_eps), kr_ctx=kv_ctx[..., D:],
+        ckv_blk=rmsnorm(kv_blk[..., :D], f(li.g_kva), li.rms_eps), kr_blk=kv_blk[..., D:],
+        w_uk=f(base.w_uk), w_uv=f(base.w_uv))]
+    o = forward(sub, 0, anchors, keep, form="gathered", blocks=blocks, scale=scale)
+    return Hd + o.reshape(B, L5, H * dv) @ f(li.w_o).T

@@ -275,3 +275,52 @@ def make_dout(wl: Workload, seed: int = 7) -> np.ndarray:
     its own seeded stream so that the forward inputs stay as they are."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, wl.B, wl.S, wl.N])))
     return _normal(rng, (wl.B, wl.block * wl.N, wl.H, wl.d_v), 1.0, wl.dtype)
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    """Inputs of one draft layer's MLA block beyond the attention's own:
+    the layer input H^(l) [B, 5N, d] (residual stream), H^ctx [B, S, d], the
+    RMSNorm weights and the projections (out x in, like the page's
+    parameter table)."""
+    hidden: int
+    q_rank: int
+    rms_eps: float
+    h_draft: np.ndarray     # [B, 5N, d]
+    h_ctx: np.ndarray       # [B, S, d]
+    g_in: np.ndarray        # [d]            input_layernorm
+    w_qa: np.ndarray        # [q_rank, d]    q_a_proj
+    g_qa: np.ndarray        # [q_rank]       q_a_layernorm
+    w_qb: np.ndarray        # [H*(d_c+d_r), q_rank]  q_b_proj, per head d_c rows then d_r rows
+    w_kva: np.ndarray       # [D + d_r, d]   kv_a_proj_with_mqa: c^KV rows then k^R rows
+    g_kva: np.ndarray       # [D]            kv_a_layernorm
+    w_o: np.ndarray         # [d, H*d_v]     o_proj
+
+
+def make_layer_inputs(wl: Workload, hidden: int, q_rank: int, seed: int = 5,
+                      rms_eps: float = 1e-6) -> LayerInputs:
+    """Seeded inputs for the MLA block around the attention (same storage
+    type as the workload): activations N(0, 1), RMSNorm weights 1 + N(0, 0.1^2),
+    projection weights N(0, 1/fan_in).  The attention's W_UK / W_UV are the
+    workload's own (kv_b_proj)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, wl.B, wl.S, wl.N,
+                                                                        hidden, q_rank])))
+    dt = wl.dtype
+    H, D, dc, dr, dv = wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v
+
+    def gain(n):
+        x = 1.0 + 0.1 * rng.standard_normal(size=n, dtype=np.float32)
+        return f32_to_bf16_bits(x) if dt == "bf16" else x.astype(np.float32)
+
+    return LayerInputs(
+        hidden=hidden, q_rank=q_rank, rms_eps=rms_eps,
+        h_draft=_normal(rng, (wl.B, wl.block * wl.N, hidden), 1.0, dt),
+        h_ctx=_normal(rng, (wl.B, wl.S, hidden), 1.0, dt),
+        g_in=gain(hidden),
+        w_qa=_normal(rng, (q_rank, hidden), float(1 / np.sqrt(hidden)), dt),
+        g_qa=gain(q_rank),
+        w_qb=_normal(rng, (H * (dc + dr), q_rank), float(1 / np.sqrt(q_rank)), dt),
+        w_kva=_normal(rng, (D + dr, hidden), float(1 / np.sqrt(hidden)), dt),
+        g_kva=gain(D),
+        w_o=_normal(rng, (hidden, H * dv), float(1 / np.sqrt(H * dv)), dt),
+    )
