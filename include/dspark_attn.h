@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 3
+#define DSPARK_ABI_VERSION 4
 
 typedef enum dspark_status {
     DSPARK_OK = 0,
@@ -267,6 +267,67 @@ dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc,
 /* Number of stage events dspark_attn_bwd_ex records for (desc, opts). */
 dspark_status dspark_attn_bwd_plan(const dspark_attn_desc* desc, const dspark_attn_opts* opts,
                                    int32_t* n_events);
+
+/* ---- the MLA block of one draft layer -----------------------------------
+ * §4 "MLA Projection" around the attention: input_layernorm, q_a_proj,
+ * q_a_layernorm, q_b_proj, kv_a_proj_with_mqa over [H^ctx ; h],
+ * kv_a_layernorm, the attention above, o_proj added back to the residual:
+ *   h = RMSNorm(H; g_in)          c^Q = RMSNorm(h W_qa^T; g_qa)
+ *   [q^C ; q^R] per head = c^Q W_qb^T
+ *   [c^KV ; k^R] = [H^ctx ; h] W_kva^T,   c^KV <- RMSNorm(c^KV; g_kva)
+ *   out = H + attention(...) W_o^T
+ * RMSNorm(x; g) = x / sqrt(mean(x^2) + rms_eps) * g (the page gives no
+ * epsilon).  The FFN half of the layer is not part of this call. */
+typedef struct dspark_layer_desc {
+    dspark_attn_desc attn;   /* the attention's problem (B, S, N, dims, dtype) */
+    int32_t hidden;          /* d: 6144 for GLM-5.2 */
+    int32_t q_rank;          /* q_lora_rank: 2048 */
+    double rms_eps;          /* >= 0 */
+} dspark_layer_desc;
+
+/* Bytes of workspace dspark_mla_layer_fwd needs (0 on an invalid descriptor):
+ * the block's intermediates (normalised h, c^Q, q^C, q^R, [c^KV ; k^R] of
+ * every context and draft row, the attention output) and the attention's own
+ * workspace.  256-byte aligned. */
+size_t dspark_mla_layer_workspace_size(const dspark_layer_desc* desc);
+
+/* The MLA block of one draft layer.  Device pointers, desc->attn.dtype:
+ *   h_draft [B, 5N, d]   H^(l), the layer input (residual stream)
+ *   h_ctx   [B, S, d]    H^ctx (already projected and normalised by main_norm)
+ *   g_in [d], w_qa [q_rank, d], g_qa [q_rank],
+ *   w_qb [H * (d_c + d_r), q_rank]  (per head: d_c q^C rows, then d_r q^R rows)
+ *   w_kva [D + d_r, d]   (c^KV rows, then k^R rows),  g_kva [D]
+ *   w_uk [H, d_c, D], w_uv [H, d_v, D]   kv_b_proj, as in dspark_attn_fwd
+ *   w_o [d, H * d_v]
+ *   anchors, keep        as in dspark_attn_fwd
+ *   out [B, 5N, d]       H + o_proj(attention); rows of padding blocks are H
+ *                        (their attention rows are 0), rows of a kept block
+ *                        with a bad anchor are NaN
+ * The projections run on rocBLAS (fp32 accumulation, no atomics: the same
+ * call gives the same bits).  The first call on a device and host thread
+ * creates a rocBLAS handle that is kept until the process ends -- the one
+ * allocation the library makes.  out must not alias any input. */
+dspark_status dspark_mla_layer_fwd(const dspark_layer_desc* desc,
+                                   const void* h_draft, const void* h_ctx,
+                                   const void* g_in, const void* w_qa, const void* g_qa,
+                                   const void* w_qb, const void* w_kva, const void* g_kva,
+                                   const void* w_uk, const void* w_uv, const void* w_o,
+                                   const int32_t* anchors, const uint8_t* keep,
+                                   void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* dspark_mla_layer_fwd with options (opts may be NULL): force_generic is
+ * passed to the attention; stage_events (at least 7) are recorded on
+ * `stream` before the first launch and after: the input RMSNorm, q_a_proj
+ * and its RMSNorm, q_b_proj, kv_a_proj and its RMSNorm / k^R split, the
+ * attention, o_proj. */
+dspark_status dspark_mla_layer_fwd_ex(const dspark_layer_desc* desc,
+                                      const void* h_draft, const void* h_ctx,
+                                      const void* g_in, const void* w_qa, const void* g_qa,
+                                      const void* w_qb, const void* w_kva, const void* g_kva,
+                                      const void* w_uk, const void* w_uv, const void* w_o,
+                                      const int32_t* anchors, const uint8_t* keep,
+                                      void* out, void* workspace, size_t ws_bytes, void* stream,
+                                      const dspark_attn_opts* opts);
 
 /* Synchronises `stream`, then reads the status area of a workspace used by
  * the last dspark_attn_fwd / dspark_attn_bwd / dspark_build_index on it.  Returns DSPARK_OK, or

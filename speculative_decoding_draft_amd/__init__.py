@@ -1,4 +1,5 @@
-"""MI355X (gfx950) DSpark draft-attention forward and backward.
+"""MI355X (gfx950) DSpark draft attention (forward, backward) and the MLA block
+of a draft layer around it.
 
 The compute lives in libdspark_attn.so (hand-written HIP kernels behind the C
 ABI of include/dspark_attn.h); this package is its Python binding.  Build the
@@ -25,6 +26,11 @@ from ._lib import (  # noqa: F401
     bwd_plan,
     bwd_workspace_size,
     BWD_GRADS,
+    LayerDesc,
+    LAYER_WEIGHTS,
+    make_layer_desc,
+    layer_workspace_size,
+    mla_layer_fwd,
     build_index,
     last_error,
     make_desc,

@@ -31,7 +31,8 @@ DSPARK_BF16 = 1
 
 EXPORTS = ("dspark_attn_workspace_size", "dspark_attn_fwd", "dspark_attn_fwd_ex", "dspark_attn_plan",
            "dspark_attn_bwd_workspace_size", "dspark_attn_bwd", "dspark_attn_bwd_ex",
-           "dspark_attn_bwd_plan", "dspark_build_index", "dspark_select_anchors_host",
+           "dspark_attn_bwd_plan", "dspark_mla_layer_workspace_size", "dspark_mla_layer_fwd",
+           "dspark_mla_layer_fwd_ex", "dspark_build_index", "dspark_select_anchors_host",
            "dspark_read_device_status", "dspark_last_error", "dspark_abi_version")
 
 
@@ -48,6 +49,11 @@ class Desc(ctypes.Structure):
                 ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("rope_base", ctypes.c_double), ("softmax_scale", ctypes.c_double),
                 ("dtype", ctypes.c_int32)]
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("attn", Desc), ("hidden", ctypes.c_int32), ("q_rank", ctypes.c_int32),
+                ("rms_eps", ctypes.c_double)]
 
 
 class Opts(ctypes.Structure):
@@ -86,6 +92,14 @@ def _load():
     lib.dspark_attn_bwd_ex.restype = i32
     lib.dspark_attn_bwd_plan.argtypes = [pd, ctypes.POINTER(Opts), ctypes.POINTER(i32)]
     lib.dspark_attn_bwd_plan.restype = i32
+    pl = ctypes.POINTER(LayerDesc)
+    lib.dspark_mla_layer_workspace_size.argtypes = [pl]
+    lib.dspark_mla_layer_workspace_size.restype = sz
+    layer_args = [pl] + [vp] * 11 + [vp, vp, vp, vp, sz, vp]
+    lib.dspark_mla_layer_fwd.argtypes = layer_args
+    lib.dspark_mla_layer_fwd.restype = i32
+    lib.dspark_mla_layer_fwd_ex.argtypes = layer_args + [ctypes.POINTER(Opts)]
+    lib.dspark_mla_layer_fwd_ex.restype = i32
     lib.dspark_build_index.argtypes = [pd, vp, vp, vp, vp, sz, vp]
     lib.dspark_build_index.restype = i32
     lib.dspark_select_anchors_host.argtypes = [vp, i32, i32, u64, vp, vp]
@@ -262,6 +276,36 @@ def attn_bwd(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk,
         return
     opts, _arr = _opts(stage_events, force_generic, 0)
     _check(lib.dspark_attn_bwd_ex(*args, ctypes.byref(opts)))
+
+
+def make_layer_desc(attn: Desc, hidden: int, q_rank: int, rms_eps: float = 1e-6) -> LayerDesc:
+    return LayerDesc(attn, int(hidden), int(q_rank), float(rms_eps))
+
+
+def layer_workspace_size(desc: LayerDesc) -> int:
+    n = int(lib.dspark_mla_layer_workspace_size(ctypes.byref(desc)))
+    if n == 0:
+        raise DSparkError(DSPARK_EINVAL, last_error())
+    return n
+
+
+LAYER_WEIGHTS = ("g_in", "w_qa", "g_qa", "w_qb", "w_kva", "g_kva", "w_uk", "w_uv", "w_o")
+
+
+def mla_layer_fwd(desc: LayerDesc, h_draft, h_ctx, weights, anchors, keep, out, workspace,
+                  stream=None, stage_events: Optional[Sequence[int]] = None,
+                  force_generic: bool = False) -> None:
+    """dspark_mla_layer_fwd / _ex; weights: a mapping named as in
+    LAYER_WEIGHTS."""
+    args = [ctypes.byref(desc), _ptr(h_draft), _ptr(h_ctx)]
+    args += [_ptr(weights[k]) for k in LAYER_WEIGHTS]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args += [_ptr(anchors), _ptr(keep), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)]
+    if stage_events is None and not force_generic:
+        _check(lib.dspark_mla_layer_fwd(*args))
+        return
+    opts, _arr = _opts(stage_events, force_generic, 0)
+    _check(lib.dspark_mla_layer_fwd_ex(*args, ctypes.byref(opts)))
 
 
 def build_index(desc: Desc, anchors, keep, index_out, workspace, stream=None) -> None:

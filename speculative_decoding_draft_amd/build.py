@@ -32,7 +32,7 @@ COMMON_FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 SOURCES = ["prep.hip", "generic.hip", "absorb.hip", "attn.hip", "uv.hip", "api.hip",
-           "sampler.cpp", "bwd_misc.hip", "bwd_gemm.hip", "bwd_attn.hip"]
+           "sampler.cpp", "bwd_misc.hip", "bwd_gemm.hip", "bwd_attn.hip", "layer.hip"]
 
 
 def _hipcc() -> str:
@@ -79,8 +79,10 @@ def build(verbose: bool = True, extra_flags=()) -> str:
                          "clang++")
     if not os.path.exists(clang):
         clang = "/opt/rocm/lib/llvm/bin/clang++"
+    # rocBLAS (the MLA block's projections) from the same directory as the
+    # HIP runtime, so that both are the instances torch has loaded
     cmd = [clang, "-shared", "-fPIC", "-o", tmp, *objs, f"-L{rt}", f"-Wl,-rpath,{rt}",
-           "-l:libamdhip64.so", "-Wl,--no-undefined", "-lstdc++", "-lm"]
+           "-l:libamdhip64.so", "-l:librocblas.so", "-Wl,--no-undefined", "-lstdc++", "-lm"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")

@@ -149,6 +149,9 @@ RopeTheta make_theta(const dspark_attn_desc& d) {
 }
 
 }  // namespace
+
+void set_last_error(const char* msg) { g_last_error = msg; }
+
 }  // namespace dspark
 
 using namespace dspark;

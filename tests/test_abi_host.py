@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert set(sd.EXPORTS) == declared
-    assert sd.abi_version() == 3
+    assert sd.abi_version() == 4
 
 
 def glm_desc(**kw):
@@ -263,3 +263,42 @@ def test_bwd_plan_and_event_count_check():
 def test_bwd_empty_problem_is_a_no_op():
     d = glm_desc(N=0)
     assert sd._lib.lib.dspark_attn_bwd(ctypes.byref(d), *([None] * 20), 0, None) == sd.DSPARK_OK
+
+
+# ---------------------------------------------------------------------------
+# MLA block entry point: validation before any launch
+# ---------------------------------------------------------------------------
+
+def layer_desc(**kw):
+    return sd.make_layer_desc(glm_desc(**kw), hidden=6144, q_rank=2048)
+
+
+def test_layer_desc_layout_and_workspace():
+    assert ctypes.sizeof(sd.LayerDesc) == ctypes.sizeof(sd._lib.Desc) + 4 + 4 + 8
+    d = layer_desc(S=2048, N=64)
+    need = sd.layer_workspace_size(d)
+    rows = 5 * 64
+    inter = (rows * 6144 + rows * 2048 + rows * 64 * 256 + (2048 + rows) * 576 * 2
+             + rows * 64 * 256) * 2
+    assert need >= inter + sd.workspace_size(d.attn)
+    bad = sd.make_layer_desc(glm_desc(), hidden=0, q_rank=2048)
+    assert sd._lib.lib.dspark_mla_layer_workspace_size(ctypes.byref(bad)) == 0
+
+
+def test_layer_null_misaligned_and_workspace_errors_before_any_launch():
+    d = layer_desc()
+    need = sd.layer_workspace_size(d)
+    good = [0x10000 * (i + 1) for i in range(14)]
+    lib = sd._lib.lib
+    call = lambda p, ws, n: lib.dspark_mla_layer_fwd(ctypes.byref(d), *p, ws, n, None)
+    for i in range(14):
+        p = list(good)
+        p[i] = None
+        assert call(p, 0x7000000, need) == sd.DSPARK_EINVAL and "NULL" in sd.last_error()
+    p = list(good)
+    p[0] += 2
+    assert call(p, 0x7000000, need) == sd.DSPARK_EINVAL and "aligned" in sd.last_error()
+    assert call(good, 0x7000000, need - 1) == sd.DSPARK_EWORKSPACE
+    assert call(good, 0x7000010, need) == sd.DSPARK_EWORKSPACE
+    neg = sd.make_layer_desc(glm_desc(), hidden=6144, q_rank=2048, rms_eps=-1.0)
+    assert lib.dspark_mla_layer_fwd(ctypes.byref(neg), *good, 0x7000000, need, None) == sd.DSPARK_EINVAL

@@ -1,0 +1,105 @@
+"""Parity of the MLA block of a draft layer (dspark_mla_layer_fwd through the
+C ABI) with the oracle's layer_forward, on the same seeded inputs.
+
+Compared per kept row: the output out = H + o_proj(attention), and the delta
+out - H (the block's contribution, smaller than H).  Rows of padding blocks
+must equal H bit for bit (their attention rows are 0).
+
+Tolerances: fp32 (generic attention, fp32 rocBLAS GEMMs): rel-L2 <= 2e-5 on
+the delta.  bf16: every intermediate (normalised h, c^Q, q, [c^KV ; k^R],
+the attention output) and the output are rounded to bf16.  The output is
+held to rel-L2 <= 5e-3.  The delta carries the attention's error (rel-L2
+~3e-3 on its bf16 output) and the projections' roundings, within 1e-2, plus
+the rounding of out itself, whose RMS is 2^-9/sqrt(3) |out| ~ 1.13e-3 |H| and
+so 1.13e-3 |H| / |delta| relative to the delta: the delta's bound is
+1e-2 + 2 x 1.13e-3 |H| / |delta| (about 2.4e-2 where |delta| / |H| = 0.16).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as wk
+from gpu_util import anchors_for, desc_for, log
+from workloads.device import to_torch, upload_anchors, upload_layer
+
+pytestmark = pytest.mark.gpu
+
+TINY = dict(H=2, D=16, d_c=8, d_r=4, d_v=8, W=6)
+
+
+def run_layer(wl, li, anchors, keep, force_generic=False):
+    import torch
+    import speculative_decoding_draft_amd as sd
+    t = upload_layer(wl)
+    desc = sd.make_layer_desc(desc_for(wl), li.hidden, li.q_rank, li.rms_eps)
+    w = {k: to_torch(getattr(li, k), wl.dtype, "cuda") for k in ("g_in", "w_qa", "g_qa", "w_qb",
+                                                                 "w_kva", "g_kva", "w_o")}
+    w["w_uk"], w["w_uv"] = t["w_uk"], t["w_uv"]
+    hd = to_torch(li.h_draft, wl.dtype, "cuda")
+    hc = to_torch(li.h_ctx, wl.dtype, "cuda")
+    a, k = upload_anchors(anchors, keep)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    out = torch.full(hd.shape, float("nan"), dtype=tdt, device="cuda")
+    ws = torch.empty(sd.layer_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    sd.mla_layer_fwd(desc, hd, hc, w, a, k, out, ws, force_generic=force_generic)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), ws
+
+
+def check(wl, li, gpu, ref, keep, tol_delta, tol_out, what):
+    H = O.dspark_oracle._f64(li.h_draft, wl.dtype)
+    kept = np.repeat(keep.astype(bool), 5, axis=1)
+    assert np.array_equal(gpu[~kept], H[~kept]), f"{what}: padding rows are not H"
+    g, r, h = gpu[kept], ref[kept], H[kept]
+    assert np.all(np.isfinite(g))
+    rel_out = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+    rel_d = float(np.linalg.norm((g - h) - (r - h)) / np.linalg.norm(r - h))
+    mx = float(np.abs(g - r).max())
+    ratio = float(np.linalg.norm(r - h) / np.linalg.norm(h))
+    if wl.dtype == "bf16":          # the output's own rounding, relative to the delta
+        tol_delta = tol_delta + 2 * 2.0 ** -9 / np.sqrt(3.0) / ratio
+    log(f"  {what}: out rel_l2={rel_out:.3e} delta rel_l2={rel_d:.3e} (bound {tol_delta:.2e}) "
+        f"max_abs={mx:.3e} |delta|/|H|={ratio:.3f}")
+    assert rel_d <= tol_delta and rel_out <= tol_out, (what, rel_d, rel_out)
+
+
+def test_layer_tiny_fp32():
+    wl = wk.make_workload("tiny-layer", B=1, S=40, N=6, dims=TINY, dtype="f32", recipe="headline",
+                          seed=31, recipe_args=dict(low_frac=0.5))
+    li = wk.make_layer_inputs(wl, hidden=24, q_rank=12, seed=32)
+    gpu, _ = run_layer(wl, li, wl.anchors, wl.keep)
+    ref = O.layer_forward(wl, li)
+    check(wl, li, gpu, ref, wl.keep, 2e-5, 2e-5, "tiny fp32")
+
+
+@pytest.mark.parametrize("k,S,N,B", [(2, 2048, 64, None), (4, 600, 24, None), (3, 400, 12, 2)])
+def test_layer_glm_dims_bf16(k, S, N, B):
+    wl = wk.scaled(k, S=S, N=N, B=B)
+    li = wk.make_layer_inputs(wl, hidden=6144, q_rank=2048, seed=33)
+    ga, gk, oa, ok = anchors_for(wl)
+    log(f"case {wl.name}")
+    gpu, ws = run_layer(wl, li, ga, gk)
+    ref = O.layer_forward(wl, li, anchors=oa, keep=ok)
+    check(wl, li, gpu, ref, ok, 1e-2, 5e-3, wl.name)
+
+
+def test_layer_generic_attention_matches():
+    """force_generic runs the attention on the generic kernel; the block's
+    output agrees with the MFMA path's within the bf16 tolerance."""
+    wl = wk.scaled(4, S=300, N=12)
+    li = wk.make_layer_inputs(wl, hidden=6144, q_rank=2048, seed=34)
+    a, _ = run_layer(wl, li, wl.anchors, wl.keep)
+    b, _ = run_layer(wl, li, wl.anchors, wl.keep, force_generic=True)
+    ref = O.layer_forward(wl, li)
+    check(wl, li, b, ref, wl.keep, 1e-2, 5e-3, "generic attention")
+    kept = np.repeat(wl.keep.astype(bool), 5, axis=1)
+    assert np.linalg.norm(a[kept] - b[kept]) / np.linalg.norm(b[kept]) < 5e-3
+
+
+def test_layer_repeat_runs_are_bit_identical():
+    wl = wk.scaled(2, S=512, N=16)
+    li = wk.make_layer_inputs(wl, hidden=6144, q_rank=2048, seed=35)
+    ga, gk, _, _ = anchors_for(wl)
+    a, _ = run_layer(wl, li, ga, gk)
+    b, _ = run_layer(wl, li, ga, gk)
+    assert np.array_equal(a, b)
