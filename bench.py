@@ -22,7 +22,9 @@ with v = min(A, W-1) + 5.
 The same line carries a "backward" object: dspark_attn_bwd on the same
 inputs with a seeded upstream gradient (--bwd-steps timed calls), its useful
 TFLOP/s (gradient products only; see bwd_useful_flop) and per-launch times.
-The headline metric is the forward's.
+A "layer" object times dspark_mla_layer_fwd (the MLA block of one draft
+layer: RMSNorms, projections, the attention, o_proj) on seeded hidden states
+and weights of the page's shapes.  The headline metric is the forward's.
 """
 from __future__ import annotations
 
@@ -249,6 +251,87 @@ def bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sp
     return out
 
 
+LAYER_STAGES = ("input_norm", "q_a", "q_b", "kv_a", "attention", "o_proj")
+
+
+def layer_flop(wl, anchors, keep, hidden, q_rank):
+    """FLOP of the MLA block on the rows the masked attention needs: the
+    query-side projections and o_proj for the rows of kept blocks, kv_a for
+    the union of the kept windows plus the kept blocks' own rows, and the
+    attention's useful FLOP.  Returns (total, {stage: flop})."""
+    H, D, dc, dr, dv = wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v
+    kept = [(b, int(anchors[b, n])) for b in range(wl.B) for n in range(wl.N) if keep[b, n]]
+    rows = 5 * len(kept)
+    union = 0
+    for b in range(wl.B):
+        cover = np.zeros(wl.S, dtype=bool)
+        for bb, a in kept:
+            if bb == b:
+                cover[max(0, a - wl.W + 1):a] = True
+        union += int(cover.sum())
+    st = {"q_a": 2 * rows * hidden * q_rank,
+          "q_b": 2 * rows * q_rank * H * (dc + dr),
+          "kv_a": 2 * (union + rows) * hidden * (D + dr),
+          "attention": useful_flop(anchors, keep, wl.W, H, D, dc, dr, dv),
+          "o_proj": 2 * rows * H * dv * hidden}
+    return sum(st.values()), st
+
+
+def bench_layer(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sptr, hip, steps,
+                hidden=6144, q_rank=2048):
+    """Times dspark_mla_layer_fwd (the MLA block of one draft layer) on the
+    same attention inputs' workload, with seeded hidden states and weights of
+    the page's shapes (d = 6144, q_lora_rank = 2048)."""
+    import workloads as wk
+    from workloads.device import to_torch
+    li = wk.make_layer_inputs(wl, hidden, q_rank, seed=5)
+    t = tensors[0]
+    w = {k: to_torch(getattr(li, k), wl.dtype, "cuda") for k in ("g_in", "w_qa", "g_qa", "w_qb",
+                                                                 "w_kva", "g_kva", "w_o")}
+    w["w_uk"], w["w_uv"] = t["w_uk"], t["w_uv"]
+    hd = to_torch(li.h_draft, wl.dtype, "cuda")
+    hc = to_torch(li.h_ctx, wl.dtype, "cuda")
+    del li
+    ld = sd.make_layer_desc(desc, hidden, q_rank)
+    out = torch.empty_like(hd)
+    ws = torch.empty(sd.layer_workspace_size(ld), dtype=torch.uint8, device="cuda")
+    args = (ld, hd, hc, w, a_dev, k_dev, out, ws)
+    # pick the GEMM kernels for these shapes first (synchronous, seconds)
+    t_tune = time.perf_counter()
+    sd.mla_layer_tune(*args, stream=sptr)
+    torch.cuda.synchronize()
+    t_tune = time.perf_counter() - t_tune
+    w0, n_w = time.perf_counter(), 0
+    while n_w < 3 or (time.perf_counter() - w0) < 0.1:
+        sd.mla_layer_fwd(*args, stream=sptr)
+        n_w += 1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sd.mla_layer_fwd(*args, stream=sptr)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ev = hip.create(len(LAYER_STAGES) + 1)
+    sd.mla_layer_fwd(*args, stream=sptr, stage_events=ev)
+    torch.cuda.synchronize()
+    stage_us = {s: hip.elapsed_ms(ev[i], ev[i + 1]) * 1e3 for i, s in enumerate(LAYER_STAGES)}
+    hip.destroy(ev)
+    flop, st_flop = layer_flop(wl, anchors, keep, hidden, q_rank)
+    dom = max(("q_a", "q_b", "kv_a", "o_proj"), key=lambda s: stage_us[s])
+    ach = st_flop[dom] / (stage_us[dom] * 1e-6) / 1e12
+    return {"ms_per_step": round(wall * 1e3, 4), "steps": steps, "warmup": n_w,
+            "hidden": hidden, "q_rank": q_rank, "gemm_tuning_s": round(t_tune, 2),
+            "useful_gflop_per_step": round(flop / 1e9, 3),
+            "value": round(flop / wall / 1e12, 3), "unit": "TFLOP/s",
+            "frac_of_bf16_peak": round(flop / wall / 1e12 / MI355X_BF16_PEAK_TFLOPS, 4),
+            "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+            "roofline": {"kernel": dom + " GEMM (rocBLAS)", "bound": "mfma",
+                         "achieved": round(ach, 1), "peak": MI355X_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / MI355X_BF16_PEAK_TFLOPS, 4),
+                         "traffic": None, "avg_launch_us": round(stage_us[dom], 2),
+                         "algorithmic_flop_per_launch": st_flop[dom]}}
+
+
 class HipEvents:
     """hipEvent_t handles from the HIP runtime torch loaded (one runtime per
     process), so that they can be recorded by the library on torch's stream."""
@@ -331,6 +414,9 @@ def main():
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the backward measurement (the 'backward' object)")
     ap.add_argument("--bwd-steps", type=int, default=20)
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the MLA block measurement (the 'layer' object)")
+    ap.add_argument("--layer-steps", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (the reference "
@@ -494,6 +580,12 @@ def main():
                                                 keep, desc, sptr, hip, args.bwd_steps)
         except Exception as e:   # the forward line is still reported
             result["backward"] = {"error": f"{type(e).__name__}: {e}"}
+    if not args.no_layer and wl.dtype == "bf16":
+        try:
+            result["layer"] = bench_layer(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep,
+                                          desc, sptr, hip, args.layer_steps)
+        except Exception as e:   # the forward line is still reported
+            result["layer"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, anchors, keep, args.cpu_budget)
     print(json.dumps(result), flush=True)

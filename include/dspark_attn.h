@@ -304,7 +304,7 @@ size_t dspark_mla_layer_workspace_size(const dspark_layer_desc* desc);
  *                        (their attention rows are 0), rows of a kept block
  *                        with a bad anchor are NaN
  * The projections run on rocBLAS (fp32 accumulation, no atomics: the same
- * call gives the same bits).  The first call on a device and host thread
+ * call gives the same bits; dspark_mla_layer_tune picks the kernels).  The first call on a device and host thread
  * creates a rocBLAS handle that is kept until the process ends -- the one
  * allocation the library makes.  out must not alias any input. */
 dspark_status dspark_mla_layer_fwd(const dspark_layer_desc* desc,
@@ -328,6 +328,23 @@ dspark_status dspark_mla_layer_fwd_ex(const dspark_layer_desc* desc,
                                       const int32_t* anchors, const uint8_t* keep,
                                       void* out, void* workspace, size_t ws_bytes, void* stream,
                                       const dspark_attn_opts* opts);
+
+/* dspark_mla_layer_fwd, once, while choosing the GEMM kernels: for each of
+ * the block's projections every rocBLAS solution that applies to its shape
+ * (and rocBLAS's default) is timed on `stream` -- which this call
+ * synchronises, repeatedly -- and the fastest is recorded for that shape on
+ * the current device; later calls of dspark_mla_layer_fwd(_ex) with the same
+ * shapes, from any thread, use the recorded choices.  Without it rocBLAS
+ * chooses (for the o_proj shape of GLM-5.2 its choice ran at half the
+ * fastest one's rate).  Same arguments and outputs as dspark_mla_layer_fwd;
+ * takes seconds; must not run under stream capture. */
+dspark_status dspark_mla_layer_tune(const dspark_layer_desc* desc,
+                                    const void* h_draft, const void* h_ctx,
+                                    const void* g_in, const void* w_qa, const void* g_qa,
+                                    const void* w_qb, const void* w_kva, const void* g_kva,
+                                    const void* w_uk, const void* w_uv, const void* w_o,
+                                    const int32_t* anchors, const uint8_t* keep,
+                                    void* out, void* workspace, size_t ws_bytes, void* stream);
 
 /* Synchronises `stream`, then reads the status area of a workspace used by
  * the last dspark_attn_fwd / dspark_attn_bwd / dspark_build_index on it.  Returns DSPARK_OK, or

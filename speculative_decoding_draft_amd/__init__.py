@@ -3,7 +3,7 @@ of a draft layer around it.
 
 The compute lives in libdspark_attn.so (hand-written HIP kernels behind the C
 ABI of include/dspark_attn.h); this package is its Python binding.  Build the
-library with ``python -m speculative_decoding_draft_amd.build``.
+library with ``python speculative_decoding_draft_amd/build.py``.
 """
 from ._lib import (  # noqa: F401
     DSPARK_BF16,
@@ -31,6 +31,7 @@ from ._lib import (  # noqa: F401
     make_layer_desc,
     layer_workspace_size,
     mla_layer_fwd,
+    mla_layer_tune,
     build_index,
     last_error,
     make_desc,

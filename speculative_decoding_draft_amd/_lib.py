@@ -32,7 +32,8 @@ DSPARK_BF16 = 1
 EXPORTS = ("dspark_attn_workspace_size", "dspark_attn_fwd", "dspark_attn_fwd_ex", "dspark_attn_plan",
            "dspark_attn_bwd_workspace_size", "dspark_attn_bwd", "dspark_attn_bwd_ex",
            "dspark_attn_bwd_plan", "dspark_mla_layer_workspace_size", "dspark_mla_layer_fwd",
-           "dspark_mla_layer_fwd_ex", "dspark_build_index", "dspark_select_anchors_host",
+           "dspark_mla_layer_fwd_ex", "dspark_mla_layer_tune", "dspark_build_index",
+           "dspark_select_anchors_host",
            "dspark_read_device_status", "dspark_last_error", "dspark_abi_version")
 
 
@@ -65,7 +66,7 @@ class Opts(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m speculative_decoding_draft_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python speculative_decoding_draft_amd/build.py`")
     # torch must bring in its HIP runtime (soname libamdhip64.so.7) first, so
     # that the library binds to that one instance: torch owns the device
     # memory and streams passed in, and a second runtime in the process would
@@ -100,6 +101,8 @@ def _load():
     lib.dspark_mla_layer_fwd.restype = i32
     lib.dspark_mla_layer_fwd_ex.argtypes = layer_args + [ctypes.POINTER(Opts)]
     lib.dspark_mla_layer_fwd_ex.restype = i32
+    lib.dspark_mla_layer_tune.argtypes = layer_args
+    lib.dspark_mla_layer_tune.restype = i32
     lib.dspark_build_index.argtypes = [pd, vp, vp, vp, vp, sz, vp]
     lib.dspark_build_index.restype = i32
     lib.dspark_select_anchors_host.argtypes = [vp, i32, i32, u64, vp, vp]
@@ -306,6 +309,16 @@ def mla_layer_fwd(desc: LayerDesc, h_draft, h_ctx, weights, anchors, keep, out, 
         return
     opts, _arr = _opts(stage_events, force_generic, 0)
     _check(lib.dspark_mla_layer_fwd_ex(*args, ctypes.byref(opts)))
+
+
+def mla_layer_tune(desc: LayerDesc, h_draft, h_ctx, weights, anchors, keep, out, workspace,
+                   stream=None) -> None:
+    """dspark_mla_layer_tune: one block call that also picks its GEMM kernels."""
+    args = [ctypes.byref(desc), _ptr(h_draft), _ptr(h_ctx)]
+    args += [_ptr(weights[k]) for k in LAYER_WEIGHTS]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args += [_ptr(anchors), _ptr(keep), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)]
+    _check(lib.dspark_mla_layer_tune(*args))
 
 
 def build_index(desc: Desc, anchors, keep, index_out, workspace, stream=None) -> None:

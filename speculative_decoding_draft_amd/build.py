@@ -1,6 +1,8 @@
 """Build libdspark_attn.so in-tree with hipcc for gfx950.
 
-    python -m speculative_decoding_draft_amd.build
+    python speculative_decoding_draft_amd/build.py
+
+(run as a file, not with -m: importing the package loads the library.)
 
 Compiles every source under csrc/ (in parallel) and links the shared library
 next to this file.  Always rebuilds.

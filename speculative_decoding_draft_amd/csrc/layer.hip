@@ -12,10 +12,15 @@
 // here; q^R and k^R go to the attention unrotated (it rotates them while
 // loading).  RMSNorm is x / sqrt(mean(x^2) + eps) * g; the page names the
 // op without a formula or epsilon, so eps is a descriptor field.
+#define ROCBLAS_BETA_FEATURES_API   // rocblas_gemm_ex_get_solutions (kernel choice)
 #include <rocblas/rocblas.h>
 
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
 
 #include "kernels.hpp"
 
@@ -71,14 +76,95 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(
     }
 }
 
+// bf16 rows with n % 512 == 0 (n <= 512 * kMaxChunks) and 16-byte aligned
+// rows: one wave per row, the row held in registers (n / 512 chunks of 8
+// per lane), reductions by shuffles only.
+constexpr int kMaxChunks = 16;
+template <int CH>
+__global__ __launch_bounds__(256) void rmsnorm_wave_kernel(
+    const bf16* __restrict__ x, size_t ldx, const bf16* __restrict__ g, bf16* __restrict__ y,
+    size_t ldy, bf16* __restrict__ tail_out, int n_tail, size_t rows, float eps) {
+    const int lane = threadIdx.x & 63;
+    constexpr int n = 512 * CH;
+    for (size_t r = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows;
+         r += (size_t)gridDim.x * 4) {
+        const bf16* xr = x + r * ldx;
+        bf16x8 v[CH];
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            v[c] = gld16(xr + 8 * (lane + 64 * c));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss += (float)v[c][i] * (float)v[c][i];
+        }
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        const float inv = rsqrtf(ss / (float)n + eps);
+        bf16* yr = y + r * ldy;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const bf16x8 gw = gld16(g + 8 * (lane + 64 * c));
+            bf16x8 o;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = (bf16)((float)v[c][i] * inv * (float)gw[i]);
+            gst16(yr + 8 * (lane + 64 * c), o);
+        }
+        if (tail_out)
+            for (int i = lane; i < n_tail; i += 64) tail_out[r * (size_t)n_tail + i] = xr[n + i];
+    }
+}
+
 template <typename T>
 hipError_t launch_rmsnorm(const T* x, size_t ldx, const T* g, T* y, size_t ldy, T* tail,
                           int n_tail, size_t rows, int n, float eps, hipStream_t s) {
     if (rows == 0) return hipSuccess;
+    const auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if constexpr (sizeof(T) == 2) {
+        const int ch = n / 512;
+        if (n % 512 == 0 && ch >= 1 && ch <= kMaxChunks && ldx % 8 == 0 && ldy % 8 == 0 &&
+            al(x) && al(y) && al(g)) {
+            const size_t want = (rows + 3) / 4;
+            const int grid = (int)(want < 16384 ? want : 16384);
+#define DSPARK_NORM_CASE(C)                                                                   \
+    case C:                                                                                   \
+        hipLaunchKernelGGL(rmsnorm_wave_kernel<C>, dim3(grid), dim3(256), 0, s, x, ldx, g, y, \
+                           ldy, tail, n_tail, rows, eps);                                     \
+        return hipGetLastError();
+            switch (ch) {
+                DSPARK_NORM_CASE(1) DSPARK_NORM_CASE(2) DSPARK_NORM_CASE(3) DSPARK_NORM_CASE(4)
+                DSPARK_NORM_CASE(6) DSPARK_NORM_CASE(8) DSPARK_NORM_CASE(12) DSPARK_NORM_CASE(16)
+                default: break;
+            }
+#undef DSPARK_NORM_CASE
+        }
+    }
     const int grid = (int)(rows < 8192 ? rows : 8192);
     hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(grid), dim3(kNormThreads), 0, s, x, ldx, g, y, ldy,
                        tail, n_tail, rows, n, eps);
     return hipGetLastError();
+}
+
+// [rows][H][dc + dr] -> [rows][H][dc] and [rows][H][dr], in 16-byte pieces
+// when dc and dr allow (vec elements of 16 bytes), element by element
+// otherwise (vec = 1)
+template <typename T>
+__global__ __launch_bounds__(256) void split_heads_kernel(const T* __restrict__ q, T* __restrict__ qn,
+                                                          T* __restrict__ qr, size_t rows, int H,
+                                                          int dc, int dr, int vec) {
+    const int w = dc + dr;
+    const size_t per_row = (size_t)H * w / vec;
+    const size_t total = rows * per_row;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (size_t)gridDim.x * blockDim.x) {
+        const size_t r = e / per_row;
+        const int k = (int)(e % per_row) * vec, h = k / w, j = k % w;
+        const T* src = q + r * (size_t)H * w + k;
+        T* dst = (j < dc) ? qn + (r * H + h) * (size_t)dc + j : qr + (r * H + h) * (size_t)dr + (j - dc);
+        if (vec * sizeof(T) == 16) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        } else {
+            *dst = *src;
+        }
+    }
 }
 
 // ---- rocBLAS: one handle per (thread, device), created on first use and
@@ -98,24 +184,82 @@ rocblas_status get_handle(rocblas_handle* h) {
     return rocblas_status_success;
 }
 
+// rocBLAS kernel choices per (device, shape), recorded by
+// dspark_mla_layer_tune: the solution index that ran fastest, or 0 for
+// rocBLAS's own choice.  Shared by all threads.
+using GemmKey = std::tuple<int, int, int, int, int, int, int, int, int>;
+std::mutex g_choice_mu;
+std::map<GemmKey, int> g_choice;
+
 // Row-major D[M][N] = A[M][K] B[N][K]^T + beta C[M][N] (leading dims in
-// elements), batched `batch` times with element strides sa, sb, sd (C = D
-// pattern when beta = 0).  In rocBLAS's column-major terms this is
-// D^T = op_T(B^T) A^T, so B goes first.
-rocblas_status gemm_nt(rocblas_handle h, bool bf16_io, int M, int N, int K, const void* A,
-                       int lda, long long sa, const void* B, int ldb, long long sb, float beta,
-                       const void* C, int ldc, void* D, int ldd, long long sd, int batch) {
+// elements; C = nullptr: D's own pattern, read only if beta != 0).  In
+// rocBLAS's column-major terms this is D^T = op_T(B^T) A^T, so B goes first.
+// tune: time every solution rocBLAS offers for the shape (and its default)
+// on the handle's stream, synchronising it, record the fastest, then run it.
+// C must not alias D when tuning (every trial rewrites D).
+rocblas_status gemm_nt(rocblas_handle h, bool bf16_io, int M, int N, int K, const void* A, int lda,
+                       const void* B, int ldb, float beta, const void* C, int ldc, void* D, int ldd,
+                       bool tune) {
     const float alpha = 1.f;
     const rocblas_datatype t = bf16_io ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-    if (batch == 1) {
+    const void* Cp = C ? C : D;
+    const int ldcp = C ? ldc : ldd;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const GemmKey key{dev, M, N, K, lda, ldb, ldd, bf16_io ? 1 : 0, beta != 0.f ? 1 : 0};
+    auto run = [&](int sol) {
         return rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, N, M, K,
-                               &alpha, B, t, ldb, A, t, lda, &beta, C ? C : D, t, C ? ldc : ldd, D,
-                               t, ldd, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+                               &alpha, B, t, ldb, A, t, lda, &beta, Cp, t, ldcp, D, t, ldd,
+                               rocblas_datatype_f32_r,
+                               sol > 0 ? rocblas_gemm_algo_solution_index
+                                       : rocblas_gemm_algo_standard,
+                               sol > 0 ? sol : 0, 0);
+    };
+    if (tune) {
+        rocblas_int n = 0;
+        rocblas_status st = rocblas_gemm_ex_get_solutions(
+            h, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &alpha, B, t, ldb, A,
+            t, lda, &beta, Cp, t, ldcp, D, t, ldd, rocblas_datatype_f32_r,
+            rocblas_gemm_algo_solution_index, 0, nullptr, &n);
+        std::vector<rocblas_int> sols(n > 0 ? n : 0);
+        if (st == rocblas_status_success && n > 0)
+            st = rocblas_gemm_ex_get_solutions(
+                h, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &alpha, B, t, ldb, A,
+                t, lda, &beta, Cp, t, ldcp, D, t, ldd, rocblas_datatype_f32_r,
+                rocblas_gemm_algo_solution_index, 0, sols.data(), &n);
+        sols.insert(sols.begin(), 0);              // rocBLAS's default
+        hipStream_t s = nullptr;
+        rocblas_get_stream(h, &s);
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
+            return rocblas_status_internal_error;
+        int best = 0;
+        float best_ms = 1e30f;
+        for (int sol : sols) {
+            if (run(sol) != rocblas_status_success) continue;      // warm-up; skips invalid ones
+            (void)hipEventRecord(e0, s);
+            bool ok = true;
+            for (int i = 0; i < 3 && ok; ++i) ok = run(sol) == rocblas_status_success;
+            (void)hipEventRecord(e1, s);
+            (void)hipEventSynchronize(e1);
+            float ms = 0.f;
+            if (ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && ms < best_ms) {
+                best_ms = ms;
+                best = sol;
+            }
+        }
+        (void)hipEventDestroy(e0);
+        (void)hipEventDestroy(e1);
+        std::lock_guard<std::mutex> g(g_choice_mu);
+        g_choice[key] = best;
     }
-    return rocblas_gemm_strided_batched_ex(
-        h, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &alpha, B, t, ldb, sb, A, t,
-        lda, sa, &beta, C ? C : D, t, C ? ldc : ldd, sd, D, t, ldd, sd, batch,
-        rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+    int sol = 0;
+    {
+        std::lock_guard<std::mutex> g(g_choice_mu);
+        const auto it = g_choice.find(key);
+        if (it != g_choice.end()) sol = it->second;
+    }
+    return run(sol);
 }
 
 }  // namespace
@@ -123,8 +267,8 @@ rocblas_status gemm_nt(rocblas_handle h, bool bf16_io, int M, int N, int K, cons
 // Workspace of dspark_mla_layer_fwd: the block's intermediates, then the
 // attention's own workspace.
 struct LayerLayout {
-    size_t hn = 0, cq = 0, qn = 0, qr = 0, kvc = 0, kvb = 0, ckv_c = 0, kr_c = 0, ckv_b = 0,
-           kr_b = 0, o = 0, attn = 0, total = 0;
+    size_t hn = 0, cq = 0, qf = 0, qn = 0, qr = 0, kvc = 0, kvb = 0, ckv_c = 0, kr_c = 0,
+           ckv_b = 0, kr_b = 0, o = 0, attn = 0, total = 0;
 };
 
 LayerLayout layer_layout(const dspark_layer_desc& L, size_t attn_ws) {
@@ -136,6 +280,7 @@ LayerLayout layer_layout(const dspark_layer_desc& L, size_t attn_ws) {
     auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
     w.hn = take(q_rows * L.hidden * e);
     w.cq = take(q_rows * L.q_rank * e);
+    w.qf = take(q_rows * d.n_heads * (d.d_nope + d.d_rope) * e);
     w.qn = take(q_rows * d.n_heads * d.d_nope * e);
     w.qr = take(q_rows * d.n_heads * d.d_rope * e + 16);
     w.kvc = take(c_rows * (d.d_latent + d.d_rope) * e);
@@ -186,14 +331,16 @@ size_t dspark_mla_layer_workspace_size(const dspark_layer_desc* desc) {
     return layer_layout(*desc, a).total;
 }
 
-dspark_status dspark_mla_layer_fwd_ex(const dspark_layer_desc* desc, const void* h_draft,
-                                      const void* h_ctx, const void* g_in, const void* w_qa,
-                                      const void* g_qa, const void* w_qb, const void* w_kva,
-                                      const void* g_kva, const void* w_uk, const void* w_uv,
-                                      const void* w_o, const int32_t* anchors,
-                                      const uint8_t* keep, void* out, void* workspace,
-                                      size_t ws_bytes, void* stream,
-                                      const dspark_attn_opts* opts) {
+}  // extern "C"
+
+namespace {
+
+dspark_status layer_fwd(const dspark_layer_desc* desc, const void* h_draft, const void* h_ctx,
+                        const void* g_in, const void* w_qa, const void* g_qa, const void* w_qb,
+                        const void* w_kva, const void* g_kva, const void* w_uk, const void* w_uv,
+                        const void* w_o, const int32_t* anchors, const uint8_t* keep, void* out,
+                        void* workspace, size_t ws_bytes, void* stream,
+                        const dspark_attn_opts* opts, bool tune) {
     set_last_error("");
     if (!desc) return lfail(DSPARK_EINVAL, "desc is NULL");
     if (desc->hidden < 1 || desc->q_rank < 1)
@@ -275,25 +422,36 @@ dspark_status dspark_mla_layer_fwd_ex(const dspark_layer_desc* desc, const void*
     LSTEP_HIP(norm(h_draft, hid, g_in, hn, hid, nullptr, 0, q_rows, hid), "input RMSNorm launch");
     LMARK();
     // c^Q = RMSNorm(h W_qa^T)
-    LSTEP_BLAS(gemm_nt(h, bf, q_rows, qk, hid, hn, hid, 0, w_qa, hid, 0, 0.f, nullptr, 0, cq, qk,
-                       0, 1), "q_a_proj GEMM");
+    LSTEP_BLAS(gemm_nt(h, bf, q_rows, qk, hid, hn, hid, w_qa, hid, 0.f, nullptr, 0, cq, qk, tune),
+               "q_a_proj GEMM");
     LSTEP_HIP(norm(cq, qk, g_qa, cq, qk, nullptr, 0, q_rows, qk), "q_a RMSNorm launch");
     LMARK();
-    // per head: q^C = c^Q W_qb[h, :d_c]^T, q^R = c^Q W_qb[h, d_c:]^T, written in
-    // the attention's [row][head][dim] layouts
-    LSTEP_BLAS(gemm_nt(h, bf, q_rows, dc, qk, cq, qk, 0, w_qb, qk, (long long)(dc + dr) * qk, 0.f,
-                       nullptr, 0, qn, H * dc, dc, H), "q_b_proj (q^C) GEMM");
-    if (dr > 0)
-        LSTEP_BLAS(gemm_nt(h, bf, q_rows, dr, qk, cq, qk, 0,
-                           static_cast<const char*>(w_qb) + (size_t)dc * qk * e, qk,
-                           (long long)(dc + dr) * qk, 0.f, nullptr, 0, qr, H * dr, dr, H),
-                   "q_b_proj (q^R) GEMM");
+    // [q^C ; q^R] per head = c^Q W_qb^T (one GEMM: per-head strided-batched GEMMs
+    // of 192 and 64 columns ran at half the rate), then split into the
+    // attention's [row][head][dim] layouts
+    void* qf = base + L.qf;
+    LSTEP_BLAS(gemm_nt(h, bf, q_rows, H * (dc + dr), qk, cq, qk, w_qb, qk, 0.f, nullptr, 0, qf,
+                       H * (dc + dr), tune), "q_b_proj GEMM");
+    {
+        const int vec = (dc % 8 == 0 && dr % 8 == 0 && bf) ? 8 : ((dc % 4 == 0 && dr % 4 == 0 && !bf) ? 4 : 1);
+        const size_t total = (size_t)q_rows * H * (dc + dr) / vec;
+        const size_t want = (total + 255) / 256;
+        const int grid = (int)(want < 16384 ? (want > 0 ? want : 1) : 16384);
+        if (bf)
+            hipLaunchKernelGGL(split_heads_kernel<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)qf,
+                               (bf16*)qn, (bf16*)qr, (size_t)q_rows, H, dc, dr, vec);
+        else
+            hipLaunchKernelGGL(split_heads_kernel<float>, dim3(grid), dim3(256), 0, s,
+                               (const float*)qf, (float*)qn, (float*)qr, (size_t)q_rows, H, dc, dr,
+                               vec);
+        LSTEP_HIP(hipGetLastError(), "q split launch");
+    }
     LMARK();
     // [c^KV ; k^R] = [H^ctx ; h] W_kva^T, then c^KV <- RMSNorm(c^KV) and the k^R split
-    LSTEP_BLAS(gemm_nt(h, bf, c_rows, D + dr, hid, h_ctx, hid, 0, w_kva, hid, 0, 0.f, nullptr, 0,
-                       kvc, D + dr, 0, 1), "kv_a_proj (context) GEMM");
-    LSTEP_BLAS(gemm_nt(h, bf, q_rows, D + dr, hid, hn, hid, 0, w_kva, hid, 0, 0.f, nullptr, 0, kvb,
-                       D + dr, 0, 1), "kv_a_proj (draft) GEMM");
+    LSTEP_BLAS(gemm_nt(h, bf, c_rows, D + dr, hid, h_ctx, hid, w_kva, hid, 0.f, nullptr, 0, kvc,
+                       D + dr, tune), "kv_a_proj (context) GEMM");
+    LSTEP_BLAS(gemm_nt(h, bf, q_rows, D + dr, hid, hn, hid, w_kva, hid, 0.f, nullptr, 0, kvb, D + dr,
+                       tune), "kv_a_proj (draft) GEMM");
     LSTEP_HIP(norm(kvc, D + dr, g_kva, ckv_c, D, kr_c, dr, c_rows, D), "kv_a RMSNorm launch");
     LSTEP_HIP(norm(kvb, D + dr, g_kva, ckv_b, D, kr_b, dr, q_rows, D), "kv_a RMSNorm launch");
     LMARK();
@@ -308,13 +466,39 @@ dspark_status dspark_mla_layer_fwd_ex(const dspark_layer_desc* desc, const void*
     if (ast != DSPARK_OK) return ast;            // dspark_last_error() says why
     LMARK();
     // out = H + o W_o^T
-    LSTEP_BLAS(gemm_nt(h, bf, q_rows, hid, H * dv, o, H * dv, 0, w_o, H * dv, 0, 1.f, h_draft, hid,
-                       out, hid, 0, 1), "o_proj GEMM");
+    LSTEP_BLAS(gemm_nt(h, bf, q_rows, hid, H * dv, o, H * dv, w_o, H * dv, 1.f, h_draft, hid, out,
+                       hid, tune), "o_proj GEMM");
     LMARK();
 #undef LSTEP_HIP
 #undef LSTEP_BLAS
 #undef LMARK
     return DSPARK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dspark_status dspark_mla_layer_fwd_ex(const dspark_layer_desc* desc, const void* h_draft,
+                                      const void* h_ctx, const void* g_in, const void* w_qa,
+                                      const void* g_qa, const void* w_qb, const void* w_kva,
+                                      const void* g_kva, const void* w_uk, const void* w_uv,
+                                      const void* w_o, const int32_t* anchors,
+                                      const uint8_t* keep, void* out, void* workspace,
+                                      size_t ws_bytes, void* stream,
+                                      const dspark_attn_opts* opts) {
+    return layer_fwd(desc, h_draft, h_ctx, g_in, w_qa, g_qa, w_qb, w_kva, g_kva, w_uk, w_uv, w_o,
+                     anchors, keep, out, workspace, ws_bytes, stream, opts, false);
+}
+
+dspark_status dspark_mla_layer_tune(const dspark_layer_desc* desc, const void* h_draft,
+                                    const void* h_ctx, const void* g_in, const void* w_qa,
+                                    const void* g_qa, const void* w_qb, const void* w_kva,
+                                    const void* g_kva, const void* w_uk, const void* w_uv,
+                                    const void* w_o, const int32_t* anchors, const uint8_t* keep,
+                                    void* out, void* workspace, size_t ws_bytes, void* stream) {
+    return layer_fwd(desc, h_draft, h_ctx, g_in, w_qa, g_qa, w_qb, w_kva, g_kva, w_uk, w_uv, w_o,
+                     anchors, keep, out, workspace, ws_bytes, stream, nullptr, true);
 }
 
 dspark_status dspark_mla_layer_fwd(const dspark_layer_desc* desc, const void* h_draft,

@@ -103,3 +103,31 @@ def test_layer_repeat_runs_are_bit_identical():
     a, _ = run_layer(wl, li, ga, gk)
     b, _ = run_layer(wl, li, ga, gk)
     assert np.array_equal(a, b)
+
+
+def test_layer_tune_then_forward():
+    """dspark_mla_layer_tune returns the block's output like the plain call and
+    records kernel choices; later plain calls use them, give identical bits to
+    each other and still match the oracle."""
+    import torch
+    import speculative_decoding_draft_amd as sd
+    wl = wk.scaled(4, S=700, N=20)
+    li = wk.make_layer_inputs(wl, hidden=6144, q_rank=2048, seed=36)
+    t = upload_layer(wl)
+    desc = sd.make_layer_desc(desc_for(wl), li.hidden, li.q_rank, li.rms_eps)
+    w = {k: to_torch(getattr(li, k), wl.dtype, "cuda") for k in ("g_in", "w_qa", "g_qa", "w_qb",
+                                                                 "w_kva", "g_kva", "w_o")}
+    w["w_uk"], w["w_uv"] = t["w_uk"], t["w_uv"]
+    hd, hc = to_torch(li.h_draft, "bf16", "cuda"), to_torch(li.h_ctx, "bf16", "cuda")
+    a, k = upload_anchors(wl.anchors, wl.keep)
+    ws = torch.empty(sd.layer_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    outs = []
+    for tune in (True, False, False):
+        out = torch.full(hd.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+        (sd.mla_layer_tune if tune else sd.mla_layer_fwd)(desc, hd, hc, w, a, k, out, ws)
+        torch.cuda.synchronize()
+        outs.append(out.float().cpu().numpy().astype(np.float64))
+    ref = O.layer_forward(wl, li)
+    for o in outs:
+        check(wl, li, o, ref, wl.keep, 1e-2, 5e-3, "tuned")
+    assert np.array_equal(outs[1], outs[2])
