@@ -49,9 +49,9 @@ KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.h
 # plain 256 MiB device copy), with the digest of the kernel's sources when the
 # counters were taken.  A kernel whose sources changed since reports null.
 PMC_TRAFFIC = {
-    "absorb": (358_772_640, "1173152b9dfcdc71"),
-    "attention": (583_813_805, "9a8efa059feee454"),
-    "w_uv": (394_468_035, "8759cdadabfffc32"),
+    "absorb": (358_772_932, "1173152b9dfcdc71"),
+    "attention": (583_907_471, "9a8efa059feee454"),
+    "w_uv": (394_468_589, "8759cdadabfffc32"),
 }
 
 
@@ -66,12 +66,12 @@ BWD_KERNEL_SOURCES = {
     "final": ("bwd_misc.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
 }
 BWD_PMC_TRAFFIC = {
-    "attention_bwd": (1_294_560_937, "ba86a7add3441456"),
-    "dw": (753_618_158, "e9bdb2e8cbad973d"),
-    "dkv": (971_080_342, "e9bdb2e8cbad973d"),
-    "dq_nope": (457_574_062, "e9bdb2e8cbad973d"),
-    "d_olat": (394_457_696, "1173152b9dfcdc71"),
-    "final": (311_151_167, "3f5a07842d4ad55c"),
+    "attention_bwd": (1_294_632_662, "ba86a7add3441456"),
+    "dw": (753_613_926, "7da7a4cb8373e829"),
+    "dkv": (971_075_413, "7da7a4cb8373e829"),
+    "dq_nope": (447_485_456, "7da7a4cb8373e829"),
+    "d_olat": (394_457_994, "1173152b9dfcdc71"),
+    "final": (311_151_661, "3f5a07842d4ad55c"),
 }
 
 

@@ -35,4 +35,11 @@ from .dspark_oracle import (  # noqa: F401
     loss,
     rmsnorm,
     layer_forward,
+    LOSS_ALPHAS,
+    eval_mask,
+    draft_logits,
+    teacher_logits,
+    confidence_logit,
+    step_terms,
+    loss_head,
 )

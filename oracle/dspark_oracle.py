@@ -553,3 +553,146 @@ def layer_forward(wl, li, anchors=None, keep=None, scale=None, blocks=None):
         w_uk=f(base.w_uk), w_uv=f(base.w_uv))]
     o = forward(sub, 0, anchors, keep, form="gathered", blocks=blocks, scale=scale)
     return Hd + o.reshape(B, L5, H * dv) @ f(li.w_o).T
+
+
+# ---------------------------------------------------------------------------
+# the output head and the training objective  (§5 "输出头": LM head, Markov
+# head, confidence head; §6 "训练目标": labels, alignment, eval_mask, CE, L1,
+# confidence BCE)
+# ---------------------------------------------------------------------------
+
+LOSS_ALPHAS = dict(ce=1.0, l1=0.9, conf=1.0)   # §6: dspark_*_alpha of the original recipe
+
+
+def eval_mask(loss_mask, anchors, keep, block: int = BLOCK) -> np.ndarray:
+    """§6 "eval_mask": step k of block n counts when A + k + 1 < S,
+    loss_mask[A + k + 1] = 1 and the block is kept, with a prefix cumprod along
+    the block (once a step is off, the later steps are off).  loss_mask[S-1] is
+    set to 0 on read.  A kept block whose anchor lies outside [0, S-2] counts
+    no step (its terms are NaN in ``loss_head``).  Returns [B, N, block] uint8."""
+    lm = np.array(loss_mask, dtype=bool, copy=True)
+    B, S = lm.shape
+    lm[:, S - 1] = False
+    N = np.asarray(anchors).shape[1]
+    m = np.zeros((B, N, block), dtype=np.uint8)
+    for b in range(B):
+        for n in range(N):
+            A = int(anchors[b, n])
+            if not keep[b, n] or A < 0 or A > S - 2:
+                continue
+            on = True
+            for k in range(block):
+                p = A + k + 1
+                on = on and p < S and bool(lm[b, p])
+                m[b, n, k] = on
+    return m
+
+
+def draft_logits(h_rows, prev_ids, w_lm, w_m1, w_m2) -> np.ndarray:
+    """§5: L = L^base + B(prev) for draft rows.  L^base = H^(L) W_lm^T (the
+    frozen Target lm_head, [V, d]); B(prev) = markov_w1[prev] markov_w2^T: the
+    Markov head embeds each position's predecessor token (the anchor at step 0,
+    the gold token x_{A+k} at step k) into r dims with markov_w1 ([V, r], a
+    lookup table) and maps it back to the vocabulary with markov_w2 ([V, r], no
+    bias).  B does not read H^(L)."""
+    e = np.asarray(w_m1, np.float64)[np.asarray(prev_ids)]
+    return np.asarray(h_rows, np.float64) @ np.asarray(w_lm, np.float64).T \
+        + e @ np.asarray(w_m2, np.float64).T
+
+
+def teacher_logits(z_rows, w_lm) -> np.ndarray:
+    """§6 "Alignment": T_k = lm_head(z_{A+k}) with the same frozen matrix."""
+    return np.asarray(z_rows, np.float64) @ np.asarray(w_lm, np.float64).T
+
+
+def confidence_logit(h_rows, prev_ids, w_m1, w_conf) -> np.ndarray:
+    """§5 "Confidence head": a bias-free linear layer over the concatenation of
+    H^(L) and the Markov embedding of prev (width d + r): one scalar per draft
+    position.  w_conf is [d + r] (the H^(L) part first)."""
+    e = np.asarray(w_m1, np.float64)[np.asarray(prev_ids)]
+    x = np.concatenate([np.asarray(h_rows, np.float64), e], axis=-1)
+    return x @ np.asarray(w_conf, np.float64)
+
+
+def step_terms(L, T, y, c):
+    """§6 per-step terms for rows of logits L (draft) and T (teacher), labels
+    y and confidence logits c:
+      ce  = -log softmax(L)[y]                      (CE against y_k)
+      l1  = || softmax(L) - softmax(T) ||_1         (L1)
+      a   = clip(1 - l1 / 2, 0, 1)                  (confidence target)
+      bce = -(a log sigmoid(c) + (1 - a) log(1 - sigmoid(c)))   (BCE with logits)
+    Returns (ce, l1, a, bce), each [rows]."""
+    L = np.asarray(L, np.float64)
+    T = np.asarray(T, np.float64)
+    p = _softmax_rows(L)
+    q = _softmax_rows(T)
+    ce = -np.log(p[np.arange(L.shape[0]), np.asarray(y)])
+    l1 = np.abs(p - q).sum(axis=1)
+    a = np.clip(1.0 - 0.5 * l1, 0.0, 1.0)
+    c = np.asarray(c, np.float64)
+    log_sig = -np.logaddexp(0.0, -c)          # log sigmoid(c)
+    log_1m = -np.logaddexp(0.0, c)            # log (1 - sigmoid(c))
+    bce = -(a * log_sig + (1.0 - a) * log_1m)
+    return ce, l1, a, bce
+
+
+def loss_head(lh, loss_mask, anchors, keep, alphas=None, blocks=None):
+    """The output head and the loss of §5–§6 for one batch (fp64).
+
+    lh: a ``workloads.LossInputs`` (input_ids [B, S], H^(L) [B, 5N, d],
+    z [B, S, d], w_lm [V, d], markov_w1 / markov_w2 [V, r], w_conf [d + r]).
+    For step k of a kept block with anchor A: prev = x_{A+k}, label
+    y_k = x_{A+k+1}, draft logits L_k from row 5n + k of H^(L), teacher logits
+    T_k from z_{A+k}.  Per-step outputs (``ce``, ``l1``, ``conf`` -- the
+    confidence logit -- and ``bce``, [B, N, 5]) are 0 where the eval mask is
+    0 and NaN for every step of a kept block whose anchor lies outside
+    [0, S-2].  The three terms are summed over the steps the eval mask keeps
+    and divided by their count (0 when no step counts); ``total`` is
+    alpha_ce ce + alpha_l1 l1 + alpha_conf bce (§6: 1, 0.9, 1).
+    blocks: optional list of (b, n) -- only those blocks' steps are computed
+    (the others are left 0); the means are then not formed (NaN)."""
+    al = dict(LOSS_ALPHAS, **(alphas or {}))
+    dt = lh.dtype
+    f = lambda a: _f64(a, dt)
+    ids = np.asarray(lh.input_ids)
+    B, S = ids.shape
+    N = np.asarray(anchors).shape[1]
+    blk = BLOCK
+    m = eval_mask(loss_mask, anchors, keep, blk)
+    out = {k: np.zeros((B, N, blk)) for k in ("ce", "l1", "conf", "bce")}
+    Hf, Z = f(lh.h_final), f(lh.z)
+    w_lm, w1, w2, wc = f(lh.w_lm), f(lh.w_m1), f(lh.w_m2), f(lh.w_conf)
+    todo = blocks if blocks is not None else [(b, n) for b in range(B) for n in range(N)]
+    for b, n in todo:
+        if not keep[b, n]:
+            continue
+        A = int(anchors[b, n])
+        if A < 0 or A > S - 2:
+            for k in out:
+                out[k][b, n, :] = np.nan
+            continue
+        ks = [k for k in range(blk) if m[b, n, k]]
+        if not ks:
+            continue
+        ks = np.array(ks)
+        prev = ids[b, A + ks]
+        rows = Hf[b, blk * n + ks]
+        L = draft_logits(rows, prev, w_lm, w1, w2)
+        T = teacher_logits(Z[b, A + ks], w_lm)
+        c = confidence_logit(rows, prev, w1, wc)
+        ce, l1, _, bce = step_terms(L, T, ids[b, A + ks + 1], c)
+        out["ce"][b, n, ks], out["l1"][b, n, ks] = ce, l1
+        out["conf"][b, n, ks], out["bce"][b, n, ks] = c, bce
+    out["eval_mask"] = m
+    cnt = int(m.sum())
+    out["count"] = cnt
+    if blocks is not None:
+        means = {k: np.nan for k in ("ce", "l1", "bce")}
+    else:
+        means = {k: (float(out[k].sum() / cnt) if cnt else 0.0) for k in ("ce", "l1", "bce")}
+        bad = any(np.isnan(out[k]).any() for k in ("ce", "l1", "bce"))
+        if bad:
+            means = {k: np.nan for k in means}
+    out["mean_ce"], out["mean_l1"], out["mean_bce"] = means["ce"], means["l1"], means["bce"]
+    out["total"] = al["ce"] * means["ce"] + al["l1"] * means["l1"] + al["conf"] * means["bce"]
+    return out

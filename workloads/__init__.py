@@ -324,3 +324,54 @@ def make_layer_inputs(wl: Workload, hidden: int, q_rank: int, seed: int = 5,
         g_kva=gain(D),
         w_o=_normal(rng, (hidden, H * dv), float(1 / np.sqrt(H * dv)), dt),
     )
+
+
+@dataclasses.dataclass
+class LossInputs:
+    """Inputs of the output head and loss (design page §5–§6) beyond the
+    anchors, keep mask and loss mask of the workload: the token ids, the
+    draft's final hidden states H^(L) [B, 5N, d], the Target's last hidden
+    states z [B, S, d], the frozen lm_head [V, d], the Markov head
+    (markov_w1 [V, r] as a lookup table, markov_w2 [V, r]) and the
+    confidence head [d + r]."""
+    vocab: int
+    hidden: int
+    rank: int
+    dtype: str
+    input_ids: np.ndarray   # [B, S] int32 in [0, V)
+    h_final: np.ndarray     # [B, 5N, d]
+    z: np.ndarray           # [B, S, d]
+    w_lm: np.ndarray        # [V, d]
+    w_m1: np.ndarray        # [V, r]
+    w_m2: np.ndarray        # [V, r]
+    w_conf: np.ndarray      # [d + r]
+
+
+def make_loss_inputs(wl: Workload, vocab: int, hidden: int, rank: int = 256, seed: int = 9,
+                     logit_std: float = 2.0, markov_std: float = 0.5) -> LossInputs:
+    """Seeded inputs for the output head and loss, in the workload's storage
+    type.  Token ids are uniform over the vocabulary.  Hidden rows are N(0, 1)
+    times a per-row gain drawn uniformly from [0.1, 2], so that the draft and
+    teacher distributions range from nearly flat to peaked and their L1
+    distance spans (0, 2).  lm_head is N(0, logit_std^2 / d) (logits of
+    standard deviation ~ logit_std x gain), markov_w1 N(0, 1), markov_w2
+    N(0, markov_std^2 / r), the confidence head N(0, 1 / (d + r))."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, wl.B, wl.S, wl.N,
+                                                                        vocab, hidden, rank])))
+    dt = wl.dtype
+
+    def rows(shape):
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        x *= rng.uniform(0.1, 2.0, size=shape[:-1] + (1,)).astype(np.float32)
+        return f32_to_bf16_bits(x) if dt == "bf16" else x
+
+    ids = rng.integers(0, vocab, size=(wl.B, wl.S), dtype=np.int32)
+    return LossInputs(
+        vocab=vocab, hidden=hidden, rank=rank, dtype=dt, input_ids=ids,
+        h_final=rows((wl.B, wl.block * wl.N, hidden)),
+        z=rows((wl.B, wl.S, hidden)),
+        w_lm=_normal(rng, (vocab, hidden), float(logit_std / np.sqrt(hidden)), dt),
+        w_m1=_normal(rng, (vocab, rank), 1.0, dt),
+        w_m2=_normal(rng, (vocab, rank), float(markov_std / np.sqrt(rank)), dt),
+        w_conf=_normal(rng, (hidden + rank,), float(1 / np.sqrt(hidden + rank)), dt),
+    )
