@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 4
+#define DSPARK_ABI_VERSION 5
 
 typedef enum dspark_status {
     DSPARK_OK = 0,
@@ -53,7 +53,8 @@ typedef enum dspark_status {
     DSPARK_EUNSUPPORTED = -2, /* valid but unsupported shape or dtype */
     DSPARK_EWORKSPACE = -3,   /* workspace missing, misaligned or too small */
     DSPARK_EHIP = -4,         /* a HIP runtime call failed (message has the HIP error) */
-    DSPARK_EANCHOR = -5       /* a kept block had an anchor outside [0, S-2] */
+    DSPARK_EANCHOR = -5,      /* a kept block had an anchor outside [0, S-2] */
+    DSPARK_ECAPACITY = -6     /* more kept blocks than dspark_loss_desc.max_kept_blocks */
 } dspark_status;
 
 typedef enum dspark_dtype {
@@ -345,6 +346,100 @@ dspark_status dspark_mla_layer_tune(const dspark_layer_desc* desc,
                                     const void* w_uk, const void* w_uv, const void* w_o,
                                     const int32_t* anchors, const uint8_t* keep,
                                     void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- the output head and the loss ------------------------------------
+ * §5 "输出头" and §6 "训练目标" of the design page, for one batch:
+ *   L_k = H^(L) W_lm^T + markov_w1[x_{A+k}] markov_w2^T   draft logits (row 5n+k of H^(L))
+ *   T_k = z_{A+k} W_lm^T                                 teacher logits (same frozen lm_head)
+ *   c_k = w_conf . [H^(L) row ; markov_w1[x_{A+k}]]      confidence logit
+ *   ce  = -log softmax(L_k)[x_{A+k+1}]
+ *   l1  = || softmax(L_k) - softmax(T_k) ||_1,   a = clip(1 - l1/2, 0, 1)
+ *   bce = BCE-with-logits(c_k, a)
+ * per step k = 0..4 of every block, and the loss
+ *   alpha_ce mean(ce) + alpha_l1 mean(l1) + alpha_conf mean(bce)
+ * with the means over the steps the eval mask keeps (§6 "eval_mask": step k
+ * counts when A+k+1 < S, loss_mask[A+k+1] = 1 (loss_mask[S-1] read as 0) and
+ * keep = 1, with a prefix cumprod along the block); 0 when no step counts.
+ * Readings: the Markov head is a bigram bias -- step k's predecessor token
+ * x_{A+k} (the anchor at k = 0, the gold token after) is embedded by
+ * markov_w1 as a lookup table and mapped back by markov_w2; H^(L) is the
+ * draft's final hidden state after its last RMSNorm. */
+typedef struct dspark_loss_desc {
+    int32_t B, S, N;          /* batch, sequence length, anchor blocks per sample */
+    int32_t vocab;            /* V (154880 for GLM-5.2), >= 1 */
+    int32_t hidden;           /* d (6144), >= 1 */
+    int32_t markov_rank;      /* r (256), >= 1 */
+    int32_t dtype;            /* dspark_dtype of H^(L), z and the weights */
+    int32_t max_kept_blocks;  /* 0: B*N.  Otherwise an upper bound on the kept
+                                 blocks of the batch: the logits are formed for
+                                 5 * max_kept_blocks rows instead of 5 * B * N */
+    double alpha_ce, alpha_l1, alpha_conf;   /* 1, 0.9, 1 in the page's recipe */
+} dspark_loss_desc;
+
+/* Bytes of workspace dspark_loss_fwd needs (0 on an invalid descriptor):
+ * a status area, the compacted block list, the gathered rows, the draft and
+ * teacher logits in fp32 ([5 * rows, V] each: 6.3 GB for 5120 rows of
+ * V = 154880) and per-chunk softmax statistics.  256-byte aligned. */
+size_t dspark_loss_workspace_size(const dspark_loss_desc* desc);
+
+/* The output head and loss.  Device pointers:
+ *   input_ids  [B, S] int32 in [0, V)     x (token ids of the Target prefill)
+ *   loss_mask  [B, S] uint8               (loss_mask[S-1] is read as 0)
+ *   anchors, keep  [B, N]                 as in dspark_attn_fwd
+ *   h_final    [B, 5N, d]                 H^(L)
+ *   z          [B, S, d]                  the Target's last hidden states
+ *   w_lm       [V, d]                     frozen lm_head
+ *   w_m1, w_m2 [V, r]                     markov_w1 (lookup), markov_w2
+ *   w_conf     [d + r]                    confidence head (H^(L) part first)
+ *   terms      [4, B, N, 5] fp32 out      planes ce, l1, c (confidence
+ *                                         logit), bce; 0 where the eval mask is 0
+ *   eval_mask  [B, N, 5] uint8 out
+ *   loss       [5] fp32 out               total, mean ce, mean l1, mean bce,
+ *                                         number of counted steps
+ * A kept block whose anchor lies outside [0, S-2] is an error detected on
+ * the device: its terms are NaN, the loss is NaN and
+ * dspark_loss_read_status reports DSPARK_EANCHOR.  More kept blocks than
+ * max_kept_blocks: every term and the loss are NaN and the status is
+ * DSPARK_ECAPACITY.  The logits are fp32 (rocBLAS GEMMs with fp32
+ * accumulation, no atomics: the same call gives the same bits);
+ * softmax statistics, L1 and the sums are fp32, the final means fp64.
+ * Uses the library's rocBLAS handle (see dspark_mla_layer_fwd). */
+dspark_status dspark_loss_fwd(const dspark_loss_desc* desc, const int32_t* input_ids,
+                              const uint8_t* loss_mask, const int32_t* anchors,
+                              const uint8_t* keep, const void* h_final, const void* z,
+                              const void* w_lm, const void* w_m1, const void* w_m2,
+                              const void* w_conf, float* terms, uint8_t* eval_mask, float* loss,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* dspark_loss_fwd with options (opts may be NULL): stage_events (at least 6)
+ * are recorded on `stream` before the first launch and after each stage:
+ * the block index and row gather, the logits GEMMs, the softmax statistics,
+ * the L1 pass, the per-step terms and the loss.  The other fields are
+ * ignored. */
+dspark_status dspark_loss_fwd_ex(const dspark_loss_desc* desc, const int32_t* input_ids,
+                                 const uint8_t* loss_mask, const int32_t* anchors,
+                                 const uint8_t* keep, const void* h_final, const void* z,
+                                 const void* w_lm, const void* w_m1, const void* w_m2,
+                                 const void* w_conf, float* terms, uint8_t* eval_mask,
+                                 float* loss, void* workspace, size_t ws_bytes, void* stream,
+                                 const dspark_attn_opts* opts);
+
+/* dspark_loss_fwd, once, while choosing the GEMM kernels for its shapes (as
+ * dspark_mla_layer_tune does; synchronises `stream`, takes seconds). */
+dspark_status dspark_loss_tune(const dspark_loss_desc* desc, const int32_t* input_ids,
+                               const uint8_t* loss_mask, const int32_t* anchors,
+                               const uint8_t* keep, const void* h_final, const void* z,
+                               const void* w_lm, const void* w_m1, const void* w_m2,
+                               const void* w_conf, float* terms, uint8_t* eval_mask, float* loss,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+/* Synchronises `stream`, then reads the status area of a workspace used by
+ * the last dspark_loss_fwd on it: DSPARK_OK, DSPARK_EANCHOR (first_bad_block
+ * = b*N + n of the first kept block with a bad anchor) or DSPARK_ECAPACITY.
+ * kept_blocks receives the number of kept blocks.  Either pointer may be
+ * NULL. */
+dspark_status dspark_loss_read_status(const void* workspace, void* stream,
+                                      int32_t* first_bad_block, int32_t* kept_blocks);
 
 /* Synchronises `stream`, then reads the status area of a workspace used by
  * the last dspark_attn_fwd / dspark_attn_bwd / dspark_build_index on it.  Returns DSPARK_OK, or

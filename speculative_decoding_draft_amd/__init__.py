@@ -1,5 +1,5 @@
-"""MI355X (gfx950) DSpark draft attention (forward, backward) and the MLA block
-of a draft layer around it.
+"""MI355X (gfx950) DSpark draft attention (forward, backward), the MLA block
+of a draft layer around it, and the draft's output head and loss.
 
 The compute lives in libdspark_attn.so (hand-written HIP kernels behind the C
 ABI of include/dspark_attn.h); this package is its Python binding.  Build the
@@ -8,6 +8,7 @@ library with ``python speculative_decoding_draft_amd/build.py``.
 from ._lib import (  # noqa: F401
     DSPARK_BF16,
     DSPARK_EANCHOR,
+    DSPARK_ECAPACITY,
     DSPARK_EHIP,
     DSPARK_EINVAL,
     DSPARK_EUNSUPPORTED,
@@ -32,6 +33,13 @@ from ._lib import (  # noqa: F401
     layer_workspace_size,
     mla_layer_fwd,
     mla_layer_tune,
+    LossDesc,
+    LOSS_INPUTS,
+    make_loss_desc,
+    loss_workspace_size,
+    loss_fwd,
+    loss_tune,
+    loss_read_status,
     build_index,
     last_error,
     make_desc,

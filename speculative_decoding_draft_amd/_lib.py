@@ -24,15 +24,19 @@ DSPARK_EUNSUPPORTED = -2
 DSPARK_EWORKSPACE = -3
 DSPARK_EHIP = -4
 DSPARK_EANCHOR = -5
+DSPARK_ECAPACITY = -6
 STATUS_NAMES = {0: "DSPARK_OK", -1: "DSPARK_EINVAL", -2: "DSPARK_EUNSUPPORTED",
-                -3: "DSPARK_EWORKSPACE", -4: "DSPARK_EHIP", -5: "DSPARK_EANCHOR"}
+                -3: "DSPARK_EWORKSPACE", -4: "DSPARK_EHIP", -5: "DSPARK_EANCHOR",
+                -6: "DSPARK_ECAPACITY"}
 DSPARK_F32 = 0
 DSPARK_BF16 = 1
 
 EXPORTS = ("dspark_attn_workspace_size", "dspark_attn_fwd", "dspark_attn_fwd_ex", "dspark_attn_plan",
            "dspark_attn_bwd_workspace_size", "dspark_attn_bwd", "dspark_attn_bwd_ex",
            "dspark_attn_bwd_plan", "dspark_mla_layer_workspace_size", "dspark_mla_layer_fwd",
-           "dspark_mla_layer_fwd_ex", "dspark_mla_layer_tune", "dspark_build_index",
+           "dspark_mla_layer_fwd_ex", "dspark_mla_layer_tune", "dspark_loss_workspace_size",
+           "dspark_loss_fwd", "dspark_loss_fwd_ex", "dspark_loss_tune", "dspark_loss_read_status",
+           "dspark_build_index",
            "dspark_select_anchors_host",
            "dspark_read_device_status", "dspark_last_error", "dspark_abi_version")
 
@@ -55,6 +59,14 @@ class Desc(ctypes.Structure):
 class LayerDesc(ctypes.Structure):
     _fields_ = [("attn", Desc), ("hidden", ctypes.c_int32), ("q_rank", ctypes.c_int32),
                 ("rms_eps", ctypes.c_double)]
+
+
+class LossDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("S", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("markov_rank", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("max_kept_blocks", ctypes.c_int32), ("alpha_ce", ctypes.c_double),
+                ("alpha_l1", ctypes.c_double), ("alpha_conf", ctypes.c_double)]
 
 
 class Opts(ctypes.Structure):
@@ -103,6 +115,18 @@ def _load():
     lib.dspark_mla_layer_fwd_ex.restype = i32
     lib.dspark_mla_layer_tune.argtypes = layer_args
     lib.dspark_mla_layer_tune.restype = i32
+    plo = ctypes.POINTER(LossDesc)
+    lib.dspark_loss_workspace_size.argtypes = [plo]
+    lib.dspark_loss_workspace_size.restype = sz
+    loss_args = [plo] + [vp] * 10 + [vp, vp, vp, vp, sz, vp]
+    lib.dspark_loss_fwd.argtypes = loss_args
+    lib.dspark_loss_fwd.restype = i32
+    lib.dspark_loss_fwd_ex.argtypes = loss_args + [ctypes.POINTER(Opts)]
+    lib.dspark_loss_fwd_ex.restype = i32
+    lib.dspark_loss_tune.argtypes = loss_args
+    lib.dspark_loss_tune.restype = i32
+    lib.dspark_loss_read_status.argtypes = [vp, vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.dspark_loss_read_status.restype = i32
     lib.dspark_build_index.argtypes = [pd, vp, vp, vp, vp, sz, vp]
     lib.dspark_build_index.restype = i32
     lib.dspark_select_anchors_host.argtypes = [vp, i32, i32, u64, vp, vp]
@@ -319,6 +343,57 @@ def mla_layer_tune(desc: LayerDesc, h_draft, h_ctx, weights, anchors, keep, out,
     ws_bytes = workspace.numel() * workspace.element_size()
     args += [_ptr(anchors), _ptr(keep), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)]
     _check(lib.dspark_mla_layer_tune(*args))
+
+
+def make_loss_desc(B: int, S: int, N: int, vocab: int, hidden: int, markov_rank: int,
+                   dtype: str = "bf16", max_kept_blocks: int = 0, alpha_ce: float = 1.0,
+                   alpha_l1: float = 0.9, alpha_conf: float = 1.0) -> LossDesc:
+    dt = {"bf16": DSPARK_BF16, "f32": DSPARK_F32}[dtype]
+    return LossDesc(int(B), int(S), int(N), int(vocab), int(hidden), int(markov_rank), dt,
+                    int(max_kept_blocks), float(alpha_ce), float(alpha_l1), float(alpha_conf))
+
+
+def loss_workspace_size(desc: LossDesc) -> int:
+    n = int(lib.dspark_loss_workspace_size(ctypes.byref(desc)))
+    if n == 0:
+        raise DSparkError(DSPARK_EINVAL, last_error())
+    return n
+
+
+LOSS_INPUTS = ("input_ids", "loss_mask", "anchors", "keep", "h_final", "z", "w_lm", "w_m1", "w_m2",
+               "w_conf")
+
+
+def _loss_args(desc, t, terms, eval_mask, loss, workspace, stream):
+    args = [ctypes.byref(desc)] + [_ptr(t[k]) for k in LOSS_INPUTS]
+    ws_bytes = workspace.numel() * workspace.element_size()
+    return args + [_ptr(terms), _ptr(eval_mask), _ptr(loss), _ptr(workspace), ws_bytes,
+                   _stream(stream)]
+
+
+def loss_fwd(desc: LossDesc, tensors, terms, eval_mask, loss, workspace, stream=None,
+             stage_events: Optional[Sequence[int]] = None) -> None:
+    """dspark_loss_fwd / _ex; tensors: a mapping named as in LOSS_INPUTS;
+    terms [4, B, N, 5] fp32, eval_mask [B, N, 5] uint8, loss [5] fp32."""
+    args = _loss_args(desc, tensors, terms, eval_mask, loss, workspace, stream)
+    if stage_events is None:
+        _check(lib.dspark_loss_fwd(*args))
+        return
+    opts, _arr = _opts(stage_events, False, 0)
+    _check(lib.dspark_loss_fwd_ex(*args, ctypes.byref(opts)))
+
+
+def loss_tune(desc: LossDesc, tensors, terms, eval_mask, loss, workspace, stream=None) -> None:
+    """dspark_loss_tune: one loss call that also picks its GEMM kernels."""
+    _check(lib.dspark_loss_tune(*_loss_args(desc, tensors, terms, eval_mask, loss, workspace, stream)))
+
+
+def loss_read_status(workspace, stream=None):
+    """Synchronises the stream; returns (status, first_bad_block, kept_blocks)."""
+    fb, kb = ctypes.c_int32(-1), ctypes.c_int32(0)
+    st = lib.dspark_loss_read_status(_ptr(workspace), _stream(stream), ctypes.byref(fb),
+                                     ctypes.byref(kb))
+    return int(st), int(fb.value), int(kb.value)
 
 
 def build_index(desc: Desc, anchors, keep, index_out, workspace, stream=None) -> None:

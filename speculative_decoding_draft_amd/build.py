@@ -34,7 +34,8 @@ COMMON_FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 SOURCES = ["prep.hip", "generic.hip", "absorb.hip", "attn.hip", "uv.hip", "api.hip",
-           "sampler.cpp", "bwd_misc.hip", "bwd_gemm.hip", "bwd_attn.hip", "layer.hip"]
+           "sampler.cpp", "bwd_misc.hip", "bwd_gemm.hip", "bwd_attn.hip", "layer.hip",
+           "blas.hip", "loss.hip"]
 
 
 def _hipcc() -> str:

@@ -12,16 +12,10 @@
 // here; q^R and k^R go to the attention unrotated (it rotates them while
 // loading).  RMSNorm is x / sqrt(mean(x^2) + eps) * g; the page names the
 // op without a formula or epsilon, so eps is a descriptor field.
-#define ROCBLAS_BETA_FEATURES_API   // rocblas_gemm_ex_get_solutions (kernel choice)
-#include <rocblas/rocblas.h>
-
 #include <cstdio>
 #include <cstring>
-#include <map>
-#include <mutex>
-#include <tuple>
-#include <vector>
 
+#include "blas.hpp"
 #include "kernels.hpp"
 
 namespace dspark {
@@ -167,101 +161,6 @@ __global__ __launch_bounds__(256) void split_heads_kernel(const T* __restrict__ 
     }
 }
 
-// ---- rocBLAS: one handle per (thread, device), created on first use and
-// kept for the life of the process (the only allocation the library makes).
-thread_local rocblas_handle t_handles[64] = {};
-
-rocblas_status get_handle(rocblas_handle* h) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return rocblas_status_invalid_handle;
-    if (!t_handles[dev]) {
-        const rocblas_status st = rocblas_create_handle(&t_handles[dev]);
-        if (st != rocblas_status_success) return st;
-        // no atomics: the same call gives the same bits
-        rocblas_set_atomics_mode(t_handles[dev], rocblas_atomics_not_allowed);
-    }
-    *h = t_handles[dev];
-    return rocblas_status_success;
-}
-
-// rocBLAS kernel choices per (device, shape), recorded by
-// dspark_mla_layer_tune: the solution index that ran fastest, or 0 for
-// rocBLAS's own choice.  Shared by all threads.
-using GemmKey = std::tuple<int, int, int, int, int, int, int, int, int>;
-std::mutex g_choice_mu;
-std::map<GemmKey, int> g_choice;
-
-// Row-major D[M][N] = A[M][K] B[N][K]^T + beta C[M][N] (leading dims in
-// elements; C = nullptr: D's own pattern, read only if beta != 0).  In
-// rocBLAS's column-major terms this is D^T = op_T(B^T) A^T, so B goes first.
-// tune: time every solution rocBLAS offers for the shape (and its default)
-// on the handle's stream, synchronising it, record the fastest, then run it.
-// C must not alias D when tuning (every trial rewrites D).
-rocblas_status gemm_nt(rocblas_handle h, bool bf16_io, int M, int N, int K, const void* A, int lda,
-                       const void* B, int ldb, float beta, const void* C, int ldc, void* D, int ldd,
-                       bool tune) {
-    const float alpha = 1.f;
-    const rocblas_datatype t = bf16_io ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-    const void* Cp = C ? C : D;
-    const int ldcp = C ? ldc : ldd;
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    const GemmKey key{dev, M, N, K, lda, ldb, ldd, bf16_io ? 1 : 0, beta != 0.f ? 1 : 0};
-    auto run = [&](int sol) {
-        return rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, N, M, K,
-                               &alpha, B, t, ldb, A, t, lda, &beta, Cp, t, ldcp, D, t, ldd,
-                               rocblas_datatype_f32_r,
-                               sol > 0 ? rocblas_gemm_algo_solution_index
-                                       : rocblas_gemm_algo_standard,
-                               sol > 0 ? sol : 0, 0);
-    };
-    if (tune) {
-        rocblas_int n = 0;
-        rocblas_status st = rocblas_gemm_ex_get_solutions(
-            h, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &alpha, B, t, ldb, A,
-            t, lda, &beta, Cp, t, ldcp, D, t, ldd, rocblas_datatype_f32_r,
-            rocblas_gemm_algo_solution_index, 0, nullptr, &n);
-        std::vector<rocblas_int> sols(n > 0 ? n : 0);
-        if (st == rocblas_status_success && n > 0)
-            st = rocblas_gemm_ex_get_solutions(
-                h, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &alpha, B, t, ldb, A,
-                t, lda, &beta, Cp, t, ldcp, D, t, ldd, rocblas_datatype_f32_r,
-                rocblas_gemm_algo_solution_index, 0, sols.data(), &n);
-        sols.insert(sols.begin(), 0);              // rocBLAS's default
-        hipStream_t s = nullptr;
-        rocblas_get_stream(h, &s);
-        hipEvent_t e0 = nullptr, e1 = nullptr;
-        if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
-            return rocblas_status_internal_error;
-        int best = 0;
-        float best_ms = 1e30f;
-        for (int sol : sols) {
-            if (run(sol) != rocblas_status_success) continue;      // warm-up; skips invalid ones
-            (void)hipEventRecord(e0, s);
-            bool ok = true;
-            for (int i = 0; i < 3 && ok; ++i) ok = run(sol) == rocblas_status_success;
-            (void)hipEventRecord(e1, s);
-            (void)hipEventSynchronize(e1);
-            float ms = 0.f;
-            if (ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess && ms < best_ms) {
-                best_ms = ms;
-                best = sol;
-            }
-        }
-        (void)hipEventDestroy(e0);
-        (void)hipEventDestroy(e1);
-        std::lock_guard<std::mutex> g(g_choice_mu);
-        g_choice[key] = best;
-    }
-    int sol = 0;
-    {
-        std::lock_guard<std::mutex> g(g_choice_mu);
-        const auto it = g_choice.find(key);
-        if (it != g_choice.end()) sol = it->second;
-    }
-    return run(sol);
-}
-
 }  // namespace
 
 // Workspace of dspark_mla_layer_fwd: the block's intermediates, then the
@@ -377,12 +276,11 @@ dspark_status layer_fwd(const dspark_layer_desc* desc, const void* h_draft, cons
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     rocblas_handle h;
-    rocblas_status bs = get_handle(&h);
-    if (bs != rocblas_status_success) return lfail(DSPARK_EHIP, "rocblas_create_handle failed", bs);
-    if ((bs = rocblas_set_stream(h, s)) != rocblas_status_success)
-        return lfail(DSPARK_EHIP, "rocblas_set_stream failed", bs);
+    rocblas_status bs = blas_handle(s, &h);
+    if (bs != rocblas_status_success) return lfail(DSPARK_EHIP, "rocBLAS handle set-up failed", bs);
 
     const bool bf = d.dtype == DSPARK_BF16;
+    const rocblas_datatype tio = bf ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
     const size_t e = bf ? 2 : 4;
     char* base = static_cast<char*>(workspace);
     void *hn = base + L.hn, *cq = base + L.cq, *qn = base + L.qn, *qr = base + L.qr;
@@ -422,7 +320,7 @@ dspark_status layer_fwd(const dspark_layer_desc* desc, const void* h_draft, cons
     LSTEP_HIP(norm(h_draft, hid, g_in, hn, hid, nullptr, 0, q_rows, hid), "input RMSNorm launch");
     LMARK();
     // c^Q = RMSNorm(h W_qa^T)
-    LSTEP_BLAS(gemm_nt(h, bf, q_rows, qk, hid, hn, hid, w_qa, hid, 0.f, nullptr, 0, cq, qk, tune),
+    LSTEP_BLAS(gemm_nt(h, tio, tio, q_rows, qk, hid, hn, hid, w_qa, hid, 0.f, nullptr, 0, cq, qk, tune),
                "q_a_proj GEMM");
     LSTEP_HIP(norm(cq, qk, g_qa, cq, qk, nullptr, 0, q_rows, qk), "q_a RMSNorm launch");
     LMARK();
@@ -430,7 +328,7 @@ dspark_status layer_fwd(const dspark_layer_desc* desc, const void* h_draft, cons
     // of 192 and 64 columns ran at half the rate), then split into the
     // attention's [row][head][dim] layouts
     void* qf = base + L.qf;
-    LSTEP_BLAS(gemm_nt(h, bf, q_rows, H * (dc + dr), qk, cq, qk, w_qb, qk, 0.f, nullptr, 0, qf,
+    LSTEP_BLAS(gemm_nt(h, tio, tio, q_rows, H * (dc + dr), qk, cq, qk, w_qb, qk, 0.f, nullptr, 0, qf,
                        H * (dc + dr), tune), "q_b_proj GEMM");
     {
         const int vec = (dc % 8 == 0 && dr % 8 == 0 && bf) ? 8 : ((dc % 4 == 0 && dr % 4 == 0 && !bf) ? 4 : 1);
@@ -448,9 +346,9 @@ dspark_status layer_fwd(const dspark_layer_desc* desc, const void* h_draft, cons
     }
     LMARK();
     // [c^KV ; k^R] = [H^ctx ; h] W_kva^T, then c^KV <- RMSNorm(c^KV) and the k^R split
-    LSTEP_BLAS(gemm_nt(h, bf, c_rows, D + dr, hid, h_ctx, hid, w_kva, hid, 0.f, nullptr, 0, kvc,
+    LSTEP_BLAS(gemm_nt(h, tio, tio, c_rows, D + dr, hid, h_ctx, hid, w_kva, hid, 0.f, nullptr, 0, kvc,
                        D + dr, tune), "kv_a_proj (context) GEMM");
-    LSTEP_BLAS(gemm_nt(h, bf, q_rows, D + dr, hid, hn, hid, w_kva, hid, 0.f, nullptr, 0, kvb, D + dr,
+    LSTEP_BLAS(gemm_nt(h, tio, tio, q_rows, D + dr, hid, hn, hid, w_kva, hid, 0.f, nullptr, 0, kvb, D + dr,
                        tune), "kv_a_proj (draft) GEMM");
     LSTEP_HIP(norm(kvc, D + dr, g_kva, ckv_c, D, kr_c, dr, c_rows, D), "kv_a RMSNorm launch");
     LSTEP_HIP(norm(kvb, D + dr, g_kva, ckv_b, D, kr_b, dr, q_rows, D), "kv_a RMSNorm launch");
@@ -466,7 +364,7 @@ dspark_status layer_fwd(const dspark_layer_desc* desc, const void* h_draft, cons
     if (ast != DSPARK_OK) return ast;            // dspark_last_error() says why
     LMARK();
     // out = H + o W_o^T
-    LSTEP_BLAS(gemm_nt(h, bf, q_rows, hid, H * dv, o, H * dv, w_o, H * dv, 1.f, h_draft, hid, out,
+    LSTEP_BLAS(gemm_nt(h, tio, tio, q_rows, hid, H * dv, o, H * dv, w_o, H * dv, 1.f, h_draft, hid, out,
                        hid, tune), "o_proj GEMM");
     LMARK();
 #undef LSTEP_HIP

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert set(sd.EXPORTS) == declared
-    assert sd.abi_version() == 4
+    assert sd.abi_version() == 5
 
 
 def glm_desc(**kw):
@@ -302,3 +302,51 @@ def test_layer_null_misaligned_and_workspace_errors_before_any_launch():
     assert call(good, 0x7000010, need) == sd.DSPARK_EWORKSPACE
     neg = sd.make_layer_desc(glm_desc(), hidden=6144, q_rank=2048, rms_eps=-1.0)
     assert lib.dspark_mla_layer_fwd(ctypes.byref(neg), *good, 0x7000000, need, None) == sd.DSPARK_EINVAL
+
+
+def test_loss_desc_layout_and_workspace():
+    assert ctypes.sizeof(sd.LossDesc) == 8 * 4 + 3 * 8
+    d = sd.make_loss_desc(B=1, S=32768, N=1024, vocab=154880, hidden=6144, markov_rank=256)
+    need = sd.loss_workspace_size(d)
+    rows = 5 * 1024
+    logits = 2 * rows * 154880 * 4
+    gathered = rows * (6144 + 256) * 2 + rows * 6144 * 2
+    stats = rows * 19 * (16 + 4)
+    assert logits + gathered + stats <= need < logits + gathered + stats + 2**20
+    # max_kept_blocks shrinks every row-sized buffer
+    d2 = sd.make_loss_desc(B=1, S=32768, N=1024, vocab=154880, hidden=6144, markov_rank=256,
+                           max_kept_blocks=768)
+    assert abs(sd.loss_workspace_size(d2) - need * 768 / 1024) < 2**20
+    for kw in (dict(vocab=0), dict(hidden=0), dict(markov_rank=0), dict(max_kept_blocks=-1),
+               dict(S=0)):
+        args = dict(B=1, S=64, N=4, vocab=100, hidden=8, markov_rank=4)
+        args.update(kw)
+        bad = sd.make_loss_desc(**args)
+        assert sd._lib.lib.dspark_loss_workspace_size(ctypes.byref(bad)) == 0
+
+
+def test_loss_null_misaligned_and_workspace_errors_before_any_launch():
+    d = sd.make_loss_desc(B=1, S=64, N=4, vocab=100, hidden=8, markov_rank=8)
+    need = sd.loss_workspace_size(d)
+    good = [0x10000 * (i + 1) for i in range(13)]
+    lib = sd._lib.lib
+    call = lambda p, ws, n: lib.dspark_loss_fwd(ctypes.byref(d), *p, ws, n, None)
+    for i in range(13):
+        p = list(good)
+        p[i] = None
+        assert call(p, 0x7000000, need) == sd.DSPARK_EINVAL and "NULL" in sd.last_error()
+    for i in (4, 5, 6, 7, 8, 9):           # the dense tensors need 16-byte alignment
+        p = list(good)
+        p[i] += 4
+        assert call(p, 0x7000000, need) == sd.DSPARK_EINVAL and "aligned" in sd.last_error()
+    p = list(good)
+    p[0] += 2                              # input_ids: int32
+    assert call(p, 0x7000000, need) == sd.DSPARK_EINVAL
+    assert call(good, 0x7000000, need - 1) == sd.DSPARK_EWORKSPACE
+    assert call(good, 0x7000010, need) == sd.DSPARK_EWORKSPACE
+    ev = (ctypes.c_void_p * 5)(*[0x100] * 5)
+    opts = sd._lib.Opts()
+    opts.stage_events = ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p))
+    opts.n_stage_events = 5
+    assert lib.dspark_loss_fwd_ex(ctypes.byref(d), *good, 0x7000000, need, None,
+                                  ctypes.byref(opts)) == sd.DSPARK_EINVAL

@@ -174,6 +174,9 @@ def _recipe_headline(rng, S, N, W, pad_frac=0.25, low_frac=0.05):
     n_pad = int(round(pad_frac * N))
     n_low = int(round(low_frac * N))
     n_hi = N - n_pad - n_low
+    if n_low > W - 1 or n_hi > S - W - 1:
+        raise ValueError(f"headline recipe: {n_low} clamped anchors need W - 1 >= {n_low} and "
+                         f"{n_hi} others need S - W - 1 >= {n_hi} distinct positions")
     low = {0, 1, W - 2} if n_low >= 3 else set()
     while len(low) < n_low:
         low.add(int(rng.integers(0, W - 1)))

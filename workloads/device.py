@@ -28,3 +28,16 @@ def upload_anchors(anchors: np.ndarray, keep: np.ndarray, device="cuda"):
     a = torch.from_numpy(np.ascontiguousarray(anchors, dtype=np.int32)).to(device)
     k = torch.from_numpy(np.ascontiguousarray(keep, dtype=np.uint8)).to(device)
     return a, k
+
+
+def upload_loss(lh, loss_mask: np.ndarray, anchors: np.ndarray, keep: np.ndarray,
+                device="cuda") -> dict:
+    """The loss head's inputs as device tensors, keyed as the binding's
+    LOSS_INPUTS."""
+    import torch
+    t = {k: to_torch(getattr(lh, k), lh.dtype, device)
+         for k in ("h_final", "z", "w_lm", "w_m1", "w_m2", "w_conf")}
+    t["input_ids"] = torch.from_numpy(np.ascontiguousarray(lh.input_ids, dtype=np.int32)).to(device)
+    t["loss_mask"] = torch.from_numpy(np.ascontiguousarray(loss_mask, dtype=np.uint8)).to(device)
+    t["anchors"], t["keep"] = upload_anchors(anchors, keep, device)
+    return t
