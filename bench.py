@@ -24,7 +24,10 @@ inputs with a seeded upstream gradient (--bwd-steps timed calls), its useful
 TFLOP/s (gradient products only; see bwd_useful_flop) and per-launch times.
 A "layer" object times dspark_mla_layer_fwd (the MLA block of one draft
 layer: RMSNorms, projections, the attention, o_proj) on seeded hidden states
-and weights of the page's shapes.  The headline metric is the forward's.
+and weights of the page's shapes.  A "loss" object times dspark_loss_fwd (the
+output head and loss: lm_head for the draft and the teacher, Markov bias,
+confidence head, CE / L1 / BCE means) at V = 154880, d = 6144, r = 256 on the
+same anchors.  The headline metric is the forward's.
 """
 from __future__ import annotations
 
@@ -332,6 +335,84 @@ def bench_layer(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sptr,
                          "algorithmic_flop_per_launch": st_flop[dom]}}
 
 
+LOSS_STAGES = ("index_gather", "gemms", "stats", "l1", "terms_reduce")
+
+
+def loss_flop(wl, keep, vocab, hidden, rank):
+    """FLOP of the output head on the rows of kept blocks: the lm_head for the
+    draft and the teacher rows and the Markov bias.  Returns (total, {stage: flop})."""
+    rows = 5 * int(keep.sum())
+    st = {"lm_head_draft": 2 * rows * hidden * vocab, "lm_head_teacher": 2 * rows * hidden * vocab,
+          "markov": 2 * rows * rank * vocab}
+    return sum(st.values()), st
+
+
+def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hidden=6144, rank=256):
+    """Times dspark_loss_fwd on seeded inputs of the page's shapes (V = 154880,
+    d = 6144, markov rank 256) with the workload's anchors, keep mask and loss
+    mask; max_kept_blocks is the number of kept blocks."""
+    import workloads as wk
+    from workloads.device import upload_loss
+    lh = wk.make_loss_inputs(wl, vocab, hidden, rank, seed=9)
+    t = upload_loss(lh, wl.loss_mask, anchors, keep)
+    del lh
+    kept = int(keep.sum())
+    d = sd.make_loss_desc(wl.B, wl.S, wl.N, vocab, hidden, rank, dtype=wl.dtype,
+                          max_kept_blocks=kept)
+    ws = torch.empty(sd.loss_workspace_size(d), dtype=torch.uint8, device="cuda")
+    terms = torch.empty((4, wl.B, wl.N, 5), dtype=torch.float32, device="cuda")
+    em = torch.empty((wl.B, wl.N, 5), dtype=torch.uint8, device="cuda")
+    loss = torch.empty(5, dtype=torch.float32, device="cuda")
+    args = (d, t, terms, em, loss, ws)
+    t_tune = time.perf_counter()
+    sd.loss_tune(*args, stream=sptr)
+    torch.cuda.synchronize()
+    t_tune = time.perf_counter() - t_tune
+    st = sd.loss_read_status(ws, stream=sptr)
+    if st[0] != 0:
+        raise RuntimeError(f"loss status {st}")
+    w0, n_w = time.perf_counter(), 0
+    while n_w < 2 or (time.perf_counter() - w0) < 0.1:
+        sd.loss_fwd(*args, stream=sptr)
+        n_w += 1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sd.loss_fwd(*args, stream=sptr)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ev = hip.create(len(LOSS_STAGES) + 1)
+    sd.loss_fwd(*args, stream=sptr, stage_events=ev)
+    torch.cuda.synchronize()
+    stage_us = {s: hip.elapsed_ms(ev[i], ev[i + 1]) * 1e3 for i, s in enumerate(LOSS_STAGES)}
+    hip.destroy(ev)
+    flop, st_flop = loss_flop(wl, keep, vocab, hidden, rank)
+    vals = loss.cpu().tolist()
+    gemm_tfs = flop / (stage_us["gemms"] * 1e-6) / 1e12
+    # the statistics pass reads the draft and teacher logits of the counted rows once
+    live = int(em.sum().item())
+    stat_bytes = 2 * live * vocab * 4
+    stat_gbs = stat_bytes / (stage_us["stats"] * 1e-6) / 1e9
+    return {"ms_per_step": round(wall * 1e3, 4), "steps": steps, "warmup": n_w,
+            "vocab": vocab, "hidden": hidden, "markov_rank": rank, "kept_blocks": kept,
+            "counted_steps": live, "gemm_tuning_s": round(t_tune, 2),
+            "useful_gflop_per_step": round(flop / 1e9, 3),
+            "value": round(flop / wall / 1e12, 3), "unit": "TFLOP/s",
+            "frac_of_bf16_peak": round(flop / wall / 1e12 / MI355X_BF16_PEAK_TFLOPS, 4),
+            "loss": {"total": vals[0], "ce": vals[1], "l1": vals[2], "bce": vals[3]},
+            "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
+            "roofline": {"kernel": "logits GEMMs (rocBLAS: Markov, draft and teacher lm_head)",
+                         "bound": "mfma", "achieved": round(gemm_tfs, 1),
+                         "peak": MI355X_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(gemm_tfs / MI355X_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "avg_launch_us": round(stage_us["gemms"], 2),
+                         "algorithmic_flop_per_launch": flop},
+            "stats_pass": {"bound": "hbm", "achieved": round(stat_gbs, 1),
+                           "peak": MI355X_HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(stat_gbs / MI355X_HBM_PEAK_GBS, 4),
+                           "algorithmic_bytes_per_launch": stat_bytes}}
+
+
 class HipEvents:
     """hipEvent_t handles from the HIP runtime torch loaded (one runtime per
     process), so that they can be recorded by the library on torch's stream."""
@@ -417,6 +498,9 @@ def main():
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the MLA block measurement (the 'layer' object)")
     ap.add_argument("--layer-steps", type=int, default=10)
+    ap.add_argument("--no-loss", action="store_true",
+                    help="skip the output head and loss measurement (the 'loss' object)")
+    ap.add_argument("--loss-steps", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (the reference "
@@ -586,6 +670,11 @@ def main():
                                           desc, sptr, hip, args.layer_steps)
         except Exception as e:   # the forward line is still reported
             result["layer"] = {"error": f"{type(e).__name__}: {e}"}
+    if not args.no_loss and wl.dtype == "bf16":
+        try:
+            result["loss"] = bench_loss(sd, torch, wl, anchors, keep, sptr, hip, args.loss_steps)
+        except Exception as e:   # the forward line is still reported
+            result["loss"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, anchors, keep, args.cpu_budget)
     print(json.dumps(result), flush=True)
