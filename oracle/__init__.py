@@ -42,4 +42,10 @@ from .dspark_oracle import (  # noqa: F401
     confidence_logit,
     step_terms,
     loss_head,
+    ring_slot,
+    decode_attention,
+    softmax_t,
+    acceptance,
+    sample_inverse_cdf,
+    spec_verify,
 )

@@ -696,3 +696,112 @@ def loss_head(lh, loss_mask, anchors, keep, alphas=None, blocks=None):
     out["mean_ce"], out["mean_l1"], out["mean_bce"] = means["ce"], means["l1"], means["bce"]
     out["total"] = al["ce"] * means["ce"] + al["l1"] * means["l1"] + al["conf"] * means["bce"]
     return out
+
+
+# ---------------------------------------------------------------------------
+# inference-time drafting: the windowed draft KV cache (parameter summary,
+# "KV cache": a draft layer keeps about W cached tokens, 576 numbers each)
+# and draft-then-verify with rejection sampling (the MTP / DSA explainer
+# page's "Rejection Sampling" passage: acceptance sum_v min(p_v, q_v))
+# ---------------------------------------------------------------------------
+
+def ring_slot(pos, slots: int):
+    """Slot of logical position pos in a draft cache of `slots` entries: the
+    cache keeps the most recent positions, position p in slot p mod slots."""
+    return np.asarray(pos) % slots
+
+
+def decode_attention(cache_ckv, cache_kr, anchors, active, q_nope, q_rope, ckv_blk, kr_blk,
+                     w_uk, w_uv, W: int, rope_base: float, dtype: str, scale=None):
+    """The draft's attention for one block per sequence at decode time (fp64):
+    the block [x_A, MASK x 4] sits at positions A..A+4 and sees, as in §3, the
+    context positions [max(0, A-W+1), A) -- read from the ring cache at slot
+    p mod C -- and its own 5 positions bidirectionally.  Keys, values and
+    queries as in §4 "MLA Projection" and "RoPE", with the true positions.
+    cache_ckv [B, C, D], cache_kr [B, C, d_r]; anchors [B]; active [B]
+    (inactive sequences give NaN rows); q_nope [B, 5, H, d_c], q_rope
+    [B, 5, H, d_r] (not rotated); ckv_blk [B, 5, D], kr_blk [B, 5, d_r].
+    Returns [B, 5, H, d_v]."""
+    f = lambda a: _f64(a, dtype)
+    cc, ck, qn, qr = f(cache_ckv), f(cache_kr), f(q_nope), f(q_rope)
+    cb, kb, wk, wv = f(ckv_blk), f(kr_blk), f(w_uk), f(w_uv)
+    B, C = cc.shape[0], cc.shape[1]
+    H, dc, dr, dv = qn.shape[2], qn.shape[3], qr.shape[3], wv.shape[1]
+    scale = softmax_scale(dc, dr) if scale is None else float(scale)
+    out = np.full((B, BLOCK, H, dv), np.nan)
+    for b in range(B):
+        if not active[b]:
+            continue
+        A = int(anchors[b])
+        ctx = np.arange(max(0, A - W + 1), A)
+        blk = A + np.arange(BLOCK)
+        slots = ring_slot(ctx, C)
+        ckv = np.concatenate([cc[b][slots], cb[b]], axis=0)
+        kr = rope_interleaved(np.concatenate([ck[b][slots], kb[b]], axis=0),
+                              np.concatenate([ctx, blk]), rope_base)
+        qrot = rope_interleaved(qr[b].transpose(1, 0, 2), blk, rope_base)     # [H, 5, d_r]
+        for h in range(H):
+            K, V = expand_head(ckv, kr, wk, wv, h)
+            Q = np.concatenate([qn[b][:, h, :], qrot[h]], axis=1)
+            out[b, :, h, :] = _softmax_rows(scale * (Q @ K.T)) @ V
+    return out
+
+
+def softmax_t(logits, temperature: float = 1.0) -> np.ndarray:
+    """softmax(logits / T) over the last axis."""
+    return _softmax_rows(np.asarray(logits, np.float64) / float(temperature))
+
+
+def acceptance(p, q) -> np.ndarray:
+    """The explainer page's acceptance rate: sum_v min(p_v, q_v) (for the
+    draft distribution q and the target distribution p)."""
+    return np.minimum(np.asarray(p, np.float64), np.asarray(q, np.float64)).sum(axis=-1)
+
+
+def sample_inverse_cdf(weights, u: float) -> int:
+    """Draw from the distribution proportional to the non-negative `weights`
+    with the uniform u in [0, 1): the first index whose cumulative weight
+    exceeds u times the total."""
+    w = np.asarray(weights, np.float64)
+    c = np.cumsum(w)
+    return int(np.argmax(c > u * c[-1]))
+
+
+def spec_verify(draft_logits, target_logits, draft_tokens, u, mode: str = "rejection",
+                temperature: float = 1.0):
+    """Verification of K drafted tokens of one sequence (fp64).
+
+    draft_logits [K, V] give q_k, target_logits [K + 1, V] give p_k
+    (p_k scores the token after the k-th drafted position; p_K is the
+    target's distribution after the last one); draft_tokens [K]; u [K + 1]
+    uniforms in [0, 1).  Both distributions are softmax(logits / T).
+    "rejection" (rejection sampling): token k is accepted when
+    u_k < a_k = min(1, p_k(x_k) / q_k(x_k)); at the first rejection j the next
+    token is drawn from the residual max(0, p_j - q_j) (normalised) with u_K;
+    when all K are accepted it is drawn from p_K with u_K.  "target_only":
+    token k is accepted when it is the target's top choice (the lowest index
+    among ties); the next token is p_j's (or p_K's) top choice.
+    Returns dict(n_accept, next_token, accept_prob [K] (a_k for every k),
+    overlap [K] = sum_v min(p_k, q_k))."""
+    q = softmax_t(draft_logits, temperature)
+    p = softmax_t(target_logits, temperature)
+    K = q.shape[0]
+    x = np.asarray(draft_tokens)
+    with np.errstate(divide="ignore", over="ignore"):
+        a = np.minimum(1.0, np.exp(np.log(p[np.arange(K), x]) - np.log(q[np.arange(K), x])))
+    res = dict(accept_prob=a, overlap=acceptance(p[:K], q))
+    j = K
+    for k in range(K):
+        ok = (u[k] < a[k]) if mode == "rejection" else (int(x[k]) == int(np.argmax(p[k])))
+        if not ok:
+            j = k
+            break
+    if mode == "rejection":
+        w = np.maximum(0.0, p[j] - q[j]) if j < K else p[K]
+        nxt = sample_inverse_cdf(w, float(u[K]))
+    elif mode == "target_only":
+        nxt = int(np.argmax(p[j]))
+    else:
+        raise ValueError(mode)
+    res["n_accept"], res["next_token"] = j, nxt
+    return res
