@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 5
+#define DSPARK_ABI_VERSION 6
 
 typedef enum dspark_status {
     DSPARK_OK = 0,
@@ -440,6 +440,97 @@ dspark_status dspark_loss_tune(const dspark_loss_desc* desc, const int32_t* inpu
  * NULL. */
 dspark_status dspark_loss_read_status(const void* workspace, void* stream,
                                       int32_t* first_bad_block, int32_t* kept_blocks);
+
+/* ---- inference-time drafting -------------------------------------------
+ * The draft's KV cache (parameter summary, "KV cache"): at inference a draft
+ * layer keeps about W cached tokens, c^KV (D numbers) and k^R (d_r numbers)
+ * each.  Here each layer and sequence owns a ring of C slots,
+ * cache_ckv [B, C, D] and cache_kr [B, C, d_r] (k^R not rotated); position
+ * p lives in slot p mod C, so C >= window - 1 keeps every context position
+ * a block can see. */
+typedef struct dspark_decode_desc {
+    dspark_attn_desc attn;   /* B sequences, N = 1, block 5, window, dims,
+                                rope_base, softmax_scale, dtype; S is ignored */
+    int32_t cache_slots;     /* C >= window - 1 */
+} dspark_decode_desc;
+
+/* Writes new context rows into the rings: row t < n_new[b] of
+ * new_ckv [B, max_new, D] / new_kr [B, max_new, d_r] is position
+ * pos0[b] + t (slot (pos0[b] + t) mod C).  When n_new[b] > C only its last C
+ * rows are written (the earlier ones would be overwritten); rows at negative
+ * positions are skipped.  pos0 and n_new are device arrays [B]. */
+dspark_status dspark_cache_append(const dspark_decode_desc* desc, const int32_t* pos0,
+                                  const int32_t* n_new, int32_t max_new, const void* new_ckv,
+                                  const void* new_kr, void* cache_ckv, void* cache_kr,
+                                  void* stream);
+
+/* Bytes of workspace dspark_decode_attn needs (0 on an invalid descriptor):
+ * the attention's workspace for B blocks (its status area first, so that
+ * dspark_read_device_status works on this workspace) and each sequence's
+ * window gathered from its ring.  256-byte aligned. */
+size_t dspark_decode_workspace_size(const dspark_decode_desc* desc);
+
+/* The draft attention for one block per sequence at decode time: the block
+ * [x_A, MASK x 4] at positions A..A+4 (anchors [B], A >= 0) attends to the
+ * context positions [max(0, A-W+1), A) held in the ring and to its own 5
+ * positions, as dspark_attn_fwd does for a training block (§3, §4).
+ *   q_nope [B, 5, H, d_c], q_rope [B, 5, H, d_r] (not rotated)
+ *   ckv_blk [B, 5, D], kr_blk [B, 5, d_r]   the block's own latents
+ *   w_uk, w_uv                              as in dspark_attn_fwd
+ *   active [B] uint8                        0: the sequence's rows are 0
+ *   out [B, 5, H, d_v]
+ * The window is gathered into a short contiguous context and the training
+ * attention runs on it with every position moved by the same offset
+ * (A - min(A, W-1)); RoPE scores depend only on differences of positions,
+ * so the result is the same.  A negative anchor on an active sequence is
+ * reported by dspark_read_device_status (DSPARK_EANCHOR) with NaN rows. */
+dspark_status dspark_decode_attn(const dspark_decode_desc* desc, const void* q_nope,
+                                 const void* q_rope, const void* cache_ckv, const void* cache_kr,
+                                 const void* ckv_blk, const void* kr_blk, const void* w_uk,
+                                 const void* w_uv, const int32_t* anchors, const uint8_t* active,
+                                 void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Verification of drafted tokens (the MTP / DSA explainer page,
+ * "Rejection Sampling"; acceptance sum_v min(p_v, q_v)). */
+typedef enum dspark_verify_mode {
+    DSPARK_VERIFY_REJECTION = 0,   /* accept x_k when u_k < min(1, p_k(x_k) / q_k(x_k)) */
+    DSPARK_VERIFY_TARGET_ONLY = 1  /* accept x_k when it is p_k's top choice */
+} dspark_verify_mode;
+
+typedef struct dspark_verify_desc {
+    int32_t B;            /* sequences */
+    int32_t K;            /* drafted tokens per sequence (5 for a DSpark block), >= 1 */
+    int32_t vocab;        /* V >= 1 */
+    int32_t mode;         /* a dspark_verify_mode */
+    double temperature;   /* > 0: p = softmax(target / T), q = softmax(draft / T) */
+} dspark_verify_desc;
+
+/* Bytes of workspace dspark_spec_verify needs (0 on an invalid descriptor). */
+size_t dspark_verify_workspace_size(const dspark_verify_desc* desc);
+
+/* Verifies K drafted tokens per sequence.  Device pointers:
+ *   draft_logits  [B, K, V] fp32      q_k
+ *   target_logits [B, K+1, V] fp32    p_k (p_k scores the token after the
+ *                                     k-th drafted position; p_K follows the last)
+ *   draft_tokens  [B, K] int32        x_k in [0, V)
+ *   uniforms      [B, K+1] fp32       u in [0, 1): u_k decides x_k, u_K draws
+ *                                     the next token
+ *   accept_prob   [B, K] fp32 out     a_k = min(1, p_k(x_k) / q_k(x_k))
+ *   overlap       [B, K] fp32 out     sum_v min(p_k, q_k)
+ *   n_accept      [B] int32 out       j = accepted drafted tokens (first rejection)
+ *   next_token    [B] int32 out       rejection mode: drawn from the residual
+ *                                     max(0, p_j - q_j) (from p_j if that is 0)
+ *                                     when j < K, from p_K when j = K -- the
+ *                                     first index whose cumulative weight
+ *                                     exceeds u_K times the total; target-only
+ *                                     mode: p_j's top choice (lowest index on ties)
+ * A drafted token outside [0, V) makes that sequence's n_accept and
+ * next_token -1.  Sums in fp32; no atomics. */
+dspark_status dspark_spec_verify(const dspark_verify_desc* desc, const float* draft_logits,
+                                 const float* target_logits, const int32_t* draft_tokens,
+                                 const float* uniforms, float* accept_prob, float* overlap,
+                                 int32_t* n_accept, int32_t* next_token, void* workspace,
+                                 size_t ws_bytes, void* stream);
 
 /* Synchronises `stream`, then reads the status area of a workspace used by
  * the last dspark_attn_fwd / dspark_attn_bwd / dspark_build_index on it.  Returns DSPARK_OK, or

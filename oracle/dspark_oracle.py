@@ -798,6 +798,8 @@ def spec_verify(draft_logits, target_logits, draft_tokens, u, mode: str = "rejec
             break
     if mode == "rejection":
         w = np.maximum(0.0, p[j] - q[j]) if j < K else p[K]
+        if w.sum() == 0.0:          # p_j = q_j: the residual is empty; draw from p_j
+            w = p[j]
         nxt = sample_inverse_cdf(w, float(u[K]))
     elif mode == "target_only":
         nxt = int(np.argmax(p[j]))

@@ -36,6 +36,8 @@ EXPORTS = ("dspark_attn_workspace_size", "dspark_attn_fwd", "dspark_attn_fwd_ex"
            "dspark_attn_bwd_plan", "dspark_mla_layer_workspace_size", "dspark_mla_layer_fwd",
            "dspark_mla_layer_fwd_ex", "dspark_mla_layer_tune", "dspark_loss_workspace_size",
            "dspark_loss_fwd", "dspark_loss_fwd_ex", "dspark_loss_tune", "dspark_loss_read_status",
+           "dspark_cache_append", "dspark_decode_workspace_size", "dspark_decode_attn",
+           "dspark_verify_workspace_size", "dspark_spec_verify",
            "dspark_build_index",
            "dspark_select_anchors_host",
            "dspark_read_device_status", "dspark_last_error", "dspark_abi_version")
@@ -67,6 +69,15 @@ class LossDesc(ctypes.Structure):
                 ("markov_rank", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("max_kept_blocks", ctypes.c_int32), ("alpha_ce", ctypes.c_double),
                 ("alpha_l1", ctypes.c_double), ("alpha_conf", ctypes.c_double)]
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [("attn", Desc), ("cache_slots", ctypes.c_int32)]
+
+
+class VerifyDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("K", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("mode", ctypes.c_int32), ("temperature", ctypes.c_double)]
 
 
 class Opts(ctypes.Structure):
@@ -127,6 +138,18 @@ def _load():
     lib.dspark_loss_tune.restype = i32
     lib.dspark_loss_read_status.argtypes = [vp, vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.dspark_loss_read_status.restype = i32
+    pdd = ctypes.POINTER(DecodeDesc)
+    lib.dspark_cache_append.argtypes = [pdd, vp, vp, i32, vp, vp, vp, vp, vp]
+    lib.dspark_cache_append.restype = i32
+    lib.dspark_decode_workspace_size.argtypes = [pdd]
+    lib.dspark_decode_workspace_size.restype = sz
+    lib.dspark_decode_attn.argtypes = [pdd] + [vp] * 11 + [vp, sz, vp]
+    lib.dspark_decode_attn.restype = i32
+    pvd = ctypes.POINTER(VerifyDesc)
+    lib.dspark_verify_workspace_size.argtypes = [pvd]
+    lib.dspark_verify_workspace_size.restype = sz
+    lib.dspark_spec_verify.argtypes = [pvd] + [vp] * 8 + [vp, sz, vp]
+    lib.dspark_spec_verify.restype = i32
     lib.dspark_build_index.argtypes = [pd, vp, vp, vp, vp, sz, vp]
     lib.dspark_build_index.restype = i32
     lib.dspark_select_anchors_host.argtypes = [vp, i32, i32, u64, vp, vp]
@@ -394,6 +417,58 @@ def loss_read_status(workspace, stream=None):
     st = lib.dspark_loss_read_status(_ptr(workspace), _stream(stream), ctypes.byref(fb),
                                      ctypes.byref(kb))
     return int(st), int(fb.value), int(kb.value)
+
+
+def make_decode_desc(attn: Desc, cache_slots: int) -> DecodeDesc:
+    return DecodeDesc(attn, int(cache_slots))
+
+
+def cache_append(desc: DecodeDesc, pos0, n_new, new_ckv, new_kr, cache_ckv, cache_kr,
+                 stream=None) -> None:
+    """dspark_cache_append; new_ckv [B, max_new, D] fixes max_new."""
+    _check(lib.dspark_cache_append(ctypes.byref(desc), _ptr(pos0), _ptr(n_new),
+                                   int(new_ckv.shape[1]), _ptr(new_ckv), _ptr(new_kr),
+                                   _ptr(cache_ckv), _ptr(cache_kr), _stream(stream)))
+
+
+def decode_workspace_size(desc: DecodeDesc) -> int:
+    n = int(lib.dspark_decode_workspace_size(ctypes.byref(desc)))
+    if n == 0:
+        raise DSparkError(DSPARK_EINVAL, last_error())
+    return n
+
+
+def decode_attn(desc: DecodeDesc, q_nope, q_rope, cache_ckv, cache_kr, ckv_blk, kr_blk, w_uk, w_uv,
+                anchors, active, out, workspace, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.dspark_decode_attn(ctypes.byref(desc), _ptr(q_nope), _ptr(q_rope), _ptr(cache_ckv),
+                                  _ptr(cache_kr), _ptr(ckv_blk), _ptr(kr_blk), _ptr(w_uk),
+                                  _ptr(w_uv), _ptr(anchors), _ptr(active), _ptr(out),
+                                  _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+VERIFY_MODES = {"rejection": 0, "target_only": 1}
+
+
+def make_verify_desc(B: int, K: int, vocab: int, mode: str = "rejection",
+                     temperature: float = 1.0) -> VerifyDesc:
+    return VerifyDesc(int(B), int(K), int(vocab), VERIFY_MODES[mode], float(temperature))
+
+
+def verify_workspace_size(desc: VerifyDesc) -> int:
+    n = int(lib.dspark_verify_workspace_size(ctypes.byref(desc)))
+    if n == 0:
+        raise DSparkError(DSPARK_EINVAL, last_error())
+    return n
+
+
+def spec_verify(desc: VerifyDesc, draft_logits, target_logits, draft_tokens, uniforms, accept_prob,
+                overlap, n_accept, next_token, workspace, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.dspark_spec_verify(ctypes.byref(desc), _ptr(draft_logits), _ptr(target_logits),
+                                  _ptr(draft_tokens), _ptr(uniforms), _ptr(accept_prob),
+                                  _ptr(overlap), _ptr(n_accept), _ptr(next_token), _ptr(workspace),
+                                  ws_bytes, _stream(stream)))
 
 
 def build_index(desc: Desc, anchors, keep, index_out, workspace, stream=None) -> None:

@@ -35,7 +35,7 @@ COMMON_FLAGS = [
 ]
 SOURCES = ["prep.hip", "generic.hip", "absorb.hip", "attn.hip", "uv.hip", "api.hip",
            "sampler.cpp", "bwd_misc.hip", "bwd_gemm.hip", "bwd_attn.hip", "layer.hip",
-           "blas.hip", "loss.hip"]
+           "blas.hip", "loss.hip", "decode.hip"]
 
 
 def _hipcc() -> str:

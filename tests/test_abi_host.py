@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert set(sd.EXPORTS) == declared
-    assert sd.abi_version() == 5
+    assert sd.abi_version() == 6
 
 
 def glm_desc(**kw):
@@ -350,3 +350,42 @@ def test_loss_null_misaligned_and_workspace_errors_before_any_launch():
     opts.n_stage_events = 5
     assert lib.dspark_loss_fwd_ex(ctypes.byref(d), *good, 0x7000000, need, None,
                                   ctypes.byref(opts)) == sd.DSPARK_EINVAL
+
+
+def test_decode_and_verify_validation_before_any_launch():
+    lib = sd._lib.lib
+    attn = glm_desc(B=4, S=0, N=1)
+    d = sd.make_decode_desc(attn, 128)
+    need = sd.decode_workspace_size(d)
+    # the attention's workspace for 4 one-block problems of S' = W + 1 rows
+    # comes first, then the gathered windows
+    assert need >= sd.workspace_size(glm_desc(B=4, S=129, N=1)) + 4 * 129 * 576 * 2
+    for bad in (sd.make_decode_desc(glm_desc(B=4, N=2), 128), sd.make_decode_desc(attn, 126)):
+        assert lib.dspark_decode_workspace_size(ctypes.byref(bad)) == 0
+    good = [0x10000 * (i + 1) for i in range(11)]
+    call = lambda p, ws, n: lib.dspark_decode_attn(ctypes.byref(d), *p, ws, n, None)
+    for i in (2, 3, 8, 9):                 # cache_ckv, cache_kr, anchors, active
+        p = list(good)
+        p[i] = None
+        assert call(p, 0x7000000, need) == sd.DSPARK_EINVAL
+    assert call(good, 0x7000000, need - 1) == sd.DSPARK_EWORKSPACE
+    assert lib.dspark_cache_append(ctypes.byref(d), None, 0x1000, 3, 0x2000, 0x3000, 0x4000,
+                                   0x5000, None) == sd.DSPARK_EINVAL
+    assert lib.dspark_cache_append(ctypes.byref(d), 0x1000, 0x1000, -1, 0x2000, 0x3000, 0x4000,
+                                   0x5000, None) == sd.DSPARK_EINVAL
+    v = sd.make_verify_desc(B=8, K=5, vocab=154880)
+    need = sd.verify_workspace_size(v)
+    assert need >= 8 * 11 * 19 * 16 + 8 * 5 * 19 * 8
+    for bad in (sd.make_verify_desc(8, 0, 100), sd.make_verify_desc(8, 65, 100),
+                sd.make_verify_desc(8, 5, 0), sd.make_verify_desc(8, 5, 100, temperature=0.0)):
+        assert lib.dspark_verify_workspace_size(ctypes.byref(bad)) == 0
+    badmode = sd.make_verify_desc(8, 5, 100)
+    badmode.mode = 7
+    assert lib.dspark_verify_workspace_size(ctypes.byref(badmode)) == 0
+    ptrs = [0x10000 * (i + 1) for i in range(8)]
+    vcall = lambda p, ws, n: lib.dspark_spec_verify(ctypes.byref(v), *p, ws, n, None)
+    for i in range(8):
+        p = list(ptrs)
+        p[i] = None
+        assert vcall(p, 0x7000000, need) == sd.DSPARK_EINVAL
+    assert vcall(ptrs, 0x7000000, need - 1) == sd.DSPARK_EWORKSPACE

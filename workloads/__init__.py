@@ -378,3 +378,53 @@ def make_loss_inputs(wl: Workload, vocab: int, hidden: int, rank: int = 256, see
         w_m2=_normal(rng, (vocab, rank), float(markov_std / np.sqrt(rank)), dt),
         w_conf=_normal(rng, (hidden + rank,), float(1 / np.sqrt(hidden + rank)), dt),
     )
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    """One decode step's attention inputs for B sequences (one draft block
+    each) and the most recent context rows of each sequence, to be written
+    into the draft cache: ctx_ckv / ctx_kr [B, n_ctx, .] hold positions
+    A - n_ctx .. A - 1 (rows at negative positions are unused)."""
+    q_nope: np.ndarray    # [B, 5, H, d_c]
+    q_rope: np.ndarray    # [B, 5, H, d_r]
+    ckv_blk: np.ndarray   # [B, 5, D]
+    kr_blk: np.ndarray    # [B, 5, d_r]
+    w_uk: np.ndarray      # [H, d_c, D]
+    w_uv: np.ndarray      # [H, d_v, D]
+    ctx_ckv: np.ndarray   # [B, n_ctx, D]
+    ctx_kr: np.ndarray    # [B, n_ctx, d_r]
+
+
+def make_decode_inputs(B: int, dims: dict, dtype: str, n_ctx: int, seed: int = 13) -> DecodeInputs:
+    """Activations N(0, 1), weights N(0, 1/D), as for a training layer."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, B, n_ctx])))
+    H, D, d_c, d_r, d_v = (dims[k] for k in ("H", "D", "d_c", "d_r", "d_v"))
+    wstd = float(1.0 / np.sqrt(D))
+    return DecodeInputs(
+        q_nope=_normal(rng, (B, BLOCK, H, d_c), 1.0, dtype),
+        q_rope=_normal(rng, (B, BLOCK, H, d_r), 1.0, dtype),
+        ckv_blk=_normal(rng, (B, BLOCK, D), 1.0, dtype),
+        kr_blk=_normal(rng, (B, BLOCK, d_r), 1.0, dtype),
+        w_uk=_normal(rng, (H, d_c, D), wstd, dtype),
+        w_uv=_normal(rng, (H, d_v, D), wstd, dtype),
+        ctx_ckv=_normal(rng, (B, n_ctx, D), 1.0, dtype),
+        ctx_kr=_normal(rng, (B, n_ctx, d_r), 1.0, dtype),
+    )
+
+
+def make_verify_inputs(B: int, K: int, vocab: int, seed: int = 17, logit_std: float = 2.0,
+                       noise_std: float = 0.7):
+    """Draft logits [B, K, V] N(0, logit_std^2); target logits [B, K+1, V]:
+    the draft's plus N(0, noise_std^2) for the first K rows (distributions
+    that overlap partly), N(0, logit_std^2) for the last; uniforms [B, K+1]
+    and [B, K] (the second set for drawing the drafted tokens) in [0, 1).
+    All fp32."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, B, K, vocab])))
+    dl = rng.standard_normal((B, K, vocab), dtype=np.float32) * np.float32(logit_std)
+    tl = np.empty((B, K + 1, vocab), dtype=np.float32)
+    tl[:, :K] = dl + rng.standard_normal((B, K, vocab), dtype=np.float32) * np.float32(noise_std)
+    tl[:, K] = rng.standard_normal((B, vocab), dtype=np.float32) * np.float32(logit_std)
+    u = rng.random((B, K + 1), dtype=np.float32)
+    u_draft = rng.random((B, K), dtype=np.float32)
+    return dl, tl, u, u_draft
