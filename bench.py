@@ -27,7 +27,11 @@ layer: RMSNorms, projections, the attention, o_proj) on seeded hidden states
 and weights of the page's shapes.  A "loss" object times dspark_loss_fwd (the
 output head and loss: lm_head for the draft and the teacher, Markov bias,
 confidence head, CE / L1 / BCE means) at V = 154880, d = 6144, r = 256 on the
-same anchors.  The headline metric is the forward's.
+same anchors.  A "decode" object times one inference-time drafting step for
+64 sequences: appending 5 accepted positions to each draft cache ring,
+the decode attention over the rings, and the rejection-sampling
+verification of 5 drafted tokens at V = 154880.  The headline metric is the
+forward's.
 """
 from __future__ import annotations
 
@@ -413,6 +417,81 @@ def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hid
                            "algorithmic_bytes_per_launch": stat_bytes}}
 
 
+def bench_decode(sd, torch, hip, steps, B=64, K=5, vocab=154880, C=128):
+    """One decode step for B sequences at GLM dims (W = 128, a ring of C
+    slots per sequence): dspark_cache_append of 5 rows, dspark_decode_attn,
+    and dspark_spec_verify (rejection sampling, K drafted tokens).  Anchors
+    are drawn uniformly from [W, 10^6); inputs are seeded."""
+    import workloads as wk
+    from workloads.device import to_torch
+    dims = wk.GLM_DIMS
+    W = dims["W"]
+    rng = np.random.default_rng(31)
+    anchors = rng.integers(W, 10**6, size=B).astype(np.int32)
+    di = wk.make_decode_inputs(B, dims, "bf16", 5, seed=31)
+    dev = lambda a: to_torch(a, "bf16", "cuda")
+    attn = sd.make_desc(B=B, S=0, N=1, window=W, n_heads=dims["H"], d_latent=dims["D"],
+                        d_nope=dims["d_c"], d_rope=dims["d_r"], d_v=dims["d_v"], dtype="bf16")
+    d = sd.make_decode_desc(attn, C)
+    cache_ckv = torch.randn((B, C, dims["D"]), device="cuda").to(torch.bfloat16)
+    cache_kr = torch.randn((B, C, dims["d_r"]), device="cuda").to(torch.bfloat16)
+    new_ckv, new_kr = dev(di.ctx_ckv), dev(di.ctx_kr)
+    pos0 = torch.tensor(anchors - 5, device="cuda")
+    n_new = torch.full((B,), 5, dtype=torch.int32, device="cuda")
+    a_dev = torch.tensor(anchors, device="cuda")
+    act = torch.ones(B, dtype=torch.uint8, device="cuda")
+    qn, qr, cb, kb = dev(di.q_nope), dev(di.q_rope), dev(di.ckv_blk), dev(di.kr_blk)
+    wuk, wuv = dev(di.w_uk), dev(di.w_uv)
+    out = torch.empty((B, 5, dims["H"], dims["d_v"]), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(sd.decode_workspace_size(d), dtype=torch.uint8, device="cuda")
+    dl, tl, u, _ = wk.make_verify_inputs(B, K, vocab, seed=37)
+    tok = torch.from_numpy(np.argmax(dl, axis=2).astype(np.int32)).to("cuda")
+    dl, tl, u = (torch.from_numpy(x).to("cuda") for x in (dl, tl, u))
+    vd = sd.make_verify_desc(B, K, vocab)
+    vws = torch.empty(sd.verify_workspace_size(vd), dtype=torch.uint8, device="cuda")
+    ap, ov = torch.empty((B, K), device="cuda"), torch.empty((B, K), device="cuda")
+    na = torch.empty(B, dtype=torch.int32, device="cuda")
+    nt = torch.empty(B, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sptr = int(stream.cuda_stream)
+
+    def append():
+        sd.cache_append(d, pos0, n_new, new_ckv, new_kr, cache_ckv, cache_kr, stream=sptr)
+
+    def attend():
+        sd.decode_attn(d, qn, qr, cache_ckv, cache_kr, cb, kb, wuk, wuv, a_dev, act, out, ws,
+                       stream=sptr)
+
+    def verify():
+        sd.spec_verify(vd, dl, tl, tok, u, ap, ov, na, nt, vws, stream=sptr)
+
+    res = {}
+    ev = hip.create(2)
+    for name, fn in (("append", append), ("attention", attend), ("verify", verify)):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        hip.record(ev[0], sptr)
+        for _ in range(steps):
+            fn()
+        hip.record(ev[1], sptr)
+        res[name] = hip.elapsed_ms(ev[0], ev[1]) * 1e3 / steps
+    hip.destroy(ev)
+    st, _ = sd.read_device_status(ws, stream=sptr)
+    if st != 0:
+        raise RuntimeError(f"decode status {st}")
+    vbytes = (4 * K + 1) * B * vocab * 4
+    vgbs = vbytes / (res["verify"] * 1e-6) / 1e9
+    return {"sequences": B, "drafted_tokens": K, "vocab": vocab, "cache_slots": C, "window": W,
+            "steps": steps, "us": {k: round(v, 2) for k, v in res.items()},
+            "us_per_step": round(sum(res.values()), 2),
+            "verify_roofline": {"bound": "hbm", "achieved": round(vgbs, 1),
+                                "peak": MI355X_HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(vgbs / MI355X_HBM_PEAK_GBS, 4),
+                                "algorithmic_bytes_per_launch": vbytes},
+            "mean_accepted": float(na.float().mean().item())}
+
+
 class HipEvents:
     """hipEvent_t handles from the HIP runtime torch loaded (one runtime per
     process), so that they can be recorded by the library on torch's stream."""
@@ -501,6 +580,9 @@ def main():
     ap.add_argument("--no-loss", action="store_true",
                     help="skip the output head and loss measurement (the 'loss' object)")
     ap.add_argument("--loss-steps", type=int, default=5)
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the inference-time drafting measurement (the 'decode' object)")
+    ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (the reference "
@@ -675,6 +757,11 @@ def main():
             result["loss"] = bench_loss(sd, torch, wl, anchors, keep, sptr, hip, args.loss_steps)
         except Exception as e:   # the forward line is still reported
             result["loss"] = {"error": f"{type(e).__name__}: {e}"}
+    if not args.no_decode and wl.dtype == "bf16":
+        try:
+            result["decode"] = bench_decode(sd, torch, hip, args.decode_steps)
+        except Exception as e:   # the forward line is still reported
+            result["decode"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, anchors, keep, args.cpu_budget)
     print(json.dumps(result), flush=True)

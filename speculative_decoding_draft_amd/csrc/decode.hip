@@ -169,8 +169,42 @@ __device__ inline const float* row_ptr(int r, int B, int K, int V, const float* 
     return r < nd ? dl + (size_t)r * V : tl + (size_t)(r - nd) * V;
 }
 
+// This thread's values of the chunk [v0, v1) of a row, times inv_t (-inf
+// outside the chunk), and their indices: 16-byte loads when VEC (V % 4 == 0),
+// value 4 (t + 256 i) + e; single loads otherwise, value t + 256 i.
+template <bool VEC>
+__device__ inline void load_vals(const float* __restrict__ x, int v0, int v1, float inv_t,
+                                 float* val) {
+    if (VEC) {
+#pragma unroll
+        for (int i = 0; i < kVPer / 4; ++i) {
+            const int v = v0 + 4 * (threadIdx.x + kVThreads * i);
+            if (v < v1) {
+                const float4 q = *reinterpret_cast<const float4*>(x + v);
+                val[4 * i] = q.x * inv_t; val[4 * i + 1] = q.y * inv_t;
+                val[4 * i + 2] = q.z * inv_t; val[4 * i + 3] = q.w * inv_t;
+            } else {
+                val[4 * i] = val[4 * i + 1] = val[4 * i + 2] = val[4 * i + 3] = -INFINITY;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kVPer; ++i) {
+            const int v = v0 + threadIdx.x + kVThreads * i;
+            val[i] = v < v1 ? x[v] * inv_t : -INFINITY;
+        }
+    }
+}
+
+template <bool VEC>
+__device__ inline int val_index(int v0, int i) {
+    return VEC ? v0 + 4 * ((int)threadIdx.x + kVThreads * (i / 4)) + (i % 4)
+               : v0 + (int)threadIdx.x + kVThreads * i;
+}
+
 // Per (row, chunk): {max of x/T, sum exp(x/T - max), index of the first
 // maximum, 0}.
+template <bool VEC>
 __global__ __launch_bounds__(kVThreads) void verify_stats_kernel(
     int B, int K, int V, int C, float inv_t, const float* __restrict__ dl,
     const float* __restrict__ tl, float4* __restrict__ part) {
@@ -180,50 +214,41 @@ __global__ __launch_bounds__(kVThreads) void verify_stats_kernel(
     const int r = blockIdx.x / C, c = blockIdx.x % C;
     const float* x = row_ptr(r, B, K, V, dl, tl);
     const int v0 = c * kVChunk, v1 = min(V, v0 + kVChunk);
-    float val[kVPer];
-    float m = -INFINITY;
-    int mi = INT_MAX;
-#pragma unroll
-    for (int i = 0; i < kVPer; ++i) {
-        const int v = v0 + threadIdx.x + kVThreads * i;
-        val[i] = v < v1 ? x[v] * inv_t : -INFINITY;
-        if (v < v1 && (val[i] > m || (val[i] == m && v < mi))) {
-            m = val[i];
-            mi = v;
-        }
-    }
-    // (max, first index) over the workgroup
-    for (int o = 32; o > 0; o >>= 1) {
-        const float om = __shfl_xor(m, o);
-        const int oi = __shfl_xor(mi, o);
-        if (om > m || (om == m && oi < mi)) {
-            m = om;
-            mi = oi;
-        }
-    }
     const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) {
-        red_m[w] = m;
-        red_i[w] = mi;
-    }
+    float val[kVPer];
+    load_vals<VEC>(x, v0, v1, inv_t, val);
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kVPer; ++i) m = fmaxf(m, val[i]);
+    m = vwave_max(m);
+    if ((threadIdx.x & 63) == 0) red_m[w] = m;
     __syncthreads();
     m = red_m[0];
-    mi = red_i[0];
-    for (int i = 1; i < kVThreads / 64; ++i)
-        if (red_m[i] > m || (red_m[i] == m && red_i[i] < mi)) {
-            m = red_m[i];
-            mi = red_i[i];
-        }
+#pragma unroll
+    for (int i = 1; i < kVThreads / 64; ++i) m = fmaxf(m, red_m[i]);
+    // first index of the maximum, and the sum of exponentials
+    int mi = INT_MAX;
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < kVPer; ++i) s += __expf(val[i] - m);
+    for (int i = 0; i < kVPer; ++i) {
+        if (val[i] == m) mi = min(mi, val_index<VEC>(v0, i));
+        s += __expf(val[i] - m);
+    }
+    for (int o = 32; o > 0; o >>= 1) mi = min(mi, __shfl_xor(mi, o));
     s = vwave_sum(s);
-    if ((threadIdx.x & 63) == 0) red_s[w] = s;
+    if ((threadIdx.x & 63) == 0) {
+        red_i[w] = mi;
+        red_s[w] = s;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
         float t = 0.f;
-        for (int i = 0; i < kVThreads / 64; ++i) t += red_s[i];
-        part[(size_t)r * C + c] = make_float4(m, t, __int_as_float(mi), 0.f);
+        int ti = INT_MAX;
+        for (int i = 0; i < kVThreads / 64; ++i) {
+            t += red_s[i];
+            ti = min(ti, red_i[i]);
+        }
+        part[(size_t)r * C + c] = make_float4(m, t, __int_as_float(ti), 0.f);
     }
 }
 
@@ -239,6 +264,7 @@ __device__ inline float chunk_lse(const float4* __restrict__ p, int C) {
 }
 
 // Per (drafted row, chunk): {sum min(p, q), sum max(0, p - q)}.
+template <bool VEC>
 __global__ __launch_bounds__(kVThreads) void verify_overlap_kernel(
     int B, int K, int V, int C, float inv_t, const float* __restrict__ dl,
     const float* __restrict__ tl, const float4* __restrict__ part, float2* __restrict__ ov) {
@@ -257,10 +283,14 @@ __global__ __launch_bounds__(kVThreads) void verify_overlap_kernel(
     const float* q = dl + (size_t)r * V;
     const float* p = tl + ((size_t)b * (K + 1) + k) * V;
     const int v0 = c * kVChunk, v1 = min(V, v0 + kVChunk);
+    float xq[kVPer], xp[kVPer];
+    load_vals<VEC>(q, v0, v1, inv_t, xq);
+    load_vals<VEC>(p, v0, v1, inv_t, xp);
     float mn = 0.f, res = 0.f;
-    for (int v = v0 + threadIdx.x; v < v1; v += kVThreads) {
-        const float qv = __expf(q[v] * inv_t - lse.x);
-        const float pv = __expf(p[v] * inv_t - lse.y);
+#pragma unroll
+    for (int i = 0; i < kVPer; ++i) {      // -inf padding: both terms 0
+        const float qv = __expf(xq[i] - lse.x);
+        const float pv = __expf(xp[i] - lse.y);
         mn += fminf(pv, qv);
         res += fmaxf(pv - qv, 0.f);
     }
@@ -279,7 +309,10 @@ __global__ __launch_bounds__(kVThreads) void verify_overlap_kernel(
     }
 }
 
-// One workgroup per sequence: decisions, outputs and the draw.
+// One workgroup per sequence: decisions, outputs and the draw.  The
+// sequence's chunk partials, drafted-token logits and uniforms are first
+// staged in LDS by the whole workgroup (dynamic LDS: (2K+1) C float4 +
+// K C float2), so that the sequential decisions read no global memory.
 constexpr int kMaxK = 64;
 __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(
     int B, int K, int V, int C, int mode, float inv_t, const float* __restrict__ dl,
@@ -287,107 +320,102 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(
     const float* __restrict__ uni, const float4* __restrict__ part,
     const float2* __restrict__ ov, float* __restrict__ accept_prob, float* __restrict__ overlap,
     int32_t* __restrict__ n_accept, int32_t* __restrict__ next_token) {
+    extern __shared__ float4 dyn[];
+    float4* sp = dyn;                                         // [(2K+1) C] partials
+    float2* so = reinterpret_cast<float2*>(dyn + (2 * K + 1) * C);   // [K C] overlap, residual
     __shared__ float lse_q[kMaxK], lse_p[kMaxK + 1];
+    __shared__ float xq_s[kMaxK], xp_s[kMaxK], u_s[kMaxK + 1];
+    __shared__ int tok_s[kMaxK];
     __shared__ int j_s, chunk_s;
     __shared__ float rem_s, lq_s, lp_s;
     __shared__ float wsum[kVThreads / 64];
     __shared__ int found_s, last_s, resid_s;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < (2 * K + 1) * C; i += kVThreads) {
+        const int k = i / C, c = i % C;
+        const size_t r = k < K ? (size_t)b * K + k : (size_t)B * K + (size_t)b * (K + 1) + (k - K);
+        sp[i] = part[r * C + c];
+    }
+    for (int i = tid; i < K * C; i += kVThreads) so[i] = ov[(size_t)b * K * C + i];
+    if (tid < K) {
+        const int x = tokens[(size_t)b * K + tid];
+        tok_s[tid] = x;
+        if (x >= 0 && x < V) {
+            xq_s[tid] = dl[((size_t)b * K + tid) * V + x] * inv_t;
+            xp_s[tid] = tl[((size_t)b * (K + 1) + tid) * V + x] * inv_t;
+        }
+    }
+    if (tid <= K) u_s[tid] = uni[(size_t)b * (K + 1) + tid];
+    __syncthreads();
     // log-sum-exps of the sequence's rows (wave w takes rows w, w + 4, ...)
     for (int k = w; k < 2 * K + 1; k += kVThreads / 64) {
-        const int r = k < K ? b * K + k : B * K + b * (K + 1) + (k - K);
-        const float l = chunk_lse(part + (size_t)r * C, C);
+        const float l = chunk_lse(sp + (size_t)k * C, C);
         if (lane == 0) {
             if (k < K) lse_q[k] = l;
             else lse_p[k - K] = l;
         }
     }
     __syncthreads();
+    // the target row k's first maximum, from the chunk partials
+    auto top = [&](int k) {
+        const float4* r = sp + (size_t)(K + k) * C;
+        float m = -INFINITY;
+        int mi = INT_MAX;
+        for (int c = 0; c < C; ++c) {
+            const int qi = __float_as_int(r[c].z);
+            if (r[c].x > m || (r[c].x == m && qi < mi)) {
+                m = r[c].x;
+                mi = qi;
+            }
+        }
+        return mi;
+    };
     if (tid == 0) {
         int bad = 0, j = K;
         for (int k = 0; k < K; ++k) {
-            const int x = tokens[(size_t)b * K + k];
+            const int x = tok_s[k];
             float a = 0.f, o = 0.f;
-            if (x < 0 || x >= V) {
-                bad = 1;
-            } else {
-                const float lq = dl[((size_t)b * K + k) * V + x] * inv_t - lse_q[k];
-                const float lp = tl[((size_t)b * (K + 1) + k) * V + x] * inv_t - lse_p[k];
-                a = fminf(1.f, __expf(lp - lq));
-            }
-            for (int c = 0; c < C; ++c) o += ov[((size_t)b * K + k) * C + c].x;
+            if (x < 0 || x >= V) bad = 1;
+            else a = fminf(1.f, __expf((xp_s[k] - lse_p[k]) - (xq_s[k] - lse_q[k])));
+            for (int c = 0; c < C; ++c) o += so[k * C + c].x;
             accept_prob[(size_t)b * K + k] = a;
             overlap[(size_t)b * K + k] = o;
             if (j == K && !bad) {
-                bool ok;
-                if (mode == DSPARK_VERIFY_REJECTION) {
-                    ok = uni[(size_t)b * (K + 1) + k] < a;
-                } else {     // target-only: the target row's first maximum
-                    const size_t r = (size_t)B * K + (size_t)b * (K + 1) + k;
-                    float m = -INFINITY;
-                    int mi = INT_MAX;
-                    for (int c = 0; c < C; ++c) {
-                        const float4 q4 = part[r * C + c];
-                        const int qi = __float_as_int(q4.z);
-                        if (q4.x > m || (q4.x == m && qi < mi)) {
-                            m = q4.x;
-                            mi = qi;
-                        }
-                    }
-                    ok = x == mi;
-                }
+                const bool ok = mode == DSPARK_VERIFY_REJECTION ? u_s[k] < a : x == top(k);
                 if (!ok) j = k;
             }
         }
         j_s = j;
         chunk_s = -1;
-        if (!bad && mode == DSPARK_VERIFY_TARGET_ONLY) {
-            const size_t r = (size_t)B * K + (size_t)b * (K + 1) + j;
-            float m = -INFINITY;
-            int mi = INT_MAX;
-            for (int c = 0; c < C; ++c) {
-                const float4 q4 = part[r * C + c];
-                const int qi = __float_as_int(q4.z);
-                if (q4.x > m || (q4.x == m && qi < mi)) {
-                    m = q4.x;
-                    mi = qi;
-                }
-            }
-            n_accept[b] = j;
-            next_token[b] = mi;
-        } else if (bad) {
+        if (bad) {
             n_accept[b] = -1;
             next_token[b] = -1;
+        } else if (mode == DSPARK_VERIFY_TARGET_ONLY) {
+            n_accept[b] = j;
+            next_token[b] = top(j);
         } else {
-            // the draw's distribution: residual of row j, or p_K; chunk masses
+            // the draw: the residual of row j, or p_j when it is empty, or p_K
             bool residual = j < K;
             float Z = 0.f;
             if (residual) {
-                for (int c = 0; c < C; ++c) Z += ov[((size_t)b * K + j) * C + c].y;
-                if (!(Z > 0.f)) residual = false;      // empty residual: draw from p_j
+                for (int c = 0; c < C; ++c) Z += so[j * C + c].y;
+                if (!(Z > 0.f)) residual = false;
             }
-            const int jp = j;                          // the target row of the draw
-            const size_t rt = (size_t)B * K + (size_t)b * (K + 1) + jp;
+            const float4* pr = sp + (size_t)(K + j) * C;       // target row j (j = K: p_K)
+            auto mass = [&](int c) {
+                return residual ? so[j * C + c].y : pr[c].y * __expf(pr[c].x - lse_p[j]);
+            };
             if (!residual) {
                 Z = 0.f;
-                for (int c = 0; c < C; ++c) {
-                    const float4 q4 = part[rt * C + c];
-                    Z += q4.y * __expf(q4.x - lse_p[jp]);
-                }
+                for (int c = 0; c < C; ++c) Z += mass(c);
             }
-            const float target = uni[(size_t)b * (K + 1) + K] * Z;
+            const float target = u_s[K] * Z;
             float cum = 0.f;
             int cs = -1, last_nz = -1;
             for (int c = 0; c < C; ++c) {
-                float mc;
-                if (residual) {
-                    mc = ov[((size_t)b * K + j) * C + c].y;
-                } else {
-                    const float4 q4 = part[rt * C + c];
-                    mc = q4.y * __expf(q4.x - lse_p[jp]);
-                }
+                const float mc = mass(c);
                 if (mc > 0.f) last_nz = c;
-                if (cs < 0 && cum + mc > target) {
+                if (cum + mc > target) {
                     cs = c;
                     break;
                 }
@@ -396,15 +424,12 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(
             if (cs < 0) {           // rounding: the total fell short of u*Z
                 cs = last_nz;
                 cum = 0.f;
-                for (int c = 0; c < cs; ++c) {
-                    cum += residual ? ov[((size_t)b * K + j) * C + c].y
-                                    : part[rt * C + c].y * __expf(part[rt * C + c].x - lse_p[jp]);
-                }
+                for (int c = 0; c < cs; ++c) cum += mass(c);
             }
             chunk_s = cs;
             rem_s = target - cum;
             lq_s = residual ? lse_q[j] : 0.f;
-            lp_s = lse_p[jp];
+            lp_s = lse_p[j];
             resid_s = residual ? 1 : 0;
             n_accept[b] = j;
         }
@@ -462,6 +487,9 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(
     if (tid == 0) next_token[b] = found_s != INT_MAX ? found_s : last_s;
 }
 
+size_t decide_lds_bytes(int K, int C) { return (size_t)(2 * K + 1) * C * 16 + (size_t)K * C * 8; }
+constexpr size_t kMaxDecideLds = 64 * 1024;
+
 struct VerifyLayout {
     size_t part = 0, ov = 0, total = 0;
     int chunks = 0;
@@ -476,6 +504,8 @@ const char* check_verify(const dspark_verify_desc* d) {
     if (!(d->temperature > 0.0) || !std::isfinite(d->temperature)) return "temperature must be > 0";
     const long long C = (d->vocab + kVChunk - 1) / kVChunk;
     if ((long long)d->B * (2 * d->K + 1) * C > INT_MAX) return "B * (2K + 1) * chunks too large";
+    if (decide_lds_bytes(d->K, (int)C) > kMaxDecideLds)
+        return "K x vocabulary chunks too large for the decision kernel's LDS ((3K+1) x ceil(V/8192) x 8 B <= 64 KB)";
     return nullptr;
 }
 
@@ -641,11 +671,19 @@ dspark_status dspark_spec_verify(const dspark_verify_desc* desc, const float* dr
     const int C = L.chunks;
     const float inv_t = (float)(1.0 / d.temperature);
     const int rows = d.B * (2 * d.K + 1);
-    hipLaunchKernelGGL(verify_stats_kernel, dim3(rows * C), dim3(kVThreads), 0, s, d.B, d.K, d.vocab,
-                       C, inv_t, draft_logits, target_logits, part);
-    hipLaunchKernelGGL(verify_overlap_kernel, dim3(d.B * d.K * C), dim3(kVThreads), 0, s, d.B, d.K,
-                       d.vocab, C, inv_t, draft_logits, target_logits, part, ov);
-    hipLaunchKernelGGL(verify_decide_kernel, dim3(d.B), dim3(kVThreads), 0, s, d.B, d.K, d.vocab, C,
+    if (d.vocab % 4 == 0 && al16(draft_logits) && al16(target_logits)) {
+        hipLaunchKernelGGL(verify_stats_kernel<true>, dim3(rows * C), dim3(kVThreads), 0, s, d.B,
+                           d.K, d.vocab, C, inv_t, draft_logits, target_logits, part);
+        hipLaunchKernelGGL(verify_overlap_kernel<true>, dim3(d.B * d.K * C), dim3(kVThreads), 0, s,
+                           d.B, d.K, d.vocab, C, inv_t, draft_logits, target_logits, part, ov);
+    } else {
+        hipLaunchKernelGGL(verify_stats_kernel<false>, dim3(rows * C), dim3(kVThreads), 0, s, d.B,
+                           d.K, d.vocab, C, inv_t, draft_logits, target_logits, part);
+        hipLaunchKernelGGL(verify_overlap_kernel<false>, dim3(d.B * d.K * C), dim3(kVThreads), 0,
+                           s, d.B, d.K, d.vocab, C, inv_t, draft_logits, target_logits, part, ov);
+    }
+    hipLaunchKernelGGL(verify_decide_kernel, dim3(d.B), dim3(kVThreads), decide_lds_bytes(d.K, C), s,
+                       d.B, d.K, d.vocab, C,
                        d.mode, inv_t, draft_logits, target_logits, draft_tokens, uniforms, part, ov,
                        accept_prob, overlap, n_accept, next_token);
     const hipError_t he = hipGetLastError();

@@ -281,7 +281,6 @@ dspark_status layer_fwd(const dspark_layer_desc* desc, const void* h_draft, cons
 
     const bool bf = d.dtype == DSPARK_BF16;
     const rocblas_datatype tio = bf ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-    const size_t e = bf ? 2 : 4;
     char* base = static_cast<char*>(workspace);
     void *hn = base + L.hn, *cq = base + L.cq, *qn = base + L.qn, *qr = base + L.qr;
     void *kvc = base + L.kvc, *kvb = base + L.kvb, *ckv_c = base + L.ckv_c, *kr_c = base + L.kr_c;
