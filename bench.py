@@ -299,7 +299,7 @@ def bench_layer(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sptr,
     hd = to_torch(li.h_draft, wl.dtype, "cuda")
     hc = to_torch(li.h_ctx, wl.dtype, "cuda")
     del li
-    ld = sd.make_layer_desc(desc, hidden, q_rank)
+    ld = sd.make_layer_desc(desc, hidden, q_rank, max_kept_blocks=int(keep.sum()))
     out = torch.empty_like(hd)
     ws = torch.empty(sd.layer_workspace_size(ld), dtype=torch.uint8, device="cuda")
     args = (ld, hd, hc, w, a_dev, k_dev, out, ws)

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 6
+#define DSPARK_ABI_VERSION 7
 
 typedef enum dspark_status {
     DSPARK_OK = 0,
@@ -284,11 +284,17 @@ typedef struct dspark_layer_desc {
     int32_t hidden;          /* d: 6144 for GLM-5.2 */
     int32_t q_rank;          /* q_lora_rank: 2048 */
     double rms_eps;          /* >= 0 */
+    int32_t max_kept_blocks; /* 0: B*N.  Otherwise an upper bound on the
+                                blocks with keep = 1: the draft-row
+                                projections and o_proj run on 5 * this many
+                                rows (the kept blocks' rows, compacted) */
 } dspark_layer_desc;
 
 /* Bytes of workspace dspark_mla_layer_fwd needs (0 on an invalid descriptor):
+ * a status area (first, as for the attention), the kept-block slot lists,
  * the block's intermediates (normalised h, c^Q, q^C, q^R, [c^KV ; k^R] of
- * every context and draft row, the attention output) and the attention's own
+ * every context and kept draft row, the attention output, the kept rows'
+ * attention output and H compacted, o_proj's result) and the attention's own
  * workspace.  256-byte aligned. */
 size_t dspark_mla_layer_workspace_size(const dspark_layer_desc* desc);
 
@@ -303,11 +309,15 @@ size_t dspark_mla_layer_workspace_size(const dspark_layer_desc* desc);
  *   anchors, keep        as in dspark_attn_fwd
  *   out [B, 5N, d]       H + o_proj(attention); rows of padding blocks are H
  *                        (their attention rows are 0), rows of a kept block
- *                        with a bad anchor are NaN
- * The projections run on rocBLAS (fp32 accumulation, no atomics: the same
- * call gives the same bits; dspark_mla_layer_tune picks the kernels).  The first call on a device and host thread
- * creates a rocBLAS handle that is kept until the process ends -- the one
- * allocation the library makes.  out must not alias any input. */
+ *                        with a bad anchor are NaN; every row is NaN when
+ *                        more than max_kept_blocks blocks are kept
+ *                        (dspark_mla_layer_read_status: DSPARK_ECAPACITY)
+ * The rows of kept blocks are compacted (5 per kept block, in (b, n) order)
+ * for the draft-row projections and o_proj.  The projections run on rocBLAS
+ * (fp32 accumulation, no atomics: the same call gives the same bits;
+ * dspark_mla_layer_tune picks the kernels).  The first call on a device and
+ * host thread creates a rocBLAS handle that is kept until the process ends
+ * -- the one allocation the library makes.  out must not alias any input. */
 dspark_status dspark_mla_layer_fwd(const dspark_layer_desc* desc,
                                    const void* h_draft, const void* h_ctx,
                                    const void* g_in, const void* w_qa, const void* g_qa,
@@ -346,6 +356,15 @@ dspark_status dspark_mla_layer_tune(const dspark_layer_desc* desc,
                                     const void* w_uk, const void* w_uv, const void* w_o,
                                     const int32_t* anchors, const uint8_t* keep,
                                     void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Synchronises `stream`, then reads the status area of a workspace used by
+ * the last dspark_mla_layer_fwd on it: DSPARK_OK, DSPARK_EANCHOR
+ * (first_bad_block = b*N + n of the first kept block with an anchor outside
+ * [0, S-2]) or DSPARK_ECAPACITY (more kept blocks than max_kept_blocks).
+ * kept_blocks receives the number of kept blocks.  Either pointer may be
+ * NULL. */
+dspark_status dspark_mla_layer_read_status(const void* workspace, void* stream,
+                                           int32_t* first_bad_block, int32_t* kept_blocks);
 
 /* ---- the output head and the loss ------------------------------------
  * §5 "输出头" and §6 "训练目标" of the design page, for one batch:

@@ -34,7 +34,7 @@ DSPARK_BF16 = 1
 EXPORTS = ("dspark_attn_workspace_size", "dspark_attn_fwd", "dspark_attn_fwd_ex", "dspark_attn_plan",
            "dspark_attn_bwd_workspace_size", "dspark_attn_bwd", "dspark_attn_bwd_ex",
            "dspark_attn_bwd_plan", "dspark_mla_layer_workspace_size", "dspark_mla_layer_fwd",
-           "dspark_mla_layer_fwd_ex", "dspark_mla_layer_tune", "dspark_loss_workspace_size",
+           "dspark_mla_layer_fwd_ex", "dspark_mla_layer_tune", "dspark_mla_layer_read_status", "dspark_loss_workspace_size",
            "dspark_loss_fwd", "dspark_loss_fwd_ex", "dspark_loss_tune", "dspark_loss_read_status",
            "dspark_cache_append", "dspark_decode_workspace_size", "dspark_decode_attn",
            "dspark_verify_workspace_size", "dspark_spec_verify",
@@ -60,7 +60,7 @@ class Desc(ctypes.Structure):
 
 class LayerDesc(ctypes.Structure):
     _fields_ = [("attn", Desc), ("hidden", ctypes.c_int32), ("q_rank", ctypes.c_int32),
-                ("rms_eps", ctypes.c_double)]
+                ("rms_eps", ctypes.c_double), ("max_kept_blocks", ctypes.c_int32)]
 
 
 class LossDesc(ctypes.Structure):
@@ -126,6 +126,8 @@ def _load():
     lib.dspark_mla_layer_fwd_ex.restype = i32
     lib.dspark_mla_layer_tune.argtypes = layer_args
     lib.dspark_mla_layer_tune.restype = i32
+    lib.dspark_mla_layer_read_status.argtypes = [vp, vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.dspark_mla_layer_read_status.restype = i32
     plo = ctypes.POINTER(LossDesc)
     lib.dspark_loss_workspace_size.argtypes = [plo]
     lib.dspark_loss_workspace_size.restype = sz
@@ -328,8 +330,17 @@ def attn_bwd(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk,
     _check(lib.dspark_attn_bwd_ex(*args, ctypes.byref(opts)))
 
 
-def make_layer_desc(attn: Desc, hidden: int, q_rank: int, rms_eps: float = 1e-6) -> LayerDesc:
-    return LayerDesc(attn, int(hidden), int(q_rank), float(rms_eps))
+def make_layer_desc(attn: Desc, hidden: int, q_rank: int, rms_eps: float = 1e-6,
+                    max_kept_blocks: int = 0) -> LayerDesc:
+    return LayerDesc(attn, int(hidden), int(q_rank), float(rms_eps), int(max_kept_blocks))
+
+
+def layer_read_status(workspace, stream=None):
+    """Synchronises the stream; returns (status, first_bad_block, kept_blocks)."""
+    fb, kb = ctypes.c_int32(-1), ctypes.c_int32(0)
+    st = lib.dspark_mla_layer_read_status(_ptr(workspace), _stream(stream), ctypes.byref(fb),
+                                          ctypes.byref(kb))
+    return int(st), int(fb.value), int(kb.value)
 
 
 def layer_workspace_size(desc: LayerDesc) -> int:

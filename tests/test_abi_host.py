@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert set(sd.EXPORTS) == declared
-    assert sd.abi_version() == 6
+    assert sd.abi_version() == 7
 
 
 def glm_desc(**kw):
@@ -274,7 +274,7 @@ def layer_desc(**kw):
 
 
 def test_layer_desc_layout_and_workspace():
-    assert ctypes.sizeof(sd.LayerDesc) == ctypes.sizeof(sd._lib.Desc) + 4 + 4 + 8
+    assert ctypes.sizeof(sd.LayerDesc) == ctypes.sizeof(sd._lib.Desc) + 4 + 4 + 8 + 8
     d = layer_desc(S=2048, N=64)
     need = sd.layer_workspace_size(d)
     rows = 5 * 64

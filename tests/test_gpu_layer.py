@@ -27,11 +27,11 @@ pytestmark = pytest.mark.gpu
 TINY = dict(H=2, D=16, d_c=8, d_r=4, d_v=8, W=6)
 
 
-def run_layer(wl, li, anchors, keep, force_generic=False):
+def run_layer(wl, li, anchors, keep, force_generic=False, max_kept=0, want_status=False):
     import torch
     import speculative_decoding_draft_amd as sd
     t = upload_layer(wl)
-    desc = sd.make_layer_desc(desc_for(wl), li.hidden, li.q_rank, li.rms_eps)
+    desc = sd.make_layer_desc(desc_for(wl), li.hidden, li.q_rank, li.rms_eps, max_kept)
     w = {k: to_torch(getattr(li, k), wl.dtype, "cuda") for k in ("g_in", "w_qa", "g_qa", "w_qb",
                                                                  "w_kva", "g_kva", "w_o")}
     w["w_uk"], w["w_uv"] = t["w_uk"], t["w_uv"]
@@ -42,7 +42,11 @@ def run_layer(wl, li, anchors, keep, force_generic=False):
     out = torch.full(hd.shape, float("nan"), dtype=tdt, device="cuda")
     ws = torch.empty(sd.layer_workspace_size(desc), dtype=torch.uint8, device="cuda")
     sd.mla_layer_fwd(desc, hd, hc, w, a, k, out, ws, force_generic=force_generic)
+    st = sd.layer_read_status(ws)
     torch.cuda.synchronize()
+    if want_status:
+        return out.float().cpu().numpy().astype(np.float64), ws, st
+    assert st[0] == sd.DSPARK_OK, st
     return out.float().cpu().numpy().astype(np.float64), ws
 
 
@@ -131,3 +135,24 @@ def test_layer_tune_then_forward():
     for o in outs:
         check(wl, li, o, ref, wl.keep, 1e-2, 5e-3, "tuned")
     assert np.array_equal(outs[1], outs[2])
+
+
+def test_layer_max_kept_blocks_exact_and_overflow():
+    """max_kept_blocks = the kept count: the draft-row GEMMs run on the kept
+    rows only and the result matches the oracle; one fewer: every row NaN and
+    DSPARK_ECAPACITY."""
+    import speculative_decoding_draft_amd as sd
+    wl = wk.scaled(4, S=600, N=24)
+    li = wk.make_layer_inputs(wl, hidden=6144, q_rank=2048, seed=37)
+    kept = int(wl.keep.sum())
+    assert kept < wl.N
+    gpu, _, st = run_layer(wl, li, wl.anchors, wl.keep, max_kept=kept, want_status=True)
+    assert st[0] == sd.DSPARK_OK and st[2] == kept
+    ref = O.layer_forward(wl, li)
+    check(wl, li, gpu, ref, wl.keep, 1e-2, 5e-3, "max_kept_blocks = kept")
+    full, _ = run_layer(wl, li, wl.anchors, wl.keep)
+    kept_rows = np.repeat(wl.keep.astype(bool), 5, axis=1)
+    assert np.array_equal(gpu[~kept_rows], full[~kept_rows])
+    gpu, _, st = run_layer(wl, li, wl.anchors, wl.keep, max_kept=kept - 1, want_status=True)
+    assert st[0] == sd.DSPARK_ECAPACITY and st[2] == kept
+    assert np.all(np.isnan(gpu))
