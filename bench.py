@@ -357,12 +357,17 @@ def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hid
     mask; max_kept_blocks is the number of kept blocks."""
     import workloads as wk
     from workloads.device import upload_loss
+    from workloads.device import to_torch
     lh = wk.make_loss_inputs(wl, vocab, hidden, rank, seed=9)
     t = upload_loss(lh, wl.loss_mask, anchors, keep)
+    # lm_head and markov_w2 side by side in one [V, d + r] array: the draft
+    # and teacher logits are then one GEMM
+    buf = to_torch(np.concatenate([lh.w_lm, lh.w_m2], axis=1), wl.dtype, "cuda")
+    t["w_lm"], t["w_m2"] = buf, buf[:, hidden:]
     del lh
     kept = int(keep.sum())
     d = sd.make_loss_desc(wl.B, wl.S, wl.N, vocab, hidden, rank, dtype=wl.dtype,
-                          max_kept_blocks=kept)
+                          max_kept_blocks=kept, w_lm_ld=hidden + rank, w_m2_ld=hidden + rank)
     ws = torch.empty(sd.loss_workspace_size(d), dtype=torch.uint8, device="cuda")
     terms = torch.empty((4, wl.B, wl.N, 5), dtype=torch.float32, device="cuda")
     em = torch.empty((wl.B, wl.N, 5), dtype=torch.uint8, device="cuda")
@@ -405,7 +410,7 @@ def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hid
             "frac_of_bf16_peak": round(flop / wall / 1e12 / MI355X_BF16_PEAK_TFLOPS, 4),
             "loss": {"total": vals[0], "ce": vals[1], "l1": vals[2], "bce": vals[3]},
             "stage_us": {k: round(v, 2) for k, v in stage_us.items()},
-            "roofline": {"kernel": "logits GEMMs (rocBLAS: Markov, draft and teacher lm_head)",
+            "roofline": {"kernel": "logits GEMM (rocBLAS: [H | e ; z | 0] [W_lm | W2]^T)",
                          "bound": "mfma", "achieved": round(gemm_tfs, 1),
                          "peak": MI355X_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(gemm_tfs / MI355X_BF16_PEAK_TFLOPS, 4), "traffic": None,

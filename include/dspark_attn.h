@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 7
+#define DSPARK_ABI_VERSION 8
 
 typedef enum dspark_status {
     DSPARK_OK = 0,
@@ -393,6 +393,8 @@ typedef struct dspark_loss_desc {
                                  blocks of the batch: the logits are formed for
                                  5 * max_kept_blocks rows instead of 5 * B * N */
     double alpha_ce, alpha_l1, alpha_conf;   /* 1, 0.9, 1 in the page's recipe */
+    int32_t w_lm_ld;          /* elements between rows of w_lm (0: hidden) */
+    int32_t w_m2_ld;          /* elements between rows of w_m2 (0: markov_rank) */
 } dspark_loss_desc;
 
 /* Bytes of workspace dspark_loss_fwd needs (0 on an invalid descriptor):
@@ -407,8 +409,9 @@ size_t dspark_loss_workspace_size(const dspark_loss_desc* desc);
  *   anchors, keep  [B, N]                 as in dspark_attn_fwd
  *   h_final    [B, 5N, d]                 H^(L)
  *   z          [B, S, d]                  the Target's last hidden states
- *   w_lm       [V, d]                     frozen lm_head
- *   w_m1, w_m2 [V, r]                     markov_w1 (lookup), markov_w2
+ *   w_lm       [V, d]                     frozen lm_head (row stride w_lm_ld)
+ *   w_m1, w_m2 [V, r]                     markov_w1 (lookup, dense), markov_w2
+ *                                         (row stride w_m2_ld)
  *   w_conf     [d + r]                    confidence head (H^(L) part first)
  *   terms      [4, B, N, 5] fp32 out      planes ce, l1, c (confidence
  *                                         logit), bce; 0 where the eval mask is 0
@@ -422,6 +425,10 @@ size_t dspark_loss_workspace_size(const dspark_loss_desc* desc);
  * DSPARK_ECAPACITY.  The logits are fp32 (rocBLAS GEMMs with fp32
  * accumulation, no atomics: the same call gives the same bits);
  * softmax statistics, L1 and the sums are fp32, the final means fp64.
+ * When lm_head and markov_w2 sit side by side in one [V, d + r] array
+ * (w_m2 = w_lm + d, w_lm_ld = w_m2_ld = d + r), the draft and teacher logits
+ * are one GEMM over [H^(L) | e] and [z | 0] with K = d + r; otherwise three
+ * (the Markov bias, the draft lm_head accumulated onto it, the teacher's).
  * Uses the library's rocBLAS handle (see dspark_mla_layer_fwd). */
 dspark_status dspark_loss_fwd(const dspark_loss_desc* desc, const int32_t* input_ids,
                               const uint8_t* loss_mask, const int32_t* anchors,

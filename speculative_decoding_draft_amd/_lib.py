@@ -68,7 +68,8 @@ class LossDesc(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("markov_rank", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("max_kept_blocks", ctypes.c_int32), ("alpha_ce", ctypes.c_double),
-                ("alpha_l1", ctypes.c_double), ("alpha_conf", ctypes.c_double)]
+                ("alpha_l1", ctypes.c_double), ("alpha_conf", ctypes.c_double),
+                ("w_lm_ld", ctypes.c_int32), ("w_m2_ld", ctypes.c_int32)]
 
 
 class DecodeDesc(ctypes.Structure):
@@ -381,10 +382,12 @@ def mla_layer_tune(desc: LayerDesc, h_draft, h_ctx, weights, anchors, keep, out,
 
 def make_loss_desc(B: int, S: int, N: int, vocab: int, hidden: int, markov_rank: int,
                    dtype: str = "bf16", max_kept_blocks: int = 0, alpha_ce: float = 1.0,
-                   alpha_l1: float = 0.9, alpha_conf: float = 1.0) -> LossDesc:
+                   alpha_l1: float = 0.9, alpha_conf: float = 1.0, w_lm_ld: int = 0,
+                   w_m2_ld: int = 0) -> LossDesc:
     dt = {"bf16": DSPARK_BF16, "f32": DSPARK_F32}[dtype]
     return LossDesc(int(B), int(S), int(N), int(vocab), int(hidden), int(markov_rank), dt,
-                    int(max_kept_blocks), float(alpha_ce), float(alpha_l1), float(alpha_conf))
+                    int(max_kept_blocks), float(alpha_ce), float(alpha_l1), float(alpha_conf),
+                    int(w_lm_ld), int(w_m2_ld))
 
 
 def loss_workspace_size(desc: LossDesc) -> int:

@@ -71,10 +71,12 @@ LossLayout loss_layout(const dspark_loss_desc& d) {
     w.status = take(kLsWords * 4);
     w.slot_blk = take((size_t)w.cap * 4);
     w.blk_slot = take((size_t)d.B * d.N * 4);
-    w.xd = take(rows * (size_t)(d.hidden + d.markov_rank) * e);
-    w.xt = take(rows * (size_t)d.hidden * e);
-    w.ld = take(rows * V * 4);
-    w.lt = take(rows * V * 4);
+    // draft rows [H^(L) | e] then teacher rows [z | 0], one [2 rows, d + r]
+    // operand; the draft logits then the teacher's, one [2 rows, V] array
+    w.xd = take(2 * rows * (size_t)(d.hidden + d.markov_rank) * e);
+    w.xt = w.xd + rows * (size_t)(d.hidden + d.markov_rank) * e;
+    w.ld = take(2 * rows * V * 4);
+    w.lt = w.ld + rows * V * 4;
     w.part = take(rows * (size_t)w.chunks * 16);
     w.l1p = take(rows * (size_t)w.chunks * 4);
     w.total = off;
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(256) void loss_gather_kernel(
     const int row = blockIdx.x, j = row / kBlock, k = row % kBlock;
     const int blk = slot_blk[j];
     T* xdr = xd + (size_t)row * (d + r);
-    T* xtr = xt + (size_t)row * d;
+    T* xtr = xt + (size_t)row * (d + r);     // [z | 0]: the Markov columns are 0
     constexpr int E = VEC ? 16 / (int)sizeof(T) : 1;    // elements per copy
     auto copy = [&](T* dst, const T* src, int n) {
         if (VEC) {
@@ -184,6 +186,7 @@ __global__ __launch_bounds__(256) void loss_gather_kernel(
             for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src ? src[i] : T(0);
         }
     };
+    copy(xtr + d, nullptr, r);
     if (blk < 0) {
         copy(xdr, nullptr, d + r);
         copy(xtr, nullptr, d);
@@ -432,6 +435,8 @@ const char* check_desc(const dspark_loss_desc* d) {
         return "vocab, hidden and markov_rank must be >= 1";
     if (d->dtype != DSPARK_BF16 && d->dtype != DSPARK_F32) return "dtype must be DSPARK_BF16 or DSPARK_F32";
     if (d->max_kept_blocks < 0) return "max_kept_blocks must be >= 0";
+    if ((d->w_lm_ld != 0 && d->w_lm_ld < d->hidden) || (d->w_m2_ld != 0 && d->w_m2_ld < d->markov_rank))
+        return "w_lm_ld / w_m2_ld must be 0 or at least hidden / markov_rank";
     if ((long long)d->B * d->N * kBlock > INT_MAX / 4) return "B * N too large";
     if ((long long)d->B * d->S > INT_MAX) return "B * S too large";
     const long long rows = (long long)kBlock * loss_cap(*d);
@@ -541,22 +546,33 @@ dspark_status loss_fwd(const dspark_loss_desc* desc, const int32_t* ids, const u
         const int ldx = hd + rk;
         const char* bad = nullptr;
         rocblas_status bs = rocblas_status_success;
-        const void* xe = (const char*)xd + (size_t)hd * (bf ? 2 : 4);
-        // L = E W2^T, then L += H W_lm^T in place.  Tuning the in-place GEMM
-        // runs it many times over L, so after a tuning pass both are run
-        // again with the recorded choices.
-        for (int pass = 0; pass < (tune ? 2 : 1) && !bad; ++pass) {
-            const bool t = tune && pass == 0;
-            if ((bs = gemm_nt(h, ti, to, rows, V, rk, xe, ldx, w_m2, rk, 0.f, nullptr, 0, ld, V,
-                              t)) != rocblas_status_success)
-                bad = "Markov GEMM";
-            else if ((bs = gemm_nt(h, ti, to, rows, V, hd, xd, ldx, w_lm, hd, 1.f, nullptr, 0, ld,
-                                   V, t)) != rocblas_status_success)
-                bad = "draft lm_head GEMM";
+        const size_t e = bf ? 2 : 4;
+        const int lm_ld = d.w_lm_ld > 0 ? d.w_lm_ld : hd, m2_ld = d.w_m2_ld > 0 ? d.w_m2_ld : rk;
+        const bool fused = lm_ld == ldx && m2_ld == ldx &&
+                           (const char*)w_m2 == (const char*)w_lm + (size_t)hd * e;
+        if (fused) {
+            // [H^(L) | e ; z | 0] [W_lm | W2]^T: draft and teacher logits at once
+            if ((bs = gemm_nt(h, ti, to, 2 * rows, V, ldx, xd, ldx, w_lm, ldx, 0.f, nullptr, 0, ld,
+                              V, tune)) != rocblas_status_success)
+                bad = "logits GEMM";
+        } else {
+            const void* xe = (const char*)xd + (size_t)hd * e;
+            // L = E W2^T, then L += H W_lm^T in place.  Tuning the in-place GEMM
+            // runs it many times over L, so after a tuning pass both are run
+            // again with the recorded choices.
+            for (int pass = 0; pass < (tune ? 2 : 1) && !bad; ++pass) {
+                const bool t = tune && pass == 0;
+                if ((bs = gemm_nt(h, ti, to, rows, V, rk, xe, ldx, w_m2, m2_ld, 0.f, nullptr, 0, ld,
+                                  V, t)) != rocblas_status_success)
+                    bad = "Markov GEMM";
+                else if ((bs = gemm_nt(h, ti, to, rows, V, hd, xd, ldx, w_lm, lm_ld, 1.f, nullptr, 0,
+                                       ld, V, t)) != rocblas_status_success)
+                    bad = "draft lm_head GEMM";
+            }
+            if (!bad && (bs = gemm_nt(h, ti, to, rows, V, hd, xt, ldx, w_lm, lm_ld, 0.f, nullptr, 0,
+                                      lt, V, tune)) != rocblas_status_success)
+                bad = "teacher lm_head GEMM";
         }
-        if (!bad && (bs = gemm_nt(h, ti, to, rows, V, hd, xt, hd, w_lm, hd, 0.f, nullptr, 0, lt, V,
-                                  tune)) != rocblas_status_success)
-            bad = "teacher lm_head GEMM";
         if (bad) {
             snprintf(t_msg, sizeof(t_msg), "%s failed (rocBLAS status %d)", bad, (int)bs);
             return lsfail(DSPARK_EHIP, t_msg);

@@ -30,13 +30,31 @@ TERM_TOL = 2e-4
 MEAN_REL = 1e-5
 
 
-def run_loss(wl, lh, anchors, keep, max_kept=0, tune=False, loss_mask=None, ws=None):
+def run_loss(wl, lh, anchors, keep, max_kept=0, tune=False, loss_mask=None, ws=None,
+             layout="dense"):
+    """layout: "dense" weights, "fused" (lm_head and markov_w2 side by side in
+    one [V, d + r] array: the one-GEMM path), "strided" (padded rows, apart)."""
     import torch
     import speculative_decoding_draft_amd as sd
+    from workloads.device import to_torch
     lm = wl.loss_mask if loss_mask is None else loss_mask
     t = upload_loss(lh, lm, anchors, keep)
+    d_, r_ = lh.hidden, lh.rank
+    lds = (0, 0)
+    if layout == "fused":
+        buf = to_torch(np.concatenate([lh.w_lm, lh.w_m2], axis=1), lh.dtype, "cuda")
+        t["w_lm"], t["w_m2"] = buf, buf[:, d_:]
+        lds = (d_ + r_, d_ + r_)
+    elif layout == "strided":
+        pad = 8
+        a = np.zeros((lh.vocab, d_ + pad), lh.w_lm.dtype)
+        a[:, :d_] = lh.w_lm
+        m = np.zeros((lh.vocab, r_ + pad), lh.w_m2.dtype)
+        m[:, :r_] = lh.w_m2
+        t["w_lm"], t["w_m2"] = to_torch(a, lh.dtype, "cuda"), to_torch(m, lh.dtype, "cuda")
+        lds = (d_ + pad, r_ + pad)
     d = sd.make_loss_desc(wl.B, wl.S, wl.N, lh.vocab, lh.hidden, lh.rank, dtype=lh.dtype,
-                          max_kept_blocks=max_kept)
+                          max_kept_blocks=max_kept, w_lm_ld=lds[0], w_m2_ld=lds[1])
     if ws is None:
         ws = torch.empty(sd.loss_workspace_size(d), dtype=torch.uint8, device="cuda")
     terms = torch.full((4, wl.B, wl.N, 5), 12345.0, dtype=torch.float32, device="cuda")
@@ -197,3 +215,18 @@ def test_loss_headline_size_sampled_blocks():
     total = means[0] + 0.9 * means[1] + means[2]
     for got, want in zip(loss[:4], [total] + means):
         assert abs(got - want) <= 1e-5 * abs(want)
+
+
+@pytest.mark.parametrize("layout,dtype", [("fused", "bf16"), ("strided", "bf16"), ("fused", "f32")])
+def test_loss_weight_layouts(layout, dtype):
+    """lm_head and markov_w2 side by side (one GEMM over [H | e ; z | 0]) and
+    padded row strides (three GEMMs) give the oracle's terms."""
+    if dtype == "bf16":
+        wl = wk.scaled(4, S=1024, N=24)
+        lh = wk.make_loss_inputs(wl, 20000, 6144, 256, seed=53)
+    else:
+        wl, lh = small(53, V=3000, d=32, r=8)
+    kept = int(wl.keep.sum())
+    terms, em, loss, st, _ = run_loss(wl, lh, wl.anchors, wl.keep, max_kept=kept, layout=layout)
+    assert st[0] == 0, st
+    check(f"{layout} {dtype}", terms, em, loss, O.loss_head(lh, wl.loss_mask, wl.anchors, wl.keep))
