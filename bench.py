@@ -561,6 +561,111 @@ def cpu_baseline(wl, anchors, keep, budget_s: float = 15.0):
                       f"(fp64 numpy, gathered form, {spent:.1f} s)"}
 
 
+def _oracle_threads() -> int:
+    try:
+        import threadpoolctl
+        return int(max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()))
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def _grow(run, items, budget_s, start=2):
+    """run(sample) on growing slices of items (doubling) until budget_s of
+    host time is spent; returns (items done, seconds)."""
+    n, spent, done = start, 0.0, []
+    while spent < budget_s and len(done) < len(items):
+        pick = items[len(done):len(done) + n]
+        t0 = time.perf_counter()
+        run(pick)
+        spent += time.perf_counter() - t0
+        done += pick
+        n *= 2
+    return done, spent
+
+
+def bwd_cpu_baseline(wl, anchors, keep, budget_s):
+    """The oracle's backward (fp64, gathered form) on random kept blocks of the
+    same workload, as useful TFLOP/s."""
+    import oracle as O
+    import workloads as wk
+    dout = wk.make_dout(wl, seed=7)
+    kept = [(b, n) for b in range(wl.B) for n in range(wl.N) if keep[b, n]]
+    order = [kept[i] for i in np.random.default_rng(1).permutation(len(kept))]
+    done, spent = _grow(lambda pick: O.backward(wl, dout, anchors=anchors, keep=keep,
+                                                form="gathered", blocks=pick), order, budget_s)
+    flop = sum(bwd_useful_flop([anchors[b, n]], [1], wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v)
+               for b, n in done)
+    return {"value": flop / spent / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(),
+            "kind": "oracle", "sample": f"{len(done)} random kept blocks of the same workload "
+                                        f"(fp64 numpy, {spent:.1f} s)"}
+
+
+def layer_cpu_baseline(budget_s, hidden=6144, q_rank=2048):
+    """The oracle's MLA block (fp64) on the headline recipe at a smaller size
+    (its projections run over every row), as useful TFLOP/s."""
+    import oracle as O
+    import workloads as wk
+    flop = spent = 0.0
+    runs = 0
+    for S, N in ((512, 8), (1024, 16), (2048, 32)):
+        wl = wk.scaled(4, S=S, N=N)
+        li = wk.make_layer_inputs(wl, hidden, q_rank, seed=5)
+        t0 = time.perf_counter()
+        O.layer_forward(wl, li)
+        spent += time.perf_counter() - t0
+        flop += layer_flop(wl, wl.anchors, wl.keep, hidden, q_rank)[0]
+        runs += 1
+        if spent > budget_s:
+            break
+    return {"value": flop / spent / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(),
+            "kind": "oracle", "sample": f"{runs} headline-recipe workloads up to S={S}, N={N} "
+                                        f"(d=6144, q_lora_rank=2048; fp64 numpy, {spent:.1f} s)"}
+
+
+def loss_cpu_baseline(wl, anchors, keep, budget_s, vocab=20000, hidden=6144, rank=256):
+    """The oracle's output head and loss (fp64) on random kept blocks of the
+    same anchors with a 20000-token vocabulary (its cost is linear in V), as
+    useful TFLOP/s."""
+    import oracle as O
+    import workloads as wk
+    lh = wk.make_loss_inputs(wl, vocab, hidden, rank, seed=9)
+    kept = [(b, n) for b in range(wl.B) for n in range(wl.N) if keep[b, n]]
+    order = [kept[i] for i in np.random.default_rng(2).permutation(len(kept))]
+    done, spent = _grow(lambda pick: O.loss_head(lh, wl.loss_mask, anchors, keep, blocks=pick),
+                        order, budget_s, start=8)
+    flop = 2 * 5 * len(done) * vocab * (2 * hidden + rank)
+    return {"value": flop / spent / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(),
+            "kind": "oracle", "sample": f"{len(done)} random kept blocks, V={vocab} "
+                                        f"(fp64 numpy, {spent:.1f} s)"}
+
+
+def decode_cpu_baseline(budget_s, K=5, vocab=154880):
+    """The oracle's decode step (decode attention over a ring and
+    rejection-sampling verification at V = 154880, fp64) for sequences of the
+    decode bench's shape, as sequences per second."""
+    import oracle as O
+    import workloads as wk
+    dims = wk.GLM_DIMS
+    B = 4
+    di = wk.make_decode_inputs(B, dims, "bf16", 5, seed=31)
+    C = dims["W"]
+    ring = np.zeros((B, C, dims["D"]), np.uint16), np.zeros((B, C, dims["d_r"]), np.uint16)
+    dl, tl, u, _ = wk.make_verify_inputs(B, K, vocab, seed=37)
+    anchors = np.full(B, 5000, np.int32)
+    spent, seqs = 0.0, 0
+    while spent < budget_s:
+        t0 = time.perf_counter()
+        O.decode_attention(ring[0], ring[1], anchors, np.ones(B), di.q_nope, di.q_rope,
+                           di.ckv_blk, di.kr_blk, di.w_uk, di.w_uv, dims["W"], 10000.0, "bf16")
+        for b in range(B):
+            O.spec_verify(dl[b], tl[b], np.argmax(dl[b], axis=1), u[b].astype(np.float64))
+        spent += time.perf_counter() - t0
+        seqs += B
+    return {"value": seqs / spent, "unit": "sequences/s", "cores": _oracle_threads(),
+            "kind": "oracle", "sample": f"{seqs} sequences (decode attention + verification, "
+                                        f"fp64 numpy, {spent:.1f} s)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -589,6 +694,9 @@ def main():
                     help="skip the inference-time drafting measurement (the 'decode' object)")
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--side-budget", type=float, default=6.0,
+                    help="host seconds for the oracle baselines of the backward, layer, loss "
+                         "and decode objects")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -749,22 +857,32 @@ def main():
         try:
             result["backward"] = bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors,
                                                 keep, desc, sptr, hip, args.bwd_steps)
+            if not args.no_cpu_baseline:
+                result["backward"]["cpu_baseline"] = bwd_cpu_baseline(wl, anchors, keep,
+                                                                       args.side_budget)
         except Exception as e:   # the forward line is still reported
             result["backward"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_layer and wl.dtype == "bf16":
         try:
             result["layer"] = bench_layer(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep,
                                           desc, sptr, hip, args.layer_steps)
+            if not args.no_cpu_baseline:
+                result["layer"]["cpu_baseline"] = layer_cpu_baseline(args.side_budget)
         except Exception as e:   # the forward line is still reported
             result["layer"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_loss and wl.dtype == "bf16":
         try:
             result["loss"] = bench_loss(sd, torch, wl, anchors, keep, sptr, hip, args.loss_steps)
+            if not args.no_cpu_baseline:
+                result["loss"]["cpu_baseline"] = loss_cpu_baseline(wl, anchors, keep,
+                                                                   args.side_budget)
         except Exception as e:   # the forward line is still reported
             result["loss"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_decode and wl.dtype == "bf16":
         try:
             result["decode"] = bench_decode(sd, torch, hip, args.decode_steps)
+            if not args.no_cpu_baseline:
+                result["decode"]["cpu_baseline"] = decode_cpu_baseline(args.side_budget)
         except Exception as e:   # the forward line is still reported
             result["decode"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_cpu_baseline:
