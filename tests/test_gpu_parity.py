@@ -351,3 +351,60 @@ def test_cfg5_full_size_sampled(sd):
     assert np.array_equal(ga, oa) and np.array_equal(gk, ok)
     for layer in range(3):
         check_sampled(wl, layer, ga, gk, oa, ok, n_random=12, seed=50 + layer)
+
+
+# ---------------------------------------------------------------------------
+# robustness: canaries, a live checker, NaN confinement
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_output_guard_regions_are_untouched(sd, dtype):
+    """NaN canaries on both sides of `out` survive the call (MFMA path for
+    bf16, generic path for fp32)."""
+    wl = wk.scaled(4, S=700, N=24) if dtype == "bf16" else wk.config(1)
+    check_full(wl, form="gathered", guard=8192)
+
+
+def test_checker_is_live(sd):
+    """The comparison fails when one output element of a kept block moves by
+    more than the tolerance: the parity checks can see a wrong result."""
+    wl = wk.scaled(4, S=700, N=24)
+    run = GpuRun(wl, 0, wl.anchors, wl.keep).run()
+    gpu = run.result()
+    ref = O.forward(wl, 0, form="gathered")
+    compare(gpu, ref, wl.keep, BF16_MAX_ABS, BF16_REL_L2, what="unmodified")
+    b, n = [(b, n) for b in range(wl.B) for n in range(wl.N) if wl.keep[b, n]][3]
+    bad = gpu.copy()
+    bad[b, 5 * n + 2, 7, 11] += 0.1
+    with pytest.raises(AssertionError):
+        compare(bad, ref, wl.keep, BF16_MAX_ABS, BF16_REL_L2, what="one element moved")
+    pad = [(b, n) for b in range(wl.B) for n in range(wl.N) if not wl.keep[b, n]][0]
+    bad = gpu.copy()
+    bad[pad[0], 5 * pad[1], 0, 0] = 1e-3          # padding rows must stay exactly 0
+    with pytest.raises(AssertionError):
+        compare(bad, ref, wl.keep, BF16_MAX_ABS, BF16_REL_L2, what="padding row written")
+
+
+@pytest.mark.parametrize("force_generic", [False, True])
+def test_nan_in_one_context_row_stays_in_its_windows(sd, force_generic):
+    """A NaN written into one context row's c^KV reaches exactly the kept
+    blocks whose window contains that row (all their rows); every other row
+    is bit for bit what it was."""
+    import torch
+    wl = wk.scaled(4, S=700, N=24)
+    base = GpuRun(wl, 0, wl.anchors, wl.keep, force_generic=force_generic).run().result()
+    kept = [(0, n) for n in range(wl.N) if wl.keep[0, n]]
+    A = int(wl.anchors[0, kept[len(kept) // 2][1]])
+    p = A - 3
+    run = GpuRun(wl, 0, wl.anchors, wl.keep, force_generic=force_generic)
+    run.t["ckv_ctx"][0, p, 17] = float("nan")
+    got = run.run().result()
+    hit = {n for (_, n) in kept if max(0, int(wl.anchors[0, n]) - wl.W + 1) <= p < int(wl.anchors[0, n])}
+    assert hit, "the poisoned row lies in no window"
+    for n in range(wl.N):
+        rows = got[0, 5 * n:5 * n + 5]
+        if n in hit:
+            assert np.all(np.isnan(rows)), n
+        else:
+            assert np.array_equal(rows, base[0, 5 * n:5 * n + 5]), n
+    log(f"  NaN at context row {p}: {len(hit)} blocks see it, the other {wl.N - len(hit)} unchanged")
