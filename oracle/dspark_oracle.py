@@ -538,11 +538,30 @@ def layer_forward(wl, li, anchors=None, keep=None, scale=None, blocks=None):
     L5 = wl.block * N
     f = lambda a: _f64(a, dt)
     Hd, Hc = f(li.h_draft), f(li.h_ctx)
-    h = rmsnorm(Hd, f(li.g_in), li.rms_eps)
-    cq = rmsnorm(h @ f(li.w_qa).T, f(li.g_qa), li.rms_eps)
-    q = (cq @ f(li.w_qb).T).reshape(B, L5, H, dc + dr)
-    kv_ctx = Hc @ f(li.w_kva).T
-    kv_blk = h @ f(li.w_kva).T
+    # the rows the result needs: with `blocks`, only those blocks' draft rows
+    # and the context rows of their windows are projected (the projections
+    # are row-wise); the other rows stay 0 and are never read
+    qrows = np.ones((B, L5), dtype=bool)
+    crows = np.ones((B, S), dtype=bool)
+    if blocks is not None:
+        an = wl.anchors if anchors is None else anchors
+        qrows[:] = False
+        crows[:] = False
+        for b, n in blocks:
+            qrows[b, wl.block * n:wl.block * (n + 1)] = True
+            A = int(an[b, n])
+            if 0 <= A <= S - 2:
+                crows[b, max(0, A - wl.W + 1):A] = True
+    h = np.zeros_like(Hd)
+    h[qrows] = rmsnorm(Hd[qrows], f(li.g_in), li.rms_eps)
+    q = np.zeros((B, L5, H * (dc + dr)))
+    cq = rmsnorm(h[qrows] @ f(li.w_qa).T, f(li.g_qa), li.rms_eps)
+    q[qrows] = cq @ f(li.w_qb).T
+    q = q.reshape(B, L5, H, dc + dr)
+    kv_ctx = np.zeros((B, S, D + dr))
+    kv_ctx[crows] = Hc[crows] @ f(li.w_kva).T
+    kv_blk = np.zeros((B, L5, D + dr))
+    kv_blk[qrows] = h[qrows] @ f(li.w_kva).T
     sub = _copy.copy(wl)
     sub.dtype = "f64"
     base = wl.layers[0]
@@ -552,7 +571,10 @@ def layer_forward(wl, li, anchors=None, keep=None, scale=None, blocks=None):
         ckv_blk=rmsnorm(kv_blk[..., :D], f(li.g_kva), li.rms_eps), kr_blk=kv_blk[..., D:],
         w_uk=f(base.w_uk), w_uv=f(base.w_uv))]
     o = forward(sub, 0, anchors, keep, form="gathered", blocks=blocks, scale=scale)
-    return Hd + o.reshape(B, L5, H * dv) @ f(li.w_o).T
+    out = np.full((B, L5, Hd.shape[-1]), np.nan)
+    o2 = o.reshape(B, L5, H * dv)
+    out[qrows] = Hd[qrows] + o2[qrows] @ f(li.w_o).T
+    return out
 
 
 # ---------------------------------------------------------------------------

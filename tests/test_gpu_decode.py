@@ -91,6 +91,16 @@ def check_decode(name, gpu, ref, active, tol):
     assert mx <= tol[0] and rel <= tol[1], (name, mx, rel)
 
 
+def test_decode_bench_shape():
+    """The decode bench's shape: 64 sequences at GLM dims, W = C = 128,
+    anchors drawn as the bench draws them."""
+    anchors = np.random.default_rng(31).integers(128, 10**6, size=64).tolist()
+    active = [1] * 64
+    gpu, ref, ring, ring_ref, st = run_decode(dict(wk.GLM_DIMS), "bf16", 128, anchors, active)
+    assert st == 0
+    check_decode("decode bench shape", gpu, ref, active, (BF16_MAX_ABS, BF16_REL_L2))
+
+
 @pytest.mark.parametrize("C", [128, 200])
 def test_decode_glm_bf16(C):
     dims = dict(wk.GLM_DIMS)

@@ -156,3 +156,35 @@ def test_layer_max_kept_blocks_exact_and_overflow():
     gpu, _, st = run_layer(wl, li, wl.anchors, wl.keep, max_kept=kept - 1, want_status=True)
     assert st[0] == sd.DSPARK_ECAPACITY and st[2] == kept
     assert np.all(np.isnan(gpu))
+
+
+def test_layer_headline_size_sampled_blocks():
+    """The configuration the benchmark times: S = 32768, N = 1024 (768 kept),
+    d = 6144, q_lora_rank = 2048, bf16, max_kept_blocks = 768.  The oracle
+    checks every row of 6 blocks (the clamped ones at anchors 0, 1 and 126
+    among them); padding rows must be exactly H."""
+    wl = wk.config(4)
+    li = wk.make_layer_inputs(wl, hidden=6144, q_rank=2048, seed=5)
+    kept = int(wl.keep.sum())
+    gpu, _ = run_layer(wl, li, wl.anchors, wl.keep, max_kept=kept)
+    ks = [n for n in range(wl.N) if wl.keep[0, n]]
+    low = [n for n in ks if wl.anchors[0, n] in (0, 1, 126)]
+    rng = np.random.default_rng(5)
+    pick = sorted(set(low) | set(rng.choice([n for n in ks if n not in low], 6 - len(low),
+                                             replace=False).tolist()))
+    ref = O.layer_forward(wl, li, blocks=[(0, n) for n in pick])
+    H = O.dspark_oracle._f64(li.h_draft, wl.dtype)
+    pad = np.repeat(~wl.keep.astype(bool), 5, axis=1)
+    assert np.array_equal(gpu[pad], H[pad]), "padding rows are not H"
+    rows = np.zeros_like(pad)
+    for n in pick:
+        rows[0, 5 * n:5 * n + 5] = True
+    g, r, h = gpu[rows], ref[rows], H[rows]
+    assert np.all(np.isfinite(g))
+    rel_out = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+    rel_d = float(np.linalg.norm((g - h) - (r - h)) / np.linalg.norm(r - h))
+    ratio = float(np.linalg.norm(r - h) / np.linalg.norm(h))
+    bound = 1e-2 + 2 * 2.0 ** -9 / np.sqrt(3.0) / ratio
+    log(f"  headline, {len(pick)} sampled blocks: out rel_l2={rel_out:.3e} "
+        f"delta rel_l2={rel_d:.3e} (bound {bound:.2e})")
+    assert rel_d <= bound and rel_out <= 5e-3

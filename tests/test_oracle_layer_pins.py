@@ -96,3 +96,18 @@ def test_library_torch_recomputation_of_the_projections():
     got = O.layer_forward(wl, li)
     kept = np.repeat(wl.keep.astype(bool), 5, axis=1)
     np.testing.assert_allclose(got[kept], ref[kept], rtol=1e-11, atol=1e-11)
+
+
+def test_block_restriction_matches_the_full_block():
+    """layer_forward(blocks=...) projects only the sampled blocks' rows and
+    their windows; their output rows equal the full computation's."""
+    wl, li = small(seed=19, B=2, N=6, S=48)
+    full = O.layer_forward(wl, li)
+    kept = [(b, n) for b in range(wl.B) for n in range(wl.N) if wl.keep[b, n]]
+    pick = kept[::2]
+    part = O.layer_forward(wl, li, blocks=pick)
+    for b, n in pick:
+        np.testing.assert_allclose(part[b, 5 * n:5 * n + 5], full[b, 5 * n:5 * n + 5],
+                                   rtol=1e-12, atol=1e-12)
+    others = [(b, n) for b in range(wl.B) for n in range(wl.N) if (b, n) not in pick]
+    assert all(np.all(np.isnan(part[b, 5 * n:5 * n + 5])) for b, n in others)
