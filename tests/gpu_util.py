@@ -69,7 +69,7 @@ def desc_for(wl, softmax_scale=0.0):
                         softmax_scale=softmax_scale, dtype=wl.dtype)
 
 
-class GpuRun:
+class ForwardRun:
     """Uploads one layer, owns out + workspace, runs the forward."""
 
     def __init__(self, wl, layer_idx=0, anchors=None, keep=None, guard=0, softmax_scale=0.0,

@@ -6,7 +6,7 @@ import pytest
 
 import oracle as O
 import workloads as wk
-from gpu_util import (BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS, F32_REL_L2, GpuRun, HipEventPool,
+from gpu_util import (BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS, F32_REL_L2, ForwardRun, HipEventPool,
                       anchors_for, compare, desc_for, log, sample_blocks)
 
 pytestmark = pytest.mark.gpu
@@ -24,7 +24,7 @@ def check_full(wl, form="dense", layer=0, force_generic=False, tol=None, guard=0
                chunk_blocks=0):
     ga, gk, oa, ok = anchors_for(wl)
     assert np.array_equal(ga, oa) and np.array_equal(gk, ok), "anchor selection differs"
-    run = GpuRun(wl, layer, ga, gk, guard=guard, force_generic=force_generic,
+    run = ForwardRun(wl, layer, ga, gk, guard=guard, force_generic=force_generic,
                  chunk_blocks=chunk_blocks).run()
     gpu = run.result()
     ref = O.forward(wl, layer, oa, ok, form=form)
@@ -160,7 +160,7 @@ def test_rounds_on_two_streams(sd, chunk):
     import torch
     wl = wk.scaled(4, S=4096, N=224)
     log(f"cfg4 recipe B1 S4096 N224, chunk {chunk}, two streams")
-    run = GpuRun(wl, 0, wl.anchors, wl.keep, guard=2048, chunk_blocks=chunk)
+    run = ForwardRun(wl, 0, wl.anchors, wl.keep, guard=2048, chunk_blocks=chunk)
     single = run.run().result()
     run.out.fill_(float("nan"))
     aux = torch.cuda.Stream()
@@ -181,7 +181,7 @@ def test_stage_events_are_recorded_in_order(sd):
     import ctypes
     import torch
     wl = wk.scaled(4, S=2048, N=100)
-    run = GpuRun(wl, 0, wl.anchors, wl.keep, chunk_blocks=16)
+    run = ForwardRun(wl, 0, wl.anchors, wl.keep, chunk_blocks=16)
     n_chunks, chunk, n_ev = sd.attn_plan(run.desc, chunk_blocks=16)
     assert (n_chunks, chunk, n_ev) == (7, 16, 2 + 4 * 7)
     hip = ctypes.CDLL("libamdhip64.so.7")
@@ -217,7 +217,7 @@ def test_bound_call_matches_plain_call(sd):
     """BoundFwd (arguments marshalled once) runs the same forward."""
     import torch
     wl = wk.scaled(4, S=2048, N=96)
-    r = GpuRun(wl, 0, wl.anchors, wl.keep)
+    r = ForwardRun(wl, 0, wl.anchors, wl.keep)
     ref = r.run().result()
     r.out.fill_(float("nan"))
     t = r.t
@@ -274,7 +274,7 @@ def test_everything_padding_on_mfma_path(sd):
                           recipe="uniform", seed=83)
     wl.keep[:] = 0
     wl.anchors[:] = -3
-    run = GpuRun(wl, 0, wl.anchors, wl.keep, guard=512).run()
+    run = ForwardRun(wl, 0, wl.anchors, wl.keep, guard=512).run()
     gpu = run.result()
     assert np.all(gpu == 0) and run.guards_intact()
     st, fb = sd.read_device_status(run.ws)
@@ -286,7 +286,7 @@ def test_bad_anchor_rows_are_nan_and_reported(sd):
                           recipe="uniform", seed=9)
     a, k = wl.anchors.copy(), wl.keep.copy()
     a[0, 7] = 511            # S - 1: invalid
-    run = GpuRun(wl, 0, a, k).run()
+    run = ForwardRun(wl, 0, a, k).run()
     st, fb = sd.read_device_status(run.ws)
     assert st == sd.DSPARK_EANCHOR and fb == 7
     gpu = run.result()
@@ -300,14 +300,14 @@ def test_bad_anchor_rows_are_nan_and_reported(sd):
 
 def test_explicit_softmax_scale(sd):
     wl = wk.scaled(4, S=1024, N=32)
-    run = GpuRun(wl, 0, wl.anchors, wl.keep, softmax_scale=0.03).run()
+    run = ForwardRun(wl, 0, wl.anchors, wl.keep, softmax_scale=0.03).run()
     ref = O.forward(wl, 0, form="gathered", scale=0.03)
     compare(run.result(), ref, wl.keep, BF16_MAX_ABS, BF16_REL_L2, what="scale 0.03")
 
 
 def test_deterministic(sd):
     wl = wk.scaled(4, S=2048, N=96)
-    r = GpuRun(wl, 0, wl.anchors, wl.keep)
+    r = ForwardRun(wl, 0, wl.anchors, wl.keep)
     a = r.run().result()
     b = r.run().result()
     assert np.array_equal(np.nan_to_num(a, nan=7.0), np.nan_to_num(b, nan=7.0))
@@ -318,7 +318,7 @@ def test_deterministic(sd):
 # ---------------------------------------------------------------------------
 
 def check_sampled(wl, layer, ga, gk, oa, ok, n_random, seed):
-    run = GpuRun(wl, layer, ga, gk).run()
+    run = ForwardRun(wl, layer, ga, gk).run()
     gpu = run.result()
     st, fb = run.sd.read_device_status(run.ws)
     assert st == 0 and fb == -1
@@ -369,7 +369,7 @@ def test_checker_is_live(sd):
     """The comparison fails when one output element of a kept block moves by
     more than the tolerance: the parity checks can see a wrong result."""
     wl = wk.scaled(4, S=700, N=24)
-    run = GpuRun(wl, 0, wl.anchors, wl.keep).run()
+    run = ForwardRun(wl, 0, wl.anchors, wl.keep).run()
     gpu = run.result()
     ref = O.forward(wl, 0, form="gathered")
     compare(gpu, ref, wl.keep, BF16_MAX_ABS, BF16_REL_L2, what="unmodified")
@@ -392,11 +392,11 @@ def test_nan_in_one_context_row_stays_in_its_windows(sd, force_generic):
     is bit for bit what it was."""
     import torch
     wl = wk.scaled(4, S=700, N=24)
-    base = GpuRun(wl, 0, wl.anchors, wl.keep, force_generic=force_generic).run().result()
+    base = ForwardRun(wl, 0, wl.anchors, wl.keep, force_generic=force_generic).run().result()
     kept = [(0, n) for n in range(wl.N) if wl.keep[0, n]]
     A = int(wl.anchors[0, kept[len(kept) // 2][1]])
     p = A - 3
-    run = GpuRun(wl, 0, wl.anchors, wl.keep, force_generic=force_generic)
+    run = ForwardRun(wl, 0, wl.anchors, wl.keep, force_generic=force_generic)
     run.t["ckv_ctx"][0, p, 17] = float("nan")
     got = run.run().result()
     hit = {n for (_, n) in kept if max(0, int(wl.anchors[0, n]) - wl.W + 1) <= p < int(wl.anchors[0, n])}
