@@ -285,7 +285,7 @@ def layer_flop(wl, anchors, keep, hidden, q_rank):
 
 
 def bench_layer(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sptr, hip, steps,
-                hidden=6144, q_rank=2048):
+                hidden=6144, q_rank=2048, tune=True):
     """Times dspark_mla_layer_fwd (the MLA block of one draft layer) on the
     same attention inputs' workload, with seeded hidden states and weights of
     the page's shapes (d = 6144, q_lora_rank = 2048)."""
@@ -305,7 +305,7 @@ def bench_layer(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sptr,
     args = (ld, hd, hc, w, a_dev, k_dev, out, ws)
     # pick the GEMM kernels for these shapes first (synchronous, seconds)
     t_tune = time.perf_counter()
-    sd.mla_layer_tune(*args, stream=sptr)
+    (sd.mla_layer_tune if tune else sd.mla_layer_fwd)(*args, stream=sptr)
     torch.cuda.synchronize()
     t_tune = time.perf_counter() - t_tune
     w0, n_w = time.perf_counter(), 0
@@ -351,7 +351,8 @@ def loss_flop(wl, keep, vocab, hidden, rank):
     return sum(st.values()), st
 
 
-def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hidden=6144, rank=256):
+def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hidden=6144, rank=256,
+               tune=True):
     """Times dspark_loss_fwd on seeded inputs of the page's shapes (V = 154880,
     d = 6144, markov rank 256) with the workload's anchors, keep mask and loss
     mask; max_kept_blocks is the number of kept blocks."""
@@ -374,7 +375,7 @@ def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hid
     loss = torch.empty(5, dtype=torch.float32, device="cuda")
     args = (d, t, terms, em, loss, ws)
     t_tune = time.perf_counter()
-    sd.loss_tune(*args, stream=sptr)
+    (sd.loss_tune if tune else sd.loss_fwd)(*args, stream=sptr)
     torch.cuda.synchronize()
     t_tune = time.perf_counter() - t_tune
     st = sd.loss_read_status(ws, stream=sptr)
@@ -693,6 +694,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the inference-time drafting measurement (the 'decode' object)")
     ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-tune", action="store_true",
+                    help="skip the rocBLAS kernel choice of the layer and loss objects (for "
+                         "counter runs; their GEMM times are then rocBLAS's defaults')")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--side-budget", type=float, default=6.0,
                     help="host seconds for the oracle baselines of the backward, layer, loss "
@@ -865,14 +869,15 @@ def main():
     if not args.no_layer and wl.dtype == "bf16":
         try:
             result["layer"] = bench_layer(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep,
-                                          desc, sptr, hip, args.layer_steps)
+                                          desc, sptr, hip, args.layer_steps, tune=not args.no_tune)
             if not args.no_cpu_baseline:
                 result["layer"]["cpu_baseline"] = layer_cpu_baseline(args.side_budget)
         except Exception as e:   # the forward line is still reported
             result["layer"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_loss and wl.dtype == "bf16":
         try:
-            result["loss"] = bench_loss(sd, torch, wl, anchors, keep, sptr, hip, args.loss_steps)
+            result["loss"] = bench_loss(sd, torch, wl, anchors, keep, sptr, hip, args.loss_steps,
+                                        tune=not args.no_tune)
             if not args.no_cpu_baseline:
                 result["loss"]["cpu_baseline"] = loss_cpu_baseline(wl, anchors, keep,
                                                                    args.side_budget)
