@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256) void loss_terms_kernel(
     const int32_t* __restrict__ anchors, const uint8_t* __restrict__ keep,
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ emask,
     const float4* __restrict__ part, const float* __restrict__ l1p, const float* __restrict__ ld,
-    const T* __restrict__ xd, const T* __restrict__ w_conf, const int32_t* __restrict__ status,
+    const T* __restrict__ xd, const T* __restrict__ w_conf, int32_t* __restrict__ status,
     float* __restrict__ terms, int n_pos) {
     const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256) void loss_terms_kernel(
         l1 = wave_sum(s);
         int y = ids[(size_t)(blk / N) * S + A + k + 1];
         if (y < 0 || y >= V) {                         // poisons the loss (reduce)
-            if (lane == 0) const_cast<int32_t*>(status)[kLsBadToken] = 1;
+            if (lane == 0) status[kLsBadToken] = 1;
             y = y < 0 ? 0 : V - 1;
         }
         ce = lse.x - ld[(size_t)row * V + y];
