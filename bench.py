@@ -342,10 +342,11 @@ def bench_layer(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sptr,
 LOSS_STAGES = ("index_gather", "gemms", "stats", "l1", "terms_reduce")
 
 
-def loss_flop(wl, keep, vocab, hidden, rank):
-    """FLOP of the output head on the rows of kept blocks: the lm_head for the
-    draft and the teacher rows and the Markov bias.  Returns (total, {stage: flop})."""
-    rows = 5 * int(keep.sum())
+def loss_flop(counted_steps, vocab, hidden, rank):
+    """FLOP of the output head on the steps the eval mask counts (the only
+    ones whose logits enter the loss): the lm_head for the draft and the
+    teacher rows and the Markov bias.  Returns (total, {stage: flop})."""
+    rows = int(counted_steps)
     st = {"lm_head_draft": 2 * rows * hidden * vocab, "lm_head_teacher": 2 * rows * hidden * vocab,
           "markov": 2 * rows * rank * vocab}
     return sum(st.values()), st
@@ -367,12 +368,19 @@ def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hid
     t["w_lm"], t["w_m2"] = buf, buf[:, hidden:]
     del lh
     kept = int(keep.sum())
-    d = sd.make_loss_desc(wl.B, wl.S, wl.N, vocab, hidden, rank, dtype=wl.dtype,
-                          max_kept_blocks=kept, w_lm_ld=hidden + rank, w_m2_ld=hidden + rank)
-    ws = torch.empty(sd.loss_workspace_size(d), dtype=torch.uint8, device="cuda")
+    mk = lambda counted: sd.make_loss_desc(wl.B, wl.S, wl.N, vocab, hidden, rank, dtype=wl.dtype,
+                                           max_kept_blocks=kept, w_lm_ld=hidden + rank,
+                                           w_m2_ld=hidden + rank, max_counted_steps=counted)
     terms = torch.empty((4, wl.B, wl.N, 5), dtype=torch.float32, device="cuda")
     em = torch.empty((wl.B, wl.N, 5), dtype=torch.uint8, device="cuda")
     loss = torch.empty(5, dtype=torch.float32, device="cuda")
+    # one call bounded by the kept blocks tells the counted steps; the timed
+    # calls form the logits of exactly those rows
+    d = mk(0)
+    ws = torch.empty(sd.loss_workspace_size(d), dtype=torch.uint8, device="cuda")
+    sd.loss_fwd(d, t, terms, em, loss, ws, stream=sptr)
+    counted = sd.loss_read_status(ws, stream=sptr)[3]
+    d = mk(counted)
     args = (d, t, terms, em, loss, ws)
     t_tune = time.perf_counter()
     (sd.loss_tune if tune else sd.loss_fwd)(*args, stream=sptr)
@@ -396,7 +404,7 @@ def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hid
     torch.cuda.synchronize()
     stage_us = {s: hip.elapsed_ms(ev[i], ev[i + 1]) * 1e3 for i, s in enumerate(LOSS_STAGES)}
     hip.destroy(ev)
-    flop, st_flop = loss_flop(wl, keep, vocab, hidden, rank)
+    flop, st_flop = loss_flop(counted, vocab, hidden, rank)
     vals = loss.cpu().tolist()
     gemm_tfs = flop / (stage_us["gemms"] * 1e-6) / 1e12
     # the statistics pass reads the draft and teacher logits of the counted rows once
@@ -405,6 +413,7 @@ def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hid
     stat_gbs = stat_bytes / (stage_us["stats"] * 1e-6) / 1e9
     return {"ms_per_step": round(wall * 1e3, 4), "steps": steps, "warmup": n_w,
             "vocab": vocab, "hidden": hidden, "markov_rank": rank, "kept_blocks": kept,
+            "logit_rows": 2 * counted,
             "counted_steps": live, "gemm_tuning_s": round(t_tune, 2),
             "useful_gflop_per_step": round(flop / 1e9, 3),
             "value": round(flop / wall / 1e12, 3), "unit": "TFLOP/s",

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 8
+#define DSPARK_ABI_VERSION 9
 
 typedef enum dspark_status {
     DSPARK_OK = 0,
@@ -390,16 +390,21 @@ typedef struct dspark_loss_desc {
     int32_t markov_rank;      /* r (256), >= 1 */
     int32_t dtype;            /* dspark_dtype of H^(L), z and the weights */
     int32_t max_kept_blocks;  /* 0: B*N.  Otherwise an upper bound on the kept
-                                 blocks of the batch: the logits are formed for
-                                 5 * max_kept_blocks rows instead of 5 * B * N */
+                                 blocks of the batch */
     double alpha_ce, alpha_l1, alpha_conf;   /* 1, 0.9, 1 in the page's recipe */
     int32_t w_lm_ld;          /* elements between rows of w_lm (0: hidden) */
     int32_t w_m2_ld;          /* elements between rows of w_m2 (0: markov_rank) */
+    int32_t max_counted_steps;/* 0: 5 * the block bound.  Otherwise an upper
+                                 bound on the steps the eval mask counts.  The
+                                 logits are formed for one row per counted
+                                 step, at most this many rows (5 * max_kept_blocks
+                                 when 0); more counted steps than rows is
+                                 DSPARK_ECAPACITY */
 } dspark_loss_desc;
 
 /* Bytes of workspace dspark_loss_fwd needs (0 on an invalid descriptor):
- * a status area, the compacted block list, the gathered rows, the draft and
- * teacher logits in fp32 ([5 * rows, V] each: 6.3 GB for 5120 rows of
+ * a status area, the row <-> step maps, the gathered rows, the draft and
+ * teacher logits in fp32 ([rows, V] each: 1.9 GB per 3132 rows of
  * V = 154880) and per-chunk softmax statistics.  256-byte aligned. */
 size_t dspark_loss_workspace_size(const dspark_loss_desc* desc);
 
@@ -420,8 +425,9 @@ size_t dspark_loss_workspace_size(const dspark_loss_desc* desc);
  *                                         number of counted steps
  * A kept block whose anchor lies outside [0, S-2] is an error detected on
  * the device: its terms are NaN, the loss is NaN and
- * dspark_loss_read_status reports DSPARK_EANCHOR.  More kept blocks than
- * max_kept_blocks: every term and the loss are NaN and the status is
+ * dspark_loss_read_status reports DSPARK_EANCHOR.  Only the counted steps'
+ * logits are formed (one compact row each).  More counted steps than the row
+ * bound: every term and the loss are NaN and the status is
  * DSPARK_ECAPACITY.  The logits are fp32 (rocBLAS GEMMs with fp32
  * accumulation, no atomics: the same call gives the same bits);
  * softmax statistics, L1 and the sums are fp32, the final means fp64.
@@ -461,11 +467,14 @@ dspark_status dspark_loss_tune(const dspark_loss_desc* desc, const int32_t* inpu
 
 /* Synchronises `stream`, then reads the status area of a workspace used by
  * the last dspark_loss_fwd on it: DSPARK_OK, DSPARK_EANCHOR (first_bad_block
- * = b*N + n of the first kept block with a bad anchor) or DSPARK_ECAPACITY.
- * kept_blocks receives the number of kept blocks.  Either pointer may be
- * NULL. */
+ * = b*N + n of the first kept block with a bad anchor), DSPARK_ECAPACITY or
+ * DSPARK_EINVAL (a token id outside [0, V)).  kept_blocks receives the
+ * number of kept blocks with valid anchors, counted_steps the number of
+ * steps the eval mask counts (a caller can size max_counted_steps from it).
+ * Any pointer may be NULL. */
 dspark_status dspark_loss_read_status(const void* workspace, void* stream,
-                                      int32_t* first_bad_block, int32_t* kept_blocks);
+                                      int32_t* first_bad_block, int32_t* kept_blocks,
+                                      int32_t* counted_steps);
 
 /* ---- inference-time drafting -------------------------------------------
  * The draft's KV cache (parameter summary, "KV cache"): at inference a draft

@@ -69,7 +69,8 @@ class LossDesc(ctypes.Structure):
                 ("markov_rank", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("max_kept_blocks", ctypes.c_int32), ("alpha_ce", ctypes.c_double),
                 ("alpha_l1", ctypes.c_double), ("alpha_conf", ctypes.c_double),
-                ("w_lm_ld", ctypes.c_int32), ("w_m2_ld", ctypes.c_int32)]
+                ("w_lm_ld", ctypes.c_int32), ("w_m2_ld", ctypes.c_int32),
+                ("max_counted_steps", ctypes.c_int32)]
 
 
 class DecodeDesc(ctypes.Structure):
@@ -139,7 +140,8 @@ def _load():
     lib.dspark_loss_fwd_ex.restype = i32
     lib.dspark_loss_tune.argtypes = loss_args
     lib.dspark_loss_tune.restype = i32
-    lib.dspark_loss_read_status.argtypes = [vp, vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.dspark_loss_read_status.argtypes = [vp, vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                            ctypes.POINTER(i32)]
     lib.dspark_loss_read_status.restype = i32
     pdd = ctypes.POINTER(DecodeDesc)
     lib.dspark_cache_append.argtypes = [pdd, vp, vp, i32, vp, vp, vp, vp, vp]
@@ -383,11 +385,11 @@ def mla_layer_tune(desc: LayerDesc, h_draft, h_ctx, weights, anchors, keep, out,
 def make_loss_desc(B: int, S: int, N: int, vocab: int, hidden: int, markov_rank: int,
                    dtype: str = "bf16", max_kept_blocks: int = 0, alpha_ce: float = 1.0,
                    alpha_l1: float = 0.9, alpha_conf: float = 1.0, w_lm_ld: int = 0,
-                   w_m2_ld: int = 0) -> LossDesc:
+                   w_m2_ld: int = 0, max_counted_steps: int = 0) -> LossDesc:
     dt = {"bf16": DSPARK_BF16, "f32": DSPARK_F32}[dtype]
     return LossDesc(int(B), int(S), int(N), int(vocab), int(hidden), int(markov_rank), dt,
                     int(max_kept_blocks), float(alpha_ce), float(alpha_l1), float(alpha_conf),
-                    int(w_lm_ld), int(w_m2_ld))
+                    int(w_lm_ld), int(w_m2_ld), int(max_counted_steps))
 
 
 def loss_workspace_size(desc: LossDesc) -> int:
@@ -426,11 +428,12 @@ def loss_tune(desc: LossDesc, tensors, terms, eval_mask, loss, workspace, stream
 
 
 def loss_read_status(workspace, stream=None):
-    """Synchronises the stream; returns (status, first_bad_block, kept_blocks)."""
-    fb, kb = ctypes.c_int32(-1), ctypes.c_int32(0)
+    """Synchronises the stream; returns (status, first_bad_block, kept_blocks,
+    counted_steps)."""
+    fb, kb, cs = ctypes.c_int32(-1), ctypes.c_int32(0), ctypes.c_int32(0)
     st = lib.dspark_loss_read_status(_ptr(workspace), _stream(stream), ctypes.byref(fb),
-                                     ctypes.byref(kb))
-    return int(st), int(fb.value), int(kb.value)
+                                     ctypes.byref(kb), ctypes.byref(cs))
+    return int(st), int(fb.value), int(kb.value), int(cs.value)
 
 
 def make_decode_desc(attn: Desc, cache_slots: int) -> DecodeDesc:

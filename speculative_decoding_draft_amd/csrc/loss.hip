@@ -8,9 +8,9 @@
 // and their means over the steps of the §6 eval mask.
 //
 // Launches (one stream):
-//   index   one workgroup: kept blocks -> compact slots, eval mask, status
-//   gather  one workgroup per row (5 per slot): [H^(L) row ; markov_w1 row]
-//           and the teacher's z row, side by side for the GEMMs
+//   index   one workgroup: eval mask, one compact row per counted step, status
+//   gather  one workgroup per row: [H^(L) row ; markov_w1 row] and
+//           [z row ; 0], side by side for the GEMMs
 //   GEMMs   rocBLAS, fp32 out: L = E W2^T, then L += H W_lm^T (beta = 1),
 //           T = Z W_lm^T  ([rows, V] each, materialised: 2 x 3.2 GB for
 //           5120 rows -- small against the HBM, and it replaces a second
@@ -43,34 +43,38 @@ constexpr int kIndexThreads = 1024;
 
 // Status area of the loss workspace (int32 words at offset 0; word 1 holds
 // the first bad block as in the attention's status area).
-enum LossStatus { kLsKept = 0, kLsFirstBad = 1, kLsOverflow = 2, kLsBadToken = 3, kLsWords = 16 };
+enum LossStatus {
+    kLsKept = 0, kLsFirstBad = 1, kLsOverflow = 2, kLsBadToken = 3, kLsCounted = 4, kLsWords = 16
+};
 
 struct LossLayout {
-    size_t status = 0, slot_blk = 0, blk_slot = 0, xd = 0, xt = 0, ld = 0, lt = 0, part = 0,
+    size_t status = 0, row_step = 0, step_row = 0, xd = 0, xt = 0, ld = 0, lt = 0, part = 0,
            l1p = 0, total = 0;
-    int cap = 0;       // compact block slots
-    int rows = 0;      // 5 * cap
+    int rows = 0;      // compact rows: one per counted step, at most this many
     int chunks = 0;    // ceil(V / kChunk)
 };
 
-int loss_cap(const dspark_loss_desc& d) {
+// Rows the logits are formed for: max_counted_steps, else 5 per block of the
+// block bound (max_kept_blocks, else B * N).
+long long loss_rows(const dspark_loss_desc& d) {
     const long long bn = (long long)d.B * d.N;
-    const long long c = d.max_kept_blocks > 0 ? std::min<long long>(d.max_kept_blocks, bn) : bn;
-    return (int)c;
+    const long long all = (long long)kBlock * bn;
+    if (d.max_counted_steps > 0) return std::min<long long>(d.max_counted_steps, all);
+    const long long blocks = d.max_kept_blocks > 0 ? std::min<long long>(d.max_kept_blocks, bn) : bn;
+    return (long long)kBlock * blocks;
 }
 
 LossLayout loss_layout(const dspark_loss_desc& d) {
     LossLayout w;
     const size_t e = d.dtype == DSPARK_BF16 ? 2 : 4;
-    w.cap = loss_cap(d);
-    w.rows = kBlock * w.cap;
+    w.rows = (int)loss_rows(d);
     w.chunks = (d.vocab + kChunk - 1) / kChunk;
     const size_t rows = (size_t)w.rows, V = (size_t)d.vocab;
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
     w.status = take(kLsWords * 4);
-    w.slot_blk = take((size_t)w.cap * 4);
-    w.blk_slot = take((size_t)d.B * d.N * 4);
+    w.row_step = take(rows * 4);
+    w.step_row = take((size_t)d.B * d.N * kBlock * 4);
     // draft rows [H^(L) | e] then teacher rows [z | 0], one [2 rows, d + r]
     // operand; the draft logits then the teacher's, one [2 rows, V] array
     w.xd = take(2 * rows * (size_t)(d.hidden + d.markov_rank) * e);
@@ -96,43 +100,49 @@ __device__ inline float wave_sum(float v) {
     return v;
 }
 
-// ---- index: compact slots of the kept blocks, eval mask, status --------
-// Blocks are taken in (b, n) order; a kept block with a valid anchor gets
-// the next slot.  One workgroup, any B * N.
+// ---- index: eval mask, one compact row per counted step, status --------
+// Blocks are taken in (b, n) order; the counted steps of a kept block with a
+// valid anchor (a prefix of its 5, by the cumprod) get the next rows.
+// row_step [rows]: step b*N*5 + n*5 + k of each row (-1 past the last);
+// step_row [B*N*5]: the row of each counted step (-1 otherwise).  One
+// workgroup, any B * N.
 __global__ __launch_bounds__(kIndexThreads) void loss_index_kernel(
-    int B, int S, int N, int cap, const int32_t* __restrict__ anchors,
+    int B, int S, int N, int cap_rows, const int32_t* __restrict__ anchors,
     const uint8_t* __restrict__ keep, const uint8_t* __restrict__ loss_mask,
-    int32_t* __restrict__ status, int32_t* __restrict__ slot_blk, int32_t* __restrict__ blk_slot,
+    int32_t* __restrict__ status, int32_t* __restrict__ row_step, int32_t* __restrict__ step_row,
     uint8_t* __restrict__ emask) {
     __shared__ int wsum[kIndexThreads / 64];
-    __shared__ int base_s, bad_s;
+    __shared__ int base_s, bad_s, kept_s;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int total = B * N;
     if (tid == 0) {
         base_s = 0;
         bad_s = INT_MAX;
+        kept_s = 0;
     }
     __syncthreads();
     for (int c0 = 0; c0 < total; c0 += kIndexThreads) {
         const int i = c0 + tid;
-        int valid = 0;
+        int cnt = 0;
         if (i < total) {
             const int b = i / N;
             const int A = anchors[i];
             const bool kp = keep[i] != 0;
-            valid = (kp && A >= 0 && A <= S - 2) ? 1 : 0;
+            const bool valid = kp && A >= 0 && A <= S - 2;
             if (kp && !valid) atomicMin(&bad_s, i);
+            if (valid) atomicAdd(&kept_s, 1);
             // §6 eval_mask: A+k+1 < S, loss_mask[A+k+1] (position S-1 read
             // as 0), prefix cumprod along the block
-            bool on = valid != 0;
+            bool on = valid;
             for (int k = 0; k < kBlock; ++k) {
                 const long long p = (long long)A + k + 1;
                 on = on && p < S - 1 && loss_mask[(size_t)b * S + p] != 0;
                 emask[(size_t)i * kBlock + k] = on ? 1 : 0;
+                cnt += on ? 1 : 0;
             }
         }
-        // exclusive scan of `valid` over the workgroup
-        int incl = valid;
+        // exclusive scan of the counted steps over the workgroup
+        int incl = cnt;
         for (int o = 1; o < 64; o <<= 1) {
             const int t = __shfl_up(incl, o);
             if (lane >= o) incl += t;
@@ -144,36 +154,42 @@ __global__ __launch_bounds__(kIndexThreads) void loss_index_kernel(
             if (j < w) before += wsum[j];
             all += wsum[j];
         }
-        const int slot = before + incl - valid;
+        const int row0 = before + incl - cnt;
         if (i < total) {
-            blk_slot[i] = valid ? slot : -1;
-            if (valid && slot < cap) slot_blk[slot] = i;
+            for (int k = 0; k < kBlock; ++k) {
+                const int row = row0 + k;
+                const bool here = k < cnt && row < cap_rows;
+                step_row[(size_t)i * kBlock + k] = here ? row : -1;
+                if (here) row_step[row] = i * kBlock + k;
+            }
         }
         __syncthreads();                       // wsum and base_s are reused
         if (tid == 0) base_s += all;
         __syncthreads();
     }
-    const int kept = base_s;
-    for (int j = kept + tid; j < cap; j += kIndexThreads) slot_blk[j] = -1;
+    const int counted = base_s;
+    for (int j = counted + tid; j < cap_rows; j += kIndexThreads) row_step[j] = -1;
     if (tid == 0) {
-        status[kLsKept] = kept;
+        status[kLsKept] = kept_s;
         status[kLsFirstBad] = bad_s == INT_MAX ? -1 : bad_s;
-        status[kLsOverflow] = kept > cap ? 1 : 0;
+        status[kLsOverflow] = counted > cap_rows ? 1 : 0;
         status[kLsBadToken] = 0;
+        status[kLsCounted] = counted;
     }
 }
 
-// ---- gather: xd[row] = [H^(L)[b, 5n+k] ; markov_w1[x_{A+k}]], xt[row] =
-// z[b, A+k] (A+k clamped to S-1: such steps are outside the eval mask).
-// Rows of empty slots are zero.  One workgroup per row.
+// ---- gather: for the row of step (b, n, k): xd[row] = [H^(L)[b, 5n+k] ;
+// markov_w1[x_{A+k}]], xt[row] = [z[b, A+k] ; 0] (A+k <= S-2 for a counted
+// step).  Rows past the last counted step are zero.  One workgroup per row.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void loss_gather_kernel(
-    int S, int N, int V, int d, int r, const int32_t* __restrict__ slot_blk,
+    int S, int N, int V, int d, int r, const int32_t* __restrict__ row_step,
     const int32_t* __restrict__ anchors, const int32_t* __restrict__ ids,
     const T* __restrict__ h_final, const T* __restrict__ z, const T* __restrict__ w_m1,
     T* __restrict__ xd, T* __restrict__ xt, int32_t* __restrict__ status) {
-    const int row = blockIdx.x, j = row / kBlock, k = row % kBlock;
-    const int blk = slot_blk[j];
+    const int row = blockIdx.x;
+    const int step = row_step[row];
+    const int blk = step < 0 ? -1 : step / kBlock, k = step < 0 ? 0 : step % kBlock;
     T* xdr = xd + (size_t)row * (d + r);
     T* xtr = xt + (size_t)row * (d + r);     // [z | 0]: the Markov columns are 0
     constexpr int E = VEC ? 16 / (int)sizeof(T) : 1;    // elements per copy
@@ -205,10 +221,7 @@ __global__ __launch_bounds__(256) void loss_gather_kernel(
     copy(xtr, z + ((size_t)b * S + pos) * d, d);
 }
 
-__device__ inline bool row_live(int row, const int32_t* slot_blk, const uint8_t* emask) {
-    const int blk = slot_blk[row / kBlock];
-    return blk >= 0 && emask[(size_t)blk * kBlock + row % kBlock] != 0;
-}
+__device__ inline bool row_live(int row, const int32_t* row_step) { return row_step[row] >= 0; }
 
 // Loads this thread's values of a kChunk-column chunk [v0, v1) of a row
 // (-inf outside it).
@@ -255,11 +268,11 @@ __device__ inline float2 block_reduce2(float a, float b, float2* red) {
 // ---- stats: per (row, chunk): {max L, sum exp(L - max), max T, sum exp(T - max)}
 template <bool VEC>
 __global__ __launch_bounds__(kStatThreads) void loss_stats_kernel(
-    int V, int C, const int32_t* __restrict__ slot_blk, const uint8_t* __restrict__ emask,
+    int V, int C, const int32_t* __restrict__ row_step,
     const float* __restrict__ ld, const float* __restrict__ lt, float4* __restrict__ part) {
     __shared__ float2 red[kStatThreads / 64];
     const int row = blockIdx.x / C, c = blockIdx.x % C;
-    if (!row_live(row, slot_blk, emask)) return;
+    if (!row_live(row, row_step)) return;
     const int v0 = c * kChunk, v1 = min(V, v0 + kChunk);
     float x[kPerThread], y[kPerThread];
     load_chunk<VEC>(ld + (size_t)row * V, v0, v1, x);
@@ -304,13 +317,13 @@ __device__ inline float2 row_lse(const float4* __restrict__ p, int C) {
 // ---- l1: per (row, chunk): sum over the chunk of |p - q|
 template <bool VEC>
 __global__ __launch_bounds__(kStatThreads) void loss_l1_kernel(
-    int V, int C, const int32_t* __restrict__ slot_blk, const uint8_t* __restrict__ emask,
+    int V, int C, const int32_t* __restrict__ row_step,
     const float* __restrict__ ld, const float* __restrict__ lt, const float4* __restrict__ part,
     float* __restrict__ l1p) {
     __shared__ float2 red[kStatThreads / 64];
     __shared__ float2 lse_s;
     const int row = blockIdx.x / C, c = blockIdx.x % C;
-    if (!row_live(row, slot_blk, emask)) return;
+    if (!row_live(row, row_step)) return;
     const int v0 = c * kChunk, v1 = min(V, v0 + kChunk);
     float x[kPerThread], y[kPerThread];
     load_chunk<VEC>(ld + (size_t)row * V, v0, v1, x);
@@ -332,7 +345,7 @@ __global__ __launch_bounds__(kStatThreads) void loss_l1_kernel(
 // ---- terms: one wave per step (b, n, k)
 template <typename T>
 __global__ __launch_bounds__(256) void loss_terms_kernel(
-    int S, int N, int V, int d, int r, int C, int cap, const int32_t* __restrict__ blk_slot,
+    int S, int N, int V, int d, int r, int C, const int32_t* __restrict__ step_row,
     const int32_t* __restrict__ anchors, const uint8_t* __restrict__ keep,
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ emask,
     const float4* __restrict__ part, const float* __restrict__ l1p, const float* __restrict__ ld,
@@ -350,7 +363,7 @@ __global__ __launch_bounds__(256) void loss_terms_kernel(
     if (overflow || bad) {
         ce = l1 = cf = bce = NAN;
     } else if (kp && emask[p]) {
-        const int row = blk_slot[blk] * kBlock + k;   // slot < cap: no overflow
+        const int row = step_row[p];                 // a counted step has a row (no overflow)
         const float2 lse = row_lse(part + (size_t)row * C, C);
         float s = 0.f;
         for (int c = lane; c < C; c += 64) s += l1p[(size_t)row * C + c];
@@ -434,12 +447,13 @@ const char* check_desc(const dspark_loss_desc* d) {
     if (d->vocab < 1 || d->hidden < 1 || d->markov_rank < 1)
         return "vocab, hidden and markov_rank must be >= 1";
     if (d->dtype != DSPARK_BF16 && d->dtype != DSPARK_F32) return "dtype must be DSPARK_BF16 or DSPARK_F32";
-    if (d->max_kept_blocks < 0) return "max_kept_blocks must be >= 0";
+    if (d->max_kept_blocks < 0 || d->max_counted_steps < 0)
+        return "max_kept_blocks and max_counted_steps must be >= 0";
     if ((d->w_lm_ld != 0 && d->w_lm_ld < d->hidden) || (d->w_m2_ld != 0 && d->w_m2_ld < d->markov_rank))
         return "w_lm_ld / w_m2_ld must be 0 or at least hidden / markov_rank";
     if ((long long)d->B * d->N * kBlock > INT_MAX / 4) return "B * N too large";
     if ((long long)d->B * d->S > INT_MAX) return "B * S too large";
-    const long long rows = (long long)kBlock * loss_cap(*d);
+    const long long rows = loss_rows(*d);
     const long long C = (d->vocab + kChunk - 1) / kChunk;
     if (rows * C > INT_MAX) return "rows x vocabulary chunks exceeds the grid limit";
     if ((long long)d->hidden + d->markov_rank > INT_MAX / 2) return "hidden + markov_rank too large";
@@ -490,8 +504,8 @@ dspark_status loss_fwd(const dspark_loss_desc* desc, const int32_t* ids, const u
     const int n_pos = B * N * kBlock;
     char* base = static_cast<char*>(workspace);
     int32_t* status = reinterpret_cast<int32_t*>(base + L.status);
-    int32_t* slot_blk = reinterpret_cast<int32_t*>(base + L.slot_blk);
-    int32_t* blk_slot = reinterpret_cast<int32_t*>(base + L.blk_slot);
+    int32_t* row_step = reinterpret_cast<int32_t*>(base + L.row_step);
+    int32_t* step_row = reinterpret_cast<int32_t*>(base + L.step_row);
     void* xd = base + L.xd;
     void* xt = base + L.xt;
     float* ld = reinterpret_cast<float*>(base + L.ld);
@@ -522,14 +536,14 @@ dspark_status loss_fwd(const dspark_loss_desc* desc, const int32_t* ids, const u
         }
     }
     LS_HIP(mark(), "hipEventRecord");
-    hipLaunchKernelGGL(loss_index_kernel, dim3(1), dim3(kIndexThreads), 0, s, B, S, N, L.cap,
-                       anchors, keep, lmask, status, slot_blk, blk_slot, emask);
+    hipLaunchKernelGGL(loss_index_kernel, dim3(1), dim3(kIndexThreads), 0, s, B, S, N, L.rows,
+                       anchors, keep, lmask, status, row_step, step_row, emask);
     LS_HIP(hipGetLastError(), "index launch");
     if (rows > 0) {
         const bool vec = ((size_t)hd * (bf ? 2 : 4)) % 16 == 0 && ((size_t)rk * (bf ? 2 : 4)) % 16 == 0;
 #define LS_GATHER(T, V_)                                                                      \
     hipLaunchKernelGGL((loss_gather_kernel<T, V_>), dim3(rows), dim3(256), 0, s, S, N, V, hd, rk, \
-                       slot_blk, anchors, ids, (const T*)h_final, (const T*)z, (const T*)w_m1,    \
+                       row_step, anchors, ids, (const T*)h_final, (const T*)z, (const T*)w_m1,    \
                        (T*)xd, (T*)xt, status)
         if (bf) {
             if (vec) LS_GATHER(bf16, true); else LS_GATHER(bf16, false);
@@ -583,20 +597,20 @@ dspark_status loss_fwd(const dspark_loss_desc* desc, const int32_t* ids, const u
     if (rows > 0) {
         if (v4)
             hipLaunchKernelGGL(loss_stats_kernel<true>, dim3(rows * C), dim3(kStatThreads), 0, s, V, C,
-                               slot_blk, emask, ld, lt, part);
+                               row_step, ld, lt, part);
         else
             hipLaunchKernelGGL(loss_stats_kernel<false>, dim3(rows * C), dim3(kStatThreads), 0, s, V,
-                               C, slot_blk, emask, ld, lt, part);
+                               C, row_step, ld, lt, part);
         LS_HIP(hipGetLastError(), "stats launch");
     }
     LS_HIP(mark(), "hipEventRecord");
     if (rows > 0) {
         if (v4)
             hipLaunchKernelGGL(loss_l1_kernel<true>, dim3(rows * C), dim3(kStatThreads), 0, s, V, C,
-                               slot_blk, emask, ld, lt, part, l1p);
+                               row_step, ld, lt, part, l1p);
         else
             hipLaunchKernelGGL(loss_l1_kernel<false>, dim3(rows * C), dim3(kStatThreads), 0, s, V, C,
-                               slot_blk, emask, ld, lt, part, l1p);
+                               row_step, ld, lt, part, l1p);
         LS_HIP(hipGetLastError(), "l1 launch");
     }
     LS_HIP(mark(), "hipEventRecord");
@@ -604,11 +618,11 @@ dspark_status loss_fwd(const dspark_loss_desc* desc, const int32_t* ids, const u
         const int grid = (n_pos + 3) / 4;
         if (bf)
             hipLaunchKernelGGL(loss_terms_kernel<bf16>, dim3(grid), dim3(256), 0, s, S, N, V, hd, rk, C,
-                               L.cap, blk_slot, anchors, keep, ids, emask, part, l1p, ld,
+                               step_row, anchors, keep, ids, emask, part, l1p, ld,
                                (const bf16*)xd, (const bf16*)w_conf, status, terms, n_pos);
         else
             hipLaunchKernelGGL(loss_terms_kernel<float>, dim3(grid), dim3(256), 0, s, S, N, V, hd, rk,
-                               C, L.cap, blk_slot, anchors, keep, ids, emask, part, l1p, ld,
+                               C, step_row, anchors, keep, ids, emask, part, l1p, ld,
                                (const float*)xd, (const float*)w_conf, status, terms, n_pos);
         LS_HIP(hipGetLastError(), "terms launch");
     }
@@ -667,9 +681,11 @@ dspark_status dspark_loss_tune(const dspark_loss_desc* desc, const int32_t* inpu
 }
 
 dspark_status dspark_loss_read_status(const void* workspace, void* stream,
-                                      int32_t* first_bad_block, int32_t* kept_blocks) {
+                                      int32_t* first_bad_block, int32_t* kept_blocks,
+                                      int32_t* counted_steps) {
     if (first_bad_block) *first_bad_block = -1;
     if (kept_blocks) *kept_blocks = 0;
+    if (counted_steps) *counted_steps = 0;
     if (!workspace) return lsfail(DSPARK_EWORKSPACE, "workspace is NULL");
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipStreamSynchronize(s);
@@ -681,13 +697,14 @@ dspark_status dspark_loss_read_status(const void* workspace, void* stream,
     }
     if (first_bad_block) *first_bad_block = w[kLsFirstBad];
     if (kept_blocks) *kept_blocks = w[kLsKept];
+    if (counted_steps) *counted_steps = w[kLsCounted];
     set_last_error("");
     if (w[kLsFirstBad] >= 0) {
         snprintf(t_msg, sizeof(t_msg), "kept block %d has an anchor outside [0, S-2]", w[kLsFirstBad]);
         return lsfail(DSPARK_EANCHOR, t_msg);
     }
     if (w[kLsOverflow]) {
-        snprintf(t_msg, sizeof(t_msg), "%d kept blocks exceed max_kept_blocks", w[kLsKept]);
+        snprintf(t_msg, sizeof(t_msg), "%d counted steps exceed the row bound", w[kLsCounted]);
         return lsfail(DSPARK_ECAPACITY, t_msg);
     }
     if (w[kLsBadToken]) return lsfail(DSPARK_EINVAL, "a token id read by the loss lies outside [0, V)");

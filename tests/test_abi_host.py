@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert set(sd.EXPORTS) == declared
-    assert sd.abi_version() == 8
+    assert sd.abi_version() == 9
 
 
 def glm_desc(**kw):
@@ -305,7 +305,7 @@ def test_layer_null_misaligned_and_workspace_errors_before_any_launch():
 
 
 def test_loss_desc_layout_and_workspace():
-    assert ctypes.sizeof(sd.LossDesc) == 8 * 4 + 3 * 8 + 8
+    assert ctypes.sizeof(sd.LossDesc) == 8 * 4 + 3 * 8 + 8 + 8
     d = sd.make_loss_desc(B=1, S=32768, N=1024, vocab=154880, hidden=6144, markov_rank=256)
     need = sd.loss_workspace_size(d)
     rows = 5 * 1024
@@ -313,12 +313,15 @@ def test_loss_desc_layout_and_workspace():
     gathered = 2 * rows * (6144 + 256) * 2
     stats = rows * 19 * (16 + 4)
     assert logits + gathered + stats <= need < logits + gathered + stats + 2**20
-    # max_kept_blocks shrinks every row-sized buffer
+    # max_kept_blocks and max_counted_steps shrink every row-sized buffer
     d2 = sd.make_loss_desc(B=1, S=32768, N=1024, vocab=154880, hidden=6144, markov_rank=256,
                            max_kept_blocks=768)
     assert abs(sd.loss_workspace_size(d2) - need * 768 / 1024) < 2**20
+    d3 = sd.make_loss_desc(B=1, S=32768, N=1024, vocab=154880, hidden=6144, markov_rank=256,
+                           max_kept_blocks=768, max_counted_steps=2560)
+    assert abs(sd.loss_workspace_size(d3) - need * 2560 / 5120) < 2**20
     for kw in (dict(vocab=0), dict(hidden=0), dict(markov_rank=0), dict(max_kept_blocks=-1),
-               dict(S=0), dict(w_lm_ld=7), dict(w_m2_ld=3)):
+               dict(S=0), dict(w_lm_ld=7), dict(w_m2_ld=3), dict(max_counted_steps=-1)):
         args = dict(B=1, S=64, N=4, vocab=100, hidden=8, markov_rank=4)
         args.update(kw)
         bad = sd.make_loss_desc(**args)

@@ -31,7 +31,7 @@ MEAN_REL = 1e-5
 
 
 def run_loss(wl, lh, anchors, keep, max_kept=0, tune=False, loss_mask=None, ws=None,
-             layout="dense"):
+             layout="dense", max_counted=0):
     """layout: "dense" weights, "fused" (lm_head and markov_w2 side by side in
     one [V, d + r] array: the one-GEMM path), "strided" (padded rows, apart)."""
     import torch
@@ -54,7 +54,8 @@ def run_loss(wl, lh, anchors, keep, max_kept=0, tune=False, loss_mask=None, ws=N
         t["w_lm"], t["w_m2"] = to_torch(a, lh.dtype, "cuda"), to_torch(m, lh.dtype, "cuda")
         lds = (d_ + pad, r_ + pad)
     d = sd.make_loss_desc(wl.B, wl.S, wl.N, lh.vocab, lh.hidden, lh.rank, dtype=lh.dtype,
-                          max_kept_blocks=max_kept, w_lm_ld=lds[0], w_m2_ld=lds[1])
+                          max_kept_blocks=max_kept, w_lm_ld=lds[0], w_m2_ld=lds[1],
+                          max_counted_steps=max_counted)
     if ws is None:
         ws = torch.empty(sd.loss_workspace_size(d), dtype=torch.uint8, device="cuda")
     terms = torch.full((4, wl.B, wl.N, 5), 12345.0, dtype=torch.float32, device="cuda")
@@ -115,16 +116,23 @@ def test_loss_glm_width_bf16(V):
     check(f"bf16 V={V}", terms, em, loss, O.loss_head(lh, wl.loss_mask, wl.anchors, wl.keep))
 
 
-def test_loss_max_kept_blocks_exact_and_overflow():
+def test_loss_row_bounds_exact_and_overflow():
+    """max_kept_blocks = the kept count, and max_counted_steps = the counted
+    steps (read back from the status area): the oracle's result; one row
+    fewer than the counted steps: every output NaN and DSPARK_ECAPACITY."""
+    import speculative_decoding_draft_amd as sd
     wl, lh = small(45, B=2, N=8, S=96, dtype="bf16", V=1000, d=64, r=16)
     kept = int(wl.keep.sum())
     ref = O.loss_head(lh, wl.loss_mask, wl.anchors, wl.keep)
     terms, em, loss, st, _ = run_loss(wl, lh, wl.anchors, wl.keep, max_kept=kept)
-    assert st[0] == 0 and st[2] == kept
+    assert st[0] == 0 and st[2] == kept and st[3] == ref["count"]
     check("max_kept_blocks = kept", terms, em, loss, ref)
-    import speculative_decoding_draft_amd as sd
-    terms, em, loss, st, _ = run_loss(wl, lh, wl.anchors, wl.keep, max_kept=kept - 1)
-    assert st[0] == sd.DSPARK_ECAPACITY and st[2] == kept
+    counted = st[3]
+    terms, em, loss, st, _ = run_loss(wl, lh, wl.anchors, wl.keep, max_counted=counted)
+    assert st[0] == 0
+    check("max_counted_steps = counted", terms, em, loss, ref)
+    terms, em, loss, st, _ = run_loss(wl, lh, wl.anchors, wl.keep, max_counted=counted - 1)
+    assert st[0] == sd.DSPARK_ECAPACITY and st[3] == counted
     assert np.all(np.isnan(terms)) and np.all(np.isnan(loss[:4]))
 
 
@@ -191,8 +199,10 @@ def test_loss_headline_size_sampled_blocks():
     wl = wk.config(4, tensors=False)
     lh = wk.make_loss_inputs(wl, 154880, 6144, 256, seed=9)
     kept = int(wl.keep.sum())
-    terms, em, loss, st, _ = run_loss(wl, lh, wl.anchors, wl.keep, max_kept=kept)
-    assert st[0] == 0 and st[2] == kept
+    counted = int(O.eval_mask(wl.loss_mask, wl.anchors, wl.keep).sum())
+    terms, em, loss, st, _ = run_loss(wl, lh, wl.anchors, wl.keep, max_kept=kept,
+                                      max_counted=counted)
+    assert st[0] == 0 and st[2] == kept and st[3] == counted
     ks = [n for n in range(wl.N) if wl.keep[0, n]]
     low = [n for n in ks if wl.anchors[0, n] in (0, 1, 126)]
     rng = np.random.default_rng(3)
