@@ -255,6 +255,26 @@ def bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sp
                            "traffic": bwd_measured_traffic(dom, wl.name),
                            "avg_launch_us": round(stage_us[dom], 2),
                            "algorithmic_bytes_per_launch": nb[dom]}
+    # a training step: the forward on the backward's workspace, then the
+    # backward reusing its index and q_abs
+    fout = torch.empty((B, L5, H, wl.d_v), dtype=torch.bfloat16, device="cuda")
+    fargs = args[:11] + (fout, ws)
+    for _ in range(3):
+        sd.attn_fwd(*fargs, stream=sptr)
+        sd.attn_bwd(*args, stream=sptr, reuse_forward=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sd.attn_fwd(*fargs, stream=sptr)
+        sd.attn_bwd(*args, stream=sptr, reuse_forward=True)
+    torch.cuda.synchronize()
+    step = (time.perf_counter() - t0) / steps
+    fflop = useful_flop(anchors, keep, wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v)
+    out["train_step"] = {"what": "dspark_attn_fwd then dspark_attn_bwd on one workspace "
+                                 "(reuse_forward: no index rebuild, no q_abs recompute)",
+                         "ms_per_step": round(step * 1e3, 4),
+                         "useful_gflop_per_step": round((flop + fflop) / 1e9, 3),
+                         "value": round((flop + fflop) / step / 1e12, 3), "unit": "TFLOP/s"}
     return out
 
 

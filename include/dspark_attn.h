@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 9
+#define DSPARK_ABI_VERSION 10
 
 typedef enum dspark_status {
     DSPARK_OK = 0,
@@ -146,6 +146,13 @@ typedef struct dspark_attn_opts {
      * during the call.  aux_stream must not be `stream`. */
     void* aux_stream;
     void* aux_events[2];
+    /* dspark_attn_bwd_ex only, nonzero: the workspace was last used by
+     * dspark_attn_fwd(_ex) with the same descriptor, inputs, anchors and keep
+     * and the same force_generic, and nothing else has written it since (a
+     * training step runs the forward on the backward's workspace: its
+     * layout begins with the forward's).  The backward then reuses the
+     * forward's block index and q_abs instead of rebuilding them. */
+    int32_t reuse_forward;
 } dspark_attn_opts;
 
 /* Launch plan of dspark_attn_fwd_ex for (desc, opts) (opts may be NULL):

@@ -86,7 +86,7 @@ class Opts(ctypes.Structure):
     _fields_ = [("stage_events", ctypes.POINTER(ctypes.c_void_p)),
                 ("n_stage_events", ctypes.c_int32), ("force_generic", ctypes.c_int32),
                 ("chunk_blocks", ctypes.c_int32), ("aux_stream", ctypes.c_void_p),
-                ("aux_events", ctypes.c_void_p * 2)]
+                ("aux_events", ctypes.c_void_p * 2), ("reuse_forward", ctypes.c_int32)]
 
 
 def _load():
@@ -317,19 +317,22 @@ BWD_GRADS = ("dq_nope", "dq_rope", "dckv_ctx", "dkr_ctx", "dckv_blk", "dkr_blk",
 
 def attn_bwd(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
              anchors, keep, dout, grads, workspace, stream=None,
-             stage_events: Optional[Sequence[int]] = None, force_generic: bool = False) -> None:
+             stage_events: Optional[Sequence[int]] = None, force_generic: bool = False,
+             reuse_forward: bool = False) -> None:
     """dspark_attn_bwd / dspark_attn_bwd_ex.  grads: a mapping with the
     output tensors named as in BWD_GRADS; raises DSparkError on a non-OK
-    status."""
+    status.  reuse_forward: the workspace holds the forward's index and q_abs
+    (see dspark_attn_opts)."""
     args = [ctypes.byref(desc)] + [_ptr(t) for t in (q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk,
                                                      kr_blk, w_uk, w_uv, anchors, keep, dout)]
     args += [_ptr(grads[k]) for k in BWD_GRADS]
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args += [_ptr(workspace), ws_bytes, _stream(stream)]
-    if stage_events is None and not force_generic:
+    if stage_events is None and not force_generic and not reuse_forward:
         _check(lib.dspark_attn_bwd(*args))
         return
     opts, _arr = _opts(stage_events, force_generic, 0)
+    opts.reuse_forward = 1 if reuse_forward else 0
     _check(lib.dspark_attn_bwd_ex(*args, ctypes.byref(opts)))
 
 

@@ -398,14 +398,26 @@ dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc, const void* q_nop
     if ((e = mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
     size_t zero_n = L.acc_rows * size_t(d.d_latent + d.d_rope);
     if (!fast) zero_n = (L.total - L.acc) / 4;     // accumulators, then the weight ones
-    DSPARK_STEP(launch_prep(p, anchors, keep, w.fwd, nullptr, L.fwd.rope_rows,
-                            fast ? nullptr : &theta, nullptr, s),
-                "index launch");
+    // reuse_forward: the forward on this workspace left the index (and, on the
+    // MFMA path, q_abs) in the same places; those launches are skipped (their
+    // stage events are still recorded)
+    const bool reuse = opts && opts->reuse_forward;
+    if (reuse) {
+        if ((e = mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    } else {
+        DSPARK_STEP(launch_prep(p, anchors, keep, w.fwd, nullptr, L.fwd.rope_rows,
+                                fast ? nullptr : &theta, nullptr, s),
+                    "index launch");
+    }
     if (fast) DSPARK_STEP(launch_bwd_order(p, w, s), "anchor-order launch");
     DSPARK_STEP(launch_bwd_zero(w.acc, zero_n, fast ? w.fwd.status + kStUnsorted : nullptr, s),
                 "accumulator clear launch");
     if (fast) {
-        DSPARK_STEP(launch_absorb(p, in, w.fwd, Chunk{0, d.B * d.N}, s), "absorb launch");
+        if (reuse) {
+            if ((e = mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        } else {
+            DSPARK_STEP(launch_absorb(p, in, w.fwd, Chunk{0, d.B * d.N}, s), "absorb launch");
+        }
         DSPARK_STEP(launch_absorb_dv(p, dout, w_uv, w.fwd, w.dolat, s), "W_UV^T dout launch");
         DSPARK_STEP(launch_bwd_attn(p, in, g, w, theta, s), "backward attention launch");
         DSPARK_STEP(launch_bwd_dkv(p, w, s), "dc^KV launch");

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert set(sd.EXPORTS) == declared
-    assert sd.abi_version() == 9
+    assert sd.abi_version() == 10
 
 
 def glm_desc(**kw):
@@ -131,8 +131,9 @@ def test_mfma_path_needs_32bit_offsets():
 
 def test_opts_struct_matches_header():
     """The binding's dspark_attn_opts has the header's layout (x86-64)."""
-    assert ctypes.sizeof(sd._lib.Opts) == 8 + 4 * 3 + 4 + 8 + 16
+    assert ctypes.sizeof(sd._lib.Opts) == 8 + 4 * 3 + 4 + 8 + 16 + 8
     assert sd._lib.Opts.aux_stream.offset == 24 and sd._lib.Opts.aux_events.offset == 32
+    assert sd._lib.Opts.reuse_forward.offset == 48
 
 
 def test_aux_stream_is_validated():

@@ -235,3 +235,44 @@ def test_bwd_sorted_path_is_deterministic():
     b = run.run().result()
     for k in GRADS:
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_bwd_reusing_the_forward_workspace_is_bit_identical(generic):
+    """A training step: the forward on the backward's workspace, then the
+    backward with reuse_forward (no index build, no q_abs recompute) gives
+    the same bits as a backward on its own (the generic path sums context
+    rows with atomics, so there the order of additions may differ: fp32
+    rounding only)."""
+    import torch
+    import speculative_decoding_draft_amd as sd
+    wl = wk.config(1) if generic else wk.scaled(4, S=700, N=24)
+    t = upload_layer(wl)
+    a, k = upload_anchors(wl.anchors, wl.keep)
+    desc = desc_for(wl)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dout_np = wk.make_dout(wl, seed=11)
+    dout = torch.from_numpy(dout_np)
+    dout = (dout.view(torch.bfloat16) if wl.dtype == "bf16" else dout).cuda()
+    B, S, L5, H = wl.B, wl.S, wl.q_len, wl.H
+    shapes = {"dq_nope": (B, L5, H, wl.d_c), "dq_rope": (B, L5, H, wl.d_r),
+              "dckv_ctx": (B, S, wl.D), "dkr_ctx": (B, S, wl.d_r),
+              "dckv_blk": (B, L5, wl.D), "dkr_blk": (B, L5, wl.d_r),
+              "dw_uk": (H, wl.d_c, wl.D), "dw_uv": (H, wl.d_v, wl.D)}
+    ws = torch.empty(sd.bwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    ins = (t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"], t["kr_blk"],
+           t["w_uk"], t["w_uv"], a, k)
+    plain = {n: torch.full(v, float("nan"), dtype=tdt, device="cuda") for n, v in shapes.items()}
+    sd.attn_bwd(desc, *ins, dout, plain, ws, force_generic=generic)
+    ws.fill_(0x7f)                              # nothing left over from the plain call
+    out = torch.empty((B, L5, H, wl.d_v), dtype=tdt, device="cuda")
+    sd.attn_fwd(desc, *ins, out, ws, force_generic=generic)
+    reuse = {n: torch.full(v, float("nan"), dtype=tdt, device="cuda") for n, v in shapes.items()}
+    sd.attn_bwd(desc, *ins, dout, reuse, ws, force_generic=generic, reuse_forward=True)
+    torch.cuda.synchronize()
+    for n in shapes:
+        if generic:
+            x, y = plain[n].double(), reuse[n].double()
+            assert float((x - y).norm() / y.norm()) < 1e-6, n
+        else:
+            assert torch.equal(plain[n], reuse[n]), n
