@@ -27,8 +27,11 @@
  *   - all tensor pointers are DEVICE pointers to contiguous row-major data,
  *     16-byte aligned, unless the comment says "host";
  *   - the caller owns every buffer, including the workspace; the library
- *     allocates and frees nothing and keeps no mutable global state, so calls
- *     on different streams with different workspaces are independent;
+ *     allocates and frees no device memory of its own, so calls on different
+ *     streams with different workspaces are independent.  The exceptions are
+ *     named where they apply: the MLA block and the loss head create one
+ *     rocBLAS handle per host thread and device on first use, and the
+ *     *_tune calls record GEMM kernel choices in a process-wide table;
  *   - `stream` is a hipStream_t (NULL = the default stream); device work is
  *     enqueued asynchronously and DSPARK_OK means "enqueued";
  *   - no C++ exception crosses the ABI; on error the function returns a
