@@ -154,7 +154,8 @@ typedef struct dspark_attn_opts {
      * and the same force_generic, and nothing else has written it since (a
      * training step runs the forward on the backward's workspace: its
      * layout begins with the forward's).  The backward then reuses the
-     * forward's block index and q_abs instead of rebuilding them. */
+     * forward's block index, q_abs and o_lat instead of rebuilding them
+     * (dW_UV then uses the forward's o_lat rows). */
     int32_t reuse_forward;
 } dspark_attn_opts;
 

@@ -419,7 +419,7 @@ dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc, const void* q_nop
             DSPARK_STEP(launch_absorb(p, in, w.fwd, Chunk{0, d.B * d.N}, s), "absorb launch");
         }
         DSPARK_STEP(launch_absorb_dv(p, dout, w_uv, w.fwd, w.dolat, s), "W_UV^T dout launch");
-        DSPARK_STEP(launch_bwd_attn(p, in, g, w, theta, s), "backward attention launch");
+        DSPARK_STEP(launch_bwd_attn(p, in, g, w, theta, s, !reuse), "backward attention launch");
         DSPARK_STEP(launch_bwd_dkv(p, w, s), "dc^KV launch");
         DSPARK_STEP(launch_bwd_dqnope(p, in, g, w, s), "dq^C launch");
         DSPARK_STEP(launch_bwd_dw(p, in, g, w, s), "weight-gradient launch");

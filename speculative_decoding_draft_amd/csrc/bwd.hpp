@@ -121,7 +121,7 @@ hipError_t launch_bwd_finalize(const Problem& p, bool bf16_io, const BwdGrads& g
 hipError_t launch_absorb_dv(const Problem& p, const void* dout, const void* w_uv,
                             const Workspace& ws, bf16* dolat, hipStream_t s);
 hipError_t launch_bwd_attn(const Problem& p, const Inputs& in, const BwdGrads& g,
-                           const BwdWork& w, const RopeTheta& th, hipStream_t s);
+                           const BwdWork& w, const RopeTheta& th, hipStream_t s, bool write_olat);
 hipError_t launch_bwd_dkv(const Problem& p, const BwdWork& w, hipStream_t s);
 hipError_t launch_bwd_dqnope(const Problem& p, const Inputs& in, const BwdGrads& g,
                              const BwdWork& w, hipStream_t s);

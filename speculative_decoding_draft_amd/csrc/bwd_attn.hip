@@ -41,6 +41,7 @@ __device__ inline bf16x4 fresh(bf16x4 v) {
     return __builtin_bit_cast(bf16x4, u);
 }
 
+template <bool WRITE_OLAT>
 __global__ __launch_bounds__(kThreads) void bwd_attn_kernel(
     const bf16* __restrict__ q_rope, const bf16* __restrict__ ckv_ctx,
     const bf16* __restrict__ kr_ctx, const bf16* __restrict__ ckv_blk,
@@ -335,7 +336,10 @@ __global__ __launch_bounds__(kThreads) void bwd_attn_kernel(
             }
         }
     };
-    ct_pass(pr, inv, o_lat);
+    // o_lat feeds only dW_UV; without WRITE_OLAT the forward's rows, already
+    // in the workspace, serve instead (a separate instantiation: a runtime
+    // branch here costs registers)
+    if constexpr (WRITE_OLAT) ct_pass(pr, inv, o_lat);
 
     // ---- dP (transposed, keys x rows) = C . d_olat over the 16 latent k-steps
 #pragma unroll
@@ -463,14 +467,15 @@ __global__ __launch_bounds__(kThreads) void bwd_attn_kernel(
 }  // namespace
 
 hipError_t launch_bwd_attn(const Problem& p, const Inputs& in, const BwdGrads& g,
-                           const BwdWork& w, const RopeTheta& th, hipStream_t s) {
+                           const BwdWork& w, const RopeTheta& th, hipStream_t s, bool write_olat) {
     const uint32_t ctx_bytes = (uint32_t)((size_t)p.B * p.S * kD * sizeof(bf16));
     const uint32_t blk_bytes = (uint32_t)((size_t)p.B * p.L5 * kD * sizeof(bf16));
     RopeTheta turns{};
     for (int k = 0; k < kDr / 2; ++k) turns.t[k] = th.t[k] * 0.15915494309189533577;  // 1 / 2pi
     int grid = p.B * p.N;
     grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL(bwd_attn_kernel, dim3(grid), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(write_olat ? bwd_attn_kernel<true> : bwd_attn_kernel<false>, dim3(grid),
+                       dim3(kThreads), 0, s,
                        (const bf16*)in.q_rope, (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
                        (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, w.fwd.srec, w.fwd.status,
                        w.fwd.qabs, w.dolat, w.fwd.olat, w.dqabs, w.qrot, w.pmat, w.dsmat,

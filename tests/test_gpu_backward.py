@@ -240,10 +240,11 @@ def test_bwd_sorted_path_is_deterministic():
 @pytest.mark.parametrize("generic", [False, True])
 def test_bwd_reusing_the_forward_workspace_is_bit_identical(generic):
     """A training step: the forward on the backward's workspace, then the
-    backward with reuse_forward (no index build, no q_abs recompute) gives
-    the same bits as a backward on its own (the generic path sums context
-    rows with atomics, so there the order of additions may differ: fp32
-    rounding only)."""
+    backward with reuse_forward (no index build, no q_abs recompute, the
+    forward's o_lat for dW_UV) gives the same bits as a backward on its own,
+    except dW_UV on the MFMA path (the forward's o_lat rows against the
+    backward's own recomputation: bf16 rounding of o_lat at most) and the
+    generic path (context sums by atomics: fp32 rounding only)."""
     import torch
     import speculative_decoding_draft_amd as sd
     wl = wk.config(1) if generic else wk.scaled(4, S=700, N=24)
@@ -271,8 +272,10 @@ def test_bwd_reusing_the_forward_workspace_is_bit_identical(generic):
     sd.attn_bwd(desc, *ins, dout, reuse, ws, force_generic=generic, reuse_forward=True)
     torch.cuda.synchronize()
     for n in shapes:
+        x, y = plain[n].double(), reuse[n].double()
         if generic:
-            x, y = plain[n].double(), reuse[n].double()
             assert float((x - y).norm() / y.norm()) < 1e-6, n
+        elif n == "dw_uv":
+            assert float((x - y).norm() / y.norm()) < 5e-3, n
         else:
             assert torch.equal(plain[n], reuse[n]), n
