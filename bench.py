@@ -56,9 +56,9 @@ KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.h
 # plain 256 MiB device copy), with the digest of the kernel's sources when the
 # counters were taken.  A kernel whose sources changed since reports null.
 PMC_TRAFFIC = {
-    "absorb": (358_772_932, "1173152b9dfcdc71"),
-    "attention": (583_907_471, "9a8efa059feee454"),
-    "w_uv": (394_468_589, "8759cdadabfffc32"),
+    "absorb": (358_772_658, "1173152b9dfcdc71"),
+    "attention": (583_589_770, "9a8efa059feee454"),
+    "w_uv": (394_468_171, "8759cdadabfffc32"),
 }
 
 
@@ -73,12 +73,12 @@ BWD_KERNEL_SOURCES = {
     "final": ("bwd_misc.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
 }
 BWD_PMC_TRAFFIC = {
-    "attention_bwd": (1_294_632_662, "ba86a7add3441456"),
-    "dw": (753_613_926, "7da7a4cb8373e829"),
-    "dkv": (971_075_413, "7da7a4cb8373e829"),
-    "dq_nope": (447_485_456, "7da7a4cb8373e829"),
-    "d_olat": (394_457_994, "1173152b9dfcdc71"),
-    "final": (311_151_661, "3f5a07842d4ad55c"),
+    "attention_bwd": (1_294_385_046, "e43a3e44ba46d298"),
+    "dw": (754_065_735, "5aa12cb6a28746ad"),
+    "dkv": (971_033_593, "5aa12cb6a28746ad"),
+    "dq_nope": (447_361_885, "5aa12cb6a28746ad"),
+    "d_olat": (394_457_779, "1173152b9dfcdc71"),
+    "final": (311_151_788, "5d5442f7c0774b7c"),
 }
 
 
@@ -200,7 +200,7 @@ def bwd_stage_bytes(wl, anchors, keep):
 
 
 def bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sptr, hip,
-                   steps):
+                   steps, train_step=True):
     """Times dspark_attn_bwd on the same inputs (layer 0) with a seeded
     upstream gradient; per-launch durations from the library's stage events
     on one extra call."""
@@ -255,6 +255,8 @@ def bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sp
                            "traffic": bwd_measured_traffic(dom, wl.name),
                            "avg_launch_us": round(stage_us[dom], 2),
                            "algorithmic_bytes_per_launch": nb[dom]}
+    if not train_step:
+        return out
     # a training step: the forward on the backward's workspace, then the
     # backward reusing its index and q_abs
     fout = torch.empty((B, L5, H, wl.d_v), dtype=torch.bfloat16, device="cuda")
@@ -723,6 +725,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the inference-time drafting measurement (the 'decode' object)")
     ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-train-step", action="store_true",
+                    help="skip the forward + backward training-step timing (for counter runs: "
+                         "its forward calls follow a backward that leaves their inputs cached)")
     ap.add_argument("--no-tune", action="store_true",
                     help="skip the rocBLAS kernel choice of the layer and loss objects (for "
                          "counter runs; their GEMM times are then rocBLAS's defaults')")
@@ -889,7 +894,8 @@ def main():
     if not args.no_bwd and wl.dtype == "bf16":
         try:
             result["backward"] = bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors,
-                                                keep, desc, sptr, hip, args.bwd_steps)
+                                                keep, desc, sptr, hip, args.bwd_steps,
+                                                train_step=not args.no_train_step)
             if not args.no_cpu_baseline:
                 result["backward"]["cpu_baseline"] = bwd_cpu_baseline(wl, anchors, keep,
                                                                        args.side_budget)
