@@ -273,10 +273,34 @@ def bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sp
     step = (time.perf_counter() - t0) / steps
     fflop = useful_flop(anchors, keep, wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v)
     out["train_step"] = {"what": "dspark_attn_fwd then dspark_attn_bwd on one workspace "
-                                 "(reuse_forward: no index rebuild, no q_abs recompute)",
+                                 "(reuse_forward: no index rebuild, no q_abs / o_lat recompute)",
                          "ms_per_step": round(step * 1e3, 4),
                          "useful_gflop_per_step": round((flop + fflop) / 1e9, 3),
                          "value": round((flop + fflop) / step / 1e12, 3), "unit": "TFLOP/s"}
+    # the same step captured once in a HIP graph and replayed
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            sd.attn_fwd(*fargs)
+            sd.attn_bwd(*args, reuse_forward=True)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            sd.attn_fwd(*fargs)
+            sd.attn_bwd(*args, reuse_forward=True)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        gstep = (time.perf_counter() - t0) / steps
+        out["train_step"]["graph_ms_per_step"] = round(gstep * 1e3, 4)
+    except Exception as e:      # the eager figure stands
+        out["train_step"]["graph_error"] = f"{type(e).__name__}: {e}"
     return out
 
 

@@ -408,3 +408,55 @@ def test_nan_in_one_context_row_stays_in_its_windows(sd, force_generic):
         else:
             assert np.array_equal(rows, base[0, 5 * n:5 * n + 5]), n
     log(f"  NaN at context row {p}: {len(hit)} blocks see it, the other {wl.N - len(hit)} unchanged")
+
+
+def test_forward_and_backward_replay_from_a_hip_graph(sd):
+    """The forward and the backward are kernel launches only (no allocation,
+    no memset, no synchronisation), so a caller can capture them in a HIP
+    graph.  Each of three replays, with the program's own eager work and a
+    synchronisation between them, gives the eager call's bits."""
+    import torch
+    from workloads.device import upload_anchors, upload_layer
+    wl = wk.scaled(4, S=700, N=24)
+    t = upload_layer(wl)
+    a, k = upload_anchors(wl.anchors, wl.keep)
+    desc = desc_for(wl)
+    ins = (t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"], t["kr_blk"],
+           t["w_uk"], t["w_uv"], a, k)
+    B, L5, H = wl.B, wl.q_len, wl.H
+    out = torch.empty((B, L5, H, wl.d_v), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(sd.bwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    dout = torch.from_numpy(wk.make_dout(wl, seed=11)).view(torch.bfloat16).cuda()
+    shapes = {"dq_nope": (B, L5, H, wl.d_c), "dq_rope": (B, L5, H, wl.d_r),
+              "dckv_ctx": (B, wl.S, wl.D), "dkr_ctx": (B, wl.S, wl.d_r),
+              "dckv_blk": (B, L5, wl.D), "dkr_blk": (B, L5, wl.d_r),
+              "dw_uk": (H, wl.d_c, wl.D), "dw_uv": (H, wl.d_v, wl.D)}
+    grads = {n: torch.empty(v, dtype=torch.bfloat16, device="cuda") for n, v in shapes.items()}
+
+    def step():
+        sd.attn_fwd(desc, *ins, out, ws)
+        sd.attn_bwd(desc, *ins, dout, grads, ws, reuse_forward=True)
+
+    step()
+    torch.cuda.synchronize()
+    eager = {"out": out.clone(), **{n: g.clone() for n, g in grads.items()}}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):            # warm-up on the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(3):
+        out.fill_(float("nan"))
+        for g in grads.values():
+            g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager["out"]), r
+        for n, g in grads.items():
+            assert torch.equal(g, eager[n]), (r, n)
+    log("  forward + backward: 3 graph replays bit-identical to the eager call")
