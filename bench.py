@@ -82,6 +82,24 @@ BWD_PMC_TRAFFIC = {
 }
 
 
+# Measured HBM bytes per call of the loss head's statistics pass (headline
+# anchors, V = 154880, d = 6144, rank 256) and of the whole verification (its
+# three launches; 64 sequences, K = 5, V = 154880): the same FETCH/WRITE
+# scaling, with the files each is built from and their digest when taken.
+SIDE_PMC_TRAFFIC = {
+    "loss_stats": (3_882_423_906, ("loss.hip", "blas.hpp", "kernels.hpp"), "37ec07b962fc373b"),
+    "verify": (436_597_498 + 398_369_123 + 4_484_617, ("decode.hip", "kernels.hpp"),
+               "4c16bfd6e3c529be"),
+}
+
+
+def side_measured_traffic(key: str, applies: bool):
+    if not applies:
+        return None
+    nbytes, files, digest = SIDE_PMC_TRAFFIC[key]
+    return nbytes if files_digest(files) == digest else None
+
+
 def files_digest(files) -> str:
     import hashlib
     csrc = os.path.join(ROOT, "speculative_decoding_draft_amd", "csrc")
@@ -475,6 +493,9 @@ def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hid
             "stats_pass": {"bound": "hbm", "achieved": round(stat_gbs, 1),
                            "peak": MI355X_HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(stat_gbs / MI355X_HBM_PEAK_GBS, 4),
+                           "traffic": side_measured_traffic(
+                               "loss_stats", wl.name.startswith("headline") and vocab == 154880
+                               and hidden == 6144 and rank == 256),
                            "algorithmic_bytes_per_launch": stat_bytes}}
 
 
@@ -549,6 +570,8 @@ def bench_decode(sd, torch, hip, steps, B=64, K=5, vocab=154880, C=128):
             "verify_roofline": {"bound": "hbm", "achieved": round(vgbs, 1),
                                 "peak": MI355X_HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(vgbs / MI355X_HBM_PEAK_GBS, 4),
+                                "traffic": side_measured_traffic(
+                                    "verify", (B, K, vocab) == (64, 5, 154880)),
                                 "algorithmic_bytes_per_launch": vbytes},
             "mean_accepted": float(na.float().mean().item())}
 
