@@ -40,11 +40,16 @@ def test_decode_attention_equals_the_training_forward(slots):
     """One block per sample: the ring cache (linear when it is as long as
     the sequence, wrapping when it holds only W - 1 or W + 1 entries) gives
     the training forward's output."""
-    wl = wk.make_workload("dec", B=3, S=64, N=1, dims=DIMS, dtype="f32", recipe="uniform",
-                          seed=5, recipe_args=dict(n_forced_low=1))
-    ref = O.forward(wl, form="gathered")
-    got = decode_from_workload(wl, slots)
-    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # one workload with every window clamped at position 0, one with most
+    # windows whole (anchor >= W - 1)
+    for B, seed, args in ((3, 5, dict(n_forced_low=1)), (6, 7, {})):
+        wl = wk.make_workload("dec", B=B, S=64, N=1, dims=DIMS, dtype="f32", recipe="uniform",
+                              seed=seed, recipe_args=args)
+        if not args:
+            assert (wl.anchors[:, 0] >= wl.W).sum() >= 3
+        ref = O.forward(wl, form="gathered")
+        got = decode_from_workload(wl, slots)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
 
 
 def test_decode_attention_is_invariant_to_a_common_position_shift():
@@ -85,6 +90,30 @@ def test_inverse_cdf_matches_searchsorted():
         u = rng.random()
         c = np.cumsum(w)
         assert O.sample_inverse_cdf(w, u) == int(np.searchsorted(c, u * c[-1], side="right"))
+
+
+def test_inverse_cdf_at_breakpoints_never_returns_a_zero_weight():
+    """The generalised inverse of a CDF F is min{i : F(i) > u}: with u = 0 it
+    skips a prefix of zero weights, and at an exact breakpoint u = F(i) it
+    returns the next index.  Weights are small integers with a power-of-two
+    total, so every breakpoint u = c_i / total is exact; the expected index
+    is the count of cumulative sums <= u * total."""
+    assert O.sample_inverse_cdf([0.0, 0.0, 0.3, 0.7], 0.0) == 2
+    assert O.sample_inverse_cdf([1.0, 1.0, 2.0], 0.25) == 1
+    assert O.sample_inverse_cdf([1.0, 1.0, 2.0], 0.5) == 2
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        w = rng.integers(0, 4, 12).astype(np.float64)
+        w[0] = 0.0
+        w[rng.integers(1, 12)] += 1.0
+        w[-1] += 64.0 - w.sum()                   # total 64
+        if w[-1] < 0:
+            continue
+        c = np.cumsum(w)
+        for u in np.concatenate([[0.0], c[:-1] / c[-1]]):
+            i = O.sample_inverse_cdf(w, float(u))
+            assert w[i] > 0
+            assert i == int(np.sum(c <= u * c[-1]))
 
 
 def grid(n):

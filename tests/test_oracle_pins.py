@@ -95,6 +95,42 @@ def test_parameter_table_fixes_the_up_projection_shapes():
 # anchors
 # ---------------------------------------------------------------------------
 
+def test_bf16_decoding_matches_torch_on_every_bit_pattern():
+    """Every one of the 65,536 bf16 bit patterns decodes to the value torch's
+    bfloat16 type gives it (a library routine): normals, subnormals, both
+    zeros (sign kept), both infinities; NaN patterns decode to NaN."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.bf16_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2 * 127                       # exponent all ones, fraction != 0
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_bf16_decoding_closed_forms():
+    """bf16 = sign, 8-bit exponent (bias 127), 7-bit fraction: the value of a
+    normal pattern is (-1)^s 2^(e-127) (1 + f/128), of a subnormal one
+    (-1)^s 2^-126 f/128."""
+    import math
+    rng = np.random.default_rng(9)
+    pats = np.concatenate([rng.integers(0, 1 << 16, 500),
+                           [0x3F80, 0xC000, 0x0001, 0x007F, 0x0080, 0x7F7F, 0x8000, 0x3F81]])
+    for p in pats.astype(np.int64).tolist():
+        s, e, f = (p >> 15) & 1, (p >> 7) & 0xFF, p & 0x7F
+        if e == 0xFF:
+            continue
+        v = math.ldexp(1.0 + f / 128.0, e - 127) if e else math.ldexp(f / 128.0, -126)
+        v = -v if s else v
+        got = float(O.bf16_to_f64(np.array([p], dtype=np.uint16))[0])
+        assert got == v and math.copysign(1.0, got) == (-1.0 if s else 1.0), hex(p)
+    named = O.bf16_to_f64(np.array([0x3F80, 0xC000, 0x0001, 0x7F80, 0xFF80, 0x7FC0],
+                                   dtype=np.uint16))
+    assert named[0] == 1.0 and named[1] == -2.0 and named[2] == 2.0 ** -133
+    assert named[3] == np.inf and named[4] == -np.inf and np.isnan(named[5])
+
+
 def test_splitmix64_published_vector():
     want = [int(r[0]) for r in golden("splitmix64_seed1234567.txt")]
     g = O.SplitMix64(1234567)
