@@ -10,8 +10,10 @@ Tolerances (per gradient tensor, over every element):
     <= 2^-9, RMS ~1.1e-3).  The MFMA path also rounds its intermediates to
     bf16 (q_abs, W_UV^T dout, P, dS', o_lat, dq_abs, rotated q^R: <= 4 such
     roundings on any chain), so its error is a few times that of one
-    rounding: rel-L2 <= 1e-2 and max|err| <= 3e-2 * max|ref|, with the
-    generic bf16 path (fp32 intermediates) held to rel-L2 <= 5e-3.
+    rounding; it is held to the forward's bar, rel-L2 <= 5e-3, with
+    max|err| <= 1e-2 * max|ref| (measured: <= 4.0e-3 and 4.9e-3), as is
+    the generic bf16 path (fp32 intermediates).  Two GPU paths compared
+    with each other carry both errors: rel-L2 <= 1e-2, 3e-2 * max|ref|.
 Rows that no kept block reaches must be exactly 0 (padding blocks' query
 and key rows, context rows outside every window); outputs are pre-filled
 with NaN so that an element the library does not write fails the check.
@@ -29,7 +31,8 @@ pytestmark = pytest.mark.gpu
 GRADS = ("dq_nope", "dq_rope", "dckv_ctx", "dkr_ctx", "dckv_blk", "dkr_blk", "dw_uk", "dw_uv")
 F32_TOL = (2e-5, 1e-4)
 BF16_GENERIC_TOL = (5e-3, 2e-2)
-BF16_MFMA_TOL = (1e-2, 3e-2)
+BF16_MFMA_TOL = (5e-3, 1e-2)
+GPU_PATHS_TOL = (1e-2, 3e-2)
 
 
 class GpuBwd:
@@ -144,7 +147,7 @@ def test_bwd_mfma_matches_generic_path():
     dout = wk.make_dout(wl, seed=12)
     fast = GpuBwd(wl, dout, ga, gk).run().result()
     gen = GpuBwd(wl, dout, ga, gk, force_generic=True).run().result()
-    check(fast, gen, BF16_MFMA_TOL, "mfma vs generic")
+    check(fast, gen, GPU_PATHS_TOL, "mfma vs generic")
 
 
 def test_bwd_repeat_runs_agree():
@@ -187,12 +190,12 @@ def test_bwd_bad_anchor_rows_are_nan(generic):
     check(gpu, ref, BF16_GENERIC_TOL if generic else BF16_MFMA_TOL, f"bad anchor generic={generic}")
 
 
-def test_bwd_headline_full_size_sampled_blocks():
+def test_bwd_headline_full_size_all_blocks():
     """Full headline size (B=1, S=32768, N=1024, 25 % padding) in the launch
-    configuration the benchmark times: the query gradients and the block-key
-    gradients of sampled blocks (every clamped-window block and random
-    others) come from that block alone and are checked against the oracle
-    block by block; every row no kept block reaches must be 0."""
+    configuration the benchmark times, every gradient over every kept
+    block.  The oracle runs in batches of kept blocks (the gradient is
+    linear in dout, so the batches' sums are the whole gradient: pinned on
+    the CPU); every row no kept block reaches must be 0."""
     wl = wk.config(4)
     dout = wk.make_dout(wl, seed=15)
     log("case headline full size")
@@ -200,14 +203,13 @@ def test_bwd_headline_full_size_sampled_blocks():
     unreached_rows_are_zero(gpu, wl, wl.anchors, wl.keep)
     for k in GRADS:
         assert np.all(np.isfinite(gpu[k])), k
-    pick = sample_blocks(wl.keep[0], wl.anchors[0], wl.W, n_random=6, seed=3)[:14]
-    ref = O.backward(wl, dout, form="gathered", blocks=[(0, n) for n in pick])
-    rows = np.zeros((1, wl.q_len), bool)
-    for n in pick:
-        rows[0, 5 * n:5 * n + 5] = True
-    check(gpu, ref, BF16_MFMA_TOL, "headline sampled", names=("dq_nope", "dq_rope", "dckv_blk",
-                                                              "dkr_blk"),
-          rows={k: rows for k in ("dq_nope", "dq_rope", "dckv_blk", "dkr_blk")})
+    kept = [int(n) for n in np.nonzero(wl.keep[0])[0]]
+    ref = None
+    for i in range(0, len(kept), 96):
+        part = O.backward(wl, dout, form="gathered", blocks=[(0, n) for n in kept[i:i + 96]])
+        ref = part if ref is None else {k: ref[k] + part[k] for k in ref}
+    log(f"  oracle over {len(kept)} kept blocks")
+    check(gpu, ref, BF16_MFMA_TOL, "headline all blocks")
 
 
 def test_bwd_unsorted_anchors_take_the_atomic_path():

@@ -61,13 +61,9 @@ def test_index_records_bit_exact(sd, k):
     # slots are the ranks of the kept blocks in (b, n) order
     rank = np.cumsum(ok.ravel().astype(np.int64)) - 1
     assert np.array_equal(rec[..., 3].ravel(), np.where(ok.ravel() == 1, rank, -1))
-    rng = np.random.default_rng(k)
     for b in range(wl.B):
-        # every block for the smaller configs, 600 of the 4096 for the largest
-        ns = range(wl.N) if wl.N <= 1024 else sorted(
-            set(rng.choice(wl.N, 600, replace=False).tolist()) | {0, wl.N - 1})
-        want = O.block_index_records(wl.S, wl.N, wl.W, oa[b], ok[b], ns=ns)
-        for n in ns:
+        want = O.block_index_records(wl.S, wl.N, wl.W, oa[b], ok[b])
+        for n in range(wl.N):
             if ok[b, n]:
                 assert rec[b, n, :3].tolist() == want[n, :3].tolist(), (b, n)
             else:
@@ -136,6 +132,20 @@ def test_cfg3_recipe_small(sd):
 def test_cfg4_recipe_small(sd):
     log("cfg4 recipe B1 S4096 N128 (padding + clamped windows)")
     check_full(wk.scaled(4, S=4096, N=128), form="gathered", guard=4096)
+
+
+def test_cfg4_recipe_shuffled_kept_anchors(sd):
+    """The page draws N anchors at random and fixes no order; here the
+    headline recipe's (anchor, keep) slots are permuted so that kept anchors
+    are out of order and padding slots sit between them."""
+    wl = wk.scaled(4, S=4096, N=128)
+    perm = np.random.default_rng(44).permutation(wl.N)
+    wl.anchors[0] = wl.anchors[0][perm]
+    wl.keep[0] = wl.keep[0][perm]
+    kept = wl.anchors[0][wl.keep[0] == 1]
+    assert np.any(np.diff(kept) < 0)
+    log("cfg4 recipe B1 S4096 N128, kept anchors shuffled")
+    check_full(wl, form="gathered", guard=1024)
 
 
 def test_cfg4_recipe_four_wave_launch(sd):
