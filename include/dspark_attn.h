@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 10
+#define DSPARK_ABI_VERSION 11
 
 typedef enum dspark_status {
     DSPARK_OK = 0,
@@ -86,14 +86,19 @@ typedef struct dspark_attn_desc {
     int32_t dtype;
 } dspark_attn_desc;
 
-/* Bytes of workspace dspark_attn_fwd needs for `desc` (0 on an invalid
- * descriptor; see dspark_last_error).  The workspace holds the per-block
- * index records, the compacted list of kept blocks, a small status area, the
- * RoPE cos/sin table (written and read by the generic path only; the MFMA
- * path evaluates RoPE inside its attention kernel) and, on the MFMA path,
- * the bf16 latent intermediates
- * q_abs and o_lat of every kept block ([5*B*N, H, D] each, row = 5 * slot +
- * query).  It must be 256-byte aligned. */
+/* Bytes of workspace dspark_attn_fwd(_ex) needs for `desc` whatever the
+ * options (0 on an invalid descriptor; see dspark_last_error).  The
+ * workspace holds the per-block index records, the compacted list of kept
+ * blocks and a small status area, and then, by path:
+ *   - generic kernels: the RoPE cos/sin table;
+ *   - three-kernel MFMA forward (the default for the MFMA shapes): the
+ *     bf16 latent intermediates q_abs and o_lat of every kept block
+ *     ([5*B*N, H, D] each, row = 5 * slot + query);
+ *   - one-launch MFMA forward (dspark_attn_opts.one_launch on a device with
+ *     256 compute units): the pipeline's control words and two rings of 32
+ *     kept blocks x 8 XCDs (the bf16 q_abs and o_lat of a block's 5 queries
+ *     and one XCD's 8 heads, 40 KB each), about 21 MB in all.
+ * It must be 256-byte aligned. */
 size_t dspark_attn_workspace_size(const dspark_attn_desc* desc);
 
 /* The masked MLA attention forward of one draft layer.
@@ -130,8 +135,9 @@ typedef struct dspark_attn_opts {
      * then for round c
      * (see dspark_attn_plan), on the stream that runs the round: [2 + 4c]
      * before its absorb, [3 + 4c] after it, [4 + 4c] after its attention
-     * kernel, [5 + 4c] after its W_UV projection.  The generic path records
-     * [0], [1] and [2] after its single kernel. */
+     * kernel, [5 + 4c] after its W_UV projection.  The generic path and
+     * the one-launch forward record [0], [1] and [2] after their single
+     * kernel. */
     void* const* stage_events;
     int32_t n_stage_events;   /* at least the count dspark_attn_plan reports */
     int32_t force_generic;    /* nonzero: use the generic fp32 kernels even
@@ -157,13 +163,37 @@ typedef struct dspark_attn_opts {
      * forward's block index, q_abs and o_lat instead of rebuilding them
      * (dW_UV then uses the forward's o_lat rows). */
     int32_t reuse_forward;
+    /* dspark_attn_fwd_ex on the MFMA shapes, nonzero: the one-launch
+     * forward instead of the three kernels (ignored with chunk_blocks or
+     * aux_stream; on a device without 256 compute units the three kernels
+     * run).  It runs absorb, attention and W_UV side by side on different
+     * compute units of each XCD, each XCD owning 8 heads, and passes q_abs
+     * and o_lat through rings in that XCD's L2 instead of HBM; it needs all
+     * 256 of its workgroups resident at once (nothing else running on the
+     * device), bounds every internal wait in time, and reports a stall
+     * through dspark_read_device_status (DSPARK_EHIP) instead of hanging.
+     * It leaves no q_abs / o_lat for reuse_forward.  Measured on the
+     * headline workload it is slower than the three kernels (each XCD
+     * re-reads every block's keys for its heads, and its units wait on one
+     * another); it is kept as a parity-tested alternative. */
+    int32_t one_launch;
 } dspark_attn_opts;
 
-/* Launch plan of dspark_attn_fwd_ex for (desc, opts) (opts may be NULL):
- * *n_chunks kernel rounds of *chunk_blocks kept blocks each (the count is an
- * upper bound: chunks past the number of kept blocks exit at once), and
- * *n_events stage events recorded when opts->stage_events is given.  Any
- * output pointer may be NULL. */
+/* Bytes of workspace dspark_attn_fwd_ex needs for (desc, opts) on a device
+ * with 256 compute units (opts may be NULL; 0 on an invalid descriptor):
+ * the size of the path those options select, which is smaller than
+ * dspark_attn_workspace_size for the one-launch forward.  On a device where
+ * the one-launch forward cannot run, the call falls back to the three-kernel
+ * forward and needs dspark_attn_workspace_size(desc) bytes (a smaller
+ * workspace is then refused with DSPARK_EWORKSPACE). */
+size_t dspark_attn_workspace_size_ex(const dspark_attn_desc* desc, const dspark_attn_opts* opts);
+
+/* Launch plan of dspark_attn_fwd_ex for (desc, opts) (opts may be NULL) on
+ * the current device: *n_chunks kernel rounds of *chunk_blocks kept blocks
+ * each (the count is an upper bound: chunks past the number of kept blocks
+ * exit at once; the one-launch forward is one round over all B*N blocks,
+ * the generic path none), and *n_events stage events recorded when
+ * opts->stage_events is given.  Any output pointer may be NULL. */
 dspark_status dspark_attn_plan(const dspark_attn_desc* desc, const dspark_attn_opts* opts,
                                int32_t* n_chunks, int32_t* chunk_blocks, int32_t* n_events);
 

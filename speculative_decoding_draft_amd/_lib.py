@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "DSPARK_OK", -1: "DSPARK_EINVAL", -2: "DSPARK_EUNSUPPORTED",
 DSPARK_F32 = 0
 DSPARK_BF16 = 1
 
-EXPORTS = ("dspark_attn_workspace_size", "dspark_attn_fwd", "dspark_attn_fwd_ex", "dspark_attn_plan",
+EXPORTS = ("dspark_attn_workspace_size", "dspark_attn_workspace_size_ex", "dspark_attn_fwd", "dspark_attn_fwd_ex", "dspark_attn_plan",
            "dspark_attn_bwd_workspace_size", "dspark_attn_bwd", "dspark_attn_bwd_ex",
            "dspark_attn_bwd_plan", "dspark_mla_layer_workspace_size", "dspark_mla_layer_fwd",
            "dspark_mla_layer_fwd_ex", "dspark_mla_layer_tune", "dspark_mla_layer_read_status", "dspark_loss_workspace_size",
@@ -86,7 +86,8 @@ class Opts(ctypes.Structure):
     _fields_ = [("stage_events", ctypes.POINTER(ctypes.c_void_p)),
                 ("n_stage_events", ctypes.c_int32), ("force_generic", ctypes.c_int32),
                 ("chunk_blocks", ctypes.c_int32), ("aux_stream", ctypes.c_void_p),
-                ("aux_events", ctypes.c_void_p * 2), ("reuse_forward", ctypes.c_int32)]
+                ("aux_events", ctypes.c_void_p * 2), ("reuse_forward", ctypes.c_int32),
+                ("one_launch", ctypes.c_int32)]
 
 
 def _load():
@@ -102,6 +103,8 @@ def _load():
     pd = ctypes.POINTER(Desc)
     lib.dspark_attn_workspace_size.argtypes = [pd]
     lib.dspark_attn_workspace_size.restype = sz
+    lib.dspark_attn_workspace_size_ex.argtypes = [pd, ctypes.POINTER(Opts)]
+    lib.dspark_attn_workspace_size_ex.restype = sz
     fwd_args = [pd] + [vp] * 8 + [vp, vp, vp, vp, sz, vp]
     lib.dspark_attn_fwd.argtypes = fwd_args
     lib.dspark_attn_fwd.restype = i32
@@ -198,6 +201,16 @@ def workspace_size(desc: Desc) -> int:
     return n
 
 
+def workspace_size_ex(desc: Desc, force_generic: bool = False, chunk_blocks: int = 0,
+                      one_launch: bool = False) -> int:
+    """dspark_attn_workspace_size_ex: bytes for the path these options select."""
+    opts, _ = _opts(None, force_generic, chunk_blocks, one_launch=one_launch)
+    n = int(lib.dspark_attn_workspace_size_ex(ctypes.byref(desc), ctypes.byref(opts)))
+    if n == 0:
+        raise DSparkError(DSPARK_EINVAL, last_error())
+    return n
+
+
 def _ptr(t) -> Optional[int]:
     if t is None:
         return None
@@ -214,8 +227,9 @@ def _stream(stream) -> Optional[int]:
 
 
 def _opts(stage_events=None, force_generic=False, chunk_blocks=0, aux_stream=None,
-          aux_events=None):
+          aux_events=None, one_launch=False):
     opts = Opts()
+    opts.one_launch = 1 if one_launch else 0
     if aux_stream is not None:
         opts.aux_stream = _stream(aux_stream)
         opts.aux_events[0], opts.aux_events[1] = aux_events
@@ -229,9 +243,10 @@ def _opts(stage_events=None, force_generic=False, chunk_blocks=0, aux_stream=Non
     return opts, keep
 
 
-def attn_plan(desc: Desc, force_generic: bool = False, chunk_blocks: int = 0):
+def attn_plan(desc: Desc, force_generic: bool = False, chunk_blocks: int = 0,
+              one_launch: bool = False):
     """dspark_attn_plan: (n_chunks, chunk_blocks, n_events)."""
-    opts, _ = _opts(None, force_generic, chunk_blocks)
+    opts, _ = _opts(None, force_generic, chunk_blocks, one_launch=one_launch)
     nc, cb, ne = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     _check(lib.dspark_attn_plan(ctypes.byref(desc), ctypes.byref(opts), ctypes.byref(nc),
                                 ctypes.byref(cb), ctypes.byref(ne)))
@@ -242,19 +257,23 @@ def attn_fwd(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk,
              anchors, keep, out, workspace, stream=None,
              stage_events: Optional[Sequence[int]] = None, force_generic: bool = False,
              chunk_blocks: int = 0, aux_stream=None,
-             aux_events: Optional[Sequence[int]] = None) -> None:
+             aux_events: Optional[Sequence[int]] = None,
+             one_launch: bool = False) -> None:
     """dspark_attn_fwd / dspark_attn_fwd_ex; raises DSparkError on a non-OK
     status.  aux_stream / aux_events (two hipEvent_t handles) run odd rounds
-    on a second stream (see dspark_attn_opts)."""
+    on a second stream; one_launch selects the one-launch forward (see
+    dspark_attn_opts)."""
     args = [ctypes.byref(desc)] + [_ptr(t) for t in (q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk,
                                                      kr_blk, w_uk, w_uv, anchors, keep, out,
                                                      workspace)]
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args += [ws_bytes, _stream(stream)]
-    if stage_events is None and not force_generic and not chunk_blocks and aux_stream is None:
+    if (stage_events is None and not force_generic and not chunk_blocks and aux_stream is None
+            and not one_launch):
         _check(lib.dspark_attn_fwd(*args))
         return
-    opts, _arr = _opts(stage_events, force_generic, chunk_blocks, aux_stream, aux_events)
+    opts, _arr = _opts(stage_events, force_generic, chunk_blocks, aux_stream, aux_events,
+                       one_launch)
     _check(lib.dspark_attn_fwd_ex(*args, ctypes.byref(opts)))
 
 
@@ -266,7 +285,7 @@ class BoundFwd:
     def __init__(self, desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
                  anchors, keep, out, workspace, stream=None, chunk_blocks: int = 0,
                  n_stage_events: int = 0, aux_stream=None,
-                 aux_events: Optional[Sequence[int]] = None):
+                 aux_events: Optional[Sequence[int]] = None, one_launch: bool = False):
         self._desc = desc
         ws_bytes = workspace.numel() * workspace.element_size()
         self._args = (ctypes.byref(desc),) + tuple(
@@ -275,10 +294,12 @@ class BoundFwd:
             ctypes.c_size_t(ws_bytes), ctypes.c_void_p(_stream(stream)))
         self._plain = lib.dspark_attn_fwd
         self._ex = lib.dspark_attn_fwd_ex
-        self._opts, _ = _opts(None, False, chunk_blocks, aux_stream, aux_events)
+        self._opts, _ = _opts(None, False, chunk_blocks, aux_stream, aux_events,
+                              one_launch)
         self._opts_ref = ctypes.byref(self._opts)
         self._events = (ctypes.c_void_p * max(1, n_stage_events))()
-        self._opts_ev, _ = _opts(None, False, chunk_blocks, aux_stream, aux_events)
+        self._opts_ev, _ = _opts(None, False, chunk_blocks, aux_stream, aux_events,
+                                 one_launch)
         self._opts_ev.stage_events = ctypes.cast(self._events, ctypes.POINTER(ctypes.c_void_p))
         self._opts_ev.n_stage_events = n_stage_events
         self._opts_ev_ref = ctypes.byref(self._opts_ev)

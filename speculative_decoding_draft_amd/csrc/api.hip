@@ -1,5 +1,6 @@
 // extern "C" entry points of libdspark_attn.so: argument validation,
 // workspace layout, kernel launches.  See include/dspark_attn.h.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -101,6 +102,9 @@ Workspace carve(void* base, const WsLayout& L) {
     w.rope = reinterpret_cast<float2*>(c + L.rope);
     w.qabs = L.qabs ? reinterpret_cast<bf16*>(c + L.qabs) : nullptr;
     w.olat = L.olat ? reinterpret_cast<bf16*>(c + L.olat) : nullptr;
+    w.ctl = L.ctl ? reinterpret_cast<int32_t*>(c + L.ctl) : nullptr;
+    w.qring = L.qring ? reinterpret_cast<bf16*>(c + L.qring) : nullptr;
+    w.oring = L.oring ? reinterpret_cast<bf16*>(c + L.oring) : nullptr;
     return w;
 }
 
@@ -148,6 +152,45 @@ RopeTheta make_theta(const dspark_attn_desc& d) {
     return th;
 }
 
+// Forward paths: the generic fp32 kernels (any shape), the three MFMA
+// kernels with q_abs / o_lat materialised in the workspace, and the fused
+// one-launch pipeline (GLM dims, 256 compute units).
+enum class FwdPath { kGeneric, kMaterialised, kFused };
+
+// The fused launch needs every one of its 256 workgroups resident at once
+// (one per compute unit) on an 8-XCD device.  Answered once per device.
+bool fused_device_ok() {
+    static std::atomic<int8_t> known[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+    if (dev < 64) {
+        const int8_t k = known[dev].load(std::memory_order_relaxed);
+        if (k != 0) return k == 1;
+    }
+    int cus = 0, nb = 0;
+    bool ok = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) ==
+                  hipSuccess &&
+              cus == kFusedCus &&
+              hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fused_kernel_fn(),
+                                                           fused_threads(), 0) == hipSuccess &&
+              nb >= 1;
+    (void)hipGetLastError();
+    if (dev < 64) known[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok;
+}
+
+FwdPath pick_path(const dspark_attn_desc& d, const dspark_attn_opts* o, bool check_device) {
+    if (!is_fast_path(d) || (o && o->force_generic)) return FwdPath::kGeneric;
+    if (!o || !o->one_launch || o->chunk_blocks > 0 || o->aux_stream)
+        return FwdPath::kMaterialised;
+    if (check_device && !fused_device_ok()) return FwdPath::kMaterialised;
+    return FwdPath::kFused;
+}
+
+WsLayout path_layout(const dspark_attn_desc& d, FwdPath path) {
+    return ws_layout(d, path == FwdPath::kMaterialised, path == FwdPath::kFused);
+}
+
 }  // namespace
 
 void set_last_error(const char* msg) { g_last_error = msg; }
@@ -166,7 +209,16 @@ size_t dspark_attn_workspace_size(const dspark_attn_desc* desc) {
     bool empty = false;
     if (check_desc(desc, &empty) != DSPARK_OK) return 0;
     g_last_error.clear();
-    return ws_layout(*desc, is_fast_path(*desc)).total;
+    const size_t any = ws_layout(*desc, is_fast_path(*desc)).total;
+    const size_t fused = is_fast_path(*desc) ? ws_layout(*desc, false, true).total : 0;
+    return any > fused ? any : fused;
+}
+
+size_t dspark_attn_workspace_size_ex(const dspark_attn_desc* desc, const dspark_attn_opts* opts) {
+    bool empty = false;
+    if (check_desc(desc, &empty) != DSPARK_OK) return 0;
+    g_last_error.clear();
+    return path_layout(*desc, pick_path(*desc, opts, false)).total;
 }
 
 dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nope,
@@ -190,8 +242,9 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
         if (ptrs[i] && i != 9 && !aligned16(ptrs[i]))
             return fail(DSPARK_EINVAL, "%s must be 16-byte aligned", names[i]);
     }
-    const bool fast = is_fast_path(d) && !(opts && opts->force_generic);
-    const WsLayout L = ws_layout(d, fast);
+    const FwdPath path = pick_path(d, opts, true);
+    const bool fast = path != FwdPath::kGeneric;
+    const WsLayout L = path_layout(d, path);
     st = check_workspace(workspace, ws_bytes, L.total);
     if (st != DSPARK_OK) return st;
 
@@ -210,9 +263,10 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
         return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[k]), s) : hipSuccess;
     };
 
+    const bool fused = path == FwdPath::kFused;
     const int chunk = chunk_blocks(d, opts);
-    const int n_chunks = fast ? (d.B * d.N + chunk - 1) / chunk : 0;
-    const int n_events = fast ? 2 + 4 * n_chunks : 3;
+    const int n_chunks = (fast && !fused) ? (d.B * d.N + chunk - 1) / chunk : 0;
+    const int n_events = (fast && !fused) ? 2 + 4 * n_chunks : 3;
     if (ev && opts->n_stage_events < n_events)
         return fail(DSPARK_EINVAL, "this call records %d stage events; n_stage_events is %d",
                     n_events, opts->n_stage_events);
@@ -230,6 +284,17 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
     hipError_t e;
     if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     const RopeTheta theta = make_theta(d);
+    if (fused) {
+        // index, padding rows and the pipeline's control words, then the
+        // whole forward in one launch
+        if ((e = launch_prep(p, anchors, keep, ws, nullptr, 0, nullptr, out, s)) != hipSuccess)
+            return hip_fail(e, "index / fill launch");
+        if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if ((e = launch_fused(p, in, ws, theta, s)) != hipSuccess)
+            return hip_fail(e, "fused forward launch");
+        if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        return ok();
+    }
     // the MFMA path evaluates RoPE inside the attention kernel; only the
     // generic path reads the table
     if ((e = launch_prep(p, anchors, keep, ws, nullptr, L.rope_rows, fast ? nullptr : &theta,
@@ -278,11 +343,14 @@ dspark_status dspark_attn_plan(const dspark_attn_desc* desc, const dspark_attn_o
     bool empty = false;
     dspark_status st = check_desc(desc, &empty);
     if (st != DSPARK_OK) return st;
-    const bool fast = is_fast_path(*desc) && !(opts && opts->force_generic) && !empty;
+    // the one-launch forward counts as one round over every block
+    const FwdPath path = empty ? FwdPath::kGeneric : pick_path(*desc, opts, true);
+    const bool fast = path == FwdPath::kMaterialised;
+    const bool fused = path == FwdPath::kFused;
     const int chunk = empty ? 0 : chunk_blocks(*desc, opts);
-    const int nc = fast ? (desc->B * desc->N + chunk - 1) / chunk : 0;
+    const int nc = fast ? (desc->B * desc->N + chunk - 1) / chunk : (fused ? 1 : 0);
     if (n_chunks) *n_chunks = nc;
-    if (chunk_out) *chunk_out = fast ? chunk : 0;
+    if (chunk_out) *chunk_out = fast ? chunk : (fused ? desc->B * desc->N : 0);
     if (n_events) *n_events = empty ? 0 : (fast ? 2 + 4 * nc : 3);
     return ok();
 }
@@ -463,6 +531,10 @@ dspark_status dspark_read_device_status(const void* workspace, void* stream,
     if (words[kStFirstBad] >= 0)
         return fail(DSPARK_EANCHOR, "kept block %d has an anchor outside [0, S-2]",
                     words[kStFirstBad]);
+    if (words[kStPipeFault] != 0)
+        return fail(DSPARK_EHIP,
+                    "the one-launch forward stalled (a unit waited past its time bound); "
+                    "its output is incomplete");
     return ok();
 }
 

@@ -24,8 +24,22 @@ constexpr int kH = 64, kD = 512, kDc = 192, kDr = 64, kDv = 256;
 constexpr int kMaxWindow = 128;    // W <= 128: at most 127 context + 5 block keys
 constexpr int kMaxKeys = kMaxWindow - 1 + kBlock;   // 132
 
-// Status area of the workspace (int32 words).
-enum StatusWord { kStKeptCount = 0, kStFirstBad = 1, kStWords = 16 };
+// Status area of the workspace (int32 words).  Word 2 belongs to the
+// backward (unsorted anchors); word 3 records a stalled fused pipeline.
+enum StatusWord { kStKeptCount = 0, kStFirstBad = 1, kStPipeFault = 3, kStWords = 16 };
+
+// Fused forward (GLM dims on a 256-CU, 8-XCD gfx950).  Each XCD owns 8 of
+// the 64 heads; the query latents and attention outputs of its heads travel
+// between its compute units through two rings of kFusedRing kept blocks in
+// that XCD's L2, coordinated by int32 counters (kFusedCtlStride words per
+// XCD, zeroed by the preparation launch).
+constexpr int kFusedXcds = 8;
+constexpr int kFusedCus = 256;
+constexpr int kFusedRing = 32;
+constexpr int kFusedHeads = kH / kFusedXcds;
+constexpr size_t kFusedSlotElems = (size_t)kBlock * kFusedHeads * kD;   // bf16 per ring slot
+constexpr int kFusedCtlStride = 576;   // 320 control words, then 8 timing words per unit
+constexpr int kFusedCtlWords = kFusedXcds * kFusedCtlStride;
 
 // RoPE angles theta_i = base^(-2i/d_r), computed on the host in fp64.
 struct RopeTheta {
@@ -43,13 +57,19 @@ struct WsLayout {
     size_t qabs = 0;     // bf16 [5*B*N][H][D]  (MFMA path; row = 5*slot + query,
                          // the same rows whatever the round size)
     size_t olat = 0;     // bf16 [5*B*N][H][D]  (MFMA path)
+    size_t ctl = 0;      // int32 [kFusedCtlWords]                 (fused path)
+    size_t qring = 0;    // bf16 [8 XCDs][kFusedRing][5][8][D]     (fused path)
+    size_t oring = 0;    // bf16 [8 XCDs][kFusedRing][5][8][D]     (fused path)
     size_t total = 0;
     int rope_rows = 0;   // S + 8
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline WsLayout ws_layout(const dspark_attn_desc& d, bool mfma) {
+// mfma: the three-kernel MFMA path (materialised q_abs / o_lat); fused: the
+// one-launch pipeline (control words and rings instead of the RoPE table and
+// the latent buffers); neither: the generic path (RoPE table).
+inline WsLayout ws_layout(const dspark_attn_desc& d, bool mfma, bool fused = false) {
     WsLayout w;
     const size_t blocks = size_t(d.B) * size_t(d.N);
     size_t off = 0;
@@ -57,6 +77,15 @@ inline WsLayout ws_layout(const dspark_attn_desc& d, bool mfma) {
     w.idx = off;    off = align256(off + blocks * 16);
     w.kept = off;   off = align256(off + blocks * 4);
     w.srec = off;   off = align256(off + blocks * 16);
+    if (fused) {
+        const size_t ring = (size_t)kFusedXcds * kFusedRing * kFusedSlotElems * 2;
+        w.rope = off;   // no table
+        w.ctl = off;    off = align256(off + (size_t)kFusedCtlWords * 4);
+        w.qring = off;  off = align256(off + ring);
+        w.oring = off;  off = align256(off + ring);
+        w.total = off;
+        return w;
+    }
     w.rope_rows = d.S + 8;
     w.rope = off;   off = align256(off + size_t(w.rope_rows) * size_t(d.d_rope / 2) * 8);
     if (mfma) {

@@ -32,10 +32,14 @@ struct Workspace {
     float2* rope;
     bf16* qabs;
     bf16* olat;
+    int32_t* ctl = nullptr;     // fused path
+    bf16* qring = nullptr;
+    bf16* oring = nullptr;
 };
 
 // Index build, and optionally (th != nullptr) the RoPE table and (out !=
 // nullptr) the rows of padding / invalid-anchor blocks, in one launch.
+// ws.ctl != nullptr: the fused path's control words are zeroed as well.
 hipError_t launch_prep(const Problem& p, const int32_t* anchors, const uint8_t* keep,
                        const Workspace& ws, int32_t* index_copy, int rope_rows,
                        const RopeTheta* th, void* out, hipStream_t s);
@@ -55,5 +59,12 @@ hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, 
                        const RopeTheta& th, hipStream_t s);
 hipError_t launch_uv(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
                      hipStream_t s);
+// The whole forward after the preparation launch as one persistent launch
+// of kFusedCus workgroups (GLM dims; the control words must be zero).
+hipError_t launch_fused(const Problem& p, const Inputs& in, const Workspace& ws,
+                        const RopeTheta& th, hipStream_t s);
+// LDS bytes and threads of the fused kernel (for the host-side residency check)
+int fused_threads();
+const void* fused_kernel_fn();
 
 }  // namespace dspark

@@ -73,7 +73,7 @@ class ForwardRun:
     """Uploads one layer, owns out + workspace, runs the forward."""
 
     def __init__(self, wl, layer_idx=0, anchors=None, keep=None, guard=0, softmax_scale=0.0,
-                 force_generic=False, chunk_blocks=0):
+                 force_generic=False, chunk_blocks=0, one_launch=False):
         import torch
         import speculative_decoding_draft_amd as sd
         self.wl, self.sd, self.torch = wl, sd, torch
@@ -90,13 +90,14 @@ class ForwardRun:
         self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
         self.force_generic = force_generic
         self.chunk_blocks = chunk_blocks
+        self.one_launch = one_launch
 
     def run(self, stream=None):
         t = self.t
         self.sd.attn_fwd(self.desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"],
                          t["ckv_blk"], t["kr_blk"], t["w_uk"], t["w_uv"], self.anchors, self.keep,
                          self.out, self.ws, stream=stream, force_generic=self.force_generic,
-                         chunk_blocks=self.chunk_blocks)
+                         chunk_blocks=self.chunk_blocks, one_launch=self.one_launch)
         return self
 
     def result(self) -> np.ndarray:

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert set(sd.EXPORTS) == declared
-    assert sd.abi_version() == 10
+    assert sd.abi_version() == 11
 
 
 def glm_desc(**kw):

@@ -21,12 +21,14 @@ def sd():
 
 
 def check_full(wl, form="dense", layer=0, force_generic=False, tol=None, guard=0,
-               chunk_blocks=0):
+               chunk_blocks=0, one_launch=False):
     ga, gk, oa, ok = anchors_for(wl)
     assert np.array_equal(ga, oa) and np.array_equal(gk, ok), "anchor selection differs"
     run = ForwardRun(wl, layer, ga, gk, guard=guard, force_generic=force_generic,
-                 chunk_blocks=chunk_blocks).run()
+                     chunk_blocks=chunk_blocks, one_launch=one_launch).run()
     gpu = run.result()
+    st, _ = run.sd.read_device_status(run.ws)
+    assert st == run.sd.DSPARK_OK, run.sd.last_error()
     ref = O.forward(wl, layer, oa, ok, form=form)
     if tol is None:
         tol = (F32_MAX_ABS, F32_REL_L2) if wl.dtype == "f32" else (BF16_MAX_ABS, BF16_REL_L2)
@@ -227,7 +229,7 @@ def test_bound_call_matches_plain_call(sd):
     """BoundFwd (arguments marshalled once) runs the same forward."""
     import torch
     wl = wk.scaled(4, S=2048, N=96)
-    r = ForwardRun(wl, 0, wl.anchors, wl.keep)
+    r = ForwardRun(wl, 0, wl.anchors, wl.keep, chunk_blocks=32)
     ref = r.run().result()
     r.out.fill_(float("nan"))
     t = r.t
@@ -470,3 +472,81 @@ def test_forward_and_backward_replay_from_a_hip_graph(sd):
         for n, g in grads.items():
             assert torch.equal(g, eager[n]), (r, n)
     log("  forward + backward: 3 graph replays bit-identical to the eager call")
+
+
+# ---------------------------------------------------------------------------
+# the one-launch forward (dspark_attn_opts.one_launch): absorb, attention and
+# W_UV on different compute units, q_abs / o_lat through per-XCD L2 rings
+# ---------------------------------------------------------------------------
+
+def _mixed():
+    return wk.make_workload("mixed-B3", B=3, S=700, N=37, dims=wk.GLM_DIMS, dtype="bf16",
+                            recipe="headline", seed=82, recipe_args=dict(pad_frac=0.3, low_frac=0.2))
+
+
+@pytest.mark.parametrize("case", ["cfg2", "cfg4-small", "cfg3-small", "mixed-B3", "window-16",
+                                  "single-block"])
+def test_one_launch_forward(sd, case):
+    """More kept blocks than the 32 ring slots (several generations per
+    slot), padding, clamped windows, B > 1, short windows, a single block."""
+    if case == "cfg2":
+        wl = wk.config(2)
+    elif case == "cfg4-small":
+        wl = wk.scaled(4, S=4096, N=600)
+    elif case == "cfg3-small":
+        wl = wk.scaled(3, S=1024, N=64)
+    elif case == "mixed-B3":
+        wl = _mixed()
+    elif case == "window-16":
+        wl = wk.make_workload("W16", B=1, S=400, N=40, dims=dict(wk.GLM_DIMS, W=16), dtype="bf16",
+                              recipe="headline", seed=56, recipe_args=dict(low_frac=0.1))
+    else:
+        wl = wk.make_workload("edge-top", B=1, S=300, N=1, dims=wk.GLM_DIMS, dtype="bf16",
+                              recipe="uniform", seed=81)
+        wl.anchors[0, 0] = 298
+        wl.loss_mask[0, 298] = wl.loss_mask[0, 299] = 1
+    log(f"one-launch forward: {case}")
+    check_full(wl, form="gathered", guard=2048, one_launch=True)
+
+
+def test_one_launch_headline_size_sampled_blocks(sd):
+    """Headline size (768 kept blocks: 24 generations per ring slot)."""
+    wl = wk.config(4)
+    run = ForwardRun(wl, 0, wl.anchors, wl.keep, one_launch=True).run()
+    gpu = run.result()
+    st, _ = sd.read_device_status(run.ws)
+    assert st == sd.DSPARK_OK, sd.last_error()
+    pick = sample_blocks(wl.keep[0], wl.anchors[0], wl.W, n_random=24, seed=7)
+    ref = O.forward(wl, 0, form="gathered", blocks=[(0, n) for n in pick])
+    compare(gpu, ref, wl.keep, BF16_MAX_ABS, BF16_REL_L2, what="one-launch headline sampled")
+
+
+def test_one_launch_repeats_bit_identically_and_matches_three_kernels(sd):
+    """Every output is computed in a fixed order whatever compute unit takes
+    its block, so two calls give the same bits; the three-kernel forward
+    agrees within the bf16 tolerance (its roundings differ)."""
+    wl = wk.scaled(4, S=2048, N=200)
+    run = ForwardRun(wl, 0, wl.anchors, wl.keep, one_launch=True)
+    a = run.run().result()
+    run.out.fill_(float("nan"))
+    b = run.run().result()
+    assert np.array_equal(np.nan_to_num(a, nan=7.0), np.nan_to_num(b, nan=7.0))
+    three = ForwardRun(wl, 0, wl.anchors, wl.keep).run().result()
+    compare(a, three, wl.keep, BF16_MAX_ABS, BF16_REL_L2, what="one-launch vs three kernels")
+
+
+def test_one_launch_bad_anchor_rows_are_nan(sd):
+    wl = wk.make_workload("badfwd", B=1, S=512, N=20, dims=wk.GLM_DIMS, dtype="bf16",
+                          recipe="uniform", seed=9)
+    a, k = wl.anchors.copy(), wl.keep.copy()
+    a[0, 7] = 511
+    run = ForwardRun(wl, 0, a, k, one_launch=True).run()
+    st, fb = sd.read_device_status(run.ws)
+    assert st == sd.DSPARK_EANCHOR and fb == 7
+    gpu = run.result()
+    assert np.all(np.isnan(gpu[0, 35:40]))
+    ok = k.copy()
+    ok[0, 7] = 0
+    ref = O.forward(wl, 0, a, ok, form="gathered")
+    gpu[0, 35:40] = 0.0
+    compare(gpu, ref, ok, BF16_MAX_ABS, BF16_REL_L2, what="one-launch other blocks")
