@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 11
+#define DSPARK_ABI_VERSION 12
 
 typedef enum dspark_status {
     DSPARK_OK = 0,
@@ -206,6 +206,44 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc,
                                  const int32_t* anchors, const uint8_t* keep,
                                  void* out, void* workspace, size_t ws_bytes,
                                  void* stream, const dspark_attn_opts* opts);
+
+/* Bytes of the status area at the start of every workspace (16 int32
+ * words), and of the status buffer dspark_attn_fwd_noalloc may be given. */
+#define DSPARK_STATUS_BYTES 64
+
+/* Size of the scratch array dspark_attn_fwd_noalloc works in (64 MiB). */
+#define DSPARK_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* The forward of dspark_attn_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc): the same inputs, output and results, and no workspace
+ * argument.  The library keeps one scratch array of
+ * DSPARK_NOALLOC_SCRATCH_BYTES in the memory of each device its code runs
+ * on, until the process ends, and this call works in it.  It calls no
+ * hipMalloc, hipFree or other allocating routine; its first call on a device
+ * looks up the array's address on that device.
+ *   status  NULL, or device memory of DSPARK_STATUS_BYTES (4-byte aligned)
+ *           that receives the call's status words, to be read with
+ *           dspark_read_device_status(status, stream, &first_bad_block).
+ *           With NULL the words stay in the array and are not readable.
+ * On the MFMA shapes (see dspark_attn_fwd) the three kernels run in rounds of
+ * as many kept blocks as the array holds q_abs / o_lat rows for (640 KiB per
+ * block at H = 64, D = 512: about 100 blocks), one round after another on
+ * `stream`; other shapes run the generic kernel.  Returns DSPARK_EUNSUPPORTED
+ * before any device work when the shape does not fit: the index (36 bytes per
+ * block of B*N) plus one block's latent rows, or on the generic path the
+ * index plus the RoPE table ((S + 8) * d_rope * 4 bytes), above the array's
+ * size.  Nothing in the array has to start at zero (each call writes all it
+ * reads).  All calls on one device share its array: calls that overlap in
+ * time on one device (on different streams or host threads) race, and their
+ * results are undefined. */
+dspark_status dspark_attn_fwd_noalloc(const dspark_attn_desc* desc,
+                                      const void* q_nope, const void* q_rope,
+                                      const void* ckv_ctx, const void* kr_ctx,
+                                      const void* ckv_blk, const void* kr_blk,
+                                      const void* w_uk, const void* w_uv,
+                                      const int32_t* anchors, const uint8_t* keep,
+                                      void* out, int32_t* status, void* stream);
 
 /* The anchor/window index builder alone (the first stage of the forward).
  * index_out [B, N, 4] int32 per block: {ctx_lo, ctx_len, pos0, slot}

@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "DSPARK_OK", -1: "DSPARK_EINVAL", -2: "DSPARK_EUNSUPPORTED",
 DSPARK_F32 = 0
 DSPARK_BF16 = 1
 
-EXPORTS = ("dspark_attn_workspace_size", "dspark_attn_workspace_size_ex", "dspark_attn_fwd", "dspark_attn_fwd_ex", "dspark_attn_plan",
+EXPORTS = ("dspark_attn_workspace_size", "dspark_attn_workspace_size_ex", "dspark_attn_fwd", "dspark_attn_fwd_ex", "dspark_attn_fwd_noalloc", "dspark_attn_plan",
            "dspark_attn_bwd_workspace_size", "dspark_attn_bwd", "dspark_attn_bwd_ex",
            "dspark_attn_bwd_plan", "dspark_mla_layer_workspace_size", "dspark_mla_layer_fwd",
            "dspark_mla_layer_fwd_ex", "dspark_mla_layer_tune", "dspark_mla_layer_read_status", "dspark_loss_workspace_size",
@@ -110,6 +110,8 @@ def _load():
     lib.dspark_attn_fwd.restype = i32
     lib.dspark_attn_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(Opts)]
     lib.dspark_attn_fwd_ex.restype = i32
+    lib.dspark_attn_fwd_noalloc.argtypes = [pd] + [vp] * 8 + [vp, vp, vp, vp, vp]
+    lib.dspark_attn_fwd_noalloc.restype = i32
     lib.dspark_attn_plan.argtypes = [pd, ctypes.POINTER(Opts)] + [ctypes.POINTER(i32)] * 3
     lib.dspark_attn_plan.restype = i32
     lib.dspark_attn_bwd_workspace_size.argtypes = [pd]
@@ -275,6 +277,24 @@ def attn_fwd(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk,
     opts, _arr = _opts(stage_events, force_generic, chunk_blocks, aux_stream, aux_events,
                        one_launch)
     _check(lib.dspark_attn_fwd_ex(*args, ctypes.byref(opts)))
+
+
+STATUS_BYTES = 64
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def attn_fwd_noalloc(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
+                     anchors, keep, out, status=None, stream=None) -> None:
+    """dspark_attn_fwd_noalloc: the forward in the library's fixed per-device
+    scratch array (no workspace).  status: None or a device tensor of at
+    least STATUS_BYTES that receives the status words (read it with
+    read_device_status)."""
+    if status is not None:
+        assert status.numel() * status.element_size() >= STATUS_BYTES
+    args = [ctypes.byref(desc)] + [_ptr(t) for t in (q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk,
+                                                     kr_blk, w_uk, w_uv, anchors, keep, out,
+                                                     status)]
+    _check(lib.dspark_attn_fwd_noalloc(*args, _stream(stream)))
 
 
 class BoundFwd:

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "bwd.hpp"
@@ -191,42 +192,100 @@ WsLayout path_layout(const dspark_attn_desc& d, FwdPath path) {
     return ws_layout(d, path == FwdPath::kMaterialised, path == FwdPath::kFused);
 }
 
-}  // namespace
 
-void set_last_error(const char* msg) { g_last_error = msg; }
+// ---------------------------------------------------------------------------
+// the allocation-free forward: a fixed scratch array on every device
+// ---------------------------------------------------------------------------
 
-}  // namespace dspark
+constexpr size_t kFixedScratchBytes = DSPARK_NOALLOC_SCRATCH_BYTES;
+static_assert(kFixedScratchBytes % 256 == 0, "scratch size must be a multiple of 256");
 
-using namespace dspark;
+// Held by every device the library runs on until the process ends.  In host
+// code this name is only a stand-in for the symbol: kernels are given the
+// address scratch_address() looked up for the current device.
+static __device__ __align__(256) unsigned char scratch[kFixedScratchBytes];
 
-extern "C" {
-
-int32_t dspark_abi_version(void) { return DSPARK_ABI_VERSION; }
-
-const char* dspark_last_error(void) { return g_last_error.c_str(); }
-
-size_t dspark_attn_workspace_size(const dspark_attn_desc* desc) {
-    bool empty = false;
-    if (check_desc(desc, &empty) != DSPARK_OK) return 0;
-    g_last_error.clear();
-    const size_t any = ws_layout(*desc, is_fast_path(*desc)).total;
-    const size_t fused = is_fast_path(*desc) ? ws_layout(*desc, false, true).total : 0;
-    return any > fused ? any : fused;
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+dspark_status scratch_address(void** out) {
+    static std::mutex mu;
+    static void* addr[64];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(DSPARK_EUNSUPPORTED, "device ordinal %d >= 64", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the scratch array");
+        if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255u) != 0)
+            return fail(DSPARK_EHIP, "scratch array address %p is not 256-byte aligned", ptr);
+        addr[dev] = ptr;
+    }
+    *out = addr[dev];
+    return DSPARK_OK;
 }
 
-size_t dspark_attn_workspace_size_ex(const dspark_attn_desc* desc, const dspark_attn_opts* opts) {
-    bool empty = false;
-    if (check_desc(desc, &empty) != DSPARK_OK) return 0;
-    g_last_error.clear();
-    return path_layout(*desc, pick_path(*desc, opts, false)).total;
+// Per-block bytes of q_abs plus o_lat on the MFMA path (5 query rows x H x D
+// bf16, twice).
+size_t latent_bytes_per_block(const dspark_attn_desc& d) {
+    return 2 * (size_t)kBlock * d.n_heads * d.d_latent * 2;
 }
 
-dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nope,
-                                 const void* q_rope, const void* ckv_ctx, const void* kr_ctx,
-                                 const void* ckv_blk, const void* kr_blk, const void* w_uk,
-                                 const void* w_uv, const int32_t* anchors, const uint8_t* keep,
-                                 void* out, void* workspace, size_t ws_bytes, void* stream,
-                                 const dspark_attn_opts* opts) {
+// Layout of the fixed scratch: the index for every block as in the
+// caller-workspace layout, then on the MFMA path the q_abs / o_lat rows of
+// one round of *round_blocks kept blocks (as many as fit; no RoPE table,
+// which that path does not read), on the generic path the RoPE table.  A
+// total above kFixedScratchBytes means the shape does not fit.
+WsLayout fixed_layout(const dspark_attn_desc& d, bool mfma, int* round_blocks) {
+    WsLayout L = ws_layout(d, false);
+    *round_blocks = 0;
+    if (!mfma) return L;
+    const size_t per = latent_bytes_per_block(d);
+    const size_t index_end = L.rope;
+    const size_t room = kFixedScratchBytes > index_end + 512 ? kFixedScratchBytes - index_end - 512
+                                                             : 0;
+    const long long blocks = (long long)d.B * d.N;
+    long long r = (long long)(room / per);
+    if (r > blocks) r = blocks;
+    if (r < 1) r = 1;   // one block: the total then tells whether it fits
+    *round_blocks = (int)r;
+    const size_t lat = (size_t)r * per / 2;
+    L.rope_rows = 0;
+    L.qabs = index_end;
+    L.olat = align256(L.qabs + lat);
+    L.total = align256(L.olat + lat);
+    return L;
+}
+
+// The workspace a round of kept slots [slot0, ...) sees when its latent rows
+// start at the beginning of the latent area: the kernels address row
+// 5 * slot + query, so the bases move back by slot0 blocks.  The shifted
+// bases are only ever offset forward again by at least slot0 blocks.
+Workspace round_latents(Workspace w, const Problem& p, int slot0) {
+    const uintptr_t back = (uintptr_t)slot0 * kBlock * p.H * p.D * sizeof(bf16);
+    w.qabs = reinterpret_cast<bf16*>(reinterpret_cast<uintptr_t>(w.qabs) - back);
+    w.olat = reinterpret_cast<bf16*>(reinterpret_cast<uintptr_t>(w.olat) - back);
+    return w;
+}
+
+// The forward behind dspark_attn_fwd_ex and dspark_attn_fwd_noalloc.  With
+// `fixed` set, the workspace is the library's per-device scratch array: the
+// MFMA path then runs in rounds whose q_abs / o_lat rows start at the array's
+// latent area (rows are addressed relative to the round), one round after
+// another on `stream`.
+struct FixedScratch {
+    void* base;         // device address of the array on the current device
+    int32_t* status;    // the caller's status words, or NULL
+};
+
+dspark_status forward_impl(const dspark_attn_desc* desc, const void* q_nope, const void* q_rope,
+                           const void* ckv_ctx, const void* kr_ctx, const void* ckv_blk,
+                           const void* kr_blk, const void* w_uk, const void* w_uv,
+                           const int32_t* anchors, const uint8_t* keep, void* out,
+                           void* workspace, size_t ws_bytes, void* stream,
+                           const dspark_attn_opts* opts, const FixedScratch* fixed) {
     bool empty = false;
     dspark_status st = check_desc(desc, &empty);
     if (st != DSPARK_OK) return st;
@@ -244,7 +303,16 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
     }
     const FwdPath path = pick_path(d, opts, true);
     const bool fast = path != FwdPath::kGeneric;
-    const WsLayout L = path_layout(d, path);
+    int round_blocks = 0;
+    const WsLayout L = fixed ? fixed_layout(d, fast, &round_blocks) : path_layout(d, path);
+    if (fixed) {
+        if (L.total > kFixedScratchBytes)
+            return fail(DSPARK_EUNSUPPORTED,
+                        "this shape needs %zu bytes of scratch; the fixed scratch array holds %zu",
+                        L.total, kFixedScratchBytes);
+        workspace = fixed->base;
+        ws_bytes = kFixedScratchBytes;
+    }
     st = check_workspace(workspace, ws_bytes, L.total);
     if (st != DSPARK_OK) return st;
 
@@ -255,7 +323,8 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
                         "shape needs %zu bytes of LDS in the generic kernel (max 65536)",
                         generic_lds_bytes(p));
     }
-    const Workspace ws = carve(workspace, L);
+    Workspace ws = carve(workspace, L);
+    if (fixed && fixed->status) ws.status = fixed->status;
     const Inputs in{q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv, out};
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* const* ev = (opts && opts->stage_events) ? opts->stage_events : nullptr;
@@ -264,7 +333,7 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
     };
 
     const bool fused = path == FwdPath::kFused;
-    const int chunk = chunk_blocks(d, opts);
+    const int chunk = fixed ? round_blocks : chunk_blocks(d, opts);
     const int n_chunks = (fast && !fused) ? (d.B * d.N + chunk - 1) / chunk : 0;
     const int n_events = (fast && !fused) ? 2 + 4 * n_chunks : 3;
     if (ev && opts->n_stage_events < n_events)
@@ -315,13 +384,14 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
             hipStream_t st = (aux && (c & 1)) ? aux : s;
             const Chunk ch{c * chunk, chunk};
             if ((e = mark_on(2 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-            if ((e = launch_absorb(p, in, ws, ch, st)) != hipSuccess)
+            const Workspace wr = fixed ? round_latents(ws, p, ch.slot0) : ws;
+            if ((e = launch_absorb(p, in, wr, ch, st)) != hipSuccess)
                 return hip_fail(e, "absorb launch");
             if ((e = mark_on(3 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-            if ((e = launch_attn(p, in, ws, ch, theta, st)) != hipSuccess)
+            if ((e = launch_attn(p, in, wr, ch, theta, st)) != hipSuccess)
                 return hip_fail(e, "attention launch");
             if ((e = mark_on(4 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-            if ((e = launch_uv(p, in, ws, ch, st)) != hipSuccess)
+            if ((e = launch_uv(p, in, wr, ch, st)) != hipSuccess)
                 return hip_fail(e, "W_UV launch");
             if ((e = mark_on(5 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
         }
@@ -336,6 +406,72 @@ dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nop
         if ((e = mark(2)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
     return ok();
+}
+
+}  // namespace
+
+void set_last_error(const char* msg) { g_last_error = msg; }
+
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" {
+
+int32_t dspark_abi_version(void) { return DSPARK_ABI_VERSION; }
+
+const char* dspark_last_error(void) { return g_last_error.c_str(); }
+
+size_t dspark_attn_workspace_size(const dspark_attn_desc* desc) {
+    bool empty = false;
+    if (check_desc(desc, &empty) != DSPARK_OK) return 0;
+    g_last_error.clear();
+    const size_t any = ws_layout(*desc, is_fast_path(*desc)).total;
+    const size_t fused = is_fast_path(*desc) ? ws_layout(*desc, false, true).total : 0;
+    return any > fused ? any : fused;
+}
+
+size_t dspark_attn_workspace_size_ex(const dspark_attn_desc* desc, const dspark_attn_opts* opts) {
+    bool empty = false;
+    if (check_desc(desc, &empty) != DSPARK_OK) return 0;
+    g_last_error.clear();
+    return path_layout(*desc, pick_path(*desc, opts, false)).total;
+}
+
+dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nope,
+                                 const void* q_rope, const void* ckv_ctx, const void* kr_ctx,
+                                 const void* ckv_blk, const void* kr_blk, const void* w_uk,
+                                 const void* w_uv, const int32_t* anchors, const uint8_t* keep,
+                                 void* out, void* workspace, size_t ws_bytes, void* stream,
+                                 const dspark_attn_opts* opts) {
+    return forward_impl(desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
+                        anchors, keep, out, workspace, ws_bytes, stream, opts, nullptr);
+}
+
+dspark_status dspark_attn_fwd_noalloc(const dspark_attn_desc* desc, const void* q_nope,
+                                      const void* q_rope, const void* ckv_ctx,
+                                      const void* kr_ctx, const void* ckv_blk,
+                                      const void* kr_blk, const void* w_uk, const void* w_uv,
+                                      const int32_t* anchors, const uint8_t* keep, void* out,
+                                      int32_t* status, void* stream) {
+    bool empty = false;
+    dspark_status st = check_desc(desc, &empty);
+    if (st != DSPARK_OK) return st;
+    if (empty) return ok();
+    if (status && (reinterpret_cast<uintptr_t>(status) & 3u) != 0)
+        return fail(DSPARK_EINVAL, "status must be 4-byte aligned");
+    // the size check needs no device: reject what does not fit first
+    int round_blocks = 0;
+    const WsLayout L = fixed_layout(*desc, is_fast_path(*desc), &round_blocks);
+    if (L.total > kFixedScratchBytes)
+        return fail(DSPARK_EUNSUPPORTED,
+                    "this shape needs %zu bytes of scratch; the fixed scratch array holds %zu",
+                    L.total, kFixedScratchBytes);
+    FixedScratch fx{nullptr, status};
+    st = scratch_address(&fx.base);
+    if (st != DSPARK_OK) return st;
+    return forward_impl(desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
+                        anchors, keep, out, nullptr, 0, stream, nullptr, &fx);
 }
 
 dspark_status dspark_attn_plan(const dspark_attn_desc* desc, const dspark_attn_opts* opts,

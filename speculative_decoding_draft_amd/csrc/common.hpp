@@ -27,6 +27,7 @@ constexpr int kMaxKeys = kMaxWindow - 1 + kBlock;   // 132
 // Status area of the workspace (int32 words).  Word 2 belongs to the
 // backward (unsorted anchors); word 3 records a stalled fused pipeline.
 enum StatusWord { kStKeptCount = 0, kStFirstBad = 1, kStPipeFault = 3, kStWords = 16 };
+static_assert(kStWords * 4 == DSPARK_STATUS_BYTES, "status area size");
 
 // Fused forward (GLM dims on a 256-CU, 8-XCD gfx950).  Each XCD owns 8 of
 // the 64 heads; the query latents and attention outputs of its heads travel

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert set(sd.EXPORTS) == declared
-    assert sd.abi_version() == 11
+    assert sd.abi_version() == 12
 
 
 def glm_desc(**kw):
@@ -393,3 +393,27 @@ def test_decode_and_verify_validation_before_any_launch():
         p[i] = None
         assert vcall(p, 0x7000000, need) == sd.DSPARK_EINVAL
     assert vcall(ptrs, 0x7000000, need - 1) == sd.DSPARK_EWORKSPACE
+
+
+@pytest.mark.parametrize("shape", [
+    dict(N=2_000_000),                 # index alone (36 bytes a block) is over 64 MiB
+    dict(S=300_000, window=256),       # generic path: RoPE table over 64 MiB
+])
+def test_noalloc_forward_rejects_shapes_beyond_its_scratch(shape):
+    """The allocation-free forward refuses, before touching a device, any
+    shape whose index and latent round (or RoPE table) exceed the fixed
+    array; a shape that fits gets past that check (and then fails on the
+    NULL tensors here)."""
+    d = glm_desc(**shape)
+    st = sd._lib.lib.dspark_attn_fwd_noalloc(ctypes.byref(d), *([None] * 12), None)
+    assert st == sd.DSPARK_EUNSUPPORTED
+    assert "scratch" in sd.last_error()
+    assert sd.NOALLOC_SCRATCH_BYTES == 64 << 20 and sd.STATUS_BYTES == 64
+
+
+def test_noalloc_forward_checks_status_alignment_and_empty_problems():
+    d = glm_desc(N=0)
+    assert sd._lib.lib.dspark_attn_fwd_noalloc(ctypes.byref(d), *([None] * 12), None) == 0
+    d = glm_desc()
+    st = sd._lib.lib.dspark_attn_fwd_noalloc(ctypes.byref(d), *([None] * 11), 0x1002, None)
+    assert st == sd.DSPARK_EINVAL and "status" in sd.last_error()
