@@ -2,22 +2,32 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
 
-A step is one dspark_attn_fwd call (index build and padding fill, absorb,
-attention, W_UV) over the whole workload, with inputs resident in HBM.  The
-default workload is the S=32768, N=1024 headline configuration (25% padding
-blocks, 5% clamped windows, synthetic N(0,1) activations and N(0,1/512)
-weights).  Prints one JSON line.
+A step is one dspark_attn_fwd call per layer (index build and padding fill,
+absorb, attention, W_UV) over the whole workload, with inputs resident in
+HBM and the L2 not flushed between steps.  The headline workload is the
+S=32768, N=1024 configuration (25% padding blocks, 5% clamped windows,
+synthetic N(0,1) activations and N(0,1/512) weights).  Prints one JSON line.
 
-Timing: warm-up steps (at least W and at least 100 ms of them: the clocks
-take tens of milliseconds to settle), then K timed steps between two
-synchronisations.
-Per-kernel durations come from HIP events that the library records on the
-launch stream between its kernels; they are recorded on every 10th timed step
-only (--event-every), since each event orders the kernels around it.
+Timing of the headline workload: exactly W warm-up steps; then 50 samples
+of 10 back-to-back steps with one hipEvent on the launch stream between
+samples (none inside a sample: an event between two calls delays the next
+one by several microseconds), whose median time per step gives `value` and
+`ms_per_step`; for several layers, a pass with events at layer boundaries
+(per-layer medians); then a separate pass of calls with the library's stage
+events between its kernels (per-kernel durations for the roofline); then
+exactly K steps with no event at all between two synchronisations, whose
+mean is reported as timing.timed_loop_ms_per_step.  The other four
+configurations are measured the same way first and reported in the
+`configs` object.
 
 Useful FLOP count only what the absorbed method must compute for kept blocks
 and visible keys: per kept block 5*H*(2*d_c*D + 2*(D+d_r)*v + 2*D*v + 2*D*d_v)
-with v = min(A, W-1) + 5.
+with v = min(A, W-1) + 5.  The roofline object takes the kernel with the
+largest share of the step against the bf16 MFMA peak (its useful FLOP per
+launch over its average launch duration), and compares the forward's
+measured HBM traffic (rocprofv3 counters, when the kernels' sources are
+those they were taken on) with the bytes the method needs (inputs read
+once, output written once).
 
 The same line carries a "backward" object: dspark_attn_bwd on the same
 inputs with a seeded upstream gradient (--bwd-steps timed calls), its useful
@@ -50,7 +60,8 @@ sys.path.insert(0, ROOT)
 MI355X_BF16_PEAK_TFLOPS = 2516.6     # 256 CU * 2.4 GHz * 4096 FLOP/CU/clk, dense
 MI355X_HBM_PEAK_GBS = 8000.0
 STAGES = ("index+fill", "absorb", "attention", "w_uv")
-KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.hip"}
+KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.hip",
+                  "index+fill": "prep.hip"}
 # Measured HBM bytes per launch on the headline workload (one round of all
 # blocks): rocprofv3 --pmc FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors from a
 # plain 256 MiB device copy), with the digest of the kernel's sources when the
@@ -629,23 +640,32 @@ def cpu_baseline(wl, anchors, keep, budget_s: float = 15.0):
         n_blocks *= 2
     flop = sum(useful_flop([anchors[b, n]], [1], wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v)
                for b, n in done)
-    try:
-        import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info())
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    return {"value": flop / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    blas = blas_info()
+    return {"value": flop / spent / 1e12, "unit": "TFLOP/s", "cores": blas["threads"],
             "kind": "oracle", "blocks_per_s": len(done) / spent,
+            "host_cores": len(os.sched_getaffinity(0)), "blas": blas["name"],
+            "blas_threads": blas["threads"], "precision": "fp64",
             "sample": f"{len(done)} random kept blocks of the same workload "
                       f"(fp64 numpy, gathered form, {spent:.1f} s)"}
 
 
-def _oracle_threads() -> int:
+def blas_info() -> dict:
+    """The BLAS library numpy's products run on and its thread count (the
+    oracle's only multi-threaded part)."""
     try:
         import threadpoolctl
-        return int(max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()))
+        libs = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            i = libs[0]
+            return {"name": f"{i.get('internal_api', '?')} {i.get('version', '')}".strip(),
+                    "threads": int(i.get("num_threads", 1))}
     except Exception:
-        return len(os.sched_getaffinity(0))
+        pass
+    return {"name": "unknown", "threads": len(os.sched_getaffinity(0))}
+
+
+def _oracle_threads() -> int:
+    return blas_info()["threads"]
 
 
 def _grow(run, items, budget_s, start=2):
@@ -745,20 +765,222 @@ def decode_cpu_baseline(budget_s, K=5, vocab=154880):
                                         f"fp64 numpy, {spent:.1f} s)"}
 
 
+# ---------------------------------------------------------------------------
+# the forward: one workload, timed three ways
+# ---------------------------------------------------------------------------
+
+def kernel_useful_flop(anchors, keep, W, H, D, d_c, d_r, d_v, block=5) -> dict:
+    """The useful FLOP of each forward kernel (the split of useful_flop):
+    absorb 2 d_c D, attention 2 (D + d_r) v + 2 D v, W_UV 2 D d_v per query
+    row and head."""
+    rows = v_rows = 0
+    for a, k in zip(np.asarray(anchors).ravel(), np.asarray(keep).ravel()):
+        if k:
+            rows += block
+            v_rows += block * (min(int(a), W - 1) + block)
+    return {"absorb": rows * H * 2 * d_c * D,
+            "attention": v_rows * H * (2 * (D + d_r) + 2 * D),
+            "w_uv": rows * H * 2 * D * d_v}
+
+
+def forward_algorithmic_bytes(wl, anchors, keep) -> int:
+    """HBM bytes the method itself needs per forward call (inputs read once,
+    output written once; bf16 = 2 B, fp32 = 4 B): the q^C and q^R rows of
+    kept blocks, the context rows in the union of the kept windows, the
+    kept blocks' own key rows, W_UK and W_UV, the anchors and keep flags,
+    and every output row (zeros for padding blocks)."""
+    H, D, dc, dr, dv = wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v
+    el = 2 if wl.dtype == "bf16" else 4
+    kept_rows = 5 * int(np.asarray(keep).sum())
+    union = 0
+    for b in range(wl.B):
+        cover = np.zeros(wl.S, dtype=bool)
+        for n in range(wl.N):
+            if keep[b, n]:
+                a = int(anchors[b, n])
+                cover[max(0, a - wl.W + 1):a] = True
+        union += int(cover.sum())
+    return (kept_rows * H * (dc + dr) * el + (union + kept_rows) * (D + dr) * el
+            + H * (dc + dv) * D * el + wl.B * wl.N * 5 + wl.B * 5 * wl.N * H * dv * el)
+
+
+def prepare_forward(sd, torch, wl, chunk_blocks=0, aux_stream=False):
+    """Anchors, device tensors of every layer, outputs, workspace and one
+    bound call per layer."""
+    from workloads.device import upload_anchors, upload_layer
+    if wl.anchor_source == "sampler":
+        anchors = np.zeros((wl.B, wl.N), np.int32)
+        keep = np.zeros((wl.B, wl.N), np.uint8)
+        for b in range(wl.B):
+            anchors[b], keep[b] = sd.select_anchors_host(wl.loss_mask[b], wl.N,
+                                                         wl.sampler_seed + b)
+    else:
+        anchors, keep = wl.anchors, wl.keep
+    L = len(wl.layers)
+    tensors = [upload_layer(wl, i) for i in range(L)]
+    a_dev, k_dev = upload_anchors(anchors, keep)
+    desc = sd.make_desc(B=wl.B, S=wl.S, N=wl.N, window=wl.W, n_heads=wl.H, d_latent=wl.D,
+                        d_nope=wl.d_c, d_rope=wl.d_r, d_v=wl.d_v, rope_base=wl.rope_base,
+                        dtype=wl.dtype)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    outs = [torch.empty((wl.B, wl.q_len, wl.H, wl.d_v), dtype=tdt, device="cuda")
+            for _ in range(L)]
+    ws = torch.empty(sd.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    sptr = int(torch.cuda.current_stream().cuda_stream)
+    n_chunks, chunk, n_ev = sd.attn_plan(desc, chunk_blocks=chunk_blocks)
+    aux, aux_ev = None, None
+    if aux_stream and n_chunks > 1:
+        aux = torch.cuda.Stream()
+        aux_ev = HIP.create(2)
+    calls = [sd.BoundFwd(desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"],
+                         t["kr_blk"], t["w_uk"], t["w_uv"], a_dev, k_dev, outs[l], ws, stream=sptr,
+                         chunk_blocks=chunk_blocks, n_stage_events=n_ev, aux_stream=aux,
+                         aux_events=aux_ev)
+             for l, t in enumerate(tensors)]
+    return dict(wl=wl, anchors=anchors, keep=keep, tensors=tensors, a_dev=a_dev, k_dev=k_dev,
+                desc=desc, outs=outs, ws=ws, sptr=sptr, calls=calls, n_chunks=n_chunks,
+                chunk=chunk, n_ev=n_ev, aux=aux, aux_ev=aux_ev, L=L)
+
+
+def stage_times(ev, n_ev, n_chunks, live):
+    """Per-stage milliseconds of one instrumented call from its stage events:
+    the index build, then absorb / attention / W_UV summed over the call's
+    rounds (and each live round's own), or the generic kernel."""
+    if n_ev == 3:      # generic path: [0] index + RoPE table [1] kernel [2]
+        return {"index+rope": HIP.elapsed_ms(ev[0], ev[1]),
+                "generic": HIP.elapsed_ms(ev[1], ev[2])}, None
+    out = {STAGES[0]: HIP.elapsed_ms(ev[0], ev[1])}
+    per_round = {s: [] for s in STAGES[1:]}
+    for c in range(n_chunks):
+        marks = (ev[2 + 4 * c], ev[3 + 4 * c], ev[4 + 4 * c], ev[5 + 4 * c])
+        for k, s in enumerate(STAGES[1:]):
+            ms = HIP.elapsed_ms(marks[k], marks[k + 1])
+            out[s] = out.get(s, 0.0) + ms
+            if c < live:
+                per_round[s].append(ms)
+    return out, per_round
+
+
+def measure_forward(torch, fw, steps, warmup, samples, sample_steps, stage_steps):
+    """Warm-up (exactly `warmup` steps), then:
+      1. `samples` samples of `sample_steps` back-to-back steps, with one
+         hipEvent on the launch stream between samples (none inside one):
+         the median over samples of the time per step;
+      2. for several layers, 50 steps with an event at every layer boundary
+         (per-layer medians);
+      3. `stage_steps` calls per layer with the library's stage events
+         between its kernels (those events order the kernels around them,
+         so they stay out of the other passes);
+      4. exactly `steps` steps with no event at all, between two
+         synchronisations (its mean is reported beside the median).
+    A step is one forward call per layer."""
+    calls, L, sptr = fw["calls"], fw["L"], fw["sptr"]
+    for _ in range(warmup):
+        for call in calls:
+            call()
+    st, fb = fw["sd"].read_device_status(fw["ws"], stream=sptr)
+    assert st == 0, fw["sd"].last_error()
+    # 1. samples
+    marks = HIP.create(samples + 1)
+    HIP.record(marks[0], sptr)
+    for i in range(samples):
+        for _ in range(sample_steps):
+            for call in calls:
+                call()
+        HIP.record(marks[i + 1], sptr)
+    torch.cuda.synchronize()
+    per_step = np.array([HIP.elapsed_ms(marks[j], marks[j + 1]) for j in range(samples)])
+    per_step /= sample_steps
+    HIP.destroy(marks)
+    # 2. layers
+    layer_ms = None
+    if L > 1:
+        n = 50
+        marks = HIP.create(n * L + 1)
+        HIP.record(marks[0], sptr)
+        for i in range(n):
+            for l, call in enumerate(calls):
+                call()
+                HIP.record(marks[i * L + l + 1], sptr)
+        torch.cuda.synchronize()
+        lay = np.array([HIP.elapsed_ms(marks[j], marks[j + 1])
+                        for j in range(n * L)]).reshape(n, L)
+        HIP.destroy(marks)
+        layer_ms = [float(np.median(lay[:, l])) for l in range(L)]
+    # 3. stage pass
+    n_ev, n_chunks = fw["n_ev"], fw["n_chunks"]
+    live = n_chunks if n_ev == 3 else min(n_chunks, -(-int(fw["keep"].sum()) // fw["chunk"]))
+    per_stage, per_round = {}, None
+    ev = HIP.create(stage_steps * L * n_ev)
+    for i in range(stage_steps):
+        for l, call in enumerate(calls):
+            call.with_events(ev[(i * L + l) * n_ev:(i * L + l + 1) * n_ev])
+    torch.cuda.synchronize()
+    for j in range(stage_steps * L):
+        tot, rounds = stage_times(ev[j * n_ev:(j + 1) * n_ev], n_ev, n_chunks, live)
+        for s, v in tot.items():
+            per_stage.setdefault(s, []).append(v)
+        if rounds is not None:
+            if per_round is None:
+                per_round = {s: [] for s in rounds}
+            for s, v in rounds.items():
+                per_round[s].append(v)
+    HIP.destroy(ev)
+    # 4. the timed loop
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for call in calls:
+            call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return {"median_ms": float(np.median(per_step)), "p10_ms": float(np.percentile(per_step, 10)),
+            "p90_ms": float(np.percentile(per_step, 90)), "layer_median_ms": layer_ms,
+            "loop_mean_ms": wall / max(steps, 1) * 1e3,
+            "stage_us": {s: float(np.mean(v)) * 1e3 for s, v in per_stage.items()},
+            "launch_us": ({s: float(np.mean(v)) * 1e3 for s, v in per_round.items()}
+                          if per_round else None),
+            "live_rounds": live}
+
+
+def config_summary(k, fw, m) -> dict:
+    """Compact per-configuration record for the `configs` object."""
+    wl, anchors, keep = fw["wl"], fw["anchors"], fw["keep"]
+    flop = useful_flop(anchors, keep, wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v) * fw["L"]
+    kept = int(keep.sum()) * fw["L"]
+    med = m["median_ms"] * 1e-3
+    out = {"workload": wl.name, "dtype": wl.dtype, "kept_blocks": kept,
+           "useful_gflop": round(flop / 1e9, 3), "median_ms": round(m["median_ms"], 4),
+           "tflops": round(flop / med / 1e12, 2), "blocks_per_s": round(kept / med, 1),
+           "frac_of_bf16_peak": round(flop / med / 1e12 / MI355X_BF16_PEAK_TFLOPS, 4),
+           "stage_us": {s: round(v, 1) for s, v in m["stage_us"].items()}}
+    if m["layer_median_ms"]:
+        out["layer_median_ms"] = [round(v, 4) for v in m["layer_median_ms"]]
+    return out
+
+
+HIP = None
+
+
 def main():
+    global HIP
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--min-warmup-ms", type=float, default=100.0,
-                    help="keep warming up until this much time has passed")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--samples", type=int, default=50,
+                    help="samples whose median time per step is reported (at least 50)")
+    ap.add_argument("--sample-steps", type=int, default=10,
+                    help="back-to-back steps per sample (events only between samples)")
+    ap.add_argument("--stage-steps", type=int, default=10,
+                    help="calls of the separate pass that records the library's stage events")
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--chunk-blocks", type=int, default=0,
                     help="kept blocks per kernel round (0: the library default)")
     ap.add_argument("--aux-stream", action="store_true",
                     help="run odd kernel rounds on a second stream (with --chunk-blocks)")
-    ap.add_argument("--event-every", type=int, default=10,
-                    help="record per-kernel stage events on every n-th timed step")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other four configurations (the 'configs' object)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the backward measurement (the 'backward' object)")
@@ -803,145 +1025,110 @@ def main():
     import torch
     import workloads as wk
     import speculative_decoding_draft_amd as sd
-    from workloads.device import upload_anchors, upload_layer
 
+    HIP = HipEvents()
+    samples = max(args.samples, 50)
+    R = max(args.sample_steps, 1)
+
+    # the other configurations first, each freed before the next
+    configs = {}
+    if not args.no_configs:
+        for k in (1, 2, 3, 4, 5):
+            if k == args.config:
+                continue
+            log_progress(f"config {k}")
+            fw = prepare_forward(sd, torch, wk.config(k))
+            fw["sd"] = sd
+            m = measure_forward(torch, fw, 0, args.warmup, samples, R, 5)
+            configs[str(k)] = config_summary(k, fw, m)
+            del fw
+            torch.cuda.empty_cache()
+
+    log_progress(f"config {args.config} (headline line)")
     wl = wk.config(args.config)
-    if wl.anchor_source == "sampler":
-        anchors = np.zeros((wl.B, wl.N), np.int32)
-        keep = np.zeros((wl.B, wl.N), np.uint8)
-        for b in range(wl.B):
-            anchors[b], keep[b] = sd.select_anchors_host(wl.loss_mask[b], wl.N, wl.sampler_seed + b)
-    else:
-        anchors, keep = wl.anchors, wl.keep
-    L = len(wl.layers)
-    tensors = [upload_layer(wl, i) for i in range(L)]
-    a_dev, k_dev = upload_anchors(anchors, keep)
-    desc = sd.make_desc(B=wl.B, S=wl.S, N=wl.N, window=wl.W, n_heads=wl.H, d_latent=wl.D,
-                        d_nope=wl.d_c, d_rope=wl.d_r, d_v=wl.d_v, rope_base=wl.rope_base,
-                        dtype=wl.dtype)
-    outs = [torch.empty((wl.B, wl.q_len, wl.H, wl.d_v), dtype=torch.bfloat16, device="cuda")
-            for _ in range(L)]
-    ws = torch.empty(sd.workspace_size(desc), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-    sptr = int(stream.cuda_stream)
-    hip = HipEvents()
+    fw = prepare_forward(sd, torch, wl, args.chunk_blocks, args.aux_stream)
+    fw["sd"] = sd
+    anchors, keep, L = fw["anchors"], fw["keep"], fw["L"]
     K = args.steps
-    n_chunks, chunk_blocks, n_ev = sd.attn_plan(desc, chunk_blocks=args.chunk_blocks)
-    # chunks past the number of kept blocks exit at once; time only real ones
-    live = min(n_chunks, -(-int(keep.sum()) // chunk_blocks))
-    aux, aux_ev = None, None
-    if args.aux_stream and n_chunks > 1:
-        aux = torch.cuda.Stream()
-        aux_ev = hip.create(2)
-    calls = [sd.BoundFwd(desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"],
-                         t["kr_blk"], t["w_uk"], t["w_uv"], a_dev, k_dev, outs[l], ws, stream=sptr,
-                         chunk_blocks=args.chunk_blocks, n_stage_events=n_ev, aux_stream=aux,
-                         aux_events=aux_ev)
-             for l, t in enumerate(tensors)]
-    # Stage events are recorded on every `event_every`-th timed step only:
-    # each event is a barrier between kernels, so recording them on every
-    # step would lengthen the steps being timed.
-    ev_steps = list(range(0, K, max(1, args.event_every)))
-    ev = hip.create(len(ev_steps) * L * n_ev)
-
-    # warm-up: at least W steps and at least --min-warmup-ms of them, so that
-    # the timed steps run at the clocks the GPU settles at under this load
-    warm_steps, warm_t0 = 0, time.perf_counter()
-    while (warm_steps < args.warmup or
-           (time.perf_counter() - warm_t0) * 1e3 < args.min_warmup_ms):
-        for call in calls:
-            call()
-        warm_steps += 1
-        if warm_steps % 10 == 0:
-            torch.cuda.synchronize()
-    st, fb = sd.read_device_status(ws, stream=sptr)
-    assert st == 0, sd.last_error()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e_i = 0
-    for i in range(K):
-        if e_i < len(ev_steps) and ev_steps[e_i] == i:
-            for l, call in enumerate(calls):
-                call.with_events(ev[(e_i * L + l) * n_ev:(e_i * L + l + 1) * n_ev])
-            e_i += 1
-        else:
-            for call in calls:
-                call()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # per instrumented call: stage time summed over its chunks; per launch:
-    # each chunk's
-    launch_us = {s: [[] for _ in range(live)] for s in STAGES[1:]}
-    per_stage = {s: [] for s in STAGES}
-    call_ms = []
-    for i in range(len(ev_steps) * L):
-        e = ev[i * n_ev:(i + 1) * n_ev]
-        call_ms.append(max(hip.elapsed_ms(e[0], e[5 + 4 * c]) for c in range(n_chunks)))
-        per_stage[STAGES[0]].append(hip.elapsed_ms(e[0], e[1]))
-        tot = {s: 0.0 for s in STAGES[1:]}
-        for c in range(n_chunks):
-            marks = (e[2 + 4 * c], e[3 + 4 * c], e[4 + 4 * c], e[5 + 4 * c])
-            for k, s in enumerate(STAGES[1:]):
-                ms = hip.elapsed_ms(marks[k], marks[k + 1])
-                tot[s] += ms
-                if c < live:
-                    launch_us[s][c].append(ms * 1e3)
-        for s in STAGES[1:]:
-            per_stage[s].append(tot[s])
-    hip.destroy(ev)
-    if aux_ev:
-        hip.destroy(aux_ev)
+    m = measure_forward(torch, fw, K, args.warmup, samples, R, args.stage_steps)
+    configs[str(args.config)] = config_summary(args.config, fw, m)
 
     flop = useful_flop(anchors, keep, wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v) * L
     kept_blocks = int(keep.sum()) * L
-    ms_per_step = wall / K * 1e3
-    value = flop / (wall / K) / 1e12
-    stage_avg_us = {s: float(np.mean(v)) * 1e3 for s, v in per_stage.items()}
-    sbytes = stage_bytes(wl, anchors, keep, chunk_blocks)
-    dom = max(("absorb", "attention", "w_uv"), key=lambda s: stage_avg_us[s])
-    # achieved = algorithmic bytes per launch / average launch duration, over
-    # the live launches of the dominant kernel
-    avg_launch_us = float(np.mean([np.mean(v) for v in launch_us[dom]]))
-    avg_launch_bytes = float(np.mean(sbytes[dom][:live]))
-    achieved = avg_launch_bytes / (avg_launch_us * 1e-6) / 1e9
+    med_s = m["median_ms"] * 1e-3
+    value = flop / med_s / 1e12
+    stage_us = m["stage_us"]
+    fast = "attention" in stage_us
     result = {
         "metric": "DSpark draft-attn fwd useful TFLOP/s + blocks/s at S=32K, N=1024 (1 GPU)",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": warm_steps,
-        "warmup_requested": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "warmup": args.warmup,
+        "ms_per_step": round(m["median_ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "S": wl.S, "N": wl.N, "W": wl.W,
                    "heads": wl.H, "layers": L, "kept_blocks_per_layer": int(keep.sum()),
                    "parallelism": "none (1 GPU)"},
-        "blocks_per_s": round(kept_blocks / (wall / K), 1),
+        "timing": {"value_from": f"median over {samples} samples of {R} back-to-back steps "
+                                 f"(one hipEvent on the launch stream between samples)",
+                   "p10_ms": round(m["p10_ms"], 4), "p90_ms": round(m["p90_ms"], 4),
+                   "timed_loop_ms_per_step": round(m["loop_mean_ms"], 4),
+                   "timed_loop": f"{K} steps, no events, synchronised on both sides",
+                   "stage_events": f"separate pass of {args.stage_steps} calls",
+                   "l2_flushed": False},
+        "blocks_per_s": round(kept_blocks / med_s, 1),
         "frac_of_bf16_peak": round(value / MI355X_BF16_PEAK_TFLOPS, 4),
         "useful_gflop_per_step": round(flop / 1e9, 3),
-        "gpu_event_us_per_call": round(float(np.mean(call_ms)) * 1e3, 2),
-        "event_steps": len(ev_steps),
-        "stage_us": {s: round(v, 2) for s, v in stage_avg_us.items()},
-        "chunks": {"chunk_blocks": chunk_blocks, "launches_per_kernel": live,
-                   "streams": 2 if aux is not None else 1},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": MI355X_HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / MI355X_HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(dom, wl.name, chunk_blocks, wl.B * wl.N),
-                     "avg_launch_us": round(avg_launch_us, 2),
-                     "algorithmic_bytes_per_launch": round(avg_launch_bytes)},
+        "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
+        "chunks": {"chunk_blocks": fw["chunk"], "launches_per_kernel": m["live_rounds"],
+                   "streams": 2 if fw["aux"] is not None else 1},
+        "roofline": None,
         "cpu_baseline": None,
     }
+    if fast:
+        # the dominant kernel against the bf16 MFMA peak: its useful FLOP per
+        # launch / its average launch duration (stage events)
+        kflop = kernel_useful_flop(anchors, keep, wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v)
+        live = m["live_rounds"]
+        dom = max(("absorb", "attention", "w_uv"), key=lambda s: stage_us[s])
+        avg_launch_us = m["launch_us"][dom]
+        flop_per_launch = kflop[dom] / live
+        achieved = flop_per_launch / (avg_launch_us * 1e-6) / 1e12
+        impl = stage_bytes(wl, anchors, keep, fw["chunk"])
+        impl_bytes = float(np.mean(impl[dom][:live]))
+        n_blocks = wl.B * wl.N
+        measured = {s: measured_traffic(s, wl.name, fw["chunk"], n_blocks)
+                    for s in ("index+fill", "absorb", "attention", "w_uv")}
+        fwd_alg = forward_algorithmic_bytes(wl, anchors, keep)
+        fwd_meas = (sum(measured.values()) if all(v is not None for v in measured.values())
+                    else None)
+        result["roofline"] = {
+            "kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+            "peak": MI355X_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
+            "traffic": measured[dom], "avg_launch_us": round(avg_launch_us, 2),
+            "useful_flop_per_launch": int(flop_per_launch),
+            "implementation_bytes_per_launch": round(impl_bytes),
+            "implementation_gbs": round(impl_bytes / (avg_launch_us * 1e-6) / 1e9, 1),
+            "forward": {"algorithmic_bytes": fwd_alg, "measured_traffic": fwd_meas,
+                        "traffic_ratio": (round(fwd_meas / fwd_alg, 3) if fwd_meas else None),
+                        "useful_flop": int(flop / L),
+                        "intensity_flop_per_byte": round(flop / L / fwd_alg, 1)}}
+    if not args.no_cpu_baseline:
+        log_progress("cpu baseline")
+        result["cpu_baseline"] = cpu_baseline(wl, anchors, keep, args.cpu_budget)
+    tensors, a_dev, k_dev, desc, sptr = fw["tensors"], fw["a_dev"], fw["k_dev"], fw["desc"], fw["sptr"]
     if not args.no_bwd and wl.dtype == "bf16":
+        log_progress("backward")
         try:
             result["backward"] = bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors,
-                                                keep, desc, sptr, hip, args.bwd_steps,
+                                                keep, desc, sptr, HIP, args.bwd_steps,
                                                 train_step=not args.no_train_step)
             if not args.no_cpu_baseline:
                 result["backward"]["cpu_baseline"] = bwd_cpu_baseline(wl, anchors, keep,
@@ -949,16 +1136,18 @@ def main():
         except Exception as e:   # the forward line is still reported
             result["backward"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_layer and wl.dtype == "bf16":
+        log_progress("layer")
         try:
             result["layer"] = bench_layer(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep,
-                                          desc, sptr, hip, args.layer_steps, tune=not args.no_tune)
+                                          desc, sptr, HIP, args.layer_steps, tune=not args.no_tune)
             if not args.no_cpu_baseline:
                 result["layer"]["cpu_baseline"] = layer_cpu_baseline(args.side_budget)
         except Exception as e:   # the forward line is still reported
             result["layer"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_loss and wl.dtype == "bf16":
+        log_progress("loss")
         try:
-            result["loss"] = bench_loss(sd, torch, wl, anchors, keep, sptr, hip, args.loss_steps,
+            result["loss"] = bench_loss(sd, torch, wl, anchors, keep, sptr, HIP, args.loss_steps,
                                         tune=not args.no_tune)
             if not args.no_cpu_baseline:
                 result["loss"]["cpu_baseline"] = loss_cpu_baseline(wl, anchors, keep,
@@ -966,15 +1155,20 @@ def main():
         except Exception as e:   # the forward line is still reported
             result["loss"] = {"error": f"{type(e).__name__}: {e}"}
     if not args.no_decode and wl.dtype == "bf16":
+        log_progress("decode")
         try:
-            result["decode"] = bench_decode(sd, torch, hip, args.decode_steps)
+            result["decode"] = bench_decode(sd, torch, HIP, args.decode_steps)
             if not args.no_cpu_baseline:
                 result["decode"]["cpu_baseline"] = decode_cpu_baseline(args.side_budget)
         except Exception as e:   # the forward line is still reported
             result["decode"] = {"error": f"{type(e).__name__}: {e}"}
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, anchors, keep, args.cpu_budget)
+    # last, so that it stays in view at the end of the line
+    result["configs"] = {k: configs[k] for k in sorted(configs)}
     print(json.dumps(result), flush=True)
+
+
+def log_progress(what: str) -> None:
+    print(f"[bench] {what}", file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

@@ -12,7 +12,9 @@
 // One workgroup stages the block's keys (<= 127 context rows + 5 block rows,
 // c^KV 512 + rotated k^R 64 each, ~152 KB) in LDS once and shares them across
 // all heads it owns; each wave owns 16 heads, i.e. 80 (query, head) rows as 5
-// MFMA column tiles of 16 heads (one per query).  Scores are computed
+// MFMA column tiles of 16 heads (one per query).  With few blocks, a
+// workgroup owns 16 heads and each of its five waves one query (one column
+// tile), so that four workgroups per block finish sooner.  Scores are computed
 // transposed (keys x rows) so that the probabilities land in registers in the
 // layout the P.V MFMA takes as its B operand; V^T fragments come straight out
 // of the row-major c^KV tile with ds_read_b64_tr_b16.  With at most 132 keys
@@ -29,7 +31,7 @@ constexpr int kKrStride = kDr + 8;    // bf16 per staged k^R row (144 B)
 constexpr int kMaxKt = (kMaxKeys + 15) / 16;   // 9 key tiles
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int WAVES>
+template <int WAVES, int QW>
 __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     const bf16* __restrict__ q_rope, const bf16* __restrict__ ckv_ctx,
     const bf16* __restrict__ kr_ctx, const bf16* __restrict__ ckv_blk,
@@ -44,7 +46,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     __shared__ double turns[kDr / 2];        // theta_i / 2pi
 
     constexpr int kThreads = WAVES * 64;
-    constexpr int kGroups = 4 / WAVES;        // workgroups per block
+    // QW = 5: each wave owns 16 heads and all 5 queries (a workgroup owns
+    // 16 * WAVES heads).  QW = 1: five waves share 16 heads and each owns one
+    // query, so that a workgroup finishes ~5x sooner when few blocks leave
+    // most compute units idle.
+    static_assert(QW == kBlock || WAVES * QW == kBlock, "queries per wave");
+    constexpr int kHeadGroups = (QW == kBlock) ? WAVES : 1;   // 16-head groups per workgroup
+    constexpr int kGroups = 4 / kHeadGroups;  // workgroups per block
     // live slots of this chunk; the grid covers the chunk's capacity, so
     // spread the live ones evenly over the XCDs
     const int n_here = min(nslots, status[kStKeptCount] - slot0);
@@ -54,13 +62,14 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     // and first reads the o_lat rows written last (still in the Infinity
     // Cache)
     const int local = n_here - 1 - lid / kGroups;   // slot within the chunk
-    const int hg0 = (lid % kGroups) * WAVES;  // first 16-head group of this workgroup
+    const int hg0 = (lid % kGroups) * kHeadGroups;  // first 16-head group of this workgroup
     const int tid = threadIdx.x;
     // wave index as a scalar: the key staging below selects its source
     // tensor per wave, which must be visible to the compiler as uniform
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
-    const int head = (hg0 + wave) * 16 + l16;   // this lane's head (B-operand column)
+    const int head = (hg0 + (QW == kBlock ? wave : 0)) * 16 + l16;   // B-operand column
+    const int tq0 = (QW == kBlock) ? 0 : wave * QW;   // this wave's first query
     for (int i = tid; i < kDr / 2; i += kThreads) turns[i] = turns_per_pos.t[i];
     __syncthreads();
 
@@ -70,11 +79,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     constexpr int kPf = 3;                         // prefetch distance (k-steps)
     static_assert(kPf <= kD / 32, "prefetched k-steps are latent ones");
     const bf16* qa = q_abs + ((size_t)kBlock * (slot0 + local) * kH + head) * kD + g * 8;
-    bf16x8 qbuf[kPf][kBlock];
+    bf16x8 qbuf[kPf][QW];
 #pragma unroll
     for (int p = 0; p < kPf; ++p)
 #pragma unroll
-        for (int t = 0; t < kBlock; ++t) qbuf[p][t] = gld16(qa + (size_t)t * kH * kD + p * 32);
+        for (int t = 0; t < QW; ++t) qbuf[p][t] = gld16(qa + (size_t)(tq0 + t) * kH * kD + p * 32);
 
     const int4 rec = srec[slot0 + local];      // {ctx_lo, ctx_len, pos0, block}
     const int blk = rec.w;
@@ -135,12 +144,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     // A fixed number of copies per wave (slots past the last key receive a
     // copy of the last key and are never read) keeps the wait counts after
     // this loop exact.  The buffer form of the copy is counted by vmcnt only.
-    static_assert(kMaxKeys % WAVES == 0, "slots per wave");
+    constexpr int kSlotsPerWave = (kMaxKeys + WAVES - 1) / WAVES;
     const __amdgpu_buffer_rsrc_t ctx_rsrc = buffer_rsrc(ckv_ctx, ctx_bytes);
     const __amdgpu_buffer_rsrc_t blk_rsrc = buffer_rsrc(ckv_blk, blk_bytes);
 #pragma unroll
-    for (int i = 0; i < kMaxKeys / WAVES; ++i) {
+    for (int i = 0; i < kSlotsPerWave; ++i) {
         const int slot = wave + i * WAVES;
+        if (kMaxKeys % WAVES != 0 && slot >= kMaxKeys) break;   // uniform per wave
         const int s = (slot < nkeys) ? slot : nkeys - 1;
         const bool is_ctx = s < ctx_len;
         const uint32_t row =
@@ -151,8 +161,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
 
     const bf16* qr = q_rope + (qrow0 * kH + head) * kDr + g * 8;
     auto q_frag = [&](int ks, int t) -> bf16x8 {
-        return (ks < kD / 32) ? gld16(qa + (size_t)t * kH * kD + ks * 32)
-                              : gld16(qr + (size_t)t * kH * kDr + (ks - kD / 32) * 32);
+        return (ks < kD / 32) ? gld16(qa + (size_t)(tq0 + t) * kH * kD + ks * 32)
+                              : gld16(qr + (size_t)(tq0 + t) * kH * kDr + (ks - kD / 32) * 32);
     };
 
     if constexpr (kKrIters == 1) {
@@ -172,11 +182,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     __syncthreads();
 
     // ---- scores, transposed: St[kt][t] = keys (16 kt + 4g + i) x head, query t
-    f32x4 st[kMaxKt][kBlock];
+    f32x4 st[kMaxKt][QW];
 #pragma unroll
     for (int kt = 0; kt < kMaxKt; ++kt)
 #pragma unroll
-        for (int t = 0; t < kBlock; ++t) st[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < QW; ++t) st[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     int krow[kMaxKt];
 #pragma unroll
@@ -202,20 +212,20 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     for (int kt = 0; kt < kMaxKt; ++kt) acur[kt] = a_frag(0, kt);
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) {
-        bf16x8 bq[kBlock];
+        bf16x8 bq[QW];
 #pragma unroll
-        for (int t = 0; t < kBlock; ++t) bq[t] = qbuf[ks % kPf][t];
+        for (int t = 0; t < QW; ++t) bq[t] = qbuf[ks % kPf][t];
         if (ks + kPf < kKs) {
 #pragma unroll
-            for (int t = 0; t < kBlock; ++t) qbuf[ks % kPf][t] = q_frag(ks + kPf, t);
+            for (int t = 0; t < QW; ++t) qbuf[ks % kPf][t] = q_frag(ks + kPf, t);
         }
         if (ks >= kD / 32) {
             const int kr = ks - kD / 32;
 #pragma unroll
-            for (int t = 0; t < kBlock; ++t) {
+            for (int t = 0; t < QW; ++t) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float2 cs = qcs[t * (kDr / 2) + kr * 16 + g * 4 + q];
+                    const float2 cs = qcs[(tq0 + t) * (kDr / 2) + kr * 16 + g * 4 + q];
                     const float x0 = (float)bq[t][2 * q], x1 = (float)bq[t][2 * q + 1];
                     bq[t][2 * q] = (bf16)(x0 * cs.x - x1 * cs.y);
                     bq[t][2 * q + 1] = (bf16)(x0 * cs.y + x1 * cs.x);
@@ -231,7 +241,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
 #pragma unroll
         for (int kt = 0; kt < kMaxKt; ++kt)
 #pragma unroll
-            for (int t = 0; t < kBlock; ++t) st[kt][t] = mfma_16x16x32(acur[kt], bq[t], st[kt][t]);
+            for (int t = 0; t < QW; ++t) st[kt][t] = mfma_16x16x32(acur[kt], bq[t], st[kt][t]);
         __builtin_amdgcn_sched_barrier(0);
         if (ks + 1 < kKs) {
 #pragma unroll
@@ -249,7 +259,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
 #pragma unroll
         for (int kt = 0; kt < kMaxKt - 1; ++kt)
 #pragma unroll
-            for (int t = 0; t < kBlock; ++t)
+            for (int t = 0; t < QW; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (kt * 16 + g * 4 + i >= nkeys) st[kt][t][i] = -INFINITY;
@@ -259,10 +269,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
         return st[kt][t][i];
     };
     const float c2 = scale * kLog2e;
-    float inv[kBlock];
-    bf16x4 pr[kMaxKt][kBlock];
+    float inv[QW];
+    bf16x4 pr[kMaxKt][QW];
 #pragma unroll
-    for (int t = 0; t < kBlock; ++t) {
+    for (int t = 0; t < QW; ++t) {
         float m = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < kMaxKt; ++kt)
@@ -314,11 +324,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     for (int mt = 0; mt < 4; ++mt) vcur[mt] = v_frag(0, 0, mt);
 #pragma unroll
     for (int c = 0; c < kD / 64; ++c) {
-        f32x4 o[4][kBlock];
+        f32x4 o[4][QW];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int t = 0; t < kBlock; ++t) o[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < QW; ++t) o[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < kKk; ++kk) {
             const bool last = (c == kD / 64 - 1) && (kk == kKk - 1);
@@ -334,14 +344,14 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                    for (int t = 0; t < kBlock; ++t)
+                    for (int t = 0; t < QW; ++t)
                         o[mt][t] = mfma_16x16x32(vcur[mt], cat(pr[2 * kk][t], pr[2 * kk + 1][t]), o[mt][t]);
             } else {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     const bf16x4 lo = __builtin_shufflevector(vcur[mt], vcur[mt], 0, 1, 2, 3);
 #pragma unroll
-                    for (int t = 0; t < kBlock; ++t) o[mt][t] = mfma_16x16x16(lo, pr[2 * kk][t], o[mt][t]);
+                    for (int t = 0; t < QW; ++t) o[mt][t] = mfma_16x16x16(lo, pr[2 * kk][t], o[mt][t]);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -351,7 +361,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
             }
         }
 #pragma unroll
-        for (int t = 0; t < kBlock; ++t) {
+        for (int t = 0; t < QW; ++t) {
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
                 const f32x4 a0 = o[2 * pp][t], a1 = o[2 * pp + 1][t];
@@ -361,7 +371,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
                     v[i] = (bf16)(a0[i] * inv[t]);
                     v[4 + i] = (bf16)(a1[i] * inv[t]);
                 }
-                gst16(ol + (size_t)t * kH * kD + c * 64 + pp * 32, v);
+                gst16(ol + (size_t)(tq0 + t) * kH * kD + c * 64 + pp * 32, v);
             }
         }
     }
@@ -371,8 +381,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
 
 hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
                        const RopeTheta& th, hipStream_t s) {
-    // few blocks: split the 64 heads over four single-wave workgroups so that
-    // more compute units take part
+    // few blocks: four workgroups per block (16 heads each, one wave per
+    // query) so that more compute units take part
     const uint32_t ctx_bytes = (uint32_t)((size_t)p.B * p.S * kD * sizeof(bf16));
     const uint32_t blk_bytes = (uint32_t)((size_t)p.B * p.L5 * kD * sizeof(bf16));
     RopeTheta turns{};
@@ -382,13 +392,13 @@ hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, 
     int grid = c.nslots * groups;
     grid = (grid + 7) / 8 * 8;
     if (split) {
-        hipLaunchKernelGGL(attn_kernel<1>, dim3(grid), dim3(64), 0, s, (const bf16*)in.q_rope,
+        hipLaunchKernelGGL((attn_kernel<kBlock, 1>), dim3(grid), dim3(kBlock * 64), 0, s, (const bf16*)in.q_rope,
                            (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
                            (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.srec,
                            ws.status, ws.qabs, ws.olat, p.S, p.N, p.L5,
                            c.slot0, c.nslots, p.scale, ctx_bytes, blk_bytes, turns);
     } else {
-        hipLaunchKernelGGL(attn_kernel<4>, dim3(grid), dim3(256), 0, s, (const bf16*)in.q_rope,
+        hipLaunchKernelGGL((attn_kernel<4, kBlock>), dim3(grid), dim3(256), 0, s, (const bf16*)in.q_rope,
                            (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
                            (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.srec,
                            ws.status, ws.qabs, ws.olat, p.S, p.N, p.L5,
