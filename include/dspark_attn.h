@@ -161,7 +161,13 @@ typedef struct dspark_attn_opts {
      * training step runs the forward on the backward's workspace: its
      * layout begins with the forward's).  The backward then reuses the
      * forward's block index, q_abs and o_lat instead of rebuilding them
-     * (dW_UV then uses the forward's o_lat rows). */
+     * (dW_UV then uses the forward's o_lat rows).  This is checked on the
+     * device: the index build of a forward (or of a backward without this
+     * option) tags the workspace with its descriptor and path, and a
+     * backward whose workspace does not carry the tag of this descriptor on
+     * the path it takes (MFMA or generic; the one-launch forward leaves no
+     * latents and never matches) writes NaN to every gradient and
+     * dspark_read_device_status then returns DSPARK_EINVAL. */
     int32_t reuse_forward;
     /* dspark_attn_fwd_ex on the MFMA shapes, nonzero: the one-launch
      * forward instead of the three kernels (ignored with chunk_blocks or
@@ -649,8 +655,10 @@ dspark_status dspark_spec_verify(const dspark_verify_desc* desc, const float* dr
 /* Synchronises `stream`, then reads the status area of a workspace used by
  * the last dspark_attn_fwd / dspark_attn_bwd / dspark_build_index on it.  Returns DSPARK_OK, or
  * DSPARK_EANCHOR with *first_bad_block = b*N + n of the first kept block
- * whose anchor was outside [0, S-2] (-1 when none).  first_bad_block may be
- * NULL. */
+ * whose anchor was outside [0, S-2] (-1 when none); DSPARK_EINVAL after a
+ * dspark_attn_bwd_ex with reuse_forward on a workspace that held no forward
+ * of its descriptor and path (its gradients are NaN); DSPARK_EHIP after a
+ * stalled one-launch forward.  first_bad_block may be NULL. */
 dspark_status dspark_read_device_status(const void* workspace, void* stream,
                                         int32_t* first_bad_block);
 

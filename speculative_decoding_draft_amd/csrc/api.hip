@@ -188,6 +188,24 @@ FwdPath pick_path(const dspark_attn_desc& d, const dspark_attn_opts* o, bool che
     return FwdPath::kFused;
 }
 
+// status[kStPathTag] written by a forward on the given path: a hash of the
+// descriptor with the path in its low two bits (never 0).  A backward with
+// reuse_forward expects the tag of the path it takes.
+int32_t forward_tag(const dspark_attn_desc& d, FwdPath path) {
+    uint32_t h = 2166136261u;
+    auto mix = [&](const void* v, size_t n) {
+        const unsigned char* c = static_cast<const unsigned char*>(v);
+        for (size_t i = 0; i < n; ++i) h = (h ^ c[i]) * 16777619u;
+    };
+    const int32_t f[] = {d.B, d.S, d.N, d.window, d.n_heads, d.d_latent, d.d_nope, d.d_rope,
+                         d.d_v, d.dtype};
+    mix(f, sizeof(f));
+    mix(&d.rope_base, sizeof(d.rope_base));
+    mix(&d.softmax_scale, sizeof(d.softmax_scale));
+    const uint32_t code = path == FwdPath::kMaterialised ? 1u : path == FwdPath::kGeneric ? 2u : 3u;
+    return (int32_t)((h & ~3u) | code);
+}
+
 WsLayout path_layout(const dspark_attn_desc& d, FwdPath path) {
     return ws_layout(d, path == FwdPath::kMaterialised, path == FwdPath::kFused);
 }
@@ -356,7 +374,8 @@ dspark_status forward_impl(const dspark_attn_desc* desc, const void* q_nope, con
     if (fused) {
         // index, padding rows and the pipeline's control words, then the
         // whole forward in one launch
-        if ((e = launch_prep(p, anchors, keep, ws, nullptr, 0, nullptr, out, s)) != hipSuccess)
+        if ((e = launch_prep(p, anchors, keep, ws, nullptr, 0, nullptr, out, s,
+                             forward_tag(d, path))) != hipSuccess)
             return hip_fail(e, "index / fill launch");
         if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
         if ((e = launch_fused(p, in, ws, theta, s)) != hipSuccess)
@@ -366,8 +385,9 @@ dspark_status forward_impl(const dspark_attn_desc* desc, const void* q_nope, con
     }
     // the MFMA path evaluates RoPE inside the attention kernel; only the
     // generic path reads the table
+    // the fixed scratch is never handed to a backward: no tag
     if ((e = launch_prep(p, anchors, keep, ws, nullptr, L.rope_rows, fast ? nullptr : &theta,
-                         fast ? out : nullptr, s)) != hipSuccess)
+                         fast ? out : nullptr, s, fixed ? 0 : forward_tag(d, path))) != hipSuccess)
         return hip_fail(e, "index / RoPE table / fill launch");
     if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if (fast) {
@@ -605,12 +625,18 @@ dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc, const void* q_nop
     // reuse_forward: the forward on this workspace left the index (and, on the
     // MFMA path, q_abs) in the same places; those launches are skipped (their
     // stage events are still recorded)
+    // reuse_forward is checked on the device: a workspace whose last index
+    // build was not for this descriptor and path gets an all-padding index
+    // here and NaN gradients at the end (dspark_read_device_status reports
+    // it); the backward's own index build leaves the same tag, since its
+    // launches also leave the index and the latents a forward would
     const bool reuse = opts && opts->reuse_forward;
+    const int32_t tag = forward_tag(d, fast ? FwdPath::kMaterialised : FwdPath::kGeneric);
     if (reuse) {
-        if ((e = mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        DSPARK_STEP(launch_bwd_reuse_check(p, w, tag, s), "reuse check launch");
     } else {
         DSPARK_STEP(launch_prep(p, anchors, keep, w.fwd, nullptr, L.fwd.rope_rows,
-                                fast ? nullptr : &theta, nullptr, s),
+                                fast ? nullptr : &theta, nullptr, s, tag),
                     "index launch");
     }
     if (fast) DSPARK_STEP(launch_bwd_order(p, w, s), "anchor-order launch");
@@ -631,12 +657,16 @@ dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc, const void* q_nop
         DSPARK_STEP(launch_bwd_generic(p, d.dtype == DSPARK_BF16, in, g, w, s),
                     "generic backward launch");
     }
-    if (fast)
-        DSPARK_STEP(launch_bwd_gather(p, g, w, theta, s), "final backward launch");
-    else
-        DSPARK_STEP(launch_bwd_finalize(p, d.dtype == DSPARK_BF16, g, w, w.fwd.idx, w.fwd.rope,
-                                        theta, true, s),
-                    "final backward launch");
+    e = fast ? launch_bwd_gather(p, g, w, theta, s)
+             : launch_bwd_finalize(p, d.dtype == DSPARK_BF16, g, w, w.fwd.idx, w.fwd.rope, theta,
+                                   true, s);
+    if (e != hipSuccess) return hip_fail(e, "final backward launch");
+    if (reuse) {
+        const int elem = (fast || d.dtype == DSPARK_BF16) ? 2 : 4;
+        if ((e = launch_bwd_reuse_fill(p, g, w, elem, s)) != hipSuccess)
+            return hip_fail(e, "reuse fill launch");
+    }
+    if ((e = mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
 #undef DSPARK_STEP
     return ok();
 }
@@ -667,6 +697,10 @@ dspark_status dspark_read_device_status(const void* workspace, void* stream,
     if (words[kStFirstBad] >= 0)
         return fail(DSPARK_EANCHOR, "kept block %d has an anchor outside [0, S-2]",
                     words[kStFirstBad]);
+    if (words[kStReuseBad] != 0)
+        return fail(DSPARK_EINVAL,
+                    "reuse_forward: the workspace's last index build was not a forward of this "
+                    "descriptor on the path this backward takes; the gradients are NaN");
     if (words[kStPipeFault] != 0)
         return fail(DSPARK_EHIP,
                     "the one-launch forward stalled (a unit waited past its time bound); "

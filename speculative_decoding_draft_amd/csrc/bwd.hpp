@@ -93,6 +93,16 @@ constexpr int kStUnsorted = 2;
 // only_if: nullptr (always), or a status word -- the clear runs only when
 // that word is nonzero.
 hipError_t launch_bwd_zero(float* p, size_t n, const int32_t* only_if, hipStream_t s);
+// reuse_forward: unless status[kStPathTag] == expect, flags the call
+// (status[kStReuseBad] = 1) and turns the index into an all-padding one (no
+// kept block, every record padding) so that the launches after it read no
+// record of another forward.
+hipError_t launch_bwd_reuse_check(const Problem& p, const BwdWork& w, int32_t expect,
+                                  hipStream_t s);
+// On a flagged call, every element of the eight gradients becomes NaN;
+// otherwise the launch exits at once.  elem: 2 (bf16) or 4 (fp32) bytes.
+hipError_t launch_bwd_reuse_fill(const Problem& p, const BwdGrads& g, const BwdWork& w,
+                                 int elem, hipStream_t s);
 // One workgroup: sets status[kStUnsorted] from the slot records.
 hipError_t launch_bwd_order(const Problem& p, const BwdWork& w, hipStream_t s);
 // MFMA path final pass: per row, the block partials of the windows that

@@ -18,6 +18,8 @@
 //   dW_UV[h] += sum_j G (o_lat_j)^T,  dW_UK[h] += sum_j q^C_j (dq_abs_j)^T
 // The sums over heads and over the blocks whose windows share a context row
 // are accumulated in fp32 (device atomics).
+#include <algorithm>
+
 #include "bwd.hpp"
 
 namespace dspark {
@@ -37,6 +39,42 @@ __global__ void zero_kernel(float4* __restrict__ p, size_t n4, const int32_t* on
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
          i += (size_t)gridDim.x * blockDim.x)
         p[i] = z;
+}
+
+// A backward told to reuse the forward's index and latents checks that the
+// workspace's last index build was for this descriptor and path.
+__global__ __launch_bounds__(256) void reuse_check_kernel(int32_t* __restrict__ status,
+                                                          int4* __restrict__ idx, int total,
+                                                          int32_t expect) {
+    if (status[kStPathTag] == expect) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) status[kStReuseBad] = 0;
+        return;
+    }
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x)
+        idx[i] = make_int4(0, 0, 0, -1);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        status[kStReuseBad] = 1;
+        status[kStKeptCount] = 0;
+        status[kStFirstBad] = -1;
+    }
+}
+
+struct GradSpans {
+    void* ptr[8];
+    size_t n[8];      // elements
+};
+
+__global__ __launch_bounds__(256) void reuse_fill_kernel(const int32_t* __restrict__ status,
+                                                         GradSpans g, int elem) {
+    if (status[kStReuseBad] == 0) return;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (int t = 0; t < 8; ++t) {
+        if (!g.ptr[t]) continue;
+        for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < g.n[t]; i += stride) {
+            if (elem == 2) static_cast<uint16_t*>(g.ptr[t])[i] = 0x7FC0u;
+            else static_cast<uint32_t*>(g.ptr[t])[i] = 0x7FC00000u;
+        }
+    }
 }
 
 int vmax_of(const Problem& p) {
@@ -440,6 +478,26 @@ __global__ __launch_bounds__(256) void gather_kernel(
 }
 
 }  // namespace
+
+hipError_t launch_bwd_reuse_check(const Problem& p, const BwdWork& w, int32_t expect,
+                                  hipStream_t s) {
+    const int total = p.B * p.N;
+    const int grid = std::max(1, std::min(256, (total + 255) / 256));
+    hipLaunchKernelGGL(reuse_check_kernel, dim3(grid), dim3(256), 0, s, w.fwd.status, w.fwd.idx,
+                       total, expect);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_reuse_fill(const Problem& p, const BwdGrads& g, const BwdWork& w,
+                                 int elem, hipStream_t s) {
+    const size_t B = p.B, L5 = p.L5, S = p.S, H = p.H;
+    GradSpans sp{{g.dq_nope, g.dq_rope, g.dckv_ctx, g.dkr_ctx, g.dckv_blk, g.dkr_blk, g.dw_uk,
+                  g.dw_uv},
+                 {B * L5 * H * p.dc, B * L5 * H * p.dr, B * S * p.D, B * S * p.dr, B * L5 * p.D,
+                  B * L5 * p.dr, H * p.dc * p.D, H * p.dv * p.D}};
+    hipLaunchKernelGGL(reuse_fill_kernel, dim3(256), dim3(256), 0, s, w.fwd.status, sp, elem);
+    return hipGetLastError();
+}
 
 hipError_t launch_bwd_order(const Problem& p, const BwdWork& w, hipStream_t s) {
     hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, s, w.fwd.srec, w.fwd.status, p.N);

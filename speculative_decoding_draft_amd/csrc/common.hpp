@@ -26,7 +26,14 @@ constexpr int kMaxKeys = kMaxWindow - 1 + kBlock;   // 132
 
 // Status area of the workspace (int32 words).  Word 2 belongs to the
 // backward (unsorted anchors); word 3 records a stalled fused pipeline.
-enum StatusWord { kStKeptCount = 0, kStFirstBad = 1, kStPipeFault = 3, kStWords = 16 };
+// Word 2 belongs to the backward (anchor order).  kStPathTag: what the last
+// index build on this workspace was for (a hash of the descriptor and the
+// forward path; 0 when nothing may reuse it).  kStReuseBad: set by a backward
+// with reuse_forward whose workspace does not hold that tag.
+enum StatusWord {
+    kStKeptCount = 0, kStFirstBad = 1, kStPipeFault = 3, kStPathTag = 4, kStReuseBad = 5,
+    kStWords = 16
+};
 static_assert(kStWords * 4 == DSPARK_STATUS_BYTES, "status area size");
 
 // Fused forward (GLM dims on a 256-CU, 8-XCD gfx950).  Each XCD owns 8 of

@@ -40,9 +40,11 @@ struct Workspace {
 // Index build, and optionally (th != nullptr) the RoPE table and (out !=
 // nullptr) the rows of padding / invalid-anchor blocks, in one launch.
 // ws.ctl != nullptr: the fused path's control words are zeroed as well.
+// path_tag goes to status[kStPathTag] (0: the index is for no forward that
+// a backward may reuse).
 hipError_t launch_prep(const Problem& p, const int32_t* anchors, const uint8_t* keep,
                        const Workspace& ws, int32_t* index_copy, int rope_rows,
-                       const RopeTheta* th, void* out, hipStream_t s);
+                       const RopeTheta* th, void* out, hipStream_t s, int32_t path_tag = 0);
 hipError_t launch_generic(const Problem& p, bool bf16_io, const Inputs& in,
                           const Workspace& ws, hipStream_t s);
 size_t generic_lds_bytes(const Problem& p);

@@ -36,12 +36,16 @@ __device__ void build_index(int total, int S, int W, const int32_t* __restrict__
                             const uint8_t* __restrict__ keep, int4* __restrict__ idx,
                             int32_t* __restrict__ kept, int4* __restrict__ srec,
                             int32_t* __restrict__ status, int4* __restrict__ idx_copy,
-                            int32_t* __restrict__ ctl, int ctl_words) {
+                            int32_t* __restrict__ ctl, int ctl_words, int32_t path_tag) {
     __shared__ int wave_count[kIndexThreads / 64];
     __shared__ int first_bad_sh;
     const int tid = threadIdx.x;
     for (int i = tid; i < ctl_words; i += kIndexThreads) ctl[i] = 0;
-    if (tid == 0) status[kStPipeFault] = 0;
+    if (tid == 0) {
+        status[kStPipeFault] = 0;
+        status[kStPathTag] = path_tag;
+        status[kStReuseBad] = 0;
+    }
     const int lane = tid & 63;
     const int wave = tid >> 6;
     if (tid == 0) first_bad_sh = INT_MAX;
@@ -141,12 +145,12 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     int total, int S, int W, const int32_t* __restrict__ anchors,
     const uint8_t* __restrict__ keep, int4* __restrict__ idx, int32_t* __restrict__ kept,
     int4* __restrict__ srec, int32_t* __restrict__ status, int4* __restrict__ idx_copy,
-    int32_t* __restrict__ ctl, int ctl_words, long long rope_n, int pairs,
+    int32_t* __restrict__ ctl, int ctl_words, int32_t path_tag, long long rope_n, int pairs,
     RopeTheta th, float2* __restrict__ table, int rope_wgs, bf16* __restrict__ out, int N,
     int L5, int H, int dv) {
     if (blockIdx.x == 0) {
         build_index(total, S, W, anchors, keep, idx, kept, srec, status, idx_copy, ctl,
-                    ctl_words);
+                    ctl_words, path_tag);
         return;
     }
     const int r = blockIdx.x - 1;
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
 
 hipError_t launch_prep(const Problem& p, const int32_t* anchors, const uint8_t* keep,
                        const Workspace& ws, int32_t* index_copy, int rope_rows,
-                       const RopeTheta* th, void* out, hipStream_t s) {
+                       const RopeTheta* th, void* out, hipStream_t s, int32_t path_tag) {
     const int pairs = p.dr / 2;
     const long long rope_n = (th && pairs > 0) ? (long long)rope_rows * pairs : 0;
     constexpr long long kRopeWgs = 128, kFillWgs = 256;
@@ -177,7 +181,7 @@ hipError_t launch_prep(const Problem& p, const int32_t* anchors, const uint8_t* 
     hipLaunchKernelGGL(prep_kernel, dim3(1 + rope_wgs + fill_wgs), dim3(kPrepThreads), 0, s,
                        p.B * p.N, p.S, p.W, anchors, keep, ws.idx, ws.kept, ws.srec, ws.status,
                        reinterpret_cast<int4*>(index_copy), ws.ctl,
-                       ws.ctl ? kFusedCtlWords : 0, rope_n, pairs > 0 ? pairs : 1,
+                       ws.ctl ? kFusedCtlWords : 0, path_tag, rope_n, pairs > 0 ? pairs : 1,
                        th ? *th : none, ws.rope, rope_wgs, static_cast<bf16*>(out), p.N, p.L5,
                        p.H, p.dv);
     return hipGetLastError();

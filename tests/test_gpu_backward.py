@@ -281,3 +281,83 @@ def test_bwd_reusing_the_forward_workspace_is_bit_identical(generic):
             assert float((x - y).norm() / y.norm()) < 5e-3, n
         else:
             assert torch.equal(plain[n], reuse[n]), n
+
+
+def _bwd_setup(wl):
+    import torch
+    import speculative_decoding_draft_amd as sd
+    t = upload_layer(wl)
+    a, k = upload_anchors(wl.anchors, wl.keep)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dout = to_torch(wk.make_dout(wl, seed=11), wl.dtype, "cuda")
+    B, S, L5, H = wl.B, wl.S, wl.q_len, wl.H
+    shapes = {"dq_nope": (B, L5, H, wl.d_c), "dq_rope": (B, L5, H, wl.d_r),
+              "dckv_ctx": (B, S, wl.D), "dkr_ctx": (B, S, wl.d_r),
+              "dckv_blk": (B, L5, wl.D), "dkr_blk": (B, L5, wl.d_r),
+              "dw_uk": (H, wl.d_c, wl.D), "dw_uv": (H, wl.d_v, wl.D)}
+    g = {n: torch.full(v, 3.0, dtype=tdt, device="cuda") for n, v in shapes.items()}
+    ins = (t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"], t["kr_blk"],
+           t["w_uk"], t["w_uv"], a, k)
+    out = torch.empty((B, L5, H, wl.d_v), dtype=tdt, device="cuda")
+    return desc_for(wl), ins, dout, g, out
+
+
+@pytest.mark.parametrize("generic", [False, True])
+def test_bwd_all_padding_gives_zero_gradients(generic):
+    """No kept block: every gradient is exactly 0 and the status is OK."""
+    import torch
+    import speculative_decoding_draft_amd as sd
+    wl = wk.make_workload("bwd-all-pad", B=2, S=256, N=12, dims=wk.GLM_DIMS, dtype="bf16",
+                          recipe="uniform", seed=84)
+    wl.keep[:] = 0
+    wl.anchors[:] = -4
+    desc, ins, dout, g, _ = _bwd_setup(wl)
+    ws = torch.empty(sd.bwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    sd.attn_bwd(desc, *ins, dout, g, ws, force_generic=generic)
+    st, fb = sd.read_device_status(ws)
+    assert st == sd.DSPARK_OK and fb == -1, sd.last_error()
+    for n, v in g.items():
+        assert bool((v == 0).all()), n
+
+
+@pytest.mark.parametrize("case", ["fresh-workspace", "one-launch-forward", "generic-forward",
+                                  "generic-backward", "other-shape"])
+def test_bwd_reuse_forward_without_a_matching_forward_is_reported(case):
+    """reuse_forward on a workspace whose last index build was not a forward
+    of this descriptor on the backward's path: every gradient is NaN and the
+    status is DSPARK_EINVAL; a matching forward afterwards makes the same
+    call succeed again."""
+    import torch
+    import speculative_decoding_draft_amd as sd
+    wl = wk.scaled(4, S=700, N=24)
+    desc, ins, dout, g, out = _bwd_setup(wl)
+    other = wk.scaled(4, S=700, N=32)
+    desc2, ins2, _, _, out2 = _bwd_setup(other)
+    n_ws = max(sd.bwd_workspace_size(desc), sd.workspace_size(desc),
+               sd.bwd_workspace_size(desc2), sd.workspace_size(desc2))
+    ws = torch.full((n_ws,), 0x7f, dtype=torch.uint8, device="cuda")
+    generic_bwd = case == "generic-backward"
+    log(f"reuse mismatch: {case}")
+    if case == "one-launch-forward":
+        sd.attn_fwd(desc, *ins, out, ws, one_launch=True)
+    elif case == "generic-forward":
+        sd.attn_fwd(desc, *ins, out, ws, force_generic=True)
+    elif case == "generic-backward":
+        sd.attn_fwd(desc, *ins, out, ws)
+    elif case == "other-shape":
+        sd.attn_fwd(desc2, *ins2, out2, ws)
+    sd.attn_bwd(desc, *ins, dout, g, ws, force_generic=generic_bwd, reuse_forward=True)
+    st, _ = sd.read_device_status(ws)
+    assert st == sd.DSPARK_EINVAL, (st, sd.last_error())
+    assert "reuse_forward" in sd.last_error()
+    for n, v in g.items():
+        assert bool(torch.isnan(v).all()), n
+    # the matching forward, then the same backward: finite gradients, OK
+    sd.attn_fwd(desc, *ins, out, ws, force_generic=generic_bwd)
+    for v in g.values():
+        v.fill_(float("nan"))
+    sd.attn_bwd(desc, *ins, dout, g, ws, force_generic=generic_bwd, reuse_forward=True)
+    st, _ = sd.read_device_status(ws)
+    assert st == sd.DSPARK_OK, sd.last_error()
+    for n, v in g.items():
+        assert bool(torch.isfinite(v).all()), n
