@@ -67,10 +67,12 @@ KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.h
 # plain 256 MiB device copy), with the digest of the kernel's sources when the
 # counters were taken.  A kernel whose sources changed since reports null.
 PMC_TRAFFIC = {
-    "absorb": (358_772_658, "1173152b9dfcdc71"),
-    "attention": (583_589_770, "9a8efa059feee454"),
-    "w_uv": (394_468_171, "8759cdadabfffc32"),
+    "absorb": (358_772_745, "a6d94fd2f33133fb"),
+    "attention": (583_875_242, "00bb1efce6168c8c"),
+    "w_uv": (394_492_808, "cef85dda6f65640e"),
+    "index+fill": (42_090_290, "2d8e19e1157fcb65"),
 }
+PMC_SOURCE = "rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, profiles/attn_fwd_headline_S32768_N1024_counters.md"
 
 
 # The same for the backward's launches (dspark_attn_bwd on the headline
@@ -84,12 +86,12 @@ BWD_KERNEL_SOURCES = {
     "final": ("bwd_misc.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
 }
 BWD_PMC_TRAFFIC = {
-    "attention_bwd": (1_294_385_046, "e43a3e44ba46d298"),
-    "dw": (754_065_735, "5aa12cb6a28746ad"),
-    "dkv": (971_033_593, "5aa12cb6a28746ad"),
-    "dq_nope": (447_361_885, "5aa12cb6a28746ad"),
-    "d_olat": (394_457_779, "1173152b9dfcdc71"),
-    "final": (311_151_788, "5d5442f7c0774b7c"),
+    "attention_bwd": (1_294_418_918, "f8f1aae7fba2a88c"),
+    "dw": (753_790_011, "077c93ab989cf579"),
+    "dkv": (971_111_482, "077c93ab989cf579"),
+    "dq_nope": (447_395_984, "077c93ab989cf579"),
+    "d_olat": (394_457_734, "a6d94fd2f33133fb"),
+    "final": (311_162_276, "65f54a7ba8f69927"),
 }
 
 
@@ -98,9 +100,9 @@ BWD_PMC_TRAFFIC = {
 # three launches; 64 sequences, K = 5, V = 154880): the same FETCH/WRITE
 # scaling, with the files each is built from and their digest when taken.
 SIDE_PMC_TRAFFIC = {
-    "loss_stats": (3_882_423_906, ("loss.hip", "blas.hpp", "kernels.hpp"), "37ec07b962fc373b"),
-    "verify": (436_597_498 + 398_369_123 + 4_484_617, ("decode.hip", "kernels.hpp"),
-               "4c16bfd6e3c529be"),
+    "loss_stats": (3_882_426_288, ("loss.hip", "blas.hpp", "kernels.hpp"), "7f5f3a3869757f4a"),
+    "verify": (436_597_519 + 398_369_304 + 4_484_620, ("decode.hip", "kernels.hpp"),
+               "25552c1280c23bfe"),
 }
 
 
@@ -1112,7 +1114,8 @@ def main():
             "kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
             "peak": MI355X_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4),
-            "traffic": measured[dom], "avg_launch_us": round(avg_launch_us, 2),
+            "traffic": measured[dom], "traffic_source": PMC_SOURCE,
+            "avg_launch_us": round(avg_launch_us, 2),
             "useful_flop_per_launch": int(flop_per_launch),
             "implementation_bytes_per_launch": round(impl_bytes),
             "implementation_gbs": round(impl_bytes / (avg_launch_us * 1e-6) / 1e9, 1),

@@ -13,7 +13,7 @@
 // Work split: a workgroup (8 waves, two per SIMD) owns one head and a
 // strided range of 32-row iterations; wave w computes output dims
 // 32w .. 32w+31, transposed (dims x rows), with its 32 x 512 slice of
-// W_UV[h] resident in registers.  One workgroup covering all 256 dims reads
+// W_UV[h] resident in registers (staged through LDS at start).  One workgroup covering all 256 dims reads
 // every o_lat row once: splitting the dims over two workgroups made both
 // read it (the second read hits L2, but a read-only probe of this pattern
 // takes 47 us with two readers against 36 with one).  The o_lat rows of an iteration
@@ -72,18 +72,39 @@ __global__ __launch_bounds__(kUvWaves * 64) void uv_kernel(const bf16* __restric
     // MFMAs the lane with k-group g holds the 8 consecutive dims
     // 32*wave + 8g .. 32*wave + 8g + 7; k-values follow the permuted o_lat
     // order (dims 32ks + 4g + 0..3 and 32ks + 16 + 4g + 0..3).
+    // W_UV[h] reaches them through the ring slots (idle until the first
+    // o_lat copy) in two halves of 128 output dims: one 1 KB weight row per
+    // wave instruction, row r of a half at slot r / 32, row r % 32 (the
+    // ring's own row stride); the four waves whose dims a half holds then
+    // read their fragments out of LDS.  Loading the fragments straight from
+    // memory (8 bytes a lane from 16 rows per instruction) made a 64-block
+    // call ~6 us slower.
+    auto slot_of = [&](int k) -> char* { return k == 0 ? s0 : k == 1 ? s1 : k == 2 ? s2 : s3; };
     bf16x8 a[kUvKs][2];
 #pragma unroll
-    for (int vt = 0; vt < 2; ++vt) {
-        const bf16* wrow = w_uv +
-                           ((size_t)h * kDv + 32 * wave + 8 * (l16 >> 2) + 4 * vt +
-                            (l16 & 3)) * kD + 4 * g;
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int ks = 0; ks < kUvKs; ++ks) a[ks][vt] = cat(gld8(wrow + 32 * ks), gld8(wrow + 32 * ks + 16));
+        for (int i = 0; i < 128 / kUvWaves; ++i) {
+            const int r = wave * (128 / kUvWaves) + i;     // uniform per wave
+            async_copy_16(w_uv + ((size_t)h * kDv + 128 * half + r) * kD + lane * 8,
+                          slot_of(r / 32) + (r % 32) * kUvLdsStride);
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+        __syncthreads();
+        if (wave / 4 == half) {
+            const char* base = slot_of(wave % 4);
+#pragma unroll
+            for (int vt = 0; vt < 2; ++vt) {
+                const bf16* row = reinterpret_cast<const bf16*>(
+                    base + (8 * (l16 >> 2) + 4 * vt + (l16 & 3)) * kUvLdsStride);
+#pragma unroll
+                for (int ks = 0; ks < kUvKs; ++ks)
+                    a[ks][vt] = cat(ld8(row + 32 * ks + 4 * g), ld8(row + 32 * ks + 16 + 4 * g));
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __syncthreads();
     }
-    // complete here, before any copy is in flight: a wait for these inside
-    // the loop would also wait for every copy issued before it
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
     // Copy of the workgroup's k-th iteration into `dst`: wave w copies rows
     // 4w .. 4w+3, one o_lat row (1 KB) per instruction; rows past the end
