@@ -243,8 +243,8 @@ __global__ __launch_bounds__(256) void dqnope_kernel(const bf16* __restrict__ dq
 // four workgroups resident per compute unit) are consecutive per head in the
 // XCD-remapped order, so a head's tiles share the rows they stream through
 // one L2.
-using CfgDwuv = Cfg<256, 128, 2, 2, true, false, true, false, 2>;
-using CfgDwuk = Cfg<256, 64, 2, 2, true, false, true, false, 2>;
+using CfgDwuv = Cfg<128, 64, 2, 2, true, false, true, false, 2>;
+using CfgDwuk = Cfg<128, 64, 2, 2, true, false, true, false, 2>;
 constexpr int kSlotChunk = 2048;     // slots whose input rows one LDS table holds
 
 template <class C, int NOUT>
