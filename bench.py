@@ -382,21 +382,25 @@ def bench_layer(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sptr,
     args = (ld, hd, hc, w, a_dev, k_dev, out, ws)
     # pick the GEMM kernels for these shapes first (synchronous, seconds)
     t_tune = time.perf_counter()
-    (sd.mla_layer_tune if tune else sd.mla_layer_fwd)(*args, stream=sptr)
+    choices = None
+    if tune:
+        choices = sd.mla_layer_tune(*args, stream=sptr)
+    else:
+        sd.mla_layer_fwd(*args, stream=sptr)
     torch.cuda.synchronize()
     t_tune = time.perf_counter() - t_tune
     w0, n_w = time.perf_counter(), 0
     while n_w < 3 or (time.perf_counter() - w0) < 0.1:
-        sd.mla_layer_fwd(*args, stream=sptr)
+        sd.mla_layer_fwd(*args, stream=sptr, gemm_choices=choices)
         n_w += 1
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        sd.mla_layer_fwd(*args, stream=sptr)
+        sd.mla_layer_fwd(*args, stream=sptr, gemm_choices=choices)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     ev = hip.create(len(LAYER_STAGES) + 1)
-    sd.mla_layer_fwd(*args, stream=sptr, stage_events=ev)
+    sd.mla_layer_fwd(*args, stream=sptr, stage_events=ev, gemm_choices=choices)
     torch.cuda.synchronize()
     stage_us = {s: hip.elapsed_ms(ev[i], ev[i + 1]) * 1e3 for i, s in enumerate(LAYER_STAGES)}
     hip.destroy(ev)
@@ -405,6 +409,7 @@ def bench_layer(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sptr,
     ach = st_flop[dom] / (stage_us[dom] * 1e-6) / 1e12
     return {"ms_per_step": round(wall * 1e3, 4), "steps": steps, "warmup": n_w,
             "hidden": hidden, "q_rank": q_rank, "gemm_tuning_s": round(t_tune, 2),
+            "gemm_choices": choices.as_list() if choices is not None else None,
             "useful_gflop_per_step": round(flop / 1e9, 3),
             "value": round(flop / wall / 1e12, 3), "unit": "TFLOP/s",
             "frac_of_bf16_peak": round(flop / wall / 1e12 / MI355X_BF16_PEAK_TFLOPS, 4),
@@ -460,7 +465,11 @@ def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hid
     d = mk(counted)
     args = (d, t, terms, em, loss, ws)
     t_tune = time.perf_counter()
-    (sd.loss_tune if tune else sd.loss_fwd)(*args, stream=sptr)
+    choices = None
+    if tune:
+        choices = sd.loss_tune(*args, stream=sptr)
+    else:
+        sd.loss_fwd(*args, stream=sptr)
     torch.cuda.synchronize()
     t_tune = time.perf_counter() - t_tune
     st = sd.loss_read_status(ws, stream=sptr)
@@ -468,16 +477,16 @@ def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hid
         raise RuntimeError(f"loss status {st}")
     w0, n_w = time.perf_counter(), 0
     while n_w < 2 or (time.perf_counter() - w0) < 0.1:
-        sd.loss_fwd(*args, stream=sptr)
+        sd.loss_fwd(*args, stream=sptr, gemm_choices=choices)
         n_w += 1
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        sd.loss_fwd(*args, stream=sptr)
+        sd.loss_fwd(*args, stream=sptr, gemm_choices=choices)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     ev = hip.create(len(LOSS_STAGES) + 1)
-    sd.loss_fwd(*args, stream=sptr, stage_events=ev)
+    sd.loss_fwd(*args, stream=sptr, stage_events=ev, gemm_choices=choices)
     torch.cuda.synchronize()
     stage_us = {s: hip.elapsed_ms(ev[i], ev[i + 1]) * 1e3 for i, s in enumerate(LOSS_STAGES)}
     hip.destroy(ev)
@@ -492,6 +501,7 @@ def bench_loss(sd, torch, wl, anchors, keep, sptr, hip, steps, vocab=154880, hid
             "vocab": vocab, "hidden": hidden, "markov_rank": rank, "kept_blocks": kept,
             "logit_rows": 2 * counted,
             "counted_steps": live, "gemm_tuning_s": round(t_tune, 2),
+            "gemm_choices": choices.as_list() if choices is not None else None,
             "useful_gflop_per_step": round(flop / 1e9, 3),
             "value": round(flop / wall / 1e12, 3), "unit": "TFLOP/s",
             "frac_of_bf16_peak": round(flop / wall / 1e12 / MI355X_BF16_PEAK_TFLOPS, 4),

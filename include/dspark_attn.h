@@ -28,10 +28,11 @@
  *     16-byte aligned, unless the comment says "host";
  *   - the caller owns every buffer, including the workspace; the library
  *     allocates and frees no device memory of its own, so calls on different
- *     streams with different workspaces are independent.  The exceptions are
- *     named where they apply: the MLA block and the loss head create one
- *     rocBLAS handle per host thread and device on first use, and the
- *     *_tune calls record GEMM kernel choices in a process-wide table;
+ *     streams with different workspaces are independent.  The one exception:
+ *     the MLA block and the loss head create one rocBLAS handle per host
+ *     thread and device on first use (rocBLAS itself works in the caller's
+ *     workspace, and GEMM kernel choices live in a caller-owned
+ *     dspark_gemm_choices table);
  *   - `stream` is a hipStream_t (NULL = the default stream); device work is
  *     enqueued asynchronously and DSPARK_OK means "enqueued";
  *   - no C++ exception crosses the ABI; on error the function returns a
@@ -48,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 12
+#define DSPARK_ABI_VERSION 13
 
 typedef enum dspark_status {
     DSPARK_OK = 0,
@@ -127,6 +128,30 @@ dspark_status dspark_attn_fwd(const dspark_attn_desc* desc,
                               void* out, void* workspace, size_t ws_bytes,
                               void* stream);
 
+/* rocBLAS kernel choices for the GEMMs of one dspark_mla_layer_fwd_ex or
+ * dspark_loss_fwd_ex call, in the order the call runs them.  Filled by
+ * dspark_mla_layer_tune / dspark_loss_tune; handed back through
+ * dspark_attn_opts.gemm_choices.  Owned by the caller (host memory); the
+ * library keeps no table of its own.  A GEMM whose (m, n, k) differs from its
+ * entry's, or past n_gemms, uses rocBLAS's own choice. */
+#define DSPARK_MAX_GEMMS 8
+typedef struct dspark_gemm_choice {
+    int32_t m, n, k;        /* the GEMM's row-major shape: D[m][n] = A[m][k] B[n][k]^T */
+    int32_t solution;       /* rocBLAS solution index; 0 = rocBLAS's own choice */
+} dspark_gemm_choice;
+typedef struct dspark_gemm_choices {
+    int32_t n_gemms;
+    dspark_gemm_choice gemm[DSPARK_MAX_GEMMS];
+} dspark_gemm_choices;
+
+/* Bytes of the MLA block's and the loss head's workspace set aside for
+ * rocBLAS, handed to it with rocblas_set_workspace at the start of each
+ * call (the handle keeps pointing there until the next call sets its own).
+ * Measured on the logits GEMM at V = 154880: with rocBLAS's own memory 462
+ * of its 682 kernels refuse to run, with 4 MiB 402, with 64 MiB 18, and the
+ * fastest needs more than 4 MiB. */
+#define DSPARK_BLAS_WORKSPACE_BYTES ((size_t)64 << 20)
+
 /* Extra controls for dspark_attn_fwd_ex (zero-initialise, then set fields). */
 typedef struct dspark_attn_opts {
     /* NULL, or hipEvent_t handles recorded between the kernels of the call,
@@ -183,6 +208,9 @@ typedef struct dspark_attn_opts {
      * re-reads every block's keys for its heads, and its units wait on one
      * another); it is kept as a parity-tested alternative. */
     int32_t one_launch;
+    /* dspark_mla_layer_fwd_ex and dspark_loss_fwd_ex: NULL (rocBLAS chooses
+     * every GEMM kernel), or the choices a *_tune call filled. */
+    const dspark_gemm_choices* gemm_choices;
 } dspark_attn_opts;
 
 /* Bytes of workspace dspark_attn_fwd_ex needs for (desc, opts) on a device
@@ -400,9 +428,11 @@ size_t dspark_mla_layer_workspace_size(const dspark_layer_desc* desc);
  * The rows of kept blocks are compacted (5 per kept block, in (b, n) order)
  * for the draft-row projections and o_proj.  The projections run on rocBLAS
  * (fp32 accumulation, no atomics: the same call gives the same bits;
- * dspark_mla_layer_tune picks the kernels).  The first call on a device and
- * host thread creates a rocBLAS handle that is kept until the process ends
- * -- the one allocation the library makes.  out must not alias any input. */
+ * dspark_mla_layer_tune picks the kernels), which works in the
+ * DSPARK_BLAS_WORKSPACE_BYTES the workspace sets aside.  The first call on a
+ * device and host thread creates a rocBLAS handle that is kept until the
+ * process ends -- the one allocation the library makes.  out must not alias
+ * any input. */
 dspark_status dspark_mla_layer_fwd(const dspark_layer_desc* desc,
                                    const void* h_draft, const void* h_ctx,
                                    const void* g_in, const void* w_qa, const void* g_qa,
@@ -412,7 +442,8 @@ dspark_status dspark_mla_layer_fwd(const dspark_layer_desc* desc,
                                    void* out, void* workspace, size_t ws_bytes, void* stream);
 
 /* dspark_mla_layer_fwd with options (opts may be NULL): force_generic is
- * passed to the attention; stage_events (at least 7) are recorded on
+ * passed to the attention; gemm_choices selects the GEMM kernels;
+ * stage_events (at least 7) are recorded on
  * `stream` before the first launch and after: the input RMSNorm, q_a_proj
  * and its RMSNorm, q_b_proj, kv_a_proj and its RMSNorm / k^R split, the
  * attention, o_proj. */
@@ -428,19 +459,20 @@ dspark_status dspark_mla_layer_fwd_ex(const dspark_layer_desc* desc,
 /* dspark_mla_layer_fwd, once, while choosing the GEMM kernels: for each of
  * the block's projections every rocBLAS solution that applies to its shape
  * (and rocBLAS's default) is timed on `stream` -- which this call
- * synchronises, repeatedly -- and the fastest is recorded for that shape on
- * the current device; later calls of dspark_mla_layer_fwd(_ex) with the same
- * shapes, from any thread, use the recorded choices.  Without it rocBLAS
- * chooses (for the o_proj shape of GLM-5.2 its choice ran at half the
- * fastest one's rate).  Same arguments and outputs as dspark_mla_layer_fwd;
- * takes seconds; must not run under stream capture. */
+ * synchronises, repeatedly -- and the fastest is written to *choices (host
+ * memory, required).  Pass it back through dspark_attn_opts.gemm_choices to
+ * dspark_mla_layer_fwd_ex calls of the same shapes on a device of the same
+ * kind.  Without it rocBLAS chooses (for the o_proj shape of GLM-5.2 its
+ * choice ran at half the fastest one's rate).  Same arguments and outputs as
+ * dspark_mla_layer_fwd; takes seconds; must not run under stream capture. */
 dspark_status dspark_mla_layer_tune(const dspark_layer_desc* desc,
                                     const void* h_draft, const void* h_ctx,
                                     const void* g_in, const void* w_qa, const void* g_qa,
                                     const void* w_qb, const void* w_kva, const void* g_kva,
                                     const void* w_uk, const void* w_uv, const void* w_o,
                                     const int32_t* anchors, const uint8_t* keep,
-                                    void* out, void* workspace, size_t ws_bytes, void* stream);
+                                    void* out, void* workspace, size_t ws_bytes, void* stream,
+                                    dspark_gemm_choices* choices);
 
 /* Synchronises `stream`, then reads the status area of a workspace used by
  * the last dspark_mla_layer_fwd on it: DSPARK_OK, DSPARK_EANCHOR
@@ -520,7 +552,8 @@ size_t dspark_loss_workspace_size(const dspark_loss_desc* desc);
  * (w_m2 = w_lm + d, w_lm_ld = w_m2_ld = d + r), the draft and teacher logits
  * are one GEMM over [H^(L) | e] and [z | 0] with K = d + r; otherwise three
  * (the Markov bias, the draft lm_head accumulated onto it, the teacher's).
- * Uses the library's rocBLAS handle (see dspark_mla_layer_fwd). */
+ * Uses the library's rocBLAS handle, working in the workspace's
+ * DSPARK_BLAS_WORKSPACE_BYTES (see dspark_mla_layer_fwd). */
 dspark_status dspark_loss_fwd(const dspark_loss_desc* desc, const int32_t* input_ids,
                               const uint8_t* loss_mask, const int32_t* anchors,
                               const uint8_t* keep, const void* h_final, const void* z,
@@ -528,11 +561,11 @@ dspark_status dspark_loss_fwd(const dspark_loss_desc* desc, const int32_t* input
                               const void* w_conf, float* terms, uint8_t* eval_mask, float* loss,
                               void* workspace, size_t ws_bytes, void* stream);
 
-/* dspark_loss_fwd with options (opts may be NULL): stage_events (at least 6)
- * are recorded on `stream` before the first launch and after each stage:
- * the block index and row gather, the logits GEMMs, the softmax statistics,
- * the L1 pass, the per-step terms and the loss.  The other fields are
- * ignored. */
+/* dspark_loss_fwd with options (opts may be NULL): gemm_choices selects the
+ * GEMM kernels; stage_events (at least 6) are recorded on `stream` before the
+ * first launch and after each stage: the block index and row gather, the
+ * logits GEMMs, the softmax statistics, the L1 pass, the per-step terms and
+ * the loss.  The other fields are ignored. */
 dspark_status dspark_loss_fwd_ex(const dspark_loss_desc* desc, const int32_t* input_ids,
                                  const uint8_t* loss_mask, const int32_t* anchors,
                                  const uint8_t* keep, const void* h_final, const void* z,
@@ -541,14 +574,16 @@ dspark_status dspark_loss_fwd_ex(const dspark_loss_desc* desc, const int32_t* in
                                  float* loss, void* workspace, size_t ws_bytes, void* stream,
                                  const dspark_attn_opts* opts);
 
-/* dspark_loss_fwd, once, while choosing the GEMM kernels for its shapes (as
- * dspark_mla_layer_tune does; synchronises `stream`, takes seconds). */
+/* dspark_loss_fwd, once, while choosing the GEMM kernels for its shapes and
+ * writing them to *choices (as dspark_mla_layer_tune does; synchronises
+ * `stream`, takes seconds). */
 dspark_status dspark_loss_tune(const dspark_loss_desc* desc, const int32_t* input_ids,
                                const uint8_t* loss_mask, const int32_t* anchors,
                                const uint8_t* keep, const void* h_final, const void* z,
                                const void* w_lm, const void* w_m1, const void* w_m2,
                                const void* w_conf, float* terms, uint8_t* eval_mask, float* loss,
-                               void* workspace, size_t ws_bytes, void* stream);
+                               void* workspace, size_t ws_bytes, void* stream,
+                               dspark_gemm_choices* choices);
 
 /* Synchronises `stream`, then reads the status area of a workspace used by
  * the last dspark_loss_fwd on it: DSPARK_OK, DSPARK_EANCHOR (first_bad_block

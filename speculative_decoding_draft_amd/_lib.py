@@ -82,12 +82,31 @@ class VerifyDesc(ctypes.Structure):
                 ("mode", ctypes.c_int32), ("temperature", ctypes.c_double)]
 
 
+MAX_GEMMS = 8
+BLAS_WORKSPACE_BYTES = 64 << 20
+
+
+class GemmChoice(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int32), ("n", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("solution", ctypes.c_int32)]
+
+
+class GemmChoices(ctypes.Structure):
+    """dspark_gemm_choices: the rocBLAS kernel choice of each GEMM of one MLA
+    block or loss call, filled by mla_layer_tune / loss_tune (caller-owned)."""
+    _fields_ = [("n_gemms", ctypes.c_int32), ("gemm", GemmChoice * MAX_GEMMS)]
+
+    def as_list(self):
+        return [(g.m, g.n, g.k, g.solution) for g in self.gemm[:self.n_gemms]]
+
+
 class Opts(ctypes.Structure):
     _fields_ = [("stage_events", ctypes.POINTER(ctypes.c_void_p)),
                 ("n_stage_events", ctypes.c_int32), ("force_generic", ctypes.c_int32),
                 ("chunk_blocks", ctypes.c_int32), ("aux_stream", ctypes.c_void_p),
                 ("aux_events", ctypes.c_void_p * 2), ("reuse_forward", ctypes.c_int32),
-                ("one_launch", ctypes.c_int32)]
+                ("one_launch", ctypes.c_int32),
+                ("gemm_choices", ctypes.POINTER(GemmChoices))]
 
 
 def _load():
@@ -131,7 +150,7 @@ def _load():
     lib.dspark_mla_layer_fwd.restype = i32
     lib.dspark_mla_layer_fwd_ex.argtypes = layer_args + [ctypes.POINTER(Opts)]
     lib.dspark_mla_layer_fwd_ex.restype = i32
-    lib.dspark_mla_layer_tune.argtypes = layer_args
+    lib.dspark_mla_layer_tune.argtypes = layer_args + [ctypes.POINTER(GemmChoices)]
     lib.dspark_mla_layer_tune.restype = i32
     lib.dspark_mla_layer_read_status.argtypes = [vp, vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.dspark_mla_layer_read_status.restype = i32
@@ -143,7 +162,7 @@ def _load():
     lib.dspark_loss_fwd.restype = i32
     lib.dspark_loss_fwd_ex.argtypes = loss_args + [ctypes.POINTER(Opts)]
     lib.dspark_loss_fwd_ex.restype = i32
-    lib.dspark_loss_tune.argtypes = loss_args
+    lib.dspark_loss_tune.argtypes = loss_args + [ctypes.POINTER(GemmChoices)]
     lib.dspark_loss_tune.restype = i32
     lib.dspark_loss_read_status.argtypes = [vp, vp, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                             ctypes.POINTER(i32)]
@@ -402,28 +421,34 @@ LAYER_WEIGHTS = ("g_in", "w_qa", "g_qa", "w_qb", "w_kva", "g_kva", "w_uk", "w_uv
 
 def mla_layer_fwd(desc: LayerDesc, h_draft, h_ctx, weights, anchors, keep, out, workspace,
                   stream=None, stage_events: Optional[Sequence[int]] = None,
-                  force_generic: bool = False) -> None:
+                  force_generic: bool = False, gemm_choices: Optional[GemmChoices] = None) -> None:
     """dspark_mla_layer_fwd / _ex; weights: a mapping named as in
-    LAYER_WEIGHTS."""
+    LAYER_WEIGHTS; gemm_choices: what mla_layer_tune returned (None: rocBLAS
+    chooses)."""
     args = [ctypes.byref(desc), _ptr(h_draft), _ptr(h_ctx)]
     args += [_ptr(weights[k]) for k in LAYER_WEIGHTS]
     ws_bytes = workspace.numel() * workspace.element_size()
     args += [_ptr(anchors), _ptr(keep), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)]
-    if stage_events is None and not force_generic:
+    if stage_events is None and not force_generic and gemm_choices is None:
         _check(lib.dspark_mla_layer_fwd(*args))
         return
     opts, _arr = _opts(stage_events, force_generic, 0)
+    if gemm_choices is not None:
+        opts.gemm_choices = ctypes.pointer(gemm_choices)
     _check(lib.dspark_mla_layer_fwd_ex(*args, ctypes.byref(opts)))
 
 
 def mla_layer_tune(desc: LayerDesc, h_draft, h_ctx, weights, anchors, keep, out, workspace,
-                   stream=None) -> None:
-    """dspark_mla_layer_tune: one block call that also picks its GEMM kernels."""
+                   stream=None) -> GemmChoices:
+    """dspark_mla_layer_tune: one block call that also picks its GEMM kernels;
+    returns them (pass to mla_layer_fwd as gemm_choices)."""
     args = [ctypes.byref(desc), _ptr(h_draft), _ptr(h_ctx)]
     args += [_ptr(weights[k]) for k in LAYER_WEIGHTS]
     ws_bytes = workspace.numel() * workspace.element_size()
     args += [_ptr(anchors), _ptr(keep), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)]
-    _check(lib.dspark_mla_layer_tune(*args))
+    choices = GemmChoices()
+    _check(lib.dspark_mla_layer_tune(*args, ctypes.byref(choices)))
+    return choices
 
 
 def make_loss_desc(B: int, S: int, N: int, vocab: int, hidden: int, markov_rank: int,
@@ -455,20 +480,29 @@ def _loss_args(desc, t, terms, eval_mask, loss, workspace, stream):
 
 
 def loss_fwd(desc: LossDesc, tensors, terms, eval_mask, loss, workspace, stream=None,
-             stage_events: Optional[Sequence[int]] = None) -> None:
+             stage_events: Optional[Sequence[int]] = None,
+             gemm_choices: Optional[GemmChoices] = None) -> None:
     """dspark_loss_fwd / _ex; tensors: a mapping named as in LOSS_INPUTS;
-    terms [4, B, N, 5] fp32, eval_mask [B, N, 5] uint8, loss [5] fp32."""
+    terms [4, B, N, 5] fp32, eval_mask [B, N, 5] uint8, loss [5] fp32;
+    gemm_choices: what loss_tune returned (None: rocBLAS chooses)."""
     args = _loss_args(desc, tensors, terms, eval_mask, loss, workspace, stream)
-    if stage_events is None:
+    if stage_events is None and gemm_choices is None:
         _check(lib.dspark_loss_fwd(*args))
         return
     opts, _arr = _opts(stage_events, False, 0)
+    if gemm_choices is not None:
+        opts.gemm_choices = ctypes.pointer(gemm_choices)
     _check(lib.dspark_loss_fwd_ex(*args, ctypes.byref(opts)))
 
 
-def loss_tune(desc: LossDesc, tensors, terms, eval_mask, loss, workspace, stream=None) -> None:
-    """dspark_loss_tune: one loss call that also picks its GEMM kernels."""
-    _check(lib.dspark_loss_tune(*_loss_args(desc, tensors, terms, eval_mask, loss, workspace, stream)))
+def loss_tune(desc: LossDesc, tensors, terms, eval_mask, loss, workspace,
+              stream=None) -> GemmChoices:
+    """dspark_loss_tune: one loss call that also picks its GEMM kernels;
+    returns them (pass to loss_fwd as gemm_choices)."""
+    choices = GemmChoices()
+    _check(lib.dspark_loss_tune(*_loss_args(desc, tensors, terms, eval_mask, loss, workspace,
+                                            stream), ctypes.byref(choices)))
+    return choices
 
 
 def loss_read_status(workspace, stream=None):

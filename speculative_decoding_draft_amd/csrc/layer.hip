@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256) void residual_scatter_kernel(
 struct LayerLayout {
     size_t status = 0, slot_blk = 0, blk_slot = 0, hn = 0, cq = 0, qf = 0, qn = 0, qr = 0,
            kvc = 0, kvb = 0, ckv_c = 0, kr_c = 0, ckv_b = 0, kr_b = 0, o = 0, o_c = 0, h_c = 0,
-           proj = 0, attn = 0, total = 0;
+           proj = 0, blas = 0, attn = 0, total = 0;
     int cap = 0;
 };
 
@@ -350,6 +350,7 @@ LayerLayout layer_layout(const dspark_layer_desc& L, size_t attn_ws) {
     w.o_c = take(k_rows * d.n_heads * d.d_v * e);
     w.h_c = take(k_rows * L.hidden * e);
     w.proj = take(k_rows * L.hidden * e);
+    w.blas = take(DSPARK_BLAS_WORKSPACE_BYTES);
     w.attn = take(attn_ws);
     w.total = off;
     return w;
@@ -400,7 +401,7 @@ dspark_status layer_fwd(const dspark_layer_desc* desc, const void* h_draft, cons
                         const void* w_kva, const void* g_kva, const void* w_uk, const void* w_uv,
                         const void* w_o, const int32_t* anchors, const uint8_t* keep, void* out,
                         void* workspace, size_t ws_bytes, void* stream,
-                        const dspark_attn_opts* opts, bool tune) {
+                        const dspark_attn_opts* opts, dspark_gemm_choices* tuned) {
     set_last_error("");
     if (!desc) return lfail(DSPARK_EINVAL, "desc is NULL");
     if (desc->hidden < 1 || desc->q_rank < 1)
@@ -440,6 +441,12 @@ dspark_status layer_fwd(const dspark_layer_desc* desc, const void* h_draft, cons
     rocblas_handle h;
     rocblas_status bs = blas_handle(s, &h);
     if (bs != rocblas_status_success) return lfail(DSPARK_EHIP, "rocBLAS handle set-up failed", bs);
+    bs = blas_use_workspace(h, static_cast<char*>(workspace) + L.blas, DSPARK_BLAS_WORKSPACE_BYTES);
+    if (bs != rocblas_status_success) return lfail(DSPARK_EHIP, "rocblas_set_workspace failed", bs);
+    if (tuned) *tuned = dspark_gemm_choices{};
+    GemmPick pick{tuned ? tuned : const_cast<dspark_gemm_choices*>(opts ? opts->gemm_choices
+                                                                          : nullptr),
+                  tuned != nullptr, 0};
 
     const bool bf = d.dtype == DSPARK_BF16;
     const rocblas_datatype tio = bf ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
@@ -495,7 +502,7 @@ dspark_status layer_fwd(const dspark_layer_desc* desc, const void* h_draft, cons
     LMARK();
     // c^Q = RMSNorm(h W_qa^T)
     LSTEP_BLAS(gemm_nt(h, tio, tio, k_rows, qk, hid, hn, hid, w_qa, hid, 0.f, nullptr, 0, cq, qk,
-                       tune), "q_a_proj GEMM");
+                       &pick), "q_a_proj GEMM");
     LSTEP_HIP(norm(cq, qk, g_qa, cq, qk, nullptr, 0, k_rows, qk, nullptr, nullptr),
               "q_a RMSNorm launch");
     LMARK();
@@ -504,7 +511,7 @@ dspark_status layer_fwd(const dspark_layer_desc* desc, const void* h_draft, cons
     // attention's [row][head][dim] layouts at the blocks' own rows
     void* qf = base + L.qf;
     LSTEP_BLAS(gemm_nt(h, tio, tio, k_rows, H * (dc + dr), qk, cq, qk, w_qb, qk, 0.f, nullptr, 0, qf,
-                       H * (dc + dr), tune), "q_b_proj GEMM");
+                       H * (dc + dr), &pick), "q_b_proj GEMM");
     {
         const int vec = (dc % 8 == 0 && dr % 8 == 0 && bf) ? 8 : ((dc % 4 == 0 && dr % 4 == 0 && !bf) ? 4 : 1);
         const size_t total = (size_t)k_rows * H * (dc + dr) / vec;
@@ -523,9 +530,9 @@ dspark_status layer_fwd(const dspark_layer_desc* desc, const void* h_draft, cons
     // [c^KV ; k^R] = [H^ctx ; h] W_kva^T, then c^KV <- RMSNorm(c^KV) and the k^R
     // split (the draft rows written back to the blocks' own rows)
     LSTEP_BLAS(gemm_nt(h, tio, tio, c_rows, D + dr, hid, h_ctx, hid, w_kva, hid, 0.f, nullptr, 0, kvc,
-                       D + dr, tune), "kv_a_proj (context) GEMM");
+                       D + dr, &pick), "kv_a_proj (context) GEMM");
     LSTEP_BLAS(gemm_nt(h, tio, tio, k_rows, D + dr, hid, hn, hid, w_kva, hid, 0.f, nullptr, 0, kvb,
-                       D + dr, tune), "kv_a_proj (draft) GEMM");
+                       D + dr, &pick), "kv_a_proj (draft) GEMM");
     LSTEP_HIP(norm(kvc, D + dr, g_kva, ckv_c, D, kr_c, dr, c_rows, D, nullptr, nullptr),
               "kv_a RMSNorm launch");
     LSTEP_HIP(norm(kvb, D + dr, g_kva, ckv_b, D, kr_b, dr, k_rows, D, nullptr, slot_blk),
@@ -561,7 +568,7 @@ dspark_status layer_fwd(const dspark_layer_desc* desc, const void* h_draft, cons
 #undef LGATHER
         LSTEP_HIP(hipGetLastError(), "o / H gather launch");
         LSTEP_BLAS(gemm_nt(h, tio, tio, k_rows, hid, n, o_c, n, w_o, n, 1.f, h_c, hid, proj, hid,
-                           tune), "o_proj GEMM");
+                           &pick), "o_proj GEMM");
 #define LSCATTER(T, VV)                                                                       \
     hipLaunchKernelGGL((residual_scatter_kernel<T, VV>), waves_grid(q_rows), dim3(256), 0, s,  \
                        (const T*)h_draft, (const T*)proj, (T*)out, (size_t)q_rows, hid, blk_slot, \
@@ -594,7 +601,7 @@ dspark_status dspark_mla_layer_fwd_ex(const dspark_layer_desc* desc, const void*
                                       size_t ws_bytes, void* stream,
                                       const dspark_attn_opts* opts) {
     return layer_fwd(desc, h_draft, h_ctx, g_in, w_qa, g_qa, w_qb, w_kva, g_kva, w_uk, w_uv, w_o,
-                     anchors, keep, out, workspace, ws_bytes, stream, opts, false);
+                     anchors, keep, out, workspace, ws_bytes, stream, opts, nullptr);
 }
 
 dspark_status dspark_mla_layer_tune(const dspark_layer_desc* desc, const void* h_draft,
@@ -602,9 +609,11 @@ dspark_status dspark_mla_layer_tune(const dspark_layer_desc* desc, const void* h
                                     const void* g_qa, const void* w_qb, const void* w_kva,
                                     const void* g_kva, const void* w_uk, const void* w_uv,
                                     const void* w_o, const int32_t* anchors, const uint8_t* keep,
-                                    void* out, void* workspace, size_t ws_bytes, void* stream) {
+                                    void* out, void* workspace, size_t ws_bytes, void* stream,
+                                    dspark_gemm_choices* choices) {
+    if (!choices) return lfail(DSPARK_EINVAL, "choices is NULL");
     return layer_fwd(desc, h_draft, h_ctx, g_in, w_qa, g_qa, w_qb, w_kva, g_kva, w_uk, w_uv, w_o,
-                     anchors, keep, out, workspace, ws_bytes, stream, nullptr, true);
+                     anchors, keep, out, workspace, ws_bytes, stream, nullptr, choices);
 }
 
 dspark_status dspark_mla_layer_fwd(const dspark_layer_desc* desc, const void* h_draft,

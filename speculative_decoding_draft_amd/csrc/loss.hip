@@ -49,7 +49,7 @@ enum LossStatus {
 
 struct LossLayout {
     size_t status = 0, row_step = 0, step_row = 0, xd = 0, xt = 0, ld = 0, lt = 0, part = 0,
-           l1p = 0, total = 0;
+           l1p = 0, blas = 0, total = 0;
     int rows = 0;      // compact rows: one per counted step, at most this many
     int chunks = 0;    // ceil(V / kChunk)
 };
@@ -83,6 +83,7 @@ LossLayout loss_layout(const dspark_loss_desc& d) {
     w.lt = w.ld + rows * V * 4;
     w.part = take(rows * (size_t)w.chunks * 16);
     w.l1p = take(rows * (size_t)w.chunks * 4);
+    w.blas = take(DSPARK_BLAS_WORKSPACE_BYTES);
     w.total = off;
     return w;
 }
@@ -465,7 +466,7 @@ dspark_status loss_fwd(const dspark_loss_desc* desc, const int32_t* ids, const u
                        const void* z, const void* w_lm, const void* w_m1, const void* w_m2,
                        const void* w_conf, float* terms, uint8_t* emask, float* loss,
                        void* workspace, size_t ws_bytes, void* stream,
-                       const dspark_attn_opts* opts, bool tune) {
+                       const dspark_attn_opts* opts, dspark_gemm_choices* tuned) {
     set_last_error("");
     if (const char* why = check_desc(desc)) return lsfail(DSPARK_EINVAL, why);
     const dspark_loss_desc& d = *desc;
@@ -535,6 +536,20 @@ dspark_status loss_fwd(const dspark_loss_desc* desc, const int32_t* ids, const u
             return lsfail(DSPARK_EHIP, t_msg);
         }
     }
+    // rocBLAS works in the workspace's own area
+    if (h) {
+        const rocblas_status ws_st = blas_use_workspace(
+            h, static_cast<char*>(workspace) + L.blas, DSPARK_BLAS_WORKSPACE_BYTES);
+        if (ws_st != rocblas_status_success) {
+            snprintf(t_msg, sizeof(t_msg), "rocblas_set_workspace failed (%d)", (int)ws_st);
+            return lsfail(DSPARK_EHIP, t_msg);
+        }
+    }
+    const bool tune = tuned != nullptr;
+    if (tuned) *tuned = dspark_gemm_choices{};
+    GemmPick pick{tuned ? tuned : const_cast<dspark_gemm_choices*>(opts ? opts->gemm_choices
+                                                                          : nullptr),
+                  tune, 0};
     LS_HIP(mark(), "hipEventRecord");
     hipLaunchKernelGGL(loss_index_kernel, dim3(1), dim3(kIndexThreads), 0, s, B, S, N, L.rows,
                        anchors, keep, lmask, status, row_step, step_row, emask);
@@ -567,24 +582,25 @@ dspark_status loss_fwd(const dspark_loss_desc* desc, const int32_t* ids, const u
         if (fused) {
             // [H^(L) | e ; z | 0] [W_lm | W2]^T: draft and teacher logits at once
             if ((bs = gemm_nt(h, ti, to, 2 * rows, V, ldx, xd, ldx, w_lm, ldx, 0.f, nullptr, 0, ld,
-                              V, tune)) != rocblas_status_success)
+                              V, &pick)) != rocblas_status_success)
                 bad = "logits GEMM";
         } else {
             const void* xe = (const char*)xd + (size_t)hd * e;
-            // L = E W2^T, then L += H W_lm^T in place.  Tuning the in-place GEMM
-            // runs it many times over L, so after a tuning pass both are run
-            // again with the recorded choices.
+            // L = E W2^T, then L += H W_lm^T in place (GEMMs 0 and 1).  Tuning
+            // the in-place GEMM runs it many times over L, so after a tuning
+            // pass both are run again with the choices just recorded.
             for (int pass = 0; pass < (tune ? 2 : 1) && !bad; ++pass) {
-                const bool t = tune && pass == 0;
+                GemmPick pp{pick.table, tune && pass == 0, 0};
                 if ((bs = gemm_nt(h, ti, to, rows, V, rk, xe, ldx, w_m2, m2_ld, 0.f, nullptr, 0, ld,
-                                  V, t)) != rocblas_status_success)
+                                  V, &pp)) != rocblas_status_success)
                     bad = "Markov GEMM";
                 else if ((bs = gemm_nt(h, ti, to, rows, V, hd, xd, ldx, w_lm, lm_ld, 1.f, nullptr, 0,
-                                       ld, V, t)) != rocblas_status_success)
+                                       ld, V, &pp)) != rocblas_status_success)
                     bad = "draft lm_head GEMM";
             }
+            pick.next = 2;
             if (!bad && (bs = gemm_nt(h, ti, to, rows, V, hd, xt, ldx, w_lm, lm_ld, 0.f, nullptr, 0,
-                                      lt, V, tune)) != rocblas_status_success)
+                                      lt, V, &pick)) != rocblas_status_success)
                 bad = "teacher lm_head GEMM";
         }
         if (bad) {
@@ -657,7 +673,7 @@ dspark_status dspark_loss_fwd_ex(const dspark_loss_desc* desc, const int32_t* in
                                  float* loss, void* workspace, size_t ws_bytes, void* stream,
                                  const dspark_attn_opts* opts) {
     return loss_fwd(desc, input_ids, loss_mask, anchors, keep, h_final, z, w_lm, w_m1, w_m2,
-                    w_conf, terms, eval_mask, loss, workspace, ws_bytes, stream, opts, false);
+                    w_conf, terms, eval_mask, loss, workspace, ws_bytes, stream, opts, nullptr);
 }
 
 dspark_status dspark_loss_fwd(const dspark_loss_desc* desc, const int32_t* input_ids,
@@ -667,7 +683,7 @@ dspark_status dspark_loss_fwd(const dspark_loss_desc* desc, const int32_t* input
                               const void* w_conf, float* terms, uint8_t* eval_mask, float* loss,
                               void* workspace, size_t ws_bytes, void* stream) {
     return loss_fwd(desc, input_ids, loss_mask, anchors, keep, h_final, z, w_lm, w_m1, w_m2,
-                    w_conf, terms, eval_mask, loss, workspace, ws_bytes, stream, nullptr, false);
+                    w_conf, terms, eval_mask, loss, workspace, ws_bytes, stream, nullptr, nullptr);
 }
 
 dspark_status dspark_loss_tune(const dspark_loss_desc* desc, const int32_t* input_ids,
@@ -675,9 +691,11 @@ dspark_status dspark_loss_tune(const dspark_loss_desc* desc, const int32_t* inpu
                                const uint8_t* keep, const void* h_final, const void* z,
                                const void* w_lm, const void* w_m1, const void* w_m2,
                                const void* w_conf, float* terms, uint8_t* eval_mask, float* loss,
-                               void* workspace, size_t ws_bytes, void* stream) {
+                               void* workspace, size_t ws_bytes, void* stream,
+                               dspark_gemm_choices* choices) {
+    if (!choices) return lsfail(DSPARK_EINVAL, "choices is NULL");
     return loss_fwd(desc, input_ids, loss_mask, anchors, keep, h_final, z, w_lm, w_m1, w_m2,
-                    w_conf, terms, eval_mask, loss, workspace, ws_bytes, stream, nullptr, true);
+                    w_conf, terms, eval_mask, loss, workspace, ws_bytes, stream, nullptr, choices);
 }
 
 dspark_status dspark_loss_read_status(const void* workspace, void* stream,

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for name in sorted(declared):
         assert hasattr(lib, name), name
     assert set(sd.EXPORTS) == declared
-    assert sd.abi_version() == 12
+    assert sd.abi_version() == 13
 
 
 def glm_desc(**kw):
@@ -131,9 +131,10 @@ def test_mfma_path_needs_32bit_offsets():
 
 def test_opts_struct_matches_header():
     """The binding's dspark_attn_opts has the header's layout (x86-64)."""
-    assert ctypes.sizeof(sd._lib.Opts) == 8 + 4 * 3 + 4 + 8 + 16 + 8
+    assert ctypes.sizeof(sd._lib.Opts) == 8 + 4 * 3 + 4 + 8 + 16 + 8 + 8
     assert sd._lib.Opts.aux_stream.offset == 24 and sd._lib.Opts.aux_events.offset == 32
-    assert sd._lib.Opts.reuse_forward.offset == 48
+    assert sd._lib.Opts.reuse_forward.offset == 48 and sd._lib.Opts.one_launch.offset == 52
+    assert sd._lib.Opts.gemm_choices.offset == 56
 
 
 def test_aux_stream_is_validated():
@@ -313,14 +314,15 @@ def test_loss_desc_layout_and_workspace():
     logits = 2 * rows * 154880 * 4
     gathered = 2 * rows * (6144 + 256) * 2
     stats = rows * 19 * (16 + 4)
-    assert logits + gathered + stats <= need < logits + gathered + stats + 2**20
+    blas = sd.BLAS_WORKSPACE_BYTES            # rocBLAS works in the caller's workspace
+    assert logits + gathered + stats + blas <= need < logits + gathered + stats + blas + 2**20
     # max_kept_blocks and max_counted_steps shrink every row-sized buffer
     d2 = sd.make_loss_desc(B=1, S=32768, N=1024, vocab=154880, hidden=6144, markov_rank=256,
                            max_kept_blocks=768)
-    assert abs(sd.loss_workspace_size(d2) - need * 768 / 1024) < 2**20
+    assert abs(sd.loss_workspace_size(d2) - blas - (need - blas) * 768 / 1024) < 2**20
     d3 = sd.make_loss_desc(B=1, S=32768, N=1024, vocab=154880, hidden=6144, markov_rank=256,
                            max_kept_blocks=768, max_counted_steps=2560)
-    assert abs(sd.loss_workspace_size(d3) - need * 2560 / 5120) < 2**20
+    assert abs(sd.loss_workspace_size(d3) - blas - (need - blas) * 2560 / 5120) < 2**20
     for kw in (dict(vocab=0), dict(hidden=0), dict(markov_rank=0), dict(max_kept_blocks=-1),
                dict(S=0), dict(w_lm_ld=7), dict(w_m2_ld=3), dict(max_counted_steps=-1)):
         args = dict(B=1, S=64, N=4, vocab=100, hidden=8, markov_rank=4)
@@ -417,3 +419,18 @@ def test_noalloc_forward_checks_status_alignment_and_empty_problems():
     d = glm_desc()
     st = sd._lib.lib.dspark_attn_fwd_noalloc(ctypes.byref(d), *([None] * 11), 0x1002, None)
     assert st == sd.DSPARK_EINVAL and "status" in sd.last_error()
+
+
+def test_tune_calls_need_a_choices_table():
+    """The *_tune calls write their GEMM choices into a caller-owned table and
+    refuse a NULL one before any device work; the table's C layout is 4
+    int32 per GEMM after the count."""
+    lib = sd._lib.lib
+    d = sd.make_layer_desc(glm_desc(), 6144, 2048)
+    assert lib.dspark_mla_layer_tune(ctypes.byref(d), *([None] * 15), 0, None, None) == sd.DSPARK_EINVAL
+    assert "choices" in sd.last_error()
+    ld = sd.make_loss_desc(1, 2048, 64, 1000, 6144, 256)
+    assert lib.dspark_loss_tune(ctypes.byref(ld), *([None] * 14), 0, None, None) == sd.DSPARK_EINVAL
+    assert "choices" in sd.last_error()
+    assert ctypes.sizeof(sd.GemmChoices) == 4 + 8 * 16
+    assert sd.BLAS_WORKSPACE_BYTES == 64 << 20

@@ -111,8 +111,9 @@ def test_layer_repeat_runs_are_bit_identical():
 
 def test_layer_tune_then_forward():
     """dspark_mla_layer_tune returns the block's output like the plain call and
-    records kernel choices; later plain calls use them, give identical bits to
-    each other and still match the oracle."""
+    writes its kernel choices into the caller's table (one per GEMM, with the
+    GEMM's shape); later calls given the table give identical bits to each
+    other and still match the oracle."""
     import torch
     import speculative_decoding_draft_amd as sd
     wl = wk.scaled(4, S=700, N=20)
@@ -126,11 +127,20 @@ def test_layer_tune_then_forward():
     a, k = upload_anchors(wl.anchors, wl.keep)
     ws = torch.empty(sd.layer_workspace_size(desc), dtype=torch.uint8, device="cuda")
     outs = []
+    choices = None
     for tune in (True, False, False):
         out = torch.full(hd.shape, float("nan"), dtype=torch.bfloat16, device="cuda")
-        (sd.mla_layer_tune if tune else sd.mla_layer_fwd)(desc, hd, hc, w, a, k, out, ws)
+        if tune:
+            choices = sd.mla_layer_tune(desc, hd, hc, w, a, k, out, ws)
+        else:
+            sd.mla_layer_fwd(desc, hd, hc, w, a, k, out, ws, gemm_choices=choices)
         torch.cuda.synchronize()
         outs.append(out.float().cpu().numpy().astype(np.float64))
+    table = choices.as_list()
+    log(f"  layer GEMM choices {table}")
+    assert len(table) == 5
+    assert [g[:3] for g in table][:2] == [(5 * wl.B * wl.N, li.q_rank, li.hidden),
+                                          (5 * wl.B * wl.N, wl.H * (wl.d_c + wl.d_r), li.q_rank)]
     ref = O.layer_forward(wl, li)
     for o in outs:
         check(wl, li, o, ref, wl.keep, 1e-2, 5e-3, "tuned")

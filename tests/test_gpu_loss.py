@@ -61,7 +61,12 @@ def run_loss(wl, lh, anchors, keep, max_kept=0, tune=False, loss_mask=None, ws=N
     terms = torch.full((4, wl.B, wl.N, 5), 12345.0, dtype=torch.float32, device="cuda")
     em = torch.full((wl.B, wl.N, 5), 7, dtype=torch.uint8, device="cuda")
     loss = torch.full((5,), 12345.0, dtype=torch.float32, device="cuda")
-    (sd.loss_tune if tune else sd.loss_fwd)(d, t, terms, em, loss, ws)
+    if tune:
+        choices = sd.loss_tune(d, t, terms, em, loss, ws)
+        assert 1 <= choices.n_gemms <= 3
+        assert all(g[1] == lh.vocab for g in choices.as_list())
+    else:
+        sd.loss_fwd(d, t, terms, em, loss, ws)
     st = sd.loss_read_status(ws)
     torch.cuda.synchronize()
     return (terms.cpu().numpy().astype(np.float64), em.cpu().numpy(),
