@@ -100,7 +100,7 @@ BWD_PMC_TRAFFIC = {
 # three launches; 64 sequences, K = 5, V = 154880): the same FETCH/WRITE
 # scaling, with the files each is built from and their digest when taken.
 SIDE_PMC_TRAFFIC = {
-    "loss_stats": (3_882_426_288, ("loss.hip", "blas.hpp", "kernels.hpp"), "7f5f3a3869757f4a"),
+    "loss_stats": (3_882_859_895, ("loss.hip", "blas.hpp", "kernels.hpp"), "a94b7e3af57b3f81"),
     "verify": (436_597_519 + 398_369_304 + 4_484_620, ("decode.hip", "kernels.hpp"),
                "25552c1280c23bfe"),
 }
@@ -816,7 +816,7 @@ def forward_algorithmic_bytes(wl, anchors, keep) -> int:
             + H * (dc + dv) * D * el + wl.B * wl.N * 5 + wl.B * 5 * wl.N * H * dv * el)
 
 
-def prepare_forward(sd, torch, wl, chunk_blocks=0, aux_stream=False):
+def prepare_forward(sd, torch, wl, chunk_blocks=0, aux_stream=False, one_launch=False):
     """Anchors, device tensors of every layer, outputs, workspace and one
     bound call per layer."""
     from workloads.device import upload_anchors, upload_layer
@@ -839,7 +839,7 @@ def prepare_forward(sd, torch, wl, chunk_blocks=0, aux_stream=False):
             for _ in range(L)]
     ws = torch.empty(sd.workspace_size(desc), dtype=torch.uint8, device="cuda")
     sptr = int(torch.cuda.current_stream().cuda_stream)
-    n_chunks, chunk, n_ev = sd.attn_plan(desc, chunk_blocks=chunk_blocks)
+    n_chunks, chunk, n_ev = sd.attn_plan(desc, chunk_blocks=chunk_blocks, one_launch=one_launch)
     aux, aux_ev = None, None
     if aux_stream and n_chunks > 1:
         aux = torch.cuda.Stream()
@@ -847,17 +847,21 @@ def prepare_forward(sd, torch, wl, chunk_blocks=0, aux_stream=False):
     calls = [sd.BoundFwd(desc, t["q_nope"], t["q_rope"], t["ckv_ctx"], t["kr_ctx"], t["ckv_blk"],
                          t["kr_blk"], t["w_uk"], t["w_uv"], a_dev, k_dev, outs[l], ws, stream=sptr,
                          chunk_blocks=chunk_blocks, n_stage_events=n_ev, aux_stream=aux,
-                         aux_events=aux_ev)
+                         aux_events=aux_ev, one_launch=one_launch)
              for l, t in enumerate(tensors)]
     return dict(wl=wl, anchors=anchors, keep=keep, tensors=tensors, a_dev=a_dev, k_dev=k_dev,
                 desc=desc, outs=outs, ws=ws, sptr=sptr, calls=calls, n_chunks=n_chunks,
-                chunk=chunk, n_ev=n_ev, aux=aux, aux_ev=aux_ev, L=L)
+                chunk=chunk, n_ev=n_ev, aux=aux, aux_ev=aux_ev, L=L, one_launch=one_launch)
 
 
-def stage_times(ev, n_ev, n_chunks, live):
+def stage_times(ev, n_ev, n_chunks, live, one_launch=False):
     """Per-stage milliseconds of one instrumented call from its stage events:
     the index build, then absorb / attention / W_UV summed over the call's
-    rounds (and each live round's own), or the generic kernel."""
+    rounds (and each live round's own), or the generic kernel, or the
+    one-launch kernel."""
+    if n_ev == 3 and one_launch:   # [0] index + padding fill [1] one launch [2]
+        return {"index+fill": HIP.elapsed_ms(ev[0], ev[1]),
+                "one_launch": HIP.elapsed_ms(ev[1], ev[2])}, None
     if n_ev == 3:      # generic path: [0] index + RoPE table [1] kernel [2]
         return {"index+rope": HIP.elapsed_ms(ev[0], ev[1]),
                 "generic": HIP.elapsed_ms(ev[1], ev[2])}, None
@@ -929,7 +933,8 @@ def measure_forward(torch, fw, steps, warmup, samples, sample_steps, stage_steps
             call.with_events(ev[(i * L + l) * n_ev:(i * L + l + 1) * n_ev])
     torch.cuda.synchronize()
     for j in range(stage_steps * L):
-        tot, rounds = stage_times(ev[j * n_ev:(j + 1) * n_ev], n_ev, n_chunks, live)
+        tot, rounds = stage_times(ev[j * n_ev:(j + 1) * n_ev], n_ev, n_chunks, live,
+                                  fw["one_launch"])
         for s, v in tot.items():
             per_stage.setdefault(s, []).append(v)
         if rounds is not None:
@@ -991,6 +996,9 @@ def main():
                     help="kept blocks per kernel round (0: the library default)")
     ap.add_argument("--aux-stream", action="store_true",
                     help="run odd kernel rounds on a second stream (with --chunk-blocks)")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="time the opt-in one-launch forward (dspark_attn_opts.one_launch) "
+                         "instead of the three kernels")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other four configurations (the 'configs' object)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -1058,7 +1066,7 @@ def main():
 
     log_progress(f"config {args.config} (headline line)")
     wl = wk.config(args.config)
-    fw = prepare_forward(sd, torch, wl, args.chunk_blocks, args.aux_stream)
+    fw = prepare_forward(sd, torch, wl, args.chunk_blocks, args.aux_stream, args.one_launch)
     fw["sd"] = sd
     anchors, keep, L = fw["anchors"], fw["keep"], fw["L"]
     K = args.steps
@@ -1099,7 +1107,8 @@ def main():
         "useful_gflop_per_step": round(flop / 1e9, 3),
         "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
         "chunks": {"chunk_blocks": fw["chunk"], "launches_per_kernel": m["live_rounds"],
-                   "streams": 2 if fw["aux"] is not None else 1},
+                   "streams": 2 if fw["aux"] is not None else 1,
+                   "one_launch": bool(args.one_launch)},
         "roofline": None,
         "cpu_baseline": None,
     }
