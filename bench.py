@@ -642,23 +642,48 @@ def cpu_baseline(wl, anchors, keep, budget_s: float = 15.0):
     kept = [(b, n) for b in range(wl.B) for n in range(wl.N) if keep[b, n]]
     rng = np.random.default_rng(0)
     order = rng.permutation(len(kept))
-    n_blocks, spent, done = 4, 0.0, []
+    n_blocks, spent, done, own = 4, 0.0, [], 0
     while spent < budget_s and len(done) < len(kept):
         pick = [kept[i] for i in order[len(done):len(done) + n_blocks]]
         t0 = time.perf_counter()
         O.forward(wl, 0, anchors, keep, form="gathered", blocks=pick)
         spent += time.perf_counter() - t0
         done += pick
+        own += oracle_forward_flop(wl, anchors, pick)
         n_blocks *= 2
     flop = sum(useful_flop([anchors[b, n]], [1], wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v)
                for b, n in done)
     blas = blas_info()
     return {"value": flop / spent / 1e12, "unit": "TFLOP/s", "cores": blas["threads"],
             "kind": "oracle", "blocks_per_s": len(done) / spent,
+            "oracle_flop": own, "oracle_tflops": own / spent / 1e12,
             "host_cores": len(os.sched_getaffinity(0)), "blas": blas["name"],
             "blas_threads": blas["threads"], "precision": "fp64",
             "sample": f"{len(done)} random kept blocks of the same workload "
                       f"(fp64 numpy, gathered form, {spent:.1f} s)"}
+
+
+def oracle_forward_flop(wl, anchors, pick) -> int:
+    """What the oracle's gathered forward itself computes for one call over
+    the blocks `pick`: per sample and head, K and V expanded at every column
+    the picked rows see (2 (d_c + d_v) D per column: K's latent part and V),
+    then per query row and head the scores and the weighted sum over its v
+    visible keys (2 v (d_c + d_r) + 2 v d_v)."""
+    total = 0
+    for b in sorted({b for b, _ in pick}):
+        cover = np.zeros(wl.S, dtype=bool)
+        n_blk, vsum = 0, 0
+        for bb, n in pick:
+            if bb != b:
+                continue
+            a = int(anchors[b, n])
+            cover[max(0, a - wl.W + 1):a] = True
+            n_blk += 1
+            vsum += min(a, wl.W - 1) + 5
+        cols = int(cover.sum()) + 5 * n_blk
+        total += wl.H * (cols * 2 * (wl.d_c + wl.d_v) * wl.D
+                         + 5 * vsum * (2 * (wl.d_c + wl.d_r) + 2 * wl.d_v))
+    return total
 
 
 def blas_info() -> dict:
