@@ -72,3 +72,25 @@ def test_noalloc_generic_path_reports_a_bad_anchor_through_status(sd):
     got[0, 10:15] = 0.0
     want[0, 10:15] = 0.0
     compare(got, want, ok, F32_MAX_ABS, F32_REL_L2, what="no-alloc vs workspace, generic")
+
+
+def test_noalloc_at_131072_positions_in_forty_rounds(sd):
+    """S = 131072, N = 4096 sampler anchors (about 40 rounds of ~100 blocks
+    through the fixed array): the same bits as the workspace forward, which
+    runs every block in one round."""
+    import torch
+    wl = wk.config(5)
+    ga = np.zeros((wl.B, wl.N), np.int32)
+    gk = np.zeros((wl.B, wl.N), np.uint8)
+    for b in range(wl.B):
+        ga[b], gk[b] = sd.select_anchors_host(wl.loss_mask[b], wl.N, wl.sampler_seed + b)
+    log(f"no-alloc forward: S=131072 N=4096 ({int(gk.sum())} kept)")
+    ref = ForwardRun(wl, 0, ga, gk).run()
+    torch.cuda.synchronize()
+    got, st, fb, intact = run_noalloc(sd, ref, guard=4096)
+    assert st == sd.DSPARK_OK and fb == -1, sd.last_error()
+    assert intact
+    want = ref.result()
+    same = np.array_equal(np.nan_to_num(got, nan=7.0), np.nan_to_num(want, nan=7.0))
+    log(f"  bit-identical to the workspace forward: {same}")
+    compare(got, want, gk, BF16_MAX_ABS, BF16_REL_L2, what="no-alloc vs workspace S=131072")
