@@ -317,6 +317,161 @@ __global__ __launch_bounds__(256) void dw_kernel(const bf16* __restrict__ olat,
     }
 }
 
+// ---- weight gradients with LDS DMA: the same reduction in 256-position x
+// (128 or 96)-output tiles, 8 per head (dW_UV 2 x 2, dW_UK 2 x 2), two
+// workgroups per compute unit.  The 2 x 2 waves each own a 128 x 64 (or
+// 128 x 48) quarter, which halves the LDS bytes read per MFMA against
+// 64 x 32 quarters; LDS bandwidth, not HBM, bounded the smaller tiles.
+// Operands reach LDS by buffer DMA (no register staging, no LDS store
+// instructions) in a ring of three 32-row stages, two stages in flight while
+// the third is consumed.  Each stage row holds its 16-byte chunks XOR-
+// swizzled by row ((2 row) mod 16), so that the transposing reads of eight
+// consecutive rows hit distinct banks.  Rows past the last kept row read
+// zero: the lat operand through the bound of its buffer resource, the
+// gathered operand through an offset past it.
+constexpr int kDwBM = 256;                          // latent positions per tile
+constexpr int kDwArow = kDwBM;                      // A stage row (elements, 512 B)
+constexpr int kDwBrow = 128;                        // B stage row (elements, 256 B)
+constexpr int kDwStage = 32 * (kDwArow + kDwBrow);  // elements per stage
+constexpr int kDwStages = 3;
+constexpr int kDwSlots = 1024;                      // slots per LDS row table
+constexpr int kDwCopies = 6;                        // DMA instructions per wave per stage
+constexpr int kDwPerHead = (kD / kDwBM) * 2 * 2;    // 4 dW_UV + 4 dW_UK tiles
+constexpr uint32_t kPastEnd = 0x80000000u;          // an offset beyond every bound used
+
+__device__ inline int dw_swz(int row) { return (2 * row) & 15; }
+
+template <int NT, int NOUT>
+__device__ inline void dw_dma_tile(const bf16* __restrict__ lat, const bf16* __restrict__ rowsrc,
+                                   const int4* __restrict__ srec, int n_slots, int h, int m0,
+                                   int n0, int N, int L5, size_t src_rows, bf16* __restrict__ dw,
+                                   bf16* lds, int* rbase) {
+    constexpr int MT = 8;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int g = lane >> 4, l16 = lane & 15;
+    const int wm = wave >> 1, wn = wave & 1;
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // the gathered operand: every input row of head h from column n0 on
+    const bf16* bbase = rowsrc + (size_t)h * NOUT + n0;
+    const i32x4 rs_b = rsrc_words(bbase, (uint32_t)(src_rows * kH * NOUT * 2 -
+                                                    ((size_t)h * NOUT + n0) * 2));
+    constexpr uint32_t kLatRow = kH * kD * 2, kSrcRow = kH * NOUT * 2;
+
+    // transposing fragment read of a swizzled stage: 16 rows of k (two
+    // reads of 4 x 4), columns r0 .. r0 + 15
+    auto frag = [&](const bf16* base, int rowlen, int r0) -> bf16x8 {
+        const int col = r0 + 4 * (l16 & 3);
+        const int rr = 4 * g + (l16 >> 2);
+        const bf16* p0 = base + rr * rowlen + ((((col >> 3) ^ dw_swz(rr)) << 3) | (col & 7));
+        const bf16* p1 = base + (rr + 16) * rowlen +
+                         ((((col >> 3) ^ dw_swz(rr + 16)) << 3) | (col & 7));
+        return cat(lds_read_tr(p0), lds_read_tr(p1));
+    };
+
+    for (int c0 = 0; c0 < n_slots; c0 += kDwSlots) {
+        const int nsl = min(kDwSlots, n_slots - c0);
+        __syncthreads();                 // the previous chunk is done with the table and stages
+        for (int i = tid; i < nsl; i += blockDim.x) {
+            const int blk = srec[c0 + i].w;
+            rbase[i] = (blk / N) * L5 + kBlock * (blk % N);
+        }
+        __syncthreads();
+        const int krows = kBlock * nsl;
+        const int steps = (krows + 31) / 32;
+        const i32x4 rs_a = rsrc_words(lat + ((size_t)kBlock * c0 * kH + h) * kD + m0,
+                                      (uint32_t)krows * kLatRow);
+
+        // stage s (rows 32 s .. 32 s + 31 of this chunk) into ring slot s % 3:
+        // A as 16 copies of two 512-byte rows, B as 8 copies of four 256-byte
+        // rows; wave w issues A copies 4w .. 4w + 3 and B copies 2w, 2w + 1
+        auto issue = [&](int s) {
+            char* st = reinterpret_cast<char*>(lds + (s % kDwStages) * kDwStage);
+            uint32_t boff[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int row = 4 * (2 * wave + q) + (lane >> 4);
+                const int k = 32 * s + row;
+                const int lc = (lane & 15) ^ dw_swz(row);
+                boff[q] = kPastEnd;
+                if (k < krows) {
+                    const int sl = k / kBlock;
+                    boff[q] = (uint32_t)(rbase[sl] + (k - kBlock * sl)) * kSrcRow + 16 * lc;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r2 = 2 * (4 * wave + q);
+                const int row = r2 + (lane >> 5);
+                const int lc = (lane & 31) ^ dw_swz(row);
+                copy_16_untracked(rs_a, (uint32_t)(32 * s + row) * kLatRow + 16 * lc,
+                                  st + r2 * (kDwArow * 2));
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                copy_16_untracked(rs_b, boff[q],
+                                  st + 32 * kDwArow * 2 + 4 * (2 * wave + q) * (kDwBrow * 2));
+        };
+
+        issue(0);
+        if (steps > 1) issue(1);
+        for (int s = 0; s < steps; ++s) {
+            // this wave's copies of stage s are done (only stage s + 1's may be
+            // in flight); the barrier makes every wave's copies visible and
+            // ends every read of the slot stage s + 2 reuses
+            if (s + 1 < steps) __builtin_amdgcn_s_waitcnt(wait_vm(kDwCopies));
+            else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+            __syncthreads();
+            if (s + 2 < steps) issue(s + 2);
+            const bf16* st = lds + (s % kDwStages) * kDwStage;
+            bf16x8 af[MT], bfr[NT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i) af[i] = frag(st, kDwArow, wm * 16 * MT + 16 * i);
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                bfr[j] = frag(st + 32 * kDwArow, kDwBrow, wn * 16 * NT + 16 * j);
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int o = n0 + wn * 16 * NT + 16 * j + l16;
+        bf16* dst = dw + ((size_t)h * NOUT + o) * kD;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            const int pos = m0 + wm * 16 * MT + 16 * i + 4 * g;
+            gst8(dst + dim_of_pos4(pos), to_bf16x4(acc[i][j]));
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void dw_dma_kernel(
+    const bf16* __restrict__ olat, const bf16* __restrict__ dout, const bf16* __restrict__ dqabs,
+    const bf16* __restrict__ q_nope, const int4* __restrict__ srec,
+    const int32_t* __restrict__ status, bf16* __restrict__ dw_uv, bf16* __restrict__ dw_uk, int N,
+    int L5, int in_rows) {
+    static_assert(kD % kDwBM == 0 && kDv == 2 * 128 && kDc == 2 * 96, "tile split");
+    __shared__ __attribute__((aligned(16))) bf16 lds[kDwStages * kDwStage];
+    __shared__ int rbase[kDwSlots];
+    const int n_slots = status[kStKeptCount];
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = lid / kDwPerHead, t = lid % kDwPerHead;
+    const int m0 = ((t & 3) >> 1) * kDwBM;
+    if (t < 4)
+        dw_dma_tile<4, kDv>(olat, dout, srec, n_slots, h, m0, (t & 1) * 128, N, L5, in_rows,
+                            dw_uv, lds, rbase);
+    else
+        dw_dma_tile<3, kDc>(dqabs, q_nope, srec, n_slots, h, m0, (t & 1) * 96, N, L5, in_rows,
+                            dw_uk, lds, rbase);
+}
+
 // ---- per block: dc_k (M = D, permuted positions) and d(R k^R)_k (M = d_r,
 // natural) for its key slots (N = 144), K = its 320 rows taken twice
 // (P with d_olat, then dS' with q_abs; the k^R part only dS' with R q^R).
@@ -401,6 +556,15 @@ hipError_t launch_bwd_dqnope(const Problem& p, const Inputs& in, const BwdGrads&
 
 hipError_t launch_bwd_dw(const Problem& p, const Inputs& in, const BwdGrads& g,
                          const BwdWork& w, hipStream_t s) {
+    // the DMA kernel addresses the gathered inputs with 32-bit offsets
+    const size_t in_rows = (size_t)p.B * p.L5;
+    if (in_rows * kH * kDv * 2 < kPastEnd && in_rows * kH * kDc * 2 < kPastEnd &&
+        (size_t)kBlock * kDwSlots * kH * kD * 2 < kPastEnd) {
+        hipLaunchKernelGGL(dw_dma_kernel, dim3(kH * kDwPerHead), dim3(256), 0, s, w.fwd.olat,
+                           (const bf16*)g.dout, w.dqabs, (const bf16*)in.q_nope, w.fwd.srec,
+                           w.fwd.status, (bf16*)g.dw_uv, (bf16*)g.dw_uk, p.N, p.L5, (int)in_rows);
+        return hipGetLastError();
+    }
     constexpr int kPerHead = (kD / CfgDwuv::BM) * (kDv / CfgDwuv::BN) +
                              (kD / CfgDwuk::BM) * (kDc / CfgDwuk::BN);
     hipLaunchKernelGGL(dw_kernel, dim3(kH * kPerHead), dim3(256), 0, s, w.fwd.olat,
