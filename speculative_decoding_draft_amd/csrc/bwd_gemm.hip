@@ -473,72 +473,187 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---- per block: dc_k (M = D, permuted positions) and d(R k^R)_k (M = d_r,
-// natural) for its key slots (N = 144), K = its 320 rows taken twice
-// (P with d_olat, then dS' with q_abs; the k^R part only dS' with R q^R).
-// When every sample's kept anchors ascend, each block writes its partial
-// rows and the final pass sums, per context row, the contiguous range of
-// blocks whose windows hold it; otherwise the sums go to the fp32
-// accumulator with atomics.  A block's own 5 keys are its alone.
-using CfgDkv = Cfg<64, kKeySlots, 4, 1, true, false, true, false>;
-__global__ __launch_bounds__(256) void dkv_kernel(const bf16* __restrict__ dolat,
-                                                  const bf16* __restrict__ qabs,
-                                                  const bf16* __restrict__ qrot,
-                                                  const bf16* __restrict__ pmat,
-                                                  const bf16* __restrict__ dsmat,
-                                                  const int4* __restrict__ srec,
-                                                  const int32_t* __restrict__ status,
-                                                  float* __restrict__ part,
-                                                  float* __restrict__ acc, int S, int N, int L5) {
-    __shared__ __attribute__((aligned(16))) bf16 lds[CfgDkv::LDS_ELEMS];
-    constexpr int kTiles = (kD + kDr) / CfgDkv::BM;    // 9
-    constexpr int kRows = kBlock * kH;                 // 320
-    const int n_live = status[kStKeptCount];
-    const int lid = xcd_balance(blockIdx.x, n_live * kTiles);
-    if (lid < 0) return;
-    const int slot = lid / kTiles, mt = lid % kTiles;
-    const int m0 = mt * CfgDkv::BM;
-    const size_t lat0 = (size_t)kBlock * slot * kH;    // first latent row (t = 0, h = 0)
-    const bf16* pm = pmat + (size_t)slot * kRows * kKeySlots;
-    const bf16* ds = dsmat + (size_t)slot * kRows * kKeySlots;
-    const bool rope_tile = m0 >= kD;
-    auto arow = [&](int k) -> const bf16* {
-        if (rope_tile) return qrot + (lat0 + (k - kRows)) * kDr;
-        return (k < kRows) ? dolat + (lat0 + k) * kD + m0 : qabs + (lat0 + k - kRows) * kD + m0;
-    };
-    auto brow = [&](int k) -> const bf16* {
-        return (k < kRows) ? pm + (size_t)k * kKeySlots : ds + (size_t)(k - kRows) * kKeySlots;
-    };
-    f32x4 a[CfgDkv::MT][CfgDkv::NT];
-    gemm_zero<CfgDkv>(a);
-    gemm_tile<CfgDkv>(arow, brow, rope_tile ? kRows / 32 : 0, 2 * kRows / 32, lds, a);
+// natural) for its key slots (N = 144): four 128-position tiles of dc (K =
+// the 320 rows twice: P with d_olat, then dS' with q_abs) and one 64-dim
+// tile of the rotated-key gradient (K = dS' with R q^R).  When every
+// sample's kept anchors ascend, each block writes its partial rows and the
+// final pass sums, per context row, the contiguous range of blocks whose
+// windows hold it; otherwise the sums go to the fp32 accumulator with
+// atomics.  A block's own 5 keys are its alone.
+// Each wave owns 32 (or 16) rows x 144 keys, so a k-step reads 11 fragments
+// for 18 MFMAs (64-row tiles: 10 for 9), and the P / dS' rows go to L2 five
+// times per block instead of nine.  Operands reach LDS by buffer DMA in a
+// three-stage ring, like the weight gradients.  A block's operand rows are
+// contiguous, so every copy is a plain range: A rows XOR-swizzled by row
+// (256-byte rows: (2 row) mod 16; 128-byte rows: row & 6), B rows (288
+// bytes, 8 dwords past a multiple of 64 banks) stored as they are, which
+// already keeps eight rows' transposing reads on distinct banks.
+constexpr int kKvBM = 128;                          // dc positions per tile
+constexpr int kKvBrow = kKeySlots;                  // B stage row (elements, 288 B)
+constexpr int kKvAbytes = 32 * kKvBM * 2;           // 8 KB
+constexpr int kKvStageBytes = kKvAbytes + 32 * kKvBrow * 2;   // + 9 KB
+constexpr int kKvStages = 3;
+constexpr int kKvTiles = kD / kKvBM + 1;            // 4 dc tiles + the k^R tile
+constexpr int kKvBcopies = 32 * kKvBrow * 2 / 1024; // 9 one-KB copies per stage
 
+template <int MT>
+__device__ inline void dkv_dma_tile(const bf16* __restrict__ dolat, const bf16* __restrict__ qabs,
+                                    const bf16* __restrict__ qrot, const bf16* __restrict__ pm,
+                                    const bf16* __restrict__ ds, size_t lat0, int m0, char* lds,
+                                    f32x4 (&acc)[MT][9]) {
+    constexpr bool kRope = MT == 1;                 // rope tile: 64 dims, rows 128 B
+    constexpr int kRows = kBlock * kH;              // 320
+    constexpr int kArow = kRope ? kDr : kKvBM;      // A stage row (elements)
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 9; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const i32x4 rs_p = rsrc_words(pm, kRows * kKeySlots * 2);
+    const i32x4 rs_ds = rsrc_words(ds, kRows * kKeySlots * 2);
+    const i32x4 rs_dol = rsrc_words(dolat + lat0 * kD + m0, kRows * kD * 2);
+    const i32x4 rs_qa = rsrc_words(qabs + lat0 * kD + m0, kRows * kD * 2);
+    const i32x4 rs_qr = rsrc_words(qrot + lat0 * kDr, kRows * kDr * 2);
+    auto swz = [](int row) { return kRope ? (row & 6) : ((2 * row) & 15); };
+
+    // stage s: k rows 32 s .. 32 s + 31 of [P | dS'] x [d_olat | q_abs]
+    // (rope: of dS' x R q^R, s >= 10)
+    auto issue = [&](int s) {
+        char* st = lds + (s % kKvStages) * kKvStageBytes;
+        const bool second = s >= kRows / 32;
+        const int r0 = 32 * (second ? s - kRows / 32 : s);
+        if constexpr (kRope) {
+            // 4 copies of eight 128-byte rows, one per wave
+            const int row = 8 * wave + (lane >> 3);
+            const int lc = (lane & 7) ^ swz(row);
+            copy_16_untracked(rs_qr, (uint32_t)(r0 + row) * (kDr * 2) + 16 * lc,
+                              st + 8 * wave * (kDr * 2));
+        } else {
+            // 8 copies of four 256-byte rows, two per wave
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int r4 = 4 * (2 * wave + q);
+                const int row = r4 + (lane >> 4);
+                const int lc = (lane & 15) ^ swz(row);
+                copy_16_untracked(second ? rs_qa : rs_dol,
+                                  (uint32_t)(r0 + row) * (kD * 2) + 16 * lc,
+                                  st + r4 * (kKvBM * 2));
+            }
+        }
+        // B: the stage's 32 rows are one contiguous 9 KB range
+        const uint32_t b0 = (uint32_t)r0 * (kKeySlots * 2);
+        for (int q = wave; q < kKvBcopies; q += 4)
+            copy_16_untracked(second ? rs_ds : rs_p, b0 + 1024 * q + 16 * lane,
+                              st + kKvAbytes + 1024 * q);
+    };
+    // copies per wave per stage: A (2, rope 1) + B (3 for wave 0, else 2)
+    constexpr int kAc = kRope ? 1 : 2;
+
+    auto frag_a = [&](const bf16* base, int r0) -> bf16x8 {
+        const int col = r0 + 4 * (l16 & 3);
+        const int rr = 4 * g + (l16 >> 2);
+        const bf16* p0 = base + rr * kArow + ((((col >> 3) ^ swz(rr)) << 3) | (col & 7));
+        const bf16* p1 = base + (rr + 16) * kArow +
+                         ((((col >> 3) ^ swz(rr + 16)) << 3) | (col & 7));
+        return cat(lds_read_tr(p0), lds_read_tr(p1));
+    };
+    auto frag_b = [&](const bf16* base, int r0) -> bf16x8 {
+        const int col = r0 + 4 * (l16 & 3);
+        const int rr = 4 * g + (l16 >> 2);
+        return cat(lds_read_tr(base + rr * kKvBrow + col),
+                   lds_read_tr(base + (rr + 16) * kKvBrow + col));
+    };
+
+    const int s0 = kRope ? kRows / 32 : 0, s1 = 2 * kRows / 32;
+    issue(s0);
+    issue(s0 + 1);
+    for (int s = s0; s < s1; ++s) {
+        if (s + 1 < s1) {
+            if (wave == 0) __builtin_amdgcn_s_waitcnt(wait_vm(kAc + 3));
+            else __builtin_amdgcn_s_waitcnt(wait_vm(kAc + 2));
+        } else {
+            __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        }
+        __syncthreads();
+        if (s + 2 < s1) issue(s + 2);
+        const char* st = lds + (s % kKvStages) * kKvStageBytes;
+        const bf16* sa = reinterpret_cast<const bf16*>(st);
+        const bf16* sb = reinterpret_cast<const bf16*>(st + kKvAbytes);
+        bf16x8 af[MT], bfr[9];
+#pragma unroll
+        for (int i = 0; i < MT; ++i) af[i] = frag_a(sa, wave * 16 * MT + 16 * i);
+#pragma unroll
+        for (int j = 0; j < 9; ++j) bfr[j] = frag_b(sb, 16 * j);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < 9; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+    }
+}
+
+template <int MT>
+__device__ inline void dkv_store(const f32x4 (&a)[MT][9], int m0, int slot, const int4* srec,
+                                 const int32_t* status, float* part, float* acc, int S, int N,
+                                 int L5) {
+    constexpr bool kRope = MT == 1;
     const int4 rec = srec[slot];
     const int blk = rec.w, b = blk / N, n = blk % N;
     const int ctx_lo = rec.x, ctx_len = rec.y, nkeys = ctx_len + kBlock;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
     const size_t arow0 = (size_t)b * (S + L5);
-    const int pos = wave * 16 + 4 * g;                  // CfgDkv: WM = 4, MT = 1
-    const int dim = rope_tile ? kD + pos : dim_of_pos4(m0 + pos);
-    if (status[kStUnsorted] == 0) {
-        // the block's own partial rows; the final pass sums the blocks whose
-        // windows cover each context row
-        float* base = part + (size_t)slot * kMaxKeys * (kD + kDr) + dim;
 #pragma unroll
-        for (int j = 0; j < CfgDkv::NT; ++j) {
-            const int key = 16 * j + l16;
-            if (key < nkeys) *reinterpret_cast<f32x4*>(base + (size_t)key * (kD + kDr)) = a[0][j];
+    for (int i = 0; i < MT; ++i) {
+        const int pos = wave * 16 * MT + 16 * i + 4 * g;
+        const int dim = kRope ? kD + pos : dim_of_pos4(m0 + pos);
+        if (status[kStUnsorted] == 0) {
+            float* base = part + (size_t)slot * kMaxKeys * (kD + kDr) + dim;
+#pragma unroll
+            for (int j = 0; j < 9; ++j) {
+                const int key = 16 * j + l16;
+                if (key < nkeys)
+                    *reinterpret_cast<f32x4*>(base + (size_t)key * (kD + kDr)) = a[i][j];
+            }
+            continue;
         }
-        return;
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+            const int key = 16 * j + l16;
+            if (key >= nkeys) continue;
+            const size_t r = arow0 + ((key < ctx_len) ? (size_t)(ctx_lo + key)
+                                                      : (size_t)S + kBlock * n + (key - ctx_len));
+            float* dst = acc + r * (kD + kDr) + dim;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) atomicAdd(dst + e, a[i][j][e]);
+        }
     }
-#pragma unroll
-    for (int j = 0; j < CfgDkv::NT; ++j) {
-        const int key = 16 * j + l16;
-        if (key >= nkeys) continue;
-        const size_t r = arow0 + ((key < ctx_len) ? (size_t)(ctx_lo + key)
-                                                  : (size_t)S + kBlock * n + (key - ctx_len));
-        float* dst = acc + r * (kD + kDr) + dim;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) atomicAdd(dst + i, a[0][j][i]);
+}
+
+__global__ __launch_bounds__(256) void dkv_dma_kernel(
+    const bf16* __restrict__ dolat, const bf16* __restrict__ qabs, const bf16* __restrict__ qrot,
+    const bf16* __restrict__ pmat, const bf16* __restrict__ dsmat, const int4* __restrict__ srec,
+    const int32_t* __restrict__ status, float* __restrict__ part, float* __restrict__ acc, int S,
+    int N, int L5) {
+    static_assert(kKeySlots == 9 * 16 && (32 * kKvBrow * 2) % 1024 == 0, "B stage copies");
+    __shared__ __attribute__((aligned(16))) char lds[kKvStages * kKvStageBytes];
+    constexpr int kRows = kBlock * kH;
+    const int n_live = status[kStKeptCount];
+    const int lid = xcd_balance(blockIdx.x, n_live * kKvTiles);
+    if (lid < 0) return;
+    const int slot = lid / kKvTiles, mt = lid % kKvTiles;
+    const size_t lat0 = (size_t)kBlock * slot * kH;
+    const bf16* pm = pmat + (size_t)slot * kRows * kKeySlots;
+    const bf16* ds = dsmat + (size_t)slot * kRows * kKeySlots;
+    if (mt < kKvTiles - 1) {
+        f32x4 a[2][9];
+        dkv_dma_tile<2>(dolat, qabs, qrot, pm, ds, lat0, mt * kKvBM, lds, a);
+        dkv_store<2>(a, mt * kKvBM, slot, srec, status, part, acc, S, N, L5);
+    } else {
+        f32x4 a[1][9];
+        dkv_dma_tile<1>(dolat, qabs, qrot, pm, ds, lat0, 0, lds, a);
+        dkv_store<1>(a, 0, slot, srec, status, part, acc, S, N, L5);
     }
 }
 
@@ -574,10 +689,9 @@ hipError_t launch_bwd_dw(const Problem& p, const Inputs& in, const BwdGrads& g,
 }
 
 hipError_t launch_bwd_dkv(const Problem& p, const BwdWork& w, hipStream_t s) {
-    constexpr int kTiles = (kD + kDr) / CfgDkv::BM;
-    int grid = p.B * p.N * kTiles;
+    int grid = p.B * p.N * kKvTiles;
     grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL(dkv_kernel, dim3(grid), dim3(256), 0, s, w.dolat, w.fwd.qabs, w.qrot,
+    hipLaunchKernelGGL(dkv_dma_kernel, dim3(grid), dim3(256), 0, s, w.dolat, w.fwd.qabs, w.qrot,
                        w.pmat, w.dsmat, w.fwd.srec, w.fwd.status, w.part, w.acc, p.S, p.N, p.L5);
     return hipGetLastError();
 }
