@@ -651,7 +651,7 @@ dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc, const void* q_nop
         DSPARK_STEP(launch_absorb_dv(p, dout, w_uv, w.fwd, w.dolat, s), "W_UV^T dout launch");
         DSPARK_STEP(launch_bwd_attn(p, in, g, w, theta, s, !reuse), "backward attention launch");
         DSPARK_STEP(launch_bwd_dkv(p, w, s), "dc^KV launch");
-        DSPARK_STEP(launch_bwd_dqnope(p, in, g, w, s), "dq^C launch");
+        DSPARK_STEP(launch_uv_dqc(p, in.w_uk, w.dqabs, w.fwd, g.dq_nope, s), "dq^C launch");
         DSPARK_STEP(launch_bwd_dw(p, in, g, w, s), "weight-gradient launch");
     } else {
         DSPARK_STEP(launch_bwd_generic(p, d.dtype == DSPARK_BF16, in, g, w, s),

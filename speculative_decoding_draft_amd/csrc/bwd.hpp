@@ -130,11 +130,13 @@ hipError_t launch_bwd_finalize(const Problem& p, bool bf16_io, const BwdGrads& g
 // with d_v = 256 input dims (absorb.hip); written in the permuted latent order.
 hipError_t launch_absorb_dv(const Problem& p, const void* dout, const void* w_uv,
                             const Workspace& ws, bf16* dolat, hipStream_t s);
+// dq^C = W_UK[h] dq_abs for every kept row: the forward's W_UV kernel with
+// 192 output dims (uv.hip).
+hipError_t launch_uv_dqc(const Problem& p, const void* w_uk, const bf16* dqabs,
+                         const Workspace& ws, void* dq_nope, hipStream_t s);
 hipError_t launch_bwd_attn(const Problem& p, const Inputs& in, const BwdGrads& g,
                            const BwdWork& w, const RopeTheta& th, hipStream_t s, bool write_olat);
 hipError_t launch_bwd_dkv(const Problem& p, const BwdWork& w, hipStream_t s);
-hipError_t launch_bwd_dqnope(const Problem& p, const Inputs& in, const BwdGrads& g,
-                             const BwdWork& w, hipStream_t s);
 hipError_t launch_bwd_dw(const Problem& p, const Inputs& in, const BwdGrads& g,
                          const BwdWork& w, hipStream_t s);
 

@@ -1,8 +1,8 @@
 // Backward of the masked latent attention, MFMA path: the dense products
 // around the attention kernel, as tiled bf16 MFMA GEMMs with fp32
-// accumulation (W_UV^T dout runs on the forward's absorb kernel).
+// accumulation (W_UV^T dout runs on the forward's absorb kernel, dq^C =
+// W_UK[h] dq_abs on its W_UV kernel).
 //
-//   dq^C   = W_UK[h] dq_abs              per head, over the kept query rows
 //   dW_UV[h] = sum_rows dout (o_lat)^T   per head, reduction over every row
 //   dW_UK[h] = sum_rows q^C (dq_abs)^T   per head
 //   dc_k  = sum_rows P d_olat + dS' q_abs, d(R k^R)_k = sum_rows dS' (R q^R)
@@ -192,49 +192,8 @@ __device__ inline void gemm_tile(const AF& arow, const BF& brow, int s0, int s1,
     }
 }
 
-// input row (b * 5N + 5n + t) of latent row R = 5 * slot + t
-__device__ inline size_t input_row(const int4* srec, int R, int N, int L5) {
-    const int blk = srec[R / kBlock].w;
-    return (size_t)(blk / N) * L5 + (size_t)kBlock * (blk % N) + R % kBlock;
-}
-
 __device__ inline bf16x4 to_bf16x4(f32x4 v) {
     return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-}
-
-// ---- dq^C[R][h] = W_UK[h] dq_abs[R][h]: M = d_c, N = rows, K = D.
-// A = W_UK[h] rows (natural), B = dq_abs rows (permuted).
-using CfgDqn = Cfg<192, 128, 2, 2, false, false, false, true, 1>;
-__global__ __launch_bounds__(256) void dqnope_kernel(const bf16* __restrict__ dqabs,
-                                                     const bf16* __restrict__ w_uk,
-                                                     const int4* __restrict__ srec,
-                                                     const int32_t* __restrict__ status,
-                                                     bf16* __restrict__ dq_nope, int N, int L5) {
-    __shared__ __attribute__((aligned(16))) bf16 lds[CfgDqn::LDS_ELEMS];
-    const int rows = kBlock * status[kStKeptCount];
-    const int m0 = blockIdx.x * CfgDqn::BM, n0 = blockIdx.y * CfgDqn::BN, h = blockIdx.z;
-    if (n0 >= rows) return;
-    const bf16* wh = w_uk + ((size_t)h * kDc + m0) * kD;
-    auto arow = [&](int r) -> const bf16* { return wh + (size_t)r * kD; };
-    auto brow = [&](int r) -> const bf16* {
-        const int R = n0 + r;
-        return R < rows ? dqabs + ((size_t)R * kH + h) * kD : nullptr;
-    };
-    f32x4 acc[CfgDqn::MT][CfgDqn::NT];
-    gemm_zero<CfgDqn>(acc);
-    gemm_tile<CfgDqn>(arow, brow, 0, kD / 32, lds, acc);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, l16 = lane & 15;
-    const int wm = wave / CfgDqn::WN, wn = wave % CfgDqn::WN;
-#pragma unroll
-    for (int j = 0; j < CfgDqn::NT; ++j) {
-        const int R = n0 + wn * (CfgDqn::BN / CfgDqn::WN) + 16 * j + l16;
-        if (R >= rows) continue;
-        bf16* dst = dq_nope + (input_row(srec, R, N, L5) * kH + h) * kDc;
-#pragma unroll
-        for (int i = 0; i < CfgDqn::MT; ++i)
-            gst8(dst + m0 + wm * (CfgDqn::BM / CfgDqn::WM) + 16 * i + 4 * g,
-                 to_bf16x4(acc[i][j]));
-    }
 }
 
 // ---- weight gradients, a reduction over every kept row: M = D (latent
@@ -658,16 +617,6 @@ __global__ __launch_bounds__(256) void dkv_dma_kernel(
 }
 
 }  // namespace
-
-hipError_t launch_bwd_dqnope(const Problem& p, const Inputs& in, const BwdGrads& g,
-                             const BwdWork& w, hipStream_t s) {
-    const int rows = kBlock * p.B * p.N;
-    static_assert(kDc % CfgDqn::BM == 0, "whole tiles");
-    const dim3 grid(kDc / CfgDqn::BM, (rows + CfgDqn::BN - 1) / CfgDqn::BN, kH);
-    hipLaunchKernelGGL(dqnope_kernel, grid, dim3(256), 0, s, w.dqabs, (const bf16*)in.w_uk,
-                       w.fwd.srec, w.fwd.status, (bf16*)g.dq_nope, p.N, p.L5);
-    return hipGetLastError();
-}
 
 hipError_t launch_bwd_dw(const Problem& p, const Inputs& in, const BwdGrads& g,
                          const BwdWork& w, hipStream_t s) {

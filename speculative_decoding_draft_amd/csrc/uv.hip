@@ -10,6 +10,10 @@
 // 32k + 4g + s for s < 4, 32k + 16 + 4g + (s-4) for s >= 4); the weight
 // fragments are read in the same order, two 8-byte pieces per lane.
 //
+// The same kernel, with 192 output dims and 6 waves, computes the
+// backward's dq^C[r][h] = W_UK[h] dq_abs[r][h] (512 -> 192): dq_abs has
+// o_lat's layout and W_UK[h] W_UV[h]'s.
+//
 // Work split: a workgroup (8 waves, two per SIMD) owns one head and a
 // strided range of 32-row iterations; wave w computes output dims
 // 32w .. 32w+31, transposed (dims x rows), with its 32 x 512 slice of
@@ -29,23 +33,37 @@ namespace dspark {
 
 namespace {
 
-constexpr int kUvWaves = 8;                   // one per 32 output dims
 constexpr int kUvRowGroups = 4;               // workgroups per head
 constexpr int kUvRows = 32;                   // o_lat rows per iteration
-constexpr int kUvCopies = kUvRows / kUvWaves; // copy instructions per wave and iteration
 constexpr int kUvLdsStride = kD * 2 + 16;     // bytes per staged o_lat row (pad: no bank conflicts)
 constexpr int kUvSlot = kUvRows * kUvLdsStride;
-constexpr int kUvEpiStride = kDv * 2 + 16;    // bytes per row of the output transpose
-constexpr int kUvStores = kUvRows * kDv * 2 / 1024 / kUvWaves;   // 1 KB stores per wave and iteration
 constexpr int kUvKs = kD / 32;                // 16 k-steps
 
+// Shape of the kernel for DOUT output dims: one wave per 32 dims.  A wave
+// issues kCopies o_lat row copies and kStores output stores (two rows each)
+// per iteration; where the waves do not divide the 32 rows (or 16 stores)
+// evenly, the last indices repeat the last row: the same bytes to the same
+// place.
+template <int DOUT>
+struct UvCfg {
+    static constexpr int kWaves = DOUT / 32;
+    static constexpr int kCopies = (kUvRows + kWaves - 1) / kWaves;
+    static constexpr int kStores = (kUvRows / 2 + kWaves - 1) / kWaves;
+    static constexpr int kEpiStride = DOUT * 2 + 16;    // bytes per row of the output transpose
+    static constexpr int kHalf = DOUT / 2;              // weight rows staged per half
+    static_assert(DOUT % 64 == 0 && kHalf <= 4 * kUvRows && kHalf % kWaves == 0, "uv shape");
+};
 
-__global__ __launch_bounds__(kUvWaves * 64) void uv_kernel(const bf16* __restrict__ w_uv,
+template <int DOUT>
+__global__ __launch_bounds__(DOUT / 32 * 64) void uv_kernel(const bf16* __restrict__ w_uv,
                                                  const bf16* __restrict__ o_lat,
                                                  const int32_t* __restrict__ kept,
                                                  const int32_t* __restrict__ status,
                                                  bf16* __restrict__ out, int N, int L5,
                                                  int slot0, int nslots) {
+    using C = UvCfg<DOUT>;
+    constexpr int kUvWaves = C::kWaves, kUvCopies = C::kCopies, kUvStores = C::kStores;
+    constexpr int kUvEpiStride = C::kEpiStride;
     // the ring slots are separate arrays so that the compiler sees that a
     // copy into one slot does not touch the slot being read
     __shared__ __attribute__((aligned(16))) char s0[kUvSlot];
@@ -73,10 +91,10 @@ __global__ __launch_bounds__(kUvWaves * 64) void uv_kernel(const bf16* __restric
     // 32*wave + 8g .. 32*wave + 8g + 7; k-values follow the permuted o_lat
     // order (dims 32ks + 4g + 0..3 and 32ks + 16 + 4g + 0..3).
     // W_UV[h] reaches them through the ring slots (idle until the first
-    // o_lat copy) in two halves of 128 output dims: one 1 KB weight row per
-    // wave instruction, row r of a half at slot r / 32, row r % 32 (the
-    // ring's own row stride); the four waves whose dims a half holds then
-    // read their fragments out of LDS.  Loading the fragments straight from
+    // o_lat copy) in two halves of DOUT / 2 output dims: one 1 KB weight row
+    // per wave instruction, row r of a half at slot r / 32, row r % 32 (the
+    // ring's own row stride); the waves whose dims a half holds then read
+    // their fragments out of LDS.  Loading the fragments straight from
     // memory (8 bytes a lane from 16 rows per instruction) made a 64-block
     // call ~6 us slower.
     auto slot_of = [&](int k) -> char* { return k == 0 ? s0 : k == 1 ? s1 : k == 2 ? s2 : s3; };
@@ -84,15 +102,15 @@ __global__ __launch_bounds__(kUvWaves * 64) void uv_kernel(const bf16* __restric
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int i = 0; i < 128 / kUvWaves; ++i) {
-            const int r = wave * (128 / kUvWaves) + i;     // uniform per wave
-            async_copy_16(w_uv + ((size_t)h * kDv + 128 * half + r) * kD + lane * 8,
+        for (int i = 0; i < C::kHalf / kUvWaves; ++i) {
+            const int r = wave * (C::kHalf / kUvWaves) + i;     // uniform per wave
+            async_copy_16(w_uv + ((size_t)h * DOUT + C::kHalf * half + r) * kD + lane * 8,
                           slot_of(r / 32) + (r % 32) * kUvLdsStride);
         }
         __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
         __syncthreads();
-        if (wave / 4 == half) {
-            const char* base = slot_of(wave % 4);
+        if (wave / (kUvWaves / 2) == half) {
+            const char* base = slot_of(wave % (kUvWaves / 2));
 #pragma unroll
             for (int vt = 0; vt < 2; ++vt) {
                 const bf16* row = reinterpret_cast<const bf16*>(
@@ -107,8 +125,8 @@ __global__ __launch_bounds__(kUvWaves * 64) void uv_kernel(const bf16* __restric
     }
 
     // Copy of the workgroup's k-th iteration into `dst`: wave w copies rows
-    // 4w .. 4w+3, one o_lat row (1 KB) per instruction; rows past the end
-    // copy the last row.  Iterations past the last one are still issued (so
+    // kCopies w .. kCopies w + kCopies - 1 (at most 31), one o_lat row (1 KB)
+    // per instruction; rows past the end copy the last row.  Iterations past the last one are still issued (so
     // that every iteration issues the same memory operations) but read
     // nothing: their offsets fall outside the buffer resource, and such
     // reads return zeros without touching memory.
@@ -118,7 +136,7 @@ __global__ __launch_bounds__(kUvWaves * 64) void uv_kernel(const bf16* __restric
                                     (uint32_t)(kUvRows * kH * kD * sizeof(bf16)));
 #pragma unroll
         for (int q = 0; q < kUvCopies; ++q) {
-            const int lr = kUvCopies * wave + q;
+            const int lr = min(kUvCopies * wave + q, kUvRows - 1);
             const int r = min(r0 + lr, rows - 1) - r0;      // negative past the end
             const uint32_t off = (r >= 0) ? (uint32_t)((r * kH + h) * kD * sizeof(bf16) + lane * 16)
                                           : 0xFFFFFFF0u;
@@ -134,13 +152,15 @@ __global__ __launch_bounds__(kUvWaves * 64) void uv_kernel(const bf16* __restric
     };
 
     // Output transpose: every wave writes its 64 B of each of the 32 rows,
-    // then wave w stores rows 4w .. 4w+3 as 2 rows x 512 B per instruction.
-    // Rows past the end repeat the last row (same values, same place).  The
-    // kept blocks of those rows (at most 2 slots) are read with scalar loads.
+    // then wave w stores rows 2 kStores w .. (at most 31) as 2 rows x
+    // DOUT x 2 B per instruction.  Rows past the end repeat the last row
+    // (same values, same place).  The kept blocks of those rows (at most 2
+    // slots: 6 consecutive rows span at most two blocks of 5) are read with
+    // scalar loads.
     bf16x8 pend[2];
     int pk[2];            // kept[] of the 2 slots from pslot on
     int pslot = 0, prow0 = 0;
-    auto out_row = [&](int j) { return 4 * wave + 2 * j + (lane >> 5); };
+    auto out_row = [&](int j) { return 2 * min(kUvStores * wave + j, kUvRows / 2 - 1) + (lane >> 5); };
     auto flush = [&]() {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -149,14 +169,16 @@ __global__ __launch_bounds__(kUvWaves * 64) void uv_kernel(const bf16* __restric
         __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
         for (int j = 0; j < kUvStores; ++j) {
+            // lanes past the row's DOUT / 8 chunks read its last chunk and store nothing
             const bf16x8 v = *reinterpret_cast<const bf16x8*>(
-                &epi[out_row(j) * kUvEpiStride + (lane & 31) * 16]);
+                &epi[out_row(j) * kUvEpiStride + min(lane & 31, DOUT / 8 - 1) * 16]);
             const int r = min(prow0 + out_row(j), rows - 1);
             const int blk = (r / kBlock == pslot) ? pk[0] : pk[1];
             const int b = blk / N, n = blk % N;
-            gst16(out + (((size_t)b * L5 + (size_t)kBlock * n + r % kBlock) * kH + h) * kDv +
-                      (lane & 31) * 8,
-                  v);
+            if ((lane & 31) < DOUT / 8)
+                gst16(out + (((size_t)b * L5 + (size_t)kBlock * n + r % kBlock) * kH + h) * DOUT +
+                          (lane & 31) * 8,
+                      v);
         }
     };
 
@@ -203,7 +225,7 @@ __global__ __launch_bounds__(kUvWaves * 64) void uv_kernel(const bf16* __restric
             }
         }
         prow0 = (rg + k * kUvRowGroups) * kUvRows;
-        pslot = min(prow0 + 4 * wave, rows - 1) / kBlock;
+        pslot = min(prow0 + 2 * min(kUvStores * wave, kUvRows / 2 - 1), rows - 1) / kBlock;
 #pragma unroll
         for (int i = 0; i < 2; ++i) pk[i] = kept[slot0 + min(pslot + i, (rows - 1) / kBlock)];
 #pragma unroll
@@ -240,9 +262,18 @@ __global__ __launch_bounds__(kUvWaves * 64) void uv_kernel(const bf16* __restric
 hipError_t launch_uv(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
                      hipStream_t s) {
     const int grid = kH * kUvRowGroups;
-    hipLaunchKernelGGL(uv_kernel, dim3(grid), dim3(kUvWaves * 64), 0, s, (const bf16*)in.w_uv, ws.olat,
-                       ws.kept, ws.status, (bf16*)in.out, p.N, p.L5, c.slot0,
-                       c.nslots);
+    hipLaunchKernelGGL(uv_kernel<kDv>, dim3(grid), dim3(UvCfg<kDv>::kWaves * 64), 0, s,
+                       (const bf16*)in.w_uv, ws.olat, ws.kept, ws.status, (bf16*)in.out, p.N,
+                       p.L5, c.slot0, c.nslots);
+    return hipGetLastError();
+}
+
+hipError_t launch_uv_dqc(const Problem& p, const void* w_uk, const bf16* dqabs,
+                         const Workspace& ws, void* dq_nope, hipStream_t s) {
+    const int grid = kH * kUvRowGroups;
+    hipLaunchKernelGGL(uv_kernel<kDc>, dim3(grid), dim3(UvCfg<kDc>::kWaves * 64), 0, s,
+                       (const bf16*)w_uk, dqabs, ws.kept, ws.status, (bf16*)dq_nope, p.N, p.L5,
+                       0, p.B * p.N);
     return hipGetLastError();
 }
 
