@@ -392,7 +392,9 @@ __global__ __launch_bounds__(256) void gather_kernel(
     __syncthreads();
     const bool unsorted = status[kStUnsorted] != 0;
     const int n_live = status[kStKeptCount];
-    const int lane = threadIdx.x & 63, sub = threadIdx.x >> 6;
+    // sub is wave-uniform: the index records are then read with scalar loads
+    // (the binary searches below run on the scalar cache)
+    const int lane = threadIdx.x & 63, sub = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const size_t rows_per_b = (size_t)p.S + p.L5;
     const size_t n_rows = (size_t)p.B * rows_per_b;
     for (size_t r = (size_t)blockIdx.x * 4 + sub; r < n_rows; r += (size_t)gridDim.x * 4) {
@@ -433,9 +435,32 @@ __global__ __launch_bounds__(256) void gather_kernel(
                 // the blocks whose windows [A-W+1, A) hold row rr: r < A <= rr + W - 1
                 const int s0 = first_after(srec, n_live, p.N, b, rr);
                 const int s1 = first_after(srec, n_live, p.N, b, rr + p.W - 1);
-                for (int sl = s0; sl < s1; ++sl) {
-                    const int4 rec = srec[sl];
-                    add_row(part + ((size_t)sl * kMaxKeys + (rr - rec.x)) * (kD + kDr));
+                // up to four covering blocks' loads in flight at once
+                for (int sl = s0; sl < s1; sl += 4) {
+                    float4 x[4][3];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if (sl + u < s1) {
+                            const int4 rec = srec[sl + u];
+                            const float4* s4 = reinterpret_cast<const float4*>(
+                                part + ((size_t)(sl + u) * kMaxKeys + (rr - rec.x)) * (kD + kDr));
+#pragma unroll
+                            for (int k = 0; k < 3; ++k)
+                                if (k < nv) x[u][k] = s4[lane + 64 * k];
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if (sl + u < s1) {
+#pragma unroll
+                            for (int k = 0; k < 3; ++k) {
+                                if (k < nv) {
+                                    v[k].x += x[u][k].x; v[k].y += x[u][k].y;
+                                    v[k].z += x[u][k].z; v[k].w += x[u][k].w;
+                                }
+                            }
+                        }
+                    }
                 }
             } else {
                 const int q = rr - p.S, n = q / kBlock, j = q % kBlock;
