@@ -67,10 +67,10 @@ KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.h
 # plain 256 MiB device copy), with the digest of the kernel's sources when the
 # counters were taken.  A kernel whose sources changed since reports null.
 PMC_TRAFFIC = {
-    "absorb": (358_772_745, "a6d94fd2f33133fb"),
-    "attention": (583_875_242, "00bb1efce6168c8c"),
-    "w_uv": (394_492_808, "cef85dda6f65640e"),
-    "index+fill": (42_090_290, "2d8e19e1157fcb65"),
+    "absorb": (358_784_611, "a6d94fd2f33133fb"),
+    "attention": (583_876_928, "00bb1efce6168c8c"),
+    "w_uv": (394_524_874, "f8e0b065f1c9d199"),
+    "index+fill": (42_090_014, "2d8e19e1157fcb65"),
 }
 PMC_SOURCE = "rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, profiles/attn_fwd_headline_S32768_N1024_counters.md"
 
@@ -81,17 +81,17 @@ BWD_KERNEL_SOURCES = {
     "attention_bwd": ("bwd_attn.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
     "dw": ("bwd_gemm.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
     "dkv": ("bwd_gemm.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
-    "dq_nope": ("bwd_gemm.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
+    "dq_nope": ("uv.hip", "common.hpp", "kernels.hpp"),
     "d_olat": ("absorb.hip", "common.hpp", "kernels.hpp"),
     "final": ("bwd_misc.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
 }
 BWD_PMC_TRAFFIC = {
-    "attention_bwd": (1_294_418_918, "f8f1aae7fba2a88c"),
-    "dw": (753_790_011, "077c93ab989cf579"),
-    "dkv": (971_111_482, "077c93ab989cf579"),
-    "dq_nope": (447_395_984, "077c93ab989cf579"),
-    "d_olat": (394_457_734, "a6d94fd2f33133fb"),
-    "final": (311_162_276, "65f54a7ba8f69927"),
+    "attention_bwd": (1_294_725_171, "b878411a2205c49e"),
+    "dw": (1_001_381_723, "a501511a9518c0db"),
+    "dkv": (1_005_547_070, "a501511a9518c0db"),
+    "dq_nope": (358_915_292, "f8e0b065f1c9d199"),
+    "d_olat": (394_473_716, "a6d94fd2f33133fb"),
+    "final": (311_311_261, "87eccf3c74993e7c"),
 }
 
 
