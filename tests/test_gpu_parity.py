@@ -155,6 +155,30 @@ def test_cfg4_recipe_four_wave_launch(sd):
     check_full(wk.scaled(4, S=4096, N=600), form="gathered")
 
 
+def test_four_wave_launch_with_shuffled_kept_anchors(sd):
+    """Enough kept blocks for the four-wave launch (one workgroup per block,
+    all 64 heads), with the kept anchors in random order: neighbouring slots'
+    windows overlap partly, fully or not at all, in either direction."""
+    wl = wk.scaled(4, S=4096, N=600)
+    perm = np.random.default_rng(45).permutation(wl.N)
+    wl.anchors[0] = wl.anchors[0][perm]
+    wl.keep[0] = wl.keep[0][perm]
+    kept = wl.anchors[0][wl.keep[0] == 1]
+    assert len(kept) >= 400 and np.any(np.diff(kept) < 0)
+    log("four-wave launch: B1 S4096 N600, kept anchors shuffled")
+    check_full(wl, form="gathered", guard=1024)
+
+
+def test_four_wave_launch_dense_windows_three_samples(sd):
+    """The four-wave launch on three samples with anchors a few positions
+    apart (windows almost equal) and clamped windows at each sample's start."""
+    wl = wk.make_workload("ring-B3", B=3, S=900, N=320, dims=wk.GLM_DIMS, dtype="bf16",
+                          recipe="headline", seed=83, recipe_args=dict(pad_frac=0.2, low_frac=0.2))
+    assert int(wl.keep.sum()) >= 600
+    log("four-wave launch: B3 S900 N320, dense anchors")
+    check_full(wl, form="gathered", guard=1024)
+
+
 @pytest.mark.parametrize("chunk", [1, 7, 64, 159, 160, 100000])
 def test_chunk_sizes(sd, chunk):
     """Kept blocks processed in rounds of `chunk` (ragged last round, rounds
