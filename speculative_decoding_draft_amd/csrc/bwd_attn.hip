@@ -57,8 +57,13 @@ __global__ __launch_bounds__(kThreads) void bwd_attn_kernel(
     __shared__ double turns[kDr / 2];        // theta_i / 2pi
 
     const int n_here = status[kStKeptCount];
-    const int slot = xcd_balance(blockIdx.x, n_here);
-    if (slot < 0) return;
+    // slots are taken in descending order: the d_olat rows the absorb
+    // kernel wrote last (still in the Infinity Cache) are read first, and
+    // the dc^KV kernel, which walks the slots upwards, then first reads the
+    // P / dS' rows written last
+    const int lid = xcd_balance(blockIdx.x, n_here);
+    if (lid < 0) return;
+    const int slot = n_here - 1 - lid;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
