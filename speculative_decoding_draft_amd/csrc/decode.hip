@@ -211,7 +211,19 @@ __global__ __launch_bounds__(kVThreads) void verify_stats_kernel(
     __shared__ float red_m[kVThreads / 64];
     __shared__ int red_i[kVThreads / 64];
     __shared__ float red_s[kVThreads / 64];
-    const int r = blockIdx.x / C, c = blockIdx.x % C;
+    // Rows in the order the overlap pass wants them still cached: every
+    // sequence's last target row first (the overlap pass does not read it),
+    // then per sequence its K drafted rows and K target rows.  The overlap
+    // pass walks the sequences downwards, so it first reads the rows read
+    // here last, which the Infinity Cache still holds.
+    const int nb = blockIdx.x / C, c = blockIdx.x % C;
+    int r;
+    if (nb < B) {
+        r = B * K + nb * (K + 1) + K;
+    } else {
+        const int bb = (nb - B) / (2 * K), j = (nb - B) % (2 * K);
+        r = j < K ? bb * K + j : B * K + bb * (K + 1) + (j - K);
+    }
     const float* x = row_ptr(r, B, K, V, dl, tl);
     const int v0 = c * kVChunk, v1 = min(V, v0 + kVChunk);
     const int w = threadIdx.x >> 6;
@@ -270,7 +282,8 @@ __global__ __launch_bounds__(kVThreads) void verify_overlap_kernel(
     const float* __restrict__ tl, const float4* __restrict__ part, float2* __restrict__ ov) {
     __shared__ float2 lse_s;
     __shared__ float2 red[kVThreads / 64];
-    const int r = blockIdx.x / C, c = blockIdx.x % C;      // r = b*K + k
+    // drafted rows from the last down (see verify_stats_kernel)
+    const int r = B * K - 1 - (int)blockIdx.x / C, c = blockIdx.x % C;   // r = b*K + k
     const int b = r / K, k = r % K;
     const int rt = B * K + b * (K + 1) + k;                // the target row
     if (threadIdx.x < 64) {
