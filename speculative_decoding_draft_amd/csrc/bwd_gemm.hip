@@ -277,10 +277,13 @@ __global__ __launch_bounds__(256) void dw_kernel(const bf16* __restrict__ olat,
 }
 
 // ---- weight gradients with LDS DMA: the same reduction in 256-position x
-// (128 or 96)-output tiles, 8 per head (dW_UV 2 x 2, dW_UK 2 x 2), two
-// workgroups per compute unit.  The 2 x 2 waves each own a 128 x 64 (or
-// 128 x 48) quarter, which halves the LDS bytes read per MFMA against
-// 64 x 32 quarters; LDS bandwidth, not HBM, bounded the smaller tiles.
+// (256 or 192)-output tiles (every output column of the head), 4 per head
+// (dW_UV and dW_UK, two position halves each), one 8-wave workgroup per
+// compute unit.  Each head's o_lat / dq_abs columns are read by one
+// workgroup only; the narrower input rows (dout, q^C) by two.  The 2 x 4
+// waves each own a 128 x 64 (or 128 x 48) part, which halves the LDS bytes
+// read per MFMA against 64 x 32 parts; LDS bandwidth, not HBM, bounded the
+// smaller tiles.
 // Operands reach LDS by buffer DMA (no register staging, no LDS store
 // instructions) in a ring of three 32-row stages, two stages in flight while
 // the third is consumed.  Each stage row holds its 16-byte chunks XOR-
@@ -290,12 +293,13 @@ __global__ __launch_bounds__(256) void dw_kernel(const bf16* __restrict__ olat,
 // gathered operand through an offset past it.
 constexpr int kDwBM = 256;                          // latent positions per tile
 constexpr int kDwArow = kDwBM;                      // A stage row (elements, 512 B)
-constexpr int kDwBrow = 128;                        // B stage row (elements, 256 B)
+constexpr int kDwBrow = 256;                        // B stage row (elements, 512 B)
 constexpr int kDwStage = 32 * (kDwArow + kDwBrow);  // elements per stage
 constexpr int kDwStages = 3;
 constexpr int kDwSlots = 1024;                      // slots per LDS row table
-constexpr int kDwCopies = 6;                        // DMA instructions per wave per stage
-constexpr int kDwPerHead = (kD / kDwBM) * 2 * 2;    // 4 dW_UV + 4 dW_UK tiles
+constexpr int kDwWaves = 8;
+constexpr int kDwCopies = 4;                        // DMA instructions per wave per stage
+constexpr int kDwPerHead = (kD / kDwBM) * 2;        // 2 dW_UV + 2 dW_UK tiles
 constexpr uint32_t kPastEnd = 0x80000000u;          // an offset beyond every bound used
 
 __device__ inline int dw_swz(int row) { return (2 * row) & 15; }
@@ -308,7 +312,7 @@ __device__ inline void dw_dma_tile(const bf16* __restrict__ lat, const bf16* __r
     constexpr int MT = 8;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int g = lane >> 4, l16 = lane & 15;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     f32x4 acc[MT][NT];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -346,16 +350,16 @@ __device__ inline void dw_dma_tile(const bf16* __restrict__ lat, const bf16* __r
                                       (uint32_t)krows * kLatRow);
 
         // stage s (rows 32 s .. 32 s + 31 of this chunk) into ring slot s % 3:
-        // A as 16 copies of two 512-byte rows, B as 8 copies of four 256-byte
-        // rows; wave w issues A copies 4w .. 4w + 3 and B copies 2w, 2w + 1
+        // A and B each as 16 copies of two 512-byte rows; wave w issues copies
+        // 2w and 2w + 1 of each
         auto issue = [&](int s) {
             char* st = reinterpret_cast<char*>(lds + (s % kDwStages) * kDwStage);
             uint32_t boff[2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                const int row = 4 * (2 * wave + q) + (lane >> 4);
+                const int row = 2 * (2 * wave + q) + (lane >> 5);
                 const int k = 32 * s + row;
-                const int lc = (lane & 15) ^ dw_swz(row);
+                const int lc = (lane & 31) ^ dw_swz(row);
                 boff[q] = kPastEnd;
                 if (k < krows) {
                     const int sl = k / kBlock;
@@ -363,8 +367,8 @@ __device__ inline void dw_dma_tile(const bf16* __restrict__ lat, const bf16* __r
                 }
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int r2 = 2 * (4 * wave + q);
+            for (int q = 0; q < 2; ++q) {
+                const int r2 = 2 * (2 * wave + q);
                 const int row = r2 + (lane >> 5);
                 const int lc = (lane & 31) ^ dw_swz(row);
                 copy_16_untracked(rs_a, (uint32_t)(32 * s + row) * kLatRow + 16 * lc,
@@ -373,7 +377,7 @@ __device__ inline void dw_dma_tile(const bf16* __restrict__ lat, const bf16* __r
 #pragma unroll
             for (int q = 0; q < 2; ++q)
                 copy_16_untracked(rs_b, boff[q],
-                                  st + 32 * kDwArow * 2 + 4 * (2 * wave + q) * (kDwBrow * 2));
+                                  st + 32 * kDwArow * 2 + 2 * (2 * wave + q) * (kDwBrow * 2));
         };
 
         issue(0);
@@ -411,24 +415,24 @@ __device__ inline void dw_dma_tile(const bf16* __restrict__ lat, const bf16* __r
     }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void dw_dma_kernel(
+__global__ __launch_bounds__(kDwWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dw_dma_kernel(
     const bf16* __restrict__ olat, const bf16* __restrict__ dout, const bf16* __restrict__ dqabs,
     const bf16* __restrict__ q_nope, const int4* __restrict__ srec,
     const int32_t* __restrict__ status, bf16* __restrict__ dw_uv, bf16* __restrict__ dw_uk, int N,
     int L5, int in_rows) {
-    static_assert(kD % kDwBM == 0 && kDv == 2 * 128 && kDc == 2 * 96, "tile split");
+    static_assert(kD % kDwBM == 0 && kDv == 4 * 64 && kDc == 4 * 48 && kDv <= kDwBrow, "tile split");
     __shared__ __attribute__((aligned(16))) bf16 lds[kDwStages * kDwStage];
     __shared__ int rbase[kDwSlots];
     const int n_slots = status[kStKeptCount];
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int h = lid / kDwPerHead, t = lid % kDwPerHead;
-    const int m0 = ((t & 3) >> 1) * kDwBM;
-    if (t < 4)
-        dw_dma_tile<4, kDv>(olat, dout, srec, n_slots, h, m0, (t & 1) * 128, N, L5, in_rows,
-                            dw_uv, lds, rbase);
+    const int m0 = (t & 1) * kDwBM;
+    if (t < 2)
+        dw_dma_tile<4, kDv>(olat, dout, srec, n_slots, h, m0, 0, N, L5, in_rows, dw_uv, lds,
+                            rbase);
     else
-        dw_dma_tile<3, kDc>(dqabs, q_nope, srec, n_slots, h, m0, (t & 1) * 96, N, L5, in_rows,
-                            dw_uk, lds, rbase);
+        dw_dma_tile<3, kDc>(dqabs, q_nope, srec, n_slots, h, m0, 0, N, L5, in_rows, dw_uk, lds,
+                            rbase);
 }
 
 // ---- per block: dc_k (M = D, permuted positions) and d(R k^R)_k (M = d_r,
@@ -624,7 +628,8 @@ hipError_t launch_bwd_dw(const Problem& p, const Inputs& in, const BwdGrads& g,
     const size_t in_rows = (size_t)p.B * p.L5;
     if (in_rows * kH * kDv * 2 < kPastEnd && in_rows * kH * kDc * 2 < kPastEnd &&
         (size_t)kBlock * kDwSlots * kH * kD * 2 < kPastEnd) {
-        hipLaunchKernelGGL(dw_dma_kernel, dim3(kH * kDwPerHead), dim3(256), 0, s, w.fwd.olat,
+        hipLaunchKernelGGL(dw_dma_kernel, dim3(kH * kDwPerHead), dim3(kDwWaves * 64), 0, s,
+                           w.fwd.olat,
                            (const bf16*)g.dout, w.dqabs, (const bf16*)in.q_nope, w.fwd.srec,
                            w.fwd.status, (bf16*)g.dw_uv, (bf16*)g.dw_uk, p.N, p.L5, (int)in_rows);
         return hipGetLastError();
