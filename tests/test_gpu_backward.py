@@ -150,6 +150,21 @@ def test_bwd_mfma_matches_generic_path():
     check(fast, gen, GPU_PATHS_TOL, "mfma vs generic")
 
 
+def test_bwd_more_kept_blocks_than_one_row_table():
+    """More than 1024 kept blocks: the weight-gradient kernel walks the rows
+    in several LDS row tables.  The fp64 oracle would need about a minute
+    for every block, so the MFMA path is held to the generic path here (that
+    path is held to the oracle at the sizes it can reach)."""
+    wl = wk.scaled(4, S=16384, N=1500)
+    ga, gk, _, _ = anchors_for(wl)
+    assert int(gk.sum()) > 1024
+    dout = wk.make_dout(wl, seed=14)
+    log(f"case {wl.name}: {int(gk.sum())} kept blocks, MFMA against generic")
+    fast = GpuBwd(wl, dout, ga, gk).run().result()
+    gen = GpuBwd(wl, dout, ga, gk, force_generic=True).run().result()
+    check(fast, gen, GPU_PATHS_TOL, "mfma vs generic, several row tables")
+
+
 def test_bwd_repeat_runs_agree():
     """A second call on the same workspace gives the same gradients (the
     accumulators are cleared by every call; atomics may reorder fp32 sums)."""
