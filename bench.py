@@ -67,10 +67,10 @@ KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.h
 # plain 256 MiB device copy), with the digest of the kernel's sources when the
 # counters were taken.  A kernel whose sources changed since reports null.
 PMC_TRAFFIC = {
-    "absorb": (358_784_611, "a6d94fd2f33133fb"),
-    "attention": (583_876_928, "00bb1efce6168c8c"),
-    "w_uv": (394_524_874, "f8e0b065f1c9d199"),
-    "index+fill": (42_090_014, "2d8e19e1157fcb65"),
+    "absorb": (358_784_681, "a6d94fd2f33133fb"),
+    "attention": (584_034_509, "00bb1efce6168c8c"),
+    "w_uv": (394_524_861, "f8e0b065f1c9d199"),
+    "index+fill": (42_090_253, "2d8e19e1157fcb65"),
 }
 PMC_SOURCE = "rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, profiles/attn_fwd_headline_S32768_N1024_counters.md"
 
@@ -86,12 +86,12 @@ BWD_KERNEL_SOURCES = {
     "final": ("bwd_misc.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
 }
 BWD_PMC_TRAFFIC = {
-    "attention_bwd": (1_294_725_171, "b878411a2205c49e"),
-    "dw": (1_001_381_723, "a501511a9518c0db"),
-    "dkv": (1_005_547_070, "a501511a9518c0db"),
-    "dq_nope": (358_915_292, "f8e0b065f1c9d199"),
-    "d_olat": (394_473_716, "a6d94fd2f33133fb"),
-    "final": (311_311_261, "87eccf3c74993e7c"),
+    "attention_bwd": (1_294_714_265, "c1db77fb0dbe5e86"),
+    "dw": (757_865_861, "80f2076d7c997560"),
+    "dkv": (1_001_790_286, "80f2076d7c997560"),
+    "dq_nope": (358_915_331, "f8e0b065f1c9d199"),
+    "d_olat": (394_473_728, "a6d94fd2f33133fb"),
+    "final": (311_311_264, "87eccf3c74993e7c"),
 }
 
 
@@ -101,8 +101,8 @@ BWD_PMC_TRAFFIC = {
 # scaling, with the files each is built from and their digest when taken.
 SIDE_PMC_TRAFFIC = {
     "loss_stats": (3_882_859_895, ("loss.hip", "blas.hpp", "kernels.hpp"), "a94b7e3af57b3f81"),
-    "verify": (436_597_519 + 398_369_304 + 4_484_620, ("decode.hip", "kernels.hpp"),
-               "25552c1280c23bfe"),
+    "verify": (436_648_344 + 398_429_336 + 4_485_120, ("decode.hip", "kernels.hpp"),
+               "995d2c8ebfedfcb3"),
 }
 
 
