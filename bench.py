@@ -293,18 +293,19 @@ def bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sp
     fout = torch.empty((B, L5, H, wl.d_v), dtype=torch.bfloat16, device="cuda")
     fargs = args[:11] + (fout, ws)
     for _ in range(3):
-        sd.attn_fwd(*fargs, stream=sptr)
-        sd.attn_bwd(*args, stream=sptr, reuse_forward=True)
+        sd.attn_fwd(*fargs, stream=sptr, for_backward=True)
+        sd.attn_bwd(*args, stream=sptr, reuse_forward=2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        sd.attn_fwd(*fargs, stream=sptr)
-        sd.attn_bwd(*args, stream=sptr, reuse_forward=True)
+        sd.attn_fwd(*fargs, stream=sptr, for_backward=True)
+        sd.attn_bwd(*args, stream=sptr, reuse_forward=2)
     torch.cuda.synchronize()
     step = (time.perf_counter() - t0) / steps
     fflop = useful_flop(anchors, keep, wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v)
     out["train_step"] = {"what": "dspark_attn_fwd then dspark_attn_bwd on one workspace "
-                                 "(reuse_forward: no index rebuild, no q_abs / o_lat recompute)",
+                                 "(the forward leaves its softmax probabilities; reuse_forward 2: "
+                                 "no index rebuild, no q_abs / o_lat / score recompute)",
                          "ms_per_step": round(step * 1e3, 4),
                          "useful_gflop_per_step": round((flop + fflop) / 1e9, 3),
                          "value": round((flop + fflop) / step / 1e12, 3), "unit": "TFLOP/s"}
@@ -313,14 +314,14 @@ def bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sp
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            sd.attn_fwd(*fargs)
-            sd.attn_bwd(*args, reuse_forward=True)
+            sd.attn_fwd(*fargs, for_backward=True)
+            sd.attn_bwd(*args, reuse_forward=2)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            sd.attn_fwd(*fargs)
-            sd.attn_bwd(*args, reuse_forward=True)
+            sd.attn_fwd(*fargs, for_backward=True)
+            sd.attn_bwd(*args, reuse_forward=2)
         for _ in range(3):
             graph.replay()
         torch.cuda.synchronize()

@@ -180,19 +180,31 @@ typedef struct dspark_attn_opts {
      * during the call.  aux_stream must not be `stream`. */
     void* aux_stream;
     void* aux_events[2];
-    /* dspark_attn_bwd_ex only, nonzero: the workspace was last used by
+    /* dspark_attn_bwd_ex, 1 or 2: the workspace was last used by
      * dspark_attn_fwd(_ex) with the same descriptor, inputs, anchors and keep
      * and the same force_generic, and nothing else has written it since (a
      * training step runs the forward on the backward's workspace: its
      * layout begins with the forward's).  The backward then reuses the
      * forward's block index, q_abs and o_lat instead of rebuilding them
-     * (dW_UV then uses the forward's o_lat rows).  This is checked on the
-     * device: the index build of a forward (or of a backward without this
-     * option) tags the workspace with its descriptor and path, and a
-     * backward whose workspace does not carry the tag of this descriptor on
-     * the path it takes (MFMA or generic; the one-launch forward leaves no
+     * (dW_UV then uses the forward's o_lat rows).  2 on the MFMA path: the
+     * forward also left its softmax probabilities (it ran with this option
+     * set, below), and the backward reads them instead of recomputing the
+     * scores; the gradients are the same bits as with 1.  This is checked on
+     * the device: the index build of a forward (or of a backward without
+     * this option) tags the workspace with its descriptor, its path and
+     * whether it left the probabilities, and a backward whose workspace does
+     * not carry a tag it accepts (1: this descriptor on the path it takes,
+     * MFMA or generic, with or without probabilities; 2: this descriptor on
+     * the MFMA path with probabilities; the one-launch forward leaves no
      * latents and never matches) writes NaN to every gradient and
-     * dspark_read_device_status then returns DSPARK_EINVAL. */
+     * dspark_read_device_status then returns DSPARK_EINVAL.
+     * dspark_attn_fwd_ex, nonzero: the workspace is a backward's for this
+     * descriptor (dspark_attn_workspace_size_ex with this option gives its
+     * size on the MFMA path; a smaller one is refused with
+     * DSPARK_EWORKSPACE), and the MFMA forward also writes its softmax
+     * probabilities there (bf16) for a backward with reuse_forward 2.
+     * Refused (DSPARK_EINVAL) with the one-launch forward; ignored on the
+     * generic path. */
     int32_t reuse_forward;
     /* dspark_attn_fwd_ex on the MFMA shapes, nonzero: the one-launch
      * forward instead of the three kernels (ignored with chunk_blocks or
@@ -216,7 +228,8 @@ typedef struct dspark_attn_opts {
 /* Bytes of workspace dspark_attn_fwd_ex needs for (desc, opts) on a device
  * with 256 compute units (opts may be NULL; 0 on an invalid descriptor):
  * the size of the path those options select, which is smaller than
- * dspark_attn_workspace_size for the one-launch forward.  On a device where
+ * dspark_attn_workspace_size for the one-launch forward, and a backward's
+ * (MFMA path) with reuse_forward set.  On a device where
  * the one-launch forward cannot run, the call falls back to the three-kernel
  * forward and needs dspark_attn_workspace_size(desc) bytes (a smaller
  * workspace is then refused with DSPARK_EWORKSPACE). */

@@ -223,9 +223,10 @@ def workspace_size(desc: Desc) -> int:
 
 
 def workspace_size_ex(desc: Desc, force_generic: bool = False, chunk_blocks: int = 0,
-                      one_launch: bool = False) -> int:
+                      one_launch: bool = False, for_backward: bool = False) -> int:
     """dspark_attn_workspace_size_ex: bytes for the path these options select."""
     opts, _ = _opts(None, force_generic, chunk_blocks, one_launch=one_launch)
+    opts.reuse_forward = 1 if for_backward else 0
     n = int(lib.dspark_attn_workspace_size_ex(ctypes.byref(desc), ctypes.byref(opts)))
     if n == 0:
         raise DSparkError(DSPARK_EINVAL, last_error())
@@ -279,22 +280,25 @@ def attn_fwd(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk,
              stage_events: Optional[Sequence[int]] = None, force_generic: bool = False,
              chunk_blocks: int = 0, aux_stream=None,
              aux_events: Optional[Sequence[int]] = None,
-             one_launch: bool = False) -> None:
+             one_launch: bool = False, for_backward: bool = False) -> None:
     """dspark_attn_fwd / dspark_attn_fwd_ex; raises DSparkError on a non-OK
     status.  aux_stream / aux_events (two hipEvent_t handles) run odd rounds
-    on a second stream; one_launch selects the one-launch forward (see
-    dspark_attn_opts)."""
+    on a second stream; one_launch selects the one-launch forward;
+    for_backward (opts.reuse_forward on a forward): workspace is a
+    backward's, and the forward also leaves its softmax probabilities there
+    for a backward with reuse_forward=2 (see dspark_attn_opts)."""
     args = [ctypes.byref(desc)] + [_ptr(t) for t in (q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk,
                                                      kr_blk, w_uk, w_uv, anchors, keep, out,
                                                      workspace)]
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args += [ws_bytes, _stream(stream)]
     if (stage_events is None and not force_generic and not chunk_blocks and aux_stream is None
-            and not one_launch):
+            and not one_launch and not for_backward):
         _check(lib.dspark_attn_fwd(*args))
         return
     opts, _arr = _opts(stage_events, force_generic, chunk_blocks, aux_stream, aux_events,
                        one_launch)
+    opts.reuse_forward = 1 if for_backward else 0
     _check(lib.dspark_attn_fwd_ex(*args, ctypes.byref(opts)))
 
 
@@ -378,11 +382,12 @@ BWD_GRADS = ("dq_nope", "dq_rope", "dckv_ctx", "dkr_ctx", "dckv_blk", "dkr_blk",
 def attn_bwd(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk, w_uv,
              anchors, keep, dout, grads, workspace, stream=None,
              stage_events: Optional[Sequence[int]] = None, force_generic: bool = False,
-             reuse_forward: bool = False) -> None:
+             reuse_forward: int = 0) -> None:
     """dspark_attn_bwd / dspark_attn_bwd_ex.  grads: a mapping with the
     output tensors named as in BWD_GRADS; raises DSparkError on a non-OK
-    status.  reuse_forward: the workspace holds the forward's index and q_abs
-    (see dspark_attn_opts)."""
+    status.  reuse_forward: 0, 1 / True (the workspace holds the forward's
+    index and q_abs) or 2 (and its softmax probabilities: a forward with
+    for_backward); see dspark_attn_opts."""
     args = [ctypes.byref(desc)] + [_ptr(t) for t in (q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk,
                                                      kr_blk, w_uk, w_uv, anchors, keep, dout)]
     args += [_ptr(grads[k]) for k in BWD_GRADS]
@@ -392,7 +397,7 @@ def attn_bwd(desc: Desc, q_nope, q_rope, ckv_ctx, kr_ctx, ckv_blk, kr_blk, w_uk,
         _check(lib.dspark_attn_bwd(*args))
         return
     opts, _arr = _opts(stage_events, force_generic, 0)
-    opts.reuse_forward = 1 if reuse_forward else 0
+    opts.reuse_forward = int(reuse_forward)
     _check(lib.dspark_attn_bwd_ex(*args, ctypes.byref(opts)))
 
 

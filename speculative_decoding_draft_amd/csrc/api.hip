@@ -189,9 +189,10 @@ FwdPath pick_path(const dspark_attn_desc& d, const dspark_attn_opts* o, bool che
 }
 
 // status[kStPathTag] written by a forward on the given path: a hash of the
-// descriptor with the path in its low two bits (never 0).  A backward with
-// reuse_forward expects the tag of the path it takes.
-int32_t forward_tag(const dspark_attn_desc& d, FwdPath path) {
+// descriptor with the path in its low three bits (never 0); with_p: the
+// forward also left its softmax probabilities for the backward.  A backward
+// with reuse_forward expects the tag of the path it takes.
+int32_t forward_tag(const dspark_attn_desc& d, FwdPath path, bool with_p = false) {
     uint32_t h = 2166136261u;
     auto mix = [&](const void* v, size_t n) {
         const unsigned char* c = static_cast<const unsigned char*>(v);
@@ -202,8 +203,10 @@ int32_t forward_tag(const dspark_attn_desc& d, FwdPath path) {
     mix(f, sizeof(f));
     mix(&d.rope_base, sizeof(d.rope_base));
     mix(&d.softmax_scale, sizeof(d.softmax_scale));
-    const uint32_t code = path == FwdPath::kMaterialised ? 1u : path == FwdPath::kGeneric ? 2u : 3u;
-    return (int32_t)((h & ~3u) | code);
+    const uint32_t code = path == FwdPath::kMaterialised ? (with_p ? 4u : 1u)
+                          : path == FwdPath::kGeneric    ? 2u
+                                                         : 3u;
+    return (int32_t)((h & ~7u) | code);
 }
 
 WsLayout path_layout(const dspark_attn_desc& d, FwdPath path) {
@@ -321,6 +324,14 @@ dspark_status forward_impl(const dspark_attn_desc* desc, const void* q_nope, con
     }
     const FwdPath path = pick_path(d, opts, true);
     const bool fast = path != FwdPath::kGeneric;
+    // reuse_forward on a forward: the workspace is a backward's, and the MFMA
+    // path also leaves its probabilities there for that backward
+    const bool for_bwd = !fixed && opts && opts->reuse_forward;
+    if (for_bwd && path == FwdPath::kFused)
+        return fail(DSPARK_EINVAL,
+                    "reuse_forward needs the three-kernel forward (the one-launch forward leaves "
+                    "no latents)");
+    const bool keep_p = for_bwd && path == FwdPath::kMaterialised;
     int round_blocks = 0;
     const WsLayout L = fixed ? fixed_layout(d, fast, &round_blocks) : path_layout(d, path);
     if (fixed) {
@@ -331,8 +342,11 @@ dspark_status forward_impl(const dspark_attn_desc* desc, const void* q_nope, con
         workspace = fixed->base;
         ws_bytes = kFixedScratchBytes;
     }
-    st = check_workspace(workspace, ws_bytes, L.total);
+    st = check_workspace(workspace, ws_bytes, keep_p ? bwd_layout(d, true).total : L.total);
     if (st != DSPARK_OK) return st;
+    bf16* pmat = keep_p
+                     ? reinterpret_cast<bf16*>(static_cast<char*>(workspace) + bwd_layout(d, true).pmat)
+                     : nullptr;
 
     const Problem p = make_problem(d);
     if (!fast) {
@@ -387,7 +401,8 @@ dspark_status forward_impl(const dspark_attn_desc* desc, const void* q_nope, con
     // generic path reads the table
     // the fixed scratch is never handed to a backward: no tag
     if ((e = launch_prep(p, anchors, keep, ws, nullptr, L.rope_rows, fast ? nullptr : &theta,
-                         fast ? out : nullptr, s, fixed ? 0 : forward_tag(d, path))) != hipSuccess)
+                         fast ? out : nullptr, s,
+                         fixed ? 0 : forward_tag(d, path, keep_p))) != hipSuccess)
         return hip_fail(e, "index / RoPE table / fill launch");
     if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if (fast) {
@@ -408,7 +423,7 @@ dspark_status forward_impl(const dspark_attn_desc* desc, const void* q_nope, con
             if ((e = launch_absorb(p, in, wr, ch, st)) != hipSuccess)
                 return hip_fail(e, "absorb launch");
             if ((e = mark_on(3 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-            if ((e = launch_attn(p, in, wr, ch, theta, st)) != hipSuccess)
+            if ((e = launch_attn(p, in, wr, ch, theta, st, pmat)) != hipSuccess)
                 return hip_fail(e, "attention launch");
             if ((e = mark_on(4 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
             if ((e = launch_uv(p, in, wr, ch, st)) != hipSuccess)
@@ -455,7 +470,11 @@ size_t dspark_attn_workspace_size_ex(const dspark_attn_desc* desc, const dspark_
     bool empty = false;
     if (check_desc(desc, &empty) != DSPARK_OK) return 0;
     g_last_error.clear();
-    return path_layout(*desc, pick_path(*desc, opts, false)).total;
+    const FwdPath path = pick_path(*desc, opts, false);
+    // reuse_forward: a backward's workspace (the MFMA path writes into it)
+    if (opts && opts->reuse_forward && path == FwdPath::kMaterialised)
+        return bwd_layout(*desc, true).total;
+    return path_layout(*desc, path).total;
 }
 
 dspark_status dspark_attn_fwd_ex(const dspark_attn_desc* desc, const void* q_nope,
@@ -630,10 +649,17 @@ dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc, const void* q_nop
     // here and NaN gradients at the end (dspark_read_device_status reports
     // it); the backward's own index build leaves the same tag, since its
     // launches also leave the index and the latents a forward would
+    // reuse_forward 2 on the MFMA path: the forward also left P (its tag
+    // says so) and the attention backward reads it instead of recomputing
+    // the scores; 1 accepts a forward with or without P
     const bool reuse = opts && opts->reuse_forward;
+    const bool load_p = reuse && fast && opts->reuse_forward == 2;
     const int32_t tag = forward_tag(d, fast ? FwdPath::kMaterialised : FwdPath::kGeneric);
+    const int32_t tag_p = forward_tag(d, FwdPath::kMaterialised, true);
     if (reuse) {
-        DSPARK_STEP(launch_bwd_reuse_check(p, w, tag, s), "reuse check launch");
+        DSPARK_STEP(launch_bwd_reuse_check(p, w, load_p ? tag_p : tag,
+                                           (fast && !load_p) ? tag_p : 0, s),
+                    "reuse check launch");
     } else {
         DSPARK_STEP(launch_prep(p, anchors, keep, w.fwd, nullptr, L.fwd.rope_rows,
                                 fast ? nullptr : &theta, nullptr, s, tag),
@@ -649,7 +675,8 @@ dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc, const void* q_nop
             DSPARK_STEP(launch_absorb(p, in, w.fwd, Chunk{0, d.B * d.N}, s), "absorb launch");
         }
         DSPARK_STEP(launch_absorb_dv(p, dout, w_uv, w.fwd, w.dolat, s), "W_UV^T dout launch");
-        DSPARK_STEP(launch_bwd_attn(p, in, g, w, theta, s, !reuse), "backward attention launch");
+        DSPARK_STEP(launch_bwd_attn(p, in, g, w, theta, s, !reuse, load_p),
+                    "backward attention launch");
         DSPARK_STEP(launch_bwd_dkv(p, w, s), "dc^KV launch");
         DSPARK_STEP(launch_uv_dqc(p, in.w_uk, w.dqabs, w.fwd, g.dq_nope, s), "dq^C launch");
         DSPARK_STEP(launch_bwd_dw(p, in, g, w, s), "weight-gradient launch");

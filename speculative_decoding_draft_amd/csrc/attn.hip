@@ -31,13 +31,16 @@ constexpr int kKrStride = kDr + 8;    // bf16 per staged k^R row (144 B)
 constexpr int kMaxKt = (kMaxKeys + 15) / 16;   // 9 key tiles
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int WAVES, int QW>
+// WRITE_P: also write the normalised probabilities, rounded to bf16, for a
+// backward that reuses them (pmat: [slot][5 H rows][144 key slots], row =
+// t H + h; keys past nkeys hold 0).
+template <int WAVES, int QW, bool WRITE_P>
 __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
     const bf16* __restrict__ q_rope, const bf16* __restrict__ ckv_ctx,
     const bf16* __restrict__ kr_ctx, const bf16* __restrict__ ckv_blk,
     const bf16* __restrict__ kr_blk, const int4* __restrict__ srec,
     const int32_t* __restrict__ status,
-    const bf16* __restrict__ q_abs, bf16* __restrict__ o_lat,
+    const bf16* __restrict__ q_abs, bf16* __restrict__ o_lat, bf16* __restrict__ pmat,
     int S, int N, int L5, int slot0, int nslots, float scale, uint32_t ctx_bytes,
     uint32_t blk_bytes, RopeTheta turns_per_pos) {
     __shared__ __attribute__((aligned(16))) bf16 ckv_l[kMaxKeys * kCkvStride];
@@ -129,8 +132,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
                 for (int q = 0; q < 4; ++q) {
                     const float2 cs = rope_cs(turns, xpos[u], ch * 4 + q);
                     const float x0 = (float)xr[u][2 * q], x1 = (float)xr[u][2 * q + 1];
-                    y[2 * q] = (bf16)(x0 * cs.x - x1 * cs.y);
-                    y[2 * q + 1] = (bf16)(x0 * cs.y + x1 * cs.x);
+                    const float2 y2 = rope_rot(x0, x1, cs);
+                    y[2 * q] = (bf16)y2.x;
+                    y[2 * q + 1] = (bf16)y2.y;
                 }
                 st16(&kr_l[s * kKrStride + ch * 8], y);
             }
@@ -227,8 +231,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
                 for (int q = 0; q < 4; ++q) {
                     const float2 cs = qcs[(tq0 + t) * (kDr / 2) + kr * 16 + g * 4 + q];
                     const float x0 = (float)bq[t][2 * q], x1 = (float)bq[t][2 * q + 1];
-                    bq[t][2 * q] = (bf16)(x0 * cs.x - x1 * cs.y);
-                    bq[t][2 * q + 1] = (bf16)(x0 * cs.y + x1 * cs.x);
+                    const float2 y2 = rope_rot(x0, x1, cs);
+                    bq[t][2 * q] = (bf16)y2.x;
+                    bq[t][2 * q + 1] = (bf16)y2.y;
                 }
             }
         }
@@ -294,6 +299,17 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
         sum += __shfl_xor(sum, 16);
         sum += __shfl_xor(sum, 32);
         inv[t] = __builtin_amdgcn_rcpf(sum);    // sum >= 1
+        if constexpr (WRITE_P) {
+            bf16* dst = pmat + (((size_t)kBlock * (slot0 + local) + tq0 + t) * kH + head) * kKeySlots +
+                        g * 4;
+#pragma unroll
+            for (int kt = 0; kt < kMaxKt; ++kt) {
+                bf16x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = (bf16)((float)pr[kt][t][i] * inv[t]);
+                gst8(dst + kt * 16, v);
+            }
+        }
     }
 
     // ---- o_lat^T = c^KV^T P^T in 64-dim chunks; lane holds dims
@@ -380,7 +396,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_kernel(
 }  // namespace
 
 hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
-                       const RopeTheta& th, hipStream_t s) {
+                       const RopeTheta& th, hipStream_t s, bf16* pmat) {
     // few blocks: four workgroups per block (16 heads each, one wave per
     // query) so that more compute units take part
     const uint32_t ctx_bytes = (uint32_t)((size_t)p.B * p.S * kD * sizeof(bf16));
@@ -391,19 +407,18 @@ hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, 
     const int groups = split ? 4 : 1;
     int grid = c.nslots * groups;
     grid = (grid + 7) / 8 * 8;
-    if (split) {
-        hipLaunchKernelGGL((attn_kernel<kBlock, 1>), dim3(grid), dim3(kBlock * 64), 0, s, (const bf16*)in.q_rope,
+    auto go = [&](auto kernel, int threads) {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, s, (const bf16*)in.q_rope,
                            (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
                            (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.srec,
-                           ws.status, ws.qabs, ws.olat, p.S, p.N, p.L5,
+                           ws.status, ws.qabs, ws.olat, pmat, p.S, p.N, p.L5,
                            c.slot0, c.nslots, p.scale, ctx_bytes, blk_bytes, turns);
-    } else {
-        hipLaunchKernelGGL((attn_kernel<4, kBlock>), dim3(grid), dim3(256), 0, s, (const bf16*)in.q_rope,
-                           (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
-                           (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, ws.srec,
-                           ws.status, ws.qabs, ws.olat, p.S, p.N, p.L5,
-                           c.slot0, c.nslots, p.scale, ctx_bytes, blk_bytes, turns);
-    }
+    };
+    if (split)
+        pmat ? go(attn_kernel<kBlock, 1, true>, kBlock * 64)
+             : go(attn_kernel<kBlock, 1, false>, kBlock * 64);
+    else
+        pmat ? go(attn_kernel<4, kBlock, true>, 256) : go(attn_kernel<4, kBlock, false>, 256);
     return hipGetLastError();
 }
 

@@ -32,7 +32,6 @@ struct BwdLayout {
     size_t total = 0;
 };
 
-constexpr int kKeySlots = 144;   // key slots of a block's P / dS rows (9 tiles of 16)
 
 inline BwdLayout bwd_layout(const dspark_attn_desc& d, bool mfma) {
     BwdLayout L;
@@ -93,12 +92,12 @@ constexpr int kStUnsorted = 2;
 // only_if: nullptr (always), or a status word -- the clear runs only when
 // that word is nonzero.
 hipError_t launch_bwd_zero(float* p, size_t n, const int32_t* only_if, hipStream_t s);
-// reuse_forward: unless status[kStPathTag] == expect, flags the call
-// (status[kStReuseBad] = 1) and turns the index into an all-padding one (no
-// kept block, every record padding) so that the launches after it read no
-// record of another forward.
+// reuse_forward: unless status[kStPathTag] is expect or (when nonzero)
+// expect2, flags the call (status[kStReuseBad] = 1) and turns the index into
+// an all-padding one (no kept block, every record padding) so that the
+// launches after it read no record of another forward.
 hipError_t launch_bwd_reuse_check(const Problem& p, const BwdWork& w, int32_t expect,
-                                  hipStream_t s);
+                                  int32_t expect2, hipStream_t s);
 // On a flagged call, every element of the eight gradients becomes NaN;
 // otherwise the launch exits at once.  elem: 2 (bf16) or 4 (fp32) bytes.
 hipError_t launch_bwd_reuse_fill(const Problem& p, const BwdGrads& g, const BwdWork& w,
@@ -134,8 +133,11 @@ hipError_t launch_absorb_dv(const Problem& p, const void* dout, const void* w_uv
 // 192 output dims (uv.hip).
 hipError_t launch_uv_dqc(const Problem& p, const void* w_uk, const bf16* dqabs,
                          const Workspace& ws, void* dq_nope, hipStream_t s);
+// write_olat: the backward has no forward before it (o_lat is recomputed);
+// load_p: the forward before it left P in pmat (scores are not recomputed).
 hipError_t launch_bwd_attn(const Problem& p, const Inputs& in, const BwdGrads& g,
-                           const BwdWork& w, const RopeTheta& th, hipStream_t s, bool write_olat);
+                           const BwdWork& w, const RopeTheta& th, hipStream_t s, bool write_olat,
+                           bool load_p);
 hipError_t launch_bwd_dkv(const Problem& p, const BwdWork& w, hipStream_t s);
 hipError_t launch_bwd_dw(const Problem& p, const Inputs& in, const BwdGrads& g,
                          const BwdWork& w, hipStream_t s);

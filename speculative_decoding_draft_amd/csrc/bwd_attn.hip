@@ -8,8 +8,9 @@
 // softmax(scale * Q K^T + Lambda(M)) V in the absorbed form (appendix
 // "Attention implementation", §4 "MLA Projection"), with e_k the
 // exponentials and l their sum (P_k = e_k / l):
-//   scores (as the forward) -> P, written out for the dc^KV products
-//   o_lat   = C^T P / l                          (for dW_UV)
+//   scores (as the forward) -> P = e / l, rounded to bf16 once (the P every
+//                             product below uses), written out for dc^KV
+//   o_lat   = C^T P                              (for dW_UV)
 //   dP_k    = d_olat . c_k                       (d_olat = W_UV^T dout, precomputed)
 //   D       = sum_k P_k dP_k
 //   dS'_k   = scale * P_k (dP_k - D)             written out for the dc^KV products
@@ -41,7 +42,10 @@ __device__ inline bf16x4 fresh(bf16x4 v) {
     return __builtin_bit_cast(bf16x4, u);
 }
 
-template <bool WRITE_OLAT>
+// WRITE_OLAT: also write o_lat (a backward without a forward before it).
+// LOAD_P: the forward on this workspace wrote P (normalised, bf16); skip the
+// scores and the softmax and read it.
+template <bool WRITE_OLAT, bool LOAD_P>
 __global__ __launch_bounds__(kThreads) void bwd_attn_kernel(
     const bf16* __restrict__ q_rope, const bf16* __restrict__ ckv_ctx,
     const bf16* __restrict__ kr_ctx, const bf16* __restrict__ ckv_blk,
@@ -78,10 +82,12 @@ __global__ __launch_bounds__(kThreads) void bwd_attn_kernel(
     const bf16* qa = q_abs + lat_row * kD + g * 8;
     const bf16* da = dolat + lat_row * kD + g * 8;
     bf16x8 qbuf[kPf][kBlock];
+    if constexpr (!LOAD_P) {
 #pragma unroll
-    for (int p = 0; p < kPf; ++p)
+        for (int p = 0; p < kPf; ++p)
 #pragma unroll
-        for (int t = 0; t < kBlock; ++t) qbuf[p][t] = gld16(qa + (size_t)t * kH * kD + p * 32);
+            for (int t = 0; t < kBlock; ++t) qbuf[p][t] = gld16(qa + (size_t)t * kH * kD + p * 32);
+    }
 
     const int4 rec = srec[slot];               // {ctx_lo, ctx_len, pos0, block}
     const int blk = rec.w;
@@ -136,8 +142,9 @@ __global__ __launch_bounds__(kThreads) void bwd_attn_kernel(
             for (int q = 0; q < 4; ++q) {
                 const float2 cs = rope_cs(turns, xpos[u], ch * 4 + q);
                 const float x0 = (float)xr[u][2 * q], x1 = (float)xr[u][2 * q + 1];
-                y[2 * q] = (bf16)(x0 * cs.x - x1 * cs.y);
-                y[2 * q + 1] = (bf16)(x0 * cs.y + x1 * cs.x);
+                const float2 y2 = rope_rot(x0, x1, cs);
+                y[2 * q] = (bf16)y2.x;
+                y[2 * q + 1] = (bf16)y2.y;
             }
             st16(&kr_l[s * kKrStride + ch * 8], y);
         }
@@ -170,92 +177,120 @@ __global__ __launch_bounds__(kThreads) void bwd_attn_kernel(
 #pragma unroll
         for (int t = 0; t < kBlock; ++t) st[kt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 acur[kMaxKt];
-#pragma unroll
-    for (int kt = 0; kt < kMaxKt; ++kt) acur[kt] = a_frag(0, kt);
     bf16* qro = qrot + lat_row * kDr + g * 8;
+    const size_t pm_row = (size_t)slot * kBlock * kH + head;
+    // P (normalised, bf16): query t, key slots 16 kt + 4g + i of this lane's head
+    bf16x4 pr[kMaxKt][kBlock];
+    if constexpr (LOAD_P) {
+        // the forward wrote P; the rotated q^R rows the k^R gradient products
+        // read are still to be written
 #pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
-        bf16x8 bq[kBlock];
-#pragma unroll
-        for (int t = 0; t < kBlock; ++t) bq[t] = qbuf[ks % kPf][t];
-        if (ks + kPf < kKs) {
-#pragma unroll
-            for (int t = 0; t < kBlock; ++t) qbuf[ks % kPf][t] = q_frag(ks + kPf, t);
-        }
-        if (ks >= kKl) {
-            const int kr = ks - kKl;
+        for (int kr = 0; kr < kDr / 32; ++kr) {
 #pragma unroll
             for (int t = 0; t < kBlock; ++t) {
+                bf16x8 x = gld16(qr + (size_t)t * kH * kDr + kr * 32);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const float2 cs = qcs[t * (kDr / 2) + kr * 16 + g * 4 + q];
-                    const float x0 = (float)bq[t][2 * q], x1 = (float)bq[t][2 * q + 1];
-                    bq[t][2 * q] = (bf16)(x0 * cs.x - x1 * cs.y);
-                    bq[t][2 * q + 1] = (bf16)(x0 * cs.y + x1 * cs.x);
+                    const float x0 = (float)x[2 * q], x1 = (float)x[2 * q + 1];
+                    const float2 y2 = rope_rot(x0, x1, cs);
+                    x[2 * q] = (bf16)y2.x;
+                    x[2 * q + 1] = (bf16)y2.y;
                 }
-                // the rotated q^R, for the k^R gradient products
-                gst16(qro + (size_t)t * kH * kDr + kr * 32, bq[t]);
+                gst16(qro + (size_t)t * kH * kDr + kr * 32, x);
             }
         }
-        bf16x8 anext[kMaxKt];
-        if (ks + 1 < kKs) {
-#pragma unroll
-            for (int kt = 0; kt < kMaxKt; ++kt) anext[kt] = a_frag(ks + 1, kt);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kt = 0; kt < kMaxKt; ++kt)
-#pragma unroll
-            for (int t = 0; t < kBlock; ++t) st[kt][t] = mfma_16x16x32(acur[kt], bq[t], st[kt][t]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (ks + 1 < kKs) {
-#pragma unroll
-            for (int kt = 0; kt < kMaxKt; ++kt) acur[kt] = anext[kt];
-        }
-    }
-    // ---- softmax: keys past nkeys are masked (exp2 of -inf is 0)
-#pragma unroll
-    for (int kt = 0; kt < kMaxKt; ++kt)
 #pragma unroll
         for (int t = 0; t < kBlock; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (kt * 16 + g * 4 + i >= nkeys) st[kt][t][i] = -INFINITY;
-    const float c2 = scale * kLog2e;
-    const size_t pm_row = (size_t)slot * kBlock * kH + head;
-    float inv[kBlock];
-    bf16x4 pr[kMaxKt][kBlock];
+            for (int kt = 0; kt < kMaxKt; ++kt)
+                pr[kt][t] = gld8(pmat + (pm_row + (size_t)t * kH) * kKeySlots + g * 4 + kt * 16);
+    } else {
 #pragma unroll
-    for (int t = 0; t < kBlock; ++t) {
-        float m = -INFINITY;
+        for (int kt = 0; kt < kMaxKt; ++kt) acur[kt] = a_frag(0, kt);
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) {
+            bf16x8 bq[kBlock];
+#pragma unroll
+            for (int t = 0; t < kBlock; ++t) bq[t] = qbuf[ks % kPf][t];
+            if (ks + kPf < kKs) {
+#pragma unroll
+                for (int t = 0; t < kBlock; ++t) qbuf[ks % kPf][t] = q_frag(ks + kPf, t);
+            }
+            if (ks >= kKl) {
+                const int kr = ks - kKl;
+#pragma unroll
+                for (int t = 0; t < kBlock; ++t) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float2 cs = qcs[t * (kDr / 2) + kr * 16 + g * 4 + q];
+                        const float x0 = (float)bq[t][2 * q], x1 = (float)bq[t][2 * q + 1];
+                        const float2 y2 = rope_rot(x0, x1, cs);
+                        bq[t][2 * q] = (bf16)y2.x;
+                        bq[t][2 * q + 1] = (bf16)y2.y;
+                    }
+                    // the rotated q^R, for the k^R gradient products
+                    gst16(qro + (size_t)t * kH * kDr + kr * 32, bq[t]);
+                }
+            }
+            bf16x8 anext[kMaxKt];
+            if (ks + 1 < kKs) {
+#pragma unroll
+                for (int kt = 0; kt < kMaxKt; ++kt) anext[kt] = a_frag(ks + 1, kt);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kt = 0; kt < kMaxKt; ++kt)
+#pragma unroll
+                for (int t = 0; t < kBlock; ++t) st[kt][t] = mfma_16x16x32(acur[kt], bq[t], st[kt][t]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < kKs) {
+#pragma unroll
+                for (int kt = 0; kt < kMaxKt; ++kt) acur[kt] = anext[kt];
+            }
+        }
+        // ---- softmax: keys past nkeys are masked (exp2 of -inf is 0)
 #pragma unroll
         for (int kt = 0; kt < kMaxKt; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) m = fmaxf(m, st[kt][t][i]);
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        const float mc = m * c2;
-        float sum = 0.f;
+            for (int t = 0; t < kBlock; ++t)
 #pragma unroll
-        for (int kt = 0; kt < kMaxKt; ++kt) {
+                for (int i = 0; i < 4; ++i)
+                    if (kt * 16 + g * 4 + i >= nkeys) st[kt][t][i] = -INFINITY;
+        const float c2 = scale * kLog2e;
+        float inv[kBlock];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(st[kt][t][i], c2, -mc));
-                pr[kt][t][i] = (bf16)p;
-                sum += p;
+        for (int t = 0; t < kBlock; ++t) {
+            float m = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < kMaxKt; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) m = fmaxf(m, st[kt][t][i]);
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            const float mc = m * c2;
+            float sum = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < kMaxKt; ++kt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(st[kt][t][i], c2, -mc));
+                    pr[kt][t][i] = (bf16)p;
+                    sum += p;
+                }
             }
-        }
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
-        inv[t] = __builtin_amdgcn_rcpf(sum);    // sum >= 1
-        // P = e / l per (row = t*H + head, key slot), for the dc^KV products
-        bf16* dst = pmat + (pm_row + (size_t)t * kH) * kKeySlots + g * 4;
+            sum += __shfl_xor(sum, 16);
+            sum += __shfl_xor(sum, 32);
+            inv[t] = __builtin_amdgcn_rcpf(sum);    // sum >= 1
+            // P = e / l per (row = t*H + head, key slot), rounded to bf16: kept in
+            // registers for every product below and written for the dc^KV ones
+            bf16* dst = pmat + (pm_row + (size_t)t * kH) * kKeySlots + g * 4;
 #pragma unroll
-        for (int kt = 0; kt < kMaxKt; ++kt) {
-            bf16x4 v;
+            for (int kt = 0; kt < kMaxKt; ++kt) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = (bf16)((float)pr[kt][t][i] * inv[t]);
-            gst8(dst + kt * 16, v);
+                for (int i = 0; i < 4; ++i) pr[kt][t][i] = (bf16)((float)pr[kt][t][i] * inv[t]);
+                gst8(dst + kt * 16, pr[kt][t]);
+            }
         }
     }
 
@@ -344,7 +379,8 @@ __global__ __launch_bounds__(kThreads) void bwd_attn_kernel(
     // o_lat feeds only dW_UV; without WRITE_OLAT the forward's rows, already
     // in the workspace, serve instead (a separate instantiation: a runtime
     // branch here costs registers)
-    if constexpr (WRITE_OLAT) ct_pass(pr, inv, o_lat);
+    const float one[kBlock] = {1.f, 1.f, 1.f, 1.f, 1.f};
+    if constexpr (WRITE_OLAT) ct_pass(pr, one, o_lat);
 
     // ---- dP (transposed, keys x rows) = C . d_olat over the 16 latent k-steps
 #pragma unroll
@@ -397,8 +433,8 @@ __global__ __launch_bounds__(kThreads) void bwd_attn_kernel(
         }
         dsum += __shfl_xor(dsum, 16);
         dsum += __shfl_xor(dsum, 32);
-        const float dd = dsum * inv[t];
-        const float f = scale * inv[t];
+        const float dd = dsum;
+        const float f = scale;
         bf16* dst = dsmat + (pm_row + (size_t)t * kH) * kKeySlots + g * 4;
 #pragma unroll
         for (int kt = 0; kt < kMaxKt; ++kt) {
@@ -410,7 +446,6 @@ __global__ __launch_bounds__(kThreads) void bwd_attn_kernel(
     }
 
     // ---- dq_abs = C^T dS'
-    const float one[kBlock] = {1.f, 1.f, 1.f, 1.f, 1.f};
     ct_pass(pr, one, dqabs);
 
     // ---- d(R q^R) = K_R^T dS' (64 dims), rotated back to dq^R
@@ -472,14 +507,19 @@ __global__ __launch_bounds__(kThreads) void bwd_attn_kernel(
 }  // namespace
 
 hipError_t launch_bwd_attn(const Problem& p, const Inputs& in, const BwdGrads& g,
-                           const BwdWork& w, const RopeTheta& th, hipStream_t s, bool write_olat) {
+                           const BwdWork& w, const RopeTheta& th, hipStream_t s, bool write_olat,
+                           bool load_p) {
     const uint32_t ctx_bytes = (uint32_t)((size_t)p.B * p.S * kD * sizeof(bf16));
     const uint32_t blk_bytes = (uint32_t)((size_t)p.B * p.L5 * kD * sizeof(bf16));
     RopeTheta turns{};
     for (int k = 0; k < kDr / 2; ++k) turns.t[k] = th.t[k] * 0.15915494309189533577;  // 1 / 2pi
     int grid = p.B * p.N;
     grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL(write_olat ? bwd_attn_kernel<true> : bwd_attn_kernel<false>, dim3(grid),
+    // a backward that writes o_lat has no forward's P to load
+    auto* kernel = write_olat ? bwd_attn_kernel<true, false>
+                   : load_p   ? bwd_attn_kernel<false, true>
+                              : bwd_attn_kernel<false, false>;
+    hipLaunchKernelGGL(kernel, dim3(grid),
                        dim3(kThreads), 0, s,
                        (const bf16*)in.q_rope, (const bf16*)in.ckv_ctx, (const bf16*)in.kr_ctx,
                        (const bf16*)in.ckv_blk, (const bf16*)in.kr_blk, w.fwd.srec, w.fwd.status,

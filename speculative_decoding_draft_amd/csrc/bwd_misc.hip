@@ -45,8 +45,9 @@ __global__ void zero_kernel(float4* __restrict__ p, size_t n4, const int32_t* on
 // workspace's last index build was for this descriptor and path.
 __global__ __launch_bounds__(256) void reuse_check_kernel(int32_t* __restrict__ status,
                                                           int4* __restrict__ idx, int total,
-                                                          int32_t expect) {
-    if (status[kStPathTag] == expect) {
+                                                          int32_t expect, int32_t expect2) {
+    const int32_t tag = status[kStPathTag];
+    if (tag == expect || (expect2 != 0 && tag == expect2)) {
         if (blockIdx.x == 0 && threadIdx.x == 0) status[kStReuseBad] = 0;
         return;
     }
@@ -505,11 +506,11 @@ __global__ __launch_bounds__(256) void gather_kernel(
 }  // namespace
 
 hipError_t launch_bwd_reuse_check(const Problem& p, const BwdWork& w, int32_t expect,
-                                  hipStream_t s) {
+                                  int32_t expect2, hipStream_t s) {
     const int total = p.B * p.N;
     const int grid = std::max(1, std::min(256, (total + 255) / 256));
     hipLaunchKernelGGL(reuse_check_kernel, dim3(grid), dim3(256), 0, s, w.fwd.status, w.fwd.idx,
-                       total, expect);
+                       total, expect, expect2);
     return hipGetLastError();
 }
 

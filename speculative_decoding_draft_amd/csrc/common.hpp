@@ -23,6 +23,7 @@ constexpr int kMaxRopePairs = 128; // d_rope <= 256
 constexpr int kH = 64, kD = 512, kDc = 192, kDr = 64, kDv = 256;
 constexpr int kMaxWindow = 128;    // W <= 128: at most 127 context + 5 block keys
 constexpr int kMaxKeys = kMaxWindow - 1 + kBlock;   // 132
+constexpr int kKeySlots = (kMaxKeys + 15) / 16 * 16;   // 144: a block's keys in 16-key tiles
 
 // Status area of the workspace (int32 words).  Word 2 belongs to the
 // backward (unsorted anchors); word 3 records a stalled fused pipeline.
@@ -232,6 +233,14 @@ __device__ inline float2 rope_cs(const double* turns, int pos, int i) {
     const double a = (double)pos * turns[i];
     const float f = (float)(a - __builtin_rint(a));
     return make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+}
+
+// One RoPE pair rotation, (x0, x1) by the angle whose (cos, sin) is cs, with
+// the multiply-adds spelled out, so that every kernel that rotates a key or
+// query row (the forward's and the backward's attention) rounds it the same
+// way whatever the compiler would otherwise contract.
+__device__ inline float2 rope_rot(float x0, float x1, float2 cs) {
+    return make_float2(__builtin_fmaf(x0, cs.x, -(x1 * cs.y)), __builtin_fmaf(x0, cs.y, x1 * cs.x));
 }
 
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16

@@ -57,8 +57,10 @@ struct Chunk {
 
 hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
                          hipStream_t s);
+// pmat: nullptr, or where the normalised probabilities go as well (bf16,
+// [slot][5 H][kKeySlots]) for a backward that reuses them.
 hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
-                       const RopeTheta& th, hipStream_t s);
+                       const RopeTheta& th, hipStream_t s, bf16* pmat = nullptr);
 hipError_t launch_uv(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
                      hipStream_t s);
 // The whole forward after the preparation launch as one persistent launch

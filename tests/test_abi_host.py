@@ -223,6 +223,12 @@ def test_bwd_workspace_holds_forward_area_and_accumulators():
     # the MFMA-path size also covers force_generic (weight accumulators)
     small = glm_desc(B=1, S=300, N=12)
     assert sd.bwd_workspace_size(small) >= (300 + 60) * (512 + 64) * 4 + wacc
+    # a forward that leaves its probabilities for the backward needs the
+    # backward's workspace on the MFMA path; the generic path leaves none
+    assert fwd < sd.workspace_size_ex(d, for_backward=True) <= bwd
+    assert sd.workspace_size_ex(d, for_backward=True) >= fwd + 2 * lat + 2 * pm
+    assert (sd.workspace_size_ex(d, force_generic=True, for_backward=True)
+            == sd.workspace_size_ex(d, force_generic=True))
 
 
 def test_bwd_null_misaligned_and_workspace_errors_before_any_launch():

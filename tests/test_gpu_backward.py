@@ -296,6 +296,58 @@ def test_bwd_reusing_the_forward_workspace_is_bit_identical(generic):
             assert float((x - y).norm() / y.norm()) < 5e-3, n
         else:
             assert torch.equal(plain[n], reuse[n]), n
+    # the forward also leaving its probabilities, the backward reading them
+    # (reuse_forward 2) instead of recomputing the scores: the same P, so the
+    # same bits as reuse_forward 1 (the generic path has no P to leave and
+    # takes the same launches as with 1)
+    ws.fill_(0x7f)
+    sd.attn_fwd(desc, *ins, out, ws, force_generic=generic, for_backward=True)
+    with_p = {n: torch.full(v, float("nan"), dtype=tdt, device="cuda") for n, v in shapes.items()}
+    sd.attn_bwd(desc, *ins, dout, with_p, ws, force_generic=generic, reuse_forward=2)
+    st, _ = sd.read_device_status(ws)
+    assert st == sd.DSPARK_OK, sd.last_error()
+    torch.cuda.synchronize()
+    for n in shapes:
+        if generic:
+            x, y = with_p[n].double(), reuse[n].double()
+            assert float((x - y).norm() / y.norm()) < 1e-6, n
+        else:
+            assert torch.equal(with_p[n], reuse[n]), n
+
+
+def test_bwd_reuse_of_probabilities_needs_a_forward_that_left_them():
+    """reuse_forward 2 after a forward without for_backward: reported
+    (EINVAL, NaN gradients); a forward with for_backward then makes it work.
+    A forward with for_backward needs a backward's workspace and the
+    three-kernel path."""
+    import torch
+    import speculative_decoding_draft_amd as sd
+    wl = wk.scaled(4, S=700, N=24)
+    desc, ins, dout, g, out = _bwd_setup(wl)
+    ws = torch.full((sd.bwd_workspace_size(desc),), 0x7f, dtype=torch.uint8, device="cuda")
+    sd.attn_fwd(desc, *ins, out, ws)
+    sd.attn_bwd(desc, *ins, dout, g, ws, reuse_forward=2)
+    st, _ = sd.read_device_status(ws)
+    assert st == sd.DSPARK_EINVAL and "reuse_forward" in sd.last_error()
+    for n, v in g.items():
+        assert bool(torch.isnan(v).all()), n
+    sd.attn_fwd(desc, *ins, out, ws, for_backward=True)
+    for v in g.values():
+        v.fill_(float("nan"))
+    sd.attn_bwd(desc, *ins, dout, g, ws, reuse_forward=2)
+    st, _ = sd.read_device_status(ws)
+    assert st == sd.DSPARK_OK, sd.last_error()
+    for n, v in g.items():
+        assert bool(torch.isfinite(v).all()), n
+    # a forward-sized workspace is refused, and so is the one-launch forward
+    small = torch.empty((sd.workspace_size(desc),), dtype=torch.uint8, device="cuda")
+    assert small.numel() < ws.numel()
+    with pytest.raises(sd.DSparkError) as e:
+        sd.attn_fwd(desc, *ins, out, small, for_backward=True)
+    assert e.value.status == sd.DSPARK_EWORKSPACE
+    with pytest.raises(sd.DSparkError) as e:
+        sd.attn_fwd(desc, *ins, out, ws, for_backward=True, one_launch=True)
+    assert e.value.status == sd.DSPARK_EINVAL and "one-launch" in sd.last_error()
 
 
 def _bwd_setup(wl):
