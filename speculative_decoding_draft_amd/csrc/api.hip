@@ -400,9 +400,10 @@ dspark_status forward_impl(const dspark_attn_desc* desc, const void* q_nope, con
     // the MFMA path evaluates RoPE inside the attention kernel; only the
     // generic path reads the table
     // the fixed scratch is never handed to a backward: no tag
+    // the MFMA path writes the rows of padding blocks in the last W_UV
+    // launch's tail instead of here
     if ((e = launch_prep(p, anchors, keep, ws, nullptr, L.rope_rows, fast ? nullptr : &theta,
-                         fast ? out : nullptr, s,
-                         fixed ? 0 : forward_tag(d, path, keep_p))) != hipSuccess)
+                         nullptr, s, fixed ? 0 : forward_tag(d, path, keep_p))) != hipSuccess)
         return hip_fail(e, "index / RoPE table / fill launch");
     if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if (fast) {
@@ -426,7 +427,9 @@ dspark_status forward_impl(const dspark_attn_desc* desc, const void* q_nope, con
             if ((e = launch_attn(p, in, wr, ch, theta, st, pmat)) != hipSuccess)
                 return hip_fail(e, "attention launch");
             if ((e = mark_on(4 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-            if ((e = launch_uv(p, in, wr, ch, st)) != hipSuccess)
+            const bool last = c == n_chunks - 1;
+            if ((e = launch_uv(p, in, wr, ch, st, last ? anchors : nullptr,
+                               last ? keep : nullptr)) != hipSuccess)
                 return hip_fail(e, "W_UV launch");
             if ((e = mark_on(5 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
         }

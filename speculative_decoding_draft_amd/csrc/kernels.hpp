@@ -61,8 +61,35 @@ hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws
 // [slot][5 H][kKeySlots]) for a backward that reuses them.
 hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
                        const RopeTheta& th, hipStream_t s, bf16* pmat = nullptr);
+// anchors / keep != nullptr: also write the rows of padding (0) and
+// invalid-anchor (NaN) blocks, with extra workgroups that run in the
+// launch's tail.
 hipError_t launch_uv(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
-                     hipStream_t s);
+                     hipStream_t s, const int32_t* anchors = nullptr,
+                     const uint8_t* keep = nullptr);
+
+// The 5 output rows of block blk (H * dv values each, contiguous) when the
+// attention path does not compute them: 0 for a padding block, NaN for a
+// kept block whose anchor is outside [0, S-2]; nothing otherwise.  All
+// threads of the workgroup take part.
+__device__ inline void fill_block(int blk, int S, int N, int L5, int H, int dv,
+                                  const int32_t* __restrict__ anchors,
+                                  const uint8_t* __restrict__ keep, bf16* __restrict__ out) {
+    bf16 fill;
+    if (keep[blk] == 0) {
+        fill = (bf16)0.0f;
+    } else {
+        const int A = anchors[blk];
+        if (A >= 0 && A <= S - 2) return;
+        fill = (bf16)__builtin_nanf("");
+    }
+    bf16x8 fv;
+    for (int e = 0; e < 8; ++e) fv[e] = fill;
+    const int b = blk / N, n = blk % N;
+    bf16* base = out + ((size_t)b * L5 + (size_t)kBlock * n) * H * dv;
+    const int chunks = kBlock * H * dv / 8;
+    for (int e = threadIdx.x; e < chunks; e += blockDim.x) gst16(base + (size_t)e * 8, fv);
+}
 // The whole forward after the preparation launch as one persistent launch
 // of kFusedCus workgroups (GLM dims; the control words must be zero).
 hipError_t launch_fused(const Problem& p, const Inputs& in, const Workspace& ws,

@@ -117,27 +117,6 @@ __device__ void rope_entry(long long e, int pairs, const RopeTheta& th,
     table[e] = make_float2(c, s);
 }
 
-// Rows of one block that the attention path does not compute: the block's
-// 5 rows of H * dv outputs are contiguous.
-__device__ void fill_block(int blk, int S, int N, int L5, int H, int dv,
-                           const int32_t* __restrict__ anchors, const uint8_t* __restrict__ keep,
-                           bf16* __restrict__ out) {
-    bf16 fill;
-    if (keep[blk] == 0) {
-        fill = (bf16)0.0f;
-    } else {
-        const int A = anchors[blk];
-        if (A >= 0 && A <= S - 2) return;
-        fill = (bf16)__builtin_nanf("");
-    }
-    bf16x8 fv;
-    for (int e = 0; e < 8; ++e) fv[e] = fill;
-    const int b = blk / N, n = blk % N;
-    bf16* base = out + ((size_t)b * L5 + (size_t)kBlock * n) * H * dv;
-    const int chunks = kBlock * H * dv / 8;
-    for (int e = threadIdx.x; e < chunks; e += kPrepThreads) gst16(base + (size_t)e * 8, fv);
-}
-
 // grid = 1 + rope_wgs + fill_wgs; out == nullptr (fill_wgs = 0) skips the fill.
 // The RoPE and fill parts loop with a grid stride, so a few hundred
 // workgroups cover any problem size.

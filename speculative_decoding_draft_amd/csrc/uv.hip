@@ -27,6 +27,8 @@
 // stored as 4 rows x 256 B per instruction.  Reading o_lat as MFMA
 // fragments straight from memory (16 rows x 64 B per instruction) and
 // storing in the tile layout made this kernel ~30% slower.
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace dspark {
@@ -60,8 +62,19 @@ __global__ __launch_bounds__(DOUT / 32 * 64) void uv_kernel(const bf16* __restri
                                                  const int32_t* __restrict__ kept,
                                                  const int32_t* __restrict__ status,
                                                  bf16* __restrict__ out, int N, int L5,
-                                                 int slot0, int nslots) {
+                                                 int slot0, int nslots,
+                                                 const int32_t* __restrict__ anchors,
+                                                 const uint8_t* __restrict__ keep, int S,
+                                                 int total_blocks, int n_fill) {
     using C = UvCfg<DOUT>;
+    // the last n_fill workgroups (dispatched after the others, so they run in
+    // the launch's tail) write the rows of padding / invalid-anchor blocks
+    const int n_work = (int)gridDim.x - n_fill;
+    if ((int)blockIdx.x >= n_work) {
+        for (int blk = (int)blockIdx.x - n_work; blk < total_blocks; blk += n_fill)
+            fill_block(blk, S, N, L5, kH, DOUT, anchors, keep, out);
+        return;
+    }
     constexpr int kUvWaves = C::kWaves, kUvCopies = C::kCopies, kUvStores = C::kStores;
     constexpr int kUvEpiStride = C::kEpiStride;
     // the ring slots are separate arrays so that the compiler sees that a
@@ -71,7 +84,7 @@ __global__ __launch_bounds__(DOUT / 32 * 64) void uv_kernel(const bf16* __restri
     __shared__ __attribute__((aligned(16))) char s2[kUvSlot];
     __shared__ __attribute__((aligned(16))) char s3[kUvSlot];
     __shared__ __attribute__((aligned(16))) char epi[kUvRows * kUvEpiStride];
-    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int lid = xcd_remap(blockIdx.x, n_work);
     const int rg = lid % kUvRowGroups;
     const int h = lid / kUvRowGroups;
     const int tid = threadIdx.x;
@@ -260,11 +273,13 @@ __global__ __launch_bounds__(DOUT / 32 * 64) void uv_kernel(const bf16* __restri
 }  // namespace
 
 hipError_t launch_uv(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
-                     hipStream_t s) {
+                     hipStream_t s, const int32_t* anchors, const uint8_t* keep) {
     const int grid = kH * kUvRowGroups;
-    hipLaunchKernelGGL(uv_kernel<kDv>, dim3(grid), dim3(UvCfg<kDv>::kWaves * 64), 0, s,
+    const int total = p.B * p.N;
+    const int n_fill = anchors ? std::min(256, total) : 0;
+    hipLaunchKernelGGL(uv_kernel<kDv>, dim3(grid + n_fill), dim3(UvCfg<kDv>::kWaves * 64), 0, s,
                        (const bf16*)in.w_uv, ws.olat, ws.kept, ws.status, (bf16*)in.out, p.N,
-                       p.L5, c.slot0, c.nslots);
+                       p.L5, c.slot0, c.nslots, anchors, keep, p.S, total, n_fill);
     return hipGetLastError();
 }
 
@@ -273,7 +288,7 @@ hipError_t launch_uv_dqc(const Problem& p, const void* w_uk, const bf16* dqabs,
     const int grid = kH * kUvRowGroups;
     hipLaunchKernelGGL(uv_kernel<kDc>, dim3(grid), dim3(UvCfg<kDc>::kWaves * 64), 0, s,
                        (const bf16*)w_uk, dqabs, ws.kept, ws.status, (bf16*)dq_nope, p.N, p.L5,
-                       0, p.B * p.N);
+                       0, p.B * p.N, nullptr, nullptr, p.S, 0, 0);
     return hipGetLastError();
 }
 
