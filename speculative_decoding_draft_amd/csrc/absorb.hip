@@ -57,12 +57,23 @@ struct AbsCfg {
     static_assert(WavesPerPart * 64 == PartCols, "a part holds whole waves' dims");
 };
 
+// acc / acc_n4 (the backward's W_UV^T dout, KD = d_v): the workgroups first
+// clear the fp32 dc^KV accumulator (acc_n4 float4) when the slots' anchors
+// do not ascend (status[kStUnsorted]): the atomic sums need it zeroed.
 template <int KD, int PARTS>
 __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
     const bf16* __restrict__ q_nope, const bf16* __restrict__ w_uk,
     const int32_t* __restrict__ kept, const int32_t* __restrict__ status,
-    bf16* __restrict__ q_abs, int N, int L5, int slot0, int nslots, uint32_t q_bytes) {
+    bf16* __restrict__ q_abs, int N, int L5, int slot0, int nslots, uint32_t q_bytes,
+    float4* __restrict__ acc, size_t acc_n4) {
     using C = AbsCfg<KD, PARTS>;
+    if constexpr (KD == kDv) {
+        if (status[kStUnsorted] != 0) {
+            for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < acc_n4;
+                 e += (size_t)gridDim.x * blockDim.x)
+                acc[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
     constexpr int kAbsKs = C::Ks, kAbsFrags = C::Frags, kAbsCopies = C::Copies;
     constexpr int kAbsStride = C::Stride, kAbsShared = C::Shared;
     // weight staging at start, then the output transpose
@@ -265,16 +276,18 @@ hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws
     hipLaunchKernelGGL((absorb_kernel<kDc, 2>), dim3(grid), dim3(kAbsWaves * 64), 0, s,
                        (const bf16*)in.q_nope, (const bf16*)in.w_uk, ws.kept, ws.status, ws.qabs,
                        p.N, p.L5, c.slot0, c.nslots,
-                       (uint32_t)((size_t)p.B * p.L5 * kH * kDc * sizeof(bf16)));
+                       (uint32_t)((size_t)p.B * p.L5 * kH * kDc * sizeof(bf16)), nullptr, 0);
     return hipGetLastError();
 }
 
 hipError_t launch_absorb_dv(const Problem& p, const void* dout, const void* w_uv,
-                            const Workspace& ws, bf16* dolat, hipStream_t s) {
+                            const Workspace& ws, bf16* dolat, float* acc, size_t n,
+                            hipStream_t s) {
     const int grid = kH * kAbsRowGroups;
     hipLaunchKernelGGL((absorb_kernel<kDv, 4>), dim3(grid), dim3(kAbsWaves * 64), 0, s,
                        (const bf16*)dout, (const bf16*)w_uv, ws.kept, ws.status, dolat, p.N, p.L5,
-                       0, p.B * p.N, (uint32_t)((size_t)p.B * p.L5 * kH * kDv * sizeof(bf16)));
+                       0, p.B * p.N, (uint32_t)((size_t)p.B * p.L5 * kH * kDv * sizeof(bf16)),
+                       reinterpret_cast<float4*>(acc), n / 4);
     return hipGetLastError();
 }
 

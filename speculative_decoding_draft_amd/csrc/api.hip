@@ -668,16 +668,23 @@ dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc, const void* q_nop
                                 fast ? nullptr : &theta, nullptr, s, tag),
                     "index launch");
     }
-    if (fast) DSPARK_STEP(launch_bwd_order(p, w, s), "anchor-order launch");
-    DSPARK_STEP(launch_bwd_zero(w.acc, zero_n, fast ? w.fwd.status + kStUnsorted : nullptr, s),
-                "accumulator clear launch");
+    // the MFMA path's anchor-order check is part of the index build, and the
+    // accumulator clear (needed only when the anchors do not ascend) part of
+    // the W_UV^T dout launch; their stage events are still recorded
+    if (fast) {
+        if ((e = mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if ((e = mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    } else {
+        DSPARK_STEP(launch_bwd_zero(w.acc, zero_n, nullptr, s), "accumulator clear launch");
+    }
     if (fast) {
         if (reuse) {
             if ((e = mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
         } else {
             DSPARK_STEP(launch_absorb(p, in, w.fwd, Chunk{0, d.B * d.N}, s), "absorb launch");
         }
-        DSPARK_STEP(launch_absorb_dv(p, dout, w_uv, w.fwd, w.dolat, s), "W_UV^T dout launch");
+        DSPARK_STEP(launch_absorb_dv(p, dout, w_uv, w.fwd, w.dolat, w.acc, zero_n, s),
+                    "W_UV^T dout launch");
         DSPARK_STEP(launch_bwd_attn(p, in, g, w, theta, s, !reuse, load_p),
                     "backward attention launch");
         DSPARK_STEP(launch_bwd_dkv(p, w, s), "dc^KV launch");

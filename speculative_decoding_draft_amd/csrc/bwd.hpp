@@ -83,11 +83,6 @@ struct BwdWork {
     float* wacc;
 };
 
-// Status word set by launch_bwd_order: nonzero when some sample's kept
-// anchors are not in ascending order (slot order).  Words 0 and 1 belong to
-// the index builder.
-constexpr int kStUnsorted = 2;
-
 // Zero the fp32 accumulators (and, on the generic path, the weight ones).
 // only_if: nullptr (always), or a status word -- the clear runs only when
 // that word is nonzero.
@@ -102,8 +97,6 @@ hipError_t launch_bwd_reuse_check(const Problem& p, const BwdWork& w, int32_t ex
 // otherwise the launch exits at once.  elem: 2 (bf16) or 4 (fp32) bytes.
 hipError_t launch_bwd_reuse_fill(const Problem& p, const BwdGrads& g, const BwdWork& w,
                                  int elem, hipStream_t s);
-// One workgroup: sets status[kStUnsorted] from the slot records.
-hipError_t launch_bwd_order(const Problem& p, const BwdWork& w, hipStream_t s);
 // MFMA path final pass: per row, the block partials of the windows that
 // cover it (ascending anchors) or the accumulator row (otherwise), converted
 // to the output type with R^T applied to dk^R; plus the query-gradient rows
@@ -127,8 +120,11 @@ hipError_t launch_bwd_finalize(const Problem& p, bool bf16_io, const BwdGrads& g
 // MFMA path (bf16, GLM dims).
 // d_olat = W_UV[h]^T dout for every kept row: the forward's absorb kernel
 // with d_v = 256 input dims (absorb.hip); written in the permuted latent order.
+// Its workgroups also clear the fp32 accumulator (n floats, a multiple of 4)
+// first when status[kStUnsorted] is set (the atomic dc^KV sums need it).
 hipError_t launch_absorb_dv(const Problem& p, const void* dout, const void* w_uv,
-                            const Workspace& ws, bf16* dolat, hipStream_t s);
+                            const Workspace& ws, bf16* dolat, float* acc, size_t n,
+                            hipStream_t s);
 // dq^C = W_UK[h] dq_abs for every kept row: the forward's W_UV kernel with
 // 192 output dims (uv.hip).
 hipError_t launch_uv_dqc(const Problem& p, const void* w_uk, const bf16* dqabs,

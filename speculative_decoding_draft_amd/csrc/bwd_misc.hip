@@ -347,24 +347,6 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(
     }
 }
 
-// status[kStUnsorted] = 1 when two consecutive kept slots of one sample have
-// descending anchors (slots are in (b, n) order).
-__global__ __launch_bounds__(1024) void order_kernel(const int4* __restrict__ srec,
-                                                     int32_t* __restrict__ status, int N) {
-    __shared__ int bad;
-    if (threadIdx.x == 0) bad = 0;
-    __syncthreads();
-    const int n_live = status[kStKeptCount];
-    int mine = 0;
-    for (int s = 1 + threadIdx.x; s < n_live; s += blockDim.x) {
-        const int4 a = srec[s - 1], c = srec[s];
-        mine |= (a.w / N == c.w / N) && (c.z < a.z);
-    }
-    if (mine) atomicOr(&bad, 1);
-    __syncthreads();
-    if (threadIdx.x == 0) status[kStUnsorted] = bad;
-}
-
 // First slot in [0, n) whose key (sample, anchor) is greater than (b, a);
 // slots are ordered by that key when the anchors ascend.
 __device__ inline int first_after(const int4* __restrict__ srec, int n, int N, int b, int a) {
@@ -522,11 +504,6 @@ hipError_t launch_bwd_reuse_fill(const Problem& p, const BwdGrads& g, const BwdW
                  {B * L5 * H * p.dc, B * L5 * H * p.dr, B * S * p.D, B * S * p.dr, B * L5 * p.D,
                   B * L5 * p.dr, H * p.dc * p.D, H * p.dv * p.D}};
     hipLaunchKernelGGL(reuse_fill_kernel, dim3(256), dim3(256), 0, s, w.fwd.status, sp, elem);
-    return hipGetLastError();
-}
-
-hipError_t launch_bwd_order(const Problem& p, const BwdWork& w, hipStream_t s) {
-    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, s, w.fwd.srec, w.fwd.status, p.N);
     return hipGetLastError();
 }
 

@@ -25,15 +25,16 @@ constexpr int kMaxWindow = 128;    // W <= 128: at most 127 context + 5 block ke
 constexpr int kMaxKeys = kMaxWindow - 1 + kBlock;   // 132
 constexpr int kKeySlots = (kMaxKeys + 15) / 16 * 16;   // 144: a block's keys in 16-key tiles
 
-// Status area of the workspace (int32 words).  Word 2 belongs to the
-// backward (unsorted anchors); word 3 records a stalled fused pipeline.
-// Word 2 belongs to the backward (anchor order).  kStPathTag: what the last
-// index build on this workspace was for (a hash of the descriptor and the
-// forward path; 0 when nothing may reuse it).  kStReuseBad: set by a backward
-// with reuse_forward whose workspace does not hold that tag.
+// Status area of the workspace (int32 words), written by the index builder
+// except where noted.  kStUnsorted: nonzero when some sample's kept anchors
+// do not ascend in slot order (the backward then sums block partials with
+// atomics).  kStPipeFault: a stalled fused pipeline.  kStPathTag: what the
+// last index build on this workspace was for (a hash of the descriptor and
+// the forward path; 0 when nothing may reuse it).  kStReuseBad: set by a
+// backward with reuse_forward whose workspace does not hold that tag.
 enum StatusWord {
-    kStKeptCount = 0, kStFirstBad = 1, kStPipeFault = 3, kStPathTag = 4, kStReuseBad = 5,
-    kStWords = 16
+    kStKeptCount = 0, kStFirstBad = 1, kStUnsorted = 2, kStPipeFault = 3, kStPathTag = 4,
+    kStReuseBad = 5, kStWords = 16
 };
 static_assert(kStWords * 4 == DSPARK_STATUS_BYTES, "status area size");
 

@@ -32,13 +32,18 @@ constexpr int kIndexThreads = kPrepThreads;
 
 // One workgroup: scans all B*N blocks in order, so the kept slots are the
 // ranks of the kept blocks in (b, n) order.
-__device__ void build_index(int total, int S, int W, const int32_t* __restrict__ anchors,
+__device__ void build_index(int total, int S, int W, int N, const int32_t* __restrict__ anchors,
                             const uint8_t* __restrict__ keep, int4* __restrict__ idx,
                             int32_t* __restrict__ kept, int4* __restrict__ srec,
                             int32_t* __restrict__ status, int4* __restrict__ idx_copy,
                             int32_t* __restrict__ ctl, int ctl_words, int32_t path_tag) {
     __shared__ int wave_count[kIndexThreads / 64];
     __shared__ int first_bad_sh;
+    // the chunk's kept blocks in slot order (block index, anchor), and the
+    // last kept block before the chunk, for the anchor-order check
+    __shared__ int2 chunk_kept[kIndexThreads];
+    __shared__ int2 prev_kept;
+    __shared__ int unsorted_sh;
     const int tid = threadIdx.x;
     for (int i = tid; i < ctl_words; i += kIndexThreads) ctl[i] = 0;
     if (tid == 0) {
@@ -48,7 +53,11 @@ __device__ void build_index(int total, int S, int W, const int32_t* __restrict__
     }
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    if (tid == 0) first_bad_sh = INT_MAX;
+    if (tid == 0) {
+        first_bad_sh = INT_MAX;
+        prev_kept = make_int2(-1, 0);
+        unsorted_sh = 0;
+    }
     int carry = 0;        // kept blocks before this chunk (same value in every thread)
     int first_bad = INT_MAX;
     __syncthreads();
@@ -83,19 +92,29 @@ __device__ void build_index(int total, int S, int W, const int32_t* __restrict__
             rec.w = before + before_in_wave;
             kept[rec.w] = i;
             srec[rec.w] = make_int4(rec.x, rec.y, rec.z, i);
+            chunk_kept[rec.w - carry] = make_int2(i, rec.z);
         }
         if (i < total) {
             idx[i] = rec;
             if (idx_copy) idx_copy[i] = rec;
         }
+        __syncthreads();
+        // anchors descend between two consecutive kept slots of one sample
+        if (state == 1) {
+            const int r = rec.w - carry;
+            const int2 prev = r > 0 ? chunk_kept[r - 1] : prev_kept;
+            if (prev.x >= 0 && prev.x / N == i / N && rec.z < prev.y) unsorted_sh = 1;
+        }
+        __syncthreads();   // wave_count, chunk_kept and prev_kept are rewritten next
+        if (tid == 0 && chunk > 0) prev_kept = chunk_kept[chunk - 1];
         carry += chunk;
-        __syncthreads();   // wave_count is rewritten by the next chunk
     }
     if (first_bad != INT_MAX) atomicMin(&first_bad_sh, first_bad);
     __syncthreads();
     if (tid == 0) {
         status[kStKeptCount] = carry;
         status[kStFirstBad] = (first_bad_sh == INT_MAX) ? -1 : first_bad_sh;
+        status[kStUnsorted] = unsorted_sh;
     }
 }
 
@@ -128,7 +147,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     RopeTheta th, float2* __restrict__ table, int rope_wgs, bf16* __restrict__ out, int N,
     int L5, int H, int dv) {
     if (blockIdx.x == 0) {
-        build_index(total, S, W, anchors, keep, idx, kept, srec, status, idx_copy, ctl,
+        build_index(total, S, W, N, anchors, keep, idx, kept, srec, status, idx_copy, ctl,
                     ctl_words, path_tag);
         return;
     }
