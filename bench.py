@@ -2,8 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
 
-A step is one dspark_attn_fwd call per layer (index build and padding fill,
-absorb, attention, W_UV) over the whole workload, with inputs resident in
+A step is one dspark_attn_fwd call per layer (index build, absorb,
+attention, W_UV with the rows of padding blocks) over the whole workload, with inputs resident in
 HBM and the L2 not flushed between steps.  The headline workload is the
 S=32768, N=1024 configuration (25% padding blocks, 5% clamped windows,
 synthetic N(0,1) activations and N(0,1/512) weights).  Prints one JSON line.
@@ -59,18 +59,18 @@ sys.path.insert(0, ROOT)
 
 MI355X_BF16_PEAK_TFLOPS = 2516.6     # 256 CU * 2.4 GHz * 4096 FLOP/CU/clk, dense
 MI355X_HBM_PEAK_GBS = 8000.0
-STAGES = ("index+fill", "absorb", "attention", "w_uv")
+STAGES = ("index", "absorb", "attention", "w_uv")
 KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.hip",
-                  "index+fill": "prep.hip"}
+                  "index": "prep.hip"}
 # Measured HBM bytes per launch on the headline workload (one round of all
 # blocks): rocprofv3 --pmc FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (factors from a
 # plain 256 MiB device copy), with the digest of the kernel's sources when the
 # counters were taken.  A kernel whose sources changed since reports null.
 PMC_TRAFFIC = {
-    "absorb": (358_784_681, "a6d94fd2f33133fb"),
-    "attention": (584_034_509, "00bb1efce6168c8c"),
-    "w_uv": (394_524_861, "f8e0b065f1c9d199"),
-    "index+fill": (42_090_253, "2d8e19e1157fcb65"),
+    "absorb": (358_784_541, "489d275b7a782f9e"),
+    "attention": (583_686_404, "c2acdff294f0041f"),
+    "w_uv": (436_545_627, "0656d251d41d0f0b"),
+    "index": (46_386, "601845af3ef99618"),
 }
 PMC_SOURCE = "rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, profiles/attn_fwd_headline_S32768_N1024_counters.md"
 
@@ -86,12 +86,12 @@ BWD_KERNEL_SOURCES = {
     "final": ("bwd_misc.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
 }
 BWD_PMC_TRAFFIC = {
-    "attention_bwd": (1_294_714_265, "c1db77fb0dbe5e86"),
-    "dw": (757_865_861, "80f2076d7c997560"),
-    "dkv": (1_001_790_286, "80f2076d7c997560"),
-    "dq_nope": (358_915_331, "f8e0b065f1c9d199"),
-    "d_olat": (394_473_728, "a6d94fd2f33133fb"),
-    "final": (311_311_264, "87eccf3c74993e7c"),
+    "attention_bwd": (1_293_956_233, "a0a5d5963b96a866"),
+    "dw": (757_438_413, "b9e0c9e4a6365d43"),
+    "dkv": (1_002_665_339, "b9e0c9e4a6365d43"),
+    "dq_nope": (358_924_491, "0656d251d41d0f0b"),
+    "d_olat": (394_472_625, "489d275b7a782f9e"),
+    "final": (311_310_969, "7968ed81c03e4164"),
 }
 
 
@@ -100,10 +100,11 @@ BWD_PMC_TRAFFIC = {
 # three launches; 64 sequences, K = 5, V = 154880): the same FETCH/WRITE
 # scaling, with the files each is built from and their digest when taken.
 SIDE_PMC_TRAFFIC = {
-    "loss_stats": (3_882_859_895, ("loss.hip", "blas.hpp", "kernels.hpp"), "a94b7e3af57b3f81"),
-    "verify": (436_648_344 + 398_429_336 + 4_485_120, ("decode.hip", "kernels.hpp"),
-               "995d2c8ebfedfcb3"),
+    "loss_stats": (3_882_860_544, ("loss.hip", "blas.hpp", "kernels.hpp"), "90dc0294b34e4a23"),
+    "verify": (436_648_376 + 398_429_184 + 4_485_120, ("decode.hip", "kernels.hpp"),
+               "10aacc9793cc2b8e"),
 }
+
 
 
 def side_measured_traffic(key: str, applies: bool):
@@ -154,7 +155,8 @@ def stage_bytes(wl, anchors, keep, chunk_blocks):
     """Algorithmic HBM bytes of each kernel launch (bf16 = 2 B), per chunk of
     `chunk_blocks` kept blocks taken in (b, n) order: every input the launch
     needs read once (its weights included), the context read as the union of
-    the chunk's kept windows, each output written once.  Returns
+    the chunk's kept windows, each output written once (the last W_UV launch
+    also writes the padding blocks' rows).  Returns
     {stage: [bytes of launch 0, launch 1, ...]}."""
     H, D, dc, dr, dv = wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v
     kept = [(b, int(anchors[b, n])) for b in range(wl.B) for n in range(wl.N) if keep[b, n]]
@@ -172,6 +174,8 @@ def stage_bytes(wl, anchors, keep, chunk_blocks):
         out["absorb"].append(rows * H * (dc + D) * 2 + H * dc * D * 2)
         out["attention"].append(rows * H * (D + dr + D) * 2 + (union + rows) * (D + dr) * 2)
         out["w_uv"].append(rows * H * (D + dv) * 2 + H * dv * D * 2)
+    # the last W_UV launch also writes the rows of padding blocks
+    out["w_uv"][-1] += (wl.B * wl.N - len(kept)) * 5 * H * dv * 2
     return out
 
 
@@ -265,15 +269,25 @@ def bench_backward(sd, torch, wl, tensors, a_dev, k_dev, anchors, keep, desc, sp
     wall = (time.perf_counter() - t0) / steps
     n_ev = sd.bwd_plan(desc)
     names = BWD_STAGES if n_ev == len(BWD_STAGES) + 1 else None
-    ev = hip.create(n_ev)
-    sd.attn_bwd(*args, stream=sptr, stage_events=ev)
+    # three instrumented calls back to back, per-stage medians: the first
+    # call's event [0] lands on an idle stream, so its first stage also holds
+    # the host's submission of the next launch
+    evs = [hip.create(n_ev) for _ in range(3)]
+    for ev in evs:
+        sd.attn_bwd(*args, stream=sptr, stage_events=ev)
     torch.cuda.synchronize()
     stage_us = {}
     if names:
-        for i, s in enumerate(names):
-            key = "index" if s in BWD_FOLDED else s
-            stage_us[key] = stage_us.get(key, 0.0) + hip.elapsed_ms(ev[i], ev[i + 1]) * 1e3
-    hip.destroy(ev)
+        for ev in evs:
+            one = {}
+            for i, s in enumerate(names):
+                key = "index" if s in BWD_FOLDED else s
+                one[key] = one.get(key, 0.0) + hip.elapsed_ms(ev[i], ev[i + 1]) * 1e3
+            for key, v in one.items():
+                stage_us.setdefault(key, []).append(v)
+        stage_us = {k: float(np.median(v)) for k, v in stage_us.items()}
+    for ev in evs:
+        hip.destroy(ev)
     flop = bwd_useful_flop(anchors, keep, wl.W, wl.H, wl.D, wl.d_c, wl.d_r, wl.d_v)
     out = {"ms_per_step": round(wall * 1e3, 4), "steps": steps, "warmup": n_w,
            "useful_gflop_per_step": round(flop / 1e9, 3),
@@ -917,8 +931,9 @@ def measure_forward(torch, fw, steps, warmup, samples, sample_steps, stage_steps
       2. for several layers, 50 steps with an event at every layer boundary
          (per-layer medians);
       3. `stage_steps` calls per layer with the library's stage events
-         between its kernels (those events order the kernels around them,
-         so they stay out of the other passes);
+         between its kernels, after one such call that is dropped (those
+         events order the kernels around them, so they stay out of the
+         other passes);
       4. exactly `steps` steps with no event at all, between two
          synchronisations (its mean is reported beside the median).
     A step is one forward call per layer."""
@@ -959,12 +974,14 @@ def measure_forward(torch, fw, steps, warmup, samples, sample_steps, stage_steps
     n_ev, n_chunks = fw["n_ev"], fw["n_chunks"]
     live = n_chunks if n_ev == 3 else min(n_chunks, -(-int(fw["keep"].sum()) // fw["chunk"]))
     per_stage, per_round = {}, None
-    ev = HIP.create(stage_steps * L * n_ev)
-    for i in range(stage_steps):
-        for l, call in enumerate(calls):
-            call.with_events(ev[(i * L + l) * n_ev:(i * L + l + 1) * n_ev])
+    # one leading instrumented call is dropped: its event [0] lands on an
+    # idle stream, so its first stage also holds the host's submission of
+    # the next launch
+    ev = HIP.create((stage_steps * L + 1) * n_ev)
+    for i in range(stage_steps * L + 1):
+        calls[(i - 1) % L].with_events(ev[i * n_ev:(i + 1) * n_ev])
     torch.cuda.synchronize()
-    for j in range(stage_steps * L):
+    for j in range(1, stage_steps * L + 1):
         tot, rounds = stage_times(ev[j * n_ev:(j + 1) * n_ev], n_ev, n_chunks, live,
                                   fw["one_launch"])
         for s, v in tot.items():
@@ -1157,7 +1174,7 @@ def main():
         impl_bytes = float(np.mean(impl[dom][:live]))
         n_blocks = wl.B * wl.N
         measured = {s: measured_traffic(s, wl.name, fw["chunk"], n_blocks)
-                    for s in ("index+fill", "absorb", "attention", "w_uv")}
+                    for s in STAGES}
         fwd_alg = forward_algorithmic_bytes(wl, anchors, keep)
         fwd_meas = (sum(measured.values()) if all(v is not None for v in measured.values())
                     else None)
