@@ -203,14 +203,18 @@ __device__ inline int val_index(int v0, int i) {
 }
 
 // Per (row, chunk): {max of x/T, sum exp(x/T - max), index of the first
-// maximum, 0}.
+// maximum, x/T at the row's drafted token when the chunk holds it (else 0)}.
+// The drafted token of draft row b K + k and target row b (K+1) + k is
+// tokens[b K + k]; the last target row of a sequence has none.
 template <bool VEC>
 __global__ __launch_bounds__(kVThreads) void verify_stats_kernel(
     int B, int K, int V, int C, float inv_t, const float* __restrict__ dl,
-    const float* __restrict__ tl, float4* __restrict__ part) {
+    const float* __restrict__ tl, const int32_t* __restrict__ tokens,
+    float4* __restrict__ part) {
     __shared__ float red_m[kVThreads / 64];
     __shared__ int red_i[kVThreads / 64];
     __shared__ float red_s[kVThreads / 64];
+    __shared__ float tok_val;
     // Rows in the order the overlap pass wants them still cached: every
     // sequence's last target row first (the overlap pass does not read it),
     // then per sequence its K drafted rows and K target rows.  The overlap
@@ -227,8 +231,21 @@ __global__ __launch_bounds__(kVThreads) void verify_stats_kernel(
     const float* x = row_ptr(r, B, K, V, dl, tl);
     const int v0 = c * kVChunk, v1 = min(V, v0 + kVChunk);
     const int w = threadIdx.x >> 6;
+    int tok = -1;
+    if (r < B * K) {
+        tok = tokens[r];
+    } else {
+        const int bb = (r - B * K) / (K + 1), k = (r - B * K) % (K + 1);
+        if (k < K) tok = tokens[bb * K + k];
+    }
+    const bool has_tok = tok >= v0 && tok < v1;     // uniform: one thread holds the value
     float val[kVPer];
     load_vals<VEC>(x, v0, v1, inv_t, val);
+    if (has_tok) {
+#pragma unroll
+        for (int i = 0; i < kVPer; ++i)
+            if (val_index<VEC>(v0, i) == tok) tok_val = val[i];
+    }
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kVPer; ++i) m = fmaxf(m, val[i]);
@@ -260,7 +277,7 @@ __global__ __launch_bounds__(kVThreads) void verify_stats_kernel(
             t += red_s[i];
             ti = min(ti, red_i[i]);
         }
-        part[(size_t)r * C + c] = make_float4(m, t, __int_as_float(ti), 0.f);
+        part[(size_t)r * C + c] = make_float4(m, t, __int_as_float(ti), has_tok ? tok_val : 0.f);
     }
 }
 
@@ -286,19 +303,36 @@ __global__ __launch_bounds__(kVThreads) void verify_overlap_kernel(
     const int r = B * K - 1 - (int)blockIdx.x / C, c = blockIdx.x % C;   // r = b*K + k
     const int b = r / K, k = r % K;
     const int rt = B * K + b * (K + 1) + k;                // the target row
-    if (threadIdx.x < 64) {
-        const float lq = chunk_lse(part + (size_t)r * C, C);
-        const float lp = chunk_lse(part + (size_t)rt * C, C);
-        if (threadIdx.x == 0) lse_s = make_float2(lq, lp);
+    // wave 0 requests the two rows' chunk partials (one per lane when
+    // C <= 64) before the chunk's values, so that the log-sum-exps overlap
+    // the value loads
+    const int lane = threadIdx.x & 63;
+    const bool one_per_lane = C <= 64;
+    float4 pq = make_float4(-INFINITY, 0.f, 0.f, 0.f), pp = pq;
+    if (threadIdx.x < 64 && one_per_lane && lane < C) {
+        pq = part[(size_t)r * C + lane];
+        pp = part[(size_t)rt * C + lane];
     }
-    __syncthreads();
-    const float2 lse = lse_s;
     const float* q = dl + (size_t)r * V;
     const float* p = tl + ((size_t)b * (K + 1) + k) * V;
     const int v0 = c * kVChunk, v1 = min(V, v0 + kVChunk);
     float xq[kVPer], xp[kVPer];
     load_vals<VEC>(q, v0, v1, inv_t, xq);
     load_vals<VEC>(p, v0, v1, inv_t, xp);
+    if (threadIdx.x < 64) {
+        float lq, lp;
+        if (one_per_lane) {     // the same operations as chunk_lse
+            const float mq = vwave_max(pq.x), mp = vwave_max(pp.x);
+            lq = mq + __logf(vwave_sum(pq.y * __expf(pq.x - mq)));
+            lp = mp + __logf(vwave_sum(pp.y * __expf(pp.x - mp)));
+        } else {
+            lq = chunk_lse(part + (size_t)r * C, C);
+            lp = chunk_lse(part + (size_t)rt * C, C);
+        }
+        if (threadIdx.x == 0) lse_s = make_float2(lq, lp);
+    }
+    __syncthreads();
+    const float2 lse = lse_s;
     float mn = 0.f, res = 0.f;
 #pragma unroll
     for (int i = 0; i < kVPer; ++i) {      // -inf padding: both terms 0
@@ -322,11 +356,38 @@ __global__ __launch_bounds__(kVThreads) void verify_overlap_kernel(
     }
 }
 
+// Index of a row's first maximum from its C partials (one wave; lanes stride
+// the chunks): the largest value, the smallest index among equal values.
+__device__ inline int chunk_top(const float4* __restrict__ p, int C) {
+    float m = -INFINITY;
+    int mi = INT_MAX;
+    for (int c = threadIdx.x & 63; c < C; c += 64) {
+        const float x = p[c].x;
+        const int qi = __float_as_int(p[c].z);
+        if (x > m || (x == m && qi < mi)) {
+            m = x;
+            mi = qi;
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        const float xm = __shfl_xor(m, o);
+        const int xi = __shfl_xor(mi, o);
+        if (xm > m || (xm == m && xi < mi)) {
+            m = xm;
+            mi = xi;
+        }
+    }
+    return mi;
+}
+
 // One workgroup per sequence: decisions, outputs and the draw.  The
-// sequence's chunk partials, drafted-token logits and uniforms are first
-// staged in LDS by the whole workgroup (dynamic LDS: (2K+1) C float4 +
-// K C float2), so that the sequential decisions read no global memory.
+// sequence's chunk partials (which carry the drafted tokens' logits) and
+// uniforms are first staged in LDS by the whole workgroup (dynamic LDS: (2K+1) C float4 +
+// K C float2), so that the decisions read no global memory.  Every sum or
+// search over the chunks runs across a wave's lanes: the per-row totals in
+// one pass spread over the waves, the chunk of the draw by a prefix scan.
 constexpr int kMaxK = 64;
+template <bool VEC>
 __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(
     int B, int K, int V, int C, int mode, float inv_t, const float* __restrict__ dl,
     const float* __restrict__ tl, const int32_t* __restrict__ tokens,
@@ -338,126 +399,181 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(
     float2* so = reinterpret_cast<float2*>(dyn + (2 * K + 1) * C);   // [K C] overlap, residual
     __shared__ float lse_q[kMaxK], lse_p[kMaxK + 1];
     __shared__ float xq_s[kMaxK], xp_s[kMaxK], u_s[kMaxK + 1];
-    __shared__ int tok_s[kMaxK];
-    __shared__ int j_s, chunk_s;
+    __shared__ float ovl_s[kMaxK], zres_s[kMaxK];
+    __shared__ int tok_s[kMaxK], top_s[kMaxK + 1];
+    __shared__ int j_s, chunk_s, resid_s;
     __shared__ float rem_s, lq_s, lp_s;
     __shared__ float wsum[kVThreads / 64];
-    __shared__ int found_s, last_s, resid_s;
+    __shared__ int found_w[kVThreads / 64], last_w[kVThreads / 64];
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const bool target_only = mode == DSPARK_VERIFY_TARGET_ONLY;
     for (int i = tid; i < (2 * K + 1) * C; i += kVThreads) {
         const int k = i / C, c = i % C;
         const size_t r = k < K ? (size_t)b * K + k : (size_t)B * K + (size_t)b * (K + 1) + (k - K);
         sp[i] = part[r * C + c];
     }
     for (int i = tid; i < K * C; i += kVThreads) so[i] = ov[(size_t)b * K * C + i];
-    if (tid < K) {
-        const int x = tokens[(size_t)b * K + tid];
-        tok_s[tid] = x;
-        if (x >= 0 && x < V) {
-            xq_s[tid] = dl[((size_t)b * K + tid) * V + x] * inv_t;
-            xp_s[tid] = tl[((size_t)b * (K + 1) + tid) * V + x] * inv_t;
-        }
-    }
+    if (tid < K) tok_s[tid] = tokens[(size_t)b * K + tid];
     if (tid <= K) u_s[tid] = uni[(size_t)b * (K + 1) + tid];
     __syncthreads();
-    // log-sum-exps of the sequence's rows (wave w takes rows w, w + 4, ...)
-    for (int k = w; k < 2 * K + 1; k += kVThreads / 64) {
-        const float l = chunk_lse(sp + (size_t)k * C, C);
-        if (lane == 0) {
-            if (k < K) lse_q[k] = l;
-            else lse_p[k - K] = l;
+    // the drafted tokens' logits (/T), recorded by the statistics pass in
+    // the partial of the chunk that holds each
+    if (tid < K) {
+        const int x = tok_s[tid];
+        if (x >= 0 && x < V) {
+            xq_s[tid] = sp[(size_t)tid * C + x / kVChunk].w;
+            xp_s[tid] = sp[(size_t)(K + tid) * C + x / kVChunk].w;
+        }
+    }
+    // per-row totals, one wave per task: the log-sum-exp of each of the
+    // 2K + 1 rows, the overlap and residual totals of each drafted row and
+    // (target-only) each target row's first maximum
+    const int n_lse = 2 * K + 1;
+    const int n_tasks = n_lse + K + (target_only ? K + 1 : 0);
+    for (int t = w; t < n_tasks; t += kVThreads / 64) {
+        if (t < n_lse) {
+            const float l = chunk_lse(sp + (size_t)t * C, C);
+            if (lane == 0) {
+                if (t < K) lse_q[t] = l;
+                else lse_p[t - K] = l;
+            }
+        } else if (t < n_lse + K) {
+            const int k = t - n_lse;
+            float o = 0.f, z = 0.f;
+            for (int c = lane; c < C; c += 64) {
+                const float2 v = so[k * C + c];
+                o += v.x;
+                z += v.y;
+            }
+            o = vwave_sum(o);
+            z = vwave_sum(z);
+            if (lane == 0) {
+                ovl_s[k] = o;
+                zres_s[k] = z;
+            }
+        } else {
+            const int k = t - n_lse - K;
+            const int top = chunk_top(sp + (size_t)(K + k) * C, C);
+            if (lane == 0) top_s[k] = top;
         }
     }
     __syncthreads();
-    // the target row k's first maximum, from the chunk partials
-    auto top = [&](int k) {
-        const float4* r = sp + (size_t)(K + k) * C;
-        float m = -INFINITY;
-        int mi = INT_MAX;
-        for (int c = 0; c < C; ++c) {
-            const int qi = __float_as_int(r[c].z);
-            if (r[c].x > m || (r[c].x == m && qi < mi)) {
-                m = r[c].x;
-                mi = qi;
-            }
-        }
-        return mi;
-    };
     if (tid == 0) {
         int bad = 0, j = K;
         for (int k = 0; k < K; ++k) {
             const int x = tok_s[k];
-            float a = 0.f, o = 0.f;
+            float a = 0.f;
             if (x < 0 || x >= V) bad = 1;
             else a = fminf(1.f, __expf((xp_s[k] - lse_p[k]) - (xq_s[k] - lse_q[k])));
-            for (int c = 0; c < C; ++c) o += so[k * C + c].x;
             accept_prob[(size_t)b * K + k] = a;
-            overlap[(size_t)b * K + k] = o;
+            overlap[(size_t)b * K + k] = ovl_s[k];
             if (j == K && !bad) {
-                const bool ok = mode == DSPARK_VERIFY_REJECTION ? u_s[k] < a : x == top(k);
+                const bool ok = target_only ? x == top_s[k] : u_s[k] < a;
                 if (!ok) j = k;
             }
         }
         j_s = j;
-        chunk_s = -1;
+        resid_s = -1;            // decided here: no draw
         if (bad) {
             n_accept[b] = -1;
             next_token[b] = -1;
-        } else if (mode == DSPARK_VERIFY_TARGET_ONLY) {
+        } else if (target_only) {
             n_accept[b] = j;
-            next_token[b] = top(j);
+            next_token[b] = top_s[j];
         } else {
             // the draw: the residual of row j, or p_j when it is empty, or p_K
-            bool residual = j < K;
-            float Z = 0.f;
-            if (residual) {
-                for (int c = 0; c < C; ++c) Z += so[j * C + c].y;
-                if (!(Z > 0.f)) residual = false;
+            n_accept[b] = j;
+            resid_s = (j < K && zres_s[j] > 0.f) ? 1 : 0;
+        }
+    }
+    __syncthreads();
+    if (resid_s < 0) return;
+    const bool residual = resid_s != 0;
+    const int j = j_s;
+    // wave 0: the chunk holding the draw, the first whose cumulative weight
+    // exceeds u Z (inclusive prefix over the lanes, 64 chunks at a time)
+    if (w == 0) {
+        const float4* pr = sp + (size_t)(K + j) * C;       // target row j (j = K: p_K)
+        const float lpj = lse_p[j];
+        auto mass = [&](int c) {
+            return residual ? so[j * C + c].y : pr[c].y * __expf(pr[c].x - lpj);
+        };
+        float Z;
+        if (residual) {
+            Z = zres_s[j];
+        } else {
+            float z = 0.f;
+            for (int c = lane; c < C; c += 64) z += mass(c);
+            Z = vwave_sum(z);
+        }
+        const float target = u_s[K] * Z;
+        float carry = 0.f, cum = 0.f;
+        int cs = -1, last_nz = -1;
+        for (int c0 = 0; c0 < C; c0 += 64) {
+            const int c = c0 + lane;
+            const float mc = c < C ? mass(c) : 0.f;
+            float incl = mc;
+            for (int o = 1; o < 64; o <<= 1) {
+                const float t = __shfl_up(incl, o);
+                if (lane >= o) incl += t;
             }
-            const float4* pr = sp + (size_t)(K + j) * C;       // target row j (j = K: p_K)
-            auto mass = [&](int c) {
-                return residual ? so[j * C + c].y : pr[c].y * __expf(pr[c].x - lse_p[j]);
-            };
-            if (!residual) {
-                Z = 0.f;
-                for (int c = 0; c < C; ++c) Z += mass(c);
+            const unsigned long long nz = __ballot(mc > 0.f);
+            const unsigned long long hit = __ballot(mc > 0.f && carry + incl > target);
+            if (nz) last_nz = c0 + 63 - __builtin_clzll(nz);
+            if (hit) {
+                const int first = __builtin_ctzll(hit);
+                const float excl = __shfl(incl - mc, first);
+                cs = c0 + first;
+                cum = carry + excl;
+                break;
             }
-            const float target = u_s[K] * Z;
-            float cum = 0.f;
-            int cs = -1, last_nz = -1;
-            for (int c = 0; c < C; ++c) {
-                const float mc = mass(c);
-                if (mc > 0.f) last_nz = c;
-                if (cum + mc > target) {
-                    cs = c;
-                    break;
-                }
-                cum += mc;
-            }
-            if (cs < 0) {           // rounding: the total fell short of u*Z
-                cs = last_nz;
-                cum = 0.f;
-                for (int c = 0; c < cs; ++c) cum += mass(c);
-            }
+            carry += __shfl(incl, 63);
+        }
+        if (cs < 0 && last_nz >= 0) {    // rounding: the total fell short of u Z
+            cs = last_nz;
+            float s = 0.f;
+            for (int c = lane; c < cs; c += 64) s += mass(c);
+            cum = vwave_sum(s);
+        }
+        if (lane == 0) {
             chunk_s = cs;
             rem_s = target - cum;
             lq_s = residual ? lse_q[j] : 0.f;
-            lp_s = lse_p[j];
-            resid_s = residual ? 1 : 0;
-            n_accept[b] = j;
+            lp_s = lpj;
         }
     }
     __syncthreads();
     const int cs = chunk_s;
-    if (cs < 0) return;                         // decided above (target-only or bad token)
+    if (cs < 0) return;
     // scan chunk cs: the first v whose cumulative weight exceeds rem
-    const bool residual = resid_s != 0;
-    const int j = j_s;
     const float* q = dl + ((size_t)b * K + (j < K ? j : 0)) * V;
     const float* p = tl + ((size_t)b * (K + 1) + j) * V;
     const float lq = lq_s, lp = lp_s, rem = rem_s;
     const int v0 = cs * kVChunk, v1 = min(V, v0 + kVChunk);
     // thread t owns the contiguous values [v0 + 32 t, v0 + 32 t + 32)
+    float xp[kVPer], xq[kVPer];
+    auto load_row = [&](const float* x, float* out) {
+        if (VEC) {     // V % 4 == 0: a 4-value group is wholly inside or outside
+#pragma unroll
+            for (int i = 0; i < kVPer / 4; ++i) {
+                const int v = v0 + kVPer * tid + 4 * i;
+                float4 t4 = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+                if (v < v1) t4 = *reinterpret_cast<const float4*>(x + v);
+                out[4 * i] = t4.x * inv_t;
+                out[4 * i + 1] = t4.y * inv_t;
+                out[4 * i + 2] = t4.z * inv_t;
+                out[4 * i + 3] = t4.w * inv_t;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kVPer; ++i) {
+                const int v = v0 + kVPer * tid + i;
+                out[i] = v < v1 ? x[v] * inv_t : -INFINITY;
+            }
+        }
+    };
+    load_row(p, xp);
+    if (residual) load_row(q, xq);
     float wv[kVPer];
     float tsum = 0.f;
     int tlast = -1;
@@ -466,8 +582,8 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(
         const int v = v0 + kVPer * tid + i;
         float x = 0.f;
         if (v < v1) {
-            const float pv = __expf(p[v] * inv_t - lp);
-            x = residual ? fmaxf(pv - __expf(q[v] * inv_t - lq), 0.f) : pv;
+            const float pv = __expf(xp[i] - lp);
+            x = residual ? fmaxf(pv - __expf(xq[i] - lq), 0.f) : pv;
         }
         wv[i] = x;
         tsum += x;
@@ -480,10 +596,6 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(
         if (lane >= o) incl += t;
     }
     if (lane == 63) wsum[w] = incl;
-    if (tid == 0) {
-        found_s = INT_MAX;
-        last_s = -1;
-    }
     __syncthreads();
     float before = incl - tsum;
     for (int i = 0; i < w; ++i) before += wsum[i];
@@ -494,10 +606,27 @@ __global__ __launch_bounds__(kVThreads) void verify_decide_kernel(
         cum += wv[i];
         if (hit == INT_MAX && wv[i] > 0.f && cum > rem) hit = v0 + kVPer * tid + i;
     }
-    if (hit != INT_MAX) atomicMin(&found_s, hit);
-    if (tlast >= 0) atomicMax(&last_s, tlast);
+    // threads own ascending value ranges: the first hit is the lowest
+    // hitting lane's, the last positive value the highest positive lane's
+    // (per wave by ballot, then over the waves; same-address LDS atomics
+    // from every lane serialise)
+    const unsigned long long hb = __ballot(hit != INT_MAX);
+    const unsigned long long lb = __ballot(tlast >= 0);
+    const int hit_w = __builtin_amdgcn_readlane(hit, hb ? __builtin_ctzll(hb) : 0);
+    const int last_v = __builtin_amdgcn_readlane(tlast, lb ? 63 - __builtin_clzll(lb) : 0);
+    if (lane == 0) {
+        found_w[w] = hb ? hit_w : INT_MAX;
+        last_w[w] = lb ? last_v : -1;
+    }
     __syncthreads();
-    if (tid == 0) next_token[b] = found_s != INT_MAX ? found_s : last_s;
+    if (tid == 0) {
+        int found = INT_MAX, last = -1;
+        for (int i = 0; i < kVThreads / 64; ++i) {
+            found = min(found, found_w[i]);
+            last = max(last, last_w[i]);
+        }
+        next_token[b] = found != INT_MAX ? found : last;
+    }
 }
 
 size_t decide_lds_bytes(int K, int C) { return (size_t)(2 * K + 1) * C * 16 + (size_t)K * C * 8; }
@@ -684,21 +813,22 @@ dspark_status dspark_spec_verify(const dspark_verify_desc* desc, const float* dr
     const int C = L.chunks;
     const float inv_t = (float)(1.0 / d.temperature);
     const int rows = d.B * (2 * d.K + 1);
-    if (d.vocab % 4 == 0 && al16(draft_logits) && al16(target_logits)) {
+    const bool vec = d.vocab % 4 == 0 && al16(draft_logits) && al16(target_logits);
+    if (vec) {
         hipLaunchKernelGGL(verify_stats_kernel<true>, dim3(rows * C), dim3(kVThreads), 0, s, d.B,
-                           d.K, d.vocab, C, inv_t, draft_logits, target_logits, part);
+                           d.K, d.vocab, C, inv_t, draft_logits, target_logits, draft_tokens, part);
         hipLaunchKernelGGL(verify_overlap_kernel<true>, dim3(d.B * d.K * C), dim3(kVThreads), 0, s,
                            d.B, d.K, d.vocab, C, inv_t, draft_logits, target_logits, part, ov);
     } else {
         hipLaunchKernelGGL(verify_stats_kernel<false>, dim3(rows * C), dim3(kVThreads), 0, s, d.B,
-                           d.K, d.vocab, C, inv_t, draft_logits, target_logits, part);
+                           d.K, d.vocab, C, inv_t, draft_logits, target_logits, draft_tokens, part);
         hipLaunchKernelGGL(verify_overlap_kernel<false>, dim3(d.B * d.K * C), dim3(kVThreads), 0,
                            s, d.B, d.K, d.vocab, C, inv_t, draft_logits, target_logits, part, ov);
     }
-    hipLaunchKernelGGL(verify_decide_kernel, dim3(d.B), dim3(kVThreads), decide_lds_bytes(d.K, C), s,
-                       d.B, d.K, d.vocab, C,
-                       d.mode, inv_t, draft_logits, target_logits, draft_tokens, uniforms, part, ov,
-                       accept_prob, overlap, n_accept, next_token);
+    auto* decide = vec ? verify_decide_kernel<true> : verify_decide_kernel<false>;
+    hipLaunchKernelGGL(decide, dim3(d.B), dim3(kVThreads), decide_lds_bytes(d.K, C), s, d.B, d.K,
+                       d.vocab, C, d.mode, inv_t, draft_logits, target_logits, draft_tokens,
+                       uniforms, part, ov, accept_prob, overlap, n_accept, next_token);
     const hipError_t he = hipGetLastError();
     if (he != hipSuccess) {
         snprintf(t_msg, sizeof(t_msg), "verify launch: %s", hipGetErrorString(he));
