@@ -25,7 +25,7 @@
 // through LDS (the weight staging area, free after start) and stored one
 // 1 KB q_abs row per instruction: in the MFMA tile layout (16 rows x 64 B
 // per instruction) the stores ran ~20% slower.
-#include "kernels.hpp"
+#include "index.hpp"
 
 namespace dspark {
 
@@ -60,12 +60,17 @@ struct AbsCfg {
 // acc / acc_n4 (the backward's W_UV^T dout, KD = d_v): the workgroups first
 // clear the fp32 dc^KV accumulator (acc_n4 float4) when the slots' anchors
 // do not ascend (status[kStUnsorted]): the atomic sums need it zeroed.
-template <int KD, int PARTS>
+// SELF_INDEX (one round of at most kSelfIndexMax blocks): every workgroup
+// builds the index itself while its first weight part is in flight and
+// keeps the slot table in LDS; workgroup 0 also writes the index records and
+// status words for the launches after it, so no launch has to precede this
+// one.
+template <int KD, int PARTS, bool SELF_INDEX = false>
 __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
     const bf16* __restrict__ q_nope, const bf16* __restrict__ w_uk,
     const int32_t* __restrict__ kept, const int32_t* __restrict__ status,
     bf16* __restrict__ q_abs, int N, int L5, int slot0, int nslots, uint32_t q_bytes,
-    float4* __restrict__ acc, size_t acc_n4) {
+    float4* __restrict__ acc, size_t acc_n4, SelfIndexArgs si) {
     using C = AbsCfg<KD, PARTS>;
     if constexpr (KD == kDv) {
         if (status[kStUnsorted] != 0) {
@@ -82,6 +87,8 @@ __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
     // copy into one does not touch the other
     __shared__ __attribute__((aligned(16))) char qa_s[kAbsFrags * 1024];
     __shared__ __attribute__((aligned(16))) char qb_s[kAbsFrags * 1024];
+    // the slot table when this launch builds the index
+    __shared__ int kept_l[SELF_INDEX ? kSelfIndexMax : 1];
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int rg = lid % kAbsRowGroups;
     const int h = lid / kAbsRowGroups;
@@ -91,9 +98,19 @@ __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
 
     // rows of this chunk: kept slots [slot0, slot0 + nslots); local row r is
     // query r % 5 of slot slot0 + r / 5
-    const int rows = kBlock * max(0, min(nslots, status[kStKeptCount] - slot0));
-    const int n_iter = (rows + kAbsRowsPerIter - 1) / kAbsRowsPerIter;
-    if (rg >= n_iter) return;
+    int rows = 0, n_iter = 0;
+    auto set_rows = [&](int n_kept) {
+        rows = kBlock * max(0, min(nslots, n_kept - slot0));
+        n_iter = (rows + kAbsRowsPerIter - 1) / kAbsRowsPerIter;
+    };
+    auto kept_at = [&](int slot) -> int {
+        if constexpr (SELF_INDEX) return kept_l[slot];
+        else return kept[slot];
+    };
+    if constexpr (!SELF_INDEX) {
+        set_rows(status[kStKeptCount]);
+        if (rg >= n_iter) return;
+    }
 
     // ---- A operand: fragment (ks, dt) holds output dims 64w + 16dt + l16
     // and k-values c = 32ks + 8g .. +7, read transposed out of the [c][d]
@@ -133,6 +150,15 @@ __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
                                   shared_area + 1024 * i);
                 }
             }
+            if constexpr (SELF_INDEX) {
+                if (part == 0) {
+                    __shared__ IndexScratch<kAbsWaves * 64> sc;
+                    set_rows(build_index<kAbsWaves * 64>(
+                        si.total, si.S, si.W, N, si.anchors, si.keep, sc, kept_l,
+                        blockIdx.x == 0, si.idx, si.kept, si.srec, si.status, nullptr, nullptr,
+                        0, si.path_tag));
+                }
+            }
             __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
             __syncthreads();
             if (wave / C::WavesPerPart == part) {
@@ -149,6 +175,11 @@ __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
             __syncthreads();
         }
+    }
+
+    // a workgroup with no rows leaves once its weight copies have landed
+    if constexpr (SELF_INDEX) {
+        if (rg >= n_iter) return;
     }
 
     // ---- q^C copies: fragment f = T * 6 + ks of an iteration holds rows
@@ -200,14 +231,14 @@ __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
     // Iteration: wait for its copy (issued one iteration earlier) and the
     // block index of the next copy, start that copy into the other buffer,
     // store the previous iteration's results, compute.
-    int cblk = kept[slot0 + copy_row(rg) / kBlock];
+    int cblk = kept_at(slot0 + copy_row(rg) / kBlock);
     stage(rg, cblk, qa_s);
-    cblk = kept[slot0 + copy_row(rg + kAbsRowGroups) / kBlock];
+    cblk = kept_at(slot0 + copy_row(rg + kAbsRowGroups) / kBlock);
     auto iteration = [&](int it, const char* cur, char* other) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();
         stage(it + kAbsRowGroups, cblk, other);
-        cblk = kept[slot0 + copy_row(it + 2 * kAbsRowGroups) / kBlock];
+        cblk = kept_at(slot0 + copy_row(it + 2 * kAbsRowGroups) / kBlock);
         if (it != rg) flush();
 
         f32x4 acc[kAbsDt][kAbsTiles];
@@ -271,12 +302,20 @@ __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
 }  // namespace
 
 hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
-                         hipStream_t s) {
+                         hipStream_t s, const int32_t* anchors, const uint8_t* keep,
+                         int32_t path_tag) {
     const int grid = kH * kAbsRowGroups;
-    hipLaunchKernelGGL((absorb_kernel<kDc, 2>), dim3(grid), dim3(kAbsWaves * 64), 0, s,
+    const bool self_index = anchors != nullptr;
+    if (self_index && (p.B * p.N > kSelfIndexMax || c.slot0 != 0 || c.nslots < p.B * p.N))
+        return hipErrorInvalidValue;
+    const SelfIndexArgs si{anchors, keep, p.B * p.N, p.S, p.W, path_tag,
+                           ws.idx, ws.kept, ws.srec, ws.status};
+    auto* kernel = self_index ? absorb_kernel<kDc, 2, true> : absorb_kernel<kDc, 2, false>;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kAbsWaves * 64), 0, s,
                        (const bf16*)in.q_nope, (const bf16*)in.w_uk, ws.kept, ws.status, ws.qabs,
                        p.N, p.L5, c.slot0, c.nslots,
-                       (uint32_t)((size_t)p.B * p.L5 * kH * kDc * sizeof(bf16)), nullptr, 0);
+                       (uint32_t)((size_t)p.B * p.L5 * kH * kDc * sizeof(bf16)), nullptr,
+                       (size_t)0, si);
     return hipGetLastError();
 }
 
@@ -287,7 +326,7 @@ hipError_t launch_absorb_dv(const Problem& p, const void* dout, const void* w_uv
     hipLaunchKernelGGL((absorb_kernel<kDv, 4>), dim3(grid), dim3(kAbsWaves * 64), 0, s,
                        (const bf16*)dout, (const bf16*)w_uv, ws.kept, ws.status, dolat, p.N, p.L5,
                        0, p.B * p.N, (uint32_t)((size_t)p.B * p.L5 * kH * kDv * sizeof(bf16)),
-                       reinterpret_cast<float4*>(acc), n / 4);
+                       reinterpret_cast<float4*>(acc), n / 4, SelfIndexArgs{});
     return hipGetLastError();
 }
 

@@ -402,9 +402,16 @@ dspark_status forward_impl(const dspark_attn_desc* desc, const void* q_nope, con
     // the fixed scratch is never handed to a backward: no tag
     // the MFMA path writes the rows of padding blocks in the last W_UV
     // launch's tail instead of here
-    if ((e = launch_prep(p, anchors, keep, ws, nullptr, L.rope_rows, fast ? nullptr : &theta,
-                         nullptr, s, fixed ? 0 : forward_tag(d, path, keep_p))) != hipSuccess)
-        return hip_fail(e, "index / RoPE table / fill launch");
+    const int32_t tag = fixed ? 0 : forward_tag(d, path, keep_p);
+    // one round of at most kSelfIndexMax blocks: the absorb launch builds the
+    // index itself and no preparation launch runs (stage event [1] then
+    // follows [0] directly)
+    const bool self_index = fast && n_chunks == 1 && d.B * d.N <= kSelfIndexMax;
+    if (!self_index) {
+        if ((e = launch_prep(p, anchors, keep, ws, nullptr, L.rope_rows,
+                             fast ? nullptr : &theta, nullptr, s, tag)) != hipSuccess)
+            return hip_fail(e, "index / RoPE table / fill launch");
+    }
     if ((e = mark(1)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if (fast) {
         hipEvent_t fork = aux ? static_cast<hipEvent_t>(opts->aux_events[0]) : nullptr;
@@ -421,7 +428,8 @@ dspark_status forward_impl(const dspark_attn_desc* desc, const void* q_nope, con
             const Chunk ch{c * chunk, chunk};
             if ((e = mark_on(2 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
             const Workspace wr = fixed ? round_latents(ws, p, ch.slot0) : ws;
-            if ((e = launch_absorb(p, in, wr, ch, st)) != hipSuccess)
+            if ((e = launch_absorb(p, in, wr, ch, st, self_index ? anchors : nullptr,
+                                   self_index ? keep : nullptr, tag)) != hipSuccess)
                 return hip_fail(e, "absorb launch");
             if ((e = mark_on(3 + 4 * c, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
             if ((e = launch_attn(p, in, wr, ch, theta, st, pmat)) != hipSuccess)
@@ -659,10 +667,15 @@ dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc, const void* q_nop
     const bool load_p = reuse && fast && opts->reuse_forward == 2;
     const int32_t tag = forward_tag(d, fast ? FwdPath::kMaterialised : FwdPath::kGeneric);
     const int32_t tag_p = forward_tag(d, FwdPath::kMaterialised, true);
+    // at most kSelfIndexMax blocks on the MFMA path: the q_abs launch builds
+    // the index itself (the index stage event follows event [0] directly)
+    const bool self_index = fast && !reuse && d.B * d.N <= kSelfIndexMax;
     if (reuse) {
         DSPARK_STEP(launch_bwd_reuse_check(p, w, load_p ? tag_p : tag,
                                            (fast && !load_p) ? tag_p : 0, s),
                     "reuse check launch");
+    } else if (self_index) {
+        if ((e = mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
     } else {
         DSPARK_STEP(launch_prep(p, anchors, keep, w.fwd, nullptr, L.fwd.rope_rows,
                                 fast ? nullptr : &theta, nullptr, s, tag),
@@ -681,7 +694,10 @@ dspark_status dspark_attn_bwd_ex(const dspark_attn_desc* desc, const void* q_nop
         if (reuse) {
             if ((e = mark()) != hipSuccess) return hip_fail(e, "hipEventRecord");
         } else {
-            DSPARK_STEP(launch_absorb(p, in, w.fwd, Chunk{0, d.B * d.N}, s), "absorb launch");
+            DSPARK_STEP(launch_absorb(p, in, w.fwd, Chunk{0, d.B * d.N}, s,
+                                      self_index ? anchors : nullptr,
+                                      self_index ? keep : nullptr, tag),
+                        "absorb launch");
         }
         DSPARK_STEP(launch_absorb_dv(p, dout, w_uv, w.fwd, w.dolat, w.acc, zero_n, s),
                     "W_UV^T dout launch");

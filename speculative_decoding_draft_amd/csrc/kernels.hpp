@@ -55,8 +55,30 @@ struct Chunk {
     int nslots;
 };
 
+// Largest B*N for which the absorb launch builds the index itself (its
+// slot table lives in LDS).
+constexpr int kSelfIndexMax = 1024;
+
+// The inputs and outputs of the index build, for an absorb launch that runs
+// it itself.
+struct SelfIndexArgs {
+    const int32_t* anchors;
+    const uint8_t* keep;
+    int total, S, W;
+    int32_t path_tag;
+    int4* idx;
+    int32_t* kept;
+    int4* srec;
+    int32_t* status;
+};
+
+// anchors / keep != nullptr: the launch also builds the index (as
+// launch_prep without RoPE table and fill, path_tag to the status area), so
+// no preparation launch precedes it; only for one round (c covers every
+// block) of at most kSelfIndexMax blocks (hipErrorInvalidValue otherwise).
 hipError_t launch_absorb(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,
-                         hipStream_t s);
+                         hipStream_t s, const int32_t* anchors = nullptr,
+                         const uint8_t* keep = nullptr, int32_t path_tag = 0);
 // pmat: nullptr, or where the normalised probabilities go as well (bf16,
 // [slot][5 H][kKeySlots]) for a backward that reuses them.
 hipError_t launch_attn(const Problem& p, const Inputs& in, const Workspace& ws, Chunk c,

@@ -1,11 +1,7 @@
 // Preparation pass, one launch: the anchor/window index, the RoPE table and
 // the rows of blocks that are not computed (padding, invalid anchors).
 //
-// Index (GLM 5.2 DSpark training-design page, §3 "attention mask"): a kept
-// block with anchor A sees the context columns [max(0, A-W+1), A) -- at most
-// W-1 of them, A excluded, the same for its 5 queries -- plus its own 5
-// draft columns; a padding block (keep = 0) sees nothing and its anchor is
-// never read.  A kept anchor must lie in [0, S-2] (§2 "Anchor sampling").
+// Index: build_index (index.hpp), run by one 1024-thread workgroup.
 //
 // RoPE (§4 "RoPE"): interleaved adjacent pairs; pair i of a vector at
 // position p rotates by p * theta_i with theta_i = base^(-2i/d_r).  The
@@ -19,9 +15,8 @@
 // Workgroup 0 builds the index; the next ones fill the RoPE table, the rest
 // fill rows, so the three parts run side by side.
 #include <algorithm>
-#include <climits>
 
-#include "kernels.hpp"
+#include "index.hpp"
 
 namespace dspark {
 
@@ -29,94 +24,6 @@ namespace {
 
 constexpr int kPrepThreads = 1024;
 constexpr int kIndexThreads = kPrepThreads;
-
-// One workgroup: scans all B*N blocks in order, so the kept slots are the
-// ranks of the kept blocks in (b, n) order.
-__device__ void build_index(int total, int S, int W, int N, const int32_t* __restrict__ anchors,
-                            const uint8_t* __restrict__ keep, int4* __restrict__ idx,
-                            int32_t* __restrict__ kept, int4* __restrict__ srec,
-                            int32_t* __restrict__ status, int4* __restrict__ idx_copy,
-                            int32_t* __restrict__ ctl, int ctl_words, int32_t path_tag) {
-    __shared__ int wave_count[kIndexThreads / 64];
-    __shared__ int first_bad_sh;
-    // the chunk's kept blocks in slot order (block index, anchor), and the
-    // last kept block before the chunk, for the anchor-order check
-    __shared__ int2 chunk_kept[kIndexThreads];
-    __shared__ int2 prev_kept;
-    __shared__ int unsorted_sh;
-    const int tid = threadIdx.x;
-    for (int i = tid; i < ctl_words; i += kIndexThreads) ctl[i] = 0;
-    if (tid == 0) {
-        status[kStPipeFault] = 0;
-        status[kStPathTag] = path_tag;
-        status[kStReuseBad] = 0;
-    }
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    if (tid == 0) {
-        first_bad_sh = INT_MAX;
-        prev_kept = make_int2(-1, 0);
-        unsorted_sh = 0;
-    }
-    int carry = 0;        // kept blocks before this chunk (same value in every thread)
-    int first_bad = INT_MAX;
-    __syncthreads();
-    for (int base = 0; base < total; base += kIndexThreads) {
-        const int i = base + tid;
-        int state = 0;    // 0 padding / out of range, 1 kept, 2 kept with a bad anchor
-        int4 rec = make_int4(0, 0, 0, -1);
-        if (i < total && keep[i] != 0) {
-            const int A = anchors[i];
-            if (A >= 0 && A <= S - 2) {
-                const int lo = (A - W + 1 > 0) ? (A - W + 1) : 0;
-                rec = make_int4(lo, A - lo, A, 0);
-                state = 1;
-            } else {
-                rec = make_int4(0, 0, 0, -2);
-                state = 2;
-                first_bad = min(first_bad, i);
-            }
-        }
-        const unsigned long long ballot = __ballot(state == 1);
-        const int before_in_wave = __popcll(ballot & ((1ull << lane) - 1ull));
-        if (lane == 0) wave_count[wave] = __popcll(ballot);
-        __syncthreads();
-        int before = carry;
-        int chunk = 0;
-        for (int w = 0; w < kIndexThreads / 64; ++w) {
-            const int c = wave_count[w];
-            if (w < wave) before += c;
-            chunk += c;
-        }
-        if (state == 1) {
-            rec.w = before + before_in_wave;
-            kept[rec.w] = i;
-            srec[rec.w] = make_int4(rec.x, rec.y, rec.z, i);
-            chunk_kept[rec.w - carry] = make_int2(i, rec.z);
-        }
-        if (i < total) {
-            idx[i] = rec;
-            if (idx_copy) idx_copy[i] = rec;
-        }
-        __syncthreads();
-        // anchors descend between two consecutive kept slots of one sample
-        if (state == 1) {
-            const int r = rec.w - carry;
-            const int2 prev = r > 0 ? chunk_kept[r - 1] : prev_kept;
-            if (prev.x >= 0 && prev.x / N == i / N && rec.z < prev.y) unsorted_sh = 1;
-        }
-        __syncthreads();   // wave_count, chunk_kept and prev_kept are rewritten next
-        if (tid == 0 && chunk > 0) prev_kept = chunk_kept[chunk - 1];
-        carry += chunk;
-    }
-    if (first_bad != INT_MAX) atomicMin(&first_bad_sh, first_bad);
-    __syncthreads();
-    if (tid == 0) {
-        status[kStKeptCount] = carry;
-        status[kStFirstBad] = (first_bad_sh == INT_MAX) ? -1 : first_bad_sh;
-        status[kStUnsorted] = unsorted_sh;
-    }
-}
 
 // table[p][i] = (cos, sin)(p * theta_i).  The angle is formed and reduced to
 // [-pi, pi] in fp64 (two-term 2*pi), then evaluated in fp32: an fp32 angle
@@ -147,8 +54,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(
     RopeTheta th, float2* __restrict__ table, int rope_wgs, bf16* __restrict__ out, int N,
     int L5, int H, int dv) {
     if (blockIdx.x == 0) {
-        build_index(total, S, W, N, anchors, keep, idx, kept, srec, status, idx_copy, ctl,
-                    ctl_words, path_tag);
+        __shared__ IndexScratch<kIndexThreads> sc;
+        build_index<kIndexThreads>(total, S, W, N, anchors, keep, sc, nullptr, true, idx, kept,
+                                   srec, status, idx_copy, ctl, ctl_words, path_tag);
         return;
     }
     const int r = blockIdx.x - 1;
