@@ -69,9 +69,9 @@ KERNEL_SOURCES = {"absorb": "absorb.hip", "attention": "attn.hip", "w_uv": "uv.h
 # The headline's index is built inside the absorb launch (no preparation
 # launch runs), so absorb's bytes include it.
 PMC_TRAFFIC = {
-    "absorb": (358_859_492, "95be09572d9a9bfd"),
-    "attention": (583_299_212, "3e2fce7fecc208d3"),
-    "w_uv": (436_545_500, "21e962f19481d329"),
+    "absorb": (358_861_477, "01b07695fce01035"),
+    "attention": (583_434_500, "4c469051f3ab5f15"),
+    "w_uv": (436_550_001, "c350d3045986165b"),
 }
 PMC_SOURCE = "rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, profiles/attn_fwd_headline_S32768_N1024_counters.md"
 
@@ -87,12 +87,12 @@ BWD_KERNEL_SOURCES = {
     "final": ("bwd_misc.hip", "bwd.hpp", "common.hpp", "kernels.hpp"),
 }
 BWD_PMC_TRAFFIC = {
-    "attention_bwd": (1_293_575_553, "a775f3577e86f2e1"),
-    "dw": (758_221_567, "8923854cc143c847"),
-    "dkv": (1_001_981_832, "8923854cc143c847"),
-    "dq_nope": (358_924_475, "21e962f19481d329"),
-    "d_olat": (394_468_505, "95be09572d9a9bfd"),
-    "final": (311_311_761, "db42b588a48bc49a"),
+    "attention_bwd": (1_293_601_290, "423619f69f79a403"),
+    "dw": (757_902_599, "3ff6fdbc26332773"),
+    "dkv": (1_001_676_042, "3ff6fdbc26332773"),
+    "dq_nope": (358_924_480, "c350d3045986165b"),
+    "d_olat": (394_464_495, "01b07695fce01035"),
+    "final": (311_311_256, "4d1dd8f62b34ea4d"),
 }
 
 
@@ -101,9 +101,9 @@ BWD_PMC_TRAFFIC = {
 # three launches; 64 sequences, K = 5, V = 154880): the same FETCH/WRITE
 # scaling, with the files each is built from and their digest when taken.
 SIDE_PMC_TRAFFIC = {
-    "loss_stats": (3_882_860_544, ("loss.hip", "blas.hpp", "kernels.hpp"), "09065d6a57d0225c"),
-    "verify": (436_689_264 + 398_406_204 + 4_409_600, ("decode.hip", "kernels.hpp"),
-               "339b2bd88284a523"),
+    "loss_stats": (3_882_859_940, ("loss.hip", "blas.hpp", "kernels.hpp"), "9133278bf6e34a79"),
+    "verify": (436_689_308 + 398_406_720 + 4_409_600, ("decode.hip", "kernels.hpp"),
+               "0e246a99590adc3e"),
 }
 
 

@@ -112,6 +112,28 @@ __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
         if (rg >= n_iter) return;
     }
 
+    // ---- q^C copies: fragment f = T * 6 + ks of an iteration holds rows
+    // 16T + l16 and k-values 32ks + 8g .. +7 (16 rows x 64 B); wave w copies
+    // fragments 3w .. 3w+2, all of row tile w / 2.  Rows past the end copy
+    // the last row.  The copies are issued from inline asm (waited for at the
+    // top of every iteration) so that the compiler adds no waits of its own.
+    auto clamp_row = [&](int r) { return (r < rows) ? r : rows - 1; };
+    const int copy_tile = (kAbsCopies * wave) / kAbsKs;
+    auto copy_row = [&](int it) { return clamp_row(it * kAbsRowsPerIter + 16 * copy_tile + l16); };
+    const i32x4 q_rs = rsrc_words(q_nope, q_bytes);
+    auto stage = [&](int it, int blk, char* dst) {
+        const int r = copy_row(it);
+        const int b = blk / N, n = blk % N;
+        const uint32_t off = (uint32_t)(
+            ((((size_t)b * L5 + (size_t)kBlock * n + r % kBlock) * kH + h) * KD + g * 8) *
+            sizeof(bf16));
+#pragma unroll
+        for (int j = 0; j < kAbsCopies; ++j) {
+            const int f = kAbsCopies * wave + j;
+            copy_16_untracked(q_rs, off + (f % kAbsKs) * 64, dst + f * 1024);
+        }
+    };
+
     // ---- A operand: fragment (ks, dt) holds output dims 64w + 16dt + l16
     // and k-values c = 32ks + 8g .. +7, read transposed out of the [c][d]
     // staging copy of one column part of the weight (the waves whose dims it
@@ -161,6 +183,9 @@ __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
             }
             __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
             __syncthreads();
+            // the first iteration's q^C copy goes out once the rows are known
+            // (the index, built during part 0), so it overlaps the next part
+            if (part == 0 && rg < n_iter) stage(rg, kept_at(slot0 + copy_row(rg) / kBlock), qa_s);
             if (wave / C::WavesPerPart == part) {
                 const int wd = wave % C::WavesPerPart;
 #pragma unroll
@@ -181,28 +206,6 @@ __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
     if constexpr (SELF_INDEX) {
         if (rg >= n_iter) return;
     }
-
-    // ---- q^C copies: fragment f = T * 6 + ks of an iteration holds rows
-    // 16T + l16 and k-values 32ks + 8g .. +7 (16 rows x 64 B); wave w copies
-    // fragments 3w .. 3w+2, all of row tile w / 2.  Rows past the end copy
-    // the last row.  The copies are issued from inline asm (waited for at the
-    // top of every iteration) so that the compiler adds no waits of its own.
-    auto clamp_row = [&](int r) { return (r < rows) ? r : rows - 1; };
-    const int copy_tile = (kAbsCopies * wave) / kAbsKs;
-    auto copy_row = [&](int it) { return clamp_row(it * kAbsRowsPerIter + 16 * copy_tile + l16); };
-    const i32x4 q_rs = rsrc_words(q_nope, q_bytes);
-    auto stage = [&](int it, int blk, char* dst) {
-        const int r = copy_row(it);
-        const int b = blk / N, n = blk % N;
-        const uint32_t off = (uint32_t)(
-            ((((size_t)b * L5 + (size_t)kBlock * n + r % kBlock) * kH + h) * KD + g * 8) *
-            sizeof(bf16));
-#pragma unroll
-        for (int j = 0; j < kAbsCopies; ++j) {
-            const int f = kAbsCopies * wave + j;
-            copy_16_untracked(q_rs, off + (f % kAbsKs) * 64, dst + f * 1024);
-        }
-    };
 
     // ---- output transpose: every wave writes its 64 dims (128 B) of each of
     // the 64 rows, then wave w stores rows 8w .. 8w+7, one 1 KB row per
@@ -231,9 +234,7 @@ __global__ __launch_bounds__(kAbsWaves * 64) void absorb_kernel(
     // Iteration: wait for its copy (issued one iteration earlier) and the
     // block index of the next copy, start that copy into the other buffer,
     // store the previous iteration's results, compute.
-    int cblk = kept_at(slot0 + copy_row(rg) / kBlock);
-    stage(rg, cblk, qa_s);
-    cblk = kept_at(slot0 + copy_row(rg + kAbsRowGroups) / kBlock);
+    int cblk = kept_at(slot0 + copy_row(rg + kAbsRowGroups) / kBlock);
     auto iteration = [&](int it, const char* cur, char* other) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();

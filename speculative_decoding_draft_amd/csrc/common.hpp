@@ -140,6 +140,13 @@ __device__ inline bf16x8 gld16(const bf16* p) { return *(const gbf16x8*)(p); }
 __device__ inline bf16x4 gld8(const bf16* p) { return *(const gbf16x4*)(p); }
 __device__ inline void gst16(bf16* p, bf16x8 v) { *(gbf16x8*)(p) = v; }
 __device__ inline void gst8(bf16* p, bf16x4 v) { *(gbf16x4*)(p) = v; }
+// Non-temporal store (the line is not kept dirty in L2), for whole rows that
+// no later launch of the call reads (the forward's output): the launch's end
+// then has fewer dirty L2 lines to write back before the next launch starts.
+// Rows a later launch reads are stored normally, so that they are read from
+// the Infinity Cache; stores of partial lines (64-byte pieces) are also
+// slower this way.
+__device__ inline void gst16_nt(bf16* p, bf16x8 v) { __builtin_nontemporal_store(v, (gbf16x8*)(p)); }
 
 // LDS accesses (pointers into __shared__ arrays)
 __device__ inline bf16x8 ld16(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }

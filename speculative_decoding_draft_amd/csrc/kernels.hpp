@@ -110,7 +110,7 @@ __device__ inline void fill_block(int blk, int S, int N, int L5, int H, int dv,
     const int b = blk / N, n = blk % N;
     bf16* base = out + ((size_t)b * L5 + (size_t)kBlock * n) * H * dv;
     const int chunks = kBlock * H * dv / 8;
-    for (int e = threadIdx.x; e < chunks; e += blockDim.x) gst16(base + (size_t)e * 8, fv);
+    for (int e = threadIdx.x; e < chunks; e += blockDim.x) gst16_nt(base + (size_t)e * 8, fv);
 }
 // The whole forward after the preparation launch as one persistent launch
 // of kFusedCus workgroups (GLM dims; the control words must be zero).

@@ -188,10 +188,14 @@ __global__ __launch_bounds__(DOUT / 32 * 64) void uv_kernel(const bf16* __restri
             const int r = min(prow0 + out_row(j), rows - 1);
             const int blk = (r / kBlock == pslot) ? pk[0] : pk[1];
             const int b = blk / N, n = blk % N;
-            if ((lane & 31) < DOUT / 8)
-                gst16(out + (((size_t)b * L5 + (size_t)kBlock * n + r % kBlock) * kH + h) * DOUT +
-                          (lane & 31) * 8,
-                      v);
+            bf16* dst = out + (((size_t)b * L5 + (size_t)kBlock * n + r % kBlock) * kH + h) * DOUT +
+                        (lane & 31) * 8;
+            // non-temporal when no wave repeats another's row pair (a repeated
+            // store would then reach HBM twice instead of merging in L2)
+            if ((lane & 31) < DOUT / 8) {
+                if constexpr (kUvStores * kUvWaves == kUvRows / 2) gst16_nt(dst, v);
+                else gst16(dst, v);
+            }
         }
     };
 
