@@ -144,3 +144,18 @@ def sample_blocks(keep_row: np.ndarray, anchors_row: np.ndarray, W: int, n_rando
     rng = np.random.default_rng(seed)
     pick = rng.choice(rest, size=min(n_random, len(rest)), replace=False).tolist() if rest else []
     return sorted(set(clamped + pick + ([rest[0], rest[-1]] if rest else [])))
+
+
+def context_of_two(seed):
+    """The shortest context a block can have: S = 2, so A = 0 is the only valid
+    anchor and every block sees only its own 5 keys.  Several kept blocks of a
+    sample share that anchor (repeated anchors are valid input), with padding
+    between them; odd N, B = 2, GLM dims (the MFMA path)."""
+    wl = wk.make_workload("ctx2", B=2, S=2, N=5, dims=wk.GLM_DIMS, dtype="bf16",
+                          recipe="sampler", seed=seed)
+    wl.anchor_source = "given"
+    wl.anchors = np.zeros((2, 5), np.int32)
+    wl.keep = np.array([[1, 1, 0, 1, 1], [0, 1, 1, 0, 1]], np.uint8)
+    wl.anchors[0, 2] = -9                   # padding slot: its anchor is never read
+    wl.loss_mask[:, :] = 1
+    return wl

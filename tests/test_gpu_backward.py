@@ -23,7 +23,7 @@ import pytest
 
 import oracle as O
 import workloads as wk
-from gpu_util import anchors_for, desc_for, log, sample_blocks
+from gpu_util import anchors_for, context_of_two, desc_for, log, sample_blocks
 from workloads.device import to_torch, upload_anchors, upload_layer
 
 pytestmark = pytest.mark.gpu
@@ -138,6 +138,13 @@ def test_bwd_generic_bf16_glm_dims():
 def test_bwd_mfma_scaled(k, S, N):
     wl = wk.scaled(k, S=S, N=N)
     run_case(wl, tol=BF16_MFMA_TOL, form="gathered")
+
+
+def test_bwd_context_of_two_positions():
+    """S = 2: every kept block anchors at 0 (repeated within a sample), so the
+    context gradients are all zero and every gradient comes from the blocks'
+    own keys; MFMA path."""
+    run_case(context_of_two(92), tol=BF16_MFMA_TOL, form="dense")
 
 
 def test_bwd_mfma_matches_generic_path():

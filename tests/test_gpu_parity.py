@@ -7,7 +7,7 @@ import pytest
 import oracle as O
 import workloads as wk
 from gpu_util import (BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS, F32_REL_L2, ForwardRun, HipEventPool,
-                      anchors_for, compare, desc_for, log, sample_blocks)
+                      anchors_for, compare, desc_for, log, sample_blocks, context_of_two)
 
 pytestmark = pytest.mark.gpu
 
@@ -296,6 +296,10 @@ def test_anchor_at_last_valid_position_and_single_block(sd):
     wl.anchors[0, 0] = 298
     wl.loss_mask[0, 298] = wl.loss_mask[0, 299] = 1
     check_full(wl, form="dense")
+
+
+def test_context_of_two_positions(sd):
+    check_full(context_of_two(91), form="dense", guard=256)
 
 
 def test_three_samples_mixed_blocks(sd):
