@@ -159,3 +159,22 @@ def context_of_two(seed):
     wl.anchors[0, 2] = -9                   # padding slot: its anchor is never read
     wl.loss_mask[:, :] = 1
     return wl
+
+
+def repeated_anchors(seed):
+    """Kept anchors drawn with replacement (about a third of them repeat an
+    earlier one), sorted, with a tenth of the slots padding and a few clamped
+    windows: at S = 640 and N = 200 enough kept blocks for the attention's
+    one-block-per-workgroup launch, and for runs of equal anchors in the
+    backward's per-row sums over covering blocks."""
+    wl = wk.make_workload("dup", B=1, S=640, N=200, dims=wk.GLM_DIMS, dtype="bf16",
+                          recipe="uniform", seed=seed)
+    rng = np.random.default_rng(seed)
+    a = np.sort(rng.integers(0, wl.S - 1, size=wl.N)).astype(np.int32)
+    a[:4] = [0, 0, 5, 126]
+    a = np.sort(a)
+    keep = (rng.random(wl.N) >= 0.1).astype(np.uint8)
+    a[keep == 0] = -1                        # padding: garbage anchors, never read
+    wl.anchors, wl.keep = a[None, :], keep[None, :]
+    wl.loss_mask[:, :] = 1
+    return wl

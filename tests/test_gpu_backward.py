@@ -23,7 +23,7 @@ import pytest
 
 import oracle as O
 import workloads as wk
-from gpu_util import anchors_for, context_of_two, desc_for, log, sample_blocks
+from gpu_util import anchors_for, context_of_two, desc_for, log, repeated_anchors, sample_blocks
 from workloads.device import to_torch, upload_anchors, upload_layer
 
 pytestmark = pytest.mark.gpu
@@ -145,6 +145,12 @@ def test_bwd_context_of_two_positions():
     context gradients are all zero and every gradient comes from the blocks'
     own keys; MFMA path."""
     run_case(context_of_two(92), tol=BF16_MFMA_TOL, form="dense")
+
+
+def test_bwd_repeated_kept_anchors():
+    """Equal anchors in a sorted sample: the per-row sums over the covering
+    blocks include runs of blocks with the same window."""
+    run_case(repeated_anchors(94), tol=BF16_MFMA_TOL, form="gathered")
 
 
 def test_bwd_mfma_matches_generic_path():

@@ -7,7 +7,8 @@ import pytest
 import oracle as O
 import workloads as wk
 from gpu_util import (BF16_MAX_ABS, BF16_REL_L2, F32_MAX_ABS, F32_REL_L2, ForwardRun, HipEventPool,
-                      anchors_for, compare, desc_for, log, sample_blocks, context_of_two)
+                      anchors_for, compare, desc_for, log, sample_blocks, context_of_two,
+                      repeated_anchors)
 
 pytestmark = pytest.mark.gpu
 
@@ -300,6 +301,13 @@ def test_anchor_at_last_valid_position_and_single_block(sd):
 
 def test_context_of_two_positions(sd):
     check_full(context_of_two(91), form="dense", guard=256)
+
+
+def test_repeated_kept_anchors(sd):
+    wl = repeated_anchors(93)
+    a = wl.anchors[0][wl.keep[0] == 1]
+    assert (wl.keep.sum() >= 160 and len(np.unique(a)) < len(a)), "case needs repeats"
+    check_full(wl, form="gathered")
 
 
 def test_three_samples_mixed_blocks(sd):
