@@ -118,6 +118,25 @@ MUTANTS = [
      "return np.asarray(pos) % slots", "return (np.asarray(pos) + 1) % slots"),
     ("decode window one position early", "dec",
      "ctx = np.arange(max(0, A - W + 1), A)", "ctx = np.arange(max(0, A - W), A)"),
+    ("padding blocks attend to their own block", "core",
+     "    if not keep_row[n]:\n        return rows\n    A = int(anchors_row[n])",
+     "    if False:\n        return rows\n    A = int(anchors_row[n])"),
+    ("dW_UK from the value path", "bwd",
+     'g["dw_uk"][h] += dKc.T @ C', 'g["dw_uk"][h] += dV[:, :d_c].T @ C'),
+    ("dK without the scale", "bwd",
+     "dK = scale * (dS.T @ Q)", "dK = (dS.T @ Q)"),
+    ("o_proj without the residual", "layer",
+     "out[qrows] = Hd[qrows] + o2[qrows] @ f(li.w_o).T", "out[qrows] = o2[qrows] @ f(li.w_o).T"),
+    ("kv_a of the draft rows from the un-normalised stream", "layer",
+     "kv_blk[qrows] = h[qrows] @ f(li.w_kva).T", "kv_blk[qrows] = Hd[qrows] @ f(li.w_kva).T"),
+    ("CE against the teacher's distribution", "loss",
+     "ce = -np.log(p[np.arange(L.shape[0]), np.asarray(y)])",
+     "ce = -np.log(q[np.arange(L.shape[0]), np.asarray(y)])"),
+    ("L1 squared", "loss",
+     "l1 = np.abs(p - q).sum(axis=1)", "l1 = ((p - q) ** 2).sum(axis=1)"),
+    ("bonus token drawn from the last drafted position", "dec",
+     "w = np.maximum(0.0, p[j] - q[j]) if j < K else p[K]",
+     "w = np.maximum(0.0, p[j] - q[j]) if j < K else p[K - 1]"),
 ]
 
 
