@@ -180,3 +180,41 @@ def test_identical_distributions_accept_everything():
     assert r["n_accept"] == 3
     np.testing.assert_allclose(r["accept_prob"], 1.0)
     np.testing.assert_allclose(r["overlap"], 1.0)
+
+
+def test_temperature_divides_the_logits():
+    """softmax(x / T): closed forms.  Logits (0, ln 4) at T = 2 are (0, ln 2),
+    probabilities (1/3, 2/3); (0, ln 9, 2 ln 9) at T = 2 give (1, 3, 9) / 13;
+    at T = 1/2 the first pair gives (1, 16) / 17."""
+    p = O.softmax_t(np.array([[0.0, np.log(4.0)]]), 2.0)[0]
+    assert np.allclose(p, [1 / 3, 2 / 3], rtol=0, atol=1e-15)
+    p = O.softmax_t(np.array([[0.0, np.log(9.0), 2 * np.log(9.0)]]), 2.0)[0]
+    assert np.allclose(p, np.array([1.0, 3.0, 9.0]) / 13.0, rtol=0, atol=1e-15)
+    p = O.softmax_t(np.array([[0.0, np.log(4.0)]]), 0.5)[0]
+    assert np.allclose(p, [1 / 17, 16 / 17], rtol=0, atol=1e-15)
+
+
+def test_temperature_flattens_and_verification_depends_on_logits_over_t():
+    """A higher temperature never lowers the entropy, and the whole
+    verification at temperature T equals the one at T = 1 on the logits
+    divided by T (decisions, draws, acceptance and overlap)."""
+    rng = np.random.default_rng(5)
+    x = rng.normal(0.0, 3.0, size=(4, 50))
+    ent = lambda p: -(p * np.log(p)).sum(axis=-1)
+    e = [ent(O.softmax_t(x, t)) for t in (0.5, 1.0, 2.0, 4.0)]
+    for lo, hi in zip(e, e[1:]):
+        assert np.all(hi >= lo - 1e-12)
+    K, V = 5, 40
+    for T in (0.7, 1.3, 2.5):
+        for s in range(20):
+            r = np.random.default_rng(100 + s)
+            dl = r.normal(0.0, 2.0, size=(K, V))
+            tl = r.normal(0.0, 2.0, size=(K + 1, V))
+            x_t = r.integers(0, V, size=K)
+            u = r.random(K + 1)
+            a = O.spec_verify(dl, tl, x_t, u, "rejection", temperature=T)
+            b = O.spec_verify(dl / T, tl / T, x_t, u, "rejection", temperature=1.0)
+            for k in ("n_accept", "next_token"):
+                assert a[k] == b[k], (T, s, k)
+            for k in ("accept_prob", "overlap"):
+                assert np.allclose(a[k], b[k], rtol=1e-12, atol=1e-15), (T, s, k)

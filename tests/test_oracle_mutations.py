@@ -137,6 +137,23 @@ MUTANTS = [
     ("bonus token drawn from the last drafted position", "dec",
      "w = np.maximum(0.0, p[j] - q[j]) if j < K else p[K]",
      "w = np.maximum(0.0, p[j] - q[j]) if j < K else p[K - 1]"),
+    ("temperature multiplies the logits", "dec",
+     "return _softmax_rows(np.asarray(logits, np.float64) / float(temperature))",
+     "return _softmax_rows(np.asarray(logits, np.float64) * float(temperature))"),
+    ("target-only compares against the draft's top choice", "dec",
+     "else (int(x[k]) == int(np.argmax(p[k])))", "else (int(x[k]) == int(np.argmax(q[k])))"),
+    ("RMSNorm gain dropped", "layer",
+     "+ eps) * np.asarray(g, np.float64)", "+ eps)"),
+    ("decode block positions start at A + 1", "dec",
+     "        blk = A + np.arange(BLOCK)\n", "        blk = A + 1 + np.arange(BLOCK)\n"),
+    ("decode queries left unrotated", "dec",
+     "Q = np.concatenate([qn[b][:, h, :], qrot[h]], axis=1)",
+     "Q = np.concatenate([qn[b][:, h, :], qr[b][:, h, :]], axis=1)"),
+    ("acceptance rate as a sum of maxima", "dec",
+     "return np.minimum(np.asarray(p, np.float64), np.asarray(q, np.float64)).sum(axis=-1)",
+     "return np.maximum(np.asarray(p, np.float64), np.asarray(q, np.float64)).sum(axis=-1)"),
+    ("rejection stops one token late", "dec",
+     "        if not ok:\n            j = k\n", "        if not ok:\n            j = min(k + 1, K)\n"),
 ]
 
 
