@@ -154,6 +154,20 @@ MUTANTS = [
      "return np.maximum(np.asarray(p, np.float64), np.asarray(q, np.float64)).sum(axis=-1)"),
     ("rejection stops one token late", "dec",
      "        if not ok:\n            j = k\n", "        if not ok:\n            j = min(k + 1, K)\n"),
+    ("mask not applied (every key visible)", "core",
+     "    logits = np.where(M, logits, -np.inf)\n", "    logits = np.where(M | True, logits, -np.inf)\n"),
+    ("softmax without its normaliser", "core",
+     "    return e / np.sum(e, axis=-1, keepdims=True)\n", "    return e\n"),
+    ("keys expanded through W_UV", "core",
+     "Kc = ckv_all @ w_uk[h].T            # [L, d_c]",
+     "Kc = ckv_all @ w_uv[h][:w_uk.shape[1]].T            # [L, d_c]"),
+    ("q_a_layernorm dropped", "layer",
+     "cq = rmsnorm(h[qrows] @ f(li.w_qa).T, f(li.g_qa), li.rms_eps)", "cq = h[qrows] @ f(li.w_qa).T"),
+    ("BCE target roles swapped", "loss",
+     "bce = -(a * log_sig + (1.0 - a) * log_1m)", "bce = -((1.0 - a) * log_sig + a * log_1m)"),
+    ("confidence head without the Markov embedding", "loss",
+     "x = np.concatenate([np.asarray(h_rows, np.float64), e], axis=-1)",
+     "x = np.concatenate([np.asarray(h_rows, np.float64), 0.0 * e], axis=-1)"),
 ]
 
 
