@@ -101,8 +101,10 @@ def test_decode_bench_shape():
     check_decode("decode bench shape", gpu, ref, active, (BF16_MAX_ABS, BF16_REL_L2))
 
 
-@pytest.mark.parametrize("C", [128, 200])
+@pytest.mark.parametrize("C", [127, 128, 200])
 def test_decode_glm_bf16(C):
+    """GLM dims, bf16; C = 127 = W - 1 is the smallest ring the window fits:
+    the window of the longest sequences then fills every slot."""
     dims = dict(wk.GLM_DIMS)
     anchors = [0, 3, 126, 127, 1_000_003, 5000, 131]
     active = [1, 1, 1, 1, 1, 0, 1]
