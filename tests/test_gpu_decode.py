@@ -189,7 +189,8 @@ def check_verify(name, inputs, got, mode, T=1.0, skip=()):
 
 
 @pytest.mark.parametrize("V,mode,T", [(1000, "rejection", 1.0), (20000, "rejection", 0.7),
-                                      (8192 * 2 + 3, "target_only", 1.0), (777, "target_only", 1.3)])
+                                      (8192 * 2 + 3, "target_only", 1.0), (777, "target_only", 1.3),
+                                      (1, "rejection", 1.0), (1, "target_only", 1.0)])
 def test_verify_matches_oracle(V, mode, T):
     inputs, got = run_verify(16, 5, V, mode, T)
     check_verify(f"verify V={V} {mode} T={T}", inputs, got, mode, T)

@@ -98,11 +98,12 @@ def small(seed, B=2, S=64, N=6, V=300, d=24, r=8, dtype="f32", recipe="headline"
     return wl, wk.make_loss_inputs(wl, V, d, r, seed=seed + 1)
 
 
-@pytest.mark.parametrize("V,d,r", [(300, 24, 8), (301, 10, 3), (8192 + 20, 32, 8)])
+@pytest.mark.parametrize("V,d,r", [(300, 24, 8), (301, 10, 3), (8192 + 20, 32, 8), (1, 12, 4)])
 def test_loss_small_fp32(V, d, r):
     """fp32 storage; V not a multiple of 4 (scalar statistics loads), d and r
-    whose rows are not 16-byte multiples (scalar gather), and V spanning two
-    statistics chunks with a ragged tail."""
+    whose rows are not 16-byte multiples (scalar gather), V spanning two
+    statistics chunks with a ragged tail, and a one-token vocabulary (CE and
+    L1 are 0, the confidence target 1)."""
     wl, lh = small(41, V=V, d=d, r=r)
     terms, em, loss, st, _ = run_loss(wl, lh, wl.anchors, wl.keep)
     assert st[0] == 0, st
